@@ -1,0 +1,412 @@
+"""Pins of the CPU oracle to what the pages and mathematics fix (no GPU).
+
+Each test checks the oracle against something other than itself: worked
+bytes from the little-endian packing convention, closed forms, invariants of
+PCA, brute force on tiny DP instances, textbook Huffman facts and the byte
+formulas the pages define.
+"""
+import itertools
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+
+from oracle import kvtc_oracle as O
+from kv_cache_compression_kvtc_amd import synth
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+# ---------------------------------------------------------------- packing
+def test_pack_golden_bytes():
+    data = json.load(open(os.path.join(GOLDEN, "pack_le.json")))
+    for case in data["cases"]:
+        b = case["width"]
+        codes = np.array([case["codes"]], dtype=np.int64)
+        bits = [b] * codes.shape[1]
+        _, row_bits = O.field_offsets(bits)
+        stride = O.row_stride_bytes(row_bits)
+        packed = O.pack_rows(codes, bits, stride)[0]
+        want = case["bytes"]
+        assert list(packed[: len(want)]) == want, case
+        assert not packed[len(want):].any(), "padding must be zero"
+        assert (O.unpack_rows(packed[None, :], bits) == codes).all()
+
+
+@pytest.mark.parametrize("b", [1, 2, 4])
+def test_unpack_matches_page_vectorised_formula(b, rng):
+    # the TurboQuant page's vectorised unpack: unpackbits(little) for b=1,
+    # (byte >> shifts) & mask for b=2 and b=4
+    n, d = 37, 96
+    packed = rng.integers(0, 256, size=(n, d * b // 8), dtype=np.uint8)
+    if b == 1:
+        page = np.unpackbits(packed, axis=1, bitorder="little")[:, :d]
+    else:
+        shifts = np.arange(0, 8, b, dtype=np.uint8)
+        page = ((packed[:, :, None] >> shifts[None, None, :]) & (2 ** b - 1)).reshape(n, -1)[:, :d]
+    ours = O.unpack_rows(packed, [b] * d)
+    assert (ours == page).all()
+
+
+def test_pack_roundtrip_mixed_widths(rng):
+    for trial in range(20):
+        r = int(rng.integers(1, 70))
+        bits = rng.choice([0, 1, 2, 3, 4, 8], size=r)
+        _, row_bits = O.field_offsets(bits)
+        stride = O.row_stride_bytes(row_bits)
+        assert stride % 4 == 0 and 8 * stride >= row_bits > 8 * stride - 32 or row_bits == 0
+        n = int(rng.integers(1, 9))
+        codes = np.stack([rng.integers(0, 2 ** int(b), size=n) if b else np.zeros(n, np.int64)
+                          for b in bits], axis=1)
+        rows = O.pack_rows(codes, bits, stride)
+        assert (O.unpack_rows(rows, bits) == codes).all()
+        # the field of component i holds its code at bit offset sum(bits[:i]) of the row
+        i = int(rng.integers(0, r))
+        off = int(np.sum(bits[:i]))
+        as_int = int.from_bytes(rows[0].tobytes(), "little")
+        assert (as_int >> off) & (2 ** int(bits[i]) - 1) == codes[0, i]
+        # bits past the last field are zero
+        assert as_int >> row_bits == 0
+
+
+# ---------------------------------------------------------------- quantiser
+def test_quantize_hand_example_half_even_and_clamp():
+    # min -1, scale 0.5, 2 bits: t = (l + 1) / 0.5
+    l = np.array([-1.0, -0.74, -0.75, 0.6, 5.0, -9.0, -0.25, 0.25])
+    # t:          0    0.52   0.5   3.2  12   -16   1.5    2.5
+    want = [0, 1, 0, 3, 3, 0, 2, 2]
+    assert list(O.quantize_affine(l, -1.0, 0.5, 2)) == want
+
+
+def test_quantize_zero_scale_gives_code_zero():
+    assert list(O.quantize_affine(np.array([3.0, -2.0]), 3.0, 0.0, 4)) == [0, 0]
+
+
+def test_mixed_quantiser_hand_example():
+    L = np.array([[0.0, 1.0, 2.0, 3.0], [10.0, 10.0, 10.0, 10.0]])
+    codes, params = O.quantize_mixed(L, [2, 2, 2, 2], group_size=4)
+    assert codes[0].tolist() == [0, 1, 2, 3]
+    assert params[0, 0].tolist() == [0.0, 1.0]
+    assert codes[1].tolist() == [0, 0, 0, 0] and params[1, 0].tolist() == [10.0, 0.0]
+    # fp16 rounding of a group min that sits far from zero (the bottom code may go unused)
+    L = np.array([[10.003, 10.006, 10.01, 10.013]])
+    codes, params = O.quantize_mixed(L, [2] * 4, group_size=4)
+    assert float(params[0, 0, 0]) == 10.0
+    assert abs(float(params[0, 0, 1]) - (0.010 / 3)) < 2e-6
+    t = (L[0] - 10.0) / float(params[0, 0, 1])
+    assert codes[0].tolist() == np.clip(np.rint(t), 0, 3).astype(int).tolist()
+    assert codes[0].min() == 1
+
+
+def test_mixed_quantiser_properties(rng):
+    L = rng.standard_normal((50, 96)) * np.linspace(3, 0.1, 96)[None, :]
+    bits = O.allocate_mixed(96, 4, 2, 0.25, 32)
+    assert bits.tolist() == [4] * 32 + [2] * 64
+    codes, params = O.quantize_mixed(L, bits, 32)
+    Lh = O.dequant_mixed(codes, params, 32)
+    for g in range(3):
+        b = int(bits[32 * g])
+        seg = slice(32 * g, 32 * g + 32)
+        assert codes[:, seg].min() >= 0 and codes[:, seg].max() <= 2 ** b - 1
+        mn16 = params[:, g, 0].astype(np.float64)[:, None]
+        sc16 = params[:, g, 1].astype(np.float64)[:, None]
+        t = (L[:, seg] - mn16) / sc16
+        inside = (t > 0) & (t < 2 ** b - 1)
+        err = np.abs(Lh[:, seg] - L[:, seg])
+        assert (err[inside] <= 0.5 * np.broadcast_to(sc16, err.shape)[inside] * (1 + 1e-12)).all()
+
+
+# ---------------------------------------------------------------- fit / PCA
+def _tiny_rows(tensor=0, S=256):
+    w = synth.WORKLOADS[1]
+    return synth.unit_rows(w, tensor, 0, 0, 0, S)
+
+
+def test_pca_orthonormal_and_eigen_residual():
+    X = _tiny_rows()
+    mean, lam, V = O.pca_fit(X)
+    D = X.shape[1]
+    assert np.abs(V.T @ V - np.eye(D)).max() <= 1e-12
+    assert np.abs(V.astype(np.float32).astype(np.float64).T @ V.astype(np.float32) - np.eye(D)).max() <= 1e-6
+    Y = X - X.mean(axis=0)
+    C = Y.T @ Y / X.shape[0]
+    assert np.abs(C @ V - V * lam[None, :]).max() <= 1e-10 * np.abs(C).max()
+    assert (np.diff(lam) <= 0).all()
+    # cross-check with a different library routine: singular values of the centred rows
+    sv = np.linalg.svd(Y, compute_uv=False)
+    assert np.allclose(lam, sv ** 2 / X.shape[0], rtol=1e-10, atol=1e-14)
+    # sign rule: the largest-magnitude entry of each column is positive
+    k = np.argmax(np.abs(V), axis=0)
+    assert (V[k, np.arange(D)] > 0).all()
+
+
+def test_latents_are_decorrelated_with_variance_lambda():
+    # a transposed basis or a wrong centring breaks this PCA property
+    X = _tiny_rows(tensor=1)
+    mean, lam, V = O.pca_fit(X)
+    L = O.project(X, mean, V)
+    Cl = L.T @ L / X.shape[0]
+    assert np.abs(L.mean(axis=0)).max() < 1e-12
+    assert np.abs(Cl - np.diag(lam)).max() <= 1e-10 * lam[0]
+
+
+def test_transform_is_invertible_at_full_rank():
+    X = _tiny_rows()
+    mean, lam, V = O.pca_fit(X)
+    Xr = O.reconstruct(O.project(X, mean, V), mean, V)
+    assert np.abs(Xr - X).max() <= 1e-12 * np.abs(X).max()
+
+
+def test_energy_rank_hand_examples():
+    lam = np.array([4.0, 3.0, 2.0, 1.0])
+    assert O.energy_rank(lam, 0.7) == 2      # cumulative 0.4, 0.7, 0.9, 1.0
+    assert O.energy_rank(lam, 0.71) == 3
+    assert O.energy_rank(lam, 0.4) == 1
+    assert O.energy_rank(lam, 1.0) == 4
+    assert O.energy_rank(np.zeros(3), 0.9) == 1
+    lam = np.arange(1, 129, dtype=np.float64) ** -1.2
+    k = O.energy_rank(lam, 0.9)
+    c = np.cumsum(lam) / lam.sum()
+    assert c[k - 1] >= 0.9 > c[k - 2]
+
+
+# ---------------------------------------------------------------- DP allocation
+def _brute(lam, budget, choices, beta):
+    best, arg = math.inf, []
+    for combo in itertools.product(sorted(choices), repeat=len(lam)):
+        if sum(combo) > budget:
+            continue
+        v = sum(lam[i] if b == 0 else beta * lam[i] * 4.0 ** -b for i, b in enumerate(combo))
+        if v < best - 1e-15 * max(1.0, best):
+            best, arg = v, [combo]
+        elif abs(v - best) <= 1e-15 * max(1.0, best):
+            arg.append(combo)
+    return best, arg
+
+
+def test_dp_matches_brute_force(rng):
+    pool = [0, 1, 2, 3, 4, 8]
+    for trial in range(60):
+        r = int(rng.integers(1, 6))
+        k = int(rng.integers(1, 5))
+        choices = tuple(sorted(rng.choice(pool, size=k, replace=False).tolist()))
+        if 0 not in choices and trial % 2 == 0:
+            choices = (0,) + choices
+        lam = np.sort(rng.gamma(1.0, 1.0, size=r))[::-1]
+        budget = int(rng.integers(0, 48))
+        beta = float(rng.choice([1.0, 0.5, 2.0]))
+        if 0 not in choices and r * min(choices) > budget:
+            with pytest.raises(O.OracleConfigError):
+                O.allocate_dp(lam, budget, choices, beta)
+            continue
+        bits = O.allocate_dp(lam, budget, choices, beta)
+        assert bits.sum() <= budget and set(bits.tolist()) <= set(choices)
+        best, args = _brute(lam, budget, choices, beta)
+        got = O.dp_objective(lam, bits, beta)
+        assert abs(got - best) <= 1e-12 * max(1.0, best)
+        if len(args) == 1:
+            assert tuple(bits.tolist()) == args[0]
+
+
+def test_dp_monotone_in_budget_and_sorted(rng):
+    lam = np.sort(rng.gamma(0.5, 1.0, size=40))[::-1]
+    prev = math.inf
+    for budget in range(0, 200, 7):
+        bits = O.allocate_dp(lam, budget, (0, 1, 2, 3, 4, 8), 1.0)
+        v = O.dp_objective(lam, bits, 1.0)
+        assert v <= prev + 1e-15
+        prev = v
+        # larger variance never gets fewer bits (exchange argument for sorted lam)
+        assert (np.diff(bits) <= 0).all()
+
+
+def test_dp_zero_budget_drops_everything():
+    assert O.allocate_dp(np.array([3.0, 1.0]), 0, (0, 1, 2), 1.0).tolist() == [0, 0]
+
+
+def test_dp_equal_lambdas_are_permutation_consistent():
+    # equal variances: the optimum splits the budget evenly (convexity of 4**-b),
+    # and any permutation of it is equally good
+    bits = O.allocate_dp(np.ones(6), 10, (0, 1, 2, 4), 1.0)
+    assert bits.sum() == 10 and max(bits) - min(bits) <= 1
+    perm = bits[::-1]
+    assert O.dp_objective(np.ones(6), perm, 1.0) == O.dp_objective(np.ones(6), bits, 1.0)
+
+
+# ---------------------------------------------------------------- Huffman
+def test_huffman_textbook_cases():
+    assert O.huffman_bits([8, 4, 2, 2]) == 16 * (0.5 * 1 + 0.25 * 2 + 0.125 * 3 * 2)  # dyadic: N*H
+    assert O.huffman_bits([5] * 16) == 80 * 4          # uniform over 16 symbols: 4 bits each
+    assert O.huffman_bits([0, 7, 0]) == 7              # one symbol: one bit each
+    assert O.huffman_bits([3, 1]) == 4
+    assert O.huffman_bits([]) == 0
+
+
+def test_huffman_within_entropy_bounds(rng):
+    for _ in range(30):
+        k = int(rng.integers(2, 40))
+        counts = rng.integers(0, 100, size=k)
+        counts[0] += 1
+        counts[1] += 1
+        N = counts.sum()
+        p = counts[counts > 0] / N
+        H = -(p * np.log2(p)).sum()
+        total = O.huffman_bits(counts)
+        assert N * H - 1e-9 <= total < N * (H + 1)
+
+
+# ---------------------------------------------------------------- whole path
+def _cfg(w, **kw):
+    c = O.Config(mode=w.mode, head_dim=w.D, heads_per_unit=w.heads_per_unit, rank=w.rank,
+                 energy=w.energy, budget=w.budget, choices=w.choices, beta=w.beta,
+                 hi_bits=w.hi_bits, lo_bits=w.lo_bits, hi_fraction=w.hi_fraction,
+                 group_size=w.group_size)
+    for k, v in kw.items():
+        setattr(c, k, v)
+    return c
+
+
+def test_zero_budget_reconstructs_the_mean():
+    w = synth.WORKLOADS[1]
+    X = synth.generate(w, 0)
+    st = O.fit(_cfg(w, budget=0), X[:, :, :256])
+    assert st.bits.sum() == 0 and st.row_stride == 0
+    rows, _ = O.append(st, X)
+    out = O.fetch(st, rows)
+    mu = O.scatter_units(np.broadcast_to(st.mu32[:, None, :], (st.U, X.shape[2], st.Dg)), 1, 2, 1)
+    assert (out == mu.astype(np.float64)).all()
+    assert (O.to_f16(out) == mu.astype(np.float16)).all()
+
+
+def test_dropped_component_contributes_exactly_nothing():
+    w = synth.WORKLOADS[1]
+    X = synth.generate(w, 1)
+    st = O.fit(_cfg(w, budget=60), X[:, :, :256])
+    rows, _ = O.append(st, X)
+    out = O.fetch(st, rows)
+    assert (st.bits == 0).any()
+    for u in range(st.U):
+        keep = st.bits[u] > 0
+        codes = O.unpack_rows(rows[u], st.bits[u])
+        Lh = O.dequant_dp(codes, st.bits[u], st.qmin32[u], st.qscale32[u])[:, keep]
+        alt = Lh @ st.V32[u][:, keep].astype(np.float64).T + st.mu32[u].astype(np.float64)
+        assert np.abs(alt - out[0, u]).max() <= 1e-12 * max(1.0, np.abs(alt).max())
+
+
+def test_same_codes_whether_tokens_arrive_one_at_a_time_or_together():
+    # KVTC page, "NOT PATH-DEPENDENT": one-at-a-time after prefill == all at once
+    w = synth.WORKLOADS[1]
+    for tensor in (0, 1):
+        X = synth.generate(w, tensor)
+        st = O.fit(_cfg(w), X[:, :, :256])
+        r_pre, _ = O.append(st, X[:, :, :256])
+        steps = [O.append(st, X[:, :, s:s + 1])[0] for s in range(256, 288)]
+        one_by_one = np.concatenate([r_pre] + steps, axis=1)
+        together = np.concatenate([r_pre, O.append(st, X[:, :, 256:288])[0]], axis=1)
+        whole = O.append(st, X)[0]
+        assert (one_by_one == together).all() and (together == whole).all()
+        assert (O.to_f16(O.fetch(st, one_by_one)) == O.to_f16(O.fetch(st, whole))).all()
+
+
+def test_near_lossless_at_full_rank_8_bits():
+    w = synth.WORKLOADS[1]
+    X = synth.generate(w, 0)[:, :, :256]
+    st = O.fit(_cfg(w, budget=8 * w.D, choices=(8,)), X)
+    assert (st.bits == 8).all()
+    rows, _ = O.append(st, X)
+    out = O.fetch(st, rows)
+    for u in range(st.U):
+        Vabs = np.abs(st.V32[u].astype(np.float64))
+        bound = Vabs @ (0.5 * st.qscale32[u].astype(np.float64) * (1 + 1e-6)) \
+            + 1e-5 * np.abs(X[0, u]).max()
+        err = np.abs(out[0, u] - X[0, u].astype(np.float64))
+        assert (err <= bound[None, :]).all()
+        assert err.max() < 0.02 * (X[0, u].max() - X[0, u].min())
+
+
+def test_out_of_range_rows_clamp_to_the_end_codes():
+    w = synth.WORKLOADS[1]
+    X = synth.generate(w, 0)[:, :, :256]
+    st = O.fit(_cfg(w), X)
+    u, i = 0, 0
+    assert st.bits[u, i] > 0
+    v = st.V32[u][:, i].astype(np.float64)
+    far = np.stack([st.mu32[u] + 1e3 * v, st.mu32[u] - 1e3 * v])       # beyond both ends
+    x = np.zeros((1, 2, 2, w.D), np.float32)
+    x[0, u] = far
+    rows, _ = O.append(st, x)
+    codes = O.unpack_rows(rows[u], st.bits[u])
+    b = int(st.bits[u, i])
+    assert codes[0, i] == 2 ** b - 1 and codes[1, i] == 0
+    Lh = O.dequant_dp(codes, st.bits[u], st.qmin32[u], st.qscale32[u])
+    assert Lh[1, i] == float(st.qmin32[u, i])
+    assert Lh[0, i] == float(st.qmin32[u, i]) + (2 ** b - 1) * float(st.qscale32[u, i])
+
+
+def test_identity_basis_reduces_to_per_channel_affine_quantisation(rng):
+    # with V = I the method is the textbook per-channel min/max quantiser
+    D, S = 8, 40
+    X = rng.standard_normal((S, D)) * np.arange(1, D + 1)
+    bits = np.array([8, 4, 4, 3, 2, 2, 1, 0])
+    mu32 = np.zeros(D, np.float32)
+    V32 = np.eye(D, dtype=np.float32)
+    qmin, qscale = O.frozen_ranges(X, mu32, V32, bits)
+    st = O.TensorState(O.Config(head_dim=D, rank=D), 1, 1, D, 1, np.array([D]), mu32[None],
+                       np.zeros((1, D)), V32[None], bits[None], qmin[None], qscale[None],
+                       O.row_stride_bytes(int(bits.sum())))
+    rows, _ = O.append(st, X[None, None].astype(np.float64))
+    out = O.fetch(st, rows)[0, 0]
+    for d in range(D):
+        b = bits[d]
+        if b == 0:
+            assert (out[:, d] == 0).all()
+            continue
+        lo, hi = X[:, d].min(), X[:, d].max()
+        lo32 = float(np.float32(lo))
+        sc32 = float(np.float32((hi - lo) / (2 ** b - 1)))
+        q = np.clip(np.rint((X[:, d] - lo32) / sc32), 0, 2 ** b - 1)
+        assert np.array_equal(out[:, d], lo32 + q * sc32)
+
+
+# ---------------------------------------------------------------- byte formulas
+def test_byte_formulas_and_entropy_fallback():
+    w = synth.WORKLOADS[1]
+    X = synth.generate(w, 0)
+    st = O.fit(_cfg(w), X[:, :, :256])
+    rows, _ = O.append(st, X)
+    S = X.shape[2]
+    rep = O.bytes_report(st, rows, None, S)
+    assert O.full_seq_bytes(1, 2, S, 64) == 1 * 2 * S * 64 * 4
+    assert rep.fp16_equiv == 1 * 2 * S * 64 * 2
+    row_bits = [st.row_bits(u) for u in range(st.U)]
+    assert rep.fixed_payload == sum((S * rb + 7) // 8 for rb in row_bits)
+    # entropy-coded payload + table never above fixed width (KVTC page, "Byte accounting")
+    assert rep.entropy_payload + rep.entropy_table <= rep.fixed_payload
+    assert rep.total <= rep.pre_entropy
+    assert rep.pre_entropy == rep.fixed_payload + rep.basis + rep.quant_params
+    assert rep.n_survived == int((st.bits > 0).sum())
+
+
+def test_palu_effective_bits_formula():
+    # PALU page: effective width ~ (r / D) * weighted average of hi and lo widths
+    bits = O.allocate_mixed(256, 4, 2, 0.25, 32)
+    assert int(bits.sum()) == 640
+    assert bits.sum() / 1024 == pytest.approx((256 / 1024) * (0.25 * 4 + 0.75 * 2))
+
+
+def test_config_errors():
+    X = np.zeros((1, 2, 4, 8))
+    with pytest.raises(O.OracleConfigError):
+        O.fit(O.Config(head_dim=8, rank=8, choices=(5,)), X)
+    with pytest.raises(O.OracleConfigError):
+        O.fit(O.Config(head_dim=8, rank=8, budget=0, choices=(1, 2)), X)
+    with pytest.raises(O.OracleConfigError):
+        O.fit(O.Config(head_dim=8, rank=8), X[:, :, :1])
+    with pytest.raises(O.OracleConfigError):
+        O.fit(O.Config(head_dim=8, rank=9), X)
+    with pytest.raises(O.OracleConfigError):
+        O.allocate_dp(np.ones(2), -1, (0, 1), 1.0)
+    with pytest.raises(O.OracleConfigError):
+        O.allocate_dp(np.ones(3), 2, (1, 2), 1.0)
