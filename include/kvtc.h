@@ -1,0 +1,245 @@
+/*
+ * kvtc.h -- C ABI of the transform-coded KV-cache library (libkvtc.so), gfx950.
+ *
+ * The method (KVTC cache module page, veloxquant_mlx.cache.kvtc_cache, module
+ * docstring "Design"; PALU cache API page, veloxquant_mlx.cache.palu_cache,
+ * "Design"): a basis, a mean and a per-component bit allocation are fitted
+ * once on the prefill rows of every unit and frozen.  A unit is one
+ * (batch, head) pair, or one (batch, contiguous head group) whose heads share
+ * one projection.  Append projects new rows through the frozen basis,
+ * quantises every kept latent component at its frozen width (0 bits drops a
+ * component) and packs the codes.  Fetch unpacks, dequantises and
+ * reconstructs the whole stored sequence to fp16 [B, H, S, D].
+ *
+ * Conventions for every entry point:
+ *   - all pointers are plain addresses; "host" pointers are CPU memory,
+ *     "dev" pointers are device (HBM) memory of the current HIP device;
+ *   - the caller owns every buffer; the library allocates no device memory,
+ *     keeps no global state and is reentrant; host scratch lives only for
+ *     the duration of a call;
+ *   - device work is enqueued on the given hipStream_t (NULL = the null
+ *     stream) and the call returns after the enqueue;
+ *   - every argument is validated before anything is launched or written; a
+ *     failing call returns a negative status and writes nothing;
+ *   - no C++ exception crosses this interface.
+ */
+#ifndef KVTC_H
+#define KVTC_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* ---------------------------------------------------------------- status */
+#define KVTC_OK          0
+#define KVTC_E_CONFIG   -1  /* invalid or infeasible configuration (budget < 0: the
+                               KVTC page's QuantizerConfigError in KVTCKVCache.__init__) */
+#define KVTC_E_SHAPE    -2  /* shape, stride or alignment does not match the state */
+#define KVTC_E_DTYPE    -3  /* unsupported element type */
+#define KVTC_E_CAPACITY -4  /* rows outside [0, capacity) */
+#define KVTC_E_STATE    -5  /* state blob missing, unfitted or corrupt */
+#define KVTC_E_BUFSIZE  -6  /* output buffer too small (the size needed is returned) */
+#define KVTC_E_DEVICE   -7  /* HIP launch or runtime error */
+#define KVTC_E_ARG      -8  /* NULL pointer or out-of-range scalar argument */
+
+#define KVTC_F32 0
+#define KVTC_F16 1
+
+/* KVTC_MODE_DP: one unit per (batch, head); per-unit DP bit allocation under a
+ *   bits-per-token budget, per-component frozen (min, scale) (KVTC page).
+ * KVTC_MODE_MIXED: one unit per (batch, group of heads_per_unit contiguous
+ *   heads) sharing one projection; the leading hi_fraction of components at
+ *   hi_bits, the rest at lo_bits; per-token (min, scale) in fp16 for every
+ *   group_size consecutive components (PALU page, palu_* parameters). */
+#define KVTC_MODE_DP    0
+#define KVTC_MODE_MIXED 1
+
+#define KVTC_MAX_CHOICES 8
+
+/* Configuration; kvtc_config_default() fills the documented defaults
+ * (KVTC page, KVTCKVCache.__init__; PALU page, PALUKVCache parameters). */
+typedef struct kvtc_config {
+    int32_t mode;              /* KVTC_MODE_DP or KVTC_MODE_MIXED */
+    int32_t head_dim;          /* D; the device path needs D % 64 == 0 */
+    int32_t heads_per_unit;    /* 1 in DP mode; the head-group size in mixed mode */
+    int32_t rank;              /* > 0: kept components per unit (<= heads_per_unit*D);
+                                  0: smallest rank reaching energy_threshold */
+    double  energy_threshold;  /* default 0.90 */
+    int32_t bit_budget;        /* DP: code bits per token per unit, >= 0; default 4*D */
+    int32_t n_choices;         /* DP: allowed widths, a subset of {0,1,2,3,4,8} */
+    int32_t choices[KVTC_MAX_CHOICES];
+    double  beta;              /* DP distortion-proxy constant, default 1.0 */
+    int32_t hi_bits;           /* mixed: default 4 */
+    int32_t lo_bits;           /* mixed: default 2 */
+    int32_t group_size;        /* mixed: components per (min, scale) pair, default 32,
+                                  must be a multiple of 16 */
+    double  hi_fraction;       /* mixed: default 0.25 */
+} kvtc_config;
+
+/* ------------------------------------------------------------ state blob */
+/* The frozen state of one tensor (K or V) is one position-independent blob:
+ * this header followed by 256-byte aligned sections at the given offsets.
+ * The host copy and the device copy hold the same bytes.  "slot" j of a unit
+ * is its j-th stored component: in DP mode the j-th component with a
+ * non-zero width (index order), in mixed mode component j. */
+#define KVTC_MAGIC   0x4354564Bu  /* "KVTC" little-endian */
+#define KVTC_VERSION 1u
+
+typedef struct kvtc_unit_info {
+    int32_t rank;        /* kept components (DP: before dropping 0-bit ones) */
+    int32_t n_slots;     /* stored components */
+    int32_t row_bits;    /* code bits per token */
+    int32_t reserved;
+} kvtc_unit_info;
+
+typedef struct kvtc_state_header {
+    uint32_t magic, version;
+    int32_t  mode, head_dim, heads_per_unit, dg;   /* dg = heads_per_unit * head_dim */
+    int64_t  batch, heads, units;                  /* units = batch*heads/heads_per_unit */
+    int32_t  rmax;          /* widest kept rank over units */
+    int32_t  kslots;        /* slot capacity per unit: max n_slots rounded up to 16 (>= 16) */
+    int32_t  row_stride;    /* bytes per stored code row: 4 * ceil(max row_bits / 32) */
+    int32_t  n_qgroups;     /* mixed: (min, scale) pairs per token; 0 in DP mode */
+    int32_t  group_size, hi_bits, lo_bits, n_hi;
+    int32_t  bit_budget, n_choices;
+    int32_t  choices[KVTC_MAX_CHOICES];
+    double   beta;
+    double   energy_threshold;
+    int32_t  rank_cfg;      /* configured rank (0 = energy threshold) */
+    int32_t  reserved0;
+    int64_t  s_prefill;     /* rows the state was fitted on (0 if built from parts) */
+    /* per-unit sections */
+    uint64_t off_unit;      /* kvtc_unit_info [units] */
+    uint64_t off_lambda;    /* double [units][dg]   eigenvalues, descending (0 if unknown) */
+    uint64_t off_bits;      /* uint8  [units][rmax] width of component i (0 = dropped) */
+    uint64_t off_qmin;      /* float  [units][rmax] DP frozen min of component i */
+    uint64_t off_qscale;    /* float  [units][rmax] DP frozen scale of component i */
+    uint64_t off_mu;        /* float  [units][dg]   mean */
+    uint64_t off_slot_comp; /* int32  [units][kslots] component index of slot j (-1 = empty) */
+    uint64_t off_slot_bits; /* uint32 [units][kslots] bit offset in the row | width << 24 */
+    uint64_t off_basis;     /* float  [units][kslots][dg] basis vector of slot j (0 = empty) */
+    uint64_t off_qlo;       /* double [units][kslots] DP: min of slot j, as stored (fp32 value) */
+    uint64_t off_qinv;      /* double [units][kslots] DP: 1/scale of slot j (0 if scale is 0) */
+    uint64_t off_w16;       /* half   [units][dg][kslots] fetch operand: DP scale_j*basis_j,
+                               mixed basis_j, rounded to fp16 */
+    uint64_t off_bias;      /* float  [units][dg] fetch bias: DP mu + sum_j min_j*basis_j,
+                               mixed mu */
+    uint64_t total_bytes;
+    uint64_t reserved[4];
+} kvtc_state_header;
+
+/* ---------------------------------------------------------- entry points */
+
+/* Fill *cfg with the defaults of the given mode and head dimension. */
+void kvtc_config_default(kvtc_config *cfg, int32_t mode, int32_t head_dim);
+
+/* Human-readable name of a status code (static string). */
+const char *kvtc_status_string(int32_t status);
+
+/* Fit the frozen state of one tensor on its prefill rows (host).
+ * KVTC page, update_and_fetch and _TensorKVTC.fit_prefill_from_pca: local PCA
+ * per unit on the prefill batch, then the DP bit allocation, then the
+ * per-component ranges; PALU page "Design" steps 1-2 for mixed mode.
+ *   rows_host   contiguous [B, H, S, D] host rows, dtype KVTC_F32 or KVTC_F16
+ *   S           prefill rows, >= 2 (the KVTC page fits on the first call with S > 1)
+ *   state_out   host buffer of *state_bytes bytes, or NULL to query the size
+ *   state_bytes in: capacity of state_out; out: bytes needed / written
+ * Returns KVTC_E_CONFIG for an invalid or infeasible configuration,
+ * KVTC_E_BUFSIZE (with *state_bytes set) if state_out is too small. */
+int32_t kvtc_fit_host(const kvtc_config *cfg, const void *rows_host, int32_t dtype,
+                      int64_t B, int64_t H, int64_t S,
+                      void *state_out, size_t *state_bytes);
+
+/* Build a state blob from an already fitted frozen state (host), for example a
+ * basis calibrated elsewhere.  Arrays are host memory, unit-major:
+ *   ranks   int32 [U]           kept components per unit (1..rmax)
+ *   mu      float [U][dg]
+ *   basis   float [U][rmax][dg] component i's basis vector in row i
+ *   lambda  double [U][dg] or NULL
+ *   bits    uint8 [U][rmax]     widths in {0,1,2,3,4,8} (DP) -- ignored in mixed
+ *                               mode, where the hi/lo rule of cfg decides them
+ *   qmin, qscale float [U][rmax] DP frozen (min, scale) -- NULL in mixed mode
+ * U = B*H/heads_per_unit, dg = heads_per_unit*head_dim. */
+int32_t kvtc_state_build(const kvtc_config *cfg, int64_t B, int64_t H, int32_t rmax,
+                         const int32_t *ranks, const float *mu, const float *basis,
+                         const double *lambda, const uint8_t *bits,
+                         const float *qmin, const float *qscale, int64_t s_prefill,
+                         void *state_out, size_t *state_bytes);
+
+/* DP bit allocation alone (host): minimise sum_i D_i(b_i) subject to
+ * sum_i b_i <= budget, b_i in choices, with D_i(0) = lambda_i and
+ * D_i(b) = beta * lambda_i * 4^-b (KVTC page: DP-optimal discrete allocation
+ * over an analytic distortion proxy; a component may get 0 bits).  Narrower
+ * widths and fewer total bits win ties.  bits_out: uint8 [r]. */
+int32_t kvtc_allocate_bits(const double *lambda, int32_t r, int32_t budget,
+                           const int32_t *choices, int32_t n_choices, double beta,
+                           uint8_t *bits_out);
+
+/* Bytes of the device code store and of the mixed-mode parameter store for a
+ * given capacity (rows per unit).  Layouts:
+ *   codes  uint8 [units][capacity][row_stride], little-endian bit stream per row,
+ *          slot j's code at bit offset (slot_bits & 0xFFFFFF), LSB first
+ *   params fp16  [units][capacity][n_qgroups][2] = (min, scale)   (mixed only) */
+int32_t kvtc_store_bytes(const void *state_host, int64_t capacity,
+                         size_t *codes_bytes, size_t *params_bytes);
+
+/* Append rows [s0, s0 + n) of every unit (device).
+ * KVTC page "Design", decode step 1: project through the frozen basis,
+ * quantise at the frozen widths, grow the latent store.  PALU page "Design",
+ * decode steps 1-2 for mixed mode.
+ *   state_host/state_dev  the same blob in host and device memory
+ *   x_dev      [B, H, n, D] rows of dtype KVTC_F16 or KVTC_F32; x_strides are in
+ *              elements for (b, h, s, d) and x_strides[3] must be 1
+ *   codes_dev  code store (layout above), params_dev the mixed-mode store (NULL in DP)
+ * Codes are computed from float64 latents, so a row's codes depend only on
+ * that row: appending one token at a time or all at once stores the same bytes.
+ * Needs s0 >= 0, n >= 0, s0 + n <= capacity. */
+int32_t kvtc_append(const void *state_host, const void *state_dev,
+                    const void *x_dev, int32_t dtype, const int64_t x_strides[4],
+                    int64_t B, int64_t H, int64_t n, int64_t s0,
+                    void *codes_dev, void *params_dev, int64_t capacity, void *hip_stream);
+
+/* Reconstruct rows [s_begin, s_end) of every unit to fp16 (device).
+ * KVTC page "Design": every call returns reconstructed fp16 [B, H, S_total, D];
+ * PALU page: latent -> dequant -> reconstruct on every fetch.
+ *   out_dev    fp16 [B, H, s_end - s_begin, D] with element strides out_strides
+ *              (out_strides[3] must be 1, rows 16-byte aligned); row s of the
+ *              store goes to out index s - s_begin.
+ * Needs 0 <= s_begin <= s_end <= capacity. */
+int32_t kvtc_fetch(const void *state_host, const void *state_dev,
+                   const void *codes_dev, const void *params_dev, int64_t capacity,
+                   int64_t s_begin, int64_t s_end,
+                   void *out_dev, const int64_t out_strides[4], void *hip_stream);
+
+/* Storage accounting of one tensor over its first S rows (host).
+ * KVTC page "Byte accounting" and the kvtc_bytes / pre_entropy_bytes
+ * properties: order-0 Huffman per kept DP component, kept only when payload +
+ * table is below fixed-width packing; basis and quantiser parameters counted
+ * at fp16.  PALU page "Byte accounting": mixed-bit latents + fp32 projection. */
+typedef struct kvtc_bytes_report {
+    uint64_t fixed_payload;       /* sum over units of ceil(S * row_bits / 8) */
+    uint64_t entropy_payload;     /* Huffman payload of entropy-coded units */
+    uint64_t entropy_table;       /* one byte per symbol of each coded component */
+    uint64_t stored_payload;      /* payload counted in total (coded or fixed) */
+    uint64_t basis;               /* DP: fp16 basis + mean; mixed: fp32 projection + mean */
+    uint64_t quant_params;        /* DP: fp16 (min, scale) per component; mixed: per token-group */
+    uint64_t total;               /* stored_payload + entropy_table + basis + quant_params */
+    uint64_t pre_entropy;         /* fixed_payload + basis + quant_params */
+    uint64_t fp16_equiv;          /* B * H * S * D * 2 */
+    uint64_t device_store;        /* units * S * row_stride (+ params) actually held on device */
+    int64_t  n_survived;          /* kept non-zero-width components over units */
+    int64_t  units_entropy_coded;
+} kvtc_bytes_report;
+
+/*   codes_host   [units][capacity][row_stride] copy of the device store
+ *   params_host  mixed-mode parameter store copy (NULL in DP mode) */
+int32_t kvtc_bytes(const void *state_host, const void *codes_host, const void *params_host,
+                   int64_t capacity, int64_t S, kvtc_bytes_report *out);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* KVTC_H */

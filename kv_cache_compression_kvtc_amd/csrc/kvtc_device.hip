@@ -1,0 +1,660 @@
+// Device half of libkvtc for gfx950 (CDNA4): the fused append and fetch
+// kernels and their C-ABI launchers.
+//
+// Append (KVTC cache module page, module docstring "Design", decode step 1;
+// PALU cache API page, "Design", decode steps 1-2): every row is centred,
+// projected through the frozen basis of its unit, each stored component is
+// quantised at its frozen width and the codes are OR-ed into a little-endian
+// bit row in LDS, which is then written to the store with coalesced stores.
+// The projection runs on fp64 MFMA so that codes are decided from latents
+// accurate to ~1e-16, i.e. identical to a float64 evaluation except when a
+// value lies within rounding distance of a quantisation boundary.
+//
+// Fetch (same pages: every call returns the whole sequence reconstructed to
+// fp16): code rows stream from HBM into LDS, each lane extracts its fields,
+// forms the fp16 contraction operand and the [tokens x slots] x [slots x d]
+// product runs on fp16 MFMA with fp32 accumulation; a bias is added, the
+// result is rounded to fp16 and transposed through LDS into fully coalesced
+// 16-byte non-temporal stores.
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cstdint>
+
+#include "kvtc.h"
+#include "kvtc_internal.h"
+
+namespace kvtc {
+namespace {
+
+typedef _Float16 half8 __attribute__((ext_vector_type(8)));
+typedef _Float16 half4 __attribute__((ext_vector_type(4)));
+typedef float floatx16 __attribute__((ext_vector_type(16)));
+typedef double doublex4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+constexpr int kThreads = 256;        // 4 waves of 64
+constexpr int kAppTok = 64;          // tokens per append block (16 per wave)
+constexpr int kAppKC = 16;           // feature columns staged per append step
+constexpr int kAppPad = kAppKC + 1;  // LDS row pitch (elements) of the staged chunks
+constexpr int kFetTok = 32;          // tokens per fetch tile (one wave)
+constexpr int kFetchRegWords = 24;   // per-lane register staging of one tile's rows+params
+constexpr int kMaxSlots = 256;
+constexpr int kMaxRowStride = 256;
+
+// ------------------------------------------------------------ small helpers
+// Nearest-even binary16 of a double from its value: the binade is read from
+// the exponent bits, power-of-two scalings are exact and rint rounds half to even.
+__device__ inline uint16_t half_bits_rne(double x) {
+    const uint64_t bits = __double_as_longlong(x);
+    const uint16_t sign = static_cast<uint16_t>((bits >> 48) & 0x8000u);
+    const uint64_t mag = bits & 0x7FFFFFFFFFFFFFFFull;
+    if (mag > 0x7FF0000000000000ull) return sign | 0x7E00u;
+    const double a = __longlong_as_double(mag);
+    if (a >= 65520.0) return sign | 0x7C00u;
+    if (a < 6.103515625e-05) return sign | static_cast<uint16_t>(__builtin_rint(a * 16777216.0));
+    int ex = static_cast<int>(mag >> 52) - 1023;
+    double q = __builtin_rint(__builtin_amdgcn_ldexp(a, 10 - ex));
+    if (q == 2048.0) {
+        q = 1024.0;
+        ++ex;
+    }
+    if (ex + 15 >= 31) return sign | 0x7C00u;
+    return sign | static_cast<uint16_t>(((ex + 15) << 10) | (static_cast<int>(q) - 1024));
+}
+
+__device__ inline double half_bits_to_double(uint16_t h) {
+    return static_cast<double>(__builtin_bit_cast(_Float16, h));
+}
+
+// ORs a width-w code into an LSB-first bit row held as 32-bit words in LDS.
+__device__ inline void or_field(uint32_t *row, uint32_t off, uint32_t w, uint32_t c) {
+    const uint32_t wi = off >> 5, sh = off & 31u;
+    atomicOr(&row[wi], c << sh);
+    if (sh + w > 32u) atomicOr(&row[wi + 1], c >> (32u - sh));
+}
+
+__device__ inline double quantise(double l, double lo, double inv, double cmax) {
+    double q = __builtin_rint((l - lo) * inv);
+    if (q != q) q = 0.0;
+    return fmin(fmax(q, 0.0), cmax);
+}
+
+template <typename XT>
+__device__ inline double load_x(const XT *p) {
+    return static_cast<double>(*p);
+}
+
+// ================================================================ append
+struct AppendArgs {
+    const void *x;
+    int64_t xsb, xsh, xss;             // element strides of x (d stride is 1)
+    int64_t n, s0, capacity;
+    const kvtc_unit_info *ui;
+    const float *mu;                   // [U][dg]
+    const float *basis;                // [U][kslots][dg]
+    const double *qlo, *qinv;          // [U][kslots]
+    const uint32_t *sbits;             // [U][kslots]
+    uint8_t *codes;                    // [U][capacity][row_stride]
+    uint32_t *params;                  // [U][capacity][n_qg] packed (min16 | scale16 << 16)
+    int dg, D, hpu, groups, kslots, row_stride, n_qg, gs;
+};
+
+// One block: 64 tokens of one unit, all of its stored components.
+// Wave w owns tokens 16w..16w+15; N-block nb covers slots 16nb..16nb+15.
+template <bool MIXED, typename XT, int NB>
+__global__ __launch_bounds__(kThreads) void append_kernel(AppendArgs a) {
+    extern __shared__ __align__(16) unsigned char smem[];
+    double *xs = reinterpret_cast<double *>(smem);                         // [2][64][kAppPad]
+    float *vs = reinterpret_cast<float *>(xs + 2 * kAppTok * kAppPad);     // [2][NB*16][kAppPad]
+    uint32_t *rows = reinterpret_cast<uint32_t *>(vs + 2 * NB * 16 * kAppPad);  // [64][row_words]
+
+    const int u = blockIdx.y;
+    const int64_t t0 = static_cast<int64_t>(blockIdx.x) * kAppTok;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int b = u / a.groups, g = u % a.groups;
+    const int nvalid = static_cast<int>(min<int64_t>(kAppTok, a.n - t0));
+    const int n_slots = a.ui[u].n_slots;
+    const int row_words = a.row_stride >> 2;
+    const XT *x = static_cast<const XT *>(a.x);
+
+    for (int w = tid; w < kAppTok * row_words; w += kThreads) rows[w] = 0u;
+
+    // staging map: thread -> (token, 4 consecutive columns) of a 64 x 16 chunk,
+    // and (slot, 4 columns) of the NB*16 x 16 basis chunk
+    const int st_tok = tid >> 2, st_col = (tid & 3) * 4;
+    constexpr int kVReps = (NB * 16 + 63) / 64;
+    double xr[4];
+    float vr[kVReps][4];
+
+    auto load_chunk = [&](int kc) {
+        const int gd = kc * kAppKC + st_col;          // column within the unit's row
+        const int j = gd / a.D, dd = gd - j * a.D;
+        const int h = g * a.hpu + j;
+        const float *mu = a.mu + static_cast<int64_t>(u) * a.dg + gd;
+        if (st_tok < nvalid) {
+            const XT *p = x + b * a.xsb + h * a.xsh + (t0 + st_tok) * a.xss + dd;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) xr[i] = load_x(p + i) - static_cast<double>(mu[i]);
+        } else {
+#pragma unroll
+            for (int i = 0; i < 4; ++i) xr[i] = 0.0;
+        }
+#pragma unroll
+        for (int rep = 0; rep < kVReps; ++rep) {
+            const int slot = rep * 64 + st_tok;
+            if (slot < NB * 16 && slot < a.kslots) {
+                const float *p = a.basis + (static_cast<int64_t>(u) * a.kslots + slot) * a.dg + gd;
+#pragma unroll
+                for (int i = 0; i < 4; ++i) vr[rep][i] = p[i];
+            } else {
+#pragma unroll
+                for (int i = 0; i < 4; ++i) vr[rep][i] = 0.0f;
+            }
+        }
+    };
+    auto store_chunk = [&](int buf) {
+        double *xb = xs + buf * kAppTok * kAppPad + st_tok * kAppPad + st_col;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) xb[i] = xr[i];
+#pragma unroll
+        for (int rep = 0; rep < kVReps; ++rep) {
+            const int slot = rep * 64 + st_tok;
+            if (slot < NB * 16) {
+                float *vb = vs + (buf * NB * 16 + slot) * kAppPad + st_col;
+#pragma unroll
+                for (int i = 0; i < 4; ++i) vb[i] = vr[rep][i];
+            }
+        }
+    };
+
+    doublex4 acc[NB];
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) acc[nb] = doublex4{0.0, 0.0, 0.0, 0.0};
+
+    const int nchunks = a.dg / kAppKC;
+    load_chunk(0);
+    store_chunk(0);
+    __syncthreads();
+    const int mrow = wave * 16 + (lane & 15);   // A operand row (token) of this lane
+    const int kcol = lane >> 4;                 // A/B operand k of this lane
+    for (int kc = 0; kc < nchunks; ++kc) {
+        const int buf = kc & 1;
+        if (kc + 1 < nchunks) load_chunk(kc + 1);
+        const double *xb = xs + buf * kAppTok * kAppPad;
+        const float *vb = vs + buf * NB * 16 * kAppPad;
+#pragma unroll
+        for (int ks = 0; ks < kAppKC / 4; ++ks) {
+            const double av = xb[mrow * kAppPad + ks * 4 + kcol];
+#pragma unroll
+            for (int nb = 0; nb < NB; ++nb) {
+                const double bv = static_cast<double>(vb[(nb * 16 + (lane & 15)) * kAppPad + ks * 4 + kcol]);
+                acc[nb] = __builtin_amdgcn_mfma_f64_16x16x4f64(av, bv, acc[nb], 0, 0, 0);
+            }
+        }
+        if (kc + 1 < nchunks) store_chunk(buf ^ 1);
+        __syncthreads();
+    }
+
+    // acc[nb][i] is the latent of token 16*wave + 4*(lane>>4) + i, slot 16*nb + (lane&15)
+    const int tbase = wave * 16 + 4 * (lane >> 4);
+    const int64_t ub = static_cast<int64_t>(u) * a.kslots;
+    if constexpr (!MIXED) {
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb) {
+            const int j = nb * 16 + (lane & 15);
+            if (j < n_slots) {
+                const double lo = a.qlo[ub + j], inv = a.qinv[ub + j];
+                const uint32_t sb = a.sbits[ub + j];
+                const uint32_t off = sb & kOffsetMask, w = sb >> 24;
+                const double cmax = static_cast<double>((1u << w) - 1u);
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const int t = tbase + i;
+                    if (t < nvalid) {
+                        const uint32_t c = static_cast<uint32_t>(quantise(acc[nb][i], lo, inv, cmax));
+                        or_field(rows + t * row_words, off, w, c);
+                    }
+                }
+            }
+        }
+    } else {
+        const int ngroups = (n_slots + a.gs - 1) / a.gs;
+        for (int gi = 0; gi < ngroups; ++gi) {
+            const int j0 = gi * a.gs, j1 = min(n_slots, j0 + a.gs);
+            const uint32_t w = a.sbits[ub + j0] >> 24;
+            const double cmax = static_cast<double>((1u << w) - 1u);
+            double mn[4], mx[4];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                mn[i] = __builtin_huge_val();
+                mx[i] = -__builtin_huge_val();
+            }
+#pragma unroll
+            for (int nb = 0; nb < NB; ++nb) {
+                const int j = nb * 16 + (lane & 15);
+                if (j >= j0 && j < j1) {
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        mn[i] = fmin(mn[i], acc[nb][i]);
+                        mx[i] = fmax(mx[i], acc[nb][i]);
+                    }
+                }
+            }
+#pragma unroll
+            for (int m = 1; m < 16; m <<= 1) {
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    mn[i] = fmin(mn[i], __shfl_xor(mn[i], m, 16));
+                    mx[i] = fmax(mx[i], __shfl_xor(mx[i], m, 16));
+                }
+            }
+            double lo16[4], inv16[4];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const uint16_t hmin = half_bits_rne(mn[i]);
+                const uint16_t hscale = half_bits_rne((mx[i] - mn[i]) / cmax);
+                lo16[i] = half_bits_to_double(hmin);
+                const double sc = half_bits_to_double(hscale);
+                inv16[i] = sc > 0.0 ? 1.0 / sc : 0.0;
+                const int t = tbase + i;
+                if ((lane & 15) == 0 && t < nvalid)
+                    a.params[(static_cast<int64_t>(u) * a.capacity + a.s0 + t0 + t) * a.n_qg + gi] =
+                        static_cast<uint32_t>(hmin) | (static_cast<uint32_t>(hscale) << 16);
+            }
+#pragma unroll
+            for (int nb = 0; nb < NB; ++nb) {
+                const int j = nb * 16 + (lane & 15);
+                if (j >= j0 && j < j1) {
+                    const uint32_t off = a.sbits[ub + j] & kOffsetMask;
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        const int t = tbase + i;
+                        if (t < nvalid) {
+                            const uint32_t c = static_cast<uint32_t>(quantise(acc[nb][i], lo16[i], inv16[i], cmax));
+                            or_field(rows + t * row_words, off, w, c);
+                        }
+                    }
+                }
+            }
+        }
+    }
+    __syncthreads();
+    if (row_words > 0) {
+        uint32_t *dst = reinterpret_cast<uint32_t *>(
+            a.codes + (static_cast<int64_t>(u) * a.capacity + a.s0 + t0) * a.row_stride);
+        for (int w = tid; w < nvalid * row_words; w += kThreads) dst[w] = rows[w];
+    }
+}
+
+// ================================================================ fetch
+struct FetchArgs {
+    const uint8_t *codes;              // [U][capacity][row_stride]
+    const uint32_t *params;            // [U][capacity][n_qg] (min16 | scale16 << 16)
+    int64_t capacity, s_begin, s_end;
+    const uint16_t *w16;               // [U][dg][kslots]
+    const float *bias;                 // [U][dg]
+    const uint32_t *sbits;             // [U][kslots]
+    _Float16 *out;
+    int64_t osb, osh, oss;             // element strides of out (d stride is 1)
+    int dg, D, hpu, groups, kslots, row_stride, n_qg, gs;
+    int nslices, nchunks, tiles_per_block, ntiles;
+    int64_t nblocks_real, nblocks_per_xcd;
+    // dynamic LDS carve-up (bytes)
+    int lds_w, lds_kmap, lds_bias, lds_wave, lds_rows, lds_par, lds_out, wpitch, opitch;
+};
+
+// One block: one (unit, d-slice of 32*NDB columns), a run of 32-token tiles;
+// each wave reconstructs whole tiles.  MFMA operands: A = W rows (d), B =
+// per-token code values (slots), C[d][token] accumulates in fp32.
+template <bool MIXED, int NDB>
+__global__ __launch_bounds__(kThreads) void fetch_kernel(FetchArgs a) {
+    extern __shared__ __align__(16) unsigned char smem[];
+    constexpr int DS = 32 * NDB;
+    // blocks are dealt to the 8 XCDs round-robin; regroup them so that the
+    // blocks of one unit (and its d-slices) run on the same XCD
+    const int64_t bid = blockIdx.x;
+    const int64_t logical = (bid & 7) * a.nblocks_per_xcd + (bid >> 3);
+    if (logical >= a.nblocks_real) return;
+    const int slice = static_cast<int>(logical % a.nslices);
+    const int64_t rest = logical / a.nslices;
+    const int chunk = static_cast<int>(rest % a.nchunks);
+    const int u = static_cast<int>(rest / a.nchunks);
+    const int b = u / a.groups, g = u % a.groups;
+    const int d0 = slice * DS;
+    const int head = g * a.hpu + d0 / a.D, dd0 = d0 % a.D;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int row_words = a.row_stride >> 2;
+    const int rw1 = row_words + 1;
+
+    _Float16 *wl = reinterpret_cast<_Float16 *>(smem + a.lds_w);       // [DS][wpitch]
+    uint32_t *kmap = reinterpret_cast<uint32_t *>(smem + a.lds_kmap);   // [kslots]
+    float *biasl = reinterpret_cast<float *>(smem + a.lds_bias);        // [DS]
+    unsigned char *wbase = smem + a.lds_wave + wave * a.lds_rows;
+    uint32_t *rowsl = reinterpret_cast<uint32_t *>(wbase);              // [32][rw1]
+    uint32_t *parl = reinterpret_cast<uint32_t *>(wbase + a.lds_par);   // [32][n_qg]
+    _Float16 *outl = reinterpret_cast<_Float16 *>(wbase + a.lds_out);   // [32][opitch]
+
+    // stage this slice of W, the slot map and the bias
+    {
+        const uint16_t *src = a.w16 + (static_cast<int64_t>(u) * a.dg + d0) * a.kslots;
+        const int vec_per_row = a.kslots / 8;
+        for (int i = tid; i < DS * vec_per_row; i += kThreads) {
+            const int r = i / vec_per_row, c = i - r * vec_per_row;
+            const u32x4 v = *reinterpret_cast<const u32x4 *>(src + r * a.kslots + c * 8);
+            *reinterpret_cast<u32x4 *>(wl + r * a.wpitch + c * 8) = v;
+        }
+        for (int i = tid; i < a.kslots; i += kThreads) kmap[i] = a.sbits[static_cast<int64_t>(u) * a.kslots + i];
+        for (int i = tid; i < DS; i += kThreads) biasl[i] = a.bias[static_cast<int64_t>(u) * a.dg + d0 + i];
+    }
+    __syncthreads();
+
+    const int tile_begin = chunk * a.tiles_per_block;
+    const int tile_end = min(a.ntiles, tile_begin + a.tiles_per_block);
+    const int tw = row_words + (MIXED ? a.n_qg : 0);      // words per token
+    const int tile_words = kFetTok * tw;
+    const int64_t ubase = static_cast<int64_t>(u) * a.capacity;
+    const uint32_t *codes32 = reinterpret_cast<const uint32_t *>(a.codes);
+
+    uint32_t reg[kFetchRegWords];
+    // rows (then params) of one tile into registers; word i of the tile is
+    // token i / row_words (params: token i / n_qg), zero-filled past the end
+    auto fetch_tile = [&](int tile) {
+        const int64_t s = a.s_begin + static_cast<int64_t>(tile) * kFetTok;
+        const int valid = static_cast<int>(min<int64_t>(kFetTok, a.s_end - s));
+        const uint32_t *src = codes32 + (ubase + s) * row_words;
+        const uint32_t *psrc = MIXED ? a.params + (ubase + s) * a.n_qg : nullptr;
+#pragma unroll
+        for (int k = 0; k < kFetchRegWords; ++k) {
+            const int i = k * 64 + lane;
+            uint32_t v = 0u;
+            if (i < tile_words) {
+                if (i < kFetTok * row_words) {
+                    if (i < valid * row_words) v = src[i];
+                } else if (MIXED) {
+                    const int pi = i - kFetTok * row_words;
+                    if (pi < valid * a.n_qg) v = psrc[pi];
+                }
+            }
+            reg[k] = v;
+        }
+    };
+    auto stash_tile = [&]() {
+#pragma unroll
+        for (int k = 0; k < kFetchRegWords; ++k) {
+            const int i = k * 64 + lane;
+            if (i < tile_words) {
+                if (i < kFetTok * row_words) {
+                    const int t = i / row_words;
+                    rowsl[t * rw1 + (i - t * row_words)] = reg[k];
+                } else if (MIXED) {
+                    parl[i - kFetTok * row_words] = reg[k];
+                }
+            }
+        }
+    };
+
+    const int tok = lane & 31;            // B-operand column / C column of this lane
+    const int khalf = (lane >> 5) * 8;    // first of the 8 slots this lane feeds per step
+    const int ksteps = a.kslots / 16;
+
+    int tile = tile_begin + wave;
+    if (tile < tile_end) fetch_tile(tile);
+    for (; tile < tile_end; tile += 4) {
+        stash_tile();
+        const int64_t s = a.s_begin + static_cast<int64_t>(tile) * kFetTok;
+        const int valid = static_cast<int>(min<int64_t>(kFetTok, a.s_end - s));
+        if (tile + 4 < tile_end) fetch_tile(tile + 4);
+        __builtin_amdgcn_wave_barrier();
+
+        floatx16 acc[NDB];
+#pragma unroll
+        for (int db = 0; db < NDB; ++db)
+#pragma unroll
+            for (int i = 0; i < 16; ++i) acc[db][i] = 0.0f;
+
+        const uint32_t *myrow = rowsl + tok * rw1;
+        for (int ks = 0; ks < ksteps; ++ks) {
+            half8 bv;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                const int slot = ks * 16 + khalf + e;
+                const uint32_t km = kmap[slot];
+                const uint32_t off = km & kOffsetMask, w = km >> 24;
+                const uint32_t wi = off >> 5;
+                const uint32_t v = __builtin_amdgcn_alignbit(myrow[wi + 1], myrow[wi], off & 31u);
+                const uint32_t c = v & ((1u << w) - 1u);
+                if constexpr (MIXED) {
+                    const uint32_t p = parl[tok * a.n_qg + slot / a.gs];
+                    const float mn = static_cast<float>(__builtin_bit_cast(_Float16, static_cast<uint16_t>(p & 0xFFFFu)));
+                    const float sc = static_cast<float>(__builtin_bit_cast(_Float16, static_cast<uint16_t>(p >> 16)));
+                    bv[e] = static_cast<_Float16>(__builtin_fmaf(static_cast<float>(c), sc, mn));
+                } else {
+                    bv[e] = static_cast<_Float16>(static_cast<float>(c));
+                }
+            }
+#pragma unroll
+            for (int db = 0; db < NDB; ++db) {
+                const half8 av = *reinterpret_cast<const half8 *>(wl + (db * 32 + tok) * a.wpitch + ks * 16 + khalf);
+                acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_f16(av, bv, acc[db], 0, 0, 0);
+            }
+        }
+        // C[d][token]: lane holds token (lane & 31), d = 32db + 8q + 4(lane>>5) + e
+#pragma unroll
+        for (int db = 0; db < NDB; ++db) {
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const int dl = db * 32 + q * 8 + (lane >> 5) * 4;
+                half4 hv;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) hv[e] = static_cast<_Float16>(acc[db][q * 4 + e] + biasl[dl + e]);
+                *reinterpret_cast<half4 *>(outl + tok * a.opitch + dl) = hv;
+            }
+        }
+        __builtin_amdgcn_wave_barrier();
+        constexpr int kChunksPerRow = DS / 8;
+        _Float16 *obase = a.out + b * a.osb + head * a.osh + dd0;
+#pragma unroll
+        for (int it = 0; it < kFetTok * kChunksPerRow / 64; ++it) {
+            const int idx = it * 64 + lane;
+            const int t = idx / kChunksPerRow, c = idx - t * kChunksPerRow;
+            if (t < valid) {
+                const u32x4 v = *reinterpret_cast<const u32x4 *>(outl + t * a.opitch + c * 8);
+                u32x4 *dst = reinterpret_cast<u32x4 *>(obase + (s + t - a.s_begin) * a.oss + c * 8);
+                __builtin_nontemporal_store(v, dst);
+            }
+        }
+        __builtin_amdgcn_wave_barrier();
+    }
+}
+
+// ============================================================== launchers
+int append_nb(int kslots) {
+    const int need = kslots / 16;
+    const int opts[] = {1, 2, 4, 6, 8, 12, 16};
+    for (int o : opts)
+        if (o >= need) return o;
+    return -1;
+}
+
+template <bool MIXED, typename XT, int NB>
+int32_t launch_append_nb(const AppendArgs &a, int64_t ntiles, int64_t U, hipStream_t stream) {
+    const size_t lds = 2 * kAppTok * kAppPad * sizeof(double) + 2 * NB * 16 * kAppPad * sizeof(float) +
+                       static_cast<size_t>(kAppTok) * (a.row_stride / 4) * sizeof(uint32_t);
+    auto kern = append_kernel<MIXED, XT, NB>;
+    if (hipFuncSetAttribute(reinterpret_cast<const void *>(kern), hipFuncAttributeMaxDynamicSharedMemorySize,
+                            static_cast<int>(lds)) != hipSuccess)
+        return KVTC_E_DEVICE;
+    hipLaunchKernelGGL(kern, dim3(static_cast<unsigned>(ntiles), static_cast<unsigned>(U)), dim3(kThreads), lds,
+                       stream, a);
+    return hipGetLastError() == hipSuccess ? KVTC_OK : KVTC_E_DEVICE;
+}
+
+template <bool MIXED, typename XT>
+int32_t launch_append(const AppendArgs &a, int64_t ntiles, int64_t U, int nb, hipStream_t st) {
+    switch (nb) {
+        case 1: return launch_append_nb<MIXED, XT, 1>(a, ntiles, U, st);
+        case 2: return launch_append_nb<MIXED, XT, 2>(a, ntiles, U, st);
+        case 4: return launch_append_nb<MIXED, XT, 4>(a, ntiles, U, st);
+        case 6: return launch_append_nb<MIXED, XT, 6>(a, ntiles, U, st);
+        case 8: return launch_append_nb<MIXED, XT, 8>(a, ntiles, U, st);
+        case 12: return launch_append_nb<MIXED, XT, 12>(a, ntiles, U, st);
+        case 16: return launch_append_nb<MIXED, XT, 16>(a, ntiles, U, st);
+        default: return KVTC_E_SHAPE;
+    }
+}
+
+template <bool MIXED, int NDB>
+int32_t launch_fetch(FetchArgs a, hipStream_t stream) {
+    constexpr int DS = 32 * NDB;
+    a.wpitch = a.kslots + 8;
+    a.opitch = DS + 8;
+    a.lds_w = 0;
+    a.lds_kmap = static_cast<int>(align_up(static_cast<uint64_t>(DS) * a.wpitch * 2, 16));
+    a.lds_bias = static_cast<int>(align_up(a.lds_kmap + a.kslots * 4, 16));
+    a.lds_wave = static_cast<int>(align_up(a.lds_bias + DS * 4, 16));
+    const int rows_b = static_cast<int>(align_up(kFetTok * (a.row_stride / 4 + 1) * 4, 16));
+    const int par_b = MIXED ? static_cast<int>(align_up(kFetTok * a.n_qg * 4, 16)) : 0;
+    const int out_b = static_cast<int>(align_up(kFetTok * a.opitch * 2, 16));
+    a.lds_par = rows_b;
+    a.lds_out = rows_b + par_b;
+    a.lds_rows = rows_b + par_b + out_b;                 // per-wave bytes
+    const size_t lds = a.lds_wave + 4 * static_cast<size_t>(a.lds_rows);
+    if (lds > 160 * 1024) return KVTC_E_SHAPE;
+    const int64_t grid = a.nblocks_per_xcd * 8;
+    auto kern = fetch_kernel<MIXED, NDB>;
+    if (hipFuncSetAttribute(reinterpret_cast<const void *>(kern), hipFuncAttributeMaxDynamicSharedMemorySize,
+                            static_cast<int>(lds)) != hipSuccess)
+        return KVTC_E_DEVICE;
+    hipLaunchKernelGGL(kern, dim3(static_cast<unsigned>(grid)), dim3(kThreads), lds, stream, a);
+    return hipGetLastError() == hipSuccess ? KVTC_OK : KVTC_E_DEVICE;
+}
+
+}  // namespace
+}  // namespace kvtc
+
+using namespace kvtc;
+
+extern "C" {
+
+int32_t kvtc_append(const void *state_host, const void *state_dev, const void *x_dev, int32_t dtype,
+                    const int64_t x_strides[4], int64_t B, int64_t H, int64_t n, int64_t s0,
+                    void *codes_dev, void *params_dev, int64_t capacity, void *hip_stream) {
+    const kvtc_state_header *h = nullptr;
+    int32_t st = check_state(state_host, &h);
+    if (st != KVTC_OK) return st;
+    if (!state_dev || !x_strides) return KVTC_E_ARG;
+    if (dtype != KVTC_F16 && dtype != KVTC_F32) return KVTC_E_DTYPE;
+    if (B != h->batch || H != h->heads) return KVTC_E_SHAPE;
+    if (x_strides[3] != 1 || x_strides[0] < 0 || x_strides[1] < 0 || x_strides[2] < 0) return KVTC_E_SHAPE;
+    if (n < 0 || s0 < 0 || capacity < 0) return KVTC_E_ARG;
+    if (s0 + n > capacity) return KVTC_E_CAPACITY;
+    if (h->kslots > kMaxSlots || h->row_stride > kMaxRowStride || h->dg % kAppKC != 0 ||
+        h->head_dim % kAppKC != 0 || h->units > 65535)
+        return KVTC_E_SHAPE;
+    const bool mixed = h->mode == KVTC_MODE_MIXED;
+    if (mixed && h->group_size % 16 != 0) return KVTC_E_STATE;
+    if (n == 0) return KVTC_OK;
+    if (!x_dev) return KVTC_E_ARG;
+    if (h->row_stride > 0 && (!codes_dev || reinterpret_cast<uintptr_t>(codes_dev) % 4 != 0)) return KVTC_E_ARG;
+    if (mixed && (!params_dev || reinterpret_cast<uintptr_t>(params_dev) % 4 != 0)) return KVTC_E_ARG;
+    const int nb = append_nb(h->kslots);
+    if (nb < 0) return KVTC_E_SHAPE;
+
+    const char *sd = static_cast<const char *>(state_dev);
+    AppendArgs a{};
+    a.x = x_dev;
+    a.xsb = x_strides[0];
+    a.xsh = x_strides[1];
+    a.xss = x_strides[2];
+    a.n = n;
+    a.s0 = s0;
+    a.capacity = capacity;
+    a.ui = reinterpret_cast<const kvtc_unit_info *>(sd + h->off_unit);
+    a.mu = reinterpret_cast<const float *>(sd + h->off_mu);
+    a.basis = reinterpret_cast<const float *>(sd + h->off_basis);
+    a.qlo = reinterpret_cast<const double *>(sd + h->off_qlo);
+    a.qinv = reinterpret_cast<const double *>(sd + h->off_qinv);
+    a.sbits = reinterpret_cast<const uint32_t *>(sd + h->off_slot_bits);
+    a.codes = static_cast<uint8_t *>(codes_dev);
+    a.params = static_cast<uint32_t *>(params_dev);
+    a.dg = h->dg;
+    a.D = h->head_dim;
+    a.hpu = h->heads_per_unit;
+    a.groups = static_cast<int>(h->heads / h->heads_per_unit);
+    a.kslots = h->kslots;
+    a.row_stride = h->row_stride;
+    a.n_qg = h->n_qgroups;
+    a.gs = h->group_size;
+    const int64_t ntiles = (n + kAppTok - 1) / kAppTok;
+    if (ntiles > 0x7FFFFFFF) return KVTC_E_SHAPE;
+    hipStream_t stream = static_cast<hipStream_t>(hip_stream);
+    if (dtype == KVTC_F16)
+        return mixed ? launch_append<true, _Float16>(a, ntiles, h->units, nb, stream)
+                     : launch_append<false, _Float16>(a, ntiles, h->units, nb, stream);
+    return mixed ? launch_append<true, float>(a, ntiles, h->units, nb, stream)
+                 : launch_append<false, float>(a, ntiles, h->units, nb, stream);
+}
+
+int32_t kvtc_fetch(const void *state_host, const void *state_dev, const void *codes_dev,
+                   const void *params_dev, int64_t capacity, int64_t s_begin, int64_t s_end,
+                   void *out_dev, const int64_t out_strides[4], void *hip_stream) {
+    const kvtc_state_header *h = nullptr;
+    int32_t st = check_state(state_host, &h);
+    if (st != KVTC_OK) return st;
+    if (!state_dev || !out_strides) return KVTC_E_ARG;
+    if (capacity < 0 || s_begin < 0 || s_end < s_begin) return KVTC_E_ARG;
+    if (s_end > capacity) return KVTC_E_CAPACITY;
+    if (out_strides[3] != 1 || out_strides[0] < 0 || out_strides[1] < 0 || out_strides[2] < 0)
+        return KVTC_E_SHAPE;
+    const bool mixed = h->mode == KVTC_MODE_MIXED;
+    if (h->kslots > kMaxSlots || h->head_dim % 64 != 0) return KVTC_E_SHAPE;
+    const int tw = h->row_stride / 4 + (mixed ? h->n_qgroups : 0);
+    if (kFetTok * tw > 64 * kFetchRegWords) return KVTC_E_SHAPE;
+    if (s_end == s_begin) return KVTC_OK;
+    if (!out_dev || reinterpret_cast<uintptr_t>(out_dev) % 16 != 0) return KVTC_E_ARG;
+    if ((out_strides[0] * 2) % 16 || (out_strides[1] * 2) % 16 || (out_strides[2] * 2) % 16) return KVTC_E_SHAPE;
+    if (h->row_stride > 0 && (!codes_dev || reinterpret_cast<uintptr_t>(codes_dev) % 4 != 0)) return KVTC_E_ARG;
+    if (mixed && (!params_dev || reinterpret_cast<uintptr_t>(params_dev) % 4 != 0)) return KVTC_E_ARG;
+
+    const char *sd = static_cast<const char *>(state_dev);
+    FetchArgs a{};
+    a.codes = static_cast<const uint8_t *>(codes_dev);
+    a.params = static_cast<const uint32_t *>(params_dev);
+    a.capacity = capacity;
+    a.s_begin = s_begin;
+    a.s_end = s_end;
+    a.w16 = reinterpret_cast<const uint16_t *>(sd + h->off_w16);
+    a.bias = reinterpret_cast<const float *>(sd + h->off_bias);
+    a.sbits = reinterpret_cast<const uint32_t *>(sd + h->off_slot_bits);
+    a.out = static_cast<_Float16 *>(out_dev);
+    a.osb = out_strides[0];
+    a.osh = out_strides[1];
+    a.oss = out_strides[2];
+    a.dg = h->dg;
+    a.D = h->head_dim;
+    a.hpu = h->heads_per_unit;
+    a.groups = static_cast<int>(h->heads / h->heads_per_unit);
+    a.kslots = h->kslots;
+    a.row_stride = h->row_stride;
+    a.n_qg = h->n_qgroups;
+    a.gs = h->group_size;
+    const int DS = (h->head_dim % 128 == 0) ? 128 : 64;
+    a.nslices = h->dg / DS;
+    const int64_t ntiles = (s_end - s_begin + kFetTok - 1) / kFetTok;
+    if (ntiles > 0x7FFFFFFF) return KVTC_E_SHAPE;
+    a.ntiles = static_cast<int>(ntiles);
+    const int64_t work = h->units * a.nslices * ntiles;
+    int64_t tpb = std::max<int64_t>(4, (work + 2047) / 2048);
+    tpb = std::min<int64_t>(tpb, ntiles);
+    a.tiles_per_block = static_cast<int>(tpb);
+    a.nchunks = static_cast<int>((ntiles + tpb - 1) / tpb);
+    a.nblocks_real = h->units * a.nslices * a.nchunks;
+    a.nblocks_per_xcd = (a.nblocks_real + 7) / 8;
+    if (a.nblocks_per_xcd * 8 > 0x7FFFFFFF) return KVTC_E_SHAPE;
+    hipStream_t stream = static_cast<hipStream_t>(hip_stream);
+    if (DS == 128) return mixed ? launch_fetch<true, 4>(a, stream) : launch_fetch<false, 4>(a, stream);
+    return mixed ? launch_fetch<true, 2>(a, stream) : launch_fetch<false, 2>(a, stream);
+}
+
+}  // extern "C"

@@ -1,0 +1,941 @@
+// Host half of libkvtc: configuration, the once-per-prefill fit (mean,
+// covariance, symmetric eigensolver, rank, DP bit allocation, frozen ranges),
+// the state-blob builder and the storage accounting.
+//
+// The method is the one of the KVTC cache module page
+// (veloxquant_mlx.cache.kvtc_cache: module docstring "Design",
+// _TensorKVTC.fit_prefill_from_pca / _requantize, KVTCKVCache.update_and_fetch)
+// and, for the group-head mode, of the PALU cache API page
+// (veloxquant_mlx.cache.palu_cache, "Design" and the palu_* parameters).
+//
+// Built with -ffp-contract=off: the DP compares sums of doubles and must
+// evaluate them exactly in the order written.
+#include <algorithm>
+#include <atomic>
+#include <cmath>
+#include <cstdlib>
+#include <cstring>
+#include <functional>
+#include <limits>
+#include <new>
+#include <queue>
+#include <thread>
+#include <vector>
+
+#include "kvtc.h"
+#include "kvtc_internal.h"
+
+namespace kvtc {
+namespace {
+
+// ------------------------------------------------------------------ threads
+int num_threads() {
+    int t = static_cast<int>(std::thread::hardware_concurrency());
+    if (const char *e = std::getenv("KVTC_THREADS")) t = std::atoi(e);
+    else if (const char *o = std::getenv("OMP_NUM_THREADS")) t = std::min(t, std::atoi(o));
+    return std::max(1, std::min(t, 64));
+}
+
+// Runs fn(i) for i in [0, n) on up to num_threads() threads.  Returns false if
+// any call threw (the work of the others still completes).
+bool parallel_for(int64_t n, const std::function<void(int64_t)> &fn) {
+    std::atomic<int64_t> next{0};
+    std::atomic<bool> ok{true};
+    auto worker = [&] {
+        for (;;) {
+            int64_t i = next.fetch_add(1);
+            if (i >= n) break;
+            try {
+                fn(i);
+            } catch (...) {
+                ok = false;
+            }
+        }
+    };
+    int64_t T = std::min<int64_t>(num_threads(), n);
+    std::vector<std::thread> pool;
+    for (int64_t t = 1; t < T; ++t) pool.emplace_back(worker);
+    worker();
+    for (auto &th : pool) th.join();
+    return ok;
+}
+
+// ------------------------------------------------------------ fp16 rounding
+// Nearest-even binary16 of a double, computed from the value (power-of-two
+// scalings are exact, rint rounds half to even in the default mode).
+uint16_t half_bits_rne(double x) {
+    uint16_t sign = std::signbit(x) ? 0x8000u : 0u;
+    double a = std::fabs(x);
+    if (std::isnan(x)) return sign | 0x7E00u;
+    if (a >= 65520.0) return sign | 0x7C00u;             // past the last finite midpoint
+    if (a < 6.103515625e-05) {                            // below 2^-14: subnormal grid 2^-24
+        double q = std::rint(std::ldexp(a, 24));
+        return sign | static_cast<uint16_t>(q);           // q == 1024 is the smallest normal
+    }
+    int e;
+    std::frexp(a, &e);                                    // a = m * 2^e, m in [0.5, 1)
+    int ex = e - 1;                                       // a in [2^ex, 2^(ex+1))
+    double q = std::rint(std::ldexp(a, 10 - ex));         // in [1024, 2048]
+    if (q == 2048.0) {
+        q = 1024.0;
+        ++ex;
+    }
+    if (ex + 15 >= 31) return sign | 0x7C00u;
+    return sign | static_cast<uint16_t>(((ex + 15) << 10) | (static_cast<int>(q) - 1024));
+}
+
+// Exact value of a binary16 bit pattern.
+double half_value(uint16_t h) {
+    const int e = (h >> 10) & 31, m = h & 1023;
+    double v;
+    if (e == 0) v = std::ldexp(static_cast<double>(m), -24);
+    else if (e == 31) v = m ? std::numeric_limits<double>::quiet_NaN() : std::numeric_limits<double>::infinity();
+    else v = std::ldexp(static_cast<double>(1024 + m), e - 25);
+    return (h & 0x8000) ? -v : v;
+}
+
+// ---------------------------------------------------------- configuration
+bool width_allowed(int b) { return b == 0 || b == 1 || b == 2 || b == 3 || b == 4 || b == 8; }
+
+int32_t validate_config(const kvtc_config *c) {
+    if (!c) return KVTC_E_ARG;
+    if (c->mode != KVTC_MODE_DP && c->mode != KVTC_MODE_MIXED) return KVTC_E_CONFIG;
+    if (c->head_dim <= 0 || c->head_dim % 64 != 0 || c->head_dim > 4096) return KVTC_E_CONFIG;
+    if (c->heads_per_unit < 1) return KVTC_E_CONFIG;
+    const int dg = c->head_dim * c->heads_per_unit;
+    if (dg > 4096) return KVTC_E_CONFIG;
+    if (c->rank < 0 || c->rank > dg) return KVTC_E_CONFIG;
+    if (c->rank == 0 && !(c->energy_threshold > 0.0 && c->energy_threshold <= 1.0)) return KVTC_E_CONFIG;
+    if (c->mode == KVTC_MODE_DP) {
+        if (c->heads_per_unit != 1) return KVTC_E_CONFIG;
+        if (c->bit_budget < 0) return KVTC_E_CONFIG;      // KVTCKVCache raises on budget < 0
+        if (c->n_choices < 1 || c->n_choices > KVTC_MAX_CHOICES) return KVTC_E_CONFIG;
+        for (int i = 0; i < c->n_choices; ++i)
+            if (!width_allowed(c->choices[i])) return KVTC_E_CONFIG;
+        if (!(c->beta > 0.0) || !std::isfinite(c->beta)) return KVTC_E_CONFIG;
+    } else {
+        if (!width_allowed(c->hi_bits) || !width_allowed(c->lo_bits) || c->hi_bits == 0 ||
+            c->lo_bits == 0)
+            return KVTC_E_CONFIG;
+        if (c->group_size < 16 || c->group_size % 16 != 0) return KVTC_E_CONFIG;
+        if (!(c->hi_fraction >= 0.0 && c->hi_fraction <= 1.0)) return KVTC_E_CONFIG;
+    }
+    return KVTC_OK;
+}
+
+// ------------------------------------------------------------ allocation
+// Exact DP of the allocation (see kvtc_allocate_bits); returns false when no
+// allocation fits the budget.
+bool dp_allocate(const double *lam, int r, int budget, const std::vector<int> &choices_in,
+                 double beta, uint8_t *bits) {
+    std::vector<int> choices(choices_in);
+    std::sort(choices.begin(), choices.end());
+    choices.erase(std::unique(choices.begin(), choices.end()), choices.end());
+    const double inf = std::numeric_limits<double>::infinity();
+    const int C = budget + 1;
+    std::vector<double> best(C, inf), nxt(C);
+    std::vector<int8_t> pick(static_cast<size_t>(r) * C, -1);
+    best[0] = 0.0;
+    for (int i = 0; i < r; ++i) {
+        std::fill(nxt.begin(), nxt.end(), inf);
+        int8_t *arg = &pick[static_cast<size_t>(i) * C];
+        for (int b : choices) {
+            if (b > budget) continue;
+            // distortion proxy: dropped -> lambda, b bits -> beta * lambda * 4^-b
+            const double d = (b == 0) ? lam[i] : beta * lam[i] * std::ldexp(1.0, -2 * b);
+            for (int c = b; c < C; ++c) {
+                const double cand = best[c - b] + d;
+                if (cand < nxt[c]) {
+                    nxt[c] = cand;
+                    arg[c] = static_cast<int8_t>(b);
+                }
+            }
+        }
+        best.swap(nxt);
+    }
+    int c_end = -1;
+    double v_end = inf;
+    for (int c = 0; c < C; ++c)
+        if (best[c] < v_end) {
+            v_end = best[c];
+            c_end = c;
+        }
+    if (c_end < 0) return false;
+    int c = c_end;
+    for (int i = r - 1; i >= 0; --i) {
+        int b = pick[static_cast<size_t>(i) * C + c];
+        bits[i] = static_cast<uint8_t>(b);
+        c -= b;
+    }
+    return c == 0;
+}
+
+int mixed_n_hi(int r, double hi_fraction, int group_size) {
+    int n_hi = group_size * static_cast<int>(std::floor(hi_fraction * r / group_size + 0.5));
+    return std::min(std::max(n_hi, 0), r);
+}
+
+int energy_rank(const double *lam, int n, double tau) {
+    double total = 0.0;
+    for (int i = 0; i < n; ++i) total += lam[i];
+    if (total <= 0.0) return 1;
+    double acc = 0.0;
+    for (int k = 1; k <= n; ++k) {
+        acc += lam[k - 1];
+        if (acc >= tau * total) return k;
+    }
+    return n;
+}
+
+// ---------------------------------------------------------- eigensolver
+// Symmetric eigendecomposition of the n x n row-major matrix A (destroyed):
+// A = Q diag(w) Q^T.  Q^T is returned row-major in qt (row k = eigenvector of
+// w[k]).  Householder tridiagonalisation with accumulated reflectors, then
+// implicit symmetric QR steps with the Wilkinson shift on the tridiagonal
+// (Golub and Van Loan, Matrix Computations, sections 8.3.1-8.3.3).
+void sym_eig(std::vector<double> &A, int n, std::vector<double> &w, std::vector<double> &qt) {
+    qt.assign(static_cast<size_t>(n) * n, 0.0);
+    for (int i = 0; i < n; ++i) qt[static_cast<size_t>(i) * n + i] = 1.0;
+    std::vector<double> v(n), p(n), z(n);
+    auto a = [&](int i, int j) -> double & { return A[static_cast<size_t>(i) * n + j]; };
+    for (int k = 0; k + 2 < n; ++k) {
+        const int m = n - k - 1;                         // size of the trailing block
+        double sigma = 0.0;
+        for (int i = 0; i < m; ++i) sigma += a(k, k + 1 + i) * a(k, k + 1 + i);
+        sigma = std::sqrt(sigma);
+        if (sigma == 0.0) continue;
+        const double x0 = a(k, k + 1);
+        const double alpha = -std::copysign(sigma, x0);
+        for (int i = 0; i < m; ++i) v[i] = a(k, k + 1 + i);
+        v[0] -= alpha;
+        double vn = 0.0;
+        for (int i = 0; i < m; ++i) vn += v[i] * v[i];
+        vn = std::sqrt(vn);
+        if (vn == 0.0) continue;
+        for (int i = 0; i < m; ++i) v[i] /= vn;
+        // p = A_sub v, w = p - (v.p) v, A_sub -= 2 (v w^T + w v^T)
+        double K = 0.0;
+        for (int i = 0; i < m; ++i) {
+            const double *row = &A[static_cast<size_t>(k + 1 + i) * n + k + 1];
+            double s = 0.0;
+            for (int j = 0; j < m; ++j) s += row[j] * v[j];
+            p[i] = s;
+            K += v[i] * s;
+        }
+        for (int i = 0; i < m; ++i) p[i] -= K * v[i];
+        for (int i = 0; i < m; ++i) {
+            double *row = &A[static_cast<size_t>(k + 1 + i) * n + k + 1];
+            const double vi2 = 2.0 * v[i], pi2 = 2.0 * p[i];
+            for (int j = 0; j < m; ++j) row[j] -= vi2 * p[j] + pi2 * v[j];
+        }
+        a(k, k + 1) = alpha;
+        a(k + 1, k) = alpha;
+        for (int i = 1; i < m; ++i) {
+            a(k, k + 1 + i) = 0.0;
+            a(k + 1 + i, k) = 0.0;
+        }
+        // accumulate Q <- Q H: rows k+1.. of Q^T get -2 v_j (v^T Q^T[k+1:, :])
+        std::fill(z.begin(), z.end(), 0.0);
+        for (int i = 0; i < m; ++i) {
+            const double *row = &qt[static_cast<size_t>(k + 1 + i) * n];
+            for (int j = 0; j < n; ++j) z[j] += v[i] * row[j];
+        }
+        for (int i = 0; i < m; ++i) {
+            double *row = &qt[static_cast<size_t>(k + 1 + i) * n];
+            const double f = 2.0 * v[i];
+            for (int j = 0; j < n; ++j) row[j] -= f * z[j];
+        }
+    }
+    std::vector<double> d(n), e(std::max(n - 1, 1), 0.0);
+    double anorm = 0.0;
+    for (int i = 0; i < n; ++i) {
+        d[i] = a(i, i);
+        if (i + 1 < n) e[i] = a(i, i + 1);
+        anorm = std::max(anorm, std::fabs(d[i]) + (i + 1 < n ? std::fabs(e[i]) : 0.0) +
+                                    (i > 0 ? std::fabs(e[i - 1]) : 0.0));
+    }
+    const double eps = std::numeric_limits<double>::epsilon();
+    auto negligible = [&](int i) {
+        return std::fabs(e[i]) <= eps * (std::fabs(d[i]) + std::fabs(d[i + 1])) ||
+               std::fabs(e[i]) <= eps * eps * anorm;
+    };
+    int hi = n - 1;
+    long iter = 0;
+    const long max_iter = 64L * n + 64;
+    while (hi > 0 && iter < max_iter) {
+        if (negligible(hi - 1)) {
+            e[hi - 1] = 0.0;
+            --hi;
+            continue;
+        }
+        int lo = hi - 1;
+        while (lo > 0 && !negligible(lo - 1)) --lo;
+        if (lo > 0) e[lo - 1] = 0.0;
+        ++iter;
+        const double dd = 0.5 * (d[hi - 1] - d[hi]);
+        const double ee = e[hi - 1];
+        const double denom = dd + std::copysign(std::hypot(dd, ee), dd);
+        const double mu = d[hi] - ee * ee / denom;
+        double x = d[lo] - mu, zb = e[lo];
+        for (int k = lo; k < hi; ++k) {
+            const double r = std::hypot(x, zb);
+            const double c = (r == 0.0) ? 1.0 : x / r;
+            const double s = (r == 0.0) ? 0.0 : zb / r;
+            if (k > lo) e[k - 1] = r;
+            const double aa = d[k], f = e[k], g = d[k + 1];
+            d[k] = c * c * aa + 2.0 * c * s * f + s * s * g;
+            d[k + 1] = s * s * aa - 2.0 * c * s * f + c * c * g;
+            e[k] = (c * c - s * s) * f + c * s * (g - aa);
+            if (k + 1 < hi) {
+                const double bulge = s * e[k + 1];
+                e[k + 1] = c * e[k + 1];
+                x = e[k];
+                zb = bulge;
+            }
+            double *rk = &qt[static_cast<size_t>(k) * n];
+            double *rk1 = &qt[static_cast<size_t>(k + 1) * n];
+            for (int j = 0; j < n; ++j) {
+                const double q0 = rk[j], q1 = rk1[j];
+                rk[j] = c * q0 + s * q1;
+                rk1[j] = -s * q0 + c * q1;
+            }
+        }
+    }
+    w = d;
+}
+
+// ------------------------------------------------------------ unit fitting
+struct UnitFit {
+    std::vector<double> mean, lam;      // [dg]
+    std::vector<double> vecs;           // [dg][dg] row k = eigenvector k (descending order)
+    int rank = 0;
+};
+
+// Reads unit u's prefill rows as float64, [S][dg], heads of the unit concatenated.
+void load_unit_rows(const void *rows, int32_t dtype, int64_t B, int64_t H, int64_t S, int D, int hpu,
+                    int64_t u, std::vector<double> &Y) {
+    const int dg = D * hpu;
+    const int64_t G = H / hpu;
+    const int64_t b = u / G, g = u % G;
+    Y.resize(static_cast<size_t>(S) * dg);
+    for (int j = 0; j < hpu; ++j) {
+        const int64_t h = g * hpu + j;
+        const int64_t base = ((b * H + h) * S) * D;
+        for (int64_t s = 0; s < S; ++s) {
+            double *dst = &Y[static_cast<size_t>(s) * dg + static_cast<size_t>(j) * D];
+            if (dtype == KVTC_F32) {
+                const float *src = static_cast<const float *>(rows) + base + s * D;
+                for (int d = 0; d < D; ++d) dst[d] = src[d];
+            } else {
+                const uint16_t *src = static_cast<const uint16_t *>(rows) + base + s * D;
+                for (int d = 0; d < D; ++d) dst[d] = half_value(src[d]);
+            }
+        }
+    }
+}
+
+// Mean and 1/S covariance of Y ([S][dg]); Y is centred in place.  Blocks of
+// the upper triangle are accumulated with rank-4 updates.
+void mean_cov(std::vector<double> &Y, int64_t S, int dg, std::vector<double> &mean,
+              std::vector<double> &C, bool inner_parallel) {
+    mean.assign(dg, 0.0);
+    for (int64_t s = 0; s < S; ++s) {
+        const double *y = &Y[static_cast<size_t>(s) * dg];
+        for (int d = 0; d < dg; ++d) mean[d] += y[d];
+    }
+    for (int d = 0; d < dg; ++d) mean[d] /= static_cast<double>(S);
+    for (int64_t s = 0; s < S; ++s) {
+        double *y = &Y[static_cast<size_t>(s) * dg];
+        for (int d = 0; d < dg; ++d) y[d] -= mean[d];
+    }
+    C.assign(static_cast<size_t>(dg) * dg, 0.0);
+    constexpr int BS = 64;
+    const int nb = (dg + BS - 1) / BS;
+    std::vector<std::pair<int, int>> blocks;
+    for (int bi = 0; bi < nb; ++bi)
+        for (int bj = bi; bj < nb; ++bj) blocks.emplace_back(bi, bj);
+    auto do_block = [&](int64_t t) {
+        const int i0 = blocks[t].first * BS, j0 = blocks[t].second * BS;
+        const int ni = std::min(BS, dg - i0), nj = std::min(BS, dg - j0);
+        double acc[BS][BS] = {};
+        int64_t s = 0;
+        for (; s + 4 <= S; s += 4) {
+            const double *y0 = &Y[static_cast<size_t>(s) * dg];
+            const double *y1 = y0 + dg, *y2 = y1 + dg, *y3 = y2 + dg;
+            for (int i = 0; i < ni; ++i) {
+                const double a0 = y0[i0 + i], a1 = y1[i0 + i], a2 = y2[i0 + i], a3 = y3[i0 + i];
+                double *row = acc[i];
+                for (int j = 0; j < nj; ++j)
+                    row[j] += a0 * y0[j0 + j] + a1 * y1[j0 + j] + a2 * y2[j0 + j] + a3 * y3[j0 + j];
+            }
+        }
+        for (; s < S; ++s) {
+            const double *y0 = &Y[static_cast<size_t>(s) * dg];
+            for (int i = 0; i < ni; ++i)
+                for (int j = 0; j < nj; ++j) acc[i][j] += y0[i0 + i] * y0[j0 + j];
+        }
+        for (int i = 0; i < ni; ++i)
+            for (int j = 0; j < nj; ++j) {
+                const double v = acc[i][j] / static_cast<double>(S);
+                C[static_cast<size_t>(i0 + i) * dg + j0 + j] = v;
+                C[static_cast<size_t>(j0 + j) * dg + i0 + i] = v;
+            }
+    };
+    if (inner_parallel) {
+        parallel_for(static_cast<int64_t>(blocks.size()), do_block);
+    } else {
+        for (size_t t = 0; t < blocks.size(); ++t) do_block(static_cast<int64_t>(t));
+    }
+}
+
+// Eigenpairs sorted by descending eigenvalue, eigenvalues clamped at 0, each
+// eigenvector signed so that its largest-magnitude entry (first on ties) is positive.
+void eig_sorted(std::vector<double> &C, int dg, UnitFit &f) {
+    std::vector<double> w, qt;
+    sym_eig(C, dg, w, qt);
+    std::vector<int> order(dg);
+    for (int i = 0; i < dg; ++i) order[i] = i;
+    std::stable_sort(order.begin(), order.end(), [&](int x, int y) { return w[x] > w[y]; });
+    f.lam.resize(dg);
+    f.vecs.resize(static_cast<size_t>(dg) * dg);
+    for (int k = 0; k < dg; ++k) {
+        f.lam[k] = std::max(w[order[k]], 0.0);
+        const double *src = &qt[static_cast<size_t>(order[k]) * dg];
+        int arg = 0;
+        double big = -1.0;
+        for (int d = 0; d < dg; ++d)
+            if (std::fabs(src[d]) > big) {
+                big = std::fabs(src[d]);
+                arg = d;
+            }
+        const double sg = src[arg] < 0 ? -1.0 : 1.0;
+        double *dst = &f.vecs[static_cast<size_t>(k) * dg];
+        for (int d = 0; d < dg; ++d) dst[d] = sg * src[d];
+    }
+}
+
+// Frozen (min, scale) of every component with non-zero width, over the
+// prefill latents (Y - mu32) . basis32 evaluated in float64.
+void frozen_ranges(const std::vector<double> &Xraw, int64_t S, int dg, const float *mu32,
+                   const float *basis32, int r, const uint8_t *bits, float *qmin, float *qscale,
+                   bool inner_parallel) {
+    std::vector<int> comps;
+    for (int i = 0; i < r; ++i) {
+        qmin[i] = 0.0f;
+        qscale[i] = 0.0f;
+        if (bits[i]) comps.push_back(i);
+    }
+    if (comps.empty()) return;
+    const int nc = static_cast<int>(comps.size());
+    const int64_t chunk = 512;
+    const int64_t nchunks = (S + chunk - 1) / chunk;
+    std::vector<double> lo(static_cast<size_t>(nchunks) * nc, std::numeric_limits<double>::infinity());
+    std::vector<double> hi(static_cast<size_t>(nchunks) * nc, -std::numeric_limits<double>::infinity());
+    std::vector<double> V(static_cast<size_t>(nc) * dg), mu(dg);
+    for (int d = 0; d < dg; ++d) mu[d] = mu32[d];
+    for (int c = 0; c < nc; ++c)
+        for (int d = 0; d < dg; ++d)
+            V[static_cast<size_t>(c) * dg + d] = basis32[static_cast<size_t>(comps[c]) * dg + d];
+    auto do_chunk = [&](int64_t t) {
+        std::vector<double> y(dg);
+        double *l = &lo[static_cast<size_t>(t) * nc], *h = &hi[static_cast<size_t>(t) * nc];
+        const int64_t s1 = std::min(S, (t + 1) * chunk);
+        for (int64_t s = t * chunk; s < s1; ++s) {
+            const double *x = &Xraw[static_cast<size_t>(s) * dg];
+            for (int d = 0; d < dg; ++d) y[d] = x[d] - mu[d];
+            for (int c = 0; c < nc; ++c) {
+                const double *v = &V[static_cast<size_t>(c) * dg];
+                double a0 = 0, a1 = 0, a2 = 0, a3 = 0;
+                int d = 0;
+                for (; d + 4 <= dg; d += 4) {
+                    a0 += y[d] * v[d];
+                    a1 += y[d + 1] * v[d + 1];
+                    a2 += y[d + 2] * v[d + 2];
+                    a3 += y[d + 3] * v[d + 3];
+                }
+                for (; d < dg; ++d) a0 += y[d] * v[d];
+                const double val = (a0 + a1) + (a2 + a3);
+                l[c] = std::min(l[c], val);
+                h[c] = std::max(h[c], val);
+            }
+        }
+    };
+    if (inner_parallel) parallel_for(nchunks, do_chunk);
+    else for (int64_t t = 0; t < nchunks; ++t) do_chunk(t);
+    for (int c = 0; c < nc; ++c) {
+        double mn = std::numeric_limits<double>::infinity(), mx = -mn;
+        for (int64_t t = 0; t < nchunks; ++t) {
+            mn = std::min(mn, lo[static_cast<size_t>(t) * nc + c]);
+            mx = std::max(mx, hi[static_cast<size_t>(t) * nc + c]);
+        }
+        const int i = comps[c];
+        qmin[i] = static_cast<float>(mn);
+        qscale[i] = mx > mn ? static_cast<float>((mx - mn) / static_cast<double>((1 << bits[i]) - 1))
+                            : 0.0f;
+    }
+}
+
+// -------------------------------------------------------------- blob build
+struct Layout {
+    uint64_t off_unit, off_lambda, off_bits, off_qmin, off_qscale, off_mu, off_slot_comp,
+        off_slot_bits, off_basis, off_qlo, off_qinv, off_w16, off_bias, total;
+};
+
+Layout plan_layout(int64_t U, int dg, int rmax, int kslots) {
+    Layout L{};
+    uint64_t o = align_up(sizeof(kvtc_state_header), kSectionAlign);
+    auto take = [&](uint64_t bytes) {
+        uint64_t at = o;
+        o = align_up(o + std::max<uint64_t>(bytes, 1), kSectionAlign);
+        return at;
+    };
+    L.off_unit = take(U * sizeof(kvtc_unit_info));
+    L.off_lambda = take(U * dg * sizeof(double));
+    L.off_bits = take(U * rmax);
+    L.off_qmin = take(U * rmax * sizeof(float));
+    L.off_qscale = take(U * rmax * sizeof(float));
+    L.off_mu = take(U * dg * sizeof(float));
+    L.off_slot_comp = take(U * kslots * sizeof(int32_t));
+    L.off_slot_bits = take(U * kslots * sizeof(uint32_t));
+    L.off_basis = take(U * static_cast<uint64_t>(kslots) * dg * sizeof(float));
+    L.off_qlo = take(U * kslots * sizeof(double));
+    L.off_qinv = take(U * kslots * sizeof(double));
+    L.off_w16 = take(U * static_cast<uint64_t>(kslots) * dg * sizeof(uint16_t));
+    L.off_bias = take(U * dg * sizeof(float));
+    L.total = o;
+    return L;
+}
+
+// Builds the blob from per-unit frozen parts.  bits is ignored (recomputed)
+// in mixed mode.  Returns a status; writes only when state_out is large enough.
+int32_t build_blob(const kvtc_config *cfg, int64_t B, int64_t H, int32_t rmax, const int32_t *ranks,
+                   const float *mu, const float *basis, const double *lambda, const uint8_t *bits_in,
+                   const float *qmin, const float *qscale, int64_t s_prefill, void *state_out,
+                   size_t *state_bytes) {
+    const int hpu = cfg->heads_per_unit;
+    const int dg = cfg->head_dim * hpu;
+    const int64_t U = B * (H / hpu);
+    std::vector<uint8_t> bits(static_cast<size_t>(U) * rmax, 0);
+    std::vector<int> n_slots(U), row_bits(U);
+    int n_hi = 0;
+    for (int64_t u = 0; u < U; ++u) {
+        const int r = ranks[u];
+        if (r < 1 || r > rmax) return KVTC_E_ARG;
+        uint8_t *bu = &bits[static_cast<size_t>(u) * rmax];
+        if (cfg->mode == KVTC_MODE_DP) {
+            for (int i = 0; i < r; ++i) {
+                const int b = bits_in[static_cast<size_t>(u) * rmax + i];
+                if (!width_allowed(b)) return KVTC_E_ARG;
+                bu[i] = static_cast<uint8_t>(b);
+            }
+        } else {
+            if (r != rmax) return KVTC_E_ARG;            // one stored rank for every group
+            n_hi = mixed_n_hi(r, cfg->hi_fraction, cfg->group_size);
+            for (int i = 0; i < r; ++i) bu[i] = static_cast<uint8_t>(i < n_hi ? cfg->hi_bits : cfg->lo_bits);
+        }
+        int ns = 0, rb = 0;
+        for (int i = 0; i < r; ++i)
+            if (bu[i]) {
+                ++ns;
+                rb += bu[i];
+            }
+        n_slots[u] = ns;
+        row_bits[u] = rb;
+    }
+    int max_slots = 0, max_bits = 0;
+    for (int64_t u = 0; u < U; ++u) {
+        max_slots = std::max(max_slots, n_slots[u]);
+        max_bits = std::max(max_bits, row_bits[u]);
+    }
+    const int kslots = std::max<int>(kSlotAlign, static_cast<int>(align_up(max_slots, kSlotAlign)));
+    const Layout L = plan_layout(U, dg, rmax, kslots);
+    if (state_out == nullptr || *state_bytes < L.total) {
+        *state_bytes = L.total;
+        return state_out == nullptr ? KVTC_OK : KVTC_E_BUFSIZE;
+    }
+    *state_bytes = L.total;
+    std::memset(state_out, 0, L.total);
+    auto *h = static_cast<kvtc_state_header *>(state_out);
+    h->magic = KVTC_MAGIC;
+    h->version = KVTC_VERSION;
+    h->mode = cfg->mode;
+    h->head_dim = cfg->head_dim;
+    h->heads_per_unit = hpu;
+    h->dg = dg;
+    h->batch = B;
+    h->heads = H;
+    h->units = U;
+    h->rmax = rmax;
+    h->kslots = kslots;
+    h->row_stride = 4 * ((max_bits + 31) / 32);
+    h->n_qgroups = cfg->mode == KVTC_MODE_MIXED ? (rmax + cfg->group_size - 1) / cfg->group_size : 0;
+    h->group_size = cfg->group_size;
+    h->hi_bits = cfg->hi_bits;
+    h->lo_bits = cfg->lo_bits;
+    h->n_hi = n_hi;
+    h->bit_budget = cfg->bit_budget;
+    h->n_choices = cfg->n_choices;
+    for (int i = 0; i < KVTC_MAX_CHOICES; ++i) h->choices[i] = cfg->choices[i];
+    h->beta = cfg->beta;
+    h->energy_threshold = cfg->energy_threshold;
+    h->rank_cfg = cfg->rank;
+    h->s_prefill = s_prefill;
+    h->off_unit = L.off_unit;
+    h->off_lambda = L.off_lambda;
+    h->off_bits = L.off_bits;
+    h->off_qmin = L.off_qmin;
+    h->off_qscale = L.off_qscale;
+    h->off_mu = L.off_mu;
+    h->off_slot_comp = L.off_slot_comp;
+    h->off_slot_bits = L.off_slot_bits;
+    h->off_basis = L.off_basis;
+    h->off_qlo = L.off_qlo;
+    h->off_qinv = L.off_qinv;
+    h->off_w16 = L.off_w16;
+    h->off_bias = L.off_bias;
+    h->total_bytes = L.total;
+
+    auto *ui = section_mut<kvtc_unit_info>(state_out, L.off_unit);
+    auto *lam_o = section_mut<double>(state_out, L.off_lambda);
+    auto *bits_o = section_mut<uint8_t>(state_out, L.off_bits);
+    auto *qmin_o = section_mut<float>(state_out, L.off_qmin);
+    auto *qscale_o = section_mut<float>(state_out, L.off_qscale);
+    auto *mu_o = section_mut<float>(state_out, L.off_mu);
+    auto *scomp = section_mut<int32_t>(state_out, L.off_slot_comp);
+    auto *sbits = section_mut<uint32_t>(state_out, L.off_slot_bits);
+    auto *sbasis = section_mut<float>(state_out, L.off_basis);
+    auto *sqlo = section_mut<double>(state_out, L.off_qlo);
+    auto *sqinv = section_mut<double>(state_out, L.off_qinv);
+    auto *w16 = section_mut<uint16_t>(state_out, L.off_w16);
+    auto *bias = section_mut<float>(state_out, L.off_bias);
+
+    parallel_for(U, [&](int64_t u) {
+        const int r = ranks[u];
+        ui[u].rank = r;
+        ui[u].n_slots = n_slots[u];
+        ui[u].row_bits = row_bits[u];
+        for (int d = 0; d < dg; ++d) {
+            mu_o[u * dg + d] = mu[u * dg + d];
+            lam_o[u * dg + d] = lambda ? lambda[u * dg + d] : 0.0;
+        }
+        const uint8_t *bu = &bits[static_cast<size_t>(u) * rmax];
+        std::vector<double> bacc(dg);
+        for (int d = 0; d < dg; ++d) bacc[d] = mu[u * dg + d];
+        int j = 0;
+        uint32_t off = 0;
+        for (int i = 0; i < rmax; ++i) {
+            const size_t ci = static_cast<size_t>(u) * rmax + i;
+            bits_o[ci] = bu[i];
+            if (cfg->mode == KVTC_MODE_DP && i < r && bu[i]) {
+                qmin_o[ci] = qmin[ci];
+                qscale_o[ci] = qscale[ci];
+            }
+            if (i >= r || bu[i] == 0) continue;
+            const size_t sj = static_cast<size_t>(u) * kslots + j;
+            scomp[sj] = i;
+            sbits[sj] = (off & kOffsetMask) | (static_cast<uint32_t>(bu[i]) << 24);
+            off += bu[i];
+            const float *src = &basis[(static_cast<size_t>(u) * rmax + i) * dg];
+            float *dst = &sbasis[sj * dg];
+            for (int d = 0; d < dg; ++d) dst[d] = src[d];
+            double wscale = 1.0;
+            if (cfg->mode == KVTC_MODE_DP) {
+                sqlo[sj] = static_cast<double>(qmin[ci]);
+                sqinv[sj] = qscale[ci] > 0.0f ? 1.0 / static_cast<double>(qscale[ci]) : 0.0;
+                wscale = static_cast<double>(qscale[ci]);
+                for (int d = 0; d < dg; ++d) bacc[d] += static_cast<double>(qmin[ci]) * src[d];
+            }
+            for (int d = 0; d < dg; ++d)
+                w16[(static_cast<size_t>(u) * dg + d) * kslots + j] =
+                    half_bits_rne(wscale * static_cast<double>(src[d]));
+            ++j;
+        }
+        for (; j < kslots; ++j) scomp[static_cast<size_t>(u) * kslots + j] = -1;
+        for (int d = 0; d < dg; ++d) bias[u * dg + d] = static_cast<float>(bacc[d]);
+    });
+    return KVTC_OK;
+}
+
+// ----------------------------------------------------------------- Huffman
+// Total bits of an optimal prefix code for the given symbol counts: the sum of
+// the internal-node weights of a Huffman tree (one bit each for a lone symbol).
+uint64_t huffman_bits(const uint64_t *counts, int n) {
+    std::priority_queue<uint64_t, std::vector<uint64_t>, std::greater<uint64_t>> q;
+    for (int i = 0; i < n; ++i)
+        if (counts[i]) q.push(counts[i]);
+    if (q.empty()) return 0;
+    if (q.size() == 1) return q.top();
+    uint64_t total = 0;
+    while (q.size() > 1) {
+        const uint64_t a = q.top();
+        q.pop();
+        const uint64_t b = q.top();
+        q.pop();
+        total += a + b;
+        q.push(a + b);
+    }
+    return total;
+}
+
+}  // namespace
+}  // namespace kvtc
+
+using namespace kvtc;
+
+// =========================================================== C entry points
+extern "C" {
+
+void kvtc_config_default(kvtc_config *cfg, int32_t mode, int32_t head_dim) {
+    if (!cfg) return;
+    std::memset(cfg, 0, sizeof(*cfg));
+    cfg->mode = mode;
+    cfg->head_dim = head_dim;
+    cfg->heads_per_unit = mode == KVTC_MODE_MIXED ? 8 : 1;
+    cfg->rank = mode == KVTC_MODE_MIXED ? 0 : head_dim;
+    cfg->energy_threshold = 0.90;
+    cfg->bit_budget = 4 * head_dim;
+    const int32_t ch[] = {0, 1, 2, 3, 4, 8};
+    cfg->n_choices = 6;
+    for (int i = 0; i < 6; ++i) cfg->choices[i] = ch[i];
+    cfg->beta = 1.0;
+    cfg->hi_bits = 4;
+    cfg->lo_bits = 2;
+    cfg->group_size = 32;
+    cfg->hi_fraction = 0.25;
+}
+
+const char *kvtc_status_string(int32_t s) {
+    switch (s) {
+        case KVTC_OK: return "ok";
+        case KVTC_E_CONFIG: return "invalid or infeasible configuration";
+        case KVTC_E_SHAPE: return "shape, stride or alignment mismatch";
+        case KVTC_E_DTYPE: return "unsupported dtype";
+        case KVTC_E_CAPACITY: return "rows outside the store capacity";
+        case KVTC_E_STATE: return "missing, unfitted or corrupt state";
+        case KVTC_E_BUFSIZE: return "output buffer too small";
+        case KVTC_E_DEVICE: return "HIP device error";
+        case KVTC_E_ARG: return "invalid argument";
+        default: return "unknown status";
+    }
+}
+
+int32_t kvtc_allocate_bits(const double *lambda, int32_t r, int32_t budget, const int32_t *choices,
+                           int32_t n_choices, double beta, uint8_t *bits_out) {
+    if (!lambda || !choices || !bits_out || r < 1 || n_choices < 1 || n_choices > KVTC_MAX_CHOICES)
+        return KVTC_E_ARG;
+    if (budget < 0) return KVTC_E_CONFIG;
+    std::vector<int> ch(choices, choices + n_choices);
+    for (int b : ch)
+        if (!width_allowed(b)) return KVTC_E_CONFIG;
+    try {
+        std::vector<uint8_t> tmp(r);
+        if (!dp_allocate(lambda, r, budget, ch, beta, tmp.data())) return KVTC_E_CONFIG;
+        std::memcpy(bits_out, tmp.data(), r);
+    } catch (const std::bad_alloc &) {
+        return KVTC_E_ARG;
+    }
+    return KVTC_OK;
+}
+
+int32_t kvtc_fit_host(const kvtc_config *cfg, const void *rows_host, int32_t dtype, int64_t B,
+                      int64_t H, int64_t S, void *state_out, size_t *state_bytes) {
+    int32_t st = validate_config(cfg);
+    if (st != KVTC_OK) return st;
+    if (!rows_host || !state_bytes) return KVTC_E_ARG;
+    if (dtype != KVTC_F32 && dtype != KVTC_F16) return KVTC_E_DTYPE;
+    if (B < 1 || H < 1 || H % cfg->heads_per_unit != 0) return KVTC_E_SHAPE;
+    if (S < 2) return KVTC_E_CONFIG;                      // fit needs a prefill with S > 1
+    const int hpu = cfg->heads_per_unit, D = cfg->head_dim, dg = D * hpu;
+    const int64_t U = B * (H / hpu);
+    try {
+        std::vector<UnitFit> fits(U);
+        const bool by_unit = U >= num_threads();
+        // 1. mean, covariance, eigenpairs per unit
+        auto fit_unit = [&](int64_t u, bool inner) {
+            std::vector<double> Y, C;
+            load_unit_rows(rows_host, dtype, B, H, S, D, hpu, u, Y);
+            mean_cov(Y, S, dg, fits[u].mean, C, inner);
+            eig_sorted(C, dg, fits[u]);
+        };
+        if (by_unit) {
+            if (!parallel_for(U, [&](int64_t u) { fit_unit(u, false); })) return KVTC_E_ARG;
+        } else {
+            // few units: parallelise the covariance inside a unit, the eigensolvers across units
+            std::vector<std::vector<double>> Cs(U);
+            for (int64_t u = 0; u < U; ++u) {
+                std::vector<double> Y;
+                load_unit_rows(rows_host, dtype, B, H, S, D, hpu, u, Y);
+                mean_cov(Y, S, dg, fits[u].mean, Cs[u], true);
+            }
+            if (!parallel_for(U, [&](int64_t u) { eig_sorted(Cs[u], dg, fits[u]); })) return KVTC_E_ARG;
+        }
+        // 2. rank per unit (mixed mode stores one rank for every group)
+        int rmax = 0;
+        for (int64_t u = 0; u < U; ++u) {
+            fits[u].rank = cfg->rank > 0 ? cfg->rank
+                                         : energy_rank(fits[u].lam.data(), dg, cfg->energy_threshold);
+            rmax = std::max(rmax, fits[u].rank);
+        }
+        if (cfg->mode == KVTC_MODE_MIXED)
+            for (auto &f : fits) f.rank = rmax;
+        // 3. frozen parts: fp32 mean and basis, DP allocation, ranges
+        std::vector<int32_t> ranks(U);
+        std::vector<float> mu(static_cast<size_t>(U) * dg), basis(static_cast<size_t>(U) * rmax * dg, 0.f);
+        std::vector<double> lam(static_cast<size_t>(U) * dg);
+        std::vector<uint8_t> bits(static_cast<size_t>(U) * rmax, 0);
+        std::vector<float> qmin(static_cast<size_t>(U) * rmax, 0.f), qscale(static_cast<size_t>(U) * rmax, 0.f);
+        std::vector<int> choices(cfg->choices, cfg->choices + cfg->n_choices);
+        std::atomic<bool> feasible{true};
+        auto freeze = [&](int64_t u, bool inner) {
+            const UnitFit &f = fits[u];
+            const int r = f.rank;
+            ranks[u] = r;
+            for (int d = 0; d < dg; ++d) {
+                mu[u * dg + d] = static_cast<float>(f.mean[d]);
+                lam[u * dg + d] = f.lam[d];
+            }
+            for (int i = 0; i < r; ++i)
+                for (int d = 0; d < dg; ++d)
+                    basis[(static_cast<size_t>(u) * rmax + i) * dg + d] =
+                        static_cast<float>(f.vecs[static_cast<size_t>(i) * dg + d]);
+            if (cfg->mode != KVTC_MODE_DP) return;
+            uint8_t *bu = &bits[static_cast<size_t>(u) * rmax];
+            if (!dp_allocate(f.lam.data(), r, cfg->bit_budget, choices, cfg->beta, bu)) {
+                feasible = false;
+                return;
+            }
+            std::vector<double> X;
+            load_unit_rows(rows_host, dtype, B, H, S, D, hpu, u, X);
+            frozen_ranges(X, S, dg, &mu[u * dg], &basis[static_cast<size_t>(u) * rmax * dg], r, bu,
+                          &qmin[static_cast<size_t>(u) * rmax], &qscale[static_cast<size_t>(u) * rmax],
+                          inner);
+        };
+        if (by_unit) {
+            if (!parallel_for(U, [&](int64_t u) { freeze(u, false); })) return KVTC_E_ARG;
+        } else {
+            for (int64_t u = 0; u < U; ++u) freeze(u, true);
+        }
+        if (!feasible) return KVTC_E_CONFIG;
+        return build_blob(cfg, B, H, rmax, ranks.data(), mu.data(), basis.data(), lam.data(),
+                          bits.data(), qmin.data(), qscale.data(), S, state_out, state_bytes);
+    } catch (const std::bad_alloc &) {
+        return KVTC_E_ARG;
+    }
+}
+
+int32_t kvtc_state_build(const kvtc_config *cfg, int64_t B, int64_t H, int32_t rmax,
+                         const int32_t *ranks, const float *mu, const float *basis,
+                         const double *lambda, const uint8_t *bits, const float *qmin,
+                         const float *qscale, int64_t s_prefill, void *state_out,
+                         size_t *state_bytes) {
+    int32_t st = validate_config(cfg);
+    if (st != KVTC_OK) return st;
+    if (!ranks || !mu || !basis || !state_bytes) return KVTC_E_ARG;
+    if (cfg->mode == KVTC_MODE_DP && (!bits || !qmin || !qscale)) return KVTC_E_ARG;
+    if (B < 1 || H < 1 || H % cfg->heads_per_unit != 0) return KVTC_E_SHAPE;
+    if (rmax < 1 || rmax > cfg->head_dim * cfg->heads_per_unit) return KVTC_E_CONFIG;
+    try {
+        return build_blob(cfg, B, H, rmax, ranks, mu, basis, lambda, bits, qmin, qscale, s_prefill,
+                          state_out, state_bytes);
+    } catch (const std::bad_alloc &) {
+        return KVTC_E_ARG;
+    }
+}
+
+int32_t kvtc_store_bytes(const void *state_host, int64_t capacity, size_t *codes_bytes,
+                         size_t *params_bytes) {
+    const kvtc_state_header *h = nullptr;
+    int32_t st = check_state(state_host, &h);
+    if (st != KVTC_OK) return st;
+    if (capacity < 0) return KVTC_E_ARG;
+    if (codes_bytes) *codes_bytes = static_cast<size_t>(h->units) * capacity * h->row_stride;
+    if (params_bytes)
+        *params_bytes = static_cast<size_t>(h->units) * capacity * h->n_qgroups * 4;
+    return KVTC_OK;
+}
+
+int32_t kvtc_bytes(const void *state_host, const void *codes_host, const void *params_host,
+                   int64_t capacity, int64_t S, kvtc_bytes_report *out) {
+    const kvtc_state_header *h = nullptr;
+    int32_t st = check_state(state_host, &h);
+    if (st != KVTC_OK) return st;
+    if (!out || (S > 0 && h->row_stride > 0 && !codes_host)) return KVTC_E_ARG;
+    if (S < 0 || S > capacity) return KVTC_E_CAPACITY;
+    (void)params_host;
+    const int64_t U = h->units;
+    const int dg = h->dg;
+    const auto *ui = section<kvtc_unit_info>(state_host, h->off_unit);
+    const auto *sbits = section<uint32_t>(state_host, h->off_slot_bits);
+    const uint8_t *codes = static_cast<const uint8_t *>(codes_host);
+    struct Per {
+        uint64_t fixed, payload, table, side, basis, qp, coded;
+    };
+    std::vector<Per> per(U);
+    try {
+        bool ok = parallel_for(U, [&](int64_t u) {
+            Per p{};
+            const int ns = ui[u].n_slots, rb = ui[u].row_bits;
+            p.fixed = (static_cast<uint64_t>(S) * rb + 7) / 8;
+            if (h->mode == KVTC_MODE_DP) {
+                p.basis = 2ull * (static_cast<uint64_t>(dg) * ns + dg);
+                p.qp = 4ull * ns;
+                uint64_t hb = 0, table = 0;
+                std::vector<uint64_t> counts(256);
+                for (int j = 0; j < ns; ++j) {
+                    const uint32_t sb = sbits[static_cast<size_t>(u) * h->kslots + j];
+                    const uint32_t off = sb & kOffsetMask, w = sb >> 24;
+                    std::fill(counts.begin(), counts.end(), 0);
+                    for (int64_t s = 0; s < S; ++s) {
+                        const uint8_t *row = codes + (static_cast<size_t>(u) * capacity + s) * h->row_stride;
+                        uint32_t c = 0;
+                        for (uint32_t k = 0; k < w; ++k) {
+                            const uint32_t bit = off + k;
+                            c |= static_cast<uint32_t>((row[bit >> 3] >> (bit & 7)) & 1u) << k;
+                        }
+                        ++counts[c];
+                    }
+                    hb += huffman_bits(counts.data(), 1 << w);
+                    table += 1ull << w;
+                }
+                const uint64_t payload = (hb + 7) / 8;
+                if (payload + table < p.fixed) {
+                    p.payload = payload;
+                    p.table = table;
+                    p.coded = 1;
+                } else {
+                    p.payload = p.fixed;
+                }
+            } else {
+                p.basis = 4ull * (static_cast<uint64_t>(dg) * ui[u].rank + dg);
+                p.qp = 4ull * static_cast<uint64_t>(S) * h->n_qgroups;
+                p.payload = p.fixed;
+            }
+            per[u] = p;
+        });
+        if (!ok) return KVTC_E_ARG;
+    } catch (const std::bad_alloc &) {
+        return KVTC_E_ARG;
+    }
+    kvtc_bytes_report r{};
+    for (int64_t u = 0; u < U; ++u) {
+        const Per &p = per[u];
+        r.fixed_payload += p.fixed;
+        if (p.coded) {
+            r.entropy_payload += p.payload;
+            r.entropy_table += p.table;
+            r.units_entropy_coded += 1;
+        }
+        r.stored_payload += p.payload;
+        r.basis += p.basis;
+        r.quant_params += p.qp;
+        r.total += p.payload + p.table + p.basis + p.qp;
+        r.pre_entropy += p.fixed + p.basis + p.qp;
+        r.n_survived += ui[u].n_slots;
+    }
+    r.fp16_equiv = static_cast<uint64_t>(h->batch) * h->heads * S * h->head_dim * 2;
+    r.device_store = static_cast<uint64_t>(U) * S * (h->row_stride + 4ull * h->n_qgroups);
+    *out = r;
+    return KVTC_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,54 @@
+// Internal helpers shared by the host and device halves of libkvtc:
+// state-blob access and validation.  Not part of the public interface.
+#pragma once
+
+#include <cstddef>
+#include <cstdint>
+#include <cstring>
+
+#include "kvtc.h"
+
+namespace kvtc {
+
+constexpr int kSlotAlign = 16;          // slots per unit are padded to a multiple of this
+constexpr int kSectionAlign = 256;      // blob sections start on this boundary
+constexpr uint32_t kOffsetMask = 0xFFFFFFu;
+
+inline uint64_t align_up(uint64_t x, uint64_t a) { return (x + a - 1) / a * a; }
+
+template <typename T>
+inline const T *section(const void *blob, uint64_t off) {
+    return reinterpret_cast<const T *>(static_cast<const char *>(blob) + off);
+}
+template <typename T>
+inline T *section_mut(void *blob, uint64_t off) {
+    return reinterpret_cast<T *>(static_cast<char *>(blob) + off);
+}
+
+// Validates the header of a host copy of a state blob.  Returns KVTC_OK or
+// KVTC_E_STATE; on success *out points at the header.
+inline int32_t check_state(const void *blob, const kvtc_state_header **out) {
+    if (blob == nullptr) return KVTC_E_ARG;
+    const auto *h = static_cast<const kvtc_state_header *>(blob);
+    if (h->magic != KVTC_MAGIC || h->version != KVTC_VERSION) return KVTC_E_STATE;
+    if (h->mode != KVTC_MODE_DP && h->mode != KVTC_MODE_MIXED) return KVTC_E_STATE;
+    if (h->head_dim <= 0 || h->heads_per_unit <= 0 || h->dg != h->head_dim * h->heads_per_unit)
+        return KVTC_E_STATE;
+    if (h->batch <= 0 || h->heads <= 0 || h->heads % h->heads_per_unit != 0 ||
+        h->units != h->batch * (h->heads / h->heads_per_unit))
+        return KVTC_E_STATE;
+    if (h->rmax <= 0 || h->rmax > h->dg || h->kslots < kSlotAlign || h->kslots % kSlotAlign != 0 ||
+        h->row_stride < 0 || h->row_stride % 4 != 0)
+        return KVTC_E_STATE;
+    if (h->mode == KVTC_MODE_MIXED && (h->n_qgroups <= 0 || h->group_size <= 0)) return KVTC_E_STATE;
+    const uint64_t offs[] = {h->off_unit, h->off_lambda, h->off_bits, h->off_qmin, h->off_qscale,
+                             h->off_mu, h->off_slot_comp, h->off_slot_bits, h->off_basis,
+                             h->off_qlo, h->off_qinv, h->off_w16, h->off_bias};
+    for (uint64_t o : offs)
+        if (o < sizeof(kvtc_state_header) || o % kSectionAlign != 0 || o >= h->total_bytes)
+            return KVTC_E_STATE;
+    if (out) *out = h;
+    return KVTC_OK;
+}
+
+}  // namespace kvtc

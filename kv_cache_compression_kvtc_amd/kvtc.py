@@ -1,0 +1,262 @@
+"""ctypes binding of libkvtc.so: the same entry points as ``include/kvtc.h``.
+
+Argument marshalling only.  Host buffers are numpy arrays, device buffers are
+torch CUDA (HIP) tensors; every step of the method runs inside the library.
+There is no fallback: if the library is missing, importing this module raises.
+"""
+from __future__ import annotations
+
+import ctypes as C
+import os
+
+import numpy as np
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libkvtc.so")
+
+OK, E_CONFIG, E_SHAPE, E_DTYPE, E_CAPACITY, E_STATE, E_BUFSIZE, E_DEVICE, E_ARG = 0, -1, -2, -3, -4, -5, -6, -7, -8
+F32, F16 = 0, 1
+MODE_DP, MODE_MIXED = 0, 1
+MAX_CHOICES = 8
+MAGIC = 0x4354564B
+
+
+class KVTCError(RuntimeError):
+    def __init__(self, status: int, what: str):
+        super().__init__(f"{what}: {status_string(status)} ({status})")
+        self.status = status
+
+
+class Config(C.Structure):
+    _fields_ = [("mode", C.c_int32), ("head_dim", C.c_int32), ("heads_per_unit", C.c_int32),
+                ("rank", C.c_int32), ("energy_threshold", C.c_double), ("bit_budget", C.c_int32),
+                ("n_choices", C.c_int32), ("choices", C.c_int32 * MAX_CHOICES), ("beta", C.c_double),
+                ("hi_bits", C.c_int32), ("lo_bits", C.c_int32), ("group_size", C.c_int32),
+                ("hi_fraction", C.c_double)]
+
+
+class UnitInfo(C.Structure):
+    _fields_ = [("rank", C.c_int32), ("n_slots", C.c_int32), ("row_bits", C.c_int32),
+                ("reserved", C.c_int32)]
+
+
+class StateHeader(C.Structure):
+    _fields_ = [("magic", C.c_uint32), ("version", C.c_uint32), ("mode", C.c_int32),
+                ("head_dim", C.c_int32), ("heads_per_unit", C.c_int32), ("dg", C.c_int32),
+                ("batch", C.c_int64), ("heads", C.c_int64), ("units", C.c_int64),
+                ("rmax", C.c_int32), ("kslots", C.c_int32), ("row_stride", C.c_int32),
+                ("n_qgroups", C.c_int32), ("group_size", C.c_int32), ("hi_bits", C.c_int32),
+                ("lo_bits", C.c_int32), ("n_hi", C.c_int32), ("bit_budget", C.c_int32),
+                ("n_choices", C.c_int32), ("choices", C.c_int32 * MAX_CHOICES), ("beta", C.c_double),
+                ("energy_threshold", C.c_double), ("rank_cfg", C.c_int32), ("reserved0", C.c_int32),
+                ("s_prefill", C.c_int64), ("off_unit", C.c_uint64), ("off_lambda", C.c_uint64),
+                ("off_bits", C.c_uint64), ("off_qmin", C.c_uint64), ("off_qscale", C.c_uint64),
+                ("off_mu", C.c_uint64), ("off_slot_comp", C.c_uint64), ("off_slot_bits", C.c_uint64),
+                ("off_basis", C.c_uint64), ("off_qlo", C.c_uint64), ("off_qinv", C.c_uint64),
+                ("off_w16", C.c_uint64), ("off_bias", C.c_uint64), ("total_bytes", C.c_uint64),
+                ("reserved", C.c_uint64 * 4)]
+
+
+class BytesReport(C.Structure):
+    _fields_ = [(n, C.c_uint64) for n in ("fixed_payload", "entropy_payload", "entropy_table",
+                                          "stored_payload", "basis", "quant_params", "total",
+                                          "pre_entropy", "fp16_equiv", "device_store")] + \
+               [("n_survived", C.c_int64), ("units_entropy_coded", C.c_int64)]
+
+    def as_dict(self):
+        return {f[0]: int(getattr(self, f[0])) for f in self._fields_}
+
+
+if not os.path.exists(LIB_PATH):
+    raise ImportError(f"{LIB_PATH} is not built; run python -m kv_cache_compression_kvtc_amd.build")
+_lib = C.CDLL(LIB_PATH)
+
+_vp, _i32, _i64, _sz = C.c_void_p, C.c_int32, C.c_int64, C.c_size_t
+_P64 = C.POINTER(C.c_int64)
+_sig = {
+    "kvtc_config_default": (None, [C.POINTER(Config), _i32, _i32]),
+    "kvtc_status_string": (C.c_char_p, [_i32]),
+    "kvtc_fit_host": (_i32, [C.POINTER(Config), _vp, _i32, _i64, _i64, _i64, _vp, C.POINTER(_sz)]),
+    "kvtc_state_build": (_i32, [C.POINTER(Config), _i64, _i64, _i32, _vp, _vp, _vp, _vp, _vp, _vp,
+                                _vp, _i64, _vp, C.POINTER(_sz)]),
+    "kvtc_allocate_bits": (_i32, [_vp, _i32, _i32, _vp, _i32, C.c_double, _vp]),
+    "kvtc_store_bytes": (_i32, [_vp, _i64, C.POINTER(_sz), C.POINTER(_sz)]),
+    "kvtc_append": (_i32, [_vp, _vp, _vp, _i32, _P64, _i64, _i64, _i64, _i64, _vp, _vp, _i64, _vp]),
+    "kvtc_fetch": (_i32, [_vp, _vp, _vp, _vp, _i64, _i64, _i64, _vp, _P64, _vp]),
+    "kvtc_bytes": (_i32, [_vp, _vp, _vp, _i64, _i64, C.POINTER(BytesReport)]),
+}
+for _name, (_res, _args) in _sig.items():
+    _f = getattr(_lib, _name)
+    _f.restype = _res
+    _f.argtypes = _args
+
+EXPORTED = tuple(_sig)
+
+
+def status_string(status: int) -> str:
+    return _lib.kvtc_status_string(status).decode()
+
+
+def _check(status: int, what: str):
+    if status != OK:
+        raise KVTCError(status, what)
+
+
+def _host_ptr(a):
+    return None if a is None else a.ctypes.data
+
+
+def _dev_ptr(t):
+    return None if t is None else t.data_ptr()
+
+
+def _strides4(t):
+    return (C.c_int64 * 4)(*[int(s) for s in t.stride()])
+
+
+def _stream_ptr(stream):
+    if stream is None:
+        import torch
+        stream = torch.cuda.current_stream()
+    return stream.cuda_stream
+
+
+# ---------------------------------------------------------------- config
+def config_default(mode: int = MODE_DP, head_dim: int = 128) -> Config:
+    cfg = Config()
+    _lib.kvtc_config_default(C.byref(cfg), mode, head_dim)
+    return cfg
+
+
+def make_config(mode="dp", head_dim=128, heads_per_unit=None, rank=0, energy=0.90, budget=None,
+                choices=(0, 1, 2, 3, 4, 8), beta=1.0, hi_bits=4, lo_bits=2, group_size=32,
+                hi_fraction=0.25) -> Config:
+    m = MODE_DP if mode == "dp" else MODE_MIXED
+    cfg = config_default(m, head_dim)
+    cfg.heads_per_unit = heads_per_unit if heads_per_unit is not None else (1 if m == MODE_DP else 8)
+    cfg.rank = rank
+    cfg.energy_threshold = energy
+    cfg.bit_budget = 4 * head_dim if budget is None else budget
+    cfg.n_choices = len(choices)
+    for i, b in enumerate(choices):
+        cfg.choices[i] = b
+    cfg.beta = beta
+    cfg.hi_bits, cfg.lo_bits, cfg.group_size, cfg.hi_fraction = hi_bits, lo_bits, group_size, hi_fraction
+    return cfg
+
+
+# ---------------------------------------------------------------- host calls
+def kvtc_fit_host(cfg: Config, rows: np.ndarray) -> np.ndarray:
+    """Fit one tensor's frozen state on contiguous host rows [B, H, S, D]; returns the blob."""
+    rows = np.ascontiguousarray(rows)
+    dtype = {np.dtype(np.float32): F32, np.dtype(np.float16): F16}.get(rows.dtype)
+    if dtype is None:
+        raise KVTCError(E_DTYPE, "kvtc_fit_host")
+    B, H, S, D = rows.shape
+    size = C.c_size_t(0)
+    _check(_lib.kvtc_fit_host(C.byref(cfg), _host_ptr(rows), dtype, B, H, S, None, C.byref(size)),
+           "kvtc_fit_host(size)")
+    blob = np.zeros(size.value, dtype=np.uint8)
+    _check(_lib.kvtc_fit_host(C.byref(cfg), _host_ptr(rows), dtype, B, H, S, _host_ptr(blob),
+                              C.byref(size)), "kvtc_fit_host")
+    return blob
+
+
+def kvtc_state_build(cfg: Config, B: int, H: int, ranks, mu, basis, lam=None, bits=None, qmin=None,
+                     qscale=None, s_prefill: int = 0) -> np.ndarray:
+    """Blob from frozen parts: ranks [U], mu [U,dg] f32, basis [U,rmax,dg] f32 (row = component),
+    lam [U,dg] f64 or None, bits [U,rmax] u8, qmin/qscale [U,rmax] f32 (DP)."""
+    ranks = np.ascontiguousarray(ranks, dtype=np.int32)
+    mu = np.ascontiguousarray(mu, dtype=np.float32)
+    basis = np.ascontiguousarray(basis, dtype=np.float32)
+    rmax = basis.shape[1]
+    conv = lambda a, dt: None if a is None else np.ascontiguousarray(a, dtype=dt)
+    lam, bits = conv(lam, np.float64), conv(bits, np.uint8)
+    qmin, qscale = conv(qmin, np.float32), conv(qscale, np.float32)
+    args = [C.byref(cfg), B, H, rmax, _host_ptr(ranks), _host_ptr(mu), _host_ptr(basis),
+            _host_ptr(lam), _host_ptr(bits), _host_ptr(qmin), _host_ptr(qscale), s_prefill]
+    size = C.c_size_t(0)
+    _check(_lib.kvtc_state_build(*args, None, C.byref(size)), "kvtc_state_build(size)")
+    blob = np.zeros(size.value, dtype=np.uint8)
+    _check(_lib.kvtc_state_build(*args, _host_ptr(blob), C.byref(size)), "kvtc_state_build")
+    return blob
+
+
+def kvtc_allocate_bits(lam, budget: int, choices, beta: float = 1.0) -> np.ndarray:
+    lam = np.ascontiguousarray(lam, dtype=np.float64)
+    ch = np.ascontiguousarray(choices, dtype=np.int32)
+    out = np.zeros(len(lam), dtype=np.uint8)
+    _check(_lib.kvtc_allocate_bits(_host_ptr(lam), len(lam), budget, _host_ptr(ch), len(ch), beta,
+                                   _host_ptr(out)), "kvtc_allocate_bits")
+    return out
+
+
+def kvtc_store_bytes(blob: np.ndarray, capacity: int):
+    cb, pb = C.c_size_t(0), C.c_size_t(0)
+    _check(_lib.kvtc_store_bytes(_host_ptr(blob), capacity, C.byref(cb), C.byref(pb)), "kvtc_store_bytes")
+    return cb.value, pb.value
+
+
+def kvtc_bytes(blob: np.ndarray, codes: np.ndarray, params, capacity: int, S: int) -> dict:
+    rep = BytesReport()
+    _check(_lib.kvtc_bytes(_host_ptr(blob), _host_ptr(np.ascontiguousarray(codes)), _host_ptr(params),
+                           capacity, S, C.byref(rep)), "kvtc_bytes")
+    return rep.as_dict()
+
+
+# ---------------------------------------------------------------- device calls
+def kvtc_append(blob: np.ndarray, blob_dev, x, s0: int, codes, params, capacity: int, stream=None):
+    """Append rows x [B, H, n, D] (fp16/fp32 device tensor) at store rows [s0, s0+n)."""
+    import torch
+    dtype = {torch.float16: F16, torch.float32: F32}.get(x.dtype)
+    if dtype is None:
+        raise KVTCError(E_DTYPE, "kvtc_append")
+    B, H, n, D = x.shape
+    _check(_lib.kvtc_append(_host_ptr(blob), _dev_ptr(blob_dev), _dev_ptr(x), dtype, _strides4(x), B, H, n,
+                            s0, _dev_ptr(codes), _dev_ptr(params), capacity, _stream_ptr(stream)),
+           "kvtc_append")
+
+
+def kvtc_fetch(blob: np.ndarray, blob_dev, codes, params, capacity: int, s_begin: int, s_end: int, out,
+               stream=None):
+    """Reconstruct store rows [s_begin, s_end) into the fp16 device tensor out [B, H, s_end-s_begin, D]."""
+    import torch
+    if out.dtype != torch.float16:
+        raise KVTCError(E_DTYPE, "kvtc_fetch")
+    _check(_lib.kvtc_fetch(_host_ptr(blob), _dev_ptr(blob_dev), _dev_ptr(codes), _dev_ptr(params), capacity,
+                           s_begin, s_end, _dev_ptr(out), _strides4(out), _stream_ptr(stream)), "kvtc_fetch")
+
+
+# ---------------------------------------------------------------- blob introspection
+def header(blob: np.ndarray) -> StateHeader:
+    return StateHeader.from_buffer_copy(blob[: C.sizeof(StateHeader)].tobytes())
+
+
+def state_view(blob: np.ndarray) -> dict:
+    """Numpy views of the blob's sections (layout of include/kvtc.h)."""
+    h = header(blob)
+    if h.magic != MAGIC:
+        raise KVTCError(E_STATE, "state_view")
+    U, dg, rmax, ks = h.units, h.dg, h.rmax, h.kslots
+
+    def sec(off, dt, shape):
+        n = int(np.prod(shape))
+        return np.frombuffer(blob, dtype=dt, count=n, offset=off).reshape(shape)
+
+    unit = sec(h.off_unit, np.int32, (U, 4))
+    return {
+        "header": h,
+        "rank": unit[:, 0], "n_slots": unit[:, 1], "row_bits": unit[:, 2],
+        "lambda": sec(h.off_lambda, np.float64, (U, dg)),
+        "bits": sec(h.off_bits, np.uint8, (U, rmax)),
+        "qmin": sec(h.off_qmin, np.float32, (U, rmax)),
+        "qscale": sec(h.off_qscale, np.float32, (U, rmax)),
+        "mu": sec(h.off_mu, np.float32, (U, dg)),
+        "slot_comp": sec(h.off_slot_comp, np.int32, (U, ks)),
+        "slot_bits": sec(h.off_slot_bits, np.uint32, (U, ks)),
+        "basis": sec(h.off_basis, np.float32, (U, ks, dg)),
+        "qlo": sec(h.off_qlo, np.float64, (U, ks)),
+        "qinv": sec(h.off_qinv, np.float64, (U, ks)),
+        "w16": sec(h.off_w16, np.float16, (U, dg, ks)),
+        "bias": sec(h.off_bias, np.float32, (U, dg)),
+    }

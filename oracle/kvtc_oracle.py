@@ -109,7 +109,9 @@ def energy_rank(lam: np.ndarray, tau: float) -> int:
 
     PALU page, ``palu_rank=None`` -> ``palu_energy_threshold`` (default 0.90).
     """
-    total = float(np.sum(lam))
+    total = 0.0
+    for v in lam:
+        total += float(v)
     if total <= 0.0:
         return 1
     acc = 0.0
