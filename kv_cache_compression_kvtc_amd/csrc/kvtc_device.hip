@@ -196,8 +196,9 @@ __global__ __launch_bounds__(kThreads) void append_kernel(AppendArgs a) {
         __syncthreads();
     }
 
-    // acc[nb][i] is the latent of token 16*wave + 4*(lane>>4) + i, slot 16*nb + (lane&15)
-    const int tbase = wave * 16 + 4 * (lane >> 4);
+    // fp64 16x16x4 result layout: acc[nb][i] is row (lane>>4) + 4i, column lane&15, i.e.
+    // the latent of token 16*wave + (lane>>4) + 4i and slot 16*nb + (lane&15)
+    const int tbase = wave * 16 + (lane >> 4);
     const int64_t ub = static_cast<int64_t>(u) * a.kslots;
     if constexpr (!MIXED) {
 #pragma unroll
@@ -210,7 +211,7 @@ __global__ __launch_bounds__(kThreads) void append_kernel(AppendArgs a) {
                 const double cmax = static_cast<double>((1u << w) - 1u);
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
-                    const int t = tbase + i;
+                    const int t = tbase + 4 * i;
                     if (t < nvalid) {
                         const uint32_t c = static_cast<uint32_t>(quantise(acc[nb][i], lo, inv, cmax));
                         or_field(rows + t * row_words, off, w, c);
@@ -257,7 +258,7 @@ __global__ __launch_bounds__(kThreads) void append_kernel(AppendArgs a) {
                 lo16[i] = half_bits_to_double(hmin);
                 const double sc = half_bits_to_double(hscale);
                 inv16[i] = sc > 0.0 ? 1.0 / sc : 0.0;
-                const int t = tbase + i;
+                const int t = tbase + 4 * i;
                 if ((lane & 15) == 0 && t < nvalid)
                     a.params[(static_cast<int64_t>(u) * a.capacity + a.s0 + t0 + t) * a.n_qg + gi] =
                         static_cast<uint32_t>(hmin) | (static_cast<uint32_t>(hscale) << 16);
@@ -269,7 +270,7 @@ __global__ __launch_bounds__(kThreads) void append_kernel(AppendArgs a) {
                     const uint32_t off = a.sbits[ub + j] & kOffsetMask;
 #pragma unroll
                     for (int i = 0; i < 4; ++i) {
-                        const int t = tbase + i;
+                        const int t = tbase + 4 * i;
                         if (t < nvalid) {
                             const uint32_t c = static_cast<uint32_t>(quantise(acc[nb][i], lo16[i], inv16[i], cmax));
                             or_field(rows + t * row_words, off, w, c);

@@ -173,6 +173,15 @@ def kvtc_state_build(cfg: Config, B: int, H: int, ranks, mu, basis, lam=None, bi
     conv = lambda a, dt: None if a is None else np.ascontiguousarray(a, dtype=dt)
     lam, bits = conv(lam, np.float64), conv(bits, np.uint8)
     qmin, qscale = conv(qmin, np.float32), conv(qscale, np.float32)
+    if cfg.heads_per_unit < 1 or H % cfg.heads_per_unit:
+        raise KVTCError(E_SHAPE, "kvtc_state_build")
+    U, dg = B * (H // cfg.heads_per_unit), cfg.head_dim * cfg.heads_per_unit
+    want = {"ranks": (ranks, (U,)), "mu": (mu, (U, dg)), "basis": (basis, (U, rmax, dg)),
+            "lam": (lam, (U, dg)), "bits": (bits, (U, rmax)), "qmin": (qmin, (U, rmax)),
+            "qscale": (qscale, (U, rmax))}
+    for name, (arr, shape) in want.items():
+        if arr is not None and arr.shape != shape:
+            raise KVTCError(E_SHAPE, f"kvtc_state_build: {name} must be {shape}, got {arr.shape}")
     args = [C.byref(cfg), B, H, rmax, _host_ptr(ranks), _host_ptr(mu), _host_ptr(basis),
             _host_ptr(lam), _host_ptr(bits), _host_ptr(qmin), _host_ptr(qscale), s_prefill]
     size = C.c_size_t(0)
@@ -205,12 +214,27 @@ def kvtc_bytes(blob: np.ndarray, codes: np.ndarray, params, capacity: int, S: in
 
 
 # ---------------------------------------------------------------- device calls
+def _check_buffers(blob, blob_dev, codes, params, capacity, what):
+    h = header(blob)
+    if blob_dev is None or blob_dev.numel() * blob_dev.element_size() < blob.nbytes or not blob_dev.is_cuda:
+        raise KVTCError(E_ARG, what + ": device state copy")
+    cb, pb = kvtc_store_bytes(blob, capacity)
+    if cb and (codes is None or not codes.is_cuda or codes.numel() * codes.element_size() < cb):
+        raise KVTCError(E_ARG, what + ": code store smaller than units*capacity*row_stride")
+    if pb and (params is None or not params.is_cuda or params.numel() * params.element_size() < pb):
+        raise KVTCError(E_ARG, what + ": parameter store too small")
+    return h
+
+
 def kvtc_append(blob: np.ndarray, blob_dev, x, s0: int, codes, params, capacity: int, stream=None):
     """Append rows x [B, H, n, D] (fp16/fp32 device tensor) at store rows [s0, s0+n)."""
     import torch
     dtype = {torch.float16: F16, torch.float32: F32}.get(x.dtype)
     if dtype is None:
         raise KVTCError(E_DTYPE, "kvtc_append")
+    h = _check_buffers(blob, blob_dev, codes, params, capacity, "kvtc_append")
+    if x.dim() != 4 or not x.is_cuda or x.shape[3] != h.head_dim:
+        raise KVTCError(E_SHAPE, "kvtc_append: x must be a device tensor [B, H, n, D]")
     B, H, n, D = x.shape
     _check(_lib.kvtc_append(_host_ptr(blob), _dev_ptr(blob_dev), _dev_ptr(x), dtype, _strides4(x), B, H, n,
                             s0, _dev_ptr(codes), _dev_ptr(params), capacity, _stream_ptr(stream)),
@@ -223,6 +247,9 @@ def kvtc_fetch(blob: np.ndarray, blob_dev, codes, params, capacity: int, s_begin
     import torch
     if out.dtype != torch.float16:
         raise KVTCError(E_DTYPE, "kvtc_fetch")
+    h = _check_buffers(blob, blob_dev, codes, params, capacity, "kvtc_fetch")
+    if not out.is_cuda or tuple(out.shape) != (h.batch, h.heads, s_end - s_begin, h.head_dim):
+        raise KVTCError(E_SHAPE, "kvtc_fetch: out must be a device tensor [B, H, s_end - s_begin, D]")
     _check(_lib.kvtc_fetch(_host_ptr(blob), _dev_ptr(blob_dev), _dev_ptr(codes), _dev_ptr(params), capacity,
                            s_begin, s_end, _dev_ptr(out), _strides4(out), _stream_ptr(stream)), "kvtc_fetch")
 

@@ -17,3 +17,11 @@ def pytest_configure(config):
 def rng():
     import numpy as np
     return np.random.default_rng(20261202)
+
+
+def pytest_sessionstart(session):
+    # tests load the built library; build it only when nothing is built yet
+    lib = os.path.join(ROOT, "kv_cache_compression_kvtc_amd", "libkvtc.so")
+    if not os.path.exists(lib):
+        from kv_cache_compression_kvtc_amd.build import build
+        build()

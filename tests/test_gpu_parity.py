@@ -1,0 +1,240 @@
+"""Device append/fetch (libkvtc HIP kernels) against the CPU oracle on MI355X.
+
+Every test calls the C-ABI through the Python binding.  Sizes are chosen so
+the oracle finishes in seconds while spanning several tiles and a ragged tail;
+the full-size batched-decode workload is checked on sampled units.
+"""
+import numpy as np
+import pytest
+
+torch = pytest.importorskip("torch")
+
+from oracle import kvtc_oracle as O
+from kv_cache_compression_kvtc_amd import synth
+
+pytestmark = pytest.mark.gpu
+
+from gpu_helpers import (DeviceStore, blob_from_oracle, check_codes_dp, check_codes_mixed,
+                         check_recon, oracle_cfg)
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    assert torch.cuda.is_available(), "the gpu tests need a HIP device"
+    from kv_cache_compression_kvtc_amd import kvtc  # noqa: F401  (fails loudly if not built)
+    yield
+    torch.cuda.synchronize()
+
+
+def small(wid, **kw):
+    w = synth.WORKLOADS[wid]
+    fields = dict(w.__dict__)
+    fields.update(kw)
+    return synth.Workload(**fields)
+
+
+def print_case(*a):
+    print("CASE", *a, flush=True)
+
+
+# ---------------------------------------------------------------- fetch on oracle stores
+FETCH_CASES = [
+    ("tiny-k", small(1), 0),
+    ("tiny-v", small(1), 1),
+    ("llama-k", small(2, s_total=4096 + 77), 0),
+    ("llama-v", small(2, s_total=4096 + 77), 1),
+    ("batched-k", small(4, B=3, s_prefill=2048, s_total=2048 + 45), 0),
+    ("long-k", small(5, s_prefill=4096, s_total=4096 + 1000), 0),
+    ("long-v", small(5, s_prefill=4096, s_total=4096 + 1000), 1),
+    ("palu-k", small(3, H=16, s_prefill=2048, s_total=2048 + 33), 0),
+    ("palu-v", small(3, H=16, s_prefill=2048, s_total=2048 + 33), 1),
+]
+
+
+@pytest.mark.parametrize("name,w,tensor", FETCH_CASES, ids=[c[0] for c in FETCH_CASES])
+def test_fetch_on_oracle_store(name, w, tensor):
+    print_case("fetch", name)
+    X = synth.generate(w, tensor)
+    st = O.fit(oracle_cfg(w), X[:, :, : w.s_prefill])
+    rows, params = O.append(st, X)
+    S = X.shape[2]
+    ds = DeviceStore(blob_from_oracle(st), capacity=S + 5)
+    ds.load_rows(rows, params)
+    out = ds.fetch(0, S)
+    check_recon(O.fetch(st, rows, params), out, name)
+
+
+# ---------------------------------------------------------------- append parity
+APPEND_CASES = FETCH_CASES
+
+
+@pytest.mark.parametrize("name,w,tensor", APPEND_CASES, ids=[c[0] for c in APPEND_CASES])
+def test_append_matches_oracle(name, w, tensor):
+    print_case("append", name)
+    X = synth.generate(w, tensor)
+    st = O.fit(oracle_cfg(w), X[:, :, : w.s_prefill])
+    S = X.shape[2]
+    ds = DeviceStore(blob_from_oracle(st), capacity=S + 3)
+    ds.append(X[:, :, : w.s_prefill], 0)
+    ds.append(X[:, :, w.s_prefill:], w.s_prefill)
+    dev_rows = ds.rows(S)
+    if w.mode == "dp":
+        check_codes_dp(st, X, dev_rows)
+    else:
+        check_codes_mixed(st, X, dev_rows, ds.params_np(S))
+    # end to end: the device fetch of the device store reconstructs what the oracle
+    # reconstructs from the same codes
+    out = ds.fetch(0, S)
+    prm = ds.params_np(S) if w.mode == "mixed" else None
+    check_recon(O.fetch(st, dev_rows, prm), out, name)
+
+
+# ---------------------------------------------------------------- determinism
+def test_token_at_a_time_equals_all_at_once():
+    # KVTC page, "NOT PATH-DEPENDENT": appending after prefill one token at a
+    # time or all at once stores the same codes and fetches the same output
+    print_case("determinism tiny")
+    w = synth.WORKLOADS[1]
+    for tensor in (0, 1):
+        X = synth.generate(w, tensor)
+        st = O.fit(oracle_cfg(w), X[:, :, :256])
+        blob = blob_from_oracle(st)
+        a, b = DeviceStore(blob, 288), DeviceStore(blob, 288)
+        a.append(X[:, :, :256], 0)
+        b.append(X[:, :, :256], 0)
+        outs_a = []
+        for s in range(256, 288):
+            a.append(X[:, :, s:s + 1], s)
+            outs_a.append(a.fetch(0, s + 1))
+        b.append(X[:, :, 256:288], 256)
+        out_b = b.fetch(0, 288)
+        assert np.array_equal(a.rows(288), b.rows(288))
+        assert torch.equal(outs_a[-1], out_b)
+        for s, o in enumerate(outs_a):                     # every decode step's fetch is a prefix
+            assert torch.equal(o, out_b[:, :, : 257 + s])
+        rows_o, _ = O.append(st, X)
+        check_codes_dp(st, X, a.rows(288))
+
+
+# ---------------------------------------------------------------- degenerate and edge cases
+def test_zero_budget_fetches_the_mean_exactly():
+    print_case("zero budget")
+    w = synth.WORKLOADS[1]
+    X = synth.generate(w, 0)
+    st = O.fit(oracle_cfg(w, budget=0), X[:, :, :256])
+    ds = DeviceStore(blob_from_oracle(st), 300)
+    ds.append(X, 0)
+    out = ds.fetch(0, 288).cpu().numpy()
+    mu = st.mu32.astype(np.float16)                        # [U, D], one unit per head here
+    assert np.array_equal(out[0], np.broadcast_to(mu[:, None, :], out[0].shape))
+
+
+def test_partial_fetch_ranges_and_strided_output():
+    print_case("partial fetch / strided out")
+    w = small(2, s_total=4096 + 100)
+    X = synth.generate(w, 1)
+    st = O.fit(oracle_cfg(w), X[:, :, :4096])
+    S = X.shape[2]
+    ds = DeviceStore(blob_from_oracle(st), S)
+    ds.append(X, 0)
+    ref = O.fetch(st, ds.rows(S))
+    # a window that starts mid-tile and ends in a ragged tail
+    out = ds.fetch(1000, 1000 + 77)
+    check_recon(ref[:, :, 1000:1077], out, "window")
+    full = ds.fetch(0, S).cpu().numpy().astype(np.float64)
+    assert np.array_equal(out.cpu().numpy(), full[:, :, 1000:1077].astype(np.float16))
+    # output written into a slice of a larger buffer (row stride 256, head stride padded)
+    big = torch.full((1, 8, S + 16, 256), -7.0, dtype=torch.float16, device="cuda:0")
+    view = big[:, :, 8:8 + S, 64:192]
+    ds.fetch(0, S, out=view)
+    assert torch.equal(view.cpu(), torch.from_numpy(full.astype(np.float16)))
+    untouched = big.clone()
+    untouched[:, :, 8:8 + S, 64:192] = -7.0
+    assert bool((untouched == -7.0).all())
+
+
+def test_append_from_strided_input_and_ragged_tail():
+    print_case("strided input")
+    w = small(2, s_total=4096 + 70)
+    X = synth.generate(w, 0)
+    st = O.fit(oracle_cfg(w), X[:, :, :4096])
+    ds = DeviceStore(blob_from_oracle(st), 4200)
+    big = torch.zeros((1, 8, 4096 + 70 + 9, 128), dtype=torch.float16, device="cuda:0")
+    big[:, :, 9:] = torch.from_numpy(X).cuda()
+    src = big[:, :, 9:]                                    # not starting at the buffer origin
+    ds.append(src[:, :, :4096 + 13], 0)                    # ragged: 4109 = 64 * 64 + 13
+    ds.append(src[:, :, 4096 + 13:], 4096 + 13)
+    check_codes_dp(st, X, ds.rows(4096 + 70))
+
+
+def test_fp32_input_rows():
+    print_case("fp32 input")
+    w = synth.WORKLOADS[1]
+    X = synth.generate(w, 1)
+    assert X.dtype == np.float32
+    st = O.fit(oracle_cfg(w, budget=200), X[:, :, :256])
+    ds = DeviceStore(blob_from_oracle(st), 288)
+    ds.append(X, 0)
+    check_codes_dp(st, X, ds.rows(288))
+
+
+def test_near_lossless_full_rank_8_bits():
+    print_case("near lossless")
+    w = synth.WORKLOADS[1]
+    X = synth.generate(w, 0)[:, :, :256]
+    st = O.fit(oracle_cfg(w, budget=8 * 64, choices=(8,)), X)
+    ds = DeviceStore(blob_from_oracle(st), 256)
+    ds.append(X, 0)
+    out = ds.fetch(0, 256).cpu().numpy().astype(np.float64)
+    rng_d = X.max(axis=2, keepdims=True) - X.min(axis=2, keepdims=True)
+    assert (np.abs(out - X) <= 0.02 * rng_d).all()
+
+
+def test_group_head_small_heads():
+    print_case("group head D=64")
+    w = synth.Workload(92, "gh64", B=2, H=4, D=64, dtype="f16", s_prefill=400, s_total=461,
+                       alpha_k=1.2, alpha_v=0.8, n_outliers_k=2, mode="mixed", heads_per_unit=2,
+                       rank=48, hi_bits=4, lo_bits=2, hi_fraction=0.25, group_size=16)
+    for tensor in (0, 1):
+        X = synth.generate(w, tensor)
+        st = O.fit(oracle_cfg(w), X[:, :, :400])
+        ds = DeviceStore(blob_from_oracle(st), 470)
+        ds.append(X, 0)
+        check_codes_mixed(st, X, ds.rows(461), ds.params_np(461))
+        check_recon(O.fetch(st, ds.rows(461), ds.params_np(461)), ds.fetch(0, 461), "gh64")
+
+
+# ---------------------------------------------------------------- full size, sampled
+def test_batched_decode_full_size_sampled_units():
+    """Batched decode at full size (B=64, H=8, D=128, 8192 stored + 1 appended),
+    launched as the benchmark launches it; every row of 24 sampled units is
+    compared with the oracle."""
+    print_case("batched decode full size")
+    w = synth.WORKLOADS[4]
+    X = synth.generate(w, 0)
+    st = O.fit(oracle_cfg(w), X[:, :, :8192])
+    S = w.s_total
+    ds = DeviceStore(blob_from_oracle(st), S)
+    x_dev = torch.from_numpy(X).cuda()
+    ds.append(x_dev[:, :, :8192], 0)
+    ds.append(x_dev[:, :, 8192:], 8192)
+    out = ds.fetch(0, S)
+    dev_rows = ds.rows(S)
+    rng = np.random.default_rng(4)
+    units = rng.choice(st.U, size=24, replace=False)
+    for u in units:
+        b, h = divmod(int(u), w.H)
+        r = int(st.r[u])
+        bits = st.bits[u, :r]
+        L = O.project(X[b, h], st.mu32[u], st.V32[u, :, :r])
+        want = O.quantize_dp(L, bits, st.qmin32[u, :r], st.qscale32[u, :r])
+        got = O.unpack_rows(dev_rows[u], bits)
+        bad = got != want
+        if bad.any():
+            i, j = np.nonzero(bad)
+            t = (L[i, j] - st.qmin32[u, j]) / st.qscale32[u, j]
+            assert all(abs((tt - np.floor(tt)) - 0.5) <= 1e-6 * (2 ** int(bits[jj]) - 1)
+                       for tt, jj in zip(t, j))
+        Lh = O.dequant_dp(got, bits, st.qmin32[u, :r], st.qscale32[u, :r])
+        ref = O.reconstruct(Lh, st.mu32[u], st.V32[u, :, :r])
+        check_recon(ref[None, None], out[b:b + 1, h:h + 1], f"unit {u}")
