@@ -1,0 +1,359 @@
+#!/usr/bin/env python
+"""Benchmark of the transform-coded KV-cache hot path on one MI355X.
+
+Headline workload (batched decode): B=64 sequences, H=8 KV heads, D=128, 8192
+rows already stored per (b, h) through a frozen per-(b, h) basis (rank 96, DP
+bit allocation at 320 bits/token from widths {0, 2, 4, 8}).  One step = append
+one new K row and one new V row per (b, h) (fp64-MFMA project + quantise +
+pack) and fetch every stored K and V row back to fp16 [B, H, S, D]
+(unpack + dequantise + fp16-MFMA reconstruct).  Inputs are resident in HBM
+before the timed region.  ``value`` is fetched positions per second
+(B * H * S per step, K and V of one position counted once).
+
+Prints one JSON line.  ``roofline`` reports the fetch kernel (the dominant
+launch): algorithmic bytes per launch / mean launch time measured with HIP
+events on the launch stream, against 8 TB/s.  ``cpu_baseline`` times the CPU
+oracle on a bounded sample of the same units.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import re
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_HBM_GBPS = 8000.0
+PMC_SUMMARY = os.path.join(ROOT, "profiles", "fetch_batched_decode_pmc.txt")
+DEVICE_SRC = os.path.join(ROOT, "kv_cache_compression_kvtc_amd", "csrc", "kvtc_device.hip")
+
+
+def parse():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=20)
+    p.add_argument("--warmup", type=int, default=3)
+    p.add_argument("--cpu-seconds", type=float, default=10.0, help="oracle sample budget")
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--extra", action="store_true", help="also time the other workloads")
+    p.add_argument("--copy-calibration", action="store_true",
+                   help="only run a device copy of known size (for HBM counter scaling)")
+    return p.parse_args()
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def source_hash() -> str:
+    return hashlib.sha256(open(DEVICE_SRC, "rb").read()).hexdigest()[:16]
+
+
+def pmc_traffic():
+    """HBM bytes per fetch launch from the committed counter summary, if it was
+    taken on the current kernel source."""
+    if not os.path.exists(PMC_SUMMARY):
+        return None
+    text = open(PMC_SUMMARY).read()
+    m_hash = re.search(r"kernel_source_sha256_16:\s*([0-9a-f]+)", text)
+    m_val = re.search(r"hbm_bytes_per_fetch_launch:\s*([0-9.eE+]+)", text)
+    if not m_hash or not m_val or m_hash.group(1) != source_hash():
+        return None
+    return float(m_val.group(1))
+
+
+# ------------------------------------------------------------------ copy calibration
+def copy_calibration():
+    import torch
+    n = 1 << 30
+    a = torch.empty(n, dtype=torch.uint8, device="cuda:0")
+    a.fill_(3)
+    b = torch.empty_like(a)
+    for _ in range(5):
+        b.copy_(a)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_bytes_each_way": n, "launches": 5}))
+
+
+# ------------------------------------------------------------------ workloads
+class TensorPath:
+    """One tensor (K or V) of a workload on the device: blob, store, rows, output."""
+
+    def __init__(self, K, w, tensor, s_fit, s_total, capacity, dev, x_host=None):
+        import torch
+        from kv_cache_compression_kvtc_amd import synth
+        X = x_host if x_host is not None else synth.generate(w, tensor, 0, s_total)
+        cfg = K.make_config(w.mode, w.D, w.heads_per_unit, w.rank, w.energy, w.budget, w.choices,
+                            w.beta, w.hi_bits, w.lo_bits, w.group_size, w.hi_fraction)
+        t = time.time()
+        self.blob = K.kvtc_fit_host(cfg, np.ascontiguousarray(X[:, :, :s_fit]))
+        self.fit_s = time.time() - t
+        self.h = K.header(self.blob)
+        self.K = K
+        self.cap = capacity
+        self.blob_dev = torch.from_numpy(self.blob).to(dev)
+        cb, pb = K.kvtc_store_bytes(self.blob, capacity)
+        self.codes = torch.zeros(max(cb, 4), dtype=torch.uint8, device=dev)
+        self.params = torch.zeros(max(pb // 4, 1), dtype=torch.int32, device=dev) if pb else None
+        self.x = torch.from_numpy(X).to(dev)
+        self.out = torch.empty((w.B, w.H, capacity, w.D), dtype=torch.float16, device=dev)
+        del X
+
+    def append(self, s0, s1):
+        self.K.kvtc_append(self.blob, self.blob_dev, self.x[:, :, s0:s1], s0, self.codes, self.params,
+                           self.cap)
+
+    def fetch(self, s0, s1):
+        self.K.kvtc_fetch(self.blob, self.blob_dev, self.codes, self.params, self.cap, s0, s1,
+                          self.out[:, :, s0:s1])
+
+    # algorithmic bytes: what the method has to move (inputs, codes, outputs, frozen state)
+    def fetch_bytes(self, S):
+        h = self.h
+        per_pos = h.row_stride / h.heads_per_unit + 4 * h.n_qgroups / h.heads_per_unit + 2 * h.head_dim
+        state = h.units * (h.dg * h.kslots * 2 + h.dg * 4 + h.kslots * 4)
+        return h.batch * h.heads * S * per_pos + state
+
+    def append_bytes(self, n, in_bytes=2):
+        h = self.h
+        per_pos = in_bytes * h.head_dim + h.row_stride / h.heads_per_unit + 4 * h.n_qgroups / h.heads_per_unit
+        state = h.units * (h.kslots * h.dg * 4 + h.dg * 4 + h.kslots * 20)
+        return h.batch * h.heads * n * per_pos + state
+
+
+def time_batched_decode(K, args, dev):
+    import torch
+    from kv_cache_compression_kvtc_amd import synth
+    w = synth.WORKLOADS[4]
+    S0 = w.s_prefill
+    s_total = S0 + args.warmup + args.steps
+    paths = []
+    for tensor in (synth.KEY, synth.VALUE):
+        t = time.time()
+        paths.append(TensorPath(K, w, tensor, S0, s_total, s_total, dev))
+        log(f"setup tensor {tensor}: {time.time() - t:.1f}s (fit {paths[-1].fit_s:.1f}s)")
+    for p in paths:
+        p.append(0, S0)                                    # rows already stored (untimed)
+    torch.cuda.synchronize()
+
+    def step(k, evs=None):
+        s = S0 + k
+        for p in paths:
+            p.append(s, s + 1)
+        for p in paths:
+            if evs is not None:
+                a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                a.record()
+                p.fetch(0, s + 1)
+                b.record()
+                evs.append((a, b))
+            else:
+                p.fetch(0, s + 1)
+
+    for k in range(args.warmup):
+        step(k)
+    torch.cuda.synchronize()
+    evs = []
+    t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0.record()
+    for k in range(args.warmup, args.warmup + args.steps):
+        step(k, evs)
+    t1.record()
+    torch.cuda.synchronize()
+    total_ms = t0.elapsed_time(t1)
+    fetch_ms = [a.elapsed_time(b) for a, b in evs]
+    sizes = [S0 + k + 1 for k in range(args.warmup, args.warmup + args.steps)]
+    positions = sum(w.B * w.H * s for s in sizes)
+    fetch_bytes = [p.fetch_bytes(s) for s in sizes for p in paths]
+    append_bytes = sum(p.append_bytes(1) for p in paths) * args.steps
+    h = paths[0].h
+    return dict(w=w, total_ms=total_ms, fetch_ms=fetch_ms, positions=positions,
+                fetch_bytes=fetch_bytes, append_bytes=append_bytes, sizes=sizes, header=h)
+
+
+def time_one_shot(K, wid, dev, reps=5):
+    """Other workloads: one-shot append of the rows after the fit prefix + full fetch."""
+    import torch
+    from kv_cache_compression_kvtc_amd import synth
+    w = synth.WORKLOADS[wid]
+    S = w.s_total
+    paths = [TensorPath(K, w, t, w.s_prefill, S, S, dev) for t in (synth.KEY, synth.VALUE)]
+    a0 = 0 if w.s_prefill == S else w.s_prefill
+    for p in paths:
+        if a0:
+            p.append(0, a0)
+    torch.cuda.synchronize()
+    res = {"append_ms": [], "fetch_ms": []}
+    for r in range(reps + 1):
+        e = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
+        e[0].record()
+        for p in paths:
+            p.append(a0, S)
+        e[1].record()
+        for p in paths:
+            p.fetch(0, S)
+        e[2].record()
+        torch.cuda.synchronize()
+        if r:
+            res["append_ms"].append(e[0].elapsed_time(e[1]))
+            res["fetch_ms"].append(e[1].elapsed_time(e[2]))
+    ap, fe = float(np.median(res["append_ms"])), float(np.median(res["fetch_ms"]))
+    fb = sum(p.fetch_bytes(S) for p in paths)
+    ab = sum(p.append_bytes(S - a0) for p in paths)
+    return {"workload": w.name, "B": w.B, "H": w.H, "D": w.D, "S": S, "append_rows": S - a0,
+            "append_ms": round(ap, 4), "fetch_ms": round(fe, 4),
+            "tokens_per_s": round(w.B * w.H * S / ((ap + fe) / 1e3), 1),
+            "fetch_GBps": round(fb / fe / 1e6, 1), "append_GBps": round(ab / ap / 1e6, 1),
+            "fetch_frac_hbm": round(fb / fe / 1e6 / PEAK_HBM_GBPS, 4)}
+
+
+def time_decode_steps(K, dev, steps=64):
+    """Llama-3-8B-like layer: prefill 4096, then per step append 1 + fetch all."""
+    import torch
+    from kv_cache_compression_kvtc_amd import synth
+    w = synth.WORKLOADS[2]
+    S0 = w.s_prefill
+    cap = S0 + steps + 1
+    paths = [TensorPath(K, w, t, S0, cap, cap, dev) for t in (synth.KEY, synth.VALUE)]
+    for p in paths:
+        p.append(0, S0)
+    torch.cuda.synchronize()
+    times = []
+    for k in range(steps):
+        s = S0 + k
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for p in paths:
+            p.append(s, s + 1)
+        for p in paths:
+            p.fetch(0, s + 1)
+        e1.record()
+        torch.cuda.synchronize()
+        times.append(e0.elapsed_time(e1))
+    med = float(np.median(times[4:]))
+    S = S0 + steps // 2
+    return {"workload": w.name, "B": w.B, "H": w.H, "D": w.D, "S_mid": S, "steps": steps,
+            "median_step_ms": round(med, 4),
+            "tokens_per_s": round(w.B * w.H * S / (med / 1e3), 1),
+            "note": "launch-latency bound: ~20 MB moved per step"}
+
+
+# ------------------------------------------------------------------ CPU oracle baseline
+def cpu_baseline(seconds):
+    """The oracle, as it stands, on whole (b, h) units of the batched-decode workload:
+    per unit and tensor, append the new row and fetch all rows.  Units are independent,
+    so positions/s extrapolate linearly to the full batch."""
+    from oracle import kvtc_oracle as O
+    from kv_cache_compression_kvtc_amd import synth
+    w = synth.WORKLOADS[4]
+    S0 = w.s_prefill
+    cfg = O.Config(mode="dp", head_dim=w.D, rank=w.rank, budget=w.budget, choices=w.choices)
+    threads = None
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max((i.get("num_threads", 1) for i in threadpool_info()), default=1)
+    except Exception:
+        threads = 1
+    rng = np.random.default_rng(7)
+    order = rng.permutation(w.B * w.H)
+    elapsed = 0.0
+    positions = 0
+    units = 0
+    for unit in order:
+        b, hh = divmod(int(unit), w.H)
+        per_unit = 0.0
+        for tensor in (synth.KEY, synth.VALUE):
+            X = synth.unit_rows(w, tensor, b, hh, 0, S0 + 1).astype(np.float16)[None, None]
+            st = O.fit(cfg, X[:, :, :S0])
+            rows, _ = O.append(st, X[:, :, :S0])               # stored rows (setup)
+            t = time.perf_counter()
+            new, _ = O.append(st, X[:, :, S0:])
+            allrows = np.concatenate([rows, new], axis=1)
+            out = O.to_f16(O.fetch(st, allrows))
+            per_unit += time.perf_counter() - t
+        elapsed += per_unit
+        positions += S0 + 1
+        units += 1
+        if elapsed >= seconds and units >= 4:
+            break
+    return {"value": round(positions / elapsed, 1), "unit": "tokens/s", "cores": int(threads),
+            "kind": "oracle",
+            "sample": f"{units} of {w.B * w.H} (b,h) units of the batched-decode workload, K and V: "
+                      f"append 1 row + fetch {S0 + 1} rows each, numpy float64; "
+                      f"{elapsed:.1f}s of CPU time, extrapolates linearly (units independent)"}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}); the path has no "
+              "cross-GPU exchange, see the sharding notes in the design document", file=sys.stderr)
+        sys.exit(2)
+    if args.copy_calibration:
+        copy_calibration()
+        return
+    import torch
+    from kv_cache_compression_kvtc_amd import kvtc as K
+    assert torch.cuda.is_available(), "bench.py needs a HIP device"
+    dev = torch.device("cuda:0")
+
+    r = time_batched_decode(K, args, dev)
+    w, h = r["w"], r["header"]
+    ms_per_step = r["total_ms"] / args.steps
+    value = r["positions"] / (r["total_ms"] / 1e3)
+    total_bytes = sum(r["fetch_bytes"]) + r["append_bytes"]
+    fetch_mean_ms = float(np.mean(r["fetch_ms"]))
+    fetch_bytes_mean = float(np.mean(r["fetch_bytes"]))
+    achieved = fetch_bytes_mean / (fetch_mean_ms / 1e3) / 1e9
+    out = {
+        "metric": "fetch+append tokens/s and achieved HBM GB/s (% of peak) at B*H*S tokens",
+        "value": round(value, 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f16",
+        "data": "synthetic",
+        "config": {"workload": "batched-decode", "B": w.B, "H": w.H, "D": w.D,
+                   "S_stored": w.s_prefill, "S_fetched": [r["sizes"][0], r["sizes"][-1]],
+                   "rank": w.rank, "bit_budget": w.budget, "bit_choices": list(w.choices),
+                   "row_stride_bytes": h.row_stride, "step": "append 1 row/seq (K,V) + fetch all rows (K,V)",
+                   "arithmetic": "fetch fp16 MFMA with fp32 accumulate; append fp64 MFMA",
+                   "parallelism": "single GPU"},
+        "hbm_GBps_step": round(total_bytes / (r["total_ms"] / 1e3) / 1e9, 1),
+        "hbm_frac_step": round(total_bytes / (r["total_ms"] / 1e3) / 1e9 / PEAK_HBM_GBPS, 4),
+        "roofline": {"kernel": "fetch_kernel<dp, 128 columns>", "bound": "hbm",
+                     "achieved": round(achieved, 1), "peak": PEAK_HBM_GBPS, "unit": "GB/s",
+                     "frac": round(achieved / PEAK_HBM_GBPS, 4),
+                     "traffic": pmc_traffic(),
+                     "algorithmic_bytes_per_launch": round(fetch_bytes_mean),
+                     "mean_launch_ms": round(fetch_mean_ms, 4),
+                     "launches": len(r["fetch_ms"])},
+    }
+    if args.extra:
+        extra = []
+        for fn in (lambda: time_one_shot(K, 5, dev), lambda: time_one_shot(K, 3, dev),
+                   lambda: time_decode_steps(K, dev)):
+            torch.cuda.empty_cache()
+            extra.append(fn())
+            log(json.dumps(extra[-1]))
+        out["other_workloads"] = extra
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(args.cpu_seconds)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -109,7 +109,9 @@ typedef struct kvtc_state_header {
     double   beta;
     double   energy_threshold;
     int32_t  rank_cfg;      /* configured rank (0 = energy threshold) */
-    int32_t  reserved0;
+    int32_t  kfetch;        /* fetch contraction length: slots regrouped into 8-slot groups of
+                               one width each (zero-padded where the width changes), rounded
+                               up to 16 */
     int64_t  s_prefill;     /* rows the state was fitted on (0 if built from parts) */
     /* per-unit sections */
     uint64_t off_unit;      /* kvtc_unit_info [units] */
@@ -123,12 +125,15 @@ typedef struct kvtc_state_header {
     uint64_t off_basis;     /* float  [units][kslots][dg] basis vector of slot j (0 = empty) */
     uint64_t off_qlo;       /* double [units][kslots] DP: min of slot j, as stored (fp32 value) */
     uint64_t off_qinv;      /* double [units][kslots] DP: 1/scale of slot j (0 if scale is 0) */
-    uint64_t off_w16;       /* half   [units][dg][kslots] fetch operand: DP scale_j*basis_j,
-                               mixed basis_j, rounded to fp16 */
+    uint64_t off_w16;       /* half   [units][dg][kfetch] fetch operand in fetch-group order:
+                               DP scale_j*basis_j, mixed basis_j, rounded to fp16; 0 for padding */
     uint64_t off_bias;      /* float  [units][dg] fetch bias: DP mu + sum_j min_j*basis_j,
                                mixed mu */
     uint64_t total_bytes;
-    uint64_t reserved[4];
+    uint64_t off_kdesc;     /* uint32 [units][kfetch/8] fetch group g (k = 8g..8g+7): bit offset
+                               of its first field (bits 0-15) | width (16-19, 0 = empty group) |
+                               quantisation group of its slots (20-31, mixed mode) */
+    uint64_t reserved[3];
 } kvtc_state_header;
 
 /* ---------------------------------------------------------- entry points */

@@ -288,27 +288,121 @@ __global__ __launch_bounds__(kThreads) void append_kernel(AppendArgs a) {
     }
 }
 
+// Few-row append (decode): one block per unit and up to 16 rows.  The whole
+// basis of the unit is staged in LDS with every load in flight at once, and the
+// N-blocks are spread over the 4 waves.  Each row goes through exactly the same
+// sequence of fp64 MFMAs (same operands, same k order) as in append_kernel, so
+// a row's codes do not depend on which kernel appended it.
+template <typename XT, int NB>
+__global__ __launch_bounds__(kThreads) void append_small_kernel(AppendArgs a) {
+    extern __shared__ __align__(16) unsigned char smem[];
+    const int xpitch = a.dg + 1, vpitch = a.dg + 1;
+    double *xs = reinterpret_cast<double *>(smem);                       // [16][xpitch]
+    float *vs = reinterpret_cast<float *>(xs + 16 * xpitch);             // [NB*16][vpitch]
+    uint32_t *rows = reinterpret_cast<uint32_t *>(vs + NB * 16 * vpitch);  // [16][row_words]
+
+    const int u = blockIdx.y;
+    const int64_t t0 = static_cast<int64_t>(blockIdx.x) * 16;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int b = u / a.groups, g = u % a.groups;
+    const int nvalid = static_cast<int>(min<int64_t>(16, a.n - t0));
+    const int n_slots = a.ui[u].n_slots;
+    const int row_words = a.row_stride >> 2;
+    const XT *x = static_cast<const XT *>(a.x);
+
+    for (int w = tid; w < 16 * row_words; w += kThreads) rows[w] = 0u;
+    {
+        const float *mu = a.mu + static_cast<int64_t>(u) * a.dg;
+#pragma unroll 4
+        for (int i = tid; i < 16 * a.dg; i += kThreads) {
+            const int t = i / a.dg, d = i - t * a.dg;
+            double v = 0.0;
+            if (t < nvalid) v = load_x(x + b * a.xsb + g * a.xsh + (t0 + t) * a.xss + d) - static_cast<double>(mu[d]);
+            xs[t * xpitch + d] = v;
+        }
+        const int q4 = a.dg / 4;
+        const float *basis = a.basis + static_cast<int64_t>(u) * a.kslots * a.dg;
+#pragma unroll 8
+        for (int i = tid; i < NB * 16 * q4; i += kThreads) {
+            const int slot = i / q4, c = (i - slot * q4) * 4;
+            float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
+            if (slot < a.kslots) v = *reinterpret_cast<const float4 *>(basis + static_cast<int64_t>(slot) * a.dg + c);
+            float *dst = vs + slot * vpitch + c;
+            dst[0] = v.x;
+            dst[1] = v.y;
+            dst[2] = v.z;
+            dst[3] = v.w;
+        }
+    }
+    __syncthreads();
+
+    constexpr int NBW = (NB + 3) / 4;       // N-blocks of this wave: wave, wave+4, ...
+    doublex4 acc[NBW];
+#pragma unroll
+    for (int q = 0; q < NBW; ++q) acc[q] = doublex4{0.0, 0.0, 0.0, 0.0};
+    const int mrow = lane & 15, kcol = lane >> 4;
+    for (int ks = 0; ks < a.dg / 4; ++ks) {
+        const double av = xs[mrow * xpitch + ks * 4 + kcol];
+#pragma unroll
+        for (int q = 0; q < NBW; ++q) {
+            const int nb = wave + 4 * q;
+            if (nb < NB) {
+                const double bv = static_cast<double>(vs[(nb * 16 + (lane & 15)) * vpitch + ks * 4 + kcol]);
+                acc[q] = __builtin_amdgcn_mfma_f64_16x16x4f64(av, bv, acc[q], 0, 0, 0);
+            }
+        }
+    }
+    const int64_t ub = static_cast<int64_t>(u) * a.kslots;
+#pragma unroll
+    for (int q = 0; q < NBW; ++q) {
+        const int nb = wave + 4 * q;
+        const int j = nb * 16 + (lane & 15);
+        if (nb < NB && j < n_slots) {
+            const double lo = a.qlo[ub + j], inv = a.qinv[ub + j];
+            const uint32_t sb = a.sbits[ub + j];
+            const uint32_t off = sb & kOffsetMask, w = sb >> 24;
+            const double cmax = static_cast<double>((1u << w) - 1u);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int t = (lane >> 4) + 4 * i;
+                if (t < nvalid) {
+                    const uint32_t c = static_cast<uint32_t>(quantise(acc[q][i], lo, inv, cmax));
+                    or_field(rows + t * row_words, off, w, c);
+                }
+            }
+        }
+    }
+    __syncthreads();
+    if (row_words > 0) {
+        uint32_t *dst = reinterpret_cast<uint32_t *>(
+            a.codes + (static_cast<int64_t>(u) * a.capacity + a.s0 + t0) * a.row_stride);
+        for (int w = tid; w < nvalid * row_words; w += kThreads) dst[w] = rows[w];
+    }
+}
+
 // ================================================================ fetch
 struct FetchArgs {
     const uint8_t *codes;              // [U][capacity][row_stride]
     const uint32_t *params;            // [U][capacity][n_qg] (min16 | scale16 << 16)
     int64_t capacity, s_begin, s_end;
-    const uint16_t *w16;               // [U][dg][kslots]
+    const uint16_t *w16;               // [U][dg][kfetch]
     const float *bias;                 // [U][dg]
-    const uint32_t *sbits;             // [U][kslots]
+    const uint32_t *kdesc;             // [U][kfetch/8]
     _Float16 *out;
     int64_t osb, osh, oss;             // element strides of out (d stride is 1)
-    int dg, D, hpu, groups, kslots, row_stride, n_qg, gs;
+    int dg, D, hpu, groups, kfetch, row_stride, n_qg;
     int nslices, nchunks, tiles_per_block, ntiles;
     int64_t nblocks_real, nblocks_per_xcd;
     // dynamic LDS carve-up (bytes)
-    int lds_w, lds_kmap, lds_bias, lds_wave, lds_rows, lds_par, lds_out, wpitch, opitch;
+    int lds_w, lds_desc, lds_bias, lds_wave, lds_rows, lds_par, lds_out, wpitch, opitch;
 };
+
+typedef _Float16 half2 __attribute__((ext_vector_type(2)));
 
 // One block: one (unit, d-slice of 32*NDB columns), a run of 32-token tiles;
 // each wave reconstructs whole tiles.  MFMA operands: A = W rows (d), B =
-// per-token code values (slots), C[d][token] accumulates in fp32.
-template <bool MIXED, int NDB>
+// per-token code values (fetch slots), C[d][token] accumulates in fp32.
+template <bool MIXED, int NDB, int KS>
 __global__ __launch_bounds__(kThreads) void fetch_kernel(FetchArgs a) {
     extern __shared__ __align__(16) unsigned char smem[];
     constexpr int DS = 32 * NDB;
@@ -326,56 +420,55 @@ __global__ __launch_bounds__(kThreads) void fetch_kernel(FetchArgs a) {
     const int head = g * a.hpu + d0 / a.D, dd0 = d0 % a.D;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int row_words = a.row_stride >> 2;
-    const int rw1 = row_words + 1;
 
     _Float16 *wl = reinterpret_cast<_Float16 *>(smem + a.lds_w);       // [DS][wpitch]
-    uint32_t *kmap = reinterpret_cast<uint32_t *>(smem + a.lds_kmap);   // [kslots]
+    uint32_t *descl = reinterpret_cast<uint32_t *>(smem + a.lds_desc);  // [kfetch/8]
     float *biasl = reinterpret_cast<float *>(smem + a.lds_bias);        // [DS]
     unsigned char *wbase = smem + a.lds_wave + wave * a.lds_rows;
-    uint32_t *rowsl = reinterpret_cast<uint32_t *>(wbase);              // [32][rw1]
+    uint32_t *rowsl = reinterpret_cast<uint32_t *>(wbase);              // [32*row_words + 2]
     uint32_t *parl = reinterpret_cast<uint32_t *>(wbase + a.lds_par);   // [32][n_qg]
     _Float16 *outl = reinterpret_cast<_Float16 *>(wbase + a.lds_out);   // [32][opitch]
 
-    // stage this slice of W, the slot map and the bias
+    // stage this slice of W, the group descriptors and the bias
     {
-        const uint16_t *src = a.w16 + (static_cast<int64_t>(u) * a.dg + d0) * a.kslots;
-        const int vec_per_row = a.kslots / 8;
+        const uint16_t *src = a.w16 + (static_cast<int64_t>(u) * a.dg + d0) * a.kfetch;
+        const int vec_per_row = a.kfetch / 8;
+#pragma unroll 4
         for (int i = tid; i < DS * vec_per_row; i += kThreads) {
             const int r = i / vec_per_row, c = i - r * vec_per_row;
-            const u32x4 v = *reinterpret_cast<const u32x4 *>(src + r * a.kslots + c * 8);
+            const u32x4 v = *reinterpret_cast<const u32x4 *>(src + r * a.kfetch + c * 8);
             *reinterpret_cast<u32x4 *>(wl + r * a.wpitch + c * 8) = v;
         }
-        for (int i = tid; i < a.kslots; i += kThreads) kmap[i] = a.sbits[static_cast<int64_t>(u) * a.kslots + i];
+        const int ngr = a.kfetch / kGroup;
+        for (int i = tid; i < ngr; i += kThreads) descl[i] = a.kdesc[static_cast<int64_t>(u) * ngr + i];
         for (int i = tid; i < DS; i += kThreads) biasl[i] = a.bias[static_cast<int64_t>(u) * a.dg + d0 + i];
     }
     __syncthreads();
 
     const int tile_begin = chunk * a.tiles_per_block;
     const int tile_end = min(a.ntiles, tile_begin + a.tiles_per_block);
-    const int tw = row_words + (MIXED ? a.n_qg : 0);      // words per token
-    const int tile_words = kFetTok * tw;
+    const int row_tile_words = kFetTok * row_words;
+    const int tile_words = row_tile_words + (MIXED ? kFetTok * a.n_qg : 0);
     const int64_t ubase = static_cast<int64_t>(u) * a.capacity;
     const uint32_t *codes32 = reinterpret_cast<const uint32_t *>(a.codes);
 
+    // rows (then params) of one tile into registers: word i of the tile's rows
+    // is row word i of the store from the tile's first row; zero past the end
     uint32_t reg[kFetchRegWords];
-    // rows (then params) of one tile into registers; word i of the tile is
-    // token i / row_words (params: token i / n_qg), zero-filled past the end
     auto fetch_tile = [&](int tile) {
         const int64_t s = a.s_begin + static_cast<int64_t>(tile) * kFetTok;
         const int valid = static_cast<int>(min<int64_t>(kFetTok, a.s_end - s));
         const uint32_t *src = codes32 + (ubase + s) * row_words;
         const uint32_t *psrc = MIXED ? a.params + (ubase + s) * a.n_qg : nullptr;
+        const int vrow = valid * row_words, vpar = MIXED ? valid * a.n_qg : 0;
 #pragma unroll
         for (int k = 0; k < kFetchRegWords; ++k) {
             const int i = k * 64 + lane;
             uint32_t v = 0u;
-            if (i < tile_words) {
-                if (i < kFetTok * row_words) {
-                    if (i < valid * row_words) v = src[i];
-                } else if (MIXED) {
-                    const int pi = i - kFetTok * row_words;
-                    if (pi < valid * a.n_qg) v = psrc[pi];
-                }
+            if (i < row_tile_words) {
+                if (i < vrow) v = src[i];
+            } else if (MIXED && i < tile_words) {
+                if (i - row_tile_words < vpar) v = psrc[i - row_tile_words];
             }
             reg[k] = v;
         }
@@ -384,20 +477,23 @@ __global__ __launch_bounds__(kThreads) void fetch_kernel(FetchArgs a) {
 #pragma unroll
         for (int k = 0; k < kFetchRegWords; ++k) {
             const int i = k * 64 + lane;
-            if (i < tile_words) {
-                if (i < kFetTok * row_words) {
-                    const int t = i / row_words;
-                    rowsl[t * rw1 + (i - t * row_words)] = reg[k];
-                } else if (MIXED) {
-                    parl[i - kFetTok * row_words] = reg[k];
-                }
-            }
+            if (i < row_tile_words) rowsl[i] = reg[k];
+            else if (MIXED && i < tile_words) parl[i - row_tile_words] = reg[k];
         }
     };
 
     const int tok = lane & 31;            // B-operand column / C column of this lane
-    const int khalf = (lane >> 5) * 8;    // first of the 8 slots this lane feeds per step
-    const int ksteps = a.kslots / 16;
+    const int half_k = lane >> 5;         // this lane feeds fetch group 2*ks + half_k
+
+    // per-lane unpack program, the same for every tile of the block: word index,
+    // shift and width of the group's 64-bit field window, quantisation group
+    uint32_t prog[KS];
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+        const uint32_t desc = descl[2 * ks + half_k];
+        const uint32_t off0 = desc & 0xFFFFu;
+        prog[ks] = (off0 >> 5) | ((off0 & 31u) << 8) | (desc & 0xFFFF0000u);
+    }
 
     int tile = tile_begin + wave;
     if (tile < tile_end) fetch_tile(tile);
@@ -414,29 +510,46 @@ __global__ __launch_bounds__(kThreads) void fetch_kernel(FetchArgs a) {
 #pragma unroll
             for (int i = 0; i < 16; ++i) acc[db][i] = 0.0f;
 
-        const uint32_t *myrow = rowsl + tok * rw1;
-        for (int ks = 0; ks < ksteps; ++ks) {
-            half8 bv;
+        const uint32_t *myrow = rowsl + tok * row_words;
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) {
+            const uint32_t pg = prog[ks];
+            const uint32_t wi = pg & 0xFFu, sh = (pg >> 8) & 31u, w = (pg >> 16) & 0xFu;
+            const uint32_t r0 = myrow[wi], r1 = myrow[wi + 1], r2 = myrow[wi + 2];
+            const uint32_t lo = __builtin_amdgcn_alignbit(r1, r0, sh);
+            const uint32_t hi = __builtin_amdgcn_alignbit(r2, r1, sh);
+            // field e sits at bit e*w of the window; only 8-bit fields reach the high word
+            const bool wide = w == 8u;
+            const uint32_t hsrc = wide ? hi : lo;
+            const uint32_t hadj = wide ? 32u : 0u;
+            uint32_t c[8];
 #pragma unroll
             for (int e = 0; e < 8; ++e) {
-                const int slot = ks * 16 + khalf + e;
-                const uint32_t km = kmap[slot];
-                const uint32_t off = km & kOffsetMask, w = km >> 24;
-                const uint32_t wi = off >> 5;
-                const uint32_t v = __builtin_amdgcn_alignbit(myrow[wi + 1], myrow[wi], off & 31u);
-                const uint32_t c = v & ((1u << w) - 1u);
-                if constexpr (MIXED) {
-                    const uint32_t p = parl[tok * a.n_qg + slot / a.gs];
-                    const float mn = static_cast<float>(__builtin_bit_cast(_Float16, static_cast<uint16_t>(p & 0xFFFFu)));
-                    const float sc = static_cast<float>(__builtin_bit_cast(_Float16, static_cast<uint16_t>(p >> 16)));
-                    bv[e] = static_cast<_Float16>(__builtin_fmaf(static_cast<float>(c), sc, mn));
-                } else {
-                    bv[e] = static_cast<_Float16>(static_cast<float>(c));
+                if (e < 4) c[e] = __builtin_amdgcn_ubfe(lo, e * w, w);
+                else c[e] = __builtin_amdgcn_ubfe(hsrc, e * w - hadj, w);
+            }
+            half8 bv;
+            if constexpr (MIXED) {
+                // dequantised latent min16 + c * scale16, one fp16 rounding (packed fma)
+                const uint32_t p = parl[tok * a.n_qg + (pg >> 20)];
+                const half2 mn2 = __builtin_bit_cast(half2, (p & 0xFFFFu) | (p << 16));
+                const half2 sc2 = __builtin_bit_cast(half2, (p >> 16) | (p & 0xFFFF0000u));
+#pragma unroll
+                for (int e = 0; e < 8; e += 2) {
+                    half2 cv;
+                    cv[0] = static_cast<_Float16>(static_cast<uint16_t>(c[e]));
+                    cv[1] = static_cast<_Float16>(static_cast<uint16_t>(c[e + 1]));
+                    const half2 r = __builtin_elementwise_fma(cv, sc2, mn2);
+                    bv[e] = r[0];
+                    bv[e + 1] = r[1];
                 }
+            } else {
+#pragma unroll
+                for (int e = 0; e < 8; ++e) bv[e] = static_cast<_Float16>(static_cast<uint16_t>(c[e]));
             }
 #pragma unroll
             for (int db = 0; db < NDB; ++db) {
-                const half8 av = *reinterpret_cast<const half8 *>(wl + (db * 32 + tok) * a.wpitch + ks * 16 + khalf);
+                const half8 av = *reinterpret_cast<const half8 *>(wl + (db * 32 + tok) * a.wpitch + ks * 16 + half_k * 8);
                 acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_f16(av, bv, acc[db], 0, 0, 0);
             }
         }
@@ -491,8 +604,45 @@ int32_t launch_append_nb(const AppendArgs &a, int64_t ntiles, int64_t U, hipStre
     return hipGetLastError() == hipSuccess ? KVTC_OK : KVTC_E_DEVICE;
 }
 
+constexpr int kSmallRows = 16;
+constexpr size_t kSmallLdsLimit = 96 * 1024;
+
+size_t small_lds_bytes(int dg, int nb, int row_stride) {
+    return 16 * static_cast<size_t>(dg + 1) * sizeof(double) + static_cast<size_t>(nb) * 16 * (dg + 1) * sizeof(float) +
+           16 * static_cast<size_t>(row_stride / 4) * sizeof(uint32_t);
+}
+
+template <typename XT, int NB>
+int32_t launch_small_nb(const AppendArgs &a, int64_t U, hipStream_t stream) {
+    const size_t lds = small_lds_bytes(a.dg, NB, a.row_stride);
+    auto kern = append_small_kernel<XT, NB>;
+    if (hipFuncSetAttribute(reinterpret_cast<const void *>(kern), hipFuncAttributeMaxDynamicSharedMemorySize,
+                            static_cast<int>(lds)) != hipSuccess)
+        return KVTC_E_DEVICE;
+    const int64_t blocks = (a.n + kSmallRows - 1) / kSmallRows;
+    hipLaunchKernelGGL(kern, dim3(static_cast<unsigned>(blocks), static_cast<unsigned>(U)), dim3(kThreads), lds,
+                       stream, a);
+    return hipGetLastError() == hipSuccess ? KVTC_OK : KVTC_E_DEVICE;
+}
+
+template <typename XT>
+int32_t launch_small(const AppendArgs &a, int64_t U, int nb, hipStream_t st) {
+    switch (nb) {
+        case 1: return launch_small_nb<XT, 1>(a, U, st);
+        case 2: return launch_small_nb<XT, 2>(a, U, st);
+        case 4: return launch_small_nb<XT, 4>(a, U, st);
+        case 6: return launch_small_nb<XT, 6>(a, U, st);
+        case 8: return launch_small_nb<XT, 8>(a, U, st);
+        case 12: return launch_small_nb<XT, 12>(a, U, st);
+        case 16: return launch_small_nb<XT, 16>(a, U, st);
+        default: return KVTC_E_SHAPE;
+    }
+}
+
 template <bool MIXED, typename XT>
 int32_t launch_append(const AppendArgs &a, int64_t ntiles, int64_t U, int nb, hipStream_t st) {
+    if (!MIXED && a.n <= kSmallRows && small_lds_bytes(a.dg, nb, a.row_stride) <= kSmallLdsLimit)
+        return launch_small<XT>(a, U, nb, st);
     switch (nb) {
         case 1: return launch_append_nb<MIXED, XT, 1>(a, ntiles, U, st);
         case 2: return launch_append_nb<MIXED, XT, 2>(a, ntiles, U, st);
@@ -505,16 +655,17 @@ int32_t launch_append(const AppendArgs &a, int64_t ntiles, int64_t U, int nb, hi
     }
 }
 
-template <bool MIXED, int NDB>
-int32_t launch_fetch(FetchArgs a, hipStream_t stream) {
+template <bool MIXED, int NDB, int KS>
+int32_t launch_fetch_ks(FetchArgs a, hipStream_t stream) {
     constexpr int DS = 32 * NDB;
-    a.wpitch = a.kslots + 8;
+    a.wpitch = a.kfetch + 8;
     a.opitch = DS + 8;
     a.lds_w = 0;
-    a.lds_kmap = static_cast<int>(align_up(static_cast<uint64_t>(DS) * a.wpitch * 2, 16));
-    a.lds_bias = static_cast<int>(align_up(a.lds_kmap + a.kslots * 4, 16));
+    a.lds_desc = static_cast<int>(align_up(static_cast<uint64_t>(DS) * a.wpitch * 2, 16));
+    a.lds_bias = static_cast<int>(align_up(a.lds_desc + (a.kfetch / kGroup) * 4, 16));
     a.lds_wave = static_cast<int>(align_up(a.lds_bias + DS * 4, 16));
-    const int rows_b = static_cast<int>(align_up(kFetTok * (a.row_stride / 4 + 1) * 4, 16));
+    // rows of a tile back to back, plus two words of slack for the 3-word field window
+    const int rows_b = static_cast<int>(align_up((kFetTok * (a.row_stride / 4) + 2) * 4, 16));
     const int par_b = MIXED ? static_cast<int>(align_up(kFetTok * a.n_qg * 4, 16)) : 0;
     const int out_b = static_cast<int>(align_up(kFetTok * a.opitch * 2, 16));
     a.lds_par = rows_b;
@@ -523,12 +674,35 @@ int32_t launch_fetch(FetchArgs a, hipStream_t stream) {
     const size_t lds = a.lds_wave + 4 * static_cast<size_t>(a.lds_rows);
     if (lds > 160 * 1024) return KVTC_E_SHAPE;
     const int64_t grid = a.nblocks_per_xcd * 8;
-    auto kern = fetch_kernel<MIXED, NDB>;
+    auto kern = fetch_kernel<MIXED, NDB, KS>;
     if (hipFuncSetAttribute(reinterpret_cast<const void *>(kern), hipFuncAttributeMaxDynamicSharedMemorySize,
                             static_cast<int>(lds)) != hipSuccess)
         return KVTC_E_DEVICE;
     hipLaunchKernelGGL(kern, dim3(static_cast<unsigned>(grid)), dim3(kThreads), lds, stream, a);
     return hipGetLastError() == hipSuccess ? KVTC_OK : KVTC_E_DEVICE;
+}
+
+template <bool MIXED, int NDB>
+int32_t launch_fetch(FetchArgs a, hipStream_t stream) {
+    switch (a.kfetch / 16) {
+        case 1: return launch_fetch_ks<MIXED, NDB, 1>(a, stream);
+        case 2: return launch_fetch_ks<MIXED, NDB, 2>(a, stream);
+        case 3: return launch_fetch_ks<MIXED, NDB, 3>(a, stream);
+        case 4: return launch_fetch_ks<MIXED, NDB, 4>(a, stream);
+        case 5: return launch_fetch_ks<MIXED, NDB, 5>(a, stream);
+        case 6: return launch_fetch_ks<MIXED, NDB, 6>(a, stream);
+        case 7: return launch_fetch_ks<MIXED, NDB, 7>(a, stream);
+        case 8: return launch_fetch_ks<MIXED, NDB, 8>(a, stream);
+        case 9: return launch_fetch_ks<MIXED, NDB, 9>(a, stream);
+        case 10: return launch_fetch_ks<MIXED, NDB, 10>(a, stream);
+        case 11: return launch_fetch_ks<MIXED, NDB, 11>(a, stream);
+        case 12: return launch_fetch_ks<MIXED, NDB, 12>(a, stream);
+        case 13: return launch_fetch_ks<MIXED, NDB, 13>(a, stream);
+        case 14: return launch_fetch_ks<MIXED, NDB, 14>(a, stream);
+        case 15: return launch_fetch_ks<MIXED, NDB, 15>(a, stream);
+        case 16: return launch_fetch_ks<MIXED, NDB, 16>(a, stream);
+        default: return KVTC_E_SHAPE;
+    }
 }
 
 }  // namespace
@@ -609,7 +783,7 @@ int32_t kvtc_fetch(const void *state_host, const void *state_dev, const void *co
     if (out_strides[3] != 1 || out_strides[0] < 0 || out_strides[1] < 0 || out_strides[2] < 0)
         return KVTC_E_SHAPE;
     const bool mixed = h->mode == KVTC_MODE_MIXED;
-    if (h->kslots > kMaxSlots || h->head_dim % 64 != 0) return KVTC_E_SHAPE;
+    if (h->kfetch > kMaxSlots || h->head_dim % 64 != 0) return KVTC_E_SHAPE;
     const int tw = h->row_stride / 4 + (mixed ? h->n_qgroups : 0);
     if (kFetTok * tw > 64 * kFetchRegWords) return KVTC_E_SHAPE;
     if (s_end == s_begin) return KVTC_OK;
@@ -627,7 +801,7 @@ int32_t kvtc_fetch(const void *state_host, const void *state_dev, const void *co
     a.s_end = s_end;
     a.w16 = reinterpret_cast<const uint16_t *>(sd + h->off_w16);
     a.bias = reinterpret_cast<const float *>(sd + h->off_bias);
-    a.sbits = reinterpret_cast<const uint32_t *>(sd + h->off_slot_bits);
+    a.kdesc = reinterpret_cast<const uint32_t *>(sd + h->off_kdesc);
     a.out = static_cast<_Float16 *>(out_dev);
     a.osb = out_strides[0];
     a.osh = out_strides[1];
@@ -636,17 +810,16 @@ int32_t kvtc_fetch(const void *state_host, const void *state_dev, const void *co
     a.D = h->head_dim;
     a.hpu = h->heads_per_unit;
     a.groups = static_cast<int>(h->heads / h->heads_per_unit);
-    a.kslots = h->kslots;
+    a.kfetch = h->kfetch;
     a.row_stride = h->row_stride;
     a.n_qg = h->n_qgroups;
-    a.gs = h->group_size;
     const int DS = (h->head_dim % 128 == 0) ? 128 : 64;
     a.nslices = h->dg / DS;
     const int64_t ntiles = (s_end - s_begin + kFetTok - 1) / kFetTok;
     if (ntiles > 0x7FFFFFFF) return KVTC_E_SHAPE;
     a.ntiles = static_cast<int>(ntiles);
     const int64_t work = h->units * a.nslices * ntiles;
-    int64_t tpb = std::max<int64_t>(4, (work + 2047) / 2048);
+    int64_t tpb = std::max<int64_t>(4, (work + 1023) / 1024);
     tpb = std::min<int64_t>(tpb, ntiles);
     a.tiles_per_block = static_cast<int>(tpb);
     a.nchunks = static_cast<int>((ntiles + tpb - 1) / tpb);

@@ -478,10 +478,10 @@ void frozen_ranges(const std::vector<double> &Xraw, int64_t S, int dg, const flo
 // -------------------------------------------------------------- blob build
 struct Layout {
     uint64_t off_unit, off_lambda, off_bits, off_qmin, off_qscale, off_mu, off_slot_comp,
-        off_slot_bits, off_basis, off_qlo, off_qinv, off_w16, off_bias, total;
+        off_slot_bits, off_basis, off_qlo, off_qinv, off_w16, off_bias, off_kdesc, total;
 };
 
-Layout plan_layout(int64_t U, int dg, int rmax, int kslots) {
+Layout plan_layout(int64_t U, int dg, int rmax, int kslots, int kfetch) {
     Layout L{};
     uint64_t o = align_up(sizeof(kvtc_state_header), kSectionAlign);
     auto take = [&](uint64_t bytes) {
@@ -500,8 +500,9 @@ Layout plan_layout(int64_t U, int dg, int rmax, int kslots) {
     L.off_basis = take(U * static_cast<uint64_t>(kslots) * dg * sizeof(float));
     L.off_qlo = take(U * kslots * sizeof(double));
     L.off_qinv = take(U * kslots * sizeof(double));
-    L.off_w16 = take(U * static_cast<uint64_t>(kslots) * dg * sizeof(uint16_t));
+    L.off_w16 = take(U * static_cast<uint64_t>(kfetch) * dg * sizeof(uint16_t));
     L.off_bias = take(U * dg * sizeof(float));
+    L.off_kdesc = take(U * static_cast<uint64_t>(kfetch / kGroup) * sizeof(uint32_t));
     L.total = o;
     return L;
 }
@@ -547,8 +548,30 @@ int32_t build_blob(const kvtc_config *cfg, int64_t B, int64_t H, int32_t rmax, c
         max_slots = std::max(max_slots, n_slots[u]);
         max_bits = std::max(max_bits, row_bits[u]);
     }
+    if (max_bits > 0xFFFF) return KVTC_E_CONFIG;
+    // fetch groups: every run of equal widths among the stored slots is cut into
+    // groups of 8 (the last one zero-padded), so that each group is one width
+    std::vector<int> n_groups(U, 0);
+    for (int64_t u = 0; u < U; ++u) {
+        const uint8_t *bu = &bits[static_cast<size_t>(u) * rmax];
+        int run = 0, prev = -1, groups = 0;
+        for (int i = 0; i < ranks[u]; ++i) {
+            if (!bu[i]) continue;
+            if (bu[i] != prev) {
+                groups += (run + kGroup - 1) / kGroup;
+                run = 0;
+                prev = bu[i];
+            }
+            ++run;
+        }
+        groups += (run + kGroup - 1) / kGroup;
+        n_groups[u] = groups;
+    }
+    int max_groups = 0;
+    for (int64_t u = 0; u < U; ++u) max_groups = std::max(max_groups, n_groups[u]);
     const int kslots = std::max<int>(kSlotAlign, static_cast<int>(align_up(max_slots, kSlotAlign)));
-    const Layout L = plan_layout(U, dg, rmax, kslots);
+    const int kfetch = std::max<int>(kSlotAlign, static_cast<int>(align_up(kGroup * max_groups, kSlotAlign)));
+    const Layout L = plan_layout(U, dg, rmax, kslots, kfetch);
     if (state_out == nullptr || *state_bytes < L.total) {
         *state_bytes = L.total;
         return state_out == nullptr ? KVTC_OK : KVTC_E_BUFSIZE;
@@ -579,6 +602,7 @@ int32_t build_blob(const kvtc_config *cfg, int64_t B, int64_t H, int32_t rmax, c
     h->beta = cfg->beta;
     h->energy_threshold = cfg->energy_threshold;
     h->rank_cfg = cfg->rank;
+    h->kfetch = kfetch;
     h->s_prefill = s_prefill;
     h->off_unit = L.off_unit;
     h->off_lambda = L.off_lambda;
@@ -593,6 +617,7 @@ int32_t build_blob(const kvtc_config *cfg, int64_t B, int64_t H, int32_t rmax, c
     h->off_qinv = L.off_qinv;
     h->off_w16 = L.off_w16;
     h->off_bias = L.off_bias;
+    h->off_kdesc = L.off_kdesc;
     h->total_bytes = L.total;
 
     auto *ui = section_mut<kvtc_unit_info>(state_out, L.off_unit);
@@ -608,6 +633,7 @@ int32_t build_blob(const kvtc_config *cfg, int64_t B, int64_t H, int32_t rmax, c
     auto *sqinv = section_mut<double>(state_out, L.off_qinv);
     auto *w16 = section_mut<uint16_t>(state_out, L.off_w16);
     auto *bias = section_mut<float>(state_out, L.off_bias);
+    auto *kdesc = section_mut<uint32_t>(state_out, L.off_kdesc);
 
     parallel_for(U, [&](int64_t u) {
         const int r = ranks[u];
@@ -623,6 +649,9 @@ int32_t build_blob(const kvtc_config *cfg, int64_t B, int64_t H, int32_t rmax, c
         for (int d = 0; d < dg; ++d) bacc[d] = mu[u * dg + d];
         int j = 0;
         uint32_t off = 0;
+        int k = 0;               // next fetch slot (8k-aligned at every width change)
+        int prev_w = -1;
+        int in_group = 0;
         for (int i = 0; i < rmax; ++i) {
             const size_t ci = static_cast<size_t>(u) * rmax + i;
             bits_o[ci] = bu[i];
@@ -645,9 +674,19 @@ int32_t build_blob(const kvtc_config *cfg, int64_t B, int64_t H, int32_t rmax, c
                 wscale = static_cast<double>(qscale[ci]);
                 for (int d = 0; d < dg; ++d) bacc[d] += static_cast<double>(qmin[ci]) * src[d];
             }
+            if (bu[i] != prev_w || in_group == kGroup) {
+                if (in_group) k = static_cast<int>(align_up(k, kGroup));
+                const uint32_t qg = cfg->mode == KVTC_MODE_MIXED ? static_cast<uint32_t>(j / cfg->group_size) : 0u;
+                kdesc[static_cast<size_t>(u) * (kfetch / kGroup) + k / kGroup] =
+                    ((off - bu[i]) & 0xFFFFu) | (static_cast<uint32_t>(bu[i]) << 16) | (qg << 20);
+                prev_w = bu[i];
+                in_group = 0;
+            }
             for (int d = 0; d < dg; ++d)
-                w16[(static_cast<size_t>(u) * dg + d) * kslots + j] =
+                w16[(static_cast<size_t>(u) * dg + d) * kfetch + k] =
                     half_bits_rne(wscale * static_cast<double>(src[d]));
+            ++k;
+            ++in_group;
             ++j;
         }
         for (; j < kslots; ++j) scomp[static_cast<size_t>(u) * kslots + j] = -1;

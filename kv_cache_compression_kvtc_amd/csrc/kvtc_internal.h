@@ -13,6 +13,7 @@ namespace kvtc {
 constexpr int kSlotAlign = 16;          // slots per unit are padded to a multiple of this
 constexpr int kSectionAlign = 256;      // blob sections start on this boundary
 constexpr uint32_t kOffsetMask = 0xFFFFFFu;
+constexpr int kGroup = 8;               // slots per fetch group (one MFMA operand half)
 
 inline uint64_t align_up(uint64_t x, uint64_t a) { return (x + a - 1) / a * a; }
 
@@ -38,12 +39,13 @@ inline int32_t check_state(const void *blob, const kvtc_state_header **out) {
         h->units != h->batch * (h->heads / h->heads_per_unit))
         return KVTC_E_STATE;
     if (h->rmax <= 0 || h->rmax > h->dg || h->kslots < kSlotAlign || h->kslots % kSlotAlign != 0 ||
-        h->row_stride < 0 || h->row_stride % 4 != 0)
+        h->row_stride < 0 || h->row_stride % 4 != 0 || h->kfetch < kSlotAlign ||
+        h->kfetch % kSlotAlign != 0)
         return KVTC_E_STATE;
     if (h->mode == KVTC_MODE_MIXED && (h->n_qgroups <= 0 || h->group_size <= 0)) return KVTC_E_STATE;
     const uint64_t offs[] = {h->off_unit, h->off_lambda, h->off_bits, h->off_qmin, h->off_qscale,
                              h->off_mu, h->off_slot_comp, h->off_slot_bits, h->off_basis,
-                             h->off_qlo, h->off_qinv, h->off_w16, h->off_bias};
+                             h->off_qlo, h->off_qinv, h->off_w16, h->off_bias, h->off_kdesc};
     for (uint64_t o : offs)
         if (o < sizeof(kvtc_state_header) || o % kSectionAlign != 0 || o >= h->total_bytes)
             return KVTC_E_STATE;

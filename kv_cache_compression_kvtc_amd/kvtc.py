@@ -48,13 +48,13 @@ class StateHeader(C.Structure):
                 ("n_qgroups", C.c_int32), ("group_size", C.c_int32), ("hi_bits", C.c_int32),
                 ("lo_bits", C.c_int32), ("n_hi", C.c_int32), ("bit_budget", C.c_int32),
                 ("n_choices", C.c_int32), ("choices", C.c_int32 * MAX_CHOICES), ("beta", C.c_double),
-                ("energy_threshold", C.c_double), ("rank_cfg", C.c_int32), ("reserved0", C.c_int32),
+                ("energy_threshold", C.c_double), ("rank_cfg", C.c_int32), ("kfetch", C.c_int32),
                 ("s_prefill", C.c_int64), ("off_unit", C.c_uint64), ("off_lambda", C.c_uint64),
                 ("off_bits", C.c_uint64), ("off_qmin", C.c_uint64), ("off_qscale", C.c_uint64),
                 ("off_mu", C.c_uint64), ("off_slot_comp", C.c_uint64), ("off_slot_bits", C.c_uint64),
                 ("off_basis", C.c_uint64), ("off_qlo", C.c_uint64), ("off_qinv", C.c_uint64),
                 ("off_w16", C.c_uint64), ("off_bias", C.c_uint64), ("total_bytes", C.c_uint64),
-                ("reserved", C.c_uint64 * 4)]
+                ("off_kdesc", C.c_uint64), ("reserved", C.c_uint64 * 3)]
 
 
 class BytesReport(C.Structure):
@@ -264,7 +264,7 @@ def state_view(blob: np.ndarray) -> dict:
     h = header(blob)
     if h.magic != MAGIC:
         raise KVTCError(E_STATE, "state_view")
-    U, dg, rmax, ks = h.units, h.dg, h.rmax, h.kslots
+    U, dg, rmax, ks, kf = h.units, h.dg, h.rmax, h.kslots, h.kfetch
 
     def sec(off, dt, shape):
         n = int(np.prod(shape))
@@ -284,6 +284,7 @@ def state_view(blob: np.ndarray) -> dict:
         "basis": sec(h.off_basis, np.float32, (U, ks, dg)),
         "qlo": sec(h.off_qlo, np.float64, (U, ks)),
         "qinv": sec(h.off_qinv, np.float64, (U, ks)),
-        "w16": sec(h.off_w16, np.float16, (U, dg, ks)),
+        "w16": sec(h.off_w16, np.float16, (U, dg, kf)),
+        "kdesc": sec(h.off_kdesc, np.uint32, (U, kf // 8)),
         "bias": sec(h.off_bias, np.float32, (U, dg)),
     }
