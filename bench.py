@@ -45,6 +45,9 @@ def parse():
     p.add_argument("--extra", action="store_true", help="also time the other workloads")
     p.add_argument("--copy-calibration", action="store_true",
                    help="only run a device copy of known size (for HBM counter scaling)")
+    p.add_argument("--pmc-summary", nargs=4, metavar=("FETCH_DIR", "WRITE_DIR", "CAL_FETCH_DIR", "CAL_WRITE_DIR"),
+                   help="write the HBM counter summary of the fetch kernel from four rocprofv3 --pmc "
+                        "csv directories (FETCH_SIZE and WRITE_SIZE of this bench, then of --copy-calibration)")
     return p.parse_args()
 
 
@@ -82,6 +85,53 @@ def copy_calibration():
     print(json.dumps({"copy_bytes_each_way": n, "launches": 5}))
 
 
+def _counter_rows(d):
+    import csv
+    import glob
+    files = glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True)
+    if len(files) != 1:
+        raise SystemExit(f"expected one counter_collection.csv under {d}, found {len(files)}")
+    return list(csv.DictReader(open(files[0])))
+
+
+def pmc_summary(fetch_dir, write_dir, cal_fetch_dir, cal_write_dir):
+    """HBM bytes per fetch launch from FETCH_SIZE / WRITE_SIZE (KiB per dispatch),
+    each scaled so that the device copy of --copy-calibration reads and writes
+    exactly its known size."""
+    def per_kernel(rows, counter, match):
+        return [float(r["Counter_Value"]) for r in rows if r["Counter_Name"] == counter and match(r["Kernel_Name"])]
+    is_fetch = lambda n: "fetch_kernel" in n
+    is_copy = lambda n: "copyBuffer" in n or "copy" in n.lower()
+    copy_kib = (1 << 30) / 1024
+    cal_f = per_kernel(_counter_rows(cal_fetch_dir), "FETCH_SIZE", is_copy)
+    cal_w = per_kernel(_counter_rows(cal_write_dir), "WRITE_SIZE", is_copy)
+    f = per_kernel(_counter_rows(fetch_dir), "FETCH_SIZE", is_fetch)
+    w = per_kernel(_counter_rows(write_dir), "WRITE_SIZE", is_fetch)
+    if not (cal_f and cal_w and f and w):
+        raise SystemExit("missing counter rows")
+    sf = copy_kib / float(np.mean(cal_f))
+    sw = copy_kib / float(np.mean(cal_w))
+    read_b = float(np.mean(f)) * sf * 1024
+    write_b = float(np.mean(w)) * sw * 1024
+    lines = [
+        "# HBM traffic of the fetch kernel, batched-decode workload (B=64, H=8, D=128, S~8195, r=96, 320 bits/token)",
+        "commands (from the repository root, each in a run of its own, csv output):",
+        "  rocprofv3 --pmc FETCH_SIZE -d <fetch_dir> -o bd --output-format csv -- python3 bench.py --steps 3 --warmup 1 --no-cpu-baseline",
+        "  rocprofv3 --pmc WRITE_SIZE -d <write_dir> -o bd --output-format csv -- python3 bench.py --steps 3 --warmup 1 --no-cpu-baseline",
+        "  rocprofv3 --pmc FETCH_SIZE -d <cal_fetch_dir> -o cal --output-format csv -- python3 bench.py --copy-calibration",
+        "  rocprofv3 --pmc WRITE_SIZE -d <cal_write_dir> -o cal --output-format csv -- python3 bench.py --copy-calibration",
+        "  python3 bench.py --pmc-summary <fetch_dir> <write_dir> <cal_fetch_dir> <cal_write_dir>",
+        f"copy calibration (1 GiB device copy): FETCH_SIZE {np.mean(cal_f):.0f} KiB -> scale {sf:.4f}; "
+        f"WRITE_SIZE {np.mean(cal_w):.0f} KiB -> scale {sw:.4f}",
+        f"fetch dispatches: {len(f)} (FETCH_SIZE), {len(w)} (WRITE_SIZE); K and V launches alternate",
+        f"FETCH_SIZE mean {np.mean(f):.1f} KiB -> {read_b / 1e6:.2f} MB read per launch",
+        f"WRITE_SIZE mean {np.mean(w):.1f} KiB -> {write_b / 1e6:.2f} MB written per launch",
+        f"hbm_bytes_per_fetch_launch: {read_b + write_b:.6e}",
+        f"kernel_source_sha256_16: {source_hash()}",
+    ]
+    return "\n".join(lines) + "\n"
+
+
 # ------------------------------------------------------------------ workloads
 class TensorPath:
     """One tensor (K or V) of a workload on the device: blob, store, rows, output."""
@@ -105,14 +155,9 @@ class TensorPath:
         self.x = torch.from_numpy(X).to(dev)
         self.out = torch.empty((w.B, w.H, capacity, w.D), dtype=torch.float16, device=dev)
         del X
-
-    def append(self, s0, s1):
-        self.K.kvtc_append(self.blob, self.blob_dev, self.x[:, :, s0:s1], s0, self.codes, self.params,
-                           self.cap)
-
-    def fetch(self, s0, s1):
-        self.K.kvtc_fetch(self.blob, self.blob_dev, self.codes, self.params, self.cap, s0, s1,
-                          self.out[:, :, s0:s1])
+        # buffers are checked once; each timed call passes only its row range
+        self.append = K.PreparedAppend(self.blob, self.blob_dev, self.x, self.codes, self.params, capacity)
+        self.fetch = K.PreparedFetch(self.blob, self.blob_dev, self.codes, self.params, capacity, self.out)
 
     # algorithmic bytes: what the method has to move (inputs, codes, outputs, frozen state)
     def fetch_bytes(self, S):
@@ -299,6 +344,12 @@ def main():
         sys.exit(2)
     if args.copy_calibration:
         copy_calibration()
+        return
+    if args.pmc_summary:
+        text = pmc_summary(*args.pmc_summary)
+        with open(PMC_SUMMARY, "w") as fh:
+            fh.write(text)
+        print(text, end="")
         return
     import torch
     from kv_cache_compression_kvtc_amd import kvtc as K

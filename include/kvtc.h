@@ -14,9 +14,10 @@
  * Conventions for every entry point:
  *   - all pointers are plain addresses; "host" pointers are CPU memory,
  *     "dev" pointers are device (HBM) memory of the current HIP device;
- *   - the caller owns every buffer; the library allocates no device memory,
- *     keeps no global state and is reentrant; host scratch lives only for
- *     the duration of a call;
+ *   - the caller owns every buffer; the library allocates no device memory
+ *     and is reentrant; host scratch lives only for the duration of a call;
+ *     its only process-wide state is the record of which kernels it has
+ *     already allowed to use a CU's whole LDS (set once per kernel and device);
  *   - device work is enqueued on the given hipStream_t (NULL = the null
  *     stream) and the call returns after the enqueue;
  *   - every argument is validated before anything is launched or written; a
@@ -109,9 +110,8 @@ typedef struct kvtc_state_header {
     double   beta;
     double   energy_threshold;
     int32_t  rank_cfg;      /* configured rank (0 = energy threshold) */
-    int32_t  kfetch;        /* fetch contraction length: slots regrouped into 8-slot groups of
-                               one width each (zero-padded where the width changes), rounded
-                               up to 16 */
+    int32_t  kfetch;        /* fetch contraction length: runs of equal widths among the
+                               stored slots, each padded to a multiple of 16 slots */
     int64_t  s_prefill;     /* rows the state was fitted on (0 if built from parts) */
     /* per-unit sections */
     uint64_t off_unit;      /* kvtc_unit_info [units] */
@@ -125,14 +125,16 @@ typedef struct kvtc_state_header {
     uint64_t off_basis;     /* float  [units][kslots][dg] basis vector of slot j (0 = empty) */
     uint64_t off_qlo;       /* double [units][kslots] DP: min of slot j, as stored (fp32 value) */
     uint64_t off_qinv;      /* double [units][kslots] DP: 1/scale of slot j (0 if scale is 0) */
-    uint64_t off_w16;       /* half   [units][dg][kfetch] fetch operand in fetch-group order:
-                               DP scale_j*basis_j, mixed basis_j, rounded to fp16; 0 for padding */
+    uint64_t off_w16;       /* half   [units][dg][kfetch] fetch operand in k-step order: DP
+                               scale_j*basis_j, mixed basis_j, rounded to fp16, 0 for padding;
+                               within each 8-slot half of a 4-bit k-step the slots are stored
+                               in the order 0,2,4,6,1,3,5,7 */
     uint64_t off_bias;      /* float  [units][dg] fetch bias: DP mu + sum_j min_j*basis_j,
                                mixed mu */
     uint64_t total_bytes;
-    uint64_t off_kdesc;     /* uint32 [units][kfetch/8] fetch group g (k = 8g..8g+7): bit offset
-                               of its first field (bits 0-15) | width (16-19, 0 = empty group) |
-                               quantisation group of its slots (20-31, mixed mode) */
+    uint64_t off_kdesc;     /* uint32 [units][kfetch/16] fetch k-step t (k = 16t..16t+15): bit
+                               offset of its first field (bits 0-15) | width of all its fields
+                               (16-19, 0 = empty) | quantisation group (20-31, mixed mode) */
     uint64_t reserved[3];
 } kvtc_state_header;
 

@@ -20,6 +20,9 @@
 
 #include <algorithm>
 #include <cstdint>
+#include <mutex>
+#include <set>
+#include <utility>
 
 #include "kvtc.h"
 #include "kvtc_internal.h"
@@ -41,6 +44,7 @@ constexpr int kFetTok = 32;          // tokens per fetch tile (one wave)
 constexpr int kFetchRegWords = 24;   // per-lane register staging of one tile's rows+params
 constexpr int kMaxSlots = 256;
 constexpr int kMaxRowStride = 256;
+constexpr int kFetchBlocks = 512;    // target block count of a fetch (one block per unit at the batched-decode shape)
 
 // ------------------------------------------------------------ small helpers
 // Nearest-even binary16 of a double from its value: the binade is read from
@@ -398,10 +402,139 @@ struct FetchArgs {
 };
 
 typedef _Float16 half2 __attribute__((ext_vector_type(2)));
+typedef float float2v __attribute__((ext_vector_type(2)));
+
+// 0x64 as the high byte of an fp16 makes the low byte an integer offset from
+// 1024: the half 0x64XX is exactly 1024 + XX.
+constexpr uint32_t kMagic = 0x64646464u;
+
+// Eight W-bit fields (W <= 3, all inside the low word) as four half2 pairs of
+// 1024 + code, in field order.
+template <int W>
+__device__ inline void small_fields(uint32_t lo, uint32_t (&pr)[4]) {
+    constexpr uint32_t kMask = (1u << W) - 1u;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+        const uint32_t c0 = (lo >> (2 * e * W)) & kMask, c1 = (lo >> ((2 * e + 1) * W)) & kMask;
+        pr[e] = (c0 | (c1 << 16)) | 0x64006400u;
+    }
+}
+
+// One lane's eight B-operand values of one k-step (16 fetch slots of a single
+// width w > 0): the fields starting at the k-step's first field plus 8w for
+// the upper operand half, read from the lane's token row as a 64-bit window
+// and turned into exact fp16 integers.  In group-head mode each code is
+// dequantised with the row's fp16 (min, scale) of the k-step's quantisation
+// group in one fp16 fma.
+template <bool MIXED>
+__device__ __forceinline__ half8 decode_kstep(uint32_t kd, const uint32_t *myrow, const uint32_t *mypar,
+                                              uint32_t half_k) {
+    const uint32_t w = (kd >> 16) & 0xFu;
+    const uint32_t off = (kd & 0xFFFFu) + (half_k << 3) * w;
+    const uint32_t wi = off >> 5, sh = off & 31u;
+    const uint32_t r0 = myrow[wi], r1 = myrow[wi + 1];
+    const uint32_t lo = __builtin_amdgcn_alignbit(r1, r0, sh);
+    uint32_t pr[4];                                        // 4 packed half2 of 1024 + code
+    if (w == 8u) {
+        const uint32_t hi = __builtin_amdgcn_alignbit(myrow[wi + 2], r1, sh);
+        pr[0] = __builtin_amdgcn_perm(kMagic, lo, 0x04010400u);
+        pr[1] = __builtin_amdgcn_perm(kMagic, lo, 0x04030402u);
+        pr[2] = __builtin_amdgcn_perm(kMagic, hi, 0x04010400u);
+        pr[3] = __builtin_amdgcn_perm(kMagic, hi, 0x04030402u);
+    } else if (w == 4u) {
+        // nibbles of a 4-bit k-step are stored in the order 0,2,4,6,1,3,5,7
+        const uint32_t ev = lo & 0x0F0F0F0Fu, od = (lo >> 4) & 0x0F0F0F0Fu;
+        pr[0] = __builtin_amdgcn_perm(kMagic, ev, 0x04010400u);
+        pr[1] = __builtin_amdgcn_perm(kMagic, ev, 0x04030402u);
+        pr[2] = __builtin_amdgcn_perm(kMagic, od, 0x04010400u);
+        pr[3] = __builtin_amdgcn_perm(kMagic, od, 0x04030402u);
+    } else if (w == 2u) {
+        small_fields<2>(lo, pr);
+    } else if (w == 1u) {
+        small_fields<1>(lo, pr);
+    } else {
+        small_fields<3>(lo, pr);
+    }
+    half8 bv;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+        // (1024 + c) - 1024 = c exactly
+        const half2 cv = __builtin_bit_cast(half2, pr[e]) -
+                         half2{static_cast<_Float16>(1024.0f), static_cast<_Float16>(1024.0f)};
+        if constexpr (MIXED) {
+            const uint32_t p = mypar[kd >> 20];
+            const half2 mn2 = __builtin_bit_cast(half2, (p & 0xFFFFu) | (p << 16));
+            const half2 sc2 = __builtin_bit_cast(half2, (p >> 16) | (p & 0xFFFF0000u));
+            const half2 r = __builtin_elementwise_fma(cv, sc2, mn2);
+            bv[2 * e] = r[0];
+            bv[2 * e + 1] = r[1];
+        } else {
+            bv[2 * e] = cv[0];
+            bv[2 * e + 1] = cv[1];
+        }
+    }
+    return bv;
+}
+
+// Accumulators seeded with the bias: C[d][token] starts at bias[d] for the
+// rows d = 32db + 8q + 4half_k + e this lane holds.
+template <int NDB>
+__device__ __forceinline__ void seed_bias(floatx16 (&acc)[NDB], const float *biasl, int half_k) {
+#pragma unroll
+    for (int db = 0; db < NDB; ++db)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            const float4 bq = *reinterpret_cast<const float4 *>(biasl + db * 32 + q * 8 + half_k * 4);
+            acc[db][q * 4 + 0] = bq.x;
+            acc[db][q * 4 + 1] = bq.y;
+            acc[db][q * 4 + 2] = bq.z;
+            acc[db][q * 4 + 3] = bq.w;
+        }
+}
+
+// fp16 rounding of a 32-token x 32*NDB-column accumulator tile, transposed
+// through this wave's LDS staging into rows of 16-byte chunks, written with
+// non-temporal stores (the first `valid` tokens only).  orow points at the
+// output row of the tile's first token, column 0 of the slice.
+template <int NDB>
+__device__ __forceinline__ void store_tile(const floatx16 (&acc)[NDB], _Float16 *outl, int opitch, int lane,
+                                           _Float16 *orow, int64_t oss, int valid) {
+    constexpr int DS = 32 * NDB;
+    const int tok = lane & 31, half_k = lane >> 5;
+#pragma unroll
+    for (int db = 0; db < NDB; ++db) {
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            const int dl = db * 32 + q * 8 + half_k * 4;
+            const float2v p0 = {acc[db][q * 4 + 0], acc[db][q * 4 + 1]};
+            const float2v p1 = {acc[db][q * 4 + 2], acc[db][q * 4 + 3]};
+            const half2 h0 = __builtin_convertvector(p0, half2), h1 = __builtin_convertvector(p1, half2);
+            half4 hv;
+            hv[0] = h0[0];
+            hv[1] = h0[1];
+            hv[2] = h1[0];
+            hv[3] = h1[1];
+            *reinterpret_cast<half4 *>(outl + tok * opitch + dl) = hv;
+        }
+    }
+    __builtin_amdgcn_wave_barrier();
+    constexpr int kChunksPerRow = DS / 8;
+#pragma unroll
+    for (int it = 0; it < kFetTok * kChunksPerRow / 64; ++it) {
+        const int idx = it * 64 + lane;
+        const int t = idx / kChunksPerRow, c = idx - t * kChunksPerRow;
+        if (t < valid) {
+            const u32x4 v = *reinterpret_cast<const u32x4 *>(outl + t * opitch + c * 8);
+            __builtin_nontemporal_store(v, reinterpret_cast<u32x4 *>(orow + t * oss + c * 8));
+        }
+    }
+    __builtin_amdgcn_wave_barrier();
+}
 
 // One block: one (unit, d-slice of 32*NDB columns), a run of 32-token tiles;
-// each wave reconstructs whole tiles.  MFMA operands: A = W rows (d), B =
-// per-token code values (fetch slots), C[d][token] accumulates in fp32.
+// each wave reconstructs whole tiles with the W slice staged in LDS.  Serves
+// contractions of any length up to 256 slots.  MFMA operands: A = W rows (d),
+// B = per-token code values (fetch slots), C[d][token] accumulates in fp32.
 template <bool MIXED, int NDB, int KS>
 __global__ __launch_bounds__(kThreads) void fetch_kernel(FetchArgs a) {
     extern __shared__ __align__(16) unsigned char smem[];
@@ -422,14 +555,13 @@ __global__ __launch_bounds__(kThreads) void fetch_kernel(FetchArgs a) {
     const int row_words = a.row_stride >> 2;
 
     _Float16 *wl = reinterpret_cast<_Float16 *>(smem + a.lds_w);       // [DS][wpitch]
-    uint32_t *descl = reinterpret_cast<uint32_t *>(smem + a.lds_desc);  // [kfetch/8]
     float *biasl = reinterpret_cast<float *>(smem + a.lds_bias);        // [DS]
     unsigned char *wbase = smem + a.lds_wave + wave * a.lds_rows;
-    uint32_t *rowsl = reinterpret_cast<uint32_t *>(wbase);              // [32*row_words + 2]
+    uint32_t *rowsl = reinterpret_cast<uint32_t *>(wbase);              // [32*row_words + 8]
     uint32_t *parl = reinterpret_cast<uint32_t *>(wbase + a.lds_par);   // [32][n_qg]
     _Float16 *outl = reinterpret_cast<_Float16 *>(wbase + a.lds_out);   // [32][opitch]
 
-    // stage this slice of W, the group descriptors and the bias
+    // stage this slice of W and the bias
     {
         const uint16_t *src = a.w16 + (static_cast<int64_t>(u) * a.dg + d0) * a.kfetch;
         const int vec_per_row = a.kfetch / 8;
@@ -439,8 +571,6 @@ __global__ __launch_bounds__(kThreads) void fetch_kernel(FetchArgs a) {
             const u32x4 v = *reinterpret_cast<const u32x4 *>(src + r * a.kfetch + c * 8);
             *reinterpret_cast<u32x4 *>(wl + r * a.wpitch + c * 8) = v;
         }
-        const int ngr = a.kfetch / kGroup;
-        for (int i = tid; i < ngr; i += kThreads) descl[i] = a.kdesc[static_cast<int64_t>(u) * ngr + i];
         for (int i = tid; i < DS; i += kThreads) biasl[i] = a.bias[static_cast<int64_t>(u) * a.dg + d0 + i];
     }
     __syncthreads();
@@ -483,17 +613,14 @@ __global__ __launch_bounds__(kThreads) void fetch_kernel(FetchArgs a) {
     };
 
     const int tok = lane & 31;            // B-operand column / C column of this lane
-    const int half_k = lane >> 5;         // this lane feeds fetch group 2*ks + half_k
+    const uint32_t half_k = lane >> 5;    // this lane feeds fetch slots 8..15 of a k-step if set
 
-    // per-lane unpack program, the same for every tile of the block: word index,
-    // shift and width of the group's 64-bit field window, quantisation group
-    uint32_t prog[KS];
+    // the unit's k-step descriptors (first field offset, width, quantisation
+    // group), block-uniform, held in scalar registers for all tiles
+    uint32_t kd[KS];
 #pragma unroll
-    for (int ks = 0; ks < KS; ++ks) {
-        const uint32_t desc = descl[2 * ks + half_k];
-        const uint32_t off0 = desc & 0xFFFFu;
-        prog[ks] = (off0 >> 5) | ((off0 & 31u) << 8) | (desc & 0xFFFF0000u);
-    }
+    for (int ks = 0; ks < KS; ++ks)
+        kd[ks] = __builtin_amdgcn_readfirstlane(a.kdesc[static_cast<int64_t>(u) * KS + ks]);
 
     int tile = tile_begin + wave;
     if (tile < tile_end) fetch_tile(tile);
@@ -505,84 +632,42 @@ __global__ __launch_bounds__(kThreads) void fetch_kernel(FetchArgs a) {
         __builtin_amdgcn_wave_barrier();
 
         floatx16 acc[NDB];
-#pragma unroll
-        for (int db = 0; db < NDB; ++db)
-#pragma unroll
-            for (int i = 0; i < 16; ++i) acc[db][i] = 0.0f;
-
+        seed_bias<NDB>(acc, biasl, half_k);
         const uint32_t *myrow = rowsl + tok * row_words;
+        const uint32_t *mypar = MIXED ? parl + tok * a.n_qg : nullptr;
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks) {
-            const uint32_t pg = prog[ks];
-            const uint32_t wi = pg & 0xFFu, sh = (pg >> 8) & 31u, w = (pg >> 16) & 0xFu;
-            const uint32_t r0 = myrow[wi], r1 = myrow[wi + 1], r2 = myrow[wi + 2];
-            const uint32_t lo = __builtin_amdgcn_alignbit(r1, r0, sh);
-            const uint32_t hi = __builtin_amdgcn_alignbit(r2, r1, sh);
-            // field e sits at bit e*w of the window; only 8-bit fields reach the high word
-            const bool wide = w == 8u;
-            const uint32_t hsrc = wide ? hi : lo;
-            const uint32_t hadj = wide ? 32u : 0u;
-            uint32_t c[8];
-#pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                if (e < 4) c[e] = __builtin_amdgcn_ubfe(lo, e * w, w);
-                else c[e] = __builtin_amdgcn_ubfe(hsrc, e * w - hadj, w);
-            }
-            half8 bv;
-            if constexpr (MIXED) {
-                // dequantised latent min16 + c * scale16, one fp16 rounding (packed fma)
-                const uint32_t p = parl[tok * a.n_qg + (pg >> 20)];
-                const half2 mn2 = __builtin_bit_cast(half2, (p & 0xFFFFu) | (p << 16));
-                const half2 sc2 = __builtin_bit_cast(half2, (p >> 16) | (p & 0xFFFF0000u));
-#pragma unroll
-                for (int e = 0; e < 8; e += 2) {
-                    half2 cv;
-                    cv[0] = static_cast<_Float16>(static_cast<uint16_t>(c[e]));
-                    cv[1] = static_cast<_Float16>(static_cast<uint16_t>(c[e + 1]));
-                    const half2 r = __builtin_elementwise_fma(cv, sc2, mn2);
-                    bv[e] = r[0];
-                    bv[e + 1] = r[1];
-                }
-            } else {
-#pragma unroll
-                for (int e = 0; e < 8; ++e) bv[e] = static_cast<_Float16>(static_cast<uint16_t>(c[e]));
-            }
+            if (((kd[ks] >> 16) & 0xFu) == 0u) continue;          // empty k-step (wave-uniform)
+            const half8 bv = decode_kstep<MIXED>(kd[ks], myrow, mypar, half_k);
 #pragma unroll
             for (int db = 0; db < NDB; ++db) {
                 const half8 av = *reinterpret_cast<const half8 *>(wl + (db * 32 + tok) * a.wpitch + ks * 16 + half_k * 8);
                 acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_f16(av, bv, acc[db], 0, 0, 0);
             }
         }
-        // C[d][token]: lane holds token (lane & 31), d = 32db + 8q + 4(lane>>5) + e
-#pragma unroll
-        for (int db = 0; db < NDB; ++db) {
-#pragma unroll
-            for (int q = 0; q < 4; ++q) {
-                const int dl = db * 32 + q * 8 + (lane >> 5) * 4;
-                half4 hv;
-#pragma unroll
-                for (int e = 0; e < 4; ++e) hv[e] = static_cast<_Float16>(acc[db][q * 4 + e] + biasl[dl + e]);
-                *reinterpret_cast<half4 *>(outl + tok * a.opitch + dl) = hv;
-            }
-        }
-        __builtin_amdgcn_wave_barrier();
-        constexpr int kChunksPerRow = DS / 8;
-        _Float16 *obase = a.out + b * a.osb + head * a.osh + dd0;
-#pragma unroll
-        for (int it = 0; it < kFetTok * kChunksPerRow / 64; ++it) {
-            const int idx = it * 64 + lane;
-            const int t = idx / kChunksPerRow, c = idx - t * kChunksPerRow;
-            if (t < valid) {
-                const u32x4 v = *reinterpret_cast<const u32x4 *>(outl + t * a.opitch + c * 8);
-                u32x4 *dst = reinterpret_cast<u32x4 *>(obase + (s + t - a.s_begin) * a.oss + c * 8);
-                __builtin_nontemporal_store(v, dst);
-            }
-        }
-        __builtin_amdgcn_wave_barrier();
+        store_tile<NDB>(acc, outl, a.opitch, lane,
+                        a.out + b * a.osb + head * a.osh + (s - a.s_begin) * a.oss + dd0, a.oss, valid);
     }
 }
 
 // ============================================================== launchers
+constexpr int kLdsMax = 160 * 1024;
+
+// Lets a kernel use up to the whole LDS of a CU as dynamic shared memory.  The
+// attribute belongs to the kernel, not to a call, so it is set once per kernel
+// (and per device; the set is an idempotent per-process cache of that fact).
+bool allow_lds(const void *kern) {
+    static std::mutex mu;
+    static std::set<std::pair<const void *, int>> done;
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return false;
+    std::lock_guard<std::mutex> lock(mu);
+    if (done.count({kern, dev})) return true;
+    if (hipFuncSetAttribute(kern, hipFuncAttributeMaxDynamicSharedMemorySize, kLdsMax) != hipSuccess) return false;
+    done.insert({kern, dev});
+    return true;
+}
+
 int append_nb(int kslots) {
     const int need = kslots / 16;
     const int opts[] = {1, 2, 4, 6, 8, 12, 16};
@@ -596,9 +681,7 @@ int32_t launch_append_nb(const AppendArgs &a, int64_t ntiles, int64_t U, hipStre
     const size_t lds = 2 * kAppTok * kAppPad * sizeof(double) + 2 * NB * 16 * kAppPad * sizeof(float) +
                        static_cast<size_t>(kAppTok) * (a.row_stride / 4) * sizeof(uint32_t);
     auto kern = append_kernel<MIXED, XT, NB>;
-    if (hipFuncSetAttribute(reinterpret_cast<const void *>(kern), hipFuncAttributeMaxDynamicSharedMemorySize,
-                            static_cast<int>(lds)) != hipSuccess)
-        return KVTC_E_DEVICE;
+    if (!allow_lds(reinterpret_cast<const void *>(kern))) return KVTC_E_DEVICE;
     hipLaunchKernelGGL(kern, dim3(static_cast<unsigned>(ntiles), static_cast<unsigned>(U)), dim3(kThreads), lds,
                        stream, a);
     return hipGetLastError() == hipSuccess ? KVTC_OK : KVTC_E_DEVICE;
@@ -616,9 +699,7 @@ template <typename XT, int NB>
 int32_t launch_small_nb(const AppendArgs &a, int64_t U, hipStream_t stream) {
     const size_t lds = small_lds_bytes(a.dg, NB, a.row_stride);
     auto kern = append_small_kernel<XT, NB>;
-    if (hipFuncSetAttribute(reinterpret_cast<const void *>(kern), hipFuncAttributeMaxDynamicSharedMemorySize,
-                            static_cast<int>(lds)) != hipSuccess)
-        return KVTC_E_DEVICE;
+    if (!allow_lds(reinterpret_cast<const void *>(kern))) return KVTC_E_DEVICE;
     const int64_t blocks = (a.n + kSmallRows - 1) / kSmallRows;
     hipLaunchKernelGGL(kern, dim3(static_cast<unsigned>(blocks), static_cast<unsigned>(U)), dim3(kThreads), lds,
                        stream, a);
@@ -662,10 +743,11 @@ int32_t launch_fetch_ks(FetchArgs a, hipStream_t stream) {
     a.opitch = DS + 8;
     a.lds_w = 0;
     a.lds_desc = static_cast<int>(align_up(static_cast<uint64_t>(DS) * a.wpitch * 2, 16));
-    a.lds_bias = static_cast<int>(align_up(a.lds_desc + (a.kfetch / kGroup) * 4, 16));
+    a.lds_bias = static_cast<int>(align_up(a.lds_desc + 16, 16));
     a.lds_wave = static_cast<int>(align_up(a.lds_bias + DS * 4, 16));
-    // rows of a tile back to back, plus two words of slack for the 3-word field window
-    const int rows_b = static_cast<int>(align_up((kFetTok * (a.row_stride / 4) + 2) * 4, 16));
+    // rows of a tile back to back, plus slack for the 3-word field window of the
+    // upper operand half of a padded k-step
+    const int rows_b = static_cast<int>(align_up((kFetTok * (a.row_stride / 4) + 8) * 4, 16));
     const int par_b = MIXED ? static_cast<int>(align_up(kFetTok * a.n_qg * 4, 16)) : 0;
     const int out_b = static_cast<int>(align_up(kFetTok * a.opitch * 2, 16));
     a.lds_par = rows_b;
@@ -675,9 +757,7 @@ int32_t launch_fetch_ks(FetchArgs a, hipStream_t stream) {
     if (lds > 160 * 1024) return KVTC_E_SHAPE;
     const int64_t grid = a.nblocks_per_xcd * 8;
     auto kern = fetch_kernel<MIXED, NDB, KS>;
-    if (hipFuncSetAttribute(reinterpret_cast<const void *>(kern), hipFuncAttributeMaxDynamicSharedMemorySize,
-                            static_cast<int>(lds)) != hipSuccess)
-        return KVTC_E_DEVICE;
+    if (!allow_lds(reinterpret_cast<const void *>(kern))) return KVTC_E_DEVICE;
     hipLaunchKernelGGL(kern, dim3(static_cast<unsigned>(grid)), dim3(kThreads), lds, stream, a);
     return hipGetLastError() == hipSuccess ? KVTC_OK : KVTC_E_DEVICE;
 }
@@ -813,14 +893,15 @@ int32_t kvtc_fetch(const void *state_host, const void *state_dev, const void *co
     a.kfetch = h->kfetch;
     a.row_stride = h->row_stride;
     a.n_qg = h->n_qgroups;
+    // a block covers whole output rows of a head (128 columns) where the head
+    // size allows, so every token's fields are decoded once per head
     const int DS = (h->head_dim % 128 == 0) ? 128 : 64;
     a.nslices = h->dg / DS;
     const int64_t ntiles = (s_end - s_begin + kFetTok - 1) / kFetTok;
     if (ntiles > 0x7FFFFFFF) return KVTC_E_SHAPE;
     a.ntiles = static_cast<int>(ntiles);
     const int64_t work = h->units * a.nslices * ntiles;
-    int64_t tpb = std::max<int64_t>(4, (work + 1023) / 1024);
-    tpb = std::min<int64_t>(tpb, ntiles);
+    const int64_t tpb = std::min<int64_t>(std::max<int64_t>(4, (work + kFetchBlocks - 1) / kFetchBlocks), ntiles);
     a.tiles_per_block = static_cast<int>(tpb);
     a.nchunks = static_cast<int>((ntiles + tpb - 1) / tpb);
     a.nblocks_real = h->units * a.nslices * a.nchunks;

@@ -502,7 +502,7 @@ Layout plan_layout(int64_t U, int dg, int rmax, int kslots, int kfetch) {
     L.off_qinv = take(U * kslots * sizeof(double));
     L.off_w16 = take(U * static_cast<uint64_t>(kfetch) * dg * sizeof(uint16_t));
     L.off_bias = take(U * dg * sizeof(float));
-    L.off_kdesc = take(U * static_cast<uint64_t>(kfetch / kGroup) * sizeof(uint32_t));
+    L.off_kdesc = take(U * static_cast<uint64_t>(kfetch / kKStep) * sizeof(uint32_t));
     L.total = o;
     return L;
 }
@@ -549,28 +549,28 @@ int32_t build_blob(const kvtc_config *cfg, int64_t B, int64_t H, int32_t rmax, c
         max_bits = std::max(max_bits, row_bits[u]);
     }
     if (max_bits > 0xFFFF) return KVTC_E_CONFIG;
-    // fetch groups: every run of equal widths among the stored slots is cut into
-    // groups of 8 (the last one zero-padded), so that each group is one width
-    std::vector<int> n_groups(U, 0);
+    // fetch k-steps: every run of equal widths among the stored slots is padded
+    // to a whole number of 16-slot k-steps, so each k-step has one width
+    std::vector<int> n_ksteps(U, 0);
     for (int64_t u = 0; u < U; ++u) {
         const uint8_t *bu = &bits[static_cast<size_t>(u) * rmax];
-        int run = 0, prev = -1, groups = 0;
+        int run = 0, prev = -1, steps = 0;
         for (int i = 0; i < ranks[u]; ++i) {
             if (!bu[i]) continue;
             if (bu[i] != prev) {
-                groups += (run + kGroup - 1) / kGroup;
+                steps += (run + kKStep - 1) / kKStep;
                 run = 0;
                 prev = bu[i];
             }
             ++run;
         }
-        groups += (run + kGroup - 1) / kGroup;
-        n_groups[u] = groups;
+        steps += (run + kKStep - 1) / kKStep;
+        n_ksteps[u] = steps;
     }
-    int max_groups = 0;
-    for (int64_t u = 0; u < U; ++u) max_groups = std::max(max_groups, n_groups[u]);
+    int max_steps = 1;
+    for (int64_t u = 0; u < U; ++u) max_steps = std::max(max_steps, n_ksteps[u]);
     const int kslots = std::max<int>(kSlotAlign, static_cast<int>(align_up(max_slots, kSlotAlign)));
-    const int kfetch = std::max<int>(kSlotAlign, static_cast<int>(align_up(kGroup * max_groups, kSlotAlign)));
+    const int kfetch = kKStep * max_steps;
     const Layout L = plan_layout(U, dg, rmax, kslots, kfetch);
     if (state_out == nullptr || *state_bytes < L.total) {
         *state_bytes = L.total;
@@ -649,9 +649,9 @@ int32_t build_blob(const kvtc_config *cfg, int64_t B, int64_t H, int32_t rmax, c
         for (int d = 0; d < dg; ++d) bacc[d] = mu[u * dg + d];
         int j = 0;
         uint32_t off = 0;
-        int k = 0;               // next fetch slot (8k-aligned at every width change)
+        int k = 0;               // next fetch slot (16-aligned at every width change)
         int prev_w = -1;
-        int in_group = 0;
+        int in_step = 0;
         for (int i = 0; i < rmax; ++i) {
             const size_t ci = static_cast<size_t>(u) * rmax + i;
             bits_o[ci] = bu[i];
@@ -663,7 +663,6 @@ int32_t build_blob(const kvtc_config *cfg, int64_t B, int64_t H, int32_t rmax, c
             const size_t sj = static_cast<size_t>(u) * kslots + j;
             scomp[sj] = i;
             sbits[sj] = (off & kOffsetMask) | (static_cast<uint32_t>(bu[i]) << 24);
-            off += bu[i];
             const float *src = &basis[(static_cast<size_t>(u) * rmax + i) * dg];
             float *dst = &sbasis[sj * dg];
             for (int d = 0; d < dg; ++d) dst[d] = src[d];
@@ -674,19 +673,28 @@ int32_t build_blob(const kvtc_config *cfg, int64_t B, int64_t H, int32_t rmax, c
                 wscale = static_cast<double>(qscale[ci]);
                 for (int d = 0; d < dg; ++d) bacc[d] += static_cast<double>(qmin[ci]) * src[d];
             }
-            if (bu[i] != prev_w || in_group == kGroup) {
-                if (in_group) k = static_cast<int>(align_up(k, kGroup));
+            if (bu[i] != prev_w || in_step == kKStep) {
+                if (in_step) k = static_cast<int>(align_up(k, kKStep));
                 const uint32_t qg = cfg->mode == KVTC_MODE_MIXED ? static_cast<uint32_t>(j / cfg->group_size) : 0u;
-                kdesc[static_cast<size_t>(u) * (kfetch / kGroup) + k / kGroup] =
-                    ((off - bu[i]) & 0xFFFFu) | (static_cast<uint32_t>(bu[i]) << 16) | (qg << 20);
+                kdesc[static_cast<size_t>(u) * (kfetch / kKStep) + k / kKStep] =
+                    (off & 0xFFFFu) | (static_cast<uint32_t>(bu[i]) << 16) | (qg << 20);
                 prev_w = bu[i];
-                in_group = 0;
+                in_step = 0;
+            }
+            // position of this slot in the k-step: 4-bit halves arrive nibble-interleaved
+            int kk = k;
+            if (bu[i] == 4) {
+                const int e = in_step % 8;
+                int p = 0;
+                while (kNibbleOrder[p] != e) ++p;
+                kk = k - e + p;
             }
             for (int d = 0; d < dg; ++d)
-                w16[(static_cast<size_t>(u) * dg + d) * kfetch + k] =
+                w16[(static_cast<size_t>(u) * dg + d) * kfetch + kk] =
                     half_bits_rne(wscale * static_cast<double>(src[d]));
+            off += bu[i];
             ++k;
-            ++in_group;
+            ++in_step;
             ++j;
         }
         for (; j < kslots; ++j) scomp[static_cast<size_t>(u) * kslots + j] = -1;

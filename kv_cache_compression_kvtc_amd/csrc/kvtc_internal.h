@@ -13,7 +13,11 @@ namespace kvtc {
 constexpr int kSlotAlign = 16;          // slots per unit are padded to a multiple of this
 constexpr int kSectionAlign = 256;      // blob sections start on this boundary
 constexpr uint32_t kOffsetMask = 0xFFFFFFu;
-constexpr int kGroup = 8;               // slots per fetch group (one MFMA operand half)
+constexpr int kKStep = 16;              // slots per fetch k-step (one MFMA K); one width each
+
+// Order in which the fetch kernel's 4-bit unpack delivers the 8 fields of one
+// operand half (even nibbles first, then odd ones); W rows are stored to match.
+constexpr int kNibbleOrder[8] = {0, 2, 4, 6, 1, 3, 5, 7};
 
 inline uint64_t align_up(uint64_t x, uint64_t a) { return (x + a - 1) / a * a; }
 

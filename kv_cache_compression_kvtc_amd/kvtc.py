@@ -285,6 +285,68 @@ def state_view(blob: np.ndarray) -> dict:
         "qlo": sec(h.off_qlo, np.float64, (U, ks)),
         "qinv": sec(h.off_qinv, np.float64, (U, ks)),
         "w16": sec(h.off_w16, np.float16, (U, dg, kf)),
-        "kdesc": sec(h.off_kdesc, np.uint32, (U, kf // 8)),
+        "kdesc": sec(h.off_kdesc, np.uint32, (U, kf // 16)),
         "bias": sec(h.off_bias, np.float32, (U, dg)),
     }
+
+
+# ---------------------------------------------------------------- prepared calls
+class PreparedAppend:
+    """kvtc_append with every buffer checked once; each call passes only the rows.
+
+    ``x_full`` is a device tensor [B, H, N, D] of rows to append; ``call(s0, s1)``
+    appends its rows [s0, s1) at store rows [s0, s1) (the same index in both).
+    """
+
+    def __init__(self, blob, blob_dev, x_full, codes, params, capacity, stream=None):
+        import torch
+        self.dtype = {torch.float16: F16, torch.float32: F32}.get(x_full.dtype)
+        if self.dtype is None:
+            raise KVTCError(E_DTYPE, "PreparedAppend")
+        h = _check_buffers(blob, blob_dev, codes, params, capacity, "PreparedAppend")
+        if x_full.dim() != 4 or not x_full.is_cuda or x_full.shape[3] != h.head_dim:
+            raise KVTCError(E_SHAPE, "PreparedAppend: x must be a device tensor [B, H, N, D]")
+        self.B, self.H, self.N = int(x_full.shape[0]), int(x_full.shape[1]), int(x_full.shape[2])
+        self.capacity = capacity
+        self._keep = (blob, blob_dev, x_full, codes, params)
+        self._args = (_host_ptr(blob), _dev_ptr(blob_dev))
+        self._x = x_full.data_ptr()
+        self._xs = int(x_full.stride(2)) * x_full.element_size()
+        self._strides = _strides4(x_full)
+        self._codes, self._params = _dev_ptr(codes), _dev_ptr(params)
+        self._stream = _stream_ptr(stream)
+        self._fn = _lib.kvtc_append
+
+    def __call__(self, s0: int, s1: int):
+        if not (0 <= s0 <= s1 <= self.N):
+            raise KVTCError(E_ARG, "PreparedAppend: rows outside x")
+        _check(self._fn(self._args[0], self._args[1], self._x + s0 * self._xs, self.dtype, self._strides,
+                        self.B, self.H, s1 - s0, s0, self._codes, self._params, self.capacity, self._stream),
+               "kvtc_append")
+
+
+class PreparedFetch:
+    """kvtc_fetch with every buffer checked once; ``call(s0, s1)`` reconstructs
+    store rows [s0, s1) into rows [s0, s1) of ``out_full`` [B, H, capacity, D]."""
+
+    def __init__(self, blob, blob_dev, codes, params, capacity, out_full, stream=None):
+        import torch
+        if out_full.dtype != torch.float16:
+            raise KVTCError(E_DTYPE, "PreparedFetch")
+        h = _check_buffers(blob, blob_dev, codes, params, capacity, "PreparedFetch")
+        if not out_full.is_cuda or out_full.dim() != 4 or tuple(out_full.shape[:2]) != (h.batch, h.heads) \
+                or out_full.shape[2] < capacity or out_full.shape[3] != h.head_dim:
+            raise KVTCError(E_SHAPE, "PreparedFetch: out must be a device tensor [B, H, >=capacity, D]")
+        self.capacity = capacity
+        self._keep = (blob, blob_dev, codes, params, out_full)
+        self._args = (_host_ptr(blob), _dev_ptr(blob_dev), _dev_ptr(codes), _dev_ptr(params))
+        self._out = out_full.data_ptr()
+        self._os = int(out_full.stride(2)) * out_full.element_size()
+        self._strides = _strides4(out_full)
+        self._stream = _stream_ptr(stream)
+        self._fn = _lib.kvtc_fetch
+
+    def __call__(self, s0: int, s1: int):
+        a = self._args
+        _check(self._fn(a[0], a[1], a[2], a[3], self.capacity, s0, s1, self._out + s0 * self._os,
+                        self._strides, self._stream), "kvtc_fetch")

@@ -238,3 +238,29 @@ def test_batched_decode_full_size_sampled_units():
         Lh = O.dequant_dp(got, bits, st.qmin32[u, :r], st.qscale32[u, :r])
         ref = O.reconstruct(Lh, st.mu32[u], st.V32[u, :, :r])
         check_recon(ref[None, None], out[b:b + 1, h:h + 1], f"unit {u}")
+
+
+def test_prepared_calls_match_the_plain_binding():
+    print_case("prepared calls")
+    from kv_cache_compression_kvtc_amd import kvtc as K
+    w = small(2, s_total=4096 + 40)
+    X = synth.generate(w, 0)
+    st = O.fit(oracle_cfg(w), X[:, :, :4096])
+    S = X.shape[2]
+    a, b = DeviceStore(blob_from_oracle(st), S), DeviceStore(blob_from_oracle(st), S)
+    x = torch.from_numpy(X).cuda()
+    a.append(x[:, :, :4096], 0)
+    for s in range(4096, S):
+        a.append(x[:, :, s:s + 1], s)
+    out_b = torch.zeros((1, 8, S, 128), dtype=torch.float16, device="cuda:0")
+    app = K.PreparedAppend(b.blob, b.blob_dev, x, b.codes, b.params, S)
+    fet = K.PreparedFetch(b.blob, b.blob_dev, b.codes, b.params, S, out_b)
+    app(0, 4096)
+    for s in range(4096, S):
+        app(s, s + 1)
+    fet(0, 1000)
+    fet(1000, S)
+    assert np.array_equal(a.rows(S), b.rows(S))
+    assert torch.equal(a.fetch(0, S), out_b)
+    with pytest.raises(K.KVTCError):
+        app(S - 1, S + 1)

@@ -165,25 +165,30 @@ def test_state_build_derived_sections_follow_their_definitions():
         sc = st.qscale32[u][comps].astype(np.float64)
         Vc = st.V32[u][:, comps].astype(np.float64)                        # [dg, ns]
         w16 = (Vc * sc[None, :]).astype(np.float16)                        # rounded once from float64
-        # fetch order: each run of equal widths is cut into groups of 8 slots,
-        # the last group of a run zero-padded; group g occupies k = 8g..8g+7
+        # fetch order: each run of equal widths is padded to whole 16-slot
+        # k-steps; inside each 8-slot half of a 4-bit k-step the slots sit in
+        # the nibble order 0,2,4,6,1,3,5,7 (the order the kernel unpacks them)
         widths = st.bits[u][comps]
-        kmap, descs, k = [], [], 0
+        nib = [0, 2, 4, 6, 1, 3, 5, 7]
+        place, descs, k, in_step = [], [], 0, 0
         for j in range(ns):
-            if j == 0 or widths[j] != widths[j - 1] or (k % 8 == 0 and kmap and kmap[-1][0] == k - 1):
-                k = (k + 7) // 8 * 8
+            if j == 0 or widths[j] != widths[j - 1] or in_step == 16:
+                k = (k + 15) // 16 * 16
                 descs.append((int(offs[j]), int(widths[j])))
-            kmap.append((k, j))
+                in_step = 0
+            e = in_step % 8
+            kk = k - e + nib.index(e) if widths[j] == 4 else k
+            place.append((kk, j))
             k += 1
+            in_step += 1
         kf = h.kfetch
-        assert kf % 16 == 0 and kf >= (k + 7) // 8 * 8
+        assert kf == 16 * len(descs)
         want = np.zeros((st.Dg, kf), np.float16)
-        for kk, j in kmap:
+        for kk, j in place:
             want[:, kk] = w16[:, j]
         assert np.array_equal(v["w16"][u], want)
         kd = v["kdesc"][u]
-        assert [(int(d & 0xFFFF), int((d >> 16) & 0xF)) for d in kd[: len(descs)]] == descs
-        assert (kd[len(descs):] == 0).all()
+        assert [(int(d & 0xFFFF), int((d >> 16) & 0xF)) for d in kd] == descs
         bias = st.mu32[u].astype(np.float64) + Vc @ st.qmin32[u][comps].astype(np.float64)
         assert np.abs(v["bias"][u] - bias).max() <= 2 ** -23 * np.abs(bias).max() * 2
         assert np.array_equal(v["qlo"][u, :ns], st.qmin32[u][comps].astype(np.float64))
