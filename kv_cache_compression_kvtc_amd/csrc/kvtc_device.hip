@@ -492,12 +492,12 @@ __device__ __forceinline__ void seed_bias(floatx16 (&acc)[NDB], const float *bia
         }
 }
 
-// fp16 rounding of a 32-token x 32*NDB-column accumulator tile, transposed
+// fp16 rounding of a 32-token x 32*NDB-column block of accumulators, transposed
 // through this wave's LDS staging into rows of 16-byte chunks, written with
 // non-temporal stores (the first `valid` tokens only).  orow points at the
-// output row of the tile's first token, column 0 of the slice.
+// output row of the tile's first token, first column of the block.
 template <int NDB>
-__device__ __forceinline__ void store_tile(const floatx16 (&acc)[NDB], _Float16 *outl, int opitch, int lane,
+__device__ __forceinline__ void store_tile(const floatx16 *acc, _Float16 *outl, int opitch, int lane,
                                            _Float16 *orow, int64_t oss, int valid) {
     constexpr int DS = 32 * NDB;
     const int tok = lane & 31, half_k = lane >> 5;
@@ -531,14 +531,28 @@ __device__ __forceinline__ void store_tile(const floatx16 (&acc)[NDB], _Float16 
     __builtin_amdgcn_wave_barrier();
 }
 
+// Waves per fetch block.
+template <int NDB>
+constexpr int fetch_waves() { return 4; }
+
+// Tiles of stored rows each fetch wave keeps in flight: two where a tile's
+// rows fit in 8 words per lane.
+template <int NDB, int RW>
+constexpr int fetch_prefetch() { return RW <= 8 ? 2 : 1; }
+
 // One block: one (unit, d-slice of 32*NDB columns), a run of 32-token tiles;
-// each wave reconstructs whole tiles with the W slice staged in LDS.  Serves
-// contractions of any length up to 256 slots.  MFMA operands: A = W rows (d),
+// each of its NW waves reconstructs whole tiles with the block's W slice in
+// LDS, prefetching the next tile's rows (RW words per lane) into registers.
+// Serves contractions of up to 256 slots.  MFMA operands: A = W rows (d),
 // B = per-token code values (fetch slots), C[d][token] accumulates in fp32.
-template <bool MIXED, int NDB, int KS>
-__global__ __launch_bounds__(kThreads) void fetch_kernel(FetchArgs a) {
+// Two such blocks fit a CU (two waves per SIMD); the epilogue writes whole
+// rows of the slice, 16-byte chunks of up to four rows per store.
+template <bool MIXED, int NDB, int KS, int RW, int NW, int PF>
+__global__ __launch_bounds__(64 * NW, 2) void fetch_kernel(FetchArgs a) {
     extern __shared__ __align__(16) unsigned char smem[];
     constexpr int DS = 32 * NDB;
+    constexpr int NT = 64 * NW;
+    constexpr int NH = NDB;                 // accumulator blocks per epilogue pass
     // blocks are dealt to the 8 XCDs round-robin; regroup them so that the
     // blocks of one unit (and its d-slices) run on the same XCD
     const int64_t bid = blockIdx.x;
@@ -566,12 +580,12 @@ __global__ __launch_bounds__(kThreads) void fetch_kernel(FetchArgs a) {
         const uint16_t *src = a.w16 + (static_cast<int64_t>(u) * a.dg + d0) * a.kfetch;
         const int vec_per_row = a.kfetch / 8;
 #pragma unroll 4
-        for (int i = tid; i < DS * vec_per_row; i += kThreads) {
+        for (int i = tid; i < DS * vec_per_row; i += NT) {
             const int r = i / vec_per_row, c = i - r * vec_per_row;
             const u32x4 v = *reinterpret_cast<const u32x4 *>(src + r * a.kfetch + c * 8);
             *reinterpret_cast<u32x4 *>(wl + r * a.wpitch + c * 8) = v;
         }
-        for (int i = tid; i < DS; i += kThreads) biasl[i] = a.bias[static_cast<int64_t>(u) * a.dg + d0 + i];
+        for (int i = tid; i < DS; i += NT) biasl[i] = a.bias[static_cast<int64_t>(u) * a.dg + d0 + i];
     }
     __syncthreads();
 
@@ -584,15 +598,14 @@ __global__ __launch_bounds__(kThreads) void fetch_kernel(FetchArgs a) {
 
     // rows (then params) of one tile into registers: word i of the tile's rows
     // is row word i of the store from the tile's first row; zero past the end
-    uint32_t reg[kFetchRegWords];
-    auto fetch_tile = [&](int tile) {
+    auto fetch_tile = [&](int tile, uint32_t (&r)[RW]) {
         const int64_t s = a.s_begin + static_cast<int64_t>(tile) * kFetTok;
         const int valid = static_cast<int>(min<int64_t>(kFetTok, a.s_end - s));
         const uint32_t *src = codes32 + (ubase + s) * row_words;
         const uint32_t *psrc = MIXED ? a.params + (ubase + s) * a.n_qg : nullptr;
         const int vrow = valid * row_words, vpar = MIXED ? valid * a.n_qg : 0;
 #pragma unroll
-        for (int k = 0; k < kFetchRegWords; ++k) {
+        for (int k = 0; k < RW; ++k) {
             const int i = k * 64 + lane;
             uint32_t v = 0u;
             if (i < row_tile_words) {
@@ -600,15 +613,15 @@ __global__ __launch_bounds__(kThreads) void fetch_kernel(FetchArgs a) {
             } else if (MIXED && i < tile_words) {
                 if (i - row_tile_words < vpar) v = psrc[i - row_tile_words];
             }
-            reg[k] = v;
+            r[k] = v;
         }
     };
-    auto stash_tile = [&]() {
+    auto stash_tile = [&](const uint32_t (&r)[RW]) {
 #pragma unroll
-        for (int k = 0; k < kFetchRegWords; ++k) {
+        for (int k = 0; k < RW; ++k) {
             const int i = k * 64 + lane;
-            if (i < row_tile_words) rowsl[i] = reg[k];
-            else if (MIXED && i < tile_words) parl[i - row_tile_words] = reg[k];
+            if (i < row_tile_words) rowsl[i] = r[k];
+            else if (MIXED && i < tile_words) parl[i - row_tile_words] = r[k];
         }
     };
 
@@ -622,15 +635,10 @@ __global__ __launch_bounds__(kThreads) void fetch_kernel(FetchArgs a) {
     for (int ks = 0; ks < KS; ++ks)
         kd[ks] = __builtin_amdgcn_readfirstlane(a.kdesc[static_cast<int64_t>(u) * KS + ks]);
 
-    int tile = tile_begin + wave;
-    if (tile < tile_end) fetch_tile(tile);
-    for (; tile < tile_end; tile += 4) {
-        stash_tile();
+    auto process = [&](int tile) {
         const int64_t s = a.s_begin + static_cast<int64_t>(tile) * kFetTok;
         const int valid = static_cast<int>(min<int64_t>(kFetTok, a.s_end - s));
-        if (tile + 4 < tile_end) fetch_tile(tile + 4);
         __builtin_amdgcn_wave_barrier();
-
         floatx16 acc[NDB];
         seed_bias<NDB>(acc, biasl, half_k);
         const uint32_t *myrow = rowsl + tok * row_words;
@@ -645,8 +653,32 @@ __global__ __launch_bounds__(kThreads) void fetch_kernel(FetchArgs a) {
                 acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_f16(av, bv, acc[db], 0, 0, 0);
             }
         }
-        store_tile<NDB>(acc, outl, a.opitch, lane,
-                        a.out + b * a.osb + head * a.osh + (s - a.s_begin) * a.oss + dd0, a.oss, valid);
+        _Float16 *orow = a.out + b * a.osb + head * a.osh + (s - a.s_begin) * a.oss + dd0;
+#pragma unroll
+        for (int hb = 0; hb < NDB; hb += NH)
+            store_tile<NH>(acc + hb, outl, a.opitch, lane, orow + hb * 32, a.oss, valid);
+    };
+
+    // wave w takes tiles w, w + NW, ...; the rows of the next PF of them are in
+    // flight in a register ring.  A wave's loads and stores retire in order, so
+    // waiting for a tile's rows also waits for every store issued before those
+    // rows were requested: with PF tiles in flight that is the stores of PF
+    // tiles back, which overlaps the store latency with PF tiles of work.
+    const int t0 = tile_begin + wave;
+    uint32_t ring[PF][RW];
+#pragma unroll
+    for (int p = 0; p < PF; ++p)
+        if (t0 + p * NW < tile_end) fetch_tile(t0 + p * NW, ring[p]);
+    for (int tile = t0; tile < tile_end; tile += PF * NW) {
+#pragma unroll
+        for (int p = 0; p < PF; ++p) {
+            const int tt = tile + p * NW;
+            if (tt < tile_end) {
+                stash_tile(ring[p]);
+                if (tt + PF * NW < tile_end) fetch_tile(tt + PF * NW, ring[p]);
+                process(tt);
+            }
+        }
     }
 }
 
@@ -736,11 +768,13 @@ int32_t launch_append(const AppendArgs &a, int64_t ntiles, int64_t U, int nb, hi
     }
 }
 
-template <bool MIXED, int NDB, int KS>
-int32_t launch_fetch_ks(FetchArgs a, hipStream_t stream) {
-    constexpr int DS = 32 * NDB;
+template <bool MIXED, int NDB, int KS, int RW>
+int32_t launch_fetch_rw(FetchArgs a, hipStream_t stream) {
+    constexpr int DS = 32 * NDB, NW = fetch_waves<NDB>();
+    constexpr int NH = NDB;
+    if (kFetTok * (a.row_stride / 4 + (MIXED ? a.n_qg : 0)) > 64 * RW) return KVTC_E_SHAPE;
     a.wpitch = a.kfetch + 8;
-    a.opitch = DS + 8;
+    a.opitch = 32 * NH + 8;
     a.lds_w = 0;
     a.lds_desc = static_cast<int>(align_up(static_cast<uint64_t>(DS) * a.wpitch * 2, 16));
     a.lds_bias = static_cast<int>(align_up(a.lds_desc + 16, 16));
@@ -753,34 +787,44 @@ int32_t launch_fetch_ks(FetchArgs a, hipStream_t stream) {
     a.lds_par = rows_b;
     a.lds_out = rows_b + par_b;
     a.lds_rows = rows_b + par_b + out_b;                 // per-wave bytes
-    const size_t lds = a.lds_wave + 4 * static_cast<size_t>(a.lds_rows);
-    if (lds > 160 * 1024) return KVTC_E_SHAPE;
+    const size_t lds = a.lds_wave + NW * static_cast<size_t>(a.lds_rows);
+    if (lds > kLdsMax) return KVTC_E_SHAPE;
     const int64_t grid = a.nblocks_per_xcd * 8;
-    auto kern = fetch_kernel<MIXED, NDB, KS>;
+    auto kern = fetch_kernel<MIXED, NDB, KS, RW, NW, fetch_prefetch<NDB, RW>()>;
     if (!allow_lds(reinterpret_cast<const void *>(kern))) return KVTC_E_DEVICE;
-    hipLaunchKernelGGL(kern, dim3(static_cast<unsigned>(grid)), dim3(kThreads), lds, stream, a);
+    hipLaunchKernelGGL(kern, dim3(static_cast<unsigned>(grid)), dim3(64 * NW), lds, stream, a);
     return hipGetLastError() == hipSuccess ? KVTC_OK : KVTC_E_DEVICE;
 }
 
+// Register staging of a tile's rows: the narrowest instantiated width that
+// holds them (whole-head tiles: 8, 16 or 24 words per lane; 64-column: 8 or 24).
+template <bool MIXED, int NDB, int KS>
+int32_t launch_fetch_ks(FetchArgs a, int rw, hipStream_t stream) {
+    if (rw <= 8) return launch_fetch_rw<MIXED, NDB, KS, 8>(a, stream);
+    if (NDB == 4 && rw <= 16) return launch_fetch_rw<MIXED, NDB, KS, (NDB == 4 ? 16 : 24)>(a, stream);
+    if (rw <= kFetchRegWords) return launch_fetch_rw<MIXED, NDB, KS, kFetchRegWords>(a, stream);
+    return KVTC_E_SHAPE;
+}
+
 template <bool MIXED, int NDB>
-int32_t launch_fetch(FetchArgs a, hipStream_t stream) {
+int32_t launch_fetch(FetchArgs a, int rw, hipStream_t stream) {
     switch (a.kfetch / 16) {
-        case 1: return launch_fetch_ks<MIXED, NDB, 1>(a, stream);
-        case 2: return launch_fetch_ks<MIXED, NDB, 2>(a, stream);
-        case 3: return launch_fetch_ks<MIXED, NDB, 3>(a, stream);
-        case 4: return launch_fetch_ks<MIXED, NDB, 4>(a, stream);
-        case 5: return launch_fetch_ks<MIXED, NDB, 5>(a, stream);
-        case 6: return launch_fetch_ks<MIXED, NDB, 6>(a, stream);
-        case 7: return launch_fetch_ks<MIXED, NDB, 7>(a, stream);
-        case 8: return launch_fetch_ks<MIXED, NDB, 8>(a, stream);
-        case 9: return launch_fetch_ks<MIXED, NDB, 9>(a, stream);
-        case 10: return launch_fetch_ks<MIXED, NDB, 10>(a, stream);
-        case 11: return launch_fetch_ks<MIXED, NDB, 11>(a, stream);
-        case 12: return launch_fetch_ks<MIXED, NDB, 12>(a, stream);
-        case 13: return launch_fetch_ks<MIXED, NDB, 13>(a, stream);
-        case 14: return launch_fetch_ks<MIXED, NDB, 14>(a, stream);
-        case 15: return launch_fetch_ks<MIXED, NDB, 15>(a, stream);
-        case 16: return launch_fetch_ks<MIXED, NDB, 16>(a, stream);
+        case 1: return launch_fetch_ks<MIXED, NDB, 1>(a, rw, stream);
+        case 2: return launch_fetch_ks<MIXED, NDB, 2>(a, rw, stream);
+        case 3: return launch_fetch_ks<MIXED, NDB, 3>(a, rw, stream);
+        case 4: return launch_fetch_ks<MIXED, NDB, 4>(a, rw, stream);
+        case 5: return launch_fetch_ks<MIXED, NDB, 5>(a, rw, stream);
+        case 6: return launch_fetch_ks<MIXED, NDB, 6>(a, rw, stream);
+        case 7: return launch_fetch_ks<MIXED, NDB, 7>(a, rw, stream);
+        case 8: return launch_fetch_ks<MIXED, NDB, 8>(a, rw, stream);
+        case 9: return launch_fetch_ks<MIXED, NDB, 9>(a, rw, stream);
+        case 10: return launch_fetch_ks<MIXED, NDB, 10>(a, rw, stream);
+        case 11: return launch_fetch_ks<MIXED, NDB, 11>(a, rw, stream);
+        case 12: return launch_fetch_ks<MIXED, NDB, 12>(a, rw, stream);
+        case 13: return launch_fetch_ks<MIXED, NDB, 13>(a, rw, stream);
+        case 14: return launch_fetch_ks<MIXED, NDB, 14>(a, rw, stream);
+        case 15: return launch_fetch_ks<MIXED, NDB, 15>(a, rw, stream);
+        case 16: return launch_fetch_ks<MIXED, NDB, 16>(a, rw, stream);
         default: return KVTC_E_SHAPE;
     }
 }
@@ -901,15 +945,17 @@ int32_t kvtc_fetch(const void *state_host, const void *state_dev, const void *co
     if (ntiles > 0x7FFFFFFF) return KVTC_E_SHAPE;
     a.ntiles = static_cast<int>(ntiles);
     const int64_t work = h->units * a.nslices * ntiles;
-    const int64_t tpb = std::min<int64_t>(std::max<int64_t>(4, (work + kFetchBlocks - 1) / kFetchBlocks), ntiles);
+    const int nw = DS == 128 ? fetch_waves<4>() : fetch_waves<2>();
+    const int64_t tpb = std::min<int64_t>(std::max<int64_t>(nw, (work + kFetchBlocks - 1) / kFetchBlocks), ntiles);
     a.tiles_per_block = static_cast<int>(tpb);
     a.nchunks = static_cast<int>((ntiles + tpb - 1) / tpb);
     a.nblocks_real = h->units * a.nslices * a.nchunks;
     a.nblocks_per_xcd = (a.nblocks_real + 7) / 8;
     if (a.nblocks_per_xcd * 8 > 0x7FFFFFFF) return KVTC_E_SHAPE;
     hipStream_t stream = static_cast<hipStream_t>(hip_stream);
-    if (DS == 128) return mixed ? launch_fetch<true, 4>(a, stream) : launch_fetch<false, 4>(a, stream);
-    return mixed ? launch_fetch<true, 2>(a, stream) : launch_fetch<false, 2>(a, stream);
+    const int rw = (kFetTok * tw + 63) / 64;
+    if (DS == 128) return mixed ? launch_fetch<true, 4>(a, rw, stream) : launch_fetch<false, 4>(a, rw, stream);
+    return mixed ? launch_fetch<true, 2>(a, rw, stream) : launch_fetch<false, 2>(a, rw, stream);
 }
 
 }  // extern "C"
