@@ -531,9 +531,15 @@ __device__ __forceinline__ void store_tile(const floatx16 *acc, _Float16 *outl, 
     __builtin_amdgcn_wave_barrier();
 }
 
-// Waves per fetch block.
-template <int NDB>
-constexpr int fetch_waves() { return 4; }
+// Waves per fetch block: four, or eight for a 128-column slice of a long
+// contraction (10+ k-steps), whose W slice leaves LDS for one block per CU.
+template <int NDB, int KS>
+constexpr int fetch_waves() { return (NDB == 4 && KS >= 10) ? 8 : 4; }
+
+// Accumulator blocks per epilogue pass: the whole slice, or half of it with
+// eight waves (whose LDS staging must then be half as large).
+template <int NDB, int NW>
+constexpr int fetch_epilogue_blocks() { return NW == 8 ? NDB / 2 : NDB; }
 
 // Tiles of stored rows each fetch wave keeps in flight: two where a tile's
 // rows fit in 8 words per lane.
@@ -545,14 +551,16 @@ constexpr int fetch_prefetch() { return RW <= 8 ? 2 : 1; }
 // LDS, prefetching the next tile's rows (RW words per lane) into registers.
 // Serves contractions of up to 256 slots.  MFMA operands: A = W rows (d),
 // B = per-token code values (fetch slots), C[d][token] accumulates in fp32.
-// Two such blocks fit a CU (two waves per SIMD); the epilogue writes whole
-// rows of the slice, 16-byte chunks of up to four rows per store.
+// With four waves two such blocks fit a CU (two waves per SIMD) and the
+// epilogue writes whole rows of the slice, 16-byte chunks of up to four rows
+// per store; with eight waves (long contractions) one block does, and the
+// epilogue writes the slice in two halves.
 template <bool MIXED, int NDB, int KS, int RW, int NW, int PF>
 __global__ __launch_bounds__(64 * NW, 2) void fetch_kernel(FetchArgs a) {
     extern __shared__ __align__(16) unsigned char smem[];
     constexpr int DS = 32 * NDB;
     constexpr int NT = 64 * NW;
-    constexpr int NH = NDB;                 // accumulator blocks per epilogue pass
+    constexpr int NH = fetch_epilogue_blocks<NDB, NW>();
     // blocks are dealt to the 8 XCDs round-robin; regroup them so that the
     // blocks of one unit (and its d-slices) run on the same XCD
     const int64_t bid = blockIdx.x;
@@ -770,8 +778,8 @@ int32_t launch_append(const AppendArgs &a, int64_t ntiles, int64_t U, int nb, hi
 
 template <bool MIXED, int NDB, int KS, int RW>
 int32_t launch_fetch_rw(FetchArgs a, hipStream_t stream) {
-    constexpr int DS = 32 * NDB, NW = fetch_waves<NDB>();
-    constexpr int NH = NDB;
+    constexpr int DS = 32 * NDB, NW = fetch_waves<NDB, KS>();
+    constexpr int NH = fetch_epilogue_blocks<NDB, NW>();
     if (kFetTok * (a.row_stride / 4 + (MIXED ? a.n_qg : 0)) > 64 * RW) return KVTC_E_SHAPE;
     a.wpitch = a.kfetch + 8;
     a.opitch = 32 * NH + 8;
@@ -945,7 +953,7 @@ int32_t kvtc_fetch(const void *state_host, const void *state_dev, const void *co
     if (ntiles > 0x7FFFFFFF) return KVTC_E_SHAPE;
     a.ntiles = static_cast<int>(ntiles);
     const int64_t work = h->units * a.nslices * ntiles;
-    const int nw = DS == 128 ? fetch_waves<4>() : fetch_waves<2>();
+    const int nw = (DS == 128 && h->kfetch >= 160) ? 8 : 4;
     const int64_t tpb = std::min<int64_t>(std::max<int64_t>(nw, (work + kFetchBlocks - 1) / kFetchBlocks), ntiles);
     a.tiles_per_block = static_cast<int>(tpb);
     a.nchunks = static_cast<int>((ntiles + tpb - 1) / tpb);
