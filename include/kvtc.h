@@ -128,7 +128,8 @@ typedef struct kvtc_state_header {
     uint64_t off_w16;       /* half   [units][dg][kfetch] fetch operand in k-step order: DP
                                scale_j*basis_j, mixed basis_j, rounded to fp16, 0 for padding;
                                within each 8-slot half of a 4-bit k-step the slots are stored
-                               in the order 0,2,4,6,1,3,5,7 */
+                               in the order 0,2,4,6,1,3,5,7; a 2-bit k-step stores its slots in
+                               the order 0,4,8,12,1,5,9,13,2,6,10,14,3,7,11,15 */
     uint64_t off_bias;      /* float  [units][dg] fetch bias: DP mu + sum_j min_j*basis_j,
                                mixed mu */
     uint64_t total_bytes;

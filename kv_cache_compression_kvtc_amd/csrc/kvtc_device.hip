@@ -395,6 +395,7 @@ struct FetchArgs {
     _Float16 *out;
     int64_t osb, osh, oss;             // element strides of out (d stride is 1)
     int dg, D, hpu, groups, kfetch, row_stride, n_qg;
+    float nqg_inv;                     // 1 / n_qg (group-head mode)
     int nslices, nchunks, tiles_per_block, ntiles;
     int64_t nblocks_real, nblocks_per_xcd;
     // dynamic LDS carve-up (bytes)
@@ -422,15 +423,17 @@ __device__ inline void small_fields(uint32_t lo, uint32_t (&pr)[4]) {
 
 // One lane's eight B-operand values of one k-step (16 fetch slots of a single
 // width w > 0): the fields starting at the k-step's first field plus 8w for
-// the upper operand half, read from the lane's token row as a 64-bit window
-// and turned into exact fp16 integers.  In group-head mode each code is
+// the upper operand half (for w = 2: the k-step's whole 32-bit window, shifted
+// by 4 bits for the upper half), read from the lane's token row as a 64-bit
+// window and turned into exact fp16 integers.  In group-head mode each code is
 // dequantised with the row's fp16 (min, scale) of the k-step's quantisation
-// group in one fp16 fma.
+// group in one fp16 fma; mypar points at the lane's token in the group-major
+// parameter staging.
 template <bool MIXED>
 __device__ __forceinline__ half8 decode_kstep(uint32_t kd, const uint32_t *myrow, const uint32_t *mypar,
                                               uint32_t half_k) {
     const uint32_t w = (kd >> 16) & 0xFu;
-    const uint32_t off = (kd & 0xFFFFu) + (half_k << 3) * w;
+    const uint32_t off = (kd & 0xFFFFu) + (w == 2u ? 0u : (half_k << 3) * w);
     const uint32_t wi = off >> 5, sh = off & 31u;
     const uint32_t r0 = myrow[wi], r1 = myrow[wi + 1];
     const uint32_t lo = __builtin_amdgcn_alignbit(r1, r0, sh);
@@ -449,7 +452,13 @@ __device__ __forceinline__ half8 decode_kstep(uint32_t kd, const uint32_t *myrow
         pr[2] = __builtin_amdgcn_perm(kMagic, od, 0x04010400u);
         pr[3] = __builtin_amdgcn_perm(kMagic, od, 0x04030402u);
     } else if (w == 2u) {
-        small_fields<2>(lo, pr);
+        // slots 0,4,8,12 then 1,5,9,13 (2,6,10,14 then 3,7,11,15 in the upper half)
+        const uint32_t t = lo >> (half_k << 2);
+        const uint32_t ev = t & 0x03030303u, od = (t >> 2) & 0x03030303u;
+        pr[0] = __builtin_amdgcn_perm(kMagic, ev, 0x04010400u);
+        pr[1] = __builtin_amdgcn_perm(kMagic, ev, 0x04030402u);
+        pr[2] = __builtin_amdgcn_perm(kMagic, od, 0x04010400u);
+        pr[3] = __builtin_amdgcn_perm(kMagic, od, 0x04030402u);
     } else if (w == 1u) {
         small_fields<1>(lo, pr);
     } else {
@@ -462,7 +471,7 @@ __device__ __forceinline__ half8 decode_kstep(uint32_t kd, const uint32_t *myrow
         const half2 cv = __builtin_bit_cast(half2, pr[e]) -
                          half2{static_cast<_Float16>(1024.0f), static_cast<_Float16>(1024.0f)};
         if constexpr (MIXED) {
-            const uint32_t p = mypar[kd >> 20];
+            const uint32_t p = mypar[(kd >> 20) * kFetTok];
             const half2 mn2 = __builtin_bit_cast(half2, (p & 0xFFFFu) | (p << 16));
             const half2 sc2 = __builtin_bit_cast(half2, (p >> 16) | (p & 0xFFFF0000u));
             const half2 r = __builtin_elementwise_fma(cv, sc2, mn2);
@@ -580,7 +589,7 @@ __global__ __launch_bounds__(64 * NW, 2) void fetch_kernel(FetchArgs a) {
     float *biasl = reinterpret_cast<float *>(smem + a.lds_bias);        // [DS]
     unsigned char *wbase = smem + a.lds_wave + wave * a.lds_rows;
     uint32_t *rowsl = reinterpret_cast<uint32_t *>(wbase);              // [32*row_words + 8]
-    uint32_t *parl = reinterpret_cast<uint32_t *>(wbase + a.lds_par);   // [32][n_qg]
+    uint32_t *parl = reinterpret_cast<uint32_t *>(wbase + a.lds_par);   // [n_qg][32]
     _Float16 *outl = reinterpret_cast<_Float16 *>(wbase + a.lds_out);   // [32][opitch]
 
     // stage this slice of W and the bias
@@ -628,8 +637,15 @@ __global__ __launch_bounds__(64 * NW, 2) void fetch_kernel(FetchArgs a) {
 #pragma unroll
         for (int k = 0; k < RW; ++k) {
             const int i = k * 64 + lane;
-            if (i < row_tile_words) rowsl[i] = r[k];
-            else if (MIXED && i < tile_words) parl[i - row_tile_words] = r[k];
+            if (i < row_tile_words) {
+                rowsl[i] = r[k];
+            } else if (MIXED && i < tile_words) {
+                // parameter word j of the tile is (token j / n_qg, group j % n_qg);
+                // staged group-major so that a k-step's reads hit 32 banks
+                const int j = i - row_tile_words;
+                const int t = static_cast<int>((static_cast<float>(j) + 0.5f) * a.nqg_inv);
+                parl[(j - t * a.n_qg) * kFetTok + t] = r[k];
+            }
         }
     };
 
@@ -650,7 +666,7 @@ __global__ __launch_bounds__(64 * NW, 2) void fetch_kernel(FetchArgs a) {
         floatx16 acc[NDB];
         seed_bias<NDB>(acc, biasl, half_k);
         const uint32_t *myrow = rowsl + tok * row_words;
-        const uint32_t *mypar = MIXED ? parl + tok * a.n_qg : nullptr;
+        const uint32_t *mypar = MIXED ? parl + tok : nullptr;
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks) {
             if (((kd[ks] >> 16) & 0xFu) == 0u) continue;          // empty k-step (wave-uniform)
@@ -945,6 +961,7 @@ int32_t kvtc_fetch(const void *state_host, const void *state_dev, const void *co
     a.kfetch = h->kfetch;
     a.row_stride = h->row_stride;
     a.n_qg = h->n_qgroups;
+    a.nqg_inv = mixed ? 1.0f / static_cast<float>(h->n_qgroups) : 0.0f;
     // a block covers whole output rows of a head (128 columns) where the head
     // size allows, so every token's fields are decoded once per head
     const int DS = (h->head_dim % 128 == 0) ? 128 : 64;
@@ -954,7 +971,9 @@ int32_t kvtc_fetch(const void *state_host, const void *state_dev, const void *co
     a.ntiles = static_cast<int>(ntiles);
     const int64_t work = h->units * a.nslices * ntiles;
     const int nw = (DS == 128 && h->kfetch >= 160) ? 8 : 4;
-    const int64_t tpb = std::min<int64_t>(std::max<int64_t>(nw, (work + kFetchBlocks - 1) / kFetchBlocks), ntiles);
+    // about two four-wave blocks, or one eight-wave block, per CU in one round
+    const int64_t target = kFetchBlocks * 4 / nw;
+    const int64_t tpb = std::min<int64_t>(std::max<int64_t>(nw, (work + target - 1) / target), ntiles);
     a.tiles_per_block = static_cast<int>(tpb);
     a.nchunks = static_cast<int>((ntiles + tpb - 1) / tpb);
     a.nblocks_real = h->units * a.nslices * a.nchunks;

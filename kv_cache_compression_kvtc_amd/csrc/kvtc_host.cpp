@@ -681,13 +681,16 @@ int32_t build_blob(const kvtc_config *cfg, int64_t B, int64_t H, int32_t rmax, c
                 prev_w = bu[i];
                 in_step = 0;
             }
-            // position of this slot in the k-step: 4-bit halves arrive nibble-interleaved
+            // position of this slot in the k-step: 4-bit halves arrive
+            // nibble-interleaved, 2-bit k-steps in the byte-lane order
             int kk = k;
             if (bu[i] == 4) {
                 const int e = in_step % 8;
                 int p = 0;
                 while (kNibbleOrder[p] != e) ++p;
                 kk = k - e + p;
+            } else if (bu[i] == 2) {
+                kk = k - in_step + kTwoBitOrder[in_step];
             }
             for (int d = 0; d < dg; ++d)
                 w16[(static_cast<size_t>(u) * dg + d) * kfetch + kk] =

@@ -18,6 +18,11 @@ constexpr int kKStep = 16;              // slots per fetch k-step (one MFMA K); 
 // Order in which the fetch kernel's 4-bit unpack delivers the 8 fields of one
 // operand half (even nibbles first, then odd ones); W rows are stored to match.
 constexpr int kNibbleOrder[8] = {0, 2, 4, 6, 1, 3, 5, 7};
+// Fetch-operand column c of a 2-bit k-step holds the field of slot
+// kTwoBitOrder[c]: masking the k-step's 32-bit window with 0x03030303 after
+// shifts of 0, 2 (lanes of the lower operand half) and 4, 6 (upper half)
+// yields the codes of these slots one per byte.  The map is its own inverse.
+constexpr int kTwoBitOrder[16] = {0, 4, 8, 12, 1, 5, 9, 13, 2, 6, 10, 14, 3, 7, 11, 15};
 
 inline uint64_t align_up(uint64_t x, uint64_t a) { return (x + a - 1) / a * a; }
 

@@ -167,9 +167,13 @@ def test_state_build_derived_sections_follow_their_definitions():
         w16 = (Vc * sc[None, :]).astype(np.float16)                        # rounded once from float64
         # fetch order: each run of equal widths is padded to whole 16-slot
         # k-steps; inside each 8-slot half of a 4-bit k-step the slots sit in
-        # the nibble order 0,2,4,6,1,3,5,7 (the order the kernel unpacks them)
+        # the nibble order 0,2,4,6,1,3,5,7 and a 2-bit k-step in the byte-lane
+        # order below (the orders the kernel unpacks them in)
         widths = st.bits[u][comps]
         nib = [0, 2, 4, 6, 1, 3, 5, 7]
+        # 2-bit k-steps: column c holds slot two[c] (codes one per byte after
+        # masking the k-step's 32-bit window with 0x03030303 at shifts 0,2,4,6)
+        two = [0, 4, 8, 12, 1, 5, 9, 13, 2, 6, 10, 14, 3, 7, 11, 15]
         place, descs, k, in_step = [], [], 0, 0
         for j in range(ns):
             if j == 0 or widths[j] != widths[j - 1] or in_step == 16:
@@ -177,7 +181,12 @@ def test_state_build_derived_sections_follow_their_definitions():
                 descs.append((int(offs[j]), int(widths[j])))
                 in_step = 0
             e = in_step % 8
-            kk = k - e + nib.index(e) if widths[j] == 4 else k
+            if widths[j] == 4:
+                kk = k - e + nib.index(e)
+            elif widths[j] == 2:
+                kk = k - in_step + two[in_step]
+            else:
+                kk = k
             place.append((kk, j))
             k += 1
             in_step += 1
