@@ -102,6 +102,7 @@ struct AppendArgs {
     uint8_t *codes;                    // [U][capacity][row_stride]
     uint32_t *params;                  // [U][capacity][n_qg] packed (min16 | scale16 << 16)
     int dg, D, hpu, groups, kslots, row_stride, n_qg, gs;
+    float inv_dg, inv_q4;              // 1/dg and 4/dg: exact quotients of small indices
 };
 
 // One block: 64 tokens of one unit, all of its stored components.
@@ -314,33 +315,73 @@ __global__ __launch_bounds__(kThreads) void append_small_kernel(AppendArgs a) {
     const int row_words = a.row_stride >> 2;
     const XT *x = static_cast<const XT *>(a.x);
 
-    for (int w = tid; w < 16 * row_words; w += kThreads) rows[w] = 0u;
+    constexpr int NBW = (NB + 3) / 4;       // N-blocks of this wave: wave, wave+4, ...
+    // Every global load of the block is issued before the first LDS write, so
+    // the kernel waits for memory once: this lane's slot constants (indices
+    // clamped; unused past n_slots), the first batch of the basis, then the
+    // valid input rows.  Quotients of indices by dg and dg/4 come from float
+    // reciprocals, exact for indices below 2^16.
+    const int64_t ub = static_cast<int64_t>(u) * a.kslots;
+    double qlo_r[NBW], qinv_r[NBW];
+    uint32_t sb_r[NBW];
+#pragma unroll
+    for (int q = 0; q < NBW; ++q) {
+        const int j = min((wave + 4 * q) * 16 + (lane & 15), a.kslots - 1);
+        qlo_r[q] = a.qlo[ub + j];
+        qinv_r[q] = a.qinv[ub + j];
+        sb_r[q] = a.sbits[ub + j];
+    }
+    const int q4 = a.dg / 4;
+    const float *basis = a.basis + static_cast<int64_t>(u) * a.kslots * a.dg;
+    const int nv = NB * 16 * q4, nload = a.kslots * q4;
+    constexpr int kBatchV = 16;
+    float4 vb[kBatchV];
+    auto load_basis = [&](int i0) {
+#pragma unroll
+        for (int q = 0; q < kBatchV; ++q) {
+            const int i = min(i0 + q * kThreads + tid, nload - 1);
+            vb[q] = *reinterpret_cast<const float4 *>(basis + static_cast<int64_t>(i) * 4);
+        }
+    };
+    auto store_basis = [&](int i0) {
+#pragma unroll
+        for (int q = 0; q < kBatchV; ++q) {
+            const int i = i0 + q * kThreads + tid;
+            if (i < nv) {
+                const int slot = static_cast<int>((static_cast<float>(i) + 0.5f) * a.inv_q4);
+                const int c = (i - slot * q4) * 4;
+                const bool keep = i < nload;           // slots past kslots are zero
+                float *dst = vs + slot * vpitch + c;
+                dst[0] = keep ? vb[q].x : 0.f;
+                dst[1] = keep ? vb[q].y : 0.f;
+                dst[2] = keep ? vb[q].z : 0.f;
+                dst[3] = keep ? vb[q].w : 0.f;
+            }
+        }
+    };
+    load_basis(0);
     {
         const float *mu = a.mu + static_cast<int64_t>(u) * a.dg;
-#pragma unroll 4
-        for (int i = tid; i < 16 * a.dg; i += kThreads) {
-            const int t = i / a.dg, d = i - t * a.dg;
-            double v = 0.0;
-            if (t < nvalid) v = load_x(x + b * a.xsb + g * a.xsh + (t0 + t) * a.xss + d) - static_cast<double>(mu[d]);
-            xs[t * xpitch + d] = v;
+        const int nx = nvalid * a.dg;
+        for (int i = tid; i < nx; i += kThreads) {
+            const int t = static_cast<int>((static_cast<float>(i) + 0.5f) * a.inv_dg);
+            const int d = i - t * a.dg;
+            xs[t * xpitch + d] =
+                load_x(x + b * a.xsb + g * a.xsh + (t0 + t) * a.xss + d) - static_cast<double>(mu[d]);
         }
-        const int q4 = a.dg / 4;
-        const float *basis = a.basis + static_cast<int64_t>(u) * a.kslots * a.dg;
-#pragma unroll 8
-        for (int i = tid; i < NB * 16 * q4; i += kThreads) {
-            const int slot = i / q4, c = (i - slot * q4) * 4;
-            float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
-            if (slot < a.kslots) v = *reinterpret_cast<const float4 *>(basis + static_cast<int64_t>(slot) * a.dg + c);
-            float *dst = vs + slot * vpitch + c;
-            dst[0] = v.x;
-            dst[1] = v.y;
-            dst[2] = v.z;
-            dst[3] = v.w;
+        for (int i = nx + tid; i < 16 * a.dg; i += kThreads) {
+            const int t = static_cast<int>((static_cast<float>(i) + 0.5f) * a.inv_dg);
+            xs[t * xpitch + (i - t * a.dg)] = 0.0;
         }
+    }
+    for (int w = tid; w < 16 * row_words; w += kThreads) rows[w] = 0u;
+    store_basis(0);
+    for (int i0 = kBatchV * kThreads; i0 < nv; i0 += kBatchV * kThreads) {
+        load_basis(i0);
+        store_basis(i0);
     }
     __syncthreads();
 
-    constexpr int NBW = (NB + 3) / 4;       // N-blocks of this wave: wave, wave+4, ...
     doublex4 acc[NBW];
 #pragma unroll
     for (int q = 0; q < NBW; ++q) acc[q] = doublex4{0.0, 0.0, 0.0, 0.0};
@@ -356,14 +397,13 @@ __global__ __launch_bounds__(kThreads) void append_small_kernel(AppendArgs a) {
             }
         }
     }
-    const int64_t ub = static_cast<int64_t>(u) * a.kslots;
 #pragma unroll
     for (int q = 0; q < NBW; ++q) {
         const int nb = wave + 4 * q;
         const int j = nb * 16 + (lane & 15);
         if (nb < NB && j < n_slots) {
-            const double lo = a.qlo[ub + j], inv = a.qinv[ub + j];
-            const uint32_t sb = a.sbits[ub + j];
+            const double lo = qlo_r[q], inv = qinv_r[q];
+            const uint32_t sb = sb_r[q];
             const uint32_t off = sb & kOffsetMask, w = sb >> 24;
             const double cmax = static_cast<double>((1u << w) - 1u);
 #pragma unroll
@@ -909,6 +949,8 @@ int32_t kvtc_append(const void *state_host, const void *state_dev, const void *x
     a.row_stride = h->row_stride;
     a.n_qg = h->n_qgroups;
     a.gs = h->group_size;
+    a.inv_dg = 1.0f / static_cast<float>(h->dg);
+    a.inv_q4 = 4.0f / static_cast<float>(h->dg);
     const int64_t ntiles = (n + kAppTok - 1) / kAppTok;
     if (ntiles > 0x7FFFFFFF) return KVTC_E_SHAPE;
     hipStream_t stream = static_cast<hipStream_t>(hip_stream);
