@@ -103,11 +103,35 @@ struct AppendArgs {
     uint32_t *params;                  // [U][capacity][n_qg] packed (min16 | scale16 << 16)
     int dg, D, hpu, groups, kslots, row_stride, n_qg, gs;
     float inv_dg, inv_q4;              // 1/dg and 4/dg: exact quotients of small indices
+    int x_vec;                         // rows and strides aligned to 4 elements (raw vector loads)
+};
+
+// Four consecutive input elements as raw bits (one 8- or 16-byte load), and
+// element i of them as a double.
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+template <typename XT>
+struct RawX4;
+template <>
+struct RawX4<_Float16> {
+    typedef u32x2 v;
+    static __device__ inline double get(v r, int i) {
+        const uint32_t w = r[i >> 1];
+        return static_cast<double>(
+            __builtin_bit_cast(_Float16, static_cast<uint16_t>((i & 1) ? (w >> 16) : (w & 0xFFFFu))));
+    }
+};
+template <>
+struct RawX4<float> {
+    typedef u32x4 v;
+    static __device__ inline double get(v r, int i) {
+        const uint32_t w = r[i];   // the element as a scalar first: bit_cast of r[i] itself reads element 0
+        return static_cast<double>(__builtin_bit_cast(float, w));
+    }
 };
 
 // One block: 64 tokens of one unit, all of its stored components.
 // Wave w owns tokens 16w..16w+15; N-block nb covers slots 16nb..16nb+15.
-template <bool MIXED, typename XT, int NB>
+template <bool MIXED, typename XT, int NB, bool XVEC>
 __global__ __launch_bounds__(kThreads) void append_kernel(AppendArgs a) {
     extern __shared__ __align__(16) unsigned char smem[];
     double *xs = reinterpret_cast<double *>(smem);                         // [2][64][kAppPad]
@@ -129,46 +153,54 @@ __global__ __launch_bounds__(kThreads) void append_kernel(AppendArgs a) {
     // and (slot, 4 columns) of the NB*16 x 16 basis chunk
     const int st_tok = tid >> 2, st_col = (tid & 3) * 4;
     constexpr int kVReps = (NB * 16 + 63) / 64;
-    double xr[4];
+    // a chunk's loads only fill these registers (indices clamped, so no load
+    // sits behind a branch); centring and the fp64 conversion happen when the
+    // chunk is written to LDS, after the MFMAs of the previous chunk, so the
+    // loads are in flight during those MFMAs
+    typename RawX4<XT>::v xv;
+    XT xraw[4];
+    float muv[4];
     float vr[kVReps][4];
+    const int tok_c = min(st_tok, nvalid - 1);
 
     auto load_chunk = [&](int kc) {
         const int gd = kc * kAppKC + st_col;          // column within the unit's row
         const int j = gd / a.D, dd = gd - j * a.D;
         const int h = g * a.hpu + j;
         const float *mu = a.mu + static_cast<int64_t>(u) * a.dg + gd;
-        if (st_tok < nvalid) {
-            const XT *p = x + b * a.xsb + h * a.xsh + (t0 + st_tok) * a.xss + dd;
-#pragma unroll
-            for (int i = 0; i < 4; ++i) xr[i] = load_x(p + i) - static_cast<double>(mu[i]);
+        const XT *p = x + b * a.xsb + h * a.xsh + (t0 + tok_c) * a.xss + dd;
+        if constexpr (XVEC) {
+            xv = *reinterpret_cast<const typename RawX4<XT>::v *>(p);
         } else {
 #pragma unroll
-            for (int i = 0; i < 4; ++i) xr[i] = 0.0;
+            for (int i = 0; i < 4; ++i) xraw[i] = p[i];
         }
 #pragma unroll
+        for (int i = 0; i < 4; ++i) muv[i] = mu[i];
+#pragma unroll
         for (int rep = 0; rep < kVReps; ++rep) {
-            const int slot = rep * 64 + st_tok;
-            if (slot < NB * 16 && slot < a.kslots) {
-                const float *p = a.basis + (static_cast<int64_t>(u) * a.kslots + slot) * a.dg + gd;
+            const int slot = min(rep * 64 + st_tok, a.kslots - 1);
+            const float *q = a.basis + (static_cast<int64_t>(u) * a.kslots + slot) * a.dg + gd;
 #pragma unroll
-                for (int i = 0; i < 4; ++i) vr[rep][i] = p[i];
-            } else {
-#pragma unroll
-                for (int i = 0; i < 4; ++i) vr[rep][i] = 0.0f;
-            }
+            for (int i = 0; i < 4; ++i) vr[rep][i] = q[i];
         }
     };
     auto store_chunk = [&](int buf) {
         double *xb = xs + buf * kAppTok * kAppPad + st_tok * kAppPad + st_col;
+        const bool tok_ok = st_tok < nvalid;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) xb[i] = xr[i];
+        for (int i = 0; i < 4; ++i) {
+            const double xi = XVEC ? RawX4<XT>::get(xv, i) : load_x(&xraw[i]);
+            xb[i] = tok_ok ? xi - static_cast<double>(muv[i]) : 0.0;
+        }
 #pragma unroll
         for (int rep = 0; rep < kVReps; ++rep) {
             const int slot = rep * 64 + st_tok;
             if (slot < NB * 16) {
+                const bool keep = slot < a.kslots;      // slots past kslots are zero
                 float *vb = vs + (buf * NB * 16 + slot) * kAppPad + st_col;
 #pragma unroll
-                for (int i = 0; i < 4; ++i) vb[i] = vr[rep][i];
+                for (int i = 0; i < 4; ++i) vb[i] = keep ? vr[rep][i] : 0.0f;
             }
         }
     };
@@ -776,7 +808,7 @@ template <bool MIXED, typename XT, int NB>
 int32_t launch_append_nb(const AppendArgs &a, int64_t ntiles, int64_t U, hipStream_t stream) {
     const size_t lds = 2 * kAppTok * kAppPad * sizeof(double) + 2 * NB * 16 * kAppPad * sizeof(float) +
                        static_cast<size_t>(kAppTok) * (a.row_stride / 4) * sizeof(uint32_t);
-    auto kern = append_kernel<MIXED, XT, NB>;
+    auto kern = a.x_vec ? append_kernel<MIXED, XT, NB, true> : append_kernel<MIXED, XT, NB, false>;
     if (!allow_lds(reinterpret_cast<const void *>(kern))) return KVTC_E_DEVICE;
     hipLaunchKernelGGL(kern, dim3(static_cast<unsigned>(ntiles), static_cast<unsigned>(U)), dim3(kThreads), lds,
                        stream, a);
@@ -949,6 +981,11 @@ int32_t kvtc_append(const void *state_host, const void *state_dev, const void *x
     a.row_stride = h->row_stride;
     a.n_qg = h->n_qgroups;
     a.gs = h->group_size;
+    {
+        const int64_t esz = dtype == KVTC_F16 ? 2 : 4;
+        a.x_vec = reinterpret_cast<uintptr_t>(x_dev) % (4 * esz) == 0 && x_strides[0] % 4 == 0 &&
+                  x_strides[1] % 4 == 0 && x_strides[2] % 4 == 0;
+    }
     a.inv_dg = 1.0f / static_cast<float>(h->dg);
     a.inv_q4 = 4.0f / static_cast<float>(h->dg);
     const int64_t ntiles = (n + kAppTok - 1) / kAppTok;
