@@ -11,6 +11,7 @@ torch = pytest.importorskip("torch")
 
 from oracle import kvtc_oracle as O
 from kv_cache_compression_kvtc_amd import synth
+from kv_cache_compression_kvtc_amd import kvtc as K
 
 pytestmark = pytest.mark.gpu
 
@@ -165,6 +166,49 @@ def test_append_from_strided_input_and_ragged_tail():
     ds.append(src[:, :, :4096 + 13], 0)                    # ragged: 4109 = 64 * 64 + 13
     ds.append(src[:, :, 4096 + 13:], 4096 + 13)
     check_codes_dp(st, X, ds.rows(4096 + 70))
+
+
+def test_unaligned_input_rows_store_the_same_bytes():
+    # rows whose start or strides are not a multiple of 4 elements take the
+    # element-wise load path of the bulk append; the codes must not depend on it
+    print_case("unaligned input")
+    for wid, tensor in ((2, 0), (1, 1)):
+        w = small(2, s_total=2048 + 37) if wid == 2 else synth.WORKLOADS[1]
+        X = synth.generate(w, tensor)
+        sp = w.s_prefill if wid == 1 else 2048
+        st = O.fit(oracle_cfg(w), X[:, :, :sp])
+        S = X.shape[2]
+        dt = torch.float16 if X.dtype == np.float16 else torch.float32
+        aligned, odd = DeviceStore(blob_from_oracle(st), S), DeviceStore(blob_from_oracle(st), S)
+        aligned.append(X, 0)
+        big = torch.zeros((w.B, w.H, S, w.D + 3), dtype=dt, device="cuda:0")
+        big[..., 1:1 + w.D] = torch.from_numpy(X).cuda()
+        src = big[..., 1:1 + w.D]                             # row stride D + 3, start offset 1
+        odd.append(src[:, :, :sp], 0)
+        odd.append(src[:, :, sp:], sp)
+        assert np.array_equal(aligned.rows(S), odd.rows(S))
+        check_codes_dp(st, X, odd.rows(S))
+
+
+def test_empty_calls_write_nothing_and_full_capacity():
+    print_case("empty calls / full capacity")
+    w = small(2, s_total=4096 + 64)
+    X = synth.generate(w, 1)
+    st = O.fit(oracle_cfg(w), X[:, :, :4096])
+    S = X.shape[2]
+    ds = DeviceStore(blob_from_oracle(st), S)              # capacity == rows appended
+    ds.codes.fill_(0xA5)
+    before = ds.codes.clone()
+    ds.append(X[:, :, :0], 0)                              # n = 0
+    ds.append(X[:, :, :0], S)                              # n = 0 at the end of the store
+    assert torch.equal(ds.codes, before)
+    out = torch.full((w.B, w.H, 4, w.D), 3.0, dtype=torch.float16, device="cuda:0")
+    K.kvtc_fetch(ds.blob, ds.blob_dev, ds.codes, ds.params, S, 17, 17, out[:, :, :0])
+    assert bool((out == 3.0).all())
+    ds.append(X, 0)                                        # fills the store exactly
+    check_codes_dp(st, X, ds.rows(S))
+    out = ds.fetch(S - 40, S)                              # the last rows, ending at capacity
+    check_recon(O.fetch(st, ds.rows(S))[:, :, S - 40:], out, "tail at capacity")
 
 
 def test_fp32_input_rows():
