@@ -94,11 +94,12 @@ def near_half_boundary(t, b):
     return np.abs(frac - 0.5) <= CODE_BAND * (2 ** b - 1)
 
 
-def check_codes_dp(st, x, dev_rows):
-    """Device codes of DP-mode rows x [B,H,n,D] against the oracle (exemption band)."""
+def check_codes_dp(st, x, dev_rows, units=None):
+    """Device codes of DP-mode rows x [B,H,n,D] against the oracle (exemption band),
+    over all units or the given ones."""
     xu = O.gather_units(np.asarray(x), st.hpu)
     total = mism = 0
-    for u in range(st.U):
+    for u in (range(st.U) if units is None else units):
         r = int(st.r[u])
         bits = st.bits[u, :r]
         L = O.project(xu[u], st.mu32[u], st.V32[u, :, :r])
@@ -129,11 +130,11 @@ def near_f16_midpoint(v):
     return d <= 1e-6 * np.abs(v)
 
 
-def check_codes_mixed(st, x, dev_rows, dev_params):
+def check_codes_mixed(st, x, dev_rows, dev_params, units=None):
     xu = O.gather_units(np.asarray(x), st.hpu)
     gs = st.cfg.group_size
     total = mism = pmism = 0
-    for u in range(st.U):
+    for u in (range(st.U) if units is None else units):
         r = int(st.r[u])
         bits = st.bits[u, :r]
         L = O.project(xu[u], st.mu32[u], st.V32[u, :, :r])
@@ -181,3 +182,25 @@ def check_recon(ref, dev, what=""):
         raise AssertionError(f"{what}: {int((~ok).sum())} outputs out of tolerance, e.g. "
                              f"{[(tuple(i), float(err[tuple(i)]), float(bound[tuple(i)])) for i in idx]}")
     return float((err / np.maximum(rng_d, 1e-30)).max())
+
+
+def unit_reference(st, rows_u, u, params_u=None):
+    """The oracle's float64 reconstruction [n, Dg] of one unit's stored rows."""
+    r = int(st.r[u])
+    bits = st.bits[u, :r]
+    codes = O.unpack_rows(rows_u, bits)
+    if st.cfg.mode == "dp":
+        Lh = O.dequant_dp(codes, bits, st.qmin32[u, :r], st.qscale32[u, :r])
+    else:
+        Lh = O.dequant_mixed(codes, params_u, st.cfg.group_size)
+    return O.reconstruct(Lh, st.mu32[u], st.V32[u, :, :r])
+
+
+def check_recon_unit(st, rows_u, u, out, params_u=None, what=""):
+    """Device fp16 output [B,H,S,D] of unit u against unit_reference."""
+    G = st.H // st.hpu
+    b, g = divmod(int(u), G)
+    dev = out[b, g * st.hpu:(g + 1) * st.hpu]                 # [hpu, S, D]
+    dev_u = dev.permute(1, 0, 2).reshape(dev.shape[1], st.hpu * st.D)
+    ref = unit_reference(st, rows_u, u, params_u)
+    return check_recon(ref[None, None], dev_u[None, None], what or f"unit {u}")

@@ -16,7 +16,7 @@ from kv_cache_compression_kvtc_amd import kvtc as K
 pytestmark = pytest.mark.gpu
 
 from gpu_helpers import (DeviceStore, blob_from_oracle, check_codes_dp, check_codes_mixed,
-                         check_recon, oracle_cfg)
+                         check_recon, check_recon_unit, oracle_cfg)
 
 
 @pytest.fixture(scope="module", autouse=True)
@@ -282,6 +282,72 @@ def test_batched_decode_full_size_sampled_units():
         Lh = O.dequant_dp(got, bits, st.qmin32[u, :r], st.qscale32[u, :r])
         ref = O.reconstruct(Lh, st.mu32[u], st.V32[u, :, :r])
         check_recon(ref[None, None], out[b:b + 1, h:h + 1], f"unit {u}")
+
+
+def test_long_context_full_size_sampled_units():
+    """Long context at full size (B=1, H=8, S=131072, rank by energy on the first
+    8192 rows), appended and fetched as the benchmark does (prefill, then one
+    one-shot append of the remaining 122880 rows, then the whole sequence)."""
+    print_case("long context full size")
+    w = synth.WORKLOADS[5]
+    S = w.s_total
+    rng = np.random.default_rng(11)
+    for tensor in (0, 1):
+        X = synth.generate(w, tensor)
+        st = O.fit(oracle_cfg(w), X[:, :, :w.s_prefill])
+        ds = DeviceStore(blob_from_oracle(st), S)
+        x_dev = torch.from_numpy(X).cuda()
+        ds.append(x_dev[:, :, :w.s_prefill], 0)
+        ds.append(x_dev[:, :, w.s_prefill:], w.s_prefill)
+        out = ds.fetch(0, S)
+        rows = ds.rows(S)
+        units = rng.choice(st.U, size=2, replace=False)
+        check_codes_dp(st, X, rows, units=units)
+        for u in units:
+            check_recon_unit(st, rows[u], u, out)
+
+
+def test_group_head_full_size_sampled_units():
+    """Group-head workload at full size (B=1, H=32 in 4 groups of 8, S=16384,
+    rank 256, 4/2-bit codes in groups of 32), one-shot append and fetch."""
+    print_case("group head full size")
+    w = synth.WORKLOADS[3]
+    S = w.s_total
+    for tensor in (0, 1):
+        X = synth.generate(w, tensor)
+        st = O.fit(oracle_cfg(w), X)
+        ds = DeviceStore(blob_from_oracle(st), S)
+        ds.append(torch.from_numpy(X).cuda(), 0)
+        out = ds.fetch(0, S)
+        rows, prm = ds.rows(S), ds.params_np(S)
+        units = [tensor, 3 - tensor]
+        check_codes_mixed(st, X, rows, prm, units=units)
+        for u in units:
+            check_recon_unit(st, rows[u], u, out, prm[u])
+
+
+def test_llama_layer_decode_full_size():
+    """Llama-3-8B-like layer at full size: prefill 4096 rows, then 256 decode
+    steps of (append one row, fetch all rows), as the benchmark runs them."""
+    print_case("llama layer decode full size")
+    w = synth.WORKLOADS[2]
+    S = w.s_total
+    for tensor in (0, 1):
+        X = synth.generate(w, tensor)
+        st = O.fit(oracle_cfg(w), X[:, :, :w.s_prefill])
+        ds = DeviceStore(blob_from_oracle(st), S)
+        x_dev = torch.from_numpy(X).cuda()
+        ds.append(x_dev[:, :, :w.s_prefill], 0)
+        mid = None
+        for s in range(w.s_prefill, S):
+            ds.append(x_dev[:, :, s:s + 1], s)
+            out = ds.fetch(0, s + 1)
+            if s == w.s_prefill + 100:
+                mid = out.clone()
+        rows = ds.rows(S)
+        check_codes_dp(st, X, rows)
+        check_recon(O.fetch(st, rows), out, "llama decode")
+        assert torch.equal(mid, out[:, :, : w.s_prefill + 101])
 
 
 def test_prepared_calls_match_the_plain_binding():
