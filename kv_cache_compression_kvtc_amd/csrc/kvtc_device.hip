@@ -22,6 +22,7 @@
 #include <cstdint>
 #include <mutex>
 #include <set>
+#include <type_traits>
 #include <utility>
 
 #include "kvtc.h"
@@ -577,7 +578,7 @@ __device__ __forceinline__ void seed_bias(floatx16 (&acc)[NDB], const float *bia
 // through this wave's LDS staging into rows of 16-byte chunks, written with
 // non-temporal stores (the first `valid` tokens only).  orow points at the
 // output row of the tile's first token, first column of the block.
-template <int NDB>
+template <int NDB, bool FULL = false>
 __device__ __forceinline__ void store_tile(const floatx16 *acc, _Float16 *outl, int opitch, int lane,
                                            _Float16 *orow, int64_t oss, int valid) {
     constexpr int DS = 32 * NDB;
@@ -600,13 +601,23 @@ __device__ __forceinline__ void store_tile(const floatx16 *acc, _Float16 *outl, 
     }
     __builtin_amdgcn_wave_barrier();
     constexpr int kChunksPerRow = DS / 8;
+    if (FULL || valid == kFetTok) {              // whole tile: no per-row masks
 #pragma unroll
-    for (int it = 0; it < kFetTok * kChunksPerRow / 64; ++it) {
-        const int idx = it * 64 + lane;
-        const int t = idx / kChunksPerRow, c = idx - t * kChunksPerRow;
-        if (t < valid) {
+        for (int it = 0; it < kFetTok * kChunksPerRow / 64; ++it) {
+            const int idx = it * 64 + lane;
+            const int t = idx / kChunksPerRow, c = idx - t * kChunksPerRow;
             const u32x4 v = *reinterpret_cast<const u32x4 *>(outl + t * opitch + c * 8);
             __builtin_nontemporal_store(v, reinterpret_cast<u32x4 *>(orow + t * oss + c * 8));
+        }
+    } else {
+#pragma unroll
+        for (int it = 0; it < kFetTok * kChunksPerRow / 64; ++it) {
+            const int idx = it * 64 + lane;
+            const int t = idx / kChunksPerRow, c = idx - t * kChunksPerRow;
+            if (t < valid) {
+                const u32x4 v = *reinterpret_cast<const u32x4 *>(outl + t * opitch + c * 8);
+                __builtin_nontemporal_store(v, reinterpret_cast<u32x4 *>(orow + t * oss + c * 8));
+            }
         }
     }
     __builtin_amdgcn_wave_barrier();
@@ -622,10 +633,11 @@ constexpr int fetch_waves() { return (NDB == 4 && KS >= 10) ? 8 : 4; }
 template <int NDB, int NW>
 constexpr int fetch_epilogue_blocks() { return NW == 8 ? NDB / 2 : NDB; }
 
-// Tiles of stored rows each fetch wave keeps in flight: two where a tile's
-// rows fit in 8 words per lane.
-template <int NDB, int RW>
-constexpr int fetch_prefetch() { return RW <= 8 ? 2 : 1; }
+// Tiles of stored rows each fetch wave keeps in flight where a tile's rows
+// fit in 8 words per lane: three (DP) or two (group-head, whose decode needs
+// more registers); one otherwise.
+template <bool MIXED, int RW>
+constexpr int fetch_prefetch() { return RW <= 8 ? (MIXED ? 2 : 3) : 1; }
 
 // One block: one (unit, d-slice of 32*NDB columns), a run of 32-token tiles;
 // each of its NW waves reconstructs whole tiles with the block's W slice in
@@ -654,7 +666,8 @@ __global__ __launch_bounds__(64 * NW, 2) void fetch_kernel(FetchArgs a) {
     const int b = u / a.groups, g = u % a.groups;
     const int d0 = slice * DS;
     const int head = g * a.hpu + d0 / a.D, dd0 = d0 % a.D;
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform: scalar tile loops
     const int row_words = a.row_stride >> 2;
 
     _Float16 *wl = reinterpret_cast<_Float16 *>(smem + a.lds_w);       // [DS][wpitch]
@@ -687,12 +700,32 @@ __global__ __launch_bounds__(64 * NW, 2) void fetch_kernel(FetchArgs a) {
 
     // rows (then params) of one tile into registers: word i of the tile's rows
     // is row word i of the store from the tile's first row; zero past the end
+    // DP tiles whose rows fit in 8 words per lane take a branch-free path:
+    // every lane loads (address clamped to the tile's last valid word) and
+    // stashes all RW words into a rows area sized for them.  Words past the
+    // valid rows repeat the last valid word: they only feed token columns
+    // that are not stored, or padding slots whose W is exactly zero (any code
+    // is a finite fp16), so they need no masking, and the loaded values are
+    // not touched until the tile is stashed.  Without per-lane branches or
+    // selects the wait counts stay exact and the ring's second tile stays in
+    // flight.
+    constexpr bool kFlat = !MIXED && RW <= 8;
     auto fetch_tile = [&](int tile, uint32_t (&r)[RW]) {
         const int64_t s = a.s_begin + static_cast<int64_t>(tile) * kFetTok;
         const int valid = static_cast<int>(min<int64_t>(kFetTok, a.s_end - s));
         const uint32_t *src = codes32 + (ubase + s) * row_words;
         const uint32_t *psrc = MIXED ? a.params + (ubase + s) * a.n_qg : nullptr;
         const int vrow = valid * row_words, vpar = MIXED ? valid * a.n_qg : 0;
+        if constexpr (kFlat) {
+            if (vrow > 0) {
+#pragma unroll
+                for (int k = 0; k < RW; ++k) r[k] = src[min(k * 64 + lane, vrow - 1)];
+            } else {
+#pragma unroll
+                for (int k = 0; k < RW; ++k) r[k] = 0u;
+            }
+            return;
+        }
 #pragma unroll
         for (int k = 0; k < RW; ++k) {
             const int i = k * 64 + lane;
@@ -706,6 +739,11 @@ __global__ __launch_bounds__(64 * NW, 2) void fetch_kernel(FetchArgs a) {
         }
     };
     auto stash_tile = [&](const uint32_t (&r)[RW]) {
+        if constexpr (kFlat) {
+#pragma unroll
+            for (int k = 0; k < RW; ++k) rowsl[k * 64 + lane] = r[k];
+            return;
+        }
 #pragma unroll
         for (int k = 0; k < RW; ++k) {
             const int i = k * 64 + lane;
@@ -731,9 +769,10 @@ __global__ __launch_bounds__(64 * NW, 2) void fetch_kernel(FetchArgs a) {
     for (int ks = 0; ks < KS; ++ks)
         kd[ks] = __builtin_amdgcn_readfirstlane(a.kdesc[static_cast<int64_t>(u) * KS + ks]);
 
-    auto process = [&](int tile) {
+    auto process = [&](int tile, auto full) {
+        constexpr bool kFull = decltype(full)::value;
         const int64_t s = a.s_begin + static_cast<int64_t>(tile) * kFetTok;
-        const int valid = static_cast<int>(min<int64_t>(kFetTok, a.s_end - s));
+        const int valid = kFull ? kFetTok : static_cast<int>(min<int64_t>(kFetTok, a.s_end - s));
         __builtin_amdgcn_wave_barrier();
         floatx16 acc[NDB];
         seed_bias<NDB>(acc, biasl, half_k);
@@ -752,7 +791,7 @@ __global__ __launch_bounds__(64 * NW, 2) void fetch_kernel(FetchArgs a) {
         _Float16 *orow = a.out + b * a.osb + head * a.osh + (s - a.s_begin) * a.oss + dd0;
 #pragma unroll
         for (int hb = 0; hb < NDB; hb += NH)
-            store_tile<NH>(acc + hb, outl, a.opitch, lane, orow + hb * 32, a.oss, valid);
+            store_tile<NH, kFull>(acc + hb, outl, a.opitch, lane, orow + hb * 32, a.oss, valid);
     };
 
     // wave w takes tiles w, w + NW, ...; the rows of the next PF of them are in
@@ -760,20 +799,53 @@ __global__ __launch_bounds__(64 * NW, 2) void fetch_kernel(FetchArgs a) {
     // waiting for a tile's rows also waits for every store issued before those
     // rows were requested: with PF tiles in flight that is the stores of PF
     // tiles back, which overlaps the store latency with PF tiles of work.
+    // Branch-free DP path: the main loop covers whole tiles only and its body
+    // has no conditions (prefetches past the run are clamped to its last tile
+    // and never processed), so the compiler keeps exact wait counts across
+    // it; the last partial round and a ragged final tile run after it.
     const int t0 = tile_begin + wave;
+    const int last = tile_end - 1;
     uint32_t ring[PF][RW];
+    if constexpr (!kFlat) {
+        // rows with parameters or wider than 8 words per lane: one loop with
+        // per-tile conditions (keeps the register footprint of one tile body)
+#pragma unroll
+        for (int p = 0; p < PF; ++p)
+            if (t0 + p * NW < tile_end) fetch_tile(t0 + p * NW, ring[p]);
+        for (int tile = t0; tile < tile_end; tile += PF * NW) {
+#pragma unroll
+            for (int p = 0; p < PF; ++p) {
+                const int tt = tile + p * NW;
+                if (tt < tile_end) {
+                    stash_tile(ring[p]);
+                    if (tt + PF * NW < tile_end) fetch_tile(tt + PF * NW, ring[p]);
+                    process(tt, std::false_type{});
+                }
+            }
+        }
+        return;
+    }
+    const bool ragged_end = a.s_begin + static_cast<int64_t>(tile_end) * kFetTok > a.s_end;
+    const int full_end = ragged_end ? tile_end - 1 : tile_end;
 #pragma unroll
     for (int p = 0; p < PF; ++p)
-        if (t0 + p * NW < tile_end) fetch_tile(t0 + p * NW, ring[p]);
-    for (int tile = t0; tile < tile_end; tile += PF * NW) {
+        if (t0 <= last) fetch_tile(min(t0 + p * NW, last), ring[p]);
+    int tile = t0;
+    for (; tile + (PF - 1) * NW < full_end; tile += PF * NW) {
 #pragma unroll
         for (int p = 0; p < PF; ++p) {
             const int tt = tile + p * NW;
-            if (tt < tile_end) {
-                stash_tile(ring[p]);
-                if (tt + PF * NW < tile_end) fetch_tile(tt + PF * NW, ring[p]);
-                process(tt);
-            }
+            stash_tile(ring[p]);
+            fetch_tile(min(tt + PF * NW, last), ring[p]);
+            process(tt, std::true_type{});
+        }
+    }
+#pragma unroll
+    for (int p = 0; p < PF; ++p) {
+        const int tt = tile + p * NW;
+        if (tt < tile_end) {
+            stash_tile(ring[p]);
+            process(tt, std::false_type{});
         }
     }
 }
@@ -876,8 +948,10 @@ int32_t launch_fetch_rw(FetchArgs a, hipStream_t stream) {
     a.lds_bias = static_cast<int>(align_up(a.lds_desc + 16, 16));
     a.lds_wave = static_cast<int>(align_up(a.lds_bias + DS * 4, 16));
     // rows of a tile back to back, plus slack for the 3-word field window of the
-    // upper operand half of a padded k-step
-    const int rows_b = static_cast<int>(align_up((kFetTok * (a.row_stride / 4) + 8) * 4, 16));
+    // upper operand half of a padded k-step (the branch-free DP path stashes all
+    // RW words per lane, so its rows area holds at least that many)
+    int rows_b = static_cast<int>(align_up((kFetTok * (a.row_stride / 4) + 8) * 4, 16));
+    if (!MIXED && RW <= 8) rows_b = std::max(rows_b, RW * 64 * 4);
     const int par_b = MIXED ? static_cast<int>(align_up(kFetTok * a.n_qg * 4, 16)) : 0;
     const int out_b = static_cast<int>(align_up(kFetTok * a.opitch * 2, 16));
     a.lds_par = rows_b;
@@ -886,7 +960,7 @@ int32_t launch_fetch_rw(FetchArgs a, hipStream_t stream) {
     const size_t lds = a.lds_wave + NW * static_cast<size_t>(a.lds_rows);
     if (lds > kLdsMax) return KVTC_E_SHAPE;
     const int64_t grid = a.nblocks_per_xcd * 8;
-    auto kern = fetch_kernel<MIXED, NDB, KS, RW, NW, fetch_prefetch<NDB, RW>()>;
+    auto kern = fetch_kernel<MIXED, NDB, KS, RW, NW, fetch_prefetch<MIXED, RW>()>;
     if (!allow_lds(reinterpret_cast<const void *>(kern))) return KVTC_E_DEVICE;
     hipLaunchKernelGGL(kern, dim3(static_cast<unsigned>(grid)), dim3(64 * NW), lds, stream, a);
     return hipGetLastError() == hipSuccess ? KVTC_OK : KVTC_E_DEVICE;
