@@ -633,11 +633,17 @@ constexpr int fetch_waves() { return (NDB == 4 && KS >= 10) ? 8 : 4; }
 template <int NDB, int NW>
 constexpr int fetch_epilogue_blocks() { return NW == 8 ? NDB / 2 : NDB; }
 
-// Tiles of stored rows each fetch wave keeps in flight where a tile's rows
-// fit in 8 words per lane: three (DP) or two (group-head, whose decode needs
-// more registers); one otherwise.
+// Tiles of stored rows each fetch wave keeps in flight: where a tile's rows
+// fit in 8 words per lane three (DP) or two (group-head, whose decode needs
+// more registers), in 16 words two (DP) or one, otherwise one.
+// Whether a fetch kernel takes the branch-free tile path (rows of at most 16
+// words per lane; four-wave group-head kernels with k >= 128 would spill on
+// it and keep the conditional loads).
+template <bool MIXED, int KS, int RW, int NW>
+constexpr bool fetch_flat() { return RW <= 16 && !(MIXED && NW == 4 && KS >= 8); }
+
 template <bool MIXED, int RW>
-constexpr int fetch_prefetch() { return RW <= 8 ? (MIXED ? 2 : 3) : 1; }
+constexpr int fetch_prefetch() { return RW <= 8 ? (MIXED ? 2 : 3) : (RW <= 16 && !MIXED ? 2 : 1); }
 
 // One block: one (unit, d-slice of 32*NDB columns), a run of 32-token tiles;
 // each of its NW waves reconstructs whole tiles with the block's W slice in
@@ -700,16 +706,16 @@ __global__ __launch_bounds__(64 * NW, 2) void fetch_kernel(FetchArgs a) {
 
     // rows (then params) of one tile into registers: word i of the tile's rows
     // is row word i of the store from the tile's first row; zero past the end
-    // DP tiles whose rows fit in 8 words per lane take a branch-free path:
-    // every lane loads (address clamped to the tile's last valid word) and
-    // stashes all RW words into a rows area sized for them.  Words past the
-    // valid rows repeat the last valid word: they only feed token columns
-    // that are not stored, or padding slots whose W is exactly zero (any code
-    // is a finite fp16), so they need no masking, and the loaded values are
-    // not touched until the tile is stashed.  Without per-lane branches or
-    // selects the wait counts stay exact and the ring's second tile stays in
-    // flight.
-    constexpr bool kFlat = !MIXED && RW <= 8;
+    // Tiles whose rows (and params) fit in 16 words per lane take a
+    // branch-free path: every lane loads (address clamped to the tile's last
+    // valid row or parameter word) and stashes all RW words into a rows area
+    // sized for them.  Words past the valid rows repeat a valid word: they only
+    // feed token columns that are not stored, or padding slots whose W is
+    // exactly zero (codes and fp16 params of valid rows are finite), so they
+    // need no masking, and the loaded values are not touched until the tile is
+    // stashed.  Without per-lane branches or selects the wait counts stay exact
+    // and the ring's other tiles stay in flight.
+    constexpr bool kFlat = fetch_flat<MIXED, KS, RW, NW>();
     auto fetch_tile = [&](int tile, uint32_t (&r)[RW]) {
         const int64_t s = a.s_begin + static_cast<int64_t>(tile) * kFetTok;
         const int valid = static_cast<int>(min<int64_t>(kFetTok, a.s_end - s));
@@ -717,7 +723,17 @@ __global__ __launch_bounds__(64 * NW, 2) void fetch_kernel(FetchArgs a) {
         const uint32_t *psrc = MIXED ? a.params + (ubase + s) * a.n_qg : nullptr;
         const int vrow = valid * row_words, vpar = MIXED ? valid * a.n_qg : 0;
         if constexpr (kFlat) {
-            if (vrow > 0) {
+            if constexpr (MIXED) {
+                // group-head: word i is a row word below row_tile_words, else a
+                // parameter word; both addresses clamped to the valid part
+#pragma unroll
+                for (int k = 0; k < RW; ++k) {
+                    const int i = k * 64 + lane;
+                    const uint32_t *ra = src + min(i, max(vrow - 1, 0));
+                    const uint32_t *pa = psrc + min(max(i - row_tile_words, 0), vpar - 1);
+                    r[k] = *(i < row_tile_words && vrow > 0 ? ra : pa);
+                }
+            } else if (vrow > 0) {
 #pragma unroll
                 for (int k = 0; k < RW; ++k) r[k] = src[min(k * 64 + lane, vrow - 1)];
             } else {
@@ -741,7 +757,18 @@ __global__ __launch_bounds__(64 * NW, 2) void fetch_kernel(FetchArgs a) {
     auto stash_tile = [&](const uint32_t (&r)[RW]) {
         if constexpr (kFlat) {
 #pragma unroll
-            for (int k = 0; k < RW; ++k) rowsl[k * 64 + lane] = r[k];
+            for (int k = 0; k < RW; ++k) {
+                rowsl[k * 64 + lane] = r[k];
+                if constexpr (MIXED) {
+                    // parameter word j = i - row_tile_words is (token j / n_qg, group
+                    // j % n_qg), staged group-major; other lanes write a dummy word
+                    // of their own past the parameters
+                    const int i = k * 64 + lane, j = i - row_tile_words;
+                    const int t = static_cast<int>((static_cast<float>(j) + 0.5f) * a.nqg_inv);
+                    const bool is_par = i >= row_tile_words && i < tile_words;
+                    parl[is_par ? (j - t * a.n_qg) * kFetTok + t : a.n_qg * kFetTok + lane] = r[k];
+                }
+            }
             return;
         }
 #pragma unroll
@@ -799,7 +826,7 @@ __global__ __launch_bounds__(64 * NW, 2) void fetch_kernel(FetchArgs a) {
     // waiting for a tile's rows also waits for every store issued before those
     // rows were requested: with PF tiles in flight that is the stores of PF
     // tiles back, which overlaps the store latency with PF tiles of work.
-    // Branch-free DP path: the main loop covers whole tiles only and its body
+    // Branch-free path: the main loop covers whole tiles only and its body
     // has no conditions (prefetches past the run are clamped to its last tile
     // and never processed), so the compiler keeps exact wait counts across
     // it; the last partial round and a ragged final tile run after it.
@@ -948,11 +975,12 @@ int32_t launch_fetch_rw(FetchArgs a, hipStream_t stream) {
     a.lds_bias = static_cast<int>(align_up(a.lds_desc + 16, 16));
     a.lds_wave = static_cast<int>(align_up(a.lds_bias + DS * 4, 16));
     // rows of a tile back to back, plus slack for the 3-word field window of the
-    // upper operand half of a padded k-step (the branch-free DP path stashes all
+    // upper operand half of a padded k-step (the branch-free path stashes all
     // RW words per lane, so its rows area holds at least that many)
     int rows_b = static_cast<int>(align_up((kFetTok * (a.row_stride / 4) + 8) * 4, 16));
-    if (!MIXED && RW <= 8) rows_b = std::max(rows_b, RW * 64 * 4);
-    const int par_b = MIXED ? static_cast<int>(align_up(kFetTok * a.n_qg * 4, 16)) : 0;
+    if (fetch_flat<MIXED, KS, RW, NW>()) rows_b = std::max(rows_b, RW * 64 * 4);
+    // (plus one dummy word per lane for the branch-free stash)
+    const int par_b = MIXED ? static_cast<int>(align_up((kFetTok * a.n_qg + 64) * 4, 16)) : 0;
     const int out_b = static_cast<int>(align_up(kFetTok * a.opitch * 2, 16));
     a.lds_par = rows_b;
     a.lds_out = rows_b + par_b;
