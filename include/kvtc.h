@@ -222,6 +222,44 @@ int32_t kvtc_fetch(const void *state_host, const void *state_dev,
                    int64_t s_begin, int64_t s_end,
                    void *out_dev, const int64_t out_strides[4], void *hip_stream);
 
+/* One tensor's operands in a paired call (kvtc_append_kv, kvtc_fetch_kv).
+ *   state_host/state_dev  the tensor's blob in host and device memory
+ *   codes_dev, params_dev its stores (params_dev NULL in DP mode), of `capacity` rows
+ *   rows_dev   append: the input rows x [B, H, n, D] (read only), of element type dtype;
+ *              fetch: the fp16 output [B, H, s_end - s_begin, D] (dtype is ignored)
+ *   strides    element strides of rows_dev for (b, h, s, d); strides[3] must be 1 */
+typedef struct kvtc_tensor_ref {
+    const void *state_host;
+    const void *state_dev;
+    void *codes_dev;
+    void *params_dev;
+    int64_t capacity;
+    void *rows_dev;
+    int32_t dtype;
+    int32_t reserved;
+    int64_t strides[4];
+} kvtc_tensor_ref;
+
+/* Append the same rows [s0, s0 + n) to the key and the value tensor of a layer
+ * in one call (device).  The KVTC page's update_and_fetch takes the new keys
+ * and values together and the KVTC cache holds one _TensorKVTC for each; this
+ * entry point does what kvtc_append does for k and then for v, with the same
+ * arguments, arithmetic, results and errors.  Decode appends (n <= 16) of two
+ * DP tensors with the same element type and unit width run as one launch;
+ * anything else as one launch per tensor.  Both tensors are validated before
+ * anything is launched. */
+int32_t kvtc_append_kv(const kvtc_tensor_ref *k, const kvtc_tensor_ref *v,
+                       int64_t B, int64_t H, int64_t n, int64_t s0, void *hip_stream);
+
+/* Reconstruct rows [s_begin, s_end) of the key and the value tensor of a layer
+ * in one call (device): the KVTC page's update_and_fetch returns the whole
+ * reconstructed keys and values of every call.  Same results and errors as
+ * kvtc_fetch for k and then for v.  Two tensors of the same mode and head size
+ * run as one launch whose blocks cover both; otherwise one launch each.  Both
+ * tensors are validated before anything is launched. */
+int32_t kvtc_fetch_kv(const kvtc_tensor_ref *k, const kvtc_tensor_ref *v,
+                      int64_t s_begin, int64_t s_end, void *hip_stream);
+
 /* Storage accounting of one tensor over its first S rows (host).
  * KVTC page "Byte accounting" and the kvtc_bytes / pre_entropy_bytes
  * properties: order-0 Huffman per kept DP component, kept only when payload +

@@ -216,6 +216,10 @@ __global__ __launch_bounds__(kThreads) void append_kernel(AppendArgs a) {
     __syncthreads();
     const int mrow = wave * 16 + (lane & 15);   // A operand row (token) of this lane
     const int kcol = lane >> 4;                 // A/B operand k of this lane
+    // k-step order: k-step 4c + e of the contraction takes, at operand k = q, the
+    // feature 16c + 4q + e (c = 16-column chunk); every append kernel uses this
+    // order, so that a lane of the decode kernel holds its operands as whole
+    // 16-byte vectors of the basis
     for (int kc = 0; kc < nchunks; ++kc) {
         const int buf = kc & 1;
         if (kc + 1 < nchunks) load_chunk(kc + 1);
@@ -223,10 +227,10 @@ __global__ __launch_bounds__(kThreads) void append_kernel(AppendArgs a) {
         const float *vb = vs + buf * NB * 16 * kAppPad;
 #pragma unroll
         for (int ks = 0; ks < kAppKC / 4; ++ks) {
-            const double av = xb[mrow * kAppPad + ks * 4 + kcol];
+            const double av = xb[mrow * kAppPad + kcol * 4 + ks];
 #pragma unroll
             for (int nb = 0; nb < NB; ++nb) {
-                const double bv = static_cast<double>(vb[(nb * 16 + (lane & 15)) * kAppPad + ks * 4 + kcol]);
+                const double bv = static_cast<double>(vb[(nb * 16 + (lane & 15)) * kAppPad + kcol * 4 + ks]);
                 acc[nb] = __builtin_amdgcn_mfma_f64_16x16x4f64(av, bv, acc[nb], 0, 0, 0);
             }
         }
@@ -420,12 +424,13 @@ __global__ __launch_bounds__(kThreads) void append_small_kernel(AppendArgs a) {
     for (int q = 0; q < NBW; ++q) acc[q] = doublex4{0.0, 0.0, 0.0, 0.0};
     const int mrow = lane & 15, kcol = lane >> 4;
     for (int ks = 0; ks < a.dg / 4; ++ks) {
-        const double av = xs[mrow * xpitch + ks * 4 + kcol];
+        const int col = (ks >> 2) * 16 + kcol * 4 + (ks & 3);   // k-step order of append_kernel
+        const double av = xs[mrow * xpitch + col];
 #pragma unroll
         for (int q = 0; q < NBW; ++q) {
             const int nb = wave + 4 * q;
             if (nb < NB) {
-                const double bv = static_cast<double>(vs[(nb * 16 + (lane & 15)) * vpitch + ks * 4 + kcol]);
+                const double bv = static_cast<double>(vs[(nb * 16 + (lane & 15)) * vpitch + col]);
                 acc[q] = __builtin_amdgcn_mfma_f64_16x16x4f64(av, bv, acc[q], 0, 0, 0);
             }
         }
@@ -457,6 +462,97 @@ __global__ __launch_bounds__(kThreads) void append_small_kernel(AppendArgs a) {
     }
 }
 
+// One decode launch covers one tensor or two (the K and V of a layer): units
+// below `split` (blockIdx.y) belong to t[0], the rest to t[1].
+struct AppendPair {
+    AppendArgs t[2];
+    int64_t split;
+};
+
+size_t decode_lds_bytes(int dg, int row_stride) {
+    return 16 * static_cast<size_t>(dg + 1) * sizeof(double) + 16 * static_cast<size_t>(row_stride / 4) * sizeof(uint32_t);
+}
+
+// Decode append (up to 16 rows per unit, DP mode, unit width DG): one block per
+// unit, one wave per 16-slot N-block.  In the k-step order of append_kernel a
+// lane's basis operands (slot 16*wave + lane%16, features 16c + 4*(lane/16) +
+// 0..3 for k-steps 4c..4c+3) are whole 16-byte vectors, loaded straight into
+// registers: the basis never passes through LDS and every load of the block is
+// in flight before its first wait; only the centred rows are staged in LDS.  The fp64 MFMA sequence per row (operands and k order) is
+// the one of append_kernel, so a row's codes do not depend on the kernel that
+// appended it.  Rows past the valid ones are left unset in LDS: a row of the
+// MFMA result depends only on the same row of A, and those rows are not used.
+template <typename XT, int DG>
+__global__ __launch_bounds__(512) void append_decode_kernel(AppendPair m) {
+    extern __shared__ __align__(16) unsigned char smem[];
+    constexpr int XP = DG + 1;          // LDS pitch (doubles) of a centred row
+    constexpr int NKS = DG / 4;         // MFMA k-steps
+    double *xs = reinterpret_cast<double *>(smem);                    // [16][XP]
+    uint32_t *rows = reinterpret_cast<uint32_t *>(xs + 16 * XP);      // [16][row_words]
+
+    const bool second = blockIdx.y >= m.split;         // block-uniform
+    const AppendArgs &a = second ? m.t[1] : m.t[0];
+    const int u = static_cast<int>(blockIdx.y - (second ? m.split : 0));
+    const int64_t t0 = static_cast<int64_t>(blockIdx.x) * 16;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int nthreads = blockDim.x;
+    const int b = u / a.groups, g = u % a.groups;
+    const int nvalid = static_cast<int>(min<int64_t>(16, a.n - t0));
+    const int row_words = a.row_stride >> 2;
+    const bool active = wave < (a.kslots >> 4);        // this tensor's N-blocks
+    const int j = wave * 16 + (lane & 15), kq = lane >> 4;
+    const int64_t ub = static_cast<int64_t>(u) * a.kslots;
+
+    float4 vr[NKS / 4];
+    double lo = 0.0, inv = 0.0;
+    uint32_t sb = 0u;
+    if (active) {
+        const float4 *vp = reinterpret_cast<const float4 *>(a.basis + (ub + j) * DG + 4 * kq);
+#pragma unroll
+        for (int c = 0; c < NKS / 4; ++c) vr[c] = vp[4 * c];
+        lo = a.qlo[ub + j];
+        inv = a.qinv[ub + j];
+        sb = a.sbits[ub + j];
+    }
+    const XT *x = static_cast<const XT *>(a.x) + b * a.xsb + g * a.xsh + t0 * a.xss;
+    const float *mu = a.mu + static_cast<int64_t>(u) * DG;
+    for (int i = tid; i < nvalid * DG; i += nthreads) {
+        const int t = i / DG, d = i % DG;
+        xs[t * XP + d] = load_x(x + t * a.xss + d) - static_cast<double>(mu[d]);
+    }
+    for (int w = tid; w < 16 * row_words; w += nthreads) rows[w] = 0u;
+    __syncthreads();
+
+    if (active) {
+        doublex4 acc = doublex4{0.0, 0.0, 0.0, 0.0};
+        const double *xr = xs + (lane & 15) * XP + 4 * kq;
+#pragma unroll
+        for (int c = 0; c < NKS / 4; ++c) {
+            acc = __builtin_amdgcn_mfma_f64_16x16x4f64(xr[16 * c + 0], static_cast<double>(vr[c].x), acc, 0, 0, 0);
+            acc = __builtin_amdgcn_mfma_f64_16x16x4f64(xr[16 * c + 1], static_cast<double>(vr[c].y), acc, 0, 0, 0);
+            acc = __builtin_amdgcn_mfma_f64_16x16x4f64(xr[16 * c + 2], static_cast<double>(vr[c].z), acc, 0, 0, 0);
+            acc = __builtin_amdgcn_mfma_f64_16x16x4f64(xr[16 * c + 3], static_cast<double>(vr[c].w), acc, 0, 0, 0);
+        }
+        // result layout: acc[i] is token kq + 4i, slot j
+        if (j < a.ui[u].n_slots) {
+            const uint32_t off = sb & kOffsetMask, w = sb >> 24;
+            const double cmax = static_cast<double>((1u << w) - 1u);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int t = kq + 4 * i;
+                if (t < nvalid) or_field(rows + t * row_words, off, w, static_cast<uint32_t>(quantise(acc[i], lo, inv, cmax)));
+            }
+        }
+    }
+    __syncthreads();
+    if (row_words > 0) {
+        uint32_t *dst = reinterpret_cast<uint32_t *>(
+            a.codes + (static_cast<int64_t>(u) * a.capacity + a.s0 + t0) * a.row_stride);
+        for (int w = tid; w < nvalid * row_words; w += nthreads) dst[w] = rows[w];
+    }
+}
+
 // ================================================================ fetch
 struct FetchArgs {
     const uint8_t *codes;              // [U][capacity][row_stride]
@@ -470,9 +566,17 @@ struct FetchArgs {
     int dg, D, hpu, groups, kfetch, row_stride, n_qg;
     float nqg_inv;                     // 1 / n_qg (group-head mode)
     int nslices, nchunks, tiles_per_block, ntiles;
-    int64_t nblocks_real, nblocks_per_xcd;
+    int nks;                           // k-steps of this tensor (kfetch / 16)
+    int64_t nblocks;                   // blocks of this tensor
     // dynamic LDS carve-up (bytes)
     int lds_w, lds_desc, lds_bias, lds_wave, lds_rows, lds_par, lds_out, wpitch, opitch;
+};
+
+// One fetch launch covers one tensor or two (the K and V of a layer): the
+// first `split` logical blocks belong to t[0], the rest to t[1].
+struct FetchPair {
+    FetchArgs t[2];
+    int64_t split, nblocks_real, nblocks_per_xcd;
 };
 
 typedef _Float16 half2 __attribute__((ext_vector_type(2)));
@@ -655,7 +759,7 @@ constexpr int fetch_prefetch() { return RW <= 8 ? (MIXED ? 2 : 3) : (RW <= 16 &&
 // per store; with eight waves (long contractions) one block does, and the
 // epilogue writes the slice in two halves.
 template <bool MIXED, int NDB, int KS, int RW, int NW, int PF>
-__global__ __launch_bounds__(64 * NW, 2) void fetch_kernel(FetchArgs a) {
+__global__ __launch_bounds__(64 * NW, 2) void fetch_kernel(FetchPair m) {
     extern __shared__ __align__(16) unsigned char smem[];
     constexpr int DS = 32 * NDB;
     constexpr int NT = 64 * NW;
@@ -663,8 +767,11 @@ __global__ __launch_bounds__(64 * NW, 2) void fetch_kernel(FetchArgs a) {
     // blocks are dealt to the 8 XCDs round-robin; regroup them so that the
     // blocks of one unit (and its d-slices) run on the same XCD
     const int64_t bid = blockIdx.x;
-    const int64_t logical = (bid & 7) * a.nblocks_per_xcd + (bid >> 3);
-    if (logical >= a.nblocks_real) return;
+    int64_t logical = (bid & 7) * m.nblocks_per_xcd + (bid >> 3);
+    if (logical >= m.nblocks_real) return;
+    const bool second = logical >= m.split;           // block-uniform
+    const FetchArgs &a = second ? m.t[1] : m.t[0];
+    if (second) logical -= m.split;
     const int slice = static_cast<int>(logical % a.nslices);
     const int64_t rest = logical / a.nslices;
     const int chunk = static_cast<int>(rest % a.nchunks);
@@ -790,11 +897,12 @@ __global__ __launch_bounds__(64 * NW, 2) void fetch_kernel(FetchArgs a) {
     const uint32_t half_k = lane >> 5;    // this lane feeds fetch slots 8..15 of a k-step if set
 
     // the unit's k-step descriptors (first field offset, width, quantisation
-    // group), block-uniform, held in scalar registers for all tiles
+    // group), block-uniform, held in scalar registers for all tiles; k-steps
+    // past this tensor's own count (a launch shared with a wider tensor) are empty
     uint32_t kd[KS];
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks)
-        kd[ks] = __builtin_amdgcn_readfirstlane(a.kdesc[static_cast<int64_t>(u) * KS + ks]);
+        kd[ks] = ks < a.nks ? __builtin_amdgcn_readfirstlane(a.kdesc[static_cast<int64_t>(u) * a.nks + ks]) : 0u;
 
     auto process = [&](int tile, auto full) {
         constexpr bool kFull = decltype(full)::value;
@@ -964,79 +1072,92 @@ int32_t launch_append(const AppendArgs &a, int64_t ntiles, int64_t U, int nb, hi
 }
 
 template <bool MIXED, int NDB, int KS, int RW>
-int32_t launch_fetch_rw(FetchArgs a, hipStream_t stream) {
+int32_t launch_fetch_rw(FetchPair m, int nt, hipStream_t stream) {
     constexpr int DS = 32 * NDB, NW = fetch_waves<NDB, KS>();
     constexpr int NH = fetch_epilogue_blocks<NDB, NW>();
-    if (kFetTok * (a.row_stride / 4 + (MIXED ? a.n_qg : 0)) > 64 * RW) return KVTC_E_SHAPE;
-    a.wpitch = a.kfetch + 8;
-    a.opitch = 32 * NH + 8;
-    a.lds_w = 0;
-    a.lds_desc = static_cast<int>(align_up(static_cast<uint64_t>(DS) * a.wpitch * 2, 16));
-    a.lds_bias = static_cast<int>(align_up(a.lds_desc + 16, 16));
-    a.lds_wave = static_cast<int>(align_up(a.lds_bias + DS * 4, 16));
-    // rows of a tile back to back, plus slack for the 3-word field window of the
-    // upper operand half of a padded k-step (the branch-free path stashes all
-    // RW words per lane, so its rows area holds at least that many)
-    int rows_b = static_cast<int>(align_up((kFetTok * (a.row_stride / 4) + 8) * 4, 16));
-    if (fetch_flat<MIXED, KS, RW, NW>()) rows_b = std::max(rows_b, RW * 64 * 4);
-    // (plus one dummy word per lane for the branch-free stash)
-    const int par_b = MIXED ? static_cast<int>(align_up((kFetTok * a.n_qg + 64) * 4, 16)) : 0;
-    const int out_b = static_cast<int>(align_up(kFetTok * a.opitch * 2, 16));
-    a.lds_par = rows_b;
-    a.lds_out = rows_b + par_b;
-    a.lds_rows = rows_b + par_b + out_b;                 // per-wave bytes
-    const size_t lds = a.lds_wave + NW * static_cast<size_t>(a.lds_rows);
+    size_t lds = 0;
+    for (int i = 0; i < nt; ++i) {
+        FetchArgs &a = m.t[i];
+        if (kFetTok * (a.row_stride / 4 + (MIXED ? a.n_qg : 0)) > 64 * RW) return KVTC_E_SHAPE;
+        a.wpitch = a.kfetch + 8;
+        a.opitch = 32 * NH + 8;
+        a.lds_w = 0;
+        a.lds_desc = static_cast<int>(align_up(static_cast<uint64_t>(DS) * a.wpitch * 2, 16));
+        a.lds_bias = static_cast<int>(align_up(a.lds_desc + 16, 16));
+        a.lds_wave = static_cast<int>(align_up(a.lds_bias + DS * 4, 16));
+        // rows of a tile back to back, plus slack for the 3-word field window of the
+        // upper operand half of a padded k-step (the branch-free path stashes all
+        // RW words per lane, so its rows area holds at least that many)
+        int rows_b = static_cast<int>(align_up((kFetTok * (a.row_stride / 4) + 8) * 4, 16));
+        if (fetch_flat<MIXED, KS, RW, NW>()) rows_b = std::max(rows_b, RW * 64 * 4);
+        // (plus one dummy word per lane for the branch-free stash)
+        const int par_b = MIXED ? static_cast<int>(align_up((kFetTok * a.n_qg + 64) * 4, 16)) : 0;
+        const int out_b = static_cast<int>(align_up(kFetTok * a.opitch * 2, 16));
+        a.lds_par = rows_b;
+        a.lds_out = rows_b + par_b;
+        a.lds_rows = rows_b + par_b + out_b;                 // per-wave bytes
+        lds = std::max(lds, a.lds_wave + NW * static_cast<size_t>(a.lds_rows));
+    }
     if (lds > kLdsMax) return KVTC_E_SHAPE;
-    const int64_t grid = a.nblocks_per_xcd * 8;
+    const int64_t grid = m.nblocks_per_xcd * 8;
     auto kern = fetch_kernel<MIXED, NDB, KS, RW, NW, fetch_prefetch<MIXED, RW>()>;
     if (!allow_lds(reinterpret_cast<const void *>(kern))) return KVTC_E_DEVICE;
-    hipLaunchKernelGGL(kern, dim3(static_cast<unsigned>(grid)), dim3(64 * NW), lds, stream, a);
+    hipLaunchKernelGGL(kern, dim3(static_cast<unsigned>(grid)), dim3(64 * NW), lds, stream, m);
     return hipGetLastError() == hipSuccess ? KVTC_OK : KVTC_E_DEVICE;
 }
 
 // Register staging of a tile's rows: the narrowest instantiated width that
 // holds them (whole-head tiles: 8, 16 or 24 words per lane; 64-column: 8 or 24).
 template <bool MIXED, int NDB, int KS>
-int32_t launch_fetch_ks(FetchArgs a, int rw, hipStream_t stream) {
-    if (rw <= 8) return launch_fetch_rw<MIXED, NDB, KS, 8>(a, stream);
-    if (NDB == 4 && rw <= 16) return launch_fetch_rw<MIXED, NDB, KS, (NDB == 4 ? 16 : 24)>(a, stream);
-    if (rw <= kFetchRegWords) return launch_fetch_rw<MIXED, NDB, KS, kFetchRegWords>(a, stream);
+int32_t launch_fetch_ks(const FetchPair &m, int nt, int rw, hipStream_t stream) {
+    if (rw <= 8) return launch_fetch_rw<MIXED, NDB, KS, 8>(m, nt, stream);
+    if (NDB == 4 && rw <= 16) return launch_fetch_rw<MIXED, NDB, KS, (NDB == 4 ? 16 : 24)>(m, nt, stream);
+    if (rw <= kFetchRegWords) return launch_fetch_rw<MIXED, NDB, KS, kFetchRegWords>(m, nt, stream);
     return KVTC_E_SHAPE;
 }
 
 template <bool MIXED, int NDB>
-int32_t launch_fetch(FetchArgs a, int rw, hipStream_t stream) {
-    switch (a.kfetch / 16) {
-        case 1: return launch_fetch_ks<MIXED, NDB, 1>(a, rw, stream);
-        case 2: return launch_fetch_ks<MIXED, NDB, 2>(a, rw, stream);
-        case 3: return launch_fetch_ks<MIXED, NDB, 3>(a, rw, stream);
-        case 4: return launch_fetch_ks<MIXED, NDB, 4>(a, rw, stream);
-        case 5: return launch_fetch_ks<MIXED, NDB, 5>(a, rw, stream);
-        case 6: return launch_fetch_ks<MIXED, NDB, 6>(a, rw, stream);
-        case 7: return launch_fetch_ks<MIXED, NDB, 7>(a, rw, stream);
-        case 8: return launch_fetch_ks<MIXED, NDB, 8>(a, rw, stream);
-        case 9: return launch_fetch_ks<MIXED, NDB, 9>(a, rw, stream);
-        case 10: return launch_fetch_ks<MIXED, NDB, 10>(a, rw, stream);
-        case 11: return launch_fetch_ks<MIXED, NDB, 11>(a, rw, stream);
-        case 12: return launch_fetch_ks<MIXED, NDB, 12>(a, rw, stream);
-        case 13: return launch_fetch_ks<MIXED, NDB, 13>(a, rw, stream);
-        case 14: return launch_fetch_ks<MIXED, NDB, 14>(a, rw, stream);
-        case 15: return launch_fetch_ks<MIXED, NDB, 15>(a, rw, stream);
-        case 16: return launch_fetch_ks<MIXED, NDB, 16>(a, rw, stream);
+int32_t launch_fetch(const FetchPair &m, int nt, int ks, int rw, hipStream_t stream) {
+    switch (ks) {
+        case 1: return launch_fetch_ks<MIXED, NDB, 1>(m, nt, rw, stream);
+        case 2: return launch_fetch_ks<MIXED, NDB, 2>(m, nt, rw, stream);
+        case 3: return launch_fetch_ks<MIXED, NDB, 3>(m, nt, rw, stream);
+        case 4: return launch_fetch_ks<MIXED, NDB, 4>(m, nt, rw, stream);
+        case 5: return launch_fetch_ks<MIXED, NDB, 5>(m, nt, rw, stream);
+        case 6: return launch_fetch_ks<MIXED, NDB, 6>(m, nt, rw, stream);
+        case 7: return launch_fetch_ks<MIXED, NDB, 7>(m, nt, rw, stream);
+        case 8: return launch_fetch_ks<MIXED, NDB, 8>(m, nt, rw, stream);
+        case 9: return launch_fetch_ks<MIXED, NDB, 9>(m, nt, rw, stream);
+        case 10: return launch_fetch_ks<MIXED, NDB, 10>(m, nt, rw, stream);
+        case 11: return launch_fetch_ks<MIXED, NDB, 11>(m, nt, rw, stream);
+        case 12: return launch_fetch_ks<MIXED, NDB, 12>(m, nt, rw, stream);
+        case 13: return launch_fetch_ks<MIXED, NDB, 13>(m, nt, rw, stream);
+        case 14: return launch_fetch_ks<MIXED, NDB, 14>(m, nt, rw, stream);
+        case 15: return launch_fetch_ks<MIXED, NDB, 15>(m, nt, rw, stream);
+        case 16: return launch_fetch_ks<MIXED, NDB, 16>(m, nt, rw, stream);
         default: return KVTC_E_SHAPE;
     }
 }
 
-}  // namespace
-}  // namespace kvtc
+// ============================================================== call plans
+// Everything a call needs to launch, after its arguments have been validated.
+struct AppendPlan {
+    AppendArgs a;
+    int64_t units, ntiles;
+    int nb;                            // 16-slot N-blocks of the bulk kernels
+    int32_t dtype;
+    bool mixed;
+};
 
-using namespace kvtc;
+struct FetchPlan {
+    FetchArgs a;
+    int ds, rw;                        // columns per block (128 or 64), row words per lane
+    bool mixed;
+};
 
-extern "C" {
-
-int32_t kvtc_append(const void *state_host, const void *state_dev, const void *x_dev, int32_t dtype,
+int32_t plan_append(const void *state_host, const void *state_dev, const void *x_dev, int32_t dtype,
                     const int64_t x_strides[4], int64_t B, int64_t H, int64_t n, int64_t s0,
-                    void *codes_dev, void *params_dev, int64_t capacity, void *hip_stream) {
+                    void *codes_dev, void *params_dev, int64_t capacity, AppendPlan *p) {
     const kvtc_state_header *h = nullptr;
     int32_t st = check_state(state_host, &h);
     if (st != KVTC_OK) return st;
@@ -1051,20 +1172,23 @@ int32_t kvtc_append(const void *state_host, const void *state_dev, const void *x
         return KVTC_E_SHAPE;
     const bool mixed = h->mode == KVTC_MODE_MIXED;
     if (mixed && h->group_size % 16 != 0) return KVTC_E_STATE;
+    *p = AppendPlan{};
+    p->a.n = n;
     if (n == 0) return KVTC_OK;
     if (!x_dev) return KVTC_E_ARG;
     if (h->row_stride > 0 && (!codes_dev || reinterpret_cast<uintptr_t>(codes_dev) % 4 != 0)) return KVTC_E_ARG;
     if (mixed && (!params_dev || reinterpret_cast<uintptr_t>(params_dev) % 4 != 0)) return KVTC_E_ARG;
     const int nb = append_nb(h->kslots);
     if (nb < 0) return KVTC_E_SHAPE;
+    const int64_t ntiles = (n + kAppTok - 1) / kAppTok;
+    if (ntiles > 0x7FFFFFFF) return KVTC_E_SHAPE;
 
     const char *sd = static_cast<const char *>(state_dev);
-    AppendArgs a{};
+    AppendArgs &a = p->a;
     a.x = x_dev;
     a.xsb = x_strides[0];
     a.xsh = x_strides[1];
     a.xss = x_strides[2];
-    a.n = n;
     a.s0 = s0;
     a.capacity = capacity;
     a.ui = reinterpret_cast<const kvtc_unit_info *>(sd + h->off_unit);
@@ -1090,19 +1214,68 @@ int32_t kvtc_append(const void *state_host, const void *state_dev, const void *x
     }
     a.inv_dg = 1.0f / static_cast<float>(h->dg);
     a.inv_q4 = 4.0f / static_cast<float>(h->dg);
-    const int64_t ntiles = (n + kAppTok - 1) / kAppTok;
-    if (ntiles > 0x7FFFFFFF) return KVTC_E_SHAPE;
-    hipStream_t stream = static_cast<hipStream_t>(hip_stream);
-    if (dtype == KVTC_F16)
-        return mixed ? launch_append<true, _Float16>(a, ntiles, h->units, nb, stream)
-                     : launch_append<false, _Float16>(a, ntiles, h->units, nb, stream);
-    return mixed ? launch_append<true, float>(a, ntiles, h->units, nb, stream)
-                 : launch_append<false, float>(a, ntiles, h->units, nb, stream);
+    p->units = h->units;
+    p->ntiles = ntiles;
+    p->nb = nb;
+    p->dtype = dtype;
+    p->mixed = mixed;
+    return KVTC_OK;
 }
 
-int32_t kvtc_fetch(const void *state_host, const void *state_dev, const void *codes_dev,
-                   const void *params_dev, int64_t capacity, int64_t s_begin, int64_t s_end,
-                   void *out_dev, const int64_t out_strides[4], void *hip_stream) {
+// Decode appends of DP tensors (one head per unit) whose unit width has a
+// register-resident kernel; one wave per 16 slots, at most dg slots.
+bool decode_path(const AppendPlan &p) {
+    return !p.mixed && p.a.n <= kSmallRows && p.a.hpu == 1 && (p.a.dg == 64 || p.a.dg == 128) &&
+           p.a.kslots <= p.a.dg;
+}
+
+template <typename XT, int DG>
+int32_t launch_decode_dg(const AppendPair &m, int64_t nrows, int64_t units, int nblk, hipStream_t stream) {
+    int row_stride = 0;
+    for (int i = 0; i < (m.split < units ? 2 : 1); ++i) row_stride = std::max(row_stride, m.t[i].row_stride);
+    const size_t lds = decode_lds_bytes(DG, row_stride);
+    auto kern = append_decode_kernel<XT, DG>;
+    const int64_t blocks = (nrows + kSmallRows - 1) / kSmallRows;
+    hipLaunchKernelGGL(kern, dim3(static_cast<unsigned>(blocks), static_cast<unsigned>(units)), dim3(64 * nblk), lds,
+                       stream, m);
+    return hipGetLastError() == hipSuccess ? KVTC_OK : KVTC_E_DEVICE;
+}
+
+// One decode launch for one plan (p1 == NULL) or for two plans of the same
+// element type and unit width (rows of every unit of p0, then of p1).
+int32_t launch_decode(const AppendPlan &p0, const AppendPlan *p1, hipStream_t stream) {
+    AppendPair m{};
+    m.t[0] = p0.a;
+    m.split = p0.units;
+    int64_t units = p0.units;
+    int nblk = p0.a.kslots / 16;
+    if (p1) {
+        m.t[1] = p1->a;
+        units += p1->units;
+        nblk = std::max(nblk, p1->a.kslots / 16);
+    }
+    if (units > 65535) return KVTC_E_SHAPE;
+    const bool f16 = p0.dtype == KVTC_F16;
+    if (p0.a.dg == 128)
+        return f16 ? launch_decode_dg<_Float16, 128>(m, p0.a.n, units, nblk, stream)
+                   : launch_decode_dg<float, 128>(m, p0.a.n, units, nblk, stream);
+    return f16 ? launch_decode_dg<_Float16, 64>(m, p0.a.n, units, nblk, stream)
+               : launch_decode_dg<float, 64>(m, p0.a.n, units, nblk, stream);
+}
+
+int32_t launch_append_plan(const AppendPlan &p, hipStream_t stream) {
+    if (p.a.n == 0) return KVTC_OK;
+    if (decode_path(p)) return launch_decode(p, nullptr, stream);
+    if (p.dtype == KVTC_F16)
+        return p.mixed ? launch_append<true, _Float16>(p.a, p.ntiles, p.units, p.nb, stream)
+                       : launch_append<false, _Float16>(p.a, p.ntiles, p.units, p.nb, stream);
+    return p.mixed ? launch_append<true, float>(p.a, p.ntiles, p.units, p.nb, stream)
+                   : launch_append<false, float>(p.a, p.ntiles, p.units, p.nb, stream);
+}
+
+int32_t plan_fetch(const void *state_host, const void *state_dev, const void *codes_dev, const void *params_dev,
+                   int64_t capacity, int64_t s_begin, int64_t s_end, void *out_dev, const int64_t out_strides[4],
+                   FetchPlan *p) {
     const kvtc_state_header *h = nullptr;
     int32_t st = check_state(state_host, &h);
     if (st != KVTC_OK) return st;
@@ -1115,6 +1288,7 @@ int32_t kvtc_fetch(const void *state_host, const void *state_dev, const void *co
     if (h->kfetch > kMaxSlots || h->head_dim % 64 != 0) return KVTC_E_SHAPE;
     const int tw = h->row_stride / 4 + (mixed ? h->n_qgroups : 0);
     if (kFetTok * tw > 64 * kFetchRegWords) return KVTC_E_SHAPE;
+    *p = FetchPlan{};
     if (s_end == s_begin) return KVTC_OK;
     if (!out_dev || reinterpret_cast<uintptr_t>(out_dev) % 16 != 0) return KVTC_E_ARG;
     if ((out_strides[0] * 2) % 16 || (out_strides[1] * 2) % 16 || (out_strides[2] * 2) % 16) return KVTC_E_SHAPE;
@@ -1122,7 +1296,7 @@ int32_t kvtc_fetch(const void *state_host, const void *state_dev, const void *co
     if (mixed && (!params_dev || reinterpret_cast<uintptr_t>(params_dev) % 4 != 0)) return KVTC_E_ARG;
 
     const char *sd = static_cast<const char *>(state_dev);
-    FetchArgs a{};
+    FetchArgs &a = p->a;
     a.codes = static_cast<const uint8_t *>(codes_dev);
     a.params = static_cast<const uint32_t *>(params_dev);
     a.capacity = capacity;
@@ -1140,6 +1314,7 @@ int32_t kvtc_fetch(const void *state_host, const void *state_dev, const void *co
     a.hpu = h->heads_per_unit;
     a.groups = static_cast<int>(h->heads / h->heads_per_unit);
     a.kfetch = h->kfetch;
+    a.nks = h->kfetch / 16;
     a.row_stride = h->row_stride;
     a.n_qg = h->n_qgroups;
     a.nqg_inv = mixed ? 1.0f / static_cast<float>(h->n_qgroups) : 0.0f;
@@ -1157,13 +1332,96 @@ int32_t kvtc_fetch(const void *state_host, const void *state_dev, const void *co
     const int64_t tpb = std::min<int64_t>(std::max<int64_t>(nw, (work + target - 1) / target), ntiles);
     a.tiles_per_block = static_cast<int>(tpb);
     a.nchunks = static_cast<int>((ntiles + tpb - 1) / tpb);
-    a.nblocks_real = h->units * a.nslices * a.nchunks;
-    a.nblocks_per_xcd = (a.nblocks_real + 7) / 8;
-    if (a.nblocks_per_xcd * 8 > 0x7FFFFFFF) return KVTC_E_SHAPE;
+    a.nblocks = h->units * a.nslices * a.nchunks;
+    if (a.nblocks > 0x7FFFFFFF) return KVTC_E_SHAPE;
+    p->ds = DS;
+    p->rw = (kFetTok * tw + 63) / 64;
+    p->mixed = mixed;
+    return KVTC_OK;
+}
+
+// One fetch launch for one plan (p1 == NULL) or for two plans of the same
+// mode and block width; the kernel is instantiated for the wider contraction.
+int32_t launch_fetch_plans(const FetchPlan &p0, const FetchPlan *p1, hipStream_t stream) {
+    FetchPair m{};
+    m.t[0] = p0.a;
+    m.split = p0.a.nblocks;
+    m.nblocks_real = p0.a.nblocks;
+    int ks = p0.a.nks, rw = p0.rw, nt = 1;
+    if (p1) {
+        m.t[1] = p1->a;
+        m.nblocks_real += p1->a.nblocks;
+        ks = std::max(ks, p1->a.nks);
+        rw = std::max(rw, p1->rw);
+        nt = 2;
+    }
+    m.nblocks_per_xcd = (m.nblocks_real + 7) / 8;
+    if (m.nblocks_per_xcd * 8 > 0x7FFFFFFF) return KVTC_E_SHAPE;
+    if (p0.ds == 128)
+        return p0.mixed ? launch_fetch<true, 4>(m, nt, ks, rw, stream) : launch_fetch<false, 4>(m, nt, ks, rw, stream);
+    return p0.mixed ? launch_fetch<true, 2>(m, nt, ks, rw, stream) : launch_fetch<false, 2>(m, nt, ks, rw, stream);
+}
+
+}  // namespace
+}  // namespace kvtc
+
+using namespace kvtc;
+
+extern "C" {
+
+int32_t kvtc_append(const void *state_host, const void *state_dev, const void *x_dev, int32_t dtype,
+                    const int64_t x_strides[4], int64_t B, int64_t H, int64_t n, int64_t s0,
+                    void *codes_dev, void *params_dev, int64_t capacity, void *hip_stream) {
+    AppendPlan p;
+    const int32_t st = plan_append(state_host, state_dev, x_dev, dtype, x_strides, B, H, n, s0, codes_dev,
+                                   params_dev, capacity, &p);
+    if (st != KVTC_OK) return st;
+    return launch_append_plan(p, static_cast<hipStream_t>(hip_stream));
+}
+
+int32_t kvtc_fetch(const void *state_host, const void *state_dev, const void *codes_dev,
+                   const void *params_dev, int64_t capacity, int64_t s_begin, int64_t s_end,
+                   void *out_dev, const int64_t out_strides[4], void *hip_stream) {
+    FetchPlan p;
+    const int32_t st = plan_fetch(state_host, state_dev, codes_dev, params_dev, capacity, s_begin, s_end, out_dev,
+                                  out_strides, &p);
+    if (st != KVTC_OK || s_end == s_begin) return st;
+    return launch_fetch_plans(p, nullptr, static_cast<hipStream_t>(hip_stream));
+}
+
+int32_t kvtc_append_kv(const kvtc_tensor_ref *k, const kvtc_tensor_ref *v, int64_t B, int64_t H, int64_t n,
+                       int64_t s0, void *hip_stream) {
+    if (!k || !v) return KVTC_E_ARG;
+    AppendPlan pk, pv;
+    int32_t st = plan_append(k->state_host, k->state_dev, k->rows_dev, k->dtype, k->strides, B, H, n, s0,
+                             k->codes_dev, k->params_dev, k->capacity, &pk);
+    if (st != KVTC_OK) return st;
+    st = plan_append(v->state_host, v->state_dev, v->rows_dev, v->dtype, v->strides, B, H, n, s0, v->codes_dev,
+                     v->params_dev, v->capacity, &pv);
+    if (st != KVTC_OK || n == 0) return st;
     hipStream_t stream = static_cast<hipStream_t>(hip_stream);
-    const int rw = (kFetTok * tw + 63) / 64;
-    if (DS == 128) return mixed ? launch_fetch<true, 4>(a, rw, stream) : launch_fetch<false, 4>(a, rw, stream);
-    return mixed ? launch_fetch<true, 2>(a, rw, stream) : launch_fetch<false, 2>(a, rw, stream);
+    if (decode_path(pk) && decode_path(pv) && pk.dtype == pv.dtype && pk.a.dg == pv.a.dg)
+        return launch_decode(pk, &pv, stream);
+    st = launch_append_plan(pk, stream);
+    if (st != KVTC_OK) return st;
+    return launch_append_plan(pv, stream);
+}
+
+int32_t kvtc_fetch_kv(const kvtc_tensor_ref *k, const kvtc_tensor_ref *v, int64_t s_begin, int64_t s_end,
+                      void *hip_stream) {
+    if (!k || !v) return KVTC_E_ARG;
+    FetchPlan pk, pv;
+    int32_t st = plan_fetch(k->state_host, k->state_dev, k->codes_dev, k->params_dev, k->capacity, s_begin, s_end,
+                            k->rows_dev, k->strides, &pk);
+    if (st != KVTC_OK) return st;
+    st = plan_fetch(v->state_host, v->state_dev, v->codes_dev, v->params_dev, v->capacity, s_begin, s_end,
+                    v->rows_dev, v->strides, &pv);
+    if (st != KVTC_OK || s_end == s_begin) return st;
+    hipStream_t stream = static_cast<hipStream_t>(hip_stream);
+    if (pk.mixed == pv.mixed && pk.ds == pv.ds) return launch_fetch_plans(pk, &pv, stream);
+    st = launch_fetch_plans(pk, nullptr, stream);
+    if (st != KVTC_OK) return st;
+    return launch_fetch_plans(pv, nullptr, stream);
 }
 
 }  // extern "C"

@@ -67,6 +67,13 @@ class BytesReport(C.Structure):
         return {f[0]: int(getattr(self, f[0])) for f in self._fields_}
 
 
+class TensorRef(C.Structure):
+    """One tensor's operands of a paired call (kvtc_tensor_ref)."""
+    _fields_ = [("state_host", C.c_void_p), ("state_dev", C.c_void_p), ("codes_dev", C.c_void_p),
+                ("params_dev", C.c_void_p), ("capacity", C.c_int64), ("rows_dev", C.c_void_p),
+                ("dtype", C.c_int32), ("reserved", C.c_int32), ("strides", C.c_int64 * 4)]
+
+
 if not os.path.exists(LIB_PATH):
     raise ImportError(f"{LIB_PATH} is not built; run python -m kv_cache_compression_kvtc_amd.build")
 _lib = C.CDLL(LIB_PATH)
@@ -84,6 +91,8 @@ _sig = {
     "kvtc_append": (_i32, [_vp, _vp, _vp, _i32, _P64, _i64, _i64, _i64, _i64, _vp, _vp, _i64, _vp]),
     "kvtc_fetch": (_i32, [_vp, _vp, _vp, _vp, _i64, _i64, _i64, _vp, _P64, _vp]),
     "kvtc_bytes": (_i32, [_vp, _vp, _vp, _i64, _i64, C.POINTER(BytesReport)]),
+    "kvtc_append_kv": (_i32, [C.POINTER(TensorRef), C.POINTER(TensorRef), _i64, _i64, _i64, _i64, _vp]),
+    "kvtc_fetch_kv": (_i32, [C.POINTER(TensorRef), C.POINTER(TensorRef), _i64, _i64, _vp]),
 }
 for _name, (_res, _args) in _sig.items():
     _f = getattr(_lib, _name)
@@ -254,6 +263,56 @@ def kvtc_fetch(blob: np.ndarray, blob_dev, codes, params, capacity: int, s_begin
                            s_begin, s_end, _dev_ptr(out), _strides4(out), _stream_ptr(stream)), "kvtc_fetch")
 
 
+def _tensor_ref(blob, blob_dev, codes, params, capacity, rows, dtype) -> TensorRef:
+    ref = TensorRef()
+    ref.state_host, ref.state_dev = _host_ptr(blob), _dev_ptr(blob_dev)
+    ref.codes_dev, ref.params_dev = _dev_ptr(codes), _dev_ptr(params)
+    ref.capacity = capacity
+    ref.rows_dev = _dev_ptr(rows)
+    ref.dtype = dtype
+    for i, st in enumerate(rows.stride()):
+        ref.strides[i] = int(st)
+    return ref
+
+
+def kvtc_append_kv(k, v, s0: int, capacity: int, stream=None):
+    """Append rows to the key and the value tensor in one call.  ``k`` and ``v`` are
+    (blob, blob_dev, x, codes, params) with x a device tensor [B, H, n, D]; both x
+    must have the same shape.  Same results as kvtc_append on each."""
+    import torch
+    refs = []
+    for (blob, blob_dev, x, codes, params) in (k, v):
+        dtype = {torch.float16: F16, torch.float32: F32}.get(x.dtype)
+        if dtype is None:
+            raise KVTCError(E_DTYPE, "kvtc_append_kv")
+        h = _check_buffers(blob, blob_dev, codes, params, capacity, "kvtc_append_kv")
+        if x.dim() != 4 or not x.is_cuda or x.shape[3] != h.head_dim:
+            raise KVTCError(E_SHAPE, "kvtc_append_kv: x must be a device tensor [B, H, n, D]")
+        refs.append(_tensor_ref(blob, blob_dev, codes, params, capacity, x, dtype))
+    if tuple(k[2].shape) != tuple(v[2].shape):
+        raise KVTCError(E_SHAPE, "kvtc_append_kv: key and value rows differ in shape")
+    B, H, n, _ = k[2].shape
+    _check(_lib.kvtc_append_kv(C.byref(refs[0]), C.byref(refs[1]), B, H, n, s0, _stream_ptr(stream)),
+           "kvtc_append_kv")
+
+
+def kvtc_fetch_kv(k, v, capacity: int, s_begin: int, s_end: int, stream=None):
+    """Reconstruct rows [s_begin, s_end) of the key and the value tensor in one call.
+    ``k`` and ``v`` are (blob, blob_dev, codes, params, out) with out an fp16 device
+    tensor [B, H, s_end - s_begin, D].  Same results as kvtc_fetch on each."""
+    import torch
+    refs = []
+    for (blob, blob_dev, codes, params, out) in (k, v):
+        if out.dtype != torch.float16:
+            raise KVTCError(E_DTYPE, "kvtc_fetch_kv")
+        h = _check_buffers(blob, blob_dev, codes, params, capacity, "kvtc_fetch_kv")
+        if not out.is_cuda or tuple(out.shape) != (h.batch, h.heads, s_end - s_begin, h.head_dim):
+            raise KVTCError(E_SHAPE, "kvtc_fetch_kv: out must be a device tensor [B, H, s_end - s_begin, D]")
+        refs.append(_tensor_ref(blob, blob_dev, codes, params, capacity, out, F16))
+    _check(_lib.kvtc_fetch_kv(C.byref(refs[0]), C.byref(refs[1]), s_begin, s_end, _stream_ptr(stream)),
+           "kvtc_fetch_kv")
+
+
 # ---------------------------------------------------------------- blob introspection
 def header(blob: np.ndarray) -> StateHeader:
     return StateHeader.from_buffer_copy(blob[: C.sizeof(StateHeader)].tobytes())
@@ -350,3 +409,66 @@ class PreparedFetch:
         a = self._args
         _check(self._fn(a[0], a[1], a[2], a[3], self.capacity, s0, s1, self._out + s0 * self._os,
                         self._strides, self._stream), "kvtc_fetch")
+
+
+class PreparedAppendKV:
+    """kvtc_append_kv with every buffer checked once: ``k`` and ``v`` are
+    (blob, blob_dev, x_full, codes, params) with x_full [B, H, N, D] device rows of
+    the same shape; ``call(s0, s1)`` appends rows [s0, s1) of both at store rows [s0, s1)."""
+
+    def __init__(self, k, v, capacity, stream=None):
+        import torch
+        self._keep = (k, v)
+        self._refs = []
+        for (blob, blob_dev, x, codes, params) in (k, v):
+            dtype = {torch.float16: F16, torch.float32: F32}.get(x.dtype)
+            if dtype is None:
+                raise KVTCError(E_DTYPE, "PreparedAppendKV")
+            h = _check_buffers(blob, blob_dev, codes, params, capacity, "PreparedAppendKV")
+            if x.dim() != 4 or not x.is_cuda or x.shape[3] != h.head_dim:
+                raise KVTCError(E_SHAPE, "PreparedAppendKV: x must be a device tensor [B, H, N, D]")
+            self._refs.append(_tensor_ref(blob, blob_dev, codes, params, capacity, x, dtype))
+        if tuple(k[2].shape) != tuple(v[2].shape):
+            raise KVTCError(E_SHAPE, "PreparedAppendKV: key and value rows differ in shape")
+        self.B, self.H, self.N = int(k[2].shape[0]), int(k[2].shape[1]), int(k[2].shape[2])
+        self._x = [k[2].data_ptr(), v[2].data_ptr()]
+        self._xs = [int(t[2].stride(2)) * t[2].element_size() for t in (k, v)]
+        self._stream = _stream_ptr(stream)
+        self._fn = _lib.kvtc_append_kv
+
+    def __call__(self, s0: int, s1: int):
+        if not (0 <= s0 <= s1 <= self.N):
+            raise KVTCError(E_ARG, "PreparedAppendKV: rows outside x")
+        for i in range(2):
+            self._refs[i].rows_dev = self._x[i] + s0 * self._xs[i]
+        _check(self._fn(C.byref(self._refs[0]), C.byref(self._refs[1]), self.B, self.H, s1 - s0, s0,
+                        self._stream), "kvtc_append_kv")
+
+
+class PreparedFetchKV:
+    """kvtc_fetch_kv with every buffer checked once: ``k`` and ``v`` are
+    (blob, blob_dev, codes, params, out_full) with out_full fp16 [B, H, >=capacity, D];
+    ``call(s0, s1)`` reconstructs store rows [s0, s1) of both into rows [s0, s1) of out_full."""
+
+    def __init__(self, k, v, capacity, stream=None):
+        import torch
+        self._keep = (k, v)
+        self._refs = []
+        self.capacity = capacity
+        for (blob, blob_dev, codes, params, out) in (k, v):
+            if out.dtype != torch.float16:
+                raise KVTCError(E_DTYPE, "PreparedFetchKV")
+            h = _check_buffers(blob, blob_dev, codes, params, capacity, "PreparedFetchKV")
+            if not out.is_cuda or out.dim() != 4 or tuple(out.shape[:2]) != (h.batch, h.heads) \
+                    or out.shape[2] < capacity or out.shape[3] != h.head_dim:
+                raise KVTCError(E_SHAPE, "PreparedFetchKV: out must be a device tensor [B, H, >=capacity, D]")
+            self._refs.append(_tensor_ref(blob, blob_dev, codes, params, capacity, out, F16))
+        self._out = [k[4].data_ptr(), v[4].data_ptr()]
+        self._os = [int(t[4].stride(2)) * t[4].element_size() for t in (k, v)]
+        self._stream = _stream_ptr(stream)
+        self._fn = _lib.kvtc_fetch_kv
+
+    def __call__(self, s0: int, s1: int):
+        for i in range(2):
+            self._refs[i].rows_dev = self._out[i] + s0 * self._os[i]
+        _check(self._fn(C.byref(self._refs[0]), C.byref(self._refs[1]), s0, s1, self._stream), "kvtc_fetch_kv")

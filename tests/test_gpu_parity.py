@@ -374,3 +374,93 @@ def test_prepared_calls_match_the_plain_binding():
     assert torch.equal(a.fetch(0, S), out_b)
     with pytest.raises(K.KVTCError):
         app(S - 1, S + 1)
+
+
+# ---------------------------------------------------------------- paired key/value calls
+KV_CASES = [
+    # name, key workload, value workload (same B, H and rows)
+    ("tiny-f32", small(1), small(1)),
+    ("batched", small(4, B=3, s_prefill=2048, s_total=2048 + 45), small(4, B=3, s_prefill=2048, s_total=2048 + 45)),
+    ("long", small(5, s_prefill=4096, s_total=4096 + 45), small(5, s_prefill=4096, s_total=4096 + 45)),
+    ("palu", small(3, H=16, s_prefill=2048, s_total=2048 + 45), small(3, H=16, s_prefill=2048, s_total=2048 + 45)),
+    # different modes: the call falls back to one launch per tensor
+    ("dp-key-mixed-value", small(2, s_prefill=2048, s_total=2048 + 45),
+     small(3, H=8, s_prefill=2048, s_total=2048 + 45)),
+]
+
+
+@pytest.mark.parametrize("name,wk,wv", KV_CASES, ids=[c[0] for c in KV_CASES])
+def test_kv_calls_match_single_calls(name, wk, wv):
+    """kvtc_append_kv / kvtc_fetch_kv store and reconstruct exactly what
+    kvtc_append / kvtc_fetch do on each tensor: a bulk prefill, decode appends of
+    1, 16 and 17 rows, whole and partial fetches.  The key tensor's single-call
+    store is also filled a row at a time and must equal a bulk append of the
+    same rows (the decode and bulk kernels agree bit for bit)."""
+    print_case("kv pair", name)
+    Xk, Xv = synth.generate(wk, 0), synth.generate(wv, 1)
+    S = Xk.shape[2]
+    sts = [O.fit(oracle_cfg(wk), Xk[:, :, :wk.s_prefill]), O.fit(oracle_cfg(wv), Xv[:, :, :wv.s_prefill])]
+    blobs = [blob_from_oracle(st) for st in sts]
+    single = [DeviceStore(b, S) for b in blobs]
+    pair = [DeviceStore(b, S) for b in blobs]
+    bulk_k = DeviceStore(blobs[0], S)
+    xs = [torch.from_numpy(Xk).cuda(), torch.from_numpy(Xv).cuda()]
+    p0 = wk.s_prefill
+    # prefill, then appends of 1, 1, 16 and 17 rows and the rest (as far as S allows)
+    cuts = sorted({min(c, S) for c in (0, p0, p0 + 1, p0 + 2, p0 + 18, p0 + 35, S)})
+    for a, e in zip(cuts[:-1], cuts[1:]):
+        for i in range(2):
+            single[i].append(xs[i][:, :, a:e], a)
+        K.kvtc_append_kv((blobs[0], pair[0].blob_dev, xs[0][:, :, a:e], pair[0].codes, pair[0].params),
+                         (blobs[1], pair[1].blob_dev, xs[1][:, :, a:e], pair[1].codes, pair[1].params), a, S)
+    bulk_k.append(xs[0][:, :, :p0], 0)
+    for s in range(p0, S):
+        bulk_k.append(xs[0][:, :, s:s + 1], s)
+    single_bulk = DeviceStore(blobs[0], S)
+    single_bulk.append(xs[0], 0)
+    for i in range(2):
+        assert np.array_equal(single[i].rows(S), pair[i].rows(S)), f"tensor {i} rows"
+        if single[i].params is not None:
+            assert torch.equal(single[i].params, pair[i].params)
+    assert np.array_equal(bulk_k.rows(S), single_bulk.rows(S)), "row-at-a-time vs bulk"
+    for (sb, se) in ((0, S), (p0 - 7, S - 3)):
+        outs = [single[i].fetch(sb, se) for i in range(2)]
+        outs_kv = [torch.full_like(o, float("nan")) for o in outs]
+        K.kvtc_fetch_kv((blobs[0], pair[0].blob_dev, pair[0].codes, pair[0].params, outs_kv[0]),
+                        (blobs[1], pair[1].blob_dev, pair[1].codes, pair[1].params, outs_kv[1]), S, sb, se)
+        for i in range(2):
+            assert torch.equal(outs[i], outs_kv[i]), (name, i, sb, se)
+    # and against the oracle: codes and reconstruction of the value tensor's pair store
+    if wv.mode == "dp":
+        check_codes_dp(sts[1], Xv, pair[1].rows(S))
+    else:
+        check_codes_mixed(sts[1], Xv, pair[1].rows(S), pair[1].params_np(S))
+    prm = pair[1].params_np(S) if wv.mode == "mixed" else None
+    check_recon(O.fetch(sts[1], pair[1].rows(S), prm), pair[1].fetch(0, S), name)
+
+
+def test_prepared_kv_calls_match_the_plain_binding():
+    print_case("prepared kv calls")
+    w = small(4, B=2, s_prefill=1024, s_total=1024 + 20)
+    Xk, Xv = synth.generate(w, 0), synth.generate(w, 1)
+    S = Xk.shape[2]
+    blobs = [blob_from_oracle(O.fit(oracle_cfg(w), X[:, :, :1024])) for X in (Xk, Xv)]
+    a = [DeviceStore(b, S) for b in blobs]
+    b = [DeviceStore(b, S) for b in blobs]
+    xs = [torch.from_numpy(Xk).cuda(), torch.from_numpy(Xv).cuda()]
+    outs = [torch.zeros((w.B, w.H, S, w.D), dtype=torch.float16, device="cuda:0") for _ in range(2)]
+    app = K.PreparedAppendKV(*[(b[i].blob, b[i].blob_dev, xs[i], b[i].codes, b[i].params) for i in range(2)], S)
+    fet = K.PreparedFetchKV(*[(b[i].blob, b[i].blob_dev, b[i].codes, b[i].params, outs[i]) for i in range(2)], S)
+    app(0, 1024)
+    for i in range(2):
+        a[i].append(xs[i][:, :, :1024], 0)
+    for s in range(1024, S):
+        app(s, s + 1)
+        fet(0, s + 1)
+        for i in range(2):
+            a[i].append(xs[i][:, :, s:s + 1], s)
+    for i in range(2):
+        assert np.array_equal(a[i].rows(S), b[i].rows(S))
+        assert torch.equal(a[i].fetch(0, S), outs[i])
+    with pytest.raises(K.KVTCError):
+        app(S - 1, S + 1)

@@ -61,12 +61,15 @@ def test_ctypes_structs_match_the_c_header(tmp_path):
     src.write_text('#include <stdio.h>\n#include <stddef.h>\n#include "kvtc.h"\n'
                    'int main(){printf("%zu %zu %zu %zu %zu %zu\\n", sizeof(kvtc_config),'
                    ' sizeof(kvtc_state_header), sizeof(kvtc_bytes_report), sizeof(kvtc_unit_info),'
-                   ' offsetof(kvtc_state_header, s_prefill), offsetof(kvtc_state_header, off_bias));}\n')
+                   ' offsetof(kvtc_state_header, s_prefill), offsetof(kvtc_state_header, off_bias));'
+                   'printf("%zu %zu %zu\\n", sizeof(kvtc_tensor_ref), offsetof(kvtc_tensor_ref, dtype),'
+                   ' offsetof(kvtc_tensor_ref, strides));}\n')
     exe = tmp_path / "s"
     subprocess.run(["gcc", "-I", os.path.dirname(HEADER), str(src), "-o", str(exe)], check=True)
     got = [int(v) for v in subprocess.run([str(exe)], capture_output=True, text=True).stdout.split()]
     want = [C.sizeof(K.Config), C.sizeof(K.StateHeader), C.sizeof(K.BytesReport), C.sizeof(K.UnitInfo),
-            K.StateHeader.s_prefill.offset, K.StateHeader.off_bias.offset]
+            K.StateHeader.s_prefill.offset, K.StateHeader.off_bias.offset,
+            C.sizeof(K.TensorRef), K.TensorRef.dtype.offset, K.TensorRef.strides.offset]
     assert got == want
 
 
@@ -313,3 +316,46 @@ def test_store_sizes():
     st = O.fit(oracle_cfg(w), synth.generate(w, 0, 0, 256))
     cb, pb = K.kvtc_store_bytes(blob_from_oracle(st), 300)
     assert cb == st.U * 300 * st.row_stride and pb == 0
+
+
+def test_paired_entry_points_validate_both_tensors_before_launch():
+    """kvtc_append_kv / kvtc_fetch_kv check the key and the value tensor before
+    anything is launched: a bad value tensor fails the call even when the key
+    tensor is valid (fake device pointers are never dereferenced)."""
+    w = synth.WORKLOADS[1]
+    st = O.fit(oracle_cfg(w), synth.generate(w, 0, 0, 256))
+    blob = blob_from_oracle(st)
+    broken = blob.copy()
+    broken[0] ^= 0xFF
+    fake = 0x1000
+
+    def ref(b, dtype=K.F32, capacity=100, strides=(2 * 64 * 10, 64 * 10, 64, 1)):
+        r = K.TensorRef()
+        r.state_host, r.state_dev, r.codes_dev, r.rows_dev = b.ctypes.data, fake, fake, fake
+        r.capacity, r.dtype = capacity, dtype
+        for i, v in enumerate(strides):
+            r.strides[i] = v
+        return r
+
+    app = _raw("kvtc_append_kv")
+    app.restype = C.c_int32
+    app.argtypes = K._sig["kvtc_append_kv"][1]
+    good = ref(blob)
+    assert app(C.byref(good), C.byref(ref(broken)), 1, 2, 10, 0, None) == K.E_STATE
+    assert app(C.byref(good), C.byref(ref(blob, dtype=9)), 1, 2, 10, 0, None) == K.E_DTYPE
+    assert app(C.byref(good), C.byref(ref(blob, capacity=50)), 1, 2, 10, 45, None) == K.E_CAPACITY
+    assert app(C.byref(good), C.byref(ref(blob)), 1, 3, 10, 0, None) == K.E_SHAPE
+    assert app(C.byref(good), None, 1, 2, 10, 0, None) == K.E_ARG
+    assert app(C.byref(good), C.byref(ref(blob)), 1, 2, 0, 0, None) == K.OK       # empty: nothing to do
+    fet = _raw("kvtc_fetch_kv")
+    fet.restype = C.c_int32
+    fet.argtypes = K._sig["kvtc_fetch_kv"][1]
+    out_strides = (2 * 100 * 64, 100 * 64, 64, 1)
+    assert fet(C.byref(ref(blob, strides=out_strides)), C.byref(ref(broken, strides=out_strides)), 0, 10,
+               None) == K.E_STATE
+    odd = (2 * 100 * 64, 100 * 64, 65, 1)                    # value rows not 16-byte aligned
+    assert fet(C.byref(ref(blob, strides=out_strides)), C.byref(ref(blob, strides=odd)), 0, 10, None) == K.E_SHAPE
+    assert fet(C.byref(ref(blob, strides=out_strides)), C.byref(ref(blob, strides=out_strides)), 0, 101,
+               None) == K.E_CAPACITY
+    assert fet(C.byref(ref(blob, strides=out_strides)), C.byref(ref(blob, strides=out_strides)), 4, 4,
+               None) == K.OK
