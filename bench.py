@@ -262,8 +262,34 @@ def time_batched_decode(K, args, dev):
     fetch_bytes = [layer.fetch_bytes(s) for s in sizes]
     append_bytes = layer.append_bytes(1) * args.steps
     h = layer.paths[0].h
+    att = time_attend(K, layer, sizes[-1], dev)
     return dict(w=w, total_ms=total_ms, fetch_ms=fetch_ms, positions=positions,
-                fetch_bytes=fetch_bytes, append_bytes=append_bytes, sizes=sizes, header=h)
+                fetch_bytes=fetch_bytes, append_bytes=append_bytes, sizes=sizes, header=h, attend=att)
+
+
+def time_attend(K, layer, S, dev, reps=20):
+    """Decode attention from the codes (one query per (b, h)) over the same
+    stored rows [0, S): what a decode step needs instead of the full fetch.
+    Algorithmic bytes: both code stores' rows plus both fp32 bases once."""
+    import torch
+    k, v = layer.paths
+    att = K.Attend((k.blob, k.blob_dev, k.codes, k.params), (v.blob, v.blob_dev, v.codes, v.params), k.cap)
+    h = k.h
+    q = torch.randn((h.batch, h.heads, h.head_dim), device=dev, dtype=torch.float16)
+    out = att(q, S)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        att(q, S, out)
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / reps
+    nbytes = sum(p.h.batch * p.h.heads * S * p.h.row_stride + p.h.units * p.h.kslots * p.h.dg * 4 for p in (k, v))
+    return {"ms_per_call": round(ms, 4), "positions_per_s": round(h.batch * h.heads * S / (ms / 1e3), 1),
+            "algorithmic_bytes": nbytes, "GBps": round(nbytes / (ms / 1e3) / 1e9, 1),
+            "frac_hbm": round(nbytes / (ms / 1e3) / 1e9 / PEAK_HBM_GBPS, 4),
+            "launches": "prep + partial + merge"}
 
 
 def time_one_shot(K, wid, dev, reps=5):
@@ -433,6 +459,10 @@ def main():
                      "mean_launch_ms": round(fetch_mean_ms, 4),
                      "launches": len(r["fetch_ms"])},
     }
+    a = r["attend"]
+    out["attend_from_codes"] = dict(a, S=r["sizes"][-1], note="one query per (b, h); softmax attention over all "
+                                    "stored K and V rows computed from the codes, no fp16 K/V written",
+                                    fetch_ms_same_rows=round(float(np.mean(r["fetch_ms"][-2:])), 4))
     if args.extra:
         extra = []
         for fn in (lambda: time_one_shot(K, 5, dev), lambda: time_one_shot(K, 3, dev),

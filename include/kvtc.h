@@ -260,6 +260,38 @@ int32_t kvtc_append_kv(const kvtc_tensor_ref *k, const kvtc_tensor_ref *v,
 int32_t kvtc_fetch_kv(const kvtc_tensor_ref *k, const kvtc_tensor_ref *v,
                       int64_t s_begin, int64_t s_end, void *hip_stream);
 
+/* Bytes of device workspace kvtc_attend needs for rows [0, s_end) of the given
+ * key and value states (per unit: the query's score coefficients; per unit and
+ * chunk of 512 rows: partial softmax statistics). */
+int32_t kvtc_attend_workspace(const void *k_state_host, const void *v_state_host, int64_t s_end,
+                              size_t *bytes);
+
+/* Decode attention over the stored rows [0, s_end) of a key and a value tensor,
+ * computed from their codes without reconstructing keys or values (device).
+ * TurboQuant cache module page, attend: one query per head is scored against
+ * every stored key, the scores are divided by sqrt(D), softmax-weighted over the
+ * stored rows, and the decoded values are summed with those weights; an empty
+ * cache gives zeros.  PALU cache API page, "Design": latents are reconstructed
+ * only for attention.  Per (b, h): out = sum_s p_s xv_s with
+ * p = softmax(q . xk_s / sqrt(D)), where xk_s, xv_s are the rows kvtc_fetch
+ * would reconstruct (before their fp16 rounding); evaluated in fp32 through the
+ * latent space: q is projected onto the key basis once, every stored key code
+ * is weighted by it, and the softmax-weighted value codes are reconstructed
+ * once per (b, h).
+ *   k, v        DP-mode tensors with one head per unit and the same B, H, D
+ *               (D <= 256); their rows_dev, dtype and strides are not used
+ *   q_dev       queries [B, H, D] of dtype q_dtype (KVTC_F16 or KVTC_F32), element
+ *               strides q_strides for (b, h, d), q_strides[2] == 1
+ *   out_dev     fp16 [B, H, D] with element strides out_strides, out_strides[2] == 1
+ *   work_dev    device workspace of at least kvtc_attend_workspace() bytes,
+ *               256-byte aligned, owned by the caller (contents are scratch)
+ * Needs 0 <= s_end <= both capacities; KVTC_E_STATE for a group-head tensor,
+ * KVTC_E_BUFSIZE for a missing or short workspace. */
+int32_t kvtc_attend(const kvtc_tensor_ref *k, const kvtc_tensor_ref *v,
+                    const void *q_dev, int32_t q_dtype, const int64_t q_strides[3], int64_t s_end,
+                    void *out_dev, const int64_t out_strides[3],
+                    void *work_dev, size_t work_bytes, void *hip_stream);
+
 /* Storage accounting of one tensor over its first S rows (host).
  * KVTC page "Byte accounting" and the kvtc_bytes / pre_entropy_bytes
  * properties: order-0 Huffman per kept DP component, kept only when payload +

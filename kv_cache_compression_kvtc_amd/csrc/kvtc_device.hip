@@ -985,6 +985,236 @@ __global__ __launch_bounds__(64 * NW, 2) void fetch_kernel(FetchPair m) {
     }
 }
 
+// ============================================================== decode attention
+// Attention of one query per (b, h) over the stored keys and values, computed
+// from the codes (TurboQuant cache module page, attend: scores of the query
+// against every stored key divided by sqrt(d), softmax over the stored rows,
+// weighted sum of the decoded values; PALU cache API page, "Design": latents
+// are reconstructed only for attention).  With the DP dequantisation
+// l_j = min_j + c_j*scale_j and x = sum_j l_j V_j + mu, the score of row s is
+//   q.x_s / sqrt(D) = sum_j c_sj * qt_j + beta,
+//   qt_j = scale_j (q.V_j) / sqrt(D),  beta = (q.mu + sum_j min_j (q.V_j)) / sqrt(D),
+// and the output is sum_s p_s x_s = sum_j abar_j scale_j V_j + bias with
+// abar_j = sum_s p_s c_sj (softmax weights p summing to one), so neither keys nor
+// values are ever reconstructed per row.  The rows are split into chunks whose
+// partial softmax statistics (max, sum, weighted code sums) are merged per unit.
+constexpr int kAttChunk = 512;       // rows per partial block
+
+struct AttendSide {
+    const uint8_t *codes;
+    int64_t capacity;
+    const kvtc_unit_info *ui;
+    const float *basis, *mu, *qmin, *qscale, *bias;
+    const int32_t *comp;
+    const uint32_t *sbits;
+    int kslots, rmax, row_words;
+};
+
+struct AttendArgs {
+    AttendSide k, v;
+    const void *q;
+    int64_t qsb, qsh;
+    int q_f16;
+    _Float16 *out;
+    int64_t osb, osh;
+    int64_t s_end;
+    int nchunks, H, D;
+    float inv_sqrt_d;
+    float *qt;          // [U][k.kslots + 1]: qt_j, then beta
+    float *part;        // [U][nchunks][v.kslots + 2]: abar partial sums, then max, sum
+};
+
+__device__ inline uint32_t row_field(const uint32_t *row, uint32_t sb) {
+    const uint32_t off = sb & kOffsetMask, w = sb >> 24;
+    const uint32_t wi = off >> 5, sh = off & 31u;
+    return __builtin_amdgcn_alignbit(row[wi + 1], row[wi], sh) & ((1u << w) - 1u);
+}
+
+__device__ inline float block_reduce(float v, float *red, bool is_max) {
+    for (int m = 32; m >= 1; m >>= 1) {
+        const float o = __shfl_xor(v, m, 64);
+        v = is_max ? fmaxf(v, o) : v + o;
+    }
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, nw = blockDim.x >> 6;
+    __syncthreads();
+    if (lane == 0) red[wave] = v;
+    __syncthreads();
+    float r = red[0];
+    for (int w = 1; w < nw; ++w) r = is_max ? fmaxf(r, red[w]) : r + red[w];
+    return r;
+}
+
+// Per unit: the query's score coefficients qt_j and offset beta (fp32).
+__global__ __launch_bounds__(256) void attend_prep_kernel(AttendArgs a) {
+    __shared__ float ql[kMaxSlots];
+    __shared__ float mpart[kMaxSlots];
+    const int u = blockIdx.x, b = u / a.H, h = u % a.H, tid = threadIdx.x;
+    for (int d = tid; d < a.D; d += blockDim.x)
+        ql[d] = a.q_f16 ? static_cast<float>(static_cast<const _Float16 *>(a.q)[b * a.qsb + h * a.qsh + d])
+                        : static_cast<const float *>(a.q)[b * a.qsb + h * a.qsh + d];
+    __syncthreads();
+    const AttendSide &k = a.k;
+    const int ns = k.ui[u].n_slots;
+    float qt = 0.f, mp = 0.f;
+    if (tid < ns) {
+        const float *vrow = k.basis + (static_cast<int64_t>(u) * k.kslots + tid) * a.D;
+        float acc = 0.f;
+        for (int d = 0; d < a.D; ++d) acc = fmaf(ql[d], vrow[d], acc);
+        const int c = k.comp[static_cast<int64_t>(u) * k.kslots + tid];
+        qt = k.qscale[static_cast<int64_t>(u) * k.rmax + c] * acc * a.inv_sqrt_d;
+        mp = k.qmin[static_cast<int64_t>(u) * k.rmax + c] * acc;
+    }
+    if (tid < k.kslots) {
+        a.qt[static_cast<int64_t>(u) * (k.kslots + 1) + tid] = qt;
+        mpart[tid] = mp;
+    }
+    __syncthreads();
+    if (tid == 0) {
+        float beta = 0.f;
+        for (int d = 0; d < a.D; ++d) beta = fmaf(ql[d], k.mu[static_cast<int64_t>(u) * a.D + d], beta);
+        for (int j = 0; j < k.kslots; ++j) beta += mpart[j];
+        a.qt[static_cast<int64_t>(u) * (k.kslots + 1) + k.kslots] = beta * a.inv_sqrt_d;
+    }
+}
+
+// Per (chunk of kAttChunk rows, unit): scores from the key codes, the chunk's
+// softmax max and sum, and the p-weighted sums of the value codes.  Rows are
+// staged in LDS at an odd pitch of at least row_words + 1 words: a thread per
+// row then reads without bank conflicts, and every row ends in a slack word for
+// its last field window (fields end inside the row, so the slack word's bits
+// are always masked off).
+__global__ __launch_bounds__(256) void attend_partial_kernel(AttendArgs a) {
+    extern __shared__ __align__(16) unsigned char smem[];
+    const int c = blockIdx.x, u = blockIdx.y, tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const AttendSide &K = a.k, &V = a.v;
+    float *qt_l = reinterpret_cast<float *>(smem);                       // [K.kslots + 1]
+    uint32_t *ksb = reinterpret_cast<uint32_t *>(qt_l + kMaxSlots + 1);  // [K.kslots]
+    uint32_t *vsb = ksb + kMaxSlots;                                     // [V.kslots]
+    float *pl = reinterpret_cast<float *>(vsb + kMaxSlots);              // [kAttChunk]
+    float *red = pl + kAttChunk;                                         // [4][kMaxSlots]
+    uint32_t *rows = reinterpret_cast<uint32_t *>(red + 4 * kMaxSlots);  // [kAttChunk][pitch]
+    const int64_t s0 = static_cast<int64_t>(c) * kAttChunk;
+    const int nrows = static_cast<int>(min<int64_t>(kAttChunk, a.s_end - s0));
+    const int nk = K.ui[u].n_slots, nv = V.ui[u].n_slots;
+    // word i of a chunk's rows goes to (i / row_words, i % row_words); the
+    // quotient from a float reciprocal is exact for i < 2^16
+    auto stage = [&](const AttendSide &T, int pitch) {
+        const uint32_t *src = reinterpret_cast<const uint32_t *>(T.codes) + (static_cast<int64_t>(u) * T.capacity + s0) * T.row_words;
+        const float inv = 1.0f / static_cast<float>(max(T.row_words, 1));
+        for (int i = tid; i < nrows * T.row_words; i += blockDim.x) {
+            const int r = static_cast<int>((static_cast<float>(i) + 0.5f) * inv);
+            rows[r * pitch + (i - r * T.row_words)] = src[i];
+        }
+    };
+    const int kp = (K.row_words + 1) | 1, vp = (V.row_words + 1) | 1;   // odd, > row_words
+
+    for (int i = tid; i <= K.kslots; i += blockDim.x) qt_l[i] = a.qt[static_cast<int64_t>(u) * (K.kslots + 1) + i];
+    for (int i = tid; i < K.kslots; i += blockDim.x) ksb[i] = K.sbits[static_cast<int64_t>(u) * K.kslots + i];
+    for (int i = tid; i < V.kslots; i += blockDim.x) vsb[i] = V.sbits[static_cast<int64_t>(u) * V.kslots + i];
+    stage(K, kp);
+    __syncthreads();
+
+    // scores of this thread's two rows (row-serial sums over the stored slots;
+    // rows past the chunk are computed on stale words and never stored)
+    float mloc = -__builtin_huge_valf();
+    {
+        const int r0 = tid, r1 = tid + 256;
+        const uint32_t *row0 = rows + r0 * kp, *row1 = rows + r1 * kp;
+        float acc0 = qt_l[K.kslots], acc1 = acc0;
+        for (int j = 0; j < nk; ++j) {
+            const uint32_t sb = ksb[j];
+            const float w = qt_l[j];
+            acc0 = fmaf(static_cast<float>(row_field(row0, sb)), w, acc0);
+            acc1 = fmaf(static_cast<float>(row_field(row1, sb)), w, acc1);
+        }
+        if (r0 < nrows) {
+            pl[r0] = acc0;
+            mloc = acc0;
+        }
+        if (r1 < nrows) {
+            pl[r1] = acc1;
+            mloc = fmaxf(mloc, acc1);
+        }
+    }
+    const float M = block_reduce(mloc, red, true);     // (its barriers also end the score phase)
+    float lsum = 0.f;
+    for (int r = tid; r < nrows; r += blockDim.x) {
+        const float p = expf(pl[r] - M);
+        pl[r] = p;
+        lsum += p;
+    }
+    stage(V, vp);
+    const float L = block_reduce(lsum, red, false);
+    __syncthreads();
+
+    // p-weighted sums of the value codes: wave w takes rows w, w+4, ...; lane
+    // takes slots lane + 64t
+    float acc[kMaxSlots / 64];
+    uint32_t mysb[kMaxSlots / 64];
+#pragma unroll
+    for (int t = 0; t < kMaxSlots / 64; ++t) {
+        acc[t] = 0.f;
+        mysb[t] = lane + 64 * t < nv ? vsb[lane + 64 * t] : 0u;
+    }
+    const int ngroups = (nv + 63) >> 6;                // wave-uniform
+    for (int r = wave; r < nrows; r += 4) {
+        const float p = pl[r];
+        const uint32_t *row = rows + r * vp;
+#pragma unroll
+        for (int t = 0; t < kMaxSlots / 64; ++t)
+            if (t < ngroups) acc[t] = fmaf(p, static_cast<float>(row_field(row, mysb[t])), acc[t]);
+    }
+    __syncthreads();                                   // the reductions' scratch is reused below
+#pragma unroll
+    for (int t = 0; t < kMaxSlots / 64; ++t) red[wave * kMaxSlots + lane + 64 * t] = acc[t];
+    __syncthreads();
+    float *dst = a.part + (static_cast<int64_t>(u) * a.nchunks + c) * (V.kslots + 2);
+    for (int j = tid; j < V.kslots; j += blockDim.x)
+        dst[j] = (red[j] + red[kMaxSlots + j]) + (red[2 * kMaxSlots + j] + red[3 * kMaxSlots + j]);
+    if (tid == 0) {
+        dst[V.kslots] = M;
+        dst[V.kslots + 1] = L;
+    }
+}
+
+// Per unit: merge the chunks' softmax statistics, then reconstruct the output
+// once: out = bias + sum_j (abar_j scale_j) V_j, rounded to fp16.
+__global__ __launch_bounds__(256) void attend_merge_kernel(AttendArgs a) {
+    __shared__ float coef[kMaxSlots];
+    __shared__ float red[4];
+    const int u = blockIdx.x, b = u / a.H, h = u % a.H, tid = threadIdx.x;
+    const AttendSide &V = a.v;
+    const int nv = V.ui[u].n_slots, stride = V.kslots + 2;
+    const float *part = a.part + static_cast<int64_t>(u) * a.nchunks * stride;
+    float m = -__builtin_huge_valf();
+    for (int c = tid; c < a.nchunks; c += blockDim.x) m = fmaxf(m, part[c * stride + V.kslots]);
+    const float M = block_reduce(m, red, true);
+    float l = 0.f;
+    for (int c = tid; c < a.nchunks; c += blockDim.x)
+        l += expf(part[c * stride + V.kslots] - M) * part[c * stride + V.kslots + 1];
+    const float L = block_reduce(l, red, false);
+    if (tid < V.kslots) {
+        float s = 0.f;
+        if (tid < nv) {
+            for (int c = 0; c < a.nchunks; ++c) s = fmaf(expf(part[c * stride + V.kslots] - M), part[c * stride + tid], s);
+            const int ci = V.comp[static_cast<int64_t>(u) * V.kslots + tid];
+            s = s / L * V.qscale[static_cast<int64_t>(u) * V.rmax + ci];
+        }
+        coef[tid] = s;
+    }
+    __syncthreads();
+    for (int d = tid; d < a.D; d += blockDim.x) {
+        float o = 0.f;
+        if (a.nchunks > 0) {
+            o = V.bias[static_cast<int64_t>(u) * a.D + d];
+            const float *vb = V.basis + static_cast<int64_t>(u) * V.kslots * a.D + d;
+            for (int j = 0; j < nv; ++j) o = fmaf(coef[j], vb[static_cast<int64_t>(j) * a.D], o);
+        }
+        a.out[b * a.osb + h * a.osh + d] = static_cast<_Float16>(o);
+    }
+}
+
 // ============================================================== launchers
 constexpr int kLdsMax = 160 * 1024;
 
@@ -1362,6 +1592,39 @@ int32_t launch_fetch_plans(const FetchPlan &p0, const FetchPlan *p1, hipStream_t
     return p0.mixed ? launch_fetch<true, 2>(m, nt, ks, rw, stream) : launch_fetch<false, 2>(m, nt, ks, rw, stream);
 }
 
+// Validation shared by the attention entry points: a DP tensor with one head
+// per unit, head size and slot count within the kernels' limits.
+int32_t attend_side_ok(const kvtc_state_header *h) {
+    if (h->mode != KVTC_MODE_DP || h->heads_per_unit != 1) return KVTC_E_STATE;
+    if (h->head_dim > kMaxSlots || h->kslots > kMaxSlots || h->row_stride > kMaxRowStride) return KVTC_E_SHAPE;
+    return KVTC_OK;
+}
+
+AttendSide attend_side(const kvtc_state_header *h, const void *state_dev, const void *codes, int64_t capacity) {
+    const char *sd = static_cast<const char *>(state_dev);
+    AttendSide sd_{};
+    sd_.codes = static_cast<const uint8_t *>(codes);
+    sd_.capacity = capacity;
+    sd_.ui = reinterpret_cast<const kvtc_unit_info *>(sd + h->off_unit);
+    sd_.basis = reinterpret_cast<const float *>(sd + h->off_basis);
+    sd_.mu = reinterpret_cast<const float *>(sd + h->off_mu);
+    sd_.qmin = reinterpret_cast<const float *>(sd + h->off_qmin);
+    sd_.qscale = reinterpret_cast<const float *>(sd + h->off_qscale);
+    sd_.bias = reinterpret_cast<const float *>(sd + h->off_bias);
+    sd_.comp = reinterpret_cast<const int32_t *>(sd + h->off_slot_comp);
+    sd_.sbits = reinterpret_cast<const uint32_t *>(sd + h->off_slot_bits);
+    sd_.kslots = h->kslots;
+    sd_.rmax = h->rmax;
+    sd_.row_words = h->row_stride / 4;
+    return sd_;
+}
+
+size_t attend_work_bytes(const kvtc_state_header *hk, const kvtc_state_header *hv, int64_t s_end) {
+    const int64_t nchunks = (s_end + kAttChunk - 1) / kAttChunk;
+    const uint64_t qt = align_up(static_cast<uint64_t>(hk->units) * (hk->kslots + 1) * sizeof(float), 256);
+    return qt + static_cast<uint64_t>(hv->units) * nchunks * (hv->kslots + 2) * sizeof(float);
+}
+
 }  // namespace
 }  // namespace kvtc
 
@@ -1422,6 +1685,80 @@ int32_t kvtc_fetch_kv(const kvtc_tensor_ref *k, const kvtc_tensor_ref *v, int64_
     st = launch_fetch_plans(pk, nullptr, stream);
     if (st != KVTC_OK) return st;
     return launch_fetch_plans(pv, nullptr, stream);
+}
+
+int32_t kvtc_attend_workspace(const void *k_state_host, const void *v_state_host, int64_t s_end, size_t *bytes) {
+    const kvtc_state_header *hk = nullptr, *hv = nullptr;
+    int32_t st = check_state(k_state_host, &hk);
+    if (st != KVTC_OK) return st;
+    st = check_state(v_state_host, &hv);
+    if (st != KVTC_OK) return st;
+    if (!bytes || s_end < 0) return KVTC_E_ARG;
+    *bytes = attend_work_bytes(hk, hv, s_end);
+    return KVTC_OK;
+}
+
+int32_t kvtc_attend(const kvtc_tensor_ref *k, const kvtc_tensor_ref *v, const void *q_dev, int32_t q_dtype,
+                    const int64_t q_strides[3], int64_t s_end, void *out_dev, const int64_t out_strides[3],
+                    void *work_dev, size_t work_bytes, void *hip_stream) {
+    if (!k || !v || !q_strides || !out_strides) return KVTC_E_ARG;
+    const kvtc_state_header *hk = nullptr, *hv = nullptr;
+    int32_t st = check_state(k->state_host, &hk);
+    if (st != KVTC_OK) return st;
+    st = check_state(v->state_host, &hv);
+    if (st != KVTC_OK) return st;
+    if ((st = attend_side_ok(hk)) != KVTC_OK || (st = attend_side_ok(hv)) != KVTC_OK) return st;
+    if (hk->batch != hv->batch || hk->heads != hv->heads || hk->head_dim != hv->head_dim) return KVTC_E_SHAPE;
+    if (q_dtype != KVTC_F16 && q_dtype != KVTC_F32) return KVTC_E_DTYPE;
+    if (q_strides[2] != 1 || out_strides[2] != 1 || q_strides[0] < 0 || q_strides[1] < 0 || out_strides[0] < 0 ||
+        out_strides[1] < 0)
+        return KVTC_E_SHAPE;
+    if (s_end < 0 || k->capacity < 0 || v->capacity < 0) return KVTC_E_ARG;
+    if (s_end > k->capacity || s_end > v->capacity) return KVTC_E_CAPACITY;
+    if (!k->state_dev || !v->state_dev || !q_dev || !out_dev) return KVTC_E_ARG;
+    if (s_end > 0 && ((hk->row_stride > 0 && (!k->codes_dev || reinterpret_cast<uintptr_t>(k->codes_dev) % 4)) ||
+                      (hv->row_stride > 0 && (!v->codes_dev || reinterpret_cast<uintptr_t>(v->codes_dev) % 4))))
+        return KVTC_E_ARG;
+    if (reinterpret_cast<uintptr_t>(out_dev) % 2 || reinterpret_cast<uintptr_t>(q_dev) % (q_dtype == KVTC_F16 ? 2 : 4))
+        return KVTC_E_ARG;
+    const size_t need = attend_work_bytes(hk, hv, s_end);
+    if (!work_dev || work_bytes < need || reinterpret_cast<uintptr_t>(work_dev) % 256) return KVTC_E_BUFSIZE;
+    const int64_t nchunks = (s_end + kAttChunk - 1) / kAttChunk;
+    if (hk->units > 0x7FFFFFFF || nchunks > 0x7FFFFFFF || hk->units > 65535) return KVTC_E_SHAPE;
+
+    AttendArgs a{};
+    a.k = attend_side(hk, k->state_dev, k->codes_dev, k->capacity);
+    a.v = attend_side(hv, v->state_dev, v->codes_dev, v->capacity);
+    a.q = q_dev;
+    a.qsb = q_strides[0];
+    a.qsh = q_strides[1];
+    a.q_f16 = q_dtype == KVTC_F16;
+    a.out = static_cast<_Float16 *>(out_dev);
+    a.osb = out_strides[0];
+    a.osh = out_strides[1];
+    a.s_end = s_end;
+    a.nchunks = static_cast<int>(nchunks);
+    a.H = static_cast<int>(hk->heads);
+    a.D = hk->head_dim;
+    a.inv_sqrt_d = 1.0f / sqrtf(static_cast<float>(hk->head_dim));
+    a.qt = static_cast<float *>(work_dev);
+    a.part = reinterpret_cast<float *>(static_cast<char *>(work_dev) +
+                                       align_up(static_cast<uint64_t>(hk->units) * (hk->kslots + 1) * sizeof(float), 256));
+    hipStream_t stream = static_cast<hipStream_t>(hip_stream);
+    const unsigned U = static_cast<unsigned>(hk->units);
+    hipLaunchKernelGGL(attend_prep_kernel, dim3(U), dim3(256), 0, stream, a);
+    if (hipGetLastError() != hipSuccess) return KVTC_E_DEVICE;
+    if (nchunks > 0) {
+        const int rw = std::max(a.k.row_words, a.v.row_words);
+        const size_t lds = (kMaxSlots + 1 + 2 * kMaxSlots + kAttChunk + 4 * kMaxSlots) * sizeof(float) +
+                           static_cast<size_t>(kAttChunk) * ((rw + 1) | 1) * sizeof(uint32_t);
+        if (lds > kLdsMax) return KVTC_E_SHAPE;
+        if (!allow_lds(reinterpret_cast<const void *>(attend_partial_kernel))) return KVTC_E_DEVICE;
+        hipLaunchKernelGGL(attend_partial_kernel, dim3(static_cast<unsigned>(nchunks), U), dim3(256), lds, stream, a);
+        if (hipGetLastError() != hipSuccess) return KVTC_E_DEVICE;
+    }
+    hipLaunchKernelGGL(attend_merge_kernel, dim3(U), dim3(256), 0, stream, a);
+    return hipGetLastError() == hipSuccess ? KVTC_OK : KVTC_E_DEVICE;
 }
 
 }  // extern "C"

@@ -93,6 +93,9 @@ _sig = {
     "kvtc_bytes": (_i32, [_vp, _vp, _vp, _i64, _i64, C.POINTER(BytesReport)]),
     "kvtc_append_kv": (_i32, [C.POINTER(TensorRef), C.POINTER(TensorRef), _i64, _i64, _i64, _i64, _vp]),
     "kvtc_fetch_kv": (_i32, [C.POINTER(TensorRef), C.POINTER(TensorRef), _i64, _i64, _vp]),
+    "kvtc_attend_workspace": (_i32, [_vp, _vp, _i64, C.POINTER(_sz)]),
+    "kvtc_attend": (_i32, [C.POINTER(TensorRef), C.POINTER(TensorRef), _vp, _i32, _P64, _i64, _vp, _P64, _vp,
+                           _sz, _vp]),
 }
 for _name, (_res, _args) in _sig.items():
     _f = getattr(_lib, _name)
@@ -311,6 +314,58 @@ def kvtc_fetch_kv(k, v, capacity: int, s_begin: int, s_end: int, stream=None):
         refs.append(_tensor_ref(blob, blob_dev, codes, params, capacity, out, F16))
     _check(_lib.kvtc_fetch_kv(C.byref(refs[0]), C.byref(refs[1]), s_begin, s_end, _stream_ptr(stream)),
            "kvtc_fetch_kv")
+
+
+def kvtc_attend_workspace(blob_k: np.ndarray, blob_v: np.ndarray, s_end: int) -> int:
+    n = C.c_size_t(0)
+    _check(_lib.kvtc_attend_workspace(_host_ptr(blob_k), _host_ptr(blob_v), s_end, C.byref(n)),
+           "kvtc_attend_workspace")
+    return n.value
+
+
+class Attend:
+    """kvtc_attend with its buffers checked once: decode attention of queries
+    [B, H, D] over store rows [0, s_end) of a key and a value tensor.  ``k`` and
+    ``v`` are (blob, blob_dev, codes, params); the device workspace is allocated
+    here (torch) for ``capacity`` rows and reused by every call."""
+
+    def __init__(self, k, v, capacity: int, stream=None):
+        import torch
+        self._keep = (k, v)
+        self._refs = []
+        for (blob, blob_dev, codes, params) in (k, v):
+            _check_buffers(blob, blob_dev, codes, params, capacity, "Attend")
+            ref = TensorRef()
+            ref.state_host, ref.state_dev = _host_ptr(blob), _dev_ptr(blob_dev)
+            ref.codes_dev, ref.params_dev = _dev_ptr(codes), _dev_ptr(params)
+            ref.capacity = capacity
+            self._refs.append(ref)
+        self.h = header(k[0])
+        self.capacity = capacity
+        nbytes = kvtc_attend_workspace(k[0], v[0], capacity)
+        self.work = torch.empty(max(nbytes, 256) + 256, dtype=torch.uint8, device=k[1].device)
+        off = (-self.work.data_ptr()) % 256
+        self._work, self._work_bytes = self.work.data_ptr() + off, self.work.numel() - off
+        self._stream = _stream_ptr(stream)
+
+    def __call__(self, q, s_end: int, out=None):
+        """Queries q: device tensor [B, H, D] (fp16 or fp32); returns fp16 [B, H, D]."""
+        import torch
+        h = self.h
+        dtype = {torch.float16: F16, torch.float32: F32}.get(q.dtype)
+        if dtype is None:
+            raise KVTCError(E_DTYPE, "kvtc_attend")
+        if not q.is_cuda or tuple(q.shape) != (h.batch, h.heads, h.head_dim):
+            raise KVTCError(E_SHAPE, "kvtc_attend: q must be a device tensor [B, H, D]")
+        if out is None:
+            out = torch.empty((h.batch, h.heads, h.head_dim), dtype=torch.float16, device=q.device)
+        if out.dtype != torch.float16 or tuple(out.shape) != tuple(q.shape):
+            raise KVTCError(E_SHAPE, "kvtc_attend: out must be fp16 [B, H, D]")
+        qs = (C.c_int64 * 3)(*[int(x) for x in q.stride()])
+        os_ = (C.c_int64 * 3)(*[int(x) for x in out.stride()])
+        _check(_lib.kvtc_attend(C.byref(self._refs[0]), C.byref(self._refs[1]), q.data_ptr(), dtype, qs, s_end,
+                                out.data_ptr(), os_, self._work, self._work_bytes, self._stream), "kvtc_attend")
+        return out
 
 
 # ---------------------------------------------------------------- blob introspection

@@ -518,6 +518,39 @@ def fetch(st: TensorState, rows: np.ndarray, params=None) -> np.ndarray:
     return scatter_units(out, st.B, st.H, st.hpu)
 
 
+# --------------------------------------------------------------------------
+# decode attention over the stored cache (TurboQuant cache module page,
+# ``attend``: one query per head, scores against every stored key divided by
+# sqrt(d), softmax over the stored rows, weighted sum of the decoded values;
+# PALU cache API page, "Design": the latents are reconstructed only for
+# attention)
+# --------------------------------------------------------------------------
+def attend_rows(Kh: np.ndarray, Vh: np.ndarray, q: np.ndarray) -> np.ndarray:
+    """Attention of one query ``q [D]`` over keys ``Kh [S, D]`` and values
+    ``Vh [S, D]``: ``softmax(Kh @ q / sqrt(D)) @ Vh`` in float64; zeros when
+    nothing is stored (the page returns zeros for an empty cache)."""
+    S, D = Kh.shape
+    if S == 0:
+        return np.zeros(D, np.float64)
+    scores = Kh.astype(np.float64) @ np.asarray(q, np.float64) / math.sqrt(D)
+    w = np.exp(scores - scores.max())          # softmax, shifted by its maximum
+    w /= w.sum()
+    return w @ Vh.astype(np.float64)
+
+
+def attend(st_k: TensorState, rows_k: np.ndarray, st_v: TensorState, rows_v: np.ndarray,
+           q: np.ndarray, params_k=None, params_v=None) -> np.ndarray:
+    """Decode attention of queries ``q [B, H, D]`` over the reconstructed keys
+    and values of the stored rows: float64 ``[B, H, D]``."""
+    Kh, Vh = fetch(st_k, rows_k, params_k), fetch(st_v, rows_v, params_v)
+    B, H = Kh.shape[:2]
+    out = np.zeros((B, H, Kh.shape[3]), np.float64)
+    for b in range(B):
+        for h in range(H):
+            out[b, h] = attend_rows(Kh[b, h], Vh[b, h], q[b, h])
+    return out
+
+
 def to_f16(x: np.ndarray) -> np.ndarray:
     """Round-to-nearest-even fp16 (the fetch output dtype)."""
     return np.asarray(x, dtype=np.float64).astype(np.float16)

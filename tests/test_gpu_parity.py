@@ -464,3 +464,93 @@ def test_prepared_kv_calls_match_the_plain_binding():
         assert torch.equal(a[i].fetch(0, S), outs[i])
     with pytest.raises(K.KVTCError):
         app(S - 1, S + 1)
+
+
+# ---------------------------------------------------------------- decode attention from the codes
+ATTEND_CASES = [
+    ("tiny", small(1)),
+    ("batched", small(4, B=3, s_prefill=2048, s_total=2048 + 45)),
+    ("long", small(5, s_prefill=4096, s_total=4096 + 1000)),
+    ("llama", small(2, s_total=4096 + 77)),
+]
+
+
+def check_attend(ref, got, Vh, what):
+    """Attention output against the oracle: within 2e-3 of each value channel's
+    range over the stored rows, plus half an fp16 ulp of the result, plus 1e-5 of
+    the unit's largest value magnitude for the fp32 sums before the fp16 rounding
+    (the only slack left when the range is zero, e.g. one stored row)."""
+    got = got.cpu().numpy().astype(np.float64) if isinstance(got, torch.Tensor) else got
+    rng_d = Vh.max(axis=2) - Vh.min(axis=2)                      # [B, H, D]
+    bound = (2e-3 * rng_d + 0.5 * np.spacing(np.abs(ref).astype(np.float16)).astype(np.float64)
+             + 1e-5 * np.abs(Vh).max(axis=(2, 3))[:, :, None])
+    err = np.abs(got - ref)
+    i = np.unravel_index(np.argmax(err - bound), err.shape)
+    assert (err <= bound).all(), (what, int((err > bound).sum()), i, float(err[i]), float(bound[i]),
+                                  float(ref[i]), float(got[i]))
+    return float((err / np.maximum(rng_d, 1e-30)).max())
+
+
+@pytest.mark.parametrize("name,w", ATTEND_CASES, ids=[c[0] for c in ATTEND_CASES])
+def test_attend_matches_oracle(name, w):
+    """kvtc_attend from the codes equals the oracle's softmax attention over the
+    reconstructed keys and values, for the whole store, a ragged prefix, an
+    empty cache, fp32 and fp16 queries and strided queries."""
+    print_case("attend", name)
+    Xk, Xv = synth.generate(w, 0), synth.generate(w, 1)
+    S = Xk.shape[2]
+    sts = [O.fit(oracle_cfg(w), X[:, :, :w.s_prefill]) for X in (Xk, Xv)]
+    stores = [DeviceStore(blob_from_oracle(st), S + 3) for st in sts]
+    for ds, X in zip(stores, (Xk, Xv)):
+        ds.append(X[:, :, :w.s_prefill], 0)
+        ds.append(X[:, :, w.s_prefill:], w.s_prefill)
+    rows = [ds.rows(S) for ds in stores]
+    att = K.Attend(*[(ds.blob, ds.blob_dev, ds.codes, ds.params) for ds in stores], S + 3)
+    rng = np.random.default_rng(5)
+    q = rng.normal(size=(w.B, w.H, w.D)) * 1.5
+    qd = torch.from_numpy(q.astype(np.float32)).cuda()
+    for s_end in (S, S - 517 if S > 600 else S - 1, 1):
+        ref = O.attend(sts[0], rows[0][:, :s_end], sts[1], rows[1][:, :s_end], q)
+        Vh = O.fetch(sts[1], rows[1][:, :s_end])
+        check_attend(ref, att(qd, s_end), Vh, f"{name} s_end={s_end}")
+    # fp16 queries, read through a strided view
+    q16 = torch.from_numpy(q.astype(np.float16)).cuda()
+    qs = torch.zeros((w.B, w.H, 2 * w.D), dtype=torch.float16, device="cuda:0")
+    qs[:, :, :w.D] = q16
+    ref = O.attend(sts[0], rows[0], sts[1], rows[1], q16.cpu().numpy().astype(np.float64))
+    check_attend(ref, att(qs[:, :, :w.D], S), O.fetch(sts[1], rows[1]), f"{name} fp16 q")
+    # empty cache: zeros (the page's attend on an empty cache)
+    assert not att(qd, 0).float().abs().sum().item()
+
+
+def test_attend_full_size_batched_decode_sampled_units():
+    """Batched decode at full size (B=64, H=8, 8193 stored rows): attention of
+    one query per (b, h) from the codes, 16 sampled units against the oracle."""
+    print_case("attend batched decode full size")
+    w = synth.WORKLOADS[4]
+    S = w.s_total
+    stores, sts, Xs = [], [], []
+    for tensor in (0, 1):
+        X = synth.generate(w, tensor)
+        st = O.fit(oracle_cfg(w), X[:, :, :8192])
+        ds = DeviceStore(blob_from_oracle(st), S)
+        x = torch.from_numpy(X).cuda()
+        ds.append(x[:, :, :8192], 0)
+        ds.append(x[:, :, 8192:], 8192)
+        stores.append(ds)
+        sts.append(st)
+        del x
+    att = K.Attend(*[(ds.blob, ds.blob_dev, ds.codes, ds.params) for ds in stores], S)
+    q = np.random.default_rng(9).normal(size=(w.B, w.H, w.D))
+    got = att(torch.from_numpy(q.astype(np.float32)).cuda(), S).cpu().numpy().astype(np.float64)
+    rows = [ds.rows(S) for ds in stores]
+    for u in np.random.default_rng(10).choice(w.B * w.H, size=16, replace=False):
+        b, h = divmod(int(u), w.H)
+        Kh = O.reconstruct(O.dequant_dp(O.unpack_rows(rows[0][u], sts[0].bits[u, :sts[0].r[u]]),
+                                        sts[0].bits[u, :sts[0].r[u]], sts[0].qmin32[u, :sts[0].r[u]],
+                                        sts[0].qscale32[u, :sts[0].r[u]]), sts[0].mu32[u], sts[0].V32[u, :, :sts[0].r[u]])
+        Vh = O.reconstruct(O.dequant_dp(O.unpack_rows(rows[1][u], sts[1].bits[u, :sts[1].r[u]]),
+                                        sts[1].bits[u, :sts[1].r[u]], sts[1].qmin32[u, :sts[1].r[u]],
+                                        sts[1].qscale32[u, :sts[1].r[u]]), sts[1].mu32[u], sts[1].V32[u, :, :sts[1].r[u]])
+        ref = O.attend_rows(Kh, Vh, q[b, h])
+        check_attend(ref[None, None], got[b:b + 1, h:h + 1], Vh[None, None], f"unit {u}")

@@ -359,3 +359,40 @@ def test_paired_entry_points_validate_both_tensors_before_launch():
                None) == K.E_CAPACITY
     assert fet(C.byref(ref(blob, strides=out_strides)), C.byref(ref(blob, strides=out_strides)), 4, 4,
                None) == K.OK
+
+
+def test_attend_validates_before_launch():
+    """kvtc_attend rejects group-head tensors, short workspaces, rows past the
+    capacity and bad query types before anything is launched."""
+    w = synth.WORKLOADS[1]
+    st = O.fit(oracle_cfg(w), synth.generate(w, 0, 0, 256))
+    blob = blob_from_oracle(st)
+    wm = synth.WORKLOADS[3]
+    Xm = synth.generate(wm, 0, 0, 64)[:, :8]
+    mixed = K.kvtc_fit_host(K.make_config("mixed", 128, 8, 64, group_size=32), np.ascontiguousarray(Xm))
+    need = K.kvtc_attend_workspace(blob, blob, 100)
+    U, ks = st.U, K.header(blob).kslots
+    assert need == -(-(U * (ks + 1) * 4) // 256) * 256 + U * 1 * (ks + 2) * 4
+    fake = 0x1000
+
+    def ref(b, capacity=100):
+        r = K.TensorRef()
+        r.state_host, r.state_dev, r.codes_dev, r.capacity = b.ctypes.data, fake, fake, capacity
+        return r
+
+    att = _raw("kvtc_attend")
+    att.restype = C.c_int32
+    att.argtypes = K._sig["kvtc_attend"][1]
+    s3 = (C.c_int64 * 3)(2 * 64, 64, 1)
+    good = ref(blob)
+    work = 0x10000
+
+    def call(kr, vr, qdt=K.F32, s_end=100, wbytes=need, work_ptr=work, qs=s3):
+        return att(C.byref(kr), C.byref(vr), fake, qdt, qs, s_end, fake, s3, work_ptr, wbytes, None)
+
+    assert call(good, ref(mixed)) == K.E_STATE
+    assert call(good, good, wbytes=need - 4) == K.E_BUFSIZE
+    assert call(good, good, work_ptr=0) == K.E_BUFSIZE
+    assert call(good, good, s_end=101) == K.E_CAPACITY
+    assert call(good, good, qdt=5) == K.E_DTYPE
+    assert call(good, good, qs=(C.c_int64 * 3)(128, 64, 2)) == K.E_SHAPE

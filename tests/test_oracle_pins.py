@@ -410,3 +410,66 @@ def test_config_errors():
         O.allocate_dp(np.ones(2), -1, (0, 1), 1.0)
     with pytest.raises(O.OracleConfigError):
         O.allocate_dp(np.ones(3), 2, (1, 2), 1.0)
+
+
+# ---------------------------------------------------------------- decode attention
+def test_attend_zero_query_is_the_plain_mean_of_values(rng):
+    # all scores equal: the softmax is uniform and attention is the mean
+    Kh, Vh = rng.normal(size=(37, 16)), rng.normal(size=(37, 16))
+    got = O.attend_rows(Kh, Vh, np.zeros(16))
+    assert np.allclose(got, np.mean(Vh, axis=0), rtol=0, atol=1e-14)
+
+
+def test_attend_single_row_and_empty_cache(rng):
+    Kh, Vh = rng.normal(size=(1, 8)), rng.normal(size=(1, 8))
+    assert np.array_equal(O.attend_rows(Kh, Vh, rng.normal(size=8)), Vh[0])
+    assert np.array_equal(O.attend_rows(np.zeros((0, 8)), np.zeros((0, 8)), np.ones(8)), np.zeros(8))
+
+
+def test_attend_two_rows_closed_form():
+    # scores differ by ln 3 after the 1/sqrt(D) scaling: weights 3/4 and 1/4
+    D = 16
+    q = np.zeros(D)
+    q[0] = 1.0
+    Kh = np.zeros((2, D))
+    Kh[0, 0] = math.sqrt(D) * math.log(3.0)
+    Vh = np.stack([np.arange(D, dtype=np.float64), -2.0 * np.ones(D)])
+    got = O.attend_rows(Kh, Vh, q)
+    assert np.allclose(got, 0.75 * Vh[0] + 0.25 * Vh[1], rtol=0, atol=1e-14)
+
+
+def test_attend_invariances(rng):
+    S, D = 50, 32
+    Kh, Vh, q = rng.normal(size=(S, D)), rng.normal(size=(S, D)), rng.normal(size=D)
+    base = O.attend_rows(Kh, Vh, q)
+    perm = rng.permutation(S)
+    assert np.allclose(O.attend_rows(Kh[perm], Vh[perm], q), base, rtol=0, atol=1e-13)
+    # a common offset of every key shifts every score by the same amount
+    assert np.allclose(O.attend_rows(Kh + rng.normal(size=D), Vh, q), base, rtol=0, atol=1e-12)
+    # the output is a convex combination of the values
+    assert (base <= Vh.max(axis=0) + 1e-12).all() and (base >= Vh.min(axis=0) - 1e-12).all()
+
+
+def test_attend_sharp_query_selects_the_best_matching_row(rng):
+    S, D = 20, 16
+    Kh = rng.normal(size=(S, D))
+    Vh = rng.normal(size=(S, D))
+    i = 7
+    q = 1e4 * Kh[i] / np.linalg.norm(Kh[i])
+    assert int(np.argmax(Kh @ q)) == i
+    assert np.allclose(O.attend_rows(Kh, Vh, q), Vh[i], rtol=0, atol=1e-12)
+
+
+def test_attend_over_a_zero_budget_value_cache_is_its_mean():
+    # a value cache with no code bits reconstructs every row to its mean, and
+    # any softmax weighting of identical rows returns that row
+    w = synth.WORKLOADS[1]
+    Xk, Xv = synth.generate(w, 0), synth.generate(w, 1)
+    cfg = O.Config(mode="dp", head_dim=w.D, rank=w.rank, budget=w.budget, choices=w.choices)
+    st_k = O.fit(cfg, Xk[:, :, :256])
+    st_v = O.fit(O.Config(mode="dp", head_dim=w.D, rank=w.rank, budget=0, choices=w.choices), Xv[:, :, :256])
+    rows_k, _ = O.append(st_k, Xk)
+    rows_v, _ = O.append(st_v, Xv)
+    q = np.random.default_rng(3).normal(size=(1, 2, w.D))
+    got = O.attend(st_k, rows_k, st_v, rows_v, q)
+    assert np.allclose(got[0], st_v.mu32.astype(np.float64), rtol=0, atol=1e-12)
