@@ -14,8 +14,10 @@ documentation pages:
   ``_requantize``; ``KVTCKVCache.__init__`` (config fields), ``update_and_fetch``
   and the byte properties;
 * the TurboQuant cache module page (``veloxquant_mlx.cache.turboquant_cache``
-  source): ``__init__`` (packed row length) and ``_unpack_indices_block`` (the
-  little-endian field order of its bit packer);
+  source): ``__init__`` (packed row length), ``_unpack_indices_block`` (the
+  little-endian field order of its bit packer) and ``attend`` (one query per
+  head: scores against the stored keys divided by sqrt(d), softmax over the
+  stored rows, weighted sum of the decoded values);
 * the PALU cache API page (``veloxquant_mlx.cache.palu_cache``): "Design",
   "Byte accounting" and the ``PALUKVCache`` parameter list.
 
