@@ -136,7 +136,9 @@ typedef struct kvtc_state_header {
     uint64_t off_kdesc;     /* uint32 [units][kfetch/16] fetch k-step t (k = 16t..16t+15): bit
                                offset of its first field (bits 0-15) | width of all its fields
                                (16-19, 0 = empty) | quantisation group (20-31, mixed mode) */
-    uint64_t reserved[3];
+    uint64_t off_fslot;     /* int32  [units][kfetch] stored slot whose fetch operand is column k
+                               of off_w16 (-1 = padding column) */
+    uint64_t reserved[2];
 } kvtc_state_header;
 
 /* ---------------------------------------------------------- entry points */

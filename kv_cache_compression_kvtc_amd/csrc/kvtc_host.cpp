@@ -478,7 +478,7 @@ void frozen_ranges(const std::vector<double> &Xraw, int64_t S, int dg, const flo
 // -------------------------------------------------------------- blob build
 struct Layout {
     uint64_t off_unit, off_lambda, off_bits, off_qmin, off_qscale, off_mu, off_slot_comp,
-        off_slot_bits, off_basis, off_qlo, off_qinv, off_w16, off_bias, off_kdesc, total;
+        off_slot_bits, off_basis, off_qlo, off_qinv, off_w16, off_bias, off_kdesc, off_fslot, total;
 };
 
 Layout plan_layout(int64_t U, int dg, int rmax, int kslots, int kfetch) {
@@ -503,6 +503,7 @@ Layout plan_layout(int64_t U, int dg, int rmax, int kslots, int kfetch) {
     L.off_w16 = take(U * static_cast<uint64_t>(kfetch) * dg * sizeof(uint16_t));
     L.off_bias = take(U * dg * sizeof(float));
     L.off_kdesc = take(U * static_cast<uint64_t>(kfetch / kKStep) * sizeof(uint32_t));
+    L.off_fslot = take(U * static_cast<uint64_t>(kfetch) * sizeof(int32_t));
     L.total = o;
     return L;
 }
@@ -618,6 +619,8 @@ int32_t build_blob(const kvtc_config *cfg, int64_t B, int64_t H, int32_t rmax, c
     h->off_w16 = L.off_w16;
     h->off_bias = L.off_bias;
     h->off_kdesc = L.off_kdesc;
+    h->off_fslot = L.off_fslot;
+    h->reserved[0] = h->reserved[1] = 0;
     h->total_bytes = L.total;
 
     auto *ui = section_mut<kvtc_unit_info>(state_out, L.off_unit);
@@ -634,6 +637,7 @@ int32_t build_blob(const kvtc_config *cfg, int64_t B, int64_t H, int32_t rmax, c
     auto *w16 = section_mut<uint16_t>(state_out, L.off_w16);
     auto *bias = section_mut<float>(state_out, L.off_bias);
     auto *kdesc = section_mut<uint32_t>(state_out, L.off_kdesc);
+    auto *fslot = section_mut<int32_t>(state_out, L.off_fslot);
 
     parallel_for(U, [&](int64_t u) {
         const int r = ranks[u];
@@ -645,6 +649,7 @@ int32_t build_blob(const kvtc_config *cfg, int64_t B, int64_t H, int32_t rmax, c
             lam_o[u * dg + d] = lambda ? lambda[u * dg + d] : 0.0;
         }
         const uint8_t *bu = &bits[static_cast<size_t>(u) * rmax];
+        for (int kk = 0; kk < kfetch; ++kk) fslot[static_cast<size_t>(u) * kfetch + kk] = -1;
         std::vector<double> bacc(dg);
         for (int d = 0; d < dg; ++d) bacc[d] = mu[u * dg + d];
         int j = 0;
@@ -695,6 +700,7 @@ int32_t build_blob(const kvtc_config *cfg, int64_t B, int64_t H, int32_t rmax, c
             for (int d = 0; d < dg; ++d)
                 w16[(static_cast<size_t>(u) * dg + d) * kfetch + kk] =
                     half_bits_rne(wscale * static_cast<double>(src[d]));
+            fslot[static_cast<size_t>(u) * kfetch + kk] = j;
             off += bu[i];
             ++k;
             ++in_step;

@@ -54,7 +54,7 @@ inline int32_t check_state(const void *blob, const kvtc_state_header **out) {
     if (h->mode == KVTC_MODE_MIXED && (h->n_qgroups <= 0 || h->group_size <= 0)) return KVTC_E_STATE;
     const uint64_t offs[] = {h->off_unit, h->off_lambda, h->off_bits, h->off_qmin, h->off_qscale,
                              h->off_mu, h->off_slot_comp, h->off_slot_bits, h->off_basis,
-                             h->off_qlo, h->off_qinv, h->off_w16, h->off_bias, h->off_kdesc};
+                             h->off_qlo, h->off_qinv, h->off_w16, h->off_bias, h->off_kdesc, h->off_fslot};
     for (uint64_t o : offs)
         if (o < sizeof(kvtc_state_header) || o % kSectionAlign != 0 || o >= h->total_bytes)
             return KVTC_E_STATE;

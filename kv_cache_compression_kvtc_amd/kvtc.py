@@ -54,7 +54,7 @@ class StateHeader(C.Structure):
                 ("off_mu", C.c_uint64), ("off_slot_comp", C.c_uint64), ("off_slot_bits", C.c_uint64),
                 ("off_basis", C.c_uint64), ("off_qlo", C.c_uint64), ("off_qinv", C.c_uint64),
                 ("off_w16", C.c_uint64), ("off_bias", C.c_uint64), ("total_bytes", C.c_uint64),
-                ("off_kdesc", C.c_uint64), ("reserved", C.c_uint64 * 3)]
+                ("off_kdesc", C.c_uint64), ("off_fslot", C.c_uint64), ("reserved", C.c_uint64 * 2)]
 
 
 class BytesReport(C.Structure):
@@ -400,6 +400,7 @@ def state_view(blob: np.ndarray) -> dict:
         "qinv": sec(h.off_qinv, np.float64, (U, ks)),
         "w16": sec(h.off_w16, np.float16, (U, dg, kf)),
         "kdesc": sec(h.off_kdesc, np.uint32, (U, kf // 16)),
+        "fslot": sec(h.off_fslot, np.int32, (U, kf)),
         "bias": sec(h.off_bias, np.float32, (U, dg)),
     }
 

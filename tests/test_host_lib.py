@@ -199,6 +199,10 @@ def test_state_build_derived_sections_follow_their_definitions():
         for kk, j in place:
             want[:, kk] = w16[:, j]
         assert np.array_equal(v["w16"][u], want)
+        fs = np.full(kf, -1, np.int32)
+        for kk, j in place:
+            fs[kk] = j
+        assert np.array_equal(v["fslot"][u], fs)
         kd = v["kdesc"][u]
         assert [(int(d & 0xFFFF), int((d >> 16) & 0xF)) for d in kd] == descs
         bias = st.mu32[u].astype(np.float64) + Vc @ st.qmin32[u][comps].astype(np.float64)
@@ -372,6 +376,8 @@ def test_attend_validates_before_launch():
     mixed = K.kvtc_fit_host(K.make_config("mixed", 128, 8, 64, group_size=32), np.ascontiguousarray(Xm))
     need = K.kvtc_attend_workspace(blob, blob, 100)
     U, ks = st.U, K.header(blob).kslots
+    # regions: qt [U][ks+1] f32 (256-byte aligned), then one 512-row chunk of
+    # partial sums [U][1][ks + 2] f32 for 100 rows
     assert need == -(-(U * (ks + 1) * 4) // 256) * 256 + U * 1 * (ks + 2) * 4
     fake = 0x1000
 
