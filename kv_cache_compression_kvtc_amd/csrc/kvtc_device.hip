@@ -999,6 +999,7 @@ __global__ __launch_bounds__(64 * NW, 2) void fetch_kernel(FetchPair m) {
 // values are ever reconstructed per row.  The rows are split into chunks whose
 // partial softmax statistics (max, sum, weighted code sums) are merged per unit.
 constexpr int kAttChunk = 512;       // rows per partial block
+constexpr int kAttKsK = 16;          // k-steps of the key contraction (kfetch <= 256)
 
 struct AttendSide {
     const uint8_t *codes;
@@ -1007,7 +1008,9 @@ struct AttendSide {
     const float *basis, *mu, *qmin, *qscale, *bias;
     const int32_t *comp;
     const uint32_t *sbits;
-    int kslots, rmax, row_words;
+    const uint32_t *kdesc;             // fetch k-step descriptors [U][kfetch/16]
+    const int32_t *fslot;              // stored slot of fetch column k [U][kfetch]
+    int kslots, rmax, row_words, kfetch;
 };
 
 struct AttendArgs {
@@ -1021,6 +1024,8 @@ struct AttendArgs {
     int nchunks, H, D;
     float inv_sqrt_d;
     float *qt;          // [U][k.kslots + 1]: qt_j, then beta
+    uint16_t *qf;       // [U][2][k.kfetch]: fp16 high and low parts of qt * 2^-e, fetch order
+    float *qmul;        // [U]: 2^e
     float *part;        // [U][nchunks][v.kslots + 2]: abar partial sums, then max, sum
 };
 
@@ -1064,12 +1069,29 @@ __global__ __launch_bounds__(256) void attend_prep_kernel(AttendArgs a) {
         qt = k.qscale[static_cast<int64_t>(u) * k.rmax + c] * acc * a.inv_sqrt_d;
         mp = k.qmin[static_cast<int64_t>(u) * k.rmax + c] * acc;
     }
+    __shared__ float qts[kMaxSlots];
+    __shared__ float red[4];
     if (tid < k.kslots) {
         a.qt[static_cast<int64_t>(u) * (k.kslots + 1) + tid] = qt;
         mpart[tid] = mp;
+        qts[tid] = qt;
     }
-    __syncthreads();
+    // the scorer's operands in fetch order: qt * 2^-e as an fp16 high part and an
+    // fp16 remainder, with 2^e > max |qt| so that neither overflows (padding
+    // columns are zero)
+    const float amax = block_reduce(fabsf(qt), red, true);
+    int e = 0;
+    if (amax > 0.f) frexpf(amax, &e);
+    for (int kk = tid; kk < k.kfetch; kk += blockDim.x) {
+        const int j = k.fslot[static_cast<int64_t>(u) * k.kfetch + kk];
+        const float v = j >= 0 ? ldexpf(qts[j], -e) : 0.f;
+        const _Float16 hi = static_cast<_Float16>(v);
+        const _Float16 lo = static_cast<_Float16>(v - static_cast<float>(hi));
+        a.qf[(static_cast<int64_t>(u) * 2 + 0) * k.kfetch + kk] = __builtin_bit_cast(uint16_t, hi);
+        a.qf[(static_cast<int64_t>(u) * 2 + 1) * k.kfetch + kk] = __builtin_bit_cast(uint16_t, lo);
+    }
     if (tid == 0) {
+        a.qmul[u] = ldexpf(1.0f, e);
         float beta = 0.f;
         for (int d = 0; d < a.D; ++d) beta = fmaf(ql[d], k.mu[static_cast<int64_t>(u) * a.D + d], beta);
         for (int j = 0; j < k.kslots; ++j) beta += mpart[j];
@@ -1089,14 +1111,14 @@ __global__ __launch_bounds__(256) void attend_partial_kernel(AttendArgs a) {
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const AttendSide &K = a.k, &V = a.v;
     float *qt_l = reinterpret_cast<float *>(smem);                       // [K.kslots + 1]
-    uint32_t *ksb = reinterpret_cast<uint32_t *>(qt_l + kMaxSlots + 1);  // [K.kslots]
+    uint32_t *ksb = reinterpret_cast<uint32_t *>(qt_l + kMaxSlots + 4);  // [2][K.kfetch] fp16 (16-byte aligned)
     uint32_t *vsb = ksb + kMaxSlots;                                     // [V.kslots]
     float *pl = reinterpret_cast<float *>(vsb + kMaxSlots);              // [kAttChunk]
     float *red = pl + kAttChunk;                                         // [4][kMaxSlots]
     uint32_t *rows = reinterpret_cast<uint32_t *>(red + 4 * kMaxSlots);  // [kAttChunk][pitch]
     const int64_t s0 = static_cast<int64_t>(c) * kAttChunk;
     const int nrows = static_cast<int>(min<int64_t>(kAttChunk, a.s_end - s0));
-    const int nk = K.ui[u].n_slots, nv = V.ui[u].n_slots;
+    const int nv = V.ui[u].n_slots;
     // word i of a chunk's rows goes to (i / row_words, i % row_words); the
     // quotient from a float reciprocal is exact for i < 2^16
     auto stage = [&](const AttendSide &T, int pitch) {
@@ -1110,24 +1132,53 @@ __global__ __launch_bounds__(256) void attend_partial_kernel(AttendArgs a) {
     const int kp = (K.row_words + 1) | 1, vp = (V.row_words + 1) | 1;   // odd, > row_words
 
     for (int i = tid; i <= K.kslots; i += blockDim.x) qt_l[i] = a.qt[static_cast<int64_t>(u) * (K.kslots + 1) + i];
-    for (int i = tid; i < K.kslots; i += blockDim.x) ksb[i] = K.sbits[static_cast<int64_t>(u) * K.kslots + i];
+    {
+        const uint32_t *src = reinterpret_cast<const uint32_t *>(a.qf + static_cast<int64_t>(u) * 2 * K.kfetch);
+        for (int i = tid; i < K.kfetch; i += blockDim.x) ksb[i] = src[i];   // 2*kfetch halves
+    }
     for (int i = tid; i < V.kslots; i += blockDim.x) vsb[i] = V.sbits[static_cast<int64_t>(u) * V.kslots + i];
     stage(K, kp);
     __syncthreads();
 
-    // scores of this thread's two rows (row-serial sums over the stored slots;
-    // rows past the chunk are computed on stale words and never stored)
+    // scores of this thread's two rows, k-step by k-step in the fetch order: the
+    // fetch kernel's field decode gives a k-step's 16 codes as exact fp16 values,
+    // which are dotted (fp32 accumulation) with the high and low fp16 parts of the
+    // prescaled coefficients; rows past the chunk are decoded from stale words and
+    // never stored, and padding columns have zero coefficients
     float mloc = -__builtin_huge_valf();
     {
+        uint32_t kd[kAttKsK];
+        const int nksK = K.kfetch / 16;
+#pragma unroll
+        for (int ks = 0; ks < kAttKsK; ++ks)
+            kd[ks] = ks < nksK ? __builtin_amdgcn_readfirstlane(K.kdesc[static_cast<int64_t>(u) * nksK + ks]) : 0u;
+        const _Float16 *qh = reinterpret_cast<const _Float16 *>(ksb), *ql = qh + K.kfetch;
         const int r0 = tid, r1 = tid + 256;
         const uint32_t *row0 = rows + r0 * kp, *row1 = rows + r1 * kp;
-        float acc0 = qt_l[K.kslots], acc1 = acc0;
-        for (int j = 0; j < nk; ++j) {
-            const uint32_t sb = ksb[j];
-            const float w = qt_l[j];
-            acc0 = fmaf(static_cast<float>(row_field(row0, sb)), w, acc0);
-            acc1 = fmaf(static_cast<float>(row_field(row1, sb)), w, acc1);
+        float acc0 = 0.f, acc1 = 0.f;
+#pragma unroll
+        for (int ks = 0; ks < kAttKsK; ++ks) {
+            if (((kd[ks] >> 16) & 0xFu) == 0u) continue;               // empty k-step (uniform)
+#pragma unroll
+            for (uint32_t hk = 0; hk < 2; ++hk) {
+                const half8 h8 = *reinterpret_cast<const half8 *>(qh + ks * 16 + hk * 8);
+                const half8 l8 = *reinterpret_cast<const half8 *>(ql + ks * 16 + hk * 8);
+                const half8 c0 = decode_kstep<false>(kd[ks], row0, nullptr, hk);
+                const half8 c1 = decode_kstep<false>(kd[ks], row1, nullptr, hk);
+#pragma unroll
+                for (int e = 0; e < 8; e += 2) {
+                    const half2 hv = {h8[e], h8[e + 1]}, lv = {l8[e], l8[e + 1]};
+                    const half2 v0 = {c0[e], c0[e + 1]}, v1 = {c1[e], c1[e + 1]};
+                    acc0 = __builtin_amdgcn_fdot2(v0, hv, acc0, false);
+                    acc0 = __builtin_amdgcn_fdot2(v0, lv, acc0, false);
+                    acc1 = __builtin_amdgcn_fdot2(v1, hv, acc1, false);
+                    acc1 = __builtin_amdgcn_fdot2(v1, lv, acc1, false);
+                }
+            }
         }
+        const float beta = qt_l[K.kslots], mul = a.qmul[u];
+        acc0 = fmaf(acc0, mul, beta);
+        acc1 = fmaf(acc1, mul, beta);
         if (r0 < nrows) {
             pl[r0] = acc0;
             mloc = acc0;
@@ -1596,7 +1647,8 @@ int32_t launch_fetch_plans(const FetchPlan &p0, const FetchPlan *p1, hipStream_t
 // per unit, head size and slot count within the kernels' limits.
 int32_t attend_side_ok(const kvtc_state_header *h) {
     if (h->mode != KVTC_MODE_DP || h->heads_per_unit != 1) return KVTC_E_STATE;
-    if (h->head_dim > kMaxSlots || h->kslots > kMaxSlots || h->row_stride > kMaxRowStride) return KVTC_E_SHAPE;
+    if (h->head_dim > kMaxSlots || h->kslots > kMaxSlots || h->kfetch > kMaxSlots || h->row_stride > kMaxRowStride)
+        return KVTC_E_SHAPE;
     return KVTC_OK;
 }
 
@@ -1613,16 +1665,34 @@ AttendSide attend_side(const kvtc_state_header *h, const void *state_dev, const 
     sd_.bias = reinterpret_cast<const float *>(sd + h->off_bias);
     sd_.comp = reinterpret_cast<const int32_t *>(sd + h->off_slot_comp);
     sd_.sbits = reinterpret_cast<const uint32_t *>(sd + h->off_slot_bits);
+    sd_.kdesc = reinterpret_cast<const uint32_t *>(sd + h->off_kdesc);
+    sd_.fslot = reinterpret_cast<const int32_t *>(sd + h->off_fslot);
     sd_.kslots = h->kslots;
     sd_.rmax = h->rmax;
     sd_.row_words = h->row_stride / 4;
+    sd_.kfetch = h->kfetch;
     return sd_;
 }
 
-size_t attend_work_bytes(const kvtc_state_header *hk, const kvtc_state_header *hv, int64_t s_end) {
+// Workspace regions, each 256-byte aligned: qt [U][kslots_k + 1] f32,
+// qf [U][2][kfetch_k] f16, qmul [U] f32, partial sums [U][nchunks][kslots_v + 2] f32.
+struct AttendWork {
+    uint64_t qt, qf, qmul, part, total;
+};
+
+AttendWork attend_work(const kvtc_state_header *hk, const kvtc_state_header *hv, int64_t s_end) {
+    AttendWork w{};
     const int64_t nchunks = (s_end + kAttChunk - 1) / kAttChunk;
-    const uint64_t qt = align_up(static_cast<uint64_t>(hk->units) * (hk->kslots + 1) * sizeof(float), 256);
-    return qt + static_cast<uint64_t>(hv->units) * nchunks * (hv->kslots + 2) * sizeof(float);
+    w.qt = 0;
+    w.qf = align_up(static_cast<uint64_t>(hk->units) * (hk->kslots + 1) * sizeof(float), 256);
+    w.qmul = w.qf + align_up(static_cast<uint64_t>(hk->units) * 2 * hk->kfetch * sizeof(uint16_t), 256);
+    w.part = w.qmul + align_up(static_cast<uint64_t>(hk->units) * sizeof(float), 256);
+    w.total = w.part + static_cast<uint64_t>(hv->units) * nchunks * (hv->kslots + 2) * sizeof(float);
+    return w;
+}
+
+size_t attend_work_bytes(const kvtc_state_header *hk, const kvtc_state_header *hv, int64_t s_end) {
+    return attend_work(hk, hv, s_end).total;
 }
 
 }  // namespace
@@ -1741,17 +1811,20 @@ int32_t kvtc_attend(const kvtc_tensor_ref *k, const kvtc_tensor_ref *v, const vo
     a.H = static_cast<int>(hk->heads);
     a.D = hk->head_dim;
     a.inv_sqrt_d = 1.0f / sqrtf(static_cast<float>(hk->head_dim));
-    a.qt = static_cast<float *>(work_dev);
-    a.part = reinterpret_cast<float *>(static_cast<char *>(work_dev) +
-                                       align_up(static_cast<uint64_t>(hk->units) * (hk->kslots + 1) * sizeof(float), 256));
+    const AttendWork wl = attend_work(hk, hv, s_end);
+    char *wb = static_cast<char *>(work_dev);
+    a.qt = reinterpret_cast<float *>(wb + wl.qt);
+    a.qf = reinterpret_cast<uint16_t *>(wb + wl.qf);
+    a.qmul = reinterpret_cast<float *>(wb + wl.qmul);
+    a.part = reinterpret_cast<float *>(wb + wl.part);
     hipStream_t stream = static_cast<hipStream_t>(hip_stream);
     const unsigned U = static_cast<unsigned>(hk->units);
     hipLaunchKernelGGL(attend_prep_kernel, dim3(U), dim3(256), 0, stream, a);
     if (hipGetLastError() != hipSuccess) return KVTC_E_DEVICE;
     if (nchunks > 0) {
         const int rw = std::max(a.k.row_words, a.v.row_words);
-        const size_t lds = (kMaxSlots + 1 + 2 * kMaxSlots + kAttChunk + 4 * kMaxSlots) * sizeof(float) +
-                           static_cast<size_t>(kAttChunk) * ((rw + 1) | 1) * sizeof(uint32_t);
+        const size_t lds = (kMaxSlots + 4 + 2 * kMaxSlots + kAttChunk + 4 * kMaxSlots) * sizeof(float) +
+                           (static_cast<size_t>(kAttChunk) * ((rw + 1) | 1) + 8) * sizeof(uint32_t);
         if (lds > kLdsMax) return KVTC_E_SHAPE;
         if (!allow_lds(reinterpret_cast<const void *>(attend_partial_kernel))) return KVTC_E_DEVICE;
         hipLaunchKernelGGL(attend_partial_kernel, dim3(static_cast<unsigned>(nchunks), U), dim3(256), lds, stream, a);

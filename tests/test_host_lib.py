@@ -375,10 +375,12 @@ def test_attend_validates_before_launch():
     Xm = synth.generate(wm, 0, 0, 64)[:, :8]
     mixed = K.kvtc_fit_host(K.make_config("mixed", 128, 8, 64, group_size=32), np.ascontiguousarray(Xm))
     need = K.kvtc_attend_workspace(blob, blob, 100)
-    U, ks = st.U, K.header(blob).kslots
-    # regions: qt [U][ks+1] f32 (256-byte aligned), then one 512-row chunk of
+    U, ks, kf = st.U, K.header(blob).kslots, K.header(blob).kfetch
+    up = lambda n: -(-n // 256) * 256
+    # regions: qt [U][ks+1] f32, fetch-order fp16 high/low coefficients [U][2][kf],
+    # the 2^e prescale [U] f32 (each 256-byte aligned), then one 512-row chunk of
     # partial sums [U][1][ks + 2] f32 for 100 rows
-    assert need == -(-(U * (ks + 1) * 4) // 256) * 256 + U * 1 * (ks + 2) * 4
+    assert need == up(U * (ks + 1) * 4) + up(U * 2 * kf * 2) + up(U * 4) + U * 1 * (ks + 2) * 4
     fake = 0x1000
 
     def ref(b, capacity=100):
