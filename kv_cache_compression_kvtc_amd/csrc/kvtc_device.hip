@@ -1554,9 +1554,11 @@ int32_t launch_append_plan(const AppendPlan &p, hipStream_t stream) {
                    : launch_append<false, float>(p.a, p.ntiles, p.units, p.nb, stream);
 }
 
+// share: how many tensors the launch is shared by (1 or 2); the block target
+// of one launch is split between them
 int32_t plan_fetch(const void *state_host, const void *state_dev, const void *codes_dev, const void *params_dev,
                    int64_t capacity, int64_t s_begin, int64_t s_end, void *out_dev, const int64_t out_strides[4],
-                   FetchPlan *p) {
+                   FetchPlan *p, int share = 1) {
     const kvtc_state_header *h = nullptr;
     int32_t st = check_state(state_host, &h);
     if (st != KVTC_OK) return st;
@@ -1609,7 +1611,8 @@ int32_t plan_fetch(const void *state_host, const void *state_dev, const void *co
     const int64_t work = h->units * a.nslices * ntiles;
     const int nw = (DS == 128 && h->kfetch >= 160) ? 8 : 4;
     // about two four-wave blocks, or one eight-wave block, per CU in one round
-    const int64_t target = kFetchBlocks * 4 / nw;
+    // (shared between the tensors of a paired launch)
+    const int64_t target = kFetchBlocks * 4 / nw / share;
     const int64_t tpb = std::min<int64_t>(std::max<int64_t>(nw, (work + target - 1) / target), ntiles);
     a.tiles_per_block = static_cast<int>(tpb);
     a.nchunks = static_cast<int>((ntiles + tpb - 1) / tpb);
@@ -1751,7 +1754,14 @@ int32_t kvtc_fetch_kv(const kvtc_tensor_ref *k, const kvtc_tensor_ref *v, int64_
                     v->rows_dev, v->strides, &pv);
     if (st != KVTC_OK || s_end == s_begin) return st;
     hipStream_t stream = static_cast<hipStream_t>(hip_stream);
-    if (pk.mixed == pv.mixed && pk.ds == pv.ds) return launch_fetch_plans(pk, &pv, stream);
+    if (pk.mixed == pv.mixed && pk.ds == pv.ds) {
+        // one launch: re-plan both with the block target split between them
+        plan_fetch(k->state_host, k->state_dev, k->codes_dev, k->params_dev, k->capacity, s_begin, s_end,
+                   k->rows_dev, k->strides, &pk, 2);
+        plan_fetch(v->state_host, v->state_dev, v->codes_dev, v->params_dev, v->capacity, s_begin, s_end,
+                   v->rows_dev, v->strides, &pv, 2);
+        return launch_fetch_plans(pk, &pv, stream);
+    }
     st = launch_fetch_plans(pk, nullptr, stream);
     if (st != KVTC_OK) return st;
     return launch_fetch_plans(pv, nullptr, stream);
