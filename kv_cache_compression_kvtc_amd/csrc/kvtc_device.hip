@@ -1756,10 +1756,12 @@ int32_t kvtc_fetch_kv(const kvtc_tensor_ref *k, const kvtc_tensor_ref *v, int64_
     hipStream_t stream = static_cast<hipStream_t>(hip_stream);
     if (pk.mixed == pv.mixed && pk.ds == pv.ds) {
         // one launch: re-plan both with the block target split between them
-        plan_fetch(k->state_host, k->state_dev, k->codes_dev, k->params_dev, k->capacity, s_begin, s_end,
-                   k->rows_dev, k->strides, &pk, 2);
-        plan_fetch(v->state_host, v->state_dev, v->codes_dev, v->params_dev, v->capacity, s_begin, s_end,
-                   v->rows_dev, v->strides, &pv, 2);
+        st = plan_fetch(k->state_host, k->state_dev, k->codes_dev, k->params_dev, k->capacity, s_begin, s_end,
+                        k->rows_dev, k->strides, &pk, 2);
+        if (st != KVTC_OK) return st;
+        st = plan_fetch(v->state_host, v->state_dev, v->codes_dev, v->params_dev, v->capacity, s_begin, s_end,
+                        v->rows_dev, v->strides, &pv, 2);
+        if (st != KVTC_OK) return st;
         return launch_fetch_plans(pk, &pv, stream);
     }
     st = launch_fetch_plans(pk, nullptr, stream);
