@@ -33,7 +33,9 @@ sys.path.insert(0, ROOT)
 
 PEAK_HBM_GBPS = 8000.0
 PMC_SUMMARY = os.path.join(ROOT, "profiles", "fetch_batched_decode_pmc.txt")
-DEVICE_SRC = os.path.join(ROOT, "kv_cache_compression_kvtc_amd", "csrc", "kvtc_device.hip")
+# the sources that decide the fetch kernel's code and launch shape
+FETCH_SRC = [os.path.join(ROOT, "kv_cache_compression_kvtc_amd", "csrc", f)
+             for f in ("kvtc_device.h", "kvtc_fetch_kernel.h", "kvtc_fetch_ks.hip", "kvtc_device.hip")]
 
 
 def parse():
@@ -57,7 +59,11 @@ def log(*a):
 
 
 def source_hash() -> str:
-    return hashlib.sha256(open(DEVICE_SRC, "rb").read()).hexdigest()[:16]
+    """Hash of the fetch kernel's sources: counters taken on other sources are not reported."""
+    h = hashlib.sha256()
+    for f in FETCH_SRC:
+        h.update(open(f, "rb").read())
+    return h.hexdigest()[:16]
 
 
 def pmc_traffic():
@@ -413,6 +419,8 @@ def main():
             fh.write(text)
         print(text, end="")
         return
+    from kv_cache_compression_kvtc_amd.build import ensure_current
+    ensure_current(log=log)                                # never time a library built from other sources
     import torch
     from kv_cache_compression_kvtc_amd import kvtc as K
     assert torch.cuda.is_available(), "bench.py needs a HIP device"

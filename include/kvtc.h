@@ -146,6 +146,11 @@ typedef struct kvtc_state_header {
 /* Fill *cfg with the defaults of the given mode and head dimension. */
 void kvtc_config_default(kvtc_config *cfg, int32_t mode, int32_t head_dim);
 
+/* Identity of this build: the first 16 hex digits of the SHA-256 over the
+ * library's source files, fixed at compile time (static string).  A caller can
+ * compare it with the hash of the sources it expects, to refuse a stale build. */
+const char *kvtc_build_id(void);
+
 /* Human-readable name of a status code (static string). */
 const char *kvtc_status_string(int32_t status);
 

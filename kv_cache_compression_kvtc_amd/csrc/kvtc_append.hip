@@ -1,0 +1,557 @@
+// Append kernels of libkvtc for gfx950 (CDNA4) and their launchers.
+//
+// Append (KVTC cache module page, module docstring "Design", decode step 1;
+// PALU cache API page, "Design", decode steps 1-2): every row is centred,
+// projected through the frozen basis of its unit, each stored component is
+// quantised at its frozen width and the codes are OR-ed into a little-endian
+// bit row in LDS, which is then written to the store with coalesced stores.
+// The projection runs on fp64 MFMA so that codes are decided from latents
+// accurate to ~1e-16, i.e. identical to a float64 evaluation except when a
+// value lies within rounding distance of a quantisation boundary.
+#include "kvtc_device.h"
+
+namespace kvtc {
+namespace {
+
+// Wave w owns tokens 16w..16w+15; N-block nb covers slots 16nb..16nb+15.
+template <bool MIXED, typename XT, int NB, bool XVEC>
+__global__ __launch_bounds__(kThreads) void append_kernel(AppendArgs a) {
+    extern __shared__ __align__(16) unsigned char smem[];
+    double *xs = reinterpret_cast<double *>(smem);                         // [2][64][kAppPad]
+    float *vs = reinterpret_cast<float *>(xs + 2 * kAppTok * kAppPad);     // [2][NB*16][kAppPad]
+    uint32_t *rows = reinterpret_cast<uint32_t *>(vs + 2 * NB * 16 * kAppPad);  // [64][row_words]
+
+    const int u = blockIdx.y;
+    const int64_t t0 = static_cast<int64_t>(blockIdx.x) * kAppTok;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int b = u / a.groups, g = u % a.groups;
+    const int nvalid = static_cast<int>(min<int64_t>(kAppTok, a.n - t0));
+    const int n_slots = a.ui[u].n_slots;
+    const int row_words = a.row_stride >> 2;
+    const XT *x = static_cast<const XT *>(a.x);
+
+    for (int w = tid; w < kAppTok * row_words; w += kThreads) rows[w] = 0u;
+
+    // staging map: thread -> (token, 4 consecutive columns) of a 64 x 16 chunk,
+    // and (slot, 4 columns) of the NB*16 x 16 basis chunk
+    const int st_tok = tid >> 2, st_col = (tid & 3) * 4;
+    constexpr int kVReps = (NB * 16 + 63) / 64;
+    // a chunk's loads only fill these registers (indices clamped, so no load
+    // sits behind a branch); centring and the fp64 conversion happen when the
+    // chunk is written to LDS, after the MFMAs of the previous chunk, so the
+    // loads are in flight during those MFMAs
+    typename RawX4<XT>::v xv;
+    XT xraw[4];
+    float muv[4];
+    float vr[kVReps][4];
+    const int tok_c = min(st_tok, nvalid - 1);
+
+    auto load_chunk = [&](int kc) {
+        const int gd = kc * kAppKC + st_col;          // column within the unit's row
+        const int j = gd / a.D, dd = gd - j * a.D;
+        const int h = g * a.hpu + j;
+        const float *mu = a.mu + static_cast<int64_t>(u) * a.dg + gd;
+        const XT *p = x + b * a.xsb + h * a.xsh + (t0 + tok_c) * a.xss + dd;
+        if constexpr (XVEC) {
+            xv = *reinterpret_cast<const typename RawX4<XT>::v *>(p);
+        } else {
+#pragma unroll
+            for (int i = 0; i < 4; ++i) xraw[i] = p[i];
+        }
+#pragma unroll
+        for (int i = 0; i < 4; ++i) muv[i] = mu[i];
+#pragma unroll
+        for (int rep = 0; rep < kVReps; ++rep) {
+            const int slot = min(rep * 64 + st_tok, a.kslots - 1);
+            const float *q = a.basis + (static_cast<int64_t>(u) * a.kslots + slot) * a.dg + gd;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) vr[rep][i] = q[i];
+        }
+    };
+    auto store_chunk = [&](int buf) {
+        double *xb = xs + buf * kAppTok * kAppPad + st_tok * kAppPad + st_col;
+        const bool tok_ok = st_tok < nvalid;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const double xi = XVEC ? RawX4<XT>::get(xv, i) : load_x(&xraw[i]);
+            xb[i] = tok_ok ? xi - static_cast<double>(muv[i]) : 0.0;
+        }
+#pragma unroll
+        for (int rep = 0; rep < kVReps; ++rep) {
+            const int slot = rep * 64 + st_tok;
+            if (slot < NB * 16) {
+                const bool keep = slot < a.kslots;      // slots past kslots are zero
+                float *vb = vs + (buf * NB * 16 + slot) * kAppPad + st_col;
+#pragma unroll
+                for (int i = 0; i < 4; ++i) vb[i] = keep ? vr[rep][i] : 0.0f;
+            }
+        }
+    };
+
+    doublex4 acc[NB];
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) acc[nb] = doublex4{0.0, 0.0, 0.0, 0.0};
+
+    const int nchunks = a.dg / kAppKC;
+    load_chunk(0);
+    store_chunk(0);
+    __syncthreads();
+    const int mrow = wave * 16 + (lane & 15);   // A operand row (token) of this lane
+    const int kcol = lane >> 4;                 // A/B operand k of this lane
+    // k-step order: k-step 4c + e of the contraction takes, at operand k = q, the
+    // feature 16c + 4q + e (c = 16-column chunk); every append kernel uses this
+    // order, so that a lane of the decode kernel holds its operands as whole
+    // 16-byte vectors of the basis
+    for (int kc = 0; kc < nchunks; ++kc) {
+        const int buf = kc & 1;
+        if (kc + 1 < nchunks) load_chunk(kc + 1);
+        const double *xb = xs + buf * kAppTok * kAppPad;
+        const float *vb = vs + buf * NB * 16 * kAppPad;
+#pragma unroll
+        for (int ks = 0; ks < kAppKC / 4; ++ks) {
+            const double av = xb[mrow * kAppPad + kcol * 4 + ks];
+#pragma unroll
+            for (int nb = 0; nb < NB; ++nb) {
+                const double bv = static_cast<double>(vb[(nb * 16 + (lane & 15)) * kAppPad + kcol * 4 + ks]);
+                acc[nb] = __builtin_amdgcn_mfma_f64_16x16x4f64(av, bv, acc[nb], 0, 0, 0);
+            }
+        }
+        if (kc + 1 < nchunks) store_chunk(buf ^ 1);
+        __syncthreads();
+    }
+
+    // fp64 16x16x4 result layout: acc[nb][i] is row (lane>>4) + 4i, column lane&15, i.e.
+    // the latent of token 16*wave + (lane>>4) + 4i and slot 16*nb + (lane&15)
+    const int tbase = wave * 16 + (lane >> 4);
+    const int64_t ub = static_cast<int64_t>(u) * a.kslots;
+    if constexpr (!MIXED) {
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb) {
+            const int j = nb * 16 + (lane & 15);
+            if (j < n_slots) {
+                const double lo = a.qlo[ub + j], inv = a.qinv[ub + j];
+                const uint32_t sb = a.sbits[ub + j];
+                const uint32_t off = sb & kOffsetMask, w = sb >> 24;
+                const double cmax = static_cast<double>((1u << w) - 1u);
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const int t = tbase + 4 * i;
+                    if (t < nvalid) {
+                        const uint32_t c = static_cast<uint32_t>(quantise(acc[nb][i], lo, inv, cmax));
+                        or_field(rows + t * row_words, off, w, c);
+                    }
+                }
+            }
+        }
+    } else {
+        const int ngroups = (n_slots + a.gs - 1) / a.gs;
+        for (int gi = 0; gi < ngroups; ++gi) {
+            const int j0 = gi * a.gs, j1 = min(n_slots, j0 + a.gs);
+            const uint32_t w = a.sbits[ub + j0] >> 24;
+            const double cmax = static_cast<double>((1u << w) - 1u);
+            double mn[4], mx[4];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                mn[i] = __builtin_huge_val();
+                mx[i] = -__builtin_huge_val();
+            }
+#pragma unroll
+            for (int nb = 0; nb < NB; ++nb) {
+                const int j = nb * 16 + (lane & 15);
+                if (j >= j0 && j < j1) {
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        mn[i] = fmin(mn[i], acc[nb][i]);
+                        mx[i] = fmax(mx[i], acc[nb][i]);
+                    }
+                }
+            }
+#pragma unroll
+            for (int m = 1; m < 16; m <<= 1) {
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    mn[i] = fmin(mn[i], __shfl_xor(mn[i], m, 16));
+                    mx[i] = fmax(mx[i], __shfl_xor(mx[i], m, 16));
+                }
+            }
+            double lo16[4], inv16[4];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const uint16_t hmin = half_bits_rne(mn[i]);
+                const uint16_t hscale = half_bits_rne((mx[i] - mn[i]) / cmax);
+                lo16[i] = half_bits_to_double(hmin);
+                const double sc = half_bits_to_double(hscale);
+                inv16[i] = sc > 0.0 ? 1.0 / sc : 0.0;
+                const int t = tbase + 4 * i;
+                if ((lane & 15) == 0 && t < nvalid)
+                    a.params[(static_cast<int64_t>(u) * a.capacity + a.s0 + t0 + t) * a.n_qg + gi] =
+                        static_cast<uint32_t>(hmin) | (static_cast<uint32_t>(hscale) << 16);
+            }
+#pragma unroll
+            for (int nb = 0; nb < NB; ++nb) {
+                const int j = nb * 16 + (lane & 15);
+                if (j >= j0 && j < j1) {
+                    const uint32_t off = a.sbits[ub + j] & kOffsetMask;
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        const int t = tbase + 4 * i;
+                        if (t < nvalid) {
+                            const uint32_t c = static_cast<uint32_t>(quantise(acc[nb][i], lo16[i], inv16[i], cmax));
+                            or_field(rows + t * row_words, off, w, c);
+                        }
+                    }
+                }
+            }
+        }
+    }
+    __syncthreads();
+    if (row_words > 0) {
+        uint32_t *dst = reinterpret_cast<uint32_t *>(
+            a.codes + (static_cast<int64_t>(u) * a.capacity + a.s0 + t0) * a.row_stride);
+        for (int w = tid; w < nvalid * row_words; w += kThreads) dst[w] = rows[w];
+    }
+}
+
+// Few-row append (decode): one block per unit and up to 16 rows.  The whole
+// basis of the unit is staged in LDS with every load in flight at once, and the
+// N-blocks are spread over the 4 waves.  Each row goes through exactly the same
+// sequence of fp64 MFMAs (same operands, same k order) as in append_kernel, so
+// a row's codes do not depend on which kernel appended it.
+template <typename XT, int NB>
+__global__ __launch_bounds__(kThreads) void append_small_kernel(AppendArgs a) {
+    extern __shared__ __align__(16) unsigned char smem[];
+    const int xpitch = a.dg + 1, vpitch = a.dg + 1;
+    double *xs = reinterpret_cast<double *>(smem);                       // [16][xpitch]
+    float *vs = reinterpret_cast<float *>(xs + 16 * xpitch);             // [NB*16][vpitch]
+    uint32_t *rows = reinterpret_cast<uint32_t *>(vs + NB * 16 * vpitch);  // [16][row_words]
+
+    const int u = blockIdx.y;
+    const int64_t t0 = static_cast<int64_t>(blockIdx.x) * 16;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int b = u / a.groups, g = u % a.groups;
+    const int nvalid = static_cast<int>(min<int64_t>(16, a.n - t0));
+    const int n_slots = a.ui[u].n_slots;
+    const int row_words = a.row_stride >> 2;
+    const XT *x = static_cast<const XT *>(a.x);
+
+    constexpr int NBW = (NB + 3) / 4;       // N-blocks of this wave: wave, wave+4, ...
+    // Every global load of the block is issued before the first LDS write, so
+    // the kernel waits for memory once: this lane's slot constants (indices
+    // clamped; unused past n_slots), the first batch of the basis, then the
+    // valid input rows.  Quotients of indices by dg and dg/4 come from float
+    // reciprocals, exact for indices below 2^16.
+    const int64_t ub = static_cast<int64_t>(u) * a.kslots;
+    double qlo_r[NBW], qinv_r[NBW];
+    uint32_t sb_r[NBW];
+#pragma unroll
+    for (int q = 0; q < NBW; ++q) {
+        const int j = min((wave + 4 * q) * 16 + (lane & 15), a.kslots - 1);
+        qlo_r[q] = a.qlo[ub + j];
+        qinv_r[q] = a.qinv[ub + j];
+        sb_r[q] = a.sbits[ub + j];
+    }
+    const int q4 = a.dg / 4;
+    const float *basis = a.basis + static_cast<int64_t>(u) * a.kslots * a.dg;
+    const int nv = NB * 16 * q4, nload = a.kslots * q4;
+    constexpr int kBatchV = 16;
+    float4 vb[kBatchV];
+    auto load_basis = [&](int i0) {
+#pragma unroll
+        for (int q = 0; q < kBatchV; ++q) {
+            const int i = min(i0 + q * kThreads + tid, nload - 1);
+            vb[q] = *reinterpret_cast<const float4 *>(basis + static_cast<int64_t>(i) * 4);
+        }
+    };
+    auto store_basis = [&](int i0) {
+#pragma unroll
+        for (int q = 0; q < kBatchV; ++q) {
+            const int i = i0 + q * kThreads + tid;
+            if (i < nv) {
+                const int slot = static_cast<int>((static_cast<float>(i) + 0.5f) * a.inv_q4);
+                const int c = (i - slot * q4) * 4;
+                const bool keep = i < nload;           // slots past kslots are zero
+                float *dst = vs + slot * vpitch + c;
+                dst[0] = keep ? vb[q].x : 0.f;
+                dst[1] = keep ? vb[q].y : 0.f;
+                dst[2] = keep ? vb[q].z : 0.f;
+                dst[3] = keep ? vb[q].w : 0.f;
+            }
+        }
+    };
+    load_basis(0);
+    {
+        const float *mu = a.mu + static_cast<int64_t>(u) * a.dg;
+        const int nx = nvalid * a.dg;
+        for (int i = tid; i < nx; i += kThreads) {
+            const int t = static_cast<int>((static_cast<float>(i) + 0.5f) * a.inv_dg);
+            const int d = i - t * a.dg;
+            xs[t * xpitch + d] =
+                load_x(x + b * a.xsb + g * a.xsh + (t0 + t) * a.xss + d) - static_cast<double>(mu[d]);
+        }
+        for (int i = nx + tid; i < 16 * a.dg; i += kThreads) {
+            const int t = static_cast<int>((static_cast<float>(i) + 0.5f) * a.inv_dg);
+            xs[t * xpitch + (i - t * a.dg)] = 0.0;
+        }
+    }
+    for (int w = tid; w < 16 * row_words; w += kThreads) rows[w] = 0u;
+    store_basis(0);
+    for (int i0 = kBatchV * kThreads; i0 < nv; i0 += kBatchV * kThreads) {
+        load_basis(i0);
+        store_basis(i0);
+    }
+    __syncthreads();
+
+    doublex4 acc[NBW];
+#pragma unroll
+    for (int q = 0; q < NBW; ++q) acc[q] = doublex4{0.0, 0.0, 0.0, 0.0};
+    const int mrow = lane & 15, kcol = lane >> 4;
+    for (int ks = 0; ks < a.dg / 4; ++ks) {
+        const int col = (ks >> 2) * 16 + kcol * 4 + (ks & 3);   // k-step order of append_kernel
+        const double av = xs[mrow * xpitch + col];
+#pragma unroll
+        for (int q = 0; q < NBW; ++q) {
+            const int nb = wave + 4 * q;
+            if (nb < NB) {
+                const double bv = static_cast<double>(vs[(nb * 16 + (lane & 15)) * vpitch + col]);
+                acc[q] = __builtin_amdgcn_mfma_f64_16x16x4f64(av, bv, acc[q], 0, 0, 0);
+            }
+        }
+    }
+#pragma unroll
+    for (int q = 0; q < NBW; ++q) {
+        const int nb = wave + 4 * q;
+        const int j = nb * 16 + (lane & 15);
+        if (nb < NB && j < n_slots) {
+            const double lo = qlo_r[q], inv = qinv_r[q];
+            const uint32_t sb = sb_r[q];
+            const uint32_t off = sb & kOffsetMask, w = sb >> 24;
+            const double cmax = static_cast<double>((1u << w) - 1u);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int t = (lane >> 4) + 4 * i;
+                if (t < nvalid) {
+                    const uint32_t c = static_cast<uint32_t>(quantise(acc[q][i], lo, inv, cmax));
+                    or_field(rows + t * row_words, off, w, c);
+                }
+            }
+        }
+    }
+    __syncthreads();
+    if (row_words > 0) {
+        uint32_t *dst = reinterpret_cast<uint32_t *>(
+            a.codes + (static_cast<int64_t>(u) * a.capacity + a.s0 + t0) * a.row_stride);
+        for (int w = tid; w < nvalid * row_words; w += kThreads) dst[w] = rows[w];
+    }
+}
+
+size_t decode_lds_bytes(int dg, int row_stride) {
+    return 16 * static_cast<size_t>(dg + 1) * sizeof(double) + 16 * static_cast<size_t>(row_stride / 4) * sizeof(uint32_t);
+}
+
+// Decode append (up to 16 rows per unit, DP mode, unit width DG): one block per
+// unit, one wave per 16-slot N-block.  In the k-step order of append_kernel a
+// lane's basis operands (slot 16*wave + lane%16, features 16c + 4*(lane/16) +
+// 0..3 for k-steps 4c..4c+3) are whole 16-byte vectors, loaded straight into
+// registers: the basis never passes through LDS and every load of the block is
+// in flight before its first wait; only the centred rows are staged in LDS.  The fp64 MFMA sequence per row (operands and k order) is
+// the one of append_kernel, so a row's codes do not depend on the kernel that
+// appended it.  Rows past the valid ones are left unset in LDS: a row of the
+// MFMA result depends only on the same row of A, and those rows are not used.
+template <typename XT, int DG>
+__global__ __launch_bounds__(512) void append_decode_kernel(AppendPair m) {
+    extern __shared__ __align__(16) unsigned char smem[];
+    constexpr int XP = DG + 1;          // LDS pitch (doubles) of a centred row
+    constexpr int NKS = DG / 4;         // MFMA k-steps
+    double *xs = reinterpret_cast<double *>(smem);                    // [16][XP]
+    uint32_t *rows = reinterpret_cast<uint32_t *>(xs + 16 * XP);      // [16][row_words]
+
+    const bool second = blockIdx.y >= m.split;         // block-uniform
+    const AppendArgs &a = second ? m.t[1] : m.t[0];
+    const int u = static_cast<int>(blockIdx.y - (second ? m.split : 0));
+    const int64_t t0 = static_cast<int64_t>(blockIdx.x) * 16;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int nthreads = blockDim.x;
+    const int b = u / a.groups, g = u % a.groups;
+    const int nvalid = static_cast<int>(min<int64_t>(16, a.n - t0));
+    const int row_words = a.row_stride >> 2;
+    const bool active = wave < (a.kslots >> 4);        // this tensor's N-blocks
+    const int j = wave * 16 + (lane & 15), kq = lane >> 4;
+    const int64_t ub = static_cast<int64_t>(u) * a.kslots;
+
+    float4 vr[NKS / 4];
+    double lo = 0.0, inv = 0.0;
+    uint32_t sb = 0u;
+    if (active) {
+        const float4 *vp = reinterpret_cast<const float4 *>(a.basis + (ub + j) * DG + 4 * kq);
+#pragma unroll
+        for (int c = 0; c < NKS / 4; ++c) vr[c] = vp[4 * c];
+        lo = a.qlo[ub + j];
+        inv = a.qinv[ub + j];
+        sb = a.sbits[ub + j];
+    }
+    const XT *x = static_cast<const XT *>(a.x) + b * a.xsb + g * a.xsh + t0 * a.xss;
+    const float *mu = a.mu + static_cast<int64_t>(u) * DG;
+    for (int i = tid; i < nvalid * DG; i += nthreads) {
+        const int t = i / DG, d = i % DG;
+        xs[t * XP + d] = load_x(x + t * a.xss + d) - static_cast<double>(mu[d]);
+    }
+    for (int w = tid; w < 16 * row_words; w += nthreads) rows[w] = 0u;
+    __syncthreads();
+
+    if (active) {
+        doublex4 acc = doublex4{0.0, 0.0, 0.0, 0.0};
+        const double *xr = xs + (lane & 15) * XP + 4 * kq;
+#pragma unroll
+        for (int c = 0; c < NKS / 4; ++c) {
+            acc = __builtin_amdgcn_mfma_f64_16x16x4f64(xr[16 * c + 0], static_cast<double>(vr[c].x), acc, 0, 0, 0);
+            acc = __builtin_amdgcn_mfma_f64_16x16x4f64(xr[16 * c + 1], static_cast<double>(vr[c].y), acc, 0, 0, 0);
+            acc = __builtin_amdgcn_mfma_f64_16x16x4f64(xr[16 * c + 2], static_cast<double>(vr[c].z), acc, 0, 0, 0);
+            acc = __builtin_amdgcn_mfma_f64_16x16x4f64(xr[16 * c + 3], static_cast<double>(vr[c].w), acc, 0, 0, 0);
+        }
+        // result layout: acc[i] is token kq + 4i, slot j
+        if (j < a.ui[u].n_slots) {
+            const uint32_t off = sb & kOffsetMask, w = sb >> 24;
+            const double cmax = static_cast<double>((1u << w) - 1u);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int t = kq + 4 * i;
+                if (t < nvalid) or_field(rows + t * row_words, off, w, static_cast<uint32_t>(quantise(acc[i], lo, inv, cmax)));
+            }
+        }
+    }
+    __syncthreads();
+    if (row_words > 0) {
+        uint32_t *dst = reinterpret_cast<uint32_t *>(
+            a.codes + (static_cast<int64_t>(u) * a.capacity + a.s0 + t0) * a.row_stride);
+        for (int w = tid; w < nvalid * row_words; w += nthreads) dst[w] = rows[w];
+    }
+}
+
+
+template <bool MIXED, typename XT, int NB>
+int32_t launch_append_nb(const AppendArgs &a, int64_t ntiles, int64_t U, hipStream_t stream) {
+    const size_t lds = 2 * kAppTok * kAppPad * sizeof(double) + 2 * NB * 16 * kAppPad * sizeof(float) +
+                       static_cast<size_t>(kAppTok) * (a.row_stride / 4) * sizeof(uint32_t);
+    auto kern = a.x_vec ? append_kernel<MIXED, XT, NB, true> : append_kernel<MIXED, XT, NB, false>;
+    if (!allow_lds(reinterpret_cast<const void *>(kern))) return KVTC_E_DEVICE;
+    hipLaunchKernelGGL(kern, dim3(static_cast<unsigned>(ntiles), static_cast<unsigned>(U)), dim3(kThreads), lds,
+                       stream, a);
+    return hipGetLastError() == hipSuccess ? KVTC_OK : KVTC_E_DEVICE;
+}
+
+
+constexpr int kSmallRows = 16;
+constexpr size_t kSmallLdsLimit = 96 * 1024;
+
+size_t small_lds_bytes(int dg, int nb, int row_stride) {
+    return 16 * static_cast<size_t>(dg + 1) * sizeof(double) + static_cast<size_t>(nb) * 16 * (dg + 1) * sizeof(float) +
+           16 * static_cast<size_t>(row_stride / 4) * sizeof(uint32_t);
+}
+
+template <typename XT, int NB>
+int32_t launch_small_nb(const AppendArgs &a, int64_t U, hipStream_t stream) {
+    const size_t lds = small_lds_bytes(a.dg, NB, a.row_stride);
+    auto kern = append_small_kernel<XT, NB>;
+    if (!allow_lds(reinterpret_cast<const void *>(kern))) return KVTC_E_DEVICE;
+    const int64_t blocks = (a.n + kSmallRows - 1) / kSmallRows;
+    hipLaunchKernelGGL(kern, dim3(static_cast<unsigned>(blocks), static_cast<unsigned>(U)), dim3(kThreads), lds,
+                       stream, a);
+    return hipGetLastError() == hipSuccess ? KVTC_OK : KVTC_E_DEVICE;
+}
+
+template <typename XT>
+int32_t launch_small(const AppendArgs &a, int64_t U, int nb, hipStream_t st) {
+    switch (nb) {
+        case 1: return launch_small_nb<XT, 1>(a, U, st);
+        case 2: return launch_small_nb<XT, 2>(a, U, st);
+        case 4: return launch_small_nb<XT, 4>(a, U, st);
+        case 6: return launch_small_nb<XT, 6>(a, U, st);
+        case 8: return launch_small_nb<XT, 8>(a, U, st);
+        case 12: return launch_small_nb<XT, 12>(a, U, st);
+        case 16: return launch_small_nb<XT, 16>(a, U, st);
+        default: return KVTC_E_SHAPE;
+    }
+}
+
+template <bool MIXED, typename XT>
+int32_t launch_append(const AppendArgs &a, int64_t ntiles, int64_t U, int nb, hipStream_t st) {
+    if (!MIXED && a.n <= kSmallRows && small_lds_bytes(a.dg, nb, a.row_stride) <= kSmallLdsLimit)
+        return launch_small<XT>(a, U, nb, st);
+    switch (nb) {
+        case 1: return launch_append_nb<MIXED, XT, 1>(a, ntiles, U, st);
+        case 2: return launch_append_nb<MIXED, XT, 2>(a, ntiles, U, st);
+        case 4: return launch_append_nb<MIXED, XT, 4>(a, ntiles, U, st);
+        case 6: return launch_append_nb<MIXED, XT, 6>(a, ntiles, U, st);
+        case 8: return launch_append_nb<MIXED, XT, 8>(a, ntiles, U, st);
+        case 12: return launch_append_nb<MIXED, XT, 12>(a, ntiles, U, st);
+        case 16: return launch_append_nb<MIXED, XT, 16>(a, ntiles, U, st);
+        default: return KVTC_E_SHAPE;
+    }
+}
+
+template <typename XT, int DG>
+int32_t launch_decode_dg(const AppendPair &m, int64_t nrows, int64_t units, int nblk, hipStream_t stream) {
+    int row_stride = 0;
+    for (int i = 0; i < (m.split < units ? 2 : 1); ++i) row_stride = std::max(row_stride, m.t[i].row_stride);
+    const size_t lds = decode_lds_bytes(DG, row_stride);
+    auto kern = append_decode_kernel<XT, DG>;
+    const int64_t blocks = (nrows + kSmallRows - 1) / kSmallRows;
+    hipLaunchKernelGGL(kern, dim3(static_cast<unsigned>(blocks), static_cast<unsigned>(units)), dim3(64 * nblk), lds,
+                       stream, m);
+    return hipGetLastError() == hipSuccess ? KVTC_OK : KVTC_E_DEVICE;
+}
+
+// One decode launch for one plan (p1 == NULL) or for two plans of the same
+
+}  // namespace
+
+int append_nb(int kslots) {
+    const int need = kslots / 16;
+    const int opts[] = {1, 2, 4, 6, 8, 12, 16};
+    for (int o : opts)
+        if (o >= need) return o;
+    return -1;
+}
+
+// Decode appends of DP tensors (one head per unit) whose unit width has a
+// register-resident kernel; one wave per 16 slots, at most dg slots.
+bool decode_path(const AppendPlan &p) {
+    return !p.mixed && p.a.n <= kSmallRows && p.a.hpu == 1 && (p.a.dg == 64 || p.a.dg == 128) &&
+           p.a.kslots <= p.a.dg;
+}
+
+
+int32_t launch_decode(const AppendPlan &p0, const AppendPlan *p1, hipStream_t stream) {
+    AppendPair m{};
+    m.t[0] = p0.a;
+    m.split = p0.units;
+    int64_t units = p0.units;
+    int nblk = p0.a.kslots / 16;
+    if (p1) {
+        m.t[1] = p1->a;
+        units += p1->units;
+        nblk = std::max(nblk, p1->a.kslots / 16);
+    }
+    if (units > 65535) return KVTC_E_SHAPE;
+    const bool f16 = p0.dtype == KVTC_F16;
+    if (p0.a.dg == 128)
+        return f16 ? launch_decode_dg<_Float16, 128>(m, p0.a.n, units, nblk, stream)
+                   : launch_decode_dg<float, 128>(m, p0.a.n, units, nblk, stream);
+    return f16 ? launch_decode_dg<_Float16, 64>(m, p0.a.n, units, nblk, stream)
+               : launch_decode_dg<float, 64>(m, p0.a.n, units, nblk, stream);
+}
+
+int32_t launch_append_plan(const AppendPlan &p, hipStream_t stream) {
+    if (p.a.n == 0) return KVTC_OK;
+    if (decode_path(p)) return launch_decode(p, nullptr, stream);
+    if (p.dtype == KVTC_F16)
+        return p.mixed ? launch_append<true, _Float16>(p.a, p.ntiles, p.units, p.nb, stream)
+                       : launch_append<false, _Float16>(p.a, p.ntiles, p.units, p.nb, stream);
+    return p.mixed ? launch_append<true, float>(p.a, p.ntiles, p.units, p.nb, stream)
+                   : launch_append<false, float>(p.a, p.ntiles, p.units, p.nb, stream);
+}
+
+// share: how many tensors the launch is shared by (1 or 2); the block target
+
+}  // namespace kvtc

@@ -1,0 +1,289 @@
+// Shared declarations of the device half of libkvtc (gfx950): element types,
+// kernel argument blocks, the field decoder shared by the fetch and attention
+// kernels, and the launchers each translation unit provides.  Not part of the
+// public interface.
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cstdint>
+
+#include "kvtc.h"
+#include "kvtc_internal.h"
+
+namespace kvtc {
+
+typedef _Float16 half8 __attribute__((ext_vector_type(8)));
+typedef _Float16 half4 __attribute__((ext_vector_type(4)));
+typedef float floatx16 __attribute__((ext_vector_type(16)));
+typedef double doublex4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+constexpr int kThreads = 256;        // 4 waves of 64
+constexpr int kAppTok = 64;          // tokens per append block (16 per wave)
+constexpr int kAppKC = 16;           // feature columns staged per append step
+constexpr int kAppPad = kAppKC + 1;  // LDS row pitch (elements) of the staged chunks
+constexpr int kFetTok = 32;          // tokens per fetch tile (one wave)
+constexpr int kFetchRegWords = 24;   // per-lane register staging of one tile's rows+params
+constexpr int kMaxSlots = 256;
+constexpr int kMaxRowStride = 256;
+constexpr int kFetchBlocks = 512;    // target block count of a fetch (one block per unit at the batched-decode shape)
+
+// ------------------------------------------------------------ small helpers
+// Nearest-even binary16 of a double from its value: the binade is read from
+// the exponent bits, power-of-two scalings are exact and rint rounds half to even.
+__device__ inline uint16_t half_bits_rne(double x) {
+    const uint64_t bits = __double_as_longlong(x);
+    const uint16_t sign = static_cast<uint16_t>((bits >> 48) & 0x8000u);
+    const uint64_t mag = bits & 0x7FFFFFFFFFFFFFFFull;
+    if (mag > 0x7FF0000000000000ull) return sign | 0x7E00u;
+    const double a = __longlong_as_double(mag);
+    if (a >= 65520.0) return sign | 0x7C00u;
+    if (a < 6.103515625e-05) return sign | static_cast<uint16_t>(__builtin_rint(a * 16777216.0));
+    int ex = static_cast<int>(mag >> 52) - 1023;
+    double q = __builtin_rint(__builtin_amdgcn_ldexp(a, 10 - ex));
+    if (q == 2048.0) {
+        q = 1024.0;
+        ++ex;
+    }
+    if (ex + 15 >= 31) return sign | 0x7C00u;
+    return sign | static_cast<uint16_t>(((ex + 15) << 10) | (static_cast<int>(q) - 1024));
+}
+
+__device__ inline double half_bits_to_double(uint16_t h) {
+    return static_cast<double>(__builtin_bit_cast(_Float16, h));
+}
+
+// ORs a width-w code into an LSB-first bit row held as 32-bit words in LDS.
+__device__ inline void or_field(uint32_t *row, uint32_t off, uint32_t w, uint32_t c) {
+    const uint32_t wi = off >> 5, sh = off & 31u;
+    atomicOr(&row[wi], c << sh);
+    if (sh + w > 32u) atomicOr(&row[wi + 1], c >> (32u - sh));
+}
+
+__device__ inline double quantise(double l, double lo, double inv, double cmax) {
+    double q = __builtin_rint((l - lo) * inv);
+    if (q != q) q = 0.0;
+    return fmin(fmax(q, 0.0), cmax);
+}
+
+template <typename XT>
+__device__ inline double load_x(const XT *p) {
+    return static_cast<double>(*p);
+}
+
+
+// ================================================================ append
+struct AppendArgs {
+    const void *x;
+    int64_t xsb, xsh, xss;             // element strides of x (d stride is 1)
+    int64_t n, s0, capacity;
+    const kvtc_unit_info *ui;
+    const float *mu;                   // [U][dg]
+    const float *basis;                // [U][kslots][dg]
+    const double *qlo, *qinv;          // [U][kslots]
+    const uint32_t *sbits;             // [U][kslots]
+    uint8_t *codes;                    // [U][capacity][row_stride]
+    uint32_t *params;                  // [U][capacity][n_qg] packed (min16 | scale16 << 16)
+    int dg, D, hpu, groups, kslots, row_stride, n_qg, gs;
+    float inv_dg, inv_q4;              // 1/dg and 4/dg: exact quotients of small indices
+    int x_vec;                         // rows and strides aligned to 4 elements (raw vector loads)
+};
+
+// Four consecutive input elements as raw bits (one 8- or 16-byte load), and
+// element i of them as a double.
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+template <typename XT>
+struct RawX4;
+template <>
+struct RawX4<_Float16> {
+    typedef u32x2 v;
+    static __device__ inline double get(v r, int i) {
+        const uint32_t w = r[i >> 1];
+        return static_cast<double>(
+            __builtin_bit_cast(_Float16, static_cast<uint16_t>((i & 1) ? (w >> 16) : (w & 0xFFFFu))));
+    }
+};
+template <>
+struct RawX4<float> {
+    typedef u32x4 v;
+    static __device__ inline double get(v r, int i) {
+        const uint32_t w = r[i];   // the element as a scalar first: bit_cast of r[i] itself reads element 0
+        return static_cast<double>(__builtin_bit_cast(float, w));
+    }
+};
+
+// One block: 64 tokens of one unit, all of its stored components.
+
+
+// One decode launch covers one tensor or two (the K and V of a layer): units
+// below `split` (blockIdx.y) belong to t[0], the rest to t[1].
+struct AppendPair {
+    AppendArgs t[2];
+    int64_t split;
+};
+
+// ================================================================ fetch
+struct FetchArgs {
+    const uint8_t *codes;              // [U][capacity][row_stride]
+    const uint32_t *params;            // [U][capacity][n_qg] (min16 | scale16 << 16)
+    int64_t capacity, s_begin, s_end;
+    const uint16_t *w16;               // [U][dg][kfetch]
+    const float *bias;                 // [U][dg]
+    const uint32_t *kdesc;             // [U][kfetch/8]
+    _Float16 *out;
+    int64_t osb, osh, oss;             // element strides of out (d stride is 1)
+    int dg, D, hpu, groups, kfetch, row_stride, n_qg;
+    float nqg_inv;                     // 1 / n_qg (group-head mode)
+    int nslices, nchunks, tiles_per_block, ntiles;
+    int nks;                           // k-steps of this tensor (kfetch / 16)
+    int64_t nblocks;                   // blocks of this tensor
+    // dynamic LDS carve-up (bytes)
+    int lds_w, lds_desc, lds_bias, lds_wave, lds_rows, lds_par, lds_out, wpitch, opitch;
+};
+
+// One fetch launch covers one tensor or two (the K and V of a layer): the
+// first `split` logical blocks belong to t[0], the rest to t[1].
+struct FetchPair {
+    FetchArgs t[2];
+    int64_t split, nblocks_real, nblocks_per_xcd;
+};
+
+typedef _Float16 half2 __attribute__((ext_vector_type(2)));
+typedef float float2v __attribute__((ext_vector_type(2)));
+
+// 0x64 as the high byte of an fp16 makes the low byte an integer offset from
+// 1024: the half 0x64XX is exactly 1024 + XX.
+constexpr uint32_t kMagic = 0x64646464u;
+
+// Eight W-bit fields (W <= 3, all inside the low word) as four half2 pairs of
+// 1024 + code, in field order.
+template <int W>
+__device__ inline void small_fields(uint32_t lo, uint32_t (&pr)[4]) {
+    constexpr uint32_t kMask = (1u << W) - 1u;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+        const uint32_t c0 = (lo >> (2 * e * W)) & kMask, c1 = (lo >> ((2 * e + 1) * W)) & kMask;
+        pr[e] = (c0 | (c1 << 16)) | 0x64006400u;
+    }
+}
+
+// One lane's eight B-operand values of one k-step (16 fetch slots of a single
+// width w > 0): the fields starting at the k-step's first field plus 8w for
+// the upper operand half (for w = 2: the k-step's whole 32-bit window, shifted
+// by 4 bits for the upper half), read from the lane's token row as a 64-bit
+// window and turned into exact fp16 integers.  In group-head mode each code is
+// dequantised with the row's fp16 (min, scale) of the k-step's quantisation
+// group in one fp16 fma; mypar points at the lane's token in the group-major
+// parameter staging.
+template <bool MIXED>
+__device__ __forceinline__ half8 decode_kstep(uint32_t kd, const uint32_t *myrow, const uint32_t *mypar,
+                                              uint32_t half_k) {
+    const uint32_t w = (kd >> 16) & 0xFu;
+    const uint32_t off = (kd & 0xFFFFu) + (w == 2u ? 0u : (half_k << 3) * w);
+    const uint32_t wi = off >> 5, sh = off & 31u;
+    const uint32_t r0 = myrow[wi], r1 = myrow[wi + 1];
+    const uint32_t lo = __builtin_amdgcn_alignbit(r1, r0, sh);
+    uint32_t pr[4];                                        // 4 packed half2 of 1024 + code
+    if (w == 8u) {
+        const uint32_t hi = __builtin_amdgcn_alignbit(myrow[wi + 2], r1, sh);
+        pr[0] = __builtin_amdgcn_perm(kMagic, lo, 0x04010400u);
+        pr[1] = __builtin_amdgcn_perm(kMagic, lo, 0x04030402u);
+        pr[2] = __builtin_amdgcn_perm(kMagic, hi, 0x04010400u);
+        pr[3] = __builtin_amdgcn_perm(kMagic, hi, 0x04030402u);
+    } else if (w == 4u) {
+        // nibbles of a 4-bit k-step are stored in the order 0,2,4,6,1,3,5,7
+        const uint32_t ev = lo & 0x0F0F0F0Fu, od = (lo >> 4) & 0x0F0F0F0Fu;
+        pr[0] = __builtin_amdgcn_perm(kMagic, ev, 0x04010400u);
+        pr[1] = __builtin_amdgcn_perm(kMagic, ev, 0x04030402u);
+        pr[2] = __builtin_amdgcn_perm(kMagic, od, 0x04010400u);
+        pr[3] = __builtin_amdgcn_perm(kMagic, od, 0x04030402u);
+    } else if (w == 2u) {
+        // slots 0,4,8,12 then 1,5,9,13 (2,6,10,14 then 3,7,11,15 in the upper half)
+        const uint32_t t = lo >> (half_k << 2);
+        const uint32_t ev = t & 0x03030303u, od = (t >> 2) & 0x03030303u;
+        pr[0] = __builtin_amdgcn_perm(kMagic, ev, 0x04010400u);
+        pr[1] = __builtin_amdgcn_perm(kMagic, ev, 0x04030402u);
+        pr[2] = __builtin_amdgcn_perm(kMagic, od, 0x04010400u);
+        pr[3] = __builtin_amdgcn_perm(kMagic, od, 0x04030402u);
+    } else if (w == 1u) {
+        small_fields<1>(lo, pr);
+    } else {
+        small_fields<3>(lo, pr);
+    }
+    half8 bv;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+        // (1024 + c) - 1024 = c exactly
+        const half2 cv = __builtin_bit_cast(half2, pr[e]) -
+                         half2{static_cast<_Float16>(1024.0f), static_cast<_Float16>(1024.0f)};
+        if constexpr (MIXED) {
+            const uint32_t p = mypar[(kd >> 20) * kFetTok];
+            const half2 mn2 = __builtin_bit_cast(half2, (p & 0xFFFFu) | (p << 16));
+            const half2 sc2 = __builtin_bit_cast(half2, (p >> 16) | (p & 0xFFFF0000u));
+            const half2 r = __builtin_elementwise_fma(cv, sc2, mn2);
+            bv[2 * e] = r[0];
+            bv[2 * e + 1] = r[1];
+        } else {
+            bv[2 * e] = cv[0];
+            bv[2 * e + 1] = cv[1];
+        }
+    }
+    return bv;
+}
+
+// Accumulators seeded with the bias: C[d][token] starts at bias[d] for the
+
+constexpr int kLdsMax = 160 * 1024;
+
+// Lets a kernel use up to the whole LDS of a CU as dynamic shared memory (set
+// once per kernel and device).
+bool allow_lds(const void *kern);
+
+// ============================================================== call plans
+// Everything a call needs to launch, after its arguments have been validated.
+struct AppendPlan {
+    AppendArgs a;
+    int64_t units, ntiles;
+    int nb;                            // 16-slot N-blocks of the bulk kernels
+    int32_t dtype;
+    bool mixed;
+};
+
+struct FetchPlan {
+    FetchArgs a;
+    int ds, rw;                        // columns per block (128 or 64), row words per lane
+    bool mixed;
+};
+
+// ------------------------------------------------------------ launchers
+// append (kvtc_append.hip)
+int32_t launch_append_plan(const AppendPlan &p, hipStream_t stream);
+bool decode_path(const AppendPlan &p);
+int32_t launch_decode(const AppendPlan &p0, const AppendPlan *p1, hipStream_t stream);
+int append_nb(int kslots);
+
+// fetch: one launcher per contraction length in 16-slot k-steps, each compiled
+// in a translation unit of its own (kvtc_fetch_ks.hip)
+#define KVTC_DECLARE_FETCH_KS(N) \
+    int32_t launch_fetch_ks##N(bool mixed, int ndb, const FetchPair &m, int nt, int rw, hipStream_t stream);
+KVTC_DECLARE_FETCH_KS(1)
+KVTC_DECLARE_FETCH_KS(2)
+KVTC_DECLARE_FETCH_KS(3)
+KVTC_DECLARE_FETCH_KS(4)
+KVTC_DECLARE_FETCH_KS(5)
+KVTC_DECLARE_FETCH_KS(6)
+KVTC_DECLARE_FETCH_KS(7)
+KVTC_DECLARE_FETCH_KS(8)
+KVTC_DECLARE_FETCH_KS(9)
+KVTC_DECLARE_FETCH_KS(10)
+KVTC_DECLARE_FETCH_KS(11)
+KVTC_DECLARE_FETCH_KS(12)
+KVTC_DECLARE_FETCH_KS(13)
+KVTC_DECLARE_FETCH_KS(14)
+KVTC_DECLARE_FETCH_KS(15)
+KVTC_DECLARE_FETCH_KS(16)
+#undef KVTC_DECLARE_FETCH_KS
+
+}  // namespace kvtc

@@ -738,8 +738,17 @@ uint64_t huffman_bits(const uint64_t *counts, int n) {
 
 using namespace kvtc;
 
+#ifndef KVTC_BUILD_ID
+#define KVTC_BUILD_ID "0000000000000000"
+#endif
+// The hash of the sources the library was built from, behind a fixed marker so
+// that a build script can read it from the file without loading the library.
+static const char kBuildIdTag[] = "kvtc-build-id:" KVTC_BUILD_ID;
+
 // =========================================================== C entry points
 extern "C" {
+
+const char *kvtc_build_id(void) { return kBuildIdTag + 14; }
 
 void kvtc_config_default(kvtc_config *cfg, int32_t mode, int32_t head_dim) {
     if (!cfg) return;

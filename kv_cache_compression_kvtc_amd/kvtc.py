@@ -83,6 +83,7 @@ _P64 = C.POINTER(C.c_int64)
 _sig = {
     "kvtc_config_default": (None, [C.POINTER(Config), _i32, _i32]),
     "kvtc_status_string": (C.c_char_p, [_i32]),
+    "kvtc_build_id": (C.c_char_p, []),
     "kvtc_fit_host": (_i32, [C.POINTER(Config), _vp, _i32, _i64, _i64, _i64, _vp, C.POINTER(_sz)]),
     "kvtc_state_build": (_i32, [C.POINTER(Config), _i64, _i64, _i32, _vp, _vp, _vp, _vp, _vp, _vp,
                                 _vp, _i64, _vp, C.POINTER(_sz)]),
@@ -103,6 +104,11 @@ for _name, (_res, _args) in _sig.items():
     _f.argtypes = _args
 
 EXPORTED = tuple(_sig)
+
+
+def build_id() -> str:
+    """Hash of the sources the loaded library was built from."""
+    return _lib.kvtc_build_id().decode()
 
 
 def status_string(status: int) -> str:

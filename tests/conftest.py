@@ -20,8 +20,8 @@ def rng():
 
 
 def pytest_sessionstart(session):
-    # tests load the built library; build it only when nothing is built yet
-    lib = os.path.join(ROOT, "kv_cache_compression_kvtc_amd", "libkvtc.so")
-    if not os.path.exists(lib):
-        from kv_cache_compression_kvtc_amd.build import build
-        build()
+    # tests load the built library: rebuild it unless it was built from the
+    # current sources (its embedded build id equals the hash of the tree), so a
+    # stale library can never run the tests
+    from kv_cache_compression_kvtc_amd.build import ensure_current
+    ensure_current(log=lambda m: print(m, file=sys.stderr, flush=True))

@@ -45,6 +45,11 @@ def blob_from_oracle(st: O.TensorState) -> np.ndarray:
 
 
 # ---------------------------------------------------------------- exports
+def test_loaded_library_was_built_from_the_current_sources():
+    from kv_cache_compression_kvtc_amd.build import source_hash, library_build_id
+    assert K.build_id() == source_hash() == library_build_id()
+
+
 def test_library_exports_every_declared_symbol():
     text = open(HEADER).read()
     declared = set(re.findall(r"^\s*(?:[\w\s\*]+?)\b(kvtc_\w+)\s*\(", text, flags=re.M))
