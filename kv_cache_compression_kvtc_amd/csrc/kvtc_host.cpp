@@ -132,7 +132,11 @@ bool dp_allocate(const double *lam, int r, int budget, const std::vector<int> &c
     std::sort(choices.begin(), choices.end());
     choices.erase(std::unique(choices.begin(), choices.end()), choices.end());
     const double inf = std::numeric_limits<double>::infinity();
-    const int C = budget + 1;
+    // no allocation spends more than r * (widest choice) bits: columns past that
+    // stay infinite, so clamping the table there changes neither the optimum
+    // nor its tie-breaking, and bounds the work for any budget
+    const int widest = choices.empty() ? 0 : choices.back();
+    const int C = static_cast<int>(std::min<int64_t>(budget, static_cast<int64_t>(r) * widest)) + 1;
     std::vector<double> best(C, inf), nxt(C);
     std::vector<int8_t> pick(static_cast<size_t>(r) * C, -1);
     best[0] = 0.0;
@@ -140,7 +144,7 @@ bool dp_allocate(const double *lam, int r, int budget, const std::vector<int> &c
         std::fill(nxt.begin(), nxt.end(), inf);
         int8_t *arg = &pick[static_cast<size_t>(i) * C];
         for (int b : choices) {
-            if (b > budget) continue;
+            if (b >= C) continue;
             // distortion proxy: dropped -> lambda, b bits -> beta * lambda * 4^-b
             const double d = (b == 0) ? lam[i] : beta * lam[i] * std::ldexp(1.0, -2 * b);
             for (int c = b; c < C; ++c) {

@@ -35,8 +35,11 @@ inline T *section_mut(void *blob, uint64_t off) {
     return reinterpret_cast<T *>(static_cast<char *>(blob) + off);
 }
 
-// Validates the header of a host copy of a state blob.  Returns KVTC_OK or
-// KVTC_E_STATE; on success *out points at the header.
+// Validates the header of a host copy of a state blob: magic, version, mode,
+// shape fields, every section's extent inside total_bytes, and the per-unit
+// counts.  The blob must hold at least total_bytes readable bytes (the caller
+// passes no length; the Python binding checks it).  Returns KVTC_OK, KVTC_E_ARG
+// for a NULL blob or KVTC_E_STATE; on success *out points at the header.
 inline int32_t check_state(const void *blob, const kvtc_state_header **out) {
     if (blob == nullptr) return KVTC_E_ARG;
     const auto *h = static_cast<const kvtc_state_header *>(blob);
@@ -52,11 +55,41 @@ inline int32_t check_state(const void *blob, const kvtc_state_header **out) {
         h->kfetch % kSlotAlign != 0)
         return KVTC_E_STATE;
     if (h->mode == KVTC_MODE_MIXED && (h->n_qgroups <= 0 || h->group_size <= 0)) return KVTC_E_STATE;
-    const uint64_t offs[] = {h->off_unit, h->off_lambda, h->off_bits, h->off_qmin, h->off_qscale,
-                             h->off_mu, h->off_slot_comp, h->off_slot_bits, h->off_basis,
-                             h->off_qlo, h->off_qinv, h->off_w16, h->off_bias, h->off_kdesc, h->off_fslot};
-    for (uint64_t o : offs)
-        if (o < sizeof(kvtc_state_header) || o % kSectionAlign != 0 || o >= h->total_bytes)
+    if (h->dg > 65536 || h->kslots > 65536 || h->kfetch > 65536 || h->row_stride > 65536 ||
+        h->units > (int64_t(1) << 31))
+        return KVTC_E_STATE;
+    // every section lies inside the blob: its start and its end, the size
+    // recomputed from the header fields (no product below can overflow 64 bits
+    // with the caps above)
+    const uint64_t U = static_cast<uint64_t>(h->units), dg = h->dg, rmax = h->rmax, ks = h->kslots,
+                   kf = h->kfetch;
+    const struct {
+        uint64_t off, bytes;
+    } secs[] = {{h->off_unit, U * sizeof(kvtc_unit_info)},
+                {h->off_lambda, U * dg * 8},
+                {h->off_bits, U * rmax},
+                {h->off_qmin, U * rmax * 4},
+                {h->off_qscale, U * rmax * 4},
+                {h->off_mu, U * dg * 4},
+                {h->off_slot_comp, U * ks * 4},
+                {h->off_slot_bits, U * ks * 4},
+                {h->off_basis, U * ks * dg * 4},
+                {h->off_qlo, U * ks * 8},
+                {h->off_qinv, U * ks * 8},
+                {h->off_w16, U * kf * dg * 2},
+                {h->off_bias, U * dg * 4},
+                {h->off_kdesc, U * (kf / kSlotAlign) * 4},
+                {h->off_fslot, U * kf * 4}};
+    for (const auto &s : secs)
+        if (s.off < sizeof(kvtc_state_header) || s.off % kSectionAlign != 0 || s.off >= h->total_bytes ||
+            s.bytes > h->total_bytes - s.off)
+            return KVTC_E_STATE;
+    // per-unit counts within the header's capacities (the kernels index the
+    // slot arrays with them)
+    const auto *ui = reinterpret_cast<const kvtc_unit_info *>(static_cast<const char *>(blob) + h->off_unit);
+    for (uint64_t u = 0; u < U; ++u)
+        if (ui[u].rank < 1 || ui[u].rank > h->rmax || ui[u].n_slots < 0 || ui[u].n_slots > h->kslots ||
+            ui[u].n_slots > ui[u].rank || ui[u].row_bits < 0 || ui[u].row_bits > 8 * h->row_stride)
             return KVTC_E_STATE;
     if (out) *out = h;
     return KVTC_OK;

@@ -219,12 +219,16 @@ def kvtc_allocate_bits(lam, budget: int, choices, beta: float = 1.0) -> np.ndarr
 
 
 def kvtc_store_bytes(blob: np.ndarray, capacity: int):
+    _check_blob(blob, "kvtc_store_bytes")
     cb, pb = C.c_size_t(0), C.c_size_t(0)
     _check(_lib.kvtc_store_bytes(_host_ptr(blob), capacity, C.byref(cb), C.byref(pb)), "kvtc_store_bytes")
     return cb.value, pb.value
 
 
 def kvtc_bytes(blob: np.ndarray, codes: np.ndarray, params, capacity: int, S: int) -> dict:
+    h = _check_blob(blob, "kvtc_bytes")
+    if np.asarray(codes).nbytes < h.units * capacity * h.row_stride:
+        raise KVTCError(E_ARG, "kvtc_bytes: code store smaller than units*capacity*row_stride")
     rep = BytesReport()
     _check(_lib.kvtc_bytes(_host_ptr(blob), _host_ptr(np.ascontiguousarray(codes)), _host_ptr(params),
                            capacity, S, C.byref(rep)), "kvtc_bytes")
@@ -232,9 +236,22 @@ def kvtc_bytes(blob: np.ndarray, codes: np.ndarray, params, capacity: int, S: in
 
 
 # ---------------------------------------------------------------- device calls
-def _check_buffers(blob, blob_dev, codes, params, capacity, what):
+def _check_blob(blob, what):
+    """The C ABI takes no blob length: a host blob must hold the header and the
+    total_bytes it declares before its pointer is passed."""
+    if not isinstance(blob, np.ndarray) or blob.dtype != np.uint8 or not blob.flags.c_contiguous:
+        raise KVTCError(E_ARG, what + ": state blob must be a contiguous uint8 array")
+    if blob.nbytes < C.sizeof(StateHeader):
+        raise KVTCError(E_STATE, what + ": state blob shorter than its header")
     h = header(blob)
-    if blob_dev is None or blob_dev.numel() * blob_dev.element_size() < blob.nbytes or not blob_dev.is_cuda:
+    if h.magic != MAGIC or blob.nbytes < h.total_bytes:
+        raise KVTCError(E_STATE, what + ": state blob shorter than its total_bytes or not a state")
+    return h
+
+
+def _check_buffers(blob, blob_dev, codes, params, capacity, what):
+    h = _check_blob(blob, what)
+    if blob_dev is None or not blob_dev.is_cuda or blob_dev.numel() * blob_dev.element_size() < h.total_bytes:
         raise KVTCError(E_ARG, what + ": device state copy")
     cb, pb = kvtc_store_bytes(blob, capacity)
     if cb and (codes is None or not codes.is_cuda or codes.numel() * codes.element_size() < cb):
@@ -323,6 +340,8 @@ def kvtc_fetch_kv(k, v, capacity: int, s_begin: int, s_end: int, stream=None):
 
 
 def kvtc_attend_workspace(blob_k: np.ndarray, blob_v: np.ndarray, s_end: int) -> int:
+    _check_blob(blob_k, "kvtc_attend_workspace")
+    _check_blob(blob_v, "kvtc_attend_workspace")
     n = C.c_size_t(0)
     _check(_lib.kvtc_attend_workspace(_host_ptr(blob_k), _host_ptr(blob_v), s_end, C.byref(n)),
            "kvtc_attend_workspace")
