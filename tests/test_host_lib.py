@@ -488,3 +488,57 @@ def test_huge_budget_allocates_quickly_and_like_the_widest_budget(rng):
         assert np.array_equal(K.kvtc_allocate_bits(lam, budget, ch), ref)
     assert time.perf_counter() - t < 2.0
     assert (ref == 8).all()
+
+
+def test_bytes_report_hand_worked_values():
+    """kvtc_bytes against values derived by hand from the KVTC page's "Byte
+    accounting" (payload, order-0 Huffman with fixed-width fallback, fp16 basis,
+    mean and (min, scale)) and the PALU page's (fp32 projection and mean, params
+    per token and quantisation group).  The oracle's byte pins use the same cases
+    at D = 4; here D = 64, the smallest head size the library accepts:
+      widths (2, 0, 1), S = 8: payload 3 (Huffman 10 + 8 bits = 3 bytes + table 6
+        is not below 3); basis 2 * (64 * 2 + 64) = 384; params 8; total 395;
+      width 8 (+ a dropped one), S = 1000, 990 zeros and 10 x 255: Huffman 1000
+        bits = 125 bytes + table 256 < 1000 -> coded; basis 2 * (64 + 64) = 256;
+        params 4; total 125 + 256 + 256 + 4 = 641; pre-entropy 1000 + 260 = 1260;
+      width 2, every code 2: S = 32 -> 4 + 4 = 8 is not below 8: 8 + 256 + 4 = 268;
+        S = 40 -> 5 + 4 < 10: 5 + 4 + 256 + 4 = 269;
+      group head, 2 heads (Dg = 128), rank 32, 16 components at 4 bits and 16 at
+        2 (96 bits), groups of 16, S = 5: payload ceil(5 * 96 / 8) = 60;
+        projection 4 * (128 * 32 + 128) = 16896; params 4 * 5 * 2 = 40; total 16996."""
+    def run(mode, hpu, H, bits, codes, group_size=32, hi_fraction=0.25):
+        bits = np.asarray(bits)
+        D = 64
+        U, r, Dg = H // hpu, len(bits), D * hpu
+        cfg = K.make_config(mode, D, hpu, r, budget=int(bits.sum()), choices=(0, 1, 2, 4, 8),
+                            group_size=group_size, hi_fraction=hi_fraction)
+        basis = np.zeros((U, r, Dg), np.float32)
+        basis[:, np.arange(r), np.arange(r)] = 1.0
+        blob = K.kvtc_state_build(cfg, 1, H, np.full(U, r), np.zeros((U, Dg)), basis, None,
+                                  np.tile(bits, (U, 1)), np.zeros((U, r)), np.ones((U, r)))
+        h = K.header(blob)
+        S = codes.shape[0]
+        rows = O.pack_rows(codes, bits, h.row_stride)
+        store = np.ascontiguousarray(np.tile(rows[None], (U, 1, 1)))
+        rep = K.kvtc_bytes(blob, store, None, S, S)
+        rep.pop("device_store")
+        return rep
+
+    codes = np.zeros((8, 3), np.int64)
+    codes[:, 0] = [0, 0, 0, 0, 0, 0, 1, 3]
+    codes[:, 2] = 1
+    assert run("dp", 1, 1, [2, 0, 1], codes) == dict(
+        fixed_payload=3, entropy_payload=0, entropy_table=0, stored_payload=3, basis=384, quant_params=8,
+        total=395, pre_entropy=395, fp16_equiv=1024, n_survived=2, units_entropy_coded=0)
+    codes = np.zeros((1000, 2), np.int64)
+    codes[:10, 0] = 255
+    assert run("dp", 1, 1, [8, 0], codes) == dict(
+        fixed_payload=1000, entropy_payload=125, entropy_table=256, stored_payload=125, basis=256,
+        quant_params=4, total=641, pre_entropy=1260, fp16_equiv=128000, n_survived=1, units_entropy_coded=1)
+    for S, coded, total in ((32, 0, 268), (40, 1, 269)):
+        rep = run("dp", 1, 1, [2], np.full((S, 1), 2, np.int64))
+        assert (rep["units_entropy_coded"], rep["total"]) == (coded, total)
+    assert run("mixed", 2, 2, [4] * 16 + [2] * 16, np.ones((5, 32), np.int64), group_size=16,
+               hi_fraction=0.5) == dict(
+        fixed_payload=60, entropy_payload=0, entropy_table=0, stored_payload=60, basis=16896, quant_params=40,
+        total=16996, pre_entropy=16996, fp16_equiv=1280, n_survived=32, units_entropy_coded=0)

@@ -389,6 +389,108 @@ def test_byte_formulas_and_entropy_fallback():
     assert rep.n_survived == int((st.bits > 0).sum())
 
 
+def _hand_state(mode, D, hpu, H, bits, group_size=32):
+    """A one-batch TensorState with the given widths (identical per unit); only
+    the fields byte accounting reads matter (basis and ranges are placeholders)."""
+    bits = np.asarray(bits, np.int64)
+    U, r, Dg = H // hpu, len(bits), D * hpu
+    cfg = O.Config(mode=mode, head_dim=D, heads_per_unit=hpu, rank=r, group_size=group_size)
+    stride = O.row_stride_bytes(int(bits.sum()))
+    return O.TensorState(cfg, 1, H, D, hpu, np.full(U, r), np.zeros((U, Dg), np.float32),
+                         np.zeros((U, Dg)), np.zeros((U, Dg, r), np.float32), np.tile(bits, (U, 1)),
+                         np.zeros((U, r), np.float32), np.ones((U, r), np.float32), stride)
+
+
+def _report_fields(rep):
+    return {k: getattr(rep, k) for k in ("fixed_payload", "entropy_payload", "entropy_table", "stored_payload",
+                                         "basis", "quant_params", "total", "pre_entropy", "fp16_equiv",
+                                         "n_survived", "units_entropy_coded")}
+
+
+def test_bytes_report_hand_worked_dp_fixed_width_fallback():
+    """KVTC page, "Byte accounting" and kvtc_fp16_bytes, worked by hand.
+    D = 4, one (b, h) unit, widths (2, 0, 1), S = 8 rows:
+      fixed payload: ceil(8 * 3 / 8) = 3 bytes;
+      Huffman: component 0 codes 0 x6, 1, 3 -> merges 1+1 = 2, 2+6 = 8 -> 10 bits;
+               component 2 all 1 (one symbol, a bit each) -> 8 bits; 18 bits -> 3 bytes;
+      table: 2**2 + 2**1 = 6 bytes; 3 + 6 = 9 is not below 3 -> fixed width is kept;
+      basis: fp16 of the 2 kept basis columns and the mean: 2 * (4 * 2 + 4) = 24;
+      quantiser params: fp16 (min, scale) per kept component: 2 * 2 * 2 = 8;
+      total = pre-entropy = 3 + 24 + 8 = 35; fp16 equivalent 8 * 4 * 2 = 64."""
+    st = _hand_state("dp", 4, 1, 1, [2, 0, 1])
+    codes = np.zeros((8, 3), np.int64)
+    codes[:, 0] = [0, 0, 0, 0, 0, 0, 1, 3]
+    codes[:, 2] = 1
+    rows = O.pack_rows(codes, st.bits[0], st.row_stride)[None]
+    assert _report_fields(O.bytes_report(st, rows, None, 8)) == dict(
+        fixed_payload=3, entropy_payload=0, entropy_table=0, stored_payload=3, basis=24, quant_params=8,
+        total=35, pre_entropy=35, fp16_equiv=64, n_survived=2, units_entropy_coded=0)
+
+
+def test_bytes_report_hand_worked_dp_entropy_coded():
+    """One 8-bit component over S = 1000 rows, 990 codes 0 and 10 codes 255:
+      fixed: 1000 bytes; Huffman: two symbols, one bit each -> 1000 bits = 125 bytes;
+      table 256 bytes; 125 + 256 = 381 < 1000 -> entropy coded;
+      basis 2 * (4 * 1 + 4) = 16; params 2 * 2 * 1 = 4;
+      total 125 + 256 + 16 + 4 = 401; pre-entropy 1000 + 16 + 4 = 1020."""
+    st = _hand_state("dp", 4, 1, 1, [8, 0])
+    codes = np.zeros((1000, 2), np.int64)
+    codes[:10, 0] = 255
+    rows = O.pack_rows(codes, st.bits[0], st.row_stride)[None]
+    assert _report_fields(O.bytes_report(st, rows, None, 1000)) == dict(
+        fixed_payload=1000, entropy_payload=125, entropy_table=256, stored_payload=125, basis=16, quant_params=4,
+        total=401, pre_entropy=1020, fp16_equiv=8000, n_survived=1, units_entropy_coded=1)
+
+
+def test_bytes_report_entropy_coding_needs_a_strict_saving():
+    """Payload + table equal to the fixed width keeps fixed width (it must be
+    strictly smaller): one 2-bit component, every code 2.
+      S = 32: fixed 8; Huffman 32 bits = 4 bytes; table 4; 4 + 4 = 8 -> fixed: 8 + 16 + 4 = 28;
+      S = 40: fixed 10; 40 bits = 5 bytes; 5 + 4 = 9 < 10 -> coded: 5 + 4 + 16 + 4 = 29."""
+    st = _hand_state("dp", 4, 1, 1, [2])
+    for S, coded, total in ((32, 0, 28), (40, 1, 29)):
+        rows = O.pack_rows(np.full((S, 1), 2, np.int64), st.bits[0], st.row_stride)[None]
+        rep = O.bytes_report(st, rows, None, S)
+        assert (rep.units_entropy_coded, rep.total, rep.basis, rep.quant_params) == (coded, total, 16, 4)
+
+
+def test_bytes_report_hand_worked_group_head():
+    """PALU page, "Byte accounting": latents at their stored width plus the fp32
+    projection and mean of the group; (min, scale) fp16 pairs per token and
+    quantisation group.  Two heads of D = 4 in one group (Dg = 8), rank 4,
+    widths (4, 4, 2, 2), quantisation groups of 2, S = 5:
+      fixed: ceil(5 * 12 / 8) = 8; projection: 4 * (8 * 4 + 8) = 160;
+      params: 4 bytes * 5 tokens * 2 groups = 40; total = pre-entropy = 208;
+      fp16 equivalent 1 * 2 * 5 * 4 * 2 = 80."""
+    st = _hand_state("mixed", 4, 2, 2, [4, 4, 2, 2], group_size=2)
+    rows = O.pack_rows(np.ones((5, 4), np.int64), st.bits[0], st.row_stride)[None]
+    assert _report_fields(O.bytes_report(st, rows, None, 5)) == dict(
+        fixed_payload=8, entropy_payload=0, entropy_table=0, stored_payload=8, basis=160, quant_params=40,
+        total=208, pre_entropy=208, fp16_equiv=80, n_survived=4, units_entropy_coded=0)
+
+
+def test_group_head_rank_is_uniform_and_the_least_meeting_every_group():
+    """PALU page: the stored latent rank is uniform across head groups; with
+    palu_rank=None it comes from the energy threshold.  The uniform rank is the
+    least one at which every group holds at least tau of its energy: here group
+    0 needs 2 components and group 1 needs 5, so both store 5."""
+    rng = np.random.default_rng(5)
+    D, hpu, S = 4, 2, 4000
+    scales = [np.array([10, 10, .01, .01, .01, .01, .01, .01]), np.array([1, 1, 1, 1, 1, .01, .01, .01])]
+    X = np.zeros((1, 4, S, D))
+    for g, sc in enumerate(scales):
+        Q, _ = np.linalg.qr(rng.normal(size=(8, 8)))
+        rows = (rng.normal(size=(S, 8)) * sc) @ Q.T
+        for j in range(hpu):
+            X[0, g * hpu + j] = rows[:, j * D:(j + 1) * D]
+    st = O.fit(O.Config(mode="mixed", head_dim=D, heads_per_unit=hpu, rank=0, energy=0.9, group_size=16), X)
+    r = int(st.r[0])
+    assert list(st.r) == [5, 5]
+    frac = np.cumsum(st.lam, axis=1) / st.lam.sum(axis=1, keepdims=True)    # energy held by the first k
+    assert (frac[:, r - 1] >= 0.9).all() and (frac[:, r - 2] < 0.9).any()
+    assert frac[0, 1] >= 0.9                                                   # group 0 alone would take 2
+
+
 def test_palu_effective_bits_formula():
     # PALU page: effective width ~ (r / D) * weighted average of hi and lo widths
     bits = O.allocate_mixed(256, 4, 2, 0.25, 32)
