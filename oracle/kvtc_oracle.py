@@ -25,7 +25,9 @@ Readings taken where the pages are silent (each is also listed with its
 reason in the design notes of the repository):
 
 * min/scale of each DP component are frozen at prefill; later latents outside
-  the prefill range clamp to the end codes;
+  the prefill range clamp to the end codes (``clamp_fraction`` measures how
+  often); ``refit`` / ``append_refit`` give the page's own alternative, the
+  ranges refitted over every accumulated row on each call;
 * the DP's "analytic distortion proxy" is ``D_i(0) = lam_i`` (dropped) and
   ``D_i(b) = beta * lam_i * 4**-b`` (Gaussian distortion-rate), ties broken
   towards fewer bits;
@@ -502,6 +504,56 @@ def append(st: TensorState, x: np.ndarray):
             params[u, :, : p.shape[1]] = p
         rows[u] = pack_rows(codes, bits, st.row_stride)
     return rows, params
+
+
+def refit(st: TensorState, X_all: np.ndarray) -> TensorState:
+    """Refit mode: the KVTC page's own decode semantics (``_TensorKVTC.append``
+    concatenates the new rows to every row accumulated so far and
+    ``_requantize`` re-projects them all through the frozen basis and mean,
+    then quantises each kept component with a min/max fitted over all of
+    them).  Basis, mean and widths stay frozen; only the per-component
+    (min, scale) are recomputed over the accumulated rows ``X_all [B, H, S, D]``,
+    in the same form as the prefill ranges (float32 min and scale of the
+    float64 latents).  DP mode only: group-head rows carry their own per-token
+    ranges.  Returns a new state; ``st`` is unchanged."""
+    assert st.cfg.mode == "dp"
+    xu = gather_units(np.asarray(X_all), st.hpu)
+    qmin = np.zeros_like(st.qmin32)
+    qscale = np.zeros_like(st.qscale32)
+    for u in range(st.U):
+        r = int(st.r[u])
+        qmin[u, :r], qscale[u, :r] = frozen_ranges(xu[u], st.mu32[u], st.V32[u, :, :r], st.bits[u, :r])
+    return TensorState(st.cfg, st.B, st.H, st.D, st.hpu, st.r, st.mu32, st.lam, st.V32, st.bits, qmin, qscale,
+                       st.row_stride)
+
+
+def append_refit(st: TensorState, X_all: np.ndarray):
+    """Refit-mode store of the accumulated rows ``X_all [B, H, S, D]``: the
+    refitted state and every row's packed codes under it ``[U, S, stride]``
+    (earlier rows' codes change whenever a range grows)."""
+    st2 = refit(st, X_all)
+    rows, _ = append(st2, X_all)
+    return st2, rows
+
+
+def clamp_fraction(st: TensorState, x: np.ndarray) -> float:
+    """Frozen mode: the fraction of kept latents of rows ``x [B, H, n, D]`` whose
+    code is decided by the clamp, i.e. whose unclamped rounded code
+    ``rint((l - min) / scale)`` lies outside [0, 2**b - 1] (a latent beyond the
+    prefill range; the cost of freezing the ranges)."""
+    xu = gather_units(np.asarray(x), st.hpu)
+    out = total = 0
+    for u in range(st.U):
+        r = int(st.r[u])
+        L = project(xu[u], st.mu32[u], st.V32[u, :, :r])
+        for i in np.flatnonzero(st.bits[u, :r]):
+            sc = float(st.qscale32[u, i])
+            if sc == 0.0:
+                continue
+            q = np.rint((L[:, i] - float(st.qmin32[u, i])) / sc)
+            out += int(((q < 0) | (q > 2 ** int(st.bits[u, i]) - 1)).sum())
+            total += L.shape[0]
+    return out / max(total, 1)
 
 
 def fetch(st: TensorState, rows: np.ndarray, params=None) -> np.ndarray:

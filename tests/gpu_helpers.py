@@ -42,6 +42,29 @@ def blob_from_oracle(st):
                               st.bits.astype(np.uint8), st.qmin32, st.qscale32)
 
 
+def state_from_blob(blob, group_size=None):
+    """The oracle's TensorState holding exactly the frozen state of a library
+    blob (for instance one written by kvtc_fit_host): fp32 mean and basis,
+    widths, fp32 (min, scale), read from the blob's sections.  A dropped
+    component has no stored basis vector; its column is left zero, which the
+    oracle never uses (a 0-bit component contributes nothing)."""
+    v = K.state_view(blob)
+    h = v["header"]
+    mode = "dp" if h.mode == K.MODE_DP else "mixed"
+    cfg = O.Config(mode=mode, head_dim=h.head_dim, heads_per_unit=h.heads_per_unit, rank=h.rank_cfg,
+                   energy=h.energy_threshold, budget=h.bit_budget,
+                   choices=tuple(h.choices[i] for i in range(h.n_choices)), beta=h.beta, hi_bits=h.hi_bits,
+                   lo_bits=h.lo_bits, group_size=h.group_size if group_size is None else group_size)
+    U, dg, rmax = h.units, h.dg, h.rmax
+    V32 = np.zeros((U, dg, rmax), np.float32)
+    for u in range(U):
+        for j in range(int(v["n_slots"][u])):
+            V32[u, :, int(v["slot_comp"][u, j])] = v["basis"][u, j]
+    return O.TensorState(cfg, h.batch, h.heads, h.head_dim, h.heads_per_unit, v["rank"].astype(np.int64).copy(),
+                         v["mu"].copy(), v["lambda"].copy(), V32, v["bits"].astype(np.int64).copy(),
+                         v["qmin"].copy(), v["qscale"].copy(), h.row_stride)
+
+
 class DeviceStore:
     """A state blob on host and device plus its code/param stores for `capacity` rows."""
 

@@ -383,6 +383,10 @@ KV_CASES = [
     ("batched", small(4, B=3, s_prefill=2048, s_total=2048 + 45), small(4, B=3, s_prefill=2048, s_total=2048 + 45)),
     ("long", small(5, s_prefill=4096, s_total=4096 + 45), small(5, s_prefill=4096, s_total=4096 + 45)),
     ("palu", small(3, H=16, s_prefill=2048, s_total=2048 + 45), small(3, H=16, s_prefill=2048, s_total=2048 + 45)),
+    # a key tensor planned for four-wave blocks (128 fetch slots) inside a launch
+    # instantiated for the value tensor's longer contraction (176 slots: eight waves)
+    ("straddle-4-8-waves", small(4, B=3, s_prefill=2048, s_total=2048 + 45),
+     small(2, B=3, s_prefill=2048, s_total=2048 + 45)),
     # different modes: the call falls back to one launch per tensor
     ("dp-key-mixed-value", small(2, s_prefill=2048, s_total=2048 + 45),
      small(3, H=8, s_prefill=2048, s_total=2048 + 45)),

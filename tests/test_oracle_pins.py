@@ -370,6 +370,73 @@ def test_identity_basis_reduces_to_per_channel_affine_quantisation(rng):
         assert np.array_equal(out[:, d], lo32 + q * sc32)
 
 
+# ---------------------------------------------------------------- refit mode
+def _identity_state(bits, D=4):
+    """One unit whose basis is the identity and mean zero: latents are the rows."""
+    bits = np.asarray(bits, np.int64)
+    r = len(bits)
+    V = np.zeros((1, D, r), np.float32)
+    V[0, np.arange(r), np.arange(r)] = 1.0
+    cfg = O.Config(mode="dp", head_dim=D, rank=r)
+    return O.TensorState(cfg, 1, 1, D, 1, np.array([r]), np.zeros((1, D), np.float32), np.zeros((1, D)), V,
+                         bits[None], np.zeros((1, r), np.float32), np.zeros((1, r), np.float32),
+                         O.row_stride_bytes(int(bits.sum())))
+
+
+def test_refit_hand_example_earlier_codes_change():
+    """KVTC page, _TensorKVTC.append / _requantize: every call re-quantises all
+    accumulated rows with a min/max fitted over all of them.  One 2-bit
+    component with latents -1, 0, 3: min -1, scale fp32(4/3), codes
+    rint((l + 1) / scale) = 0, rint(0.74999997) = 1, rint(2.9999999) = 3.
+    After a row with latent 5 arrives: min -1, scale 6/3 = 2, and the earlier
+    rows now get 0, rint(0.5) = 0 (half to even), 2, and the new row 3."""
+    st = _identity_state([2, 0])
+    X = np.zeros((1, 1, 4, 4))
+    X[0, 0, :, 0] = [-1, 0, 3, 5]
+    st3, rows3 = O.append_refit(st, X[:, :, :3])
+    assert st3.qmin32[0, 0] == np.float32(-1) and st3.qscale32[0, 0] == np.float32(4 / 3)
+    assert O.unpack_rows(rows3[0], st.bits[0])[:, 0].tolist() == [0, 1, 3]
+    st4, rows4 = O.append_refit(st, X)
+    assert st4.qmin32[0, 0] == -1 and st4.qscale32[0, 0] == 2
+    assert O.unpack_rows(rows4[0], st.bits[0])[:, 0].tolist() == [0, 0, 2, 3]
+    # the frozen state of the first three rows clamps the new latent to the top code
+    assert O.unpack_rows(O.append(st3, X)[0][0], st.bits[0])[:, 0].tolist() == [0, 1, 3, 3]
+    assert O.clamp_fraction(st3, X[:, :, 3:]) == 1.0 and O.clamp_fraction(st3, X[:, :, :3]) == 0.0
+
+
+def test_refit_over_the_prefill_reproduces_the_fitted_ranges():
+    w = synth.WORKLOADS[1]
+    X = synth.generate(w, 0)
+    st = O.fit(_cfg(w), X[:, :, :256])
+    st2 = O.refit(st, X[:, :, :256])
+    assert np.array_equal(st2.qmin32, st.qmin32) and np.array_equal(st2.qscale32, st.qscale32)
+    assert O.clamp_fraction(st, X[:, :, :256]) == 0.0
+
+
+def test_refit_uses_the_whole_code_range_and_never_clamps():
+    """With min and max fitted over the accumulated rows, each kept component
+    with a non-zero range takes code 0 at its minimum and 2**b - 1 at its
+    maximum, and every latent decodes within half a step of itself."""
+    w = synth.WORKLOADS[1]
+    X = synth.generate(w, 1)
+    st = O.fit(_cfg(w), X[:, :, :256])
+    st2, rows = O.append_refit(st, X)
+    xu = O.gather_units(X, 1)
+    for u in range(st.U):
+        r = int(st.r[u])
+        bits = st.bits[u, :r]
+        codes = O.unpack_rows(rows[u], bits)
+        L = O.project(xu[u], st.mu32[u], st.V32[u, :, :r])
+        Lh = O.dequant_dp(codes, bits, st2.qmin32[u, :r], st2.qscale32[u, :r])
+        for i in np.flatnonzero(bits):
+            sc = float(st2.qscale32[u, i])
+            assert sc > 0
+            assert codes[:, i].min() == 0 and codes[:, i].max() == 2 ** int(bits[i]) - 1
+            assert (np.abs(Lh[:, i] - L[:, i]) <= 0.5 * sc * (1 + 1e-6)).all()
+    # the rows after the prefill do fall outside the frozen ranges now and then
+    assert 0.0 < O.clamp_fraction(st, X[:, :, 256:]) < 0.2
+
+
 # ---------------------------------------------------------------- byte formulas
 def test_byte_formulas_and_entropy_fallback():
     w = synth.WORKLOADS[1]
