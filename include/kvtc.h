@@ -299,6 +299,55 @@ int32_t kvtc_attend(const kvtc_tensor_ref *k, const kvtc_tensor_ref *v,
                     void *out_dev, const int64_t out_strides[3],
                     void *work_dev, size_t work_bytes, void *hip_stream);
 
+/* ------------------------------------------------------------ refit mode
+ * KVTC cache module page, _TensorKVTC.append and _requantize: every call joins
+ * the new rows to all rows accumulated so far, re-projects them through the
+ * frozen basis and mean, and quantises each kept component with a min/max
+ * fitted over all of them; the basis, mean and widths never change, the
+ * per-component (min, scale) and every stored code follow the accumulated
+ * sequence.  (kvtc_append instead keeps the prefill ranges frozen and clamps.)
+ * DP-mode tensors only (group-head rows carry per-token ranges already);
+ * KVTC_E_STATE otherwise.
+ *
+ * Buffers, owned by the caller, all device memory:
+ *   latents_dev  double [units][capacity][kslots]: the fp64 latents of every
+ *                appended row (computed once per row; a row's latents never
+ *                change under the frozen basis), 8-byte aligned
+ *   refit_dev    256-byte aligned, of the size kvtc_refit_bytes returns; its
+ *                sections, each 256-byte aligned, in this order:
+ *                  qmin32, qscale32  float  [units][kslots] the refitted min and
+ *                                    scale of slot j (fp32 of the float64 min and
+ *                                    of (max - min) / (2^b - 1); scale 0 for a
+ *                                    constant component)
+ *                  qlo, qinv         double [units][kslots] the quantiser's min and 1/scale
+ *                  w16               half   [units][dg][kfetch] fetch operand, laid
+ *                                    out as the blob's off_w16 section
+ *                  bias              float  [units][dg] fetch bias (as off_bias)
+ *                  part              double [units][chunks][kslots][2] scratch, with
+ *                                    chunks = clamp(ceil(capacity / 256), 1, 256)
+ */
+int32_t kvtc_refit_bytes(const void *state_host, int64_t capacity, size_t *latent_bytes, size_t *refit_bytes);
+
+/* Refit-mode append (device): the latents of rows x [B, H, n, D] go to rows
+ * [s0, s0 + n) of the latent store; then every kept component's range is
+ * refitted over rows [0, s0 + n) of the store (the accumulated sequence; rows
+ * past it are ignored, so lowering s0 + n is the page's trim), refit_dev's
+ * quantiser and fetch operands are rewritten, and the codes of every row
+ * [0, s0 + n) are re-quantised and re-packed into codes_dev (layout as for
+ * kvtc_append).  n = 0 refits the first s0 rows.  Arguments and errors as for
+ * kvtc_append; a row's latents and codes depend only on the rows accumulated,
+ * not on how they arrived. */
+int32_t kvtc_append_refit(const void *state_host, const void *state_dev, const void *x_dev, int32_t dtype,
+                          const int64_t x_strides[4], int64_t B, int64_t H, int64_t n, int64_t s0,
+                          void *latents_dev, void *codes_dev, void *refit_dev, int64_t capacity, void *hip_stream);
+
+/* Refit-mode fetch (device): kvtc_fetch of rows [s_begin, s_end) dequantised
+ * with the ranges of the last kvtc_append_refit (refit_dev's fetch operands).
+ * Arguments and errors as for kvtc_fetch. */
+int32_t kvtc_fetch_refit(const void *state_host, const void *state_dev, const void *codes_dev,
+                         const void *refit_dev, int64_t capacity, int64_t s_begin, int64_t s_end,
+                         void *out_dev, const int64_t out_strides[4], void *hip_stream);
+
 /* Storage accounting of one tensor over its first S rows (host).
  * KVTC page "Byte accounting" and the kvtc_bytes / pre_entropy_bytes
  * properties: order-0 Huffman per kept DP component, kept only when payload +

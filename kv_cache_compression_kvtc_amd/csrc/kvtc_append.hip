@@ -217,7 +217,10 @@ __global__ __launch_bounds__(kThreads) void append_kernel(AppendArgs a) {
 // N-blocks are spread over the 4 waves.  Each row goes through exactly the same
 // sequence of fp64 MFMAs (same operands, same k order) as in append_kernel, so
 // a row's codes do not depend on which kernel appended it.
-template <typename XT, int NB>
+// With LAT set (refit mode) the latents themselves are the output: the fp64
+// result of every slot below kslots goes to a.lat[u][s0 + t][j] and no codes are
+// formed.
+template <typename XT, int NB, bool LAT = false>
 __global__ __launch_bounds__(kThreads) void append_small_kernel(AppendArgs a) {
     extern __shared__ __align__(16) unsigned char smem[];
     const int xpitch = a.dg + 1, vpitch = a.dg + 1;
@@ -316,6 +319,23 @@ __global__ __launch_bounds__(kThreads) void append_small_kernel(AppendArgs a) {
                 acc[q] = __builtin_amdgcn_mfma_f64_16x16x4f64(av, bv, acc[q], 0, 0, 0);
             }
         }
+    }
+    if constexpr (LAT) {
+        // result layout: acc[q][i] is token (lane >> 4) + 4i, slot 16 * (wave + 4q) + lane % 16
+#pragma unroll
+        for (int q = 0; q < NBW; ++q) {
+            const int nb = wave + 4 * q;
+            const int j = nb * 16 + (lane & 15);
+            if (nb < NB && j < a.kslots) {
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const int t = (lane >> 4) + 4 * i;
+                    if (t < nvalid)
+                        a.lat[(static_cast<int64_t>(u) * a.capacity + a.s0 + t0 + t) * a.kslots + j] = acc[q][i];
+                }
+            }
+        }
+        return;
     }
 #pragma unroll
     for (int q = 0; q < NBW; ++q) {
@@ -460,6 +480,33 @@ int32_t launch_small_nb(const AppendArgs &a, int64_t U, hipStream_t stream) {
     return hipGetLastError() == hipSuccess ? KVTC_OK : KVTC_E_DEVICE;
 }
 
+template <typename XT, int NB>
+int32_t launch_refit_nb(const AppendArgs &a, int64_t U, hipStream_t stream) {
+    const size_t lds = small_lds_bytes(a.dg, NB, a.row_stride);
+    if (lds > kLdsMax) return KVTC_E_SHAPE;
+    auto kern = append_small_kernel<XT, NB, true>;
+    if (!allow_lds(reinterpret_cast<const void *>(kern))) return KVTC_E_DEVICE;
+    const int64_t blocks = (a.n + kSmallRows - 1) / kSmallRows;
+    if (blocks > 0x7FFFFFFF) return KVTC_E_SHAPE;
+    hipLaunchKernelGGL(kern, dim3(static_cast<unsigned>(blocks), static_cast<unsigned>(U)), dim3(kThreads), lds,
+                       stream, a);
+    return hipGetLastError() == hipSuccess ? KVTC_OK : KVTC_E_DEVICE;
+}
+
+template <typename XT>
+int32_t launch_refit(const AppendArgs &a, int64_t U, int nb, hipStream_t st) {
+    switch (nb) {
+        case 1: return launch_refit_nb<XT, 1>(a, U, st);
+        case 2: return launch_refit_nb<XT, 2>(a, U, st);
+        case 4: return launch_refit_nb<XT, 4>(a, U, st);
+        case 6: return launch_refit_nb<XT, 6>(a, U, st);
+        case 8: return launch_refit_nb<XT, 8>(a, U, st);
+        case 12: return launch_refit_nb<XT, 12>(a, U, st);
+        case 16: return launch_refit_nb<XT, 16>(a, U, st);
+        default: return KVTC_E_SHAPE;
+    }
+}
+
 template <typename XT>
 int32_t launch_small(const AppendArgs &a, int64_t U, int nb, hipStream_t st) {
     switch (nb) {
@@ -540,6 +587,15 @@ int32_t launch_decode(const AppendPlan &p0, const AppendPlan *p1, hipStream_t st
                    : launch_decode_dg<float, 128>(m, p0.a.n, units, nblk, stream);
     return f16 ? launch_decode_dg<_Float16, 64>(m, p0.a.n, units, nblk, stream)
                : launch_decode_dg<float, 64>(m, p0.a.n, units, nblk, stream);
+}
+
+// Refit mode: every row's latents come from append_small_kernel's fp64 MFMA
+// sequence whatever n is, so a row's latents do not depend on the call.
+int32_t launch_refit_project(const AppendPlan &p, hipStream_t stream) {
+    if (p.a.n == 0) return KVTC_OK;
+    if (p.mixed || !p.a.lat) return KVTC_E_STATE;
+    return p.dtype == KVTC_F16 ? launch_refit<_Float16>(p.a, p.units, p.nb, stream)
+                               : launch_refit<float>(p.a, p.units, p.nb, stream);
 }
 
 int32_t launch_append_plan(const AppendPlan &p, hipStream_t stream) {

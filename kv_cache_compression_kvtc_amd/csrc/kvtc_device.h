@@ -86,6 +86,7 @@ struct AppendArgs {
     const uint32_t *sbits;             // [U][kslots]
     uint8_t *codes;                    // [U][capacity][row_stride]
     uint32_t *params;                  // [U][capacity][n_qg] packed (min16 | scale16 << 16)
+    double *lat;                       // refit mode: latents [U][capacity][kslots] (else unused)
     int dg, D, hpu, groups, kslots, row_stride, n_qg, gs;
     float inv_dg, inv_q4;              // 1/dg and 4/dg: exact quotients of small indices
     int x_vec;                         // rows and strides aligned to 4 elements (raw vector loads)
@@ -257,12 +258,69 @@ struct FetchPlan {
     bool mixed;
 };
 
+// ------------------------------------------------------------ refit mode
+// Device buffer of a refit-mode tensor (caller-owned), sections 256-byte aligned
+// in this order: qmin32, qscale32 float [U][kslots] (the refitted ranges of
+// slot j), qlo, qinv double [U][kslots] (the quantiser's min and 1/scale),
+// w16 half [U][dg][kfetch] and bias float [U][dg] (fetch operands, laid out as
+// the blob's), part double [U][chunks][kslots][2] (per-chunk min and max).
+struct RefitLayout {
+    uint64_t qmin32, qscale32, qlo, qinv, w16, bias, part, total;
+    int chunks;
+};
+
+inline RefitLayout refit_layout(const kvtc_state_header *h, int64_t capacity) {
+    RefitLayout L{};
+    const uint64_t U = static_cast<uint64_t>(h->units), ks = h->kslots;
+    int64_t c = (capacity + 255) / 256;
+    L.chunks = static_cast<int>(c < 1 ? 1 : (c > 256 ? 256 : c));
+    uint64_t o = 0;
+    auto take = [&](uint64_t bytes) {
+        const uint64_t at = o;
+        o = align_up(o + (bytes ? bytes : 1), kSectionAlign);
+        return at;
+    };
+    L.qmin32 = take(U * ks * 4);
+    L.qscale32 = take(U * ks * 4);
+    L.qlo = take(U * ks * 8);
+    L.qinv = take(U * ks * 8);
+    L.w16 = take(U * static_cast<uint64_t>(h->dg) * h->kfetch * 2);
+    L.bias = take(U * static_cast<uint64_t>(h->dg) * 4);
+    L.part = take(U * static_cast<uint64_t>(L.chunks) * ks * 16);
+    L.total = o;
+    return L;
+}
+
+struct RefitArgs {
+    const double *lat;                 // [U][capacity][kslots] latents of the stored rows
+    int64_t capacity, S;               // rows [0, S) are accumulated
+    int64_t rows_per_chunk;
+    const kvtc_unit_info *ui;
+    const uint32_t *sbits;             // [U][kslots]
+    const float *basis;                // [U][kslots][dg]
+    const float *mu;                   // [U][dg]
+    const int32_t *fslot;              // [U][kfetch]
+    float *qmin32, *qscale32;          // [U][kslots]
+    double *qlo, *qinv;                // [U][kslots]
+    uint16_t *w16;                     // [U][dg][kfetch]
+    float *bias;                       // [U][dg]
+    double *part;                      // [U][chunks][kslots][2]
+    uint8_t *codes;                    // [U][capacity][row_stride]
+    int kslots, dg, kfetch, row_stride, chunks;
+};
+
+// Ranges over rows [0, S), the quantiser and fetch operands they imply, then
+// the codes of every row [0, S) re-quantised and re-packed (kvtc_refit.hip).
+int32_t launch_refit_requantise(const RefitArgs &a, int64_t units, hipStream_t stream);
+
 // ------------------------------------------------------------ launchers
 // append (kvtc_append.hip)
 int32_t launch_append_plan(const AppendPlan &p, hipStream_t stream);
 bool decode_path(const AppendPlan &p);
 int32_t launch_decode(const AppendPlan &p0, const AppendPlan *p1, hipStream_t stream);
 int append_nb(int kslots);
+// refit mode: fp64 latents of rows [s0, s0 + n) into a.lat (kvtc_append.hip)
+int32_t launch_refit_project(const AppendPlan &p, hipStream_t stream);
 
 // fetch: one launcher per contraction length in 16-slot k-steps, each compiled
 // in a translation unit of its own (kvtc_fetch_ks.hip)

@@ -266,4 +266,83 @@ int32_t kvtc_fetch_kv(const kvtc_tensor_ref *k, const kvtc_tensor_ref *v, int64_
     return launch_fetch_plans(pv, nullptr, stream);
 }
 
+// ------------------------------------------------------------ refit mode
+int32_t kvtc_refit_bytes(const void *state_host, int64_t capacity, size_t *latent_bytes, size_t *refit_bytes) {
+    const kvtc_state_header *h = nullptr;
+    const int32_t st = check_state(state_host, &h);
+    if (st != KVTC_OK) return st;
+    if (h->mode != KVTC_MODE_DP) return KVTC_E_STATE;
+    if (capacity < 0) return KVTC_E_ARG;
+    if (latent_bytes) *latent_bytes = static_cast<size_t>(h->units) * capacity * h->kslots * sizeof(double);
+    if (refit_bytes) *refit_bytes = refit_layout(h, capacity).total;
+    return KVTC_OK;
+}
+
+int32_t kvtc_append_refit(const void *state_host, const void *state_dev, const void *x_dev, int32_t dtype,
+                          const int64_t x_strides[4], int64_t B, int64_t H, int64_t n, int64_t s0, void *latents_dev,
+                          void *codes_dev, void *refit_dev, int64_t capacity, void *hip_stream) {
+    AppendPlan p;
+    int32_t st = plan_append(state_host, state_dev, x_dev, dtype, x_strides, B, H, n, s0, codes_dev, nullptr,
+                             capacity, &p);
+    if (st != KVTC_OK) return st;
+    const kvtc_state_header *h = static_cast<const kvtc_state_header *>(state_host);
+    if (h->mode != KVTC_MODE_DP) return KVTC_E_STATE;
+    if (h->kslots > 256) return KVTC_E_SHAPE;
+    if (!latents_dev || reinterpret_cast<uintptr_t>(latents_dev) % 8 || !refit_dev ||
+        reinterpret_cast<uintptr_t>(refit_dev) % kSectionAlign)
+        return KVTC_E_ARG;
+    const int64_t S = s0 + n;
+    if (S > 0 && h->row_stride > 0 && (!codes_dev || reinterpret_cast<uintptr_t>(codes_dev) % 4)) return KVTC_E_ARG;
+    hipStream_t stream = static_cast<hipStream_t>(hip_stream);
+    // latents of the new rows
+    p.a.lat = static_cast<double *>(latents_dev);
+    st = launch_refit_project(p, stream);
+    if (st != KVTC_OK) return st;
+    // ranges over every accumulated row, then all of their codes
+    const char *sd = static_cast<const char *>(state_dev);
+    char *rb = static_cast<char *>(refit_dev);
+    const RefitLayout L = refit_layout(h, capacity);
+    RefitArgs a{};
+    a.lat = static_cast<const double *>(latents_dev);
+    a.capacity = capacity;
+    a.S = S;
+    a.ui = reinterpret_cast<const kvtc_unit_info *>(sd + h->off_unit);
+    a.sbits = reinterpret_cast<const uint32_t *>(sd + h->off_slot_bits);
+    a.basis = reinterpret_cast<const float *>(sd + h->off_basis);
+    a.mu = reinterpret_cast<const float *>(sd + h->off_mu);
+    a.fslot = reinterpret_cast<const int32_t *>(sd + h->off_fslot);
+    a.qmin32 = reinterpret_cast<float *>(rb + L.qmin32);
+    a.qscale32 = reinterpret_cast<float *>(rb + L.qscale32);
+    a.qlo = reinterpret_cast<double *>(rb + L.qlo);
+    a.qinv = reinterpret_cast<double *>(rb + L.qinv);
+    a.w16 = reinterpret_cast<uint16_t *>(rb + L.w16);
+    a.bias = reinterpret_cast<float *>(rb + L.bias);
+    a.part = reinterpret_cast<double *>(rb + L.part);
+    a.codes = static_cast<uint8_t *>(codes_dev);
+    a.kslots = h->kslots;
+    a.dg = h->dg;
+    a.kfetch = h->kfetch;
+    a.row_stride = h->row_stride;
+    a.chunks = L.chunks;
+    return launch_refit_requantise(a, h->units, stream);
+}
+
+int32_t kvtc_fetch_refit(const void *state_host, const void *state_dev, const void *codes_dev, const void *refit_dev,
+                         int64_t capacity, int64_t s_begin, int64_t s_end, void *out_dev, const int64_t out_strides[4],
+                         void *hip_stream) {
+    FetchPlan p;
+    const int32_t st = plan_fetch(state_host, state_dev, codes_dev, nullptr, capacity, s_begin, s_end, out_dev,
+                                  out_strides, &p);
+    if (st != KVTC_OK) return st;
+    const kvtc_state_header *h = static_cast<const kvtc_state_header *>(state_host);
+    if (h->mode != KVTC_MODE_DP) return KVTC_E_STATE;
+    if (!refit_dev || reinterpret_cast<uintptr_t>(refit_dev) % kSectionAlign) return KVTC_E_ARG;
+    if (s_end == s_begin) return KVTC_OK;
+    const RefitLayout L = refit_layout(h, capacity);
+    const char *rb = static_cast<const char *>(refit_dev);
+    p.a.w16 = reinterpret_cast<const uint16_t *>(rb + L.w16);
+    p.a.bias = reinterpret_cast<const float *>(rb + L.bias);
+    return launch_fetch_plans(p, nullptr, static_cast<hipStream_t>(hip_stream));
+}
+
 }  // extern "C"

@@ -94,6 +94,9 @@ _sig = {
     "kvtc_bytes": (_i32, [_vp, _vp, _vp, _i64, _i64, C.POINTER(BytesReport)]),
     "kvtc_append_kv": (_i32, [C.POINTER(TensorRef), C.POINTER(TensorRef), _i64, _i64, _i64, _i64, _vp]),
     "kvtc_fetch_kv": (_i32, [C.POINTER(TensorRef), C.POINTER(TensorRef), _i64, _i64, _vp]),
+    "kvtc_refit_bytes": (_i32, [_vp, _i64, C.POINTER(_sz), C.POINTER(_sz)]),
+    "kvtc_append_refit": (_i32, [_vp, _vp, _vp, _i32, _P64, _i64, _i64, _i64, _i64, _vp, _vp, _vp, _i64, _vp]),
+    "kvtc_fetch_refit": (_i32, [_vp, _vp, _vp, _vp, _i64, _i64, _i64, _vp, _P64, _vp]),
     "kvtc_attend_workspace": (_i32, [_vp, _vp, _i64, C.POINTER(_sz)]),
     "kvtc_attend": (_i32, [C.POINTER(TensorRef), C.POINTER(TensorRef), _vp, _i32, _P64, _i64, _vp, _P64, _vp,
                            _sz, _vp]),
@@ -337,6 +340,80 @@ def kvtc_fetch_kv(k, v, capacity: int, s_begin: int, s_end: int, stream=None):
         refs.append(_tensor_ref(blob, blob_dev, codes, params, capacity, out, F16))
     _check(_lib.kvtc_fetch_kv(C.byref(refs[0]), C.byref(refs[1]), s_begin, s_end, _stream_ptr(stream)),
            "kvtc_fetch_kv")
+
+
+# ---------------------------------------------------------------- refit mode
+def kvtc_refit_bytes(blob: np.ndarray, capacity: int):
+    """(latent store bytes, refit buffer bytes) of a refit-mode DP tensor."""
+    _check_blob(blob, "kvtc_refit_bytes")
+    lb, rb = C.c_size_t(0), C.c_size_t(0)
+    _check(_lib.kvtc_refit_bytes(_host_ptr(blob), capacity, C.byref(lb), C.byref(rb)), "kvtc_refit_bytes")
+    return lb.value, rb.value
+
+
+def refit_sections(blob: np.ndarray, capacity: int) -> dict:
+    """Byte offsets of the refit buffer's sections (the layout kvtc.h documents)."""
+    h = header(blob)
+    U, ks = h.units, h.kslots
+    chunks = min(max((capacity + 255) // 256, 1), 256)
+    out, o = {}, 0
+    for name, nbytes in (("qmin32", U * ks * 4), ("qscale32", U * ks * 4), ("qlo", U * ks * 8),
+                         ("qinv", U * ks * 8), ("w16", U * h.dg * h.kfetch * 2), ("bias", U * h.dg * 4),
+                         ("part", U * chunks * ks * 16)):
+        out[name] = (o, nbytes)
+        o = (o + max(nbytes, 1) + 255) // 256 * 256
+    return out
+
+
+class RefitStore:
+    """Device buffers of one refit-mode tensor for ``capacity`` rows: the fp64
+    latent store, the code store and the refit buffer (torch allocations)."""
+
+    def __init__(self, blob, blob_dev, capacity, device="cuda:0"):
+        import torch
+        _check_blob(blob, "RefitStore")
+        lb, rb = kvtc_refit_bytes(blob, capacity)
+        cb, _ = kvtc_store_bytes(blob, capacity)
+        self.blob, self.blob_dev, self.capacity = blob, blob_dev, capacity
+        self.latents = torch.zeros(max(lb // 8, 1), dtype=torch.float64, device=device)
+        self.codes = torch.zeros(max(cb, 4), dtype=torch.uint8, device=device)
+        self._refit = torch.zeros(rb + 256, dtype=torch.uint8, device=device)
+        self._off = (-self._refit.data_ptr()) % 256
+        self.refit = self._refit[self._off: self._off + rb]
+        _check_buffers(blob, blob_dev, self.codes, None, capacity, "RefitStore")
+
+    def append(self, x, s0: int, stream=None):
+        """kvtc_append_refit of rows x [B, H, n, D] at store rows [s0, s0 + n)."""
+        import torch
+        dtype = {torch.float16: F16, torch.float32: F32}.get(x.dtype)
+        if dtype is None:
+            raise KVTCError(E_DTYPE, "kvtc_append_refit")
+        h = header(self.blob)
+        if x.dim() != 4 or not x.is_cuda or x.shape[3] != h.head_dim:
+            raise KVTCError(E_SHAPE, "kvtc_append_refit: x must be a device tensor [B, H, n, D]")
+        B, H, n, _ = x.shape
+        _check(_lib.kvtc_append_refit(_host_ptr(self.blob), _dev_ptr(self.blob_dev), _dev_ptr(x), dtype, _strides4(x),
+                                      B, H, n, s0, _dev_ptr(self.latents), _dev_ptr(self.codes),
+                                      self.refit.data_ptr(), self.capacity, _stream_ptr(stream)), "kvtc_append_refit")
+
+    def fetch(self, s_begin: int, s_end: int, out, stream=None):
+        """kvtc_fetch_refit of store rows [s_begin, s_end) into fp16 out [B, H, s_end - s_begin, D]."""
+        import torch
+        h = header(self.blob)
+        if out.dtype != torch.float16 or not out.is_cuda or \
+                tuple(out.shape) != (h.batch, h.heads, s_end - s_begin, h.head_dim):
+            raise KVTCError(E_SHAPE, "kvtc_fetch_refit: out must be fp16 [B, H, s_end - s_begin, D]")
+        _check(_lib.kvtc_fetch_refit(_host_ptr(self.blob), _dev_ptr(self.blob_dev), _dev_ptr(self.codes),
+                                     self.refit.data_ptr(), self.capacity, s_begin, s_end, _dev_ptr(out),
+                                     _strides4(out), _stream_ptr(stream)), "kvtc_fetch_refit")
+
+    def ranges(self):
+        """The refitted (qmin32, qscale32) per slot, as host arrays [units, kslots]."""
+        h = header(self.blob)
+        sec = refit_sections(self.blob, self.capacity)
+        raw = self.refit.cpu().numpy()
+        get = lambda name: raw[sec[name][0]: sec[name][0] + sec[name][1]].view(np.float32).reshape(h.units, h.kslots)
+        return get("qmin32").copy(), get("qscale32").copy()
 
 
 def kvtc_attend_workspace(blob_k: np.ndarray, blob_v: np.ndarray, s_end: int) -> int:

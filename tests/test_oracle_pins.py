@@ -642,3 +642,19 @@ def test_attend_over_a_zero_budget_value_cache_is_its_mean():
     q = np.random.default_rng(3).normal(size=(1, 2, w.D))
     got = O.attend(st_k, rows_k, st_v, rows_v, q)
     assert np.allclose(got[0], st_v.mu32.astype(np.float64), rtol=0, atol=1e-12)
+
+
+@pytest.mark.parametrize("wid,tensor", [(2, 0), (2, 1), (5, 0), (5, 1)])
+def test_frozen_mode_clamp_rate(wid, tensor):
+    """How often the frozen prefill ranges decide a code by clamping, on the
+    rows appended after the prefill (Llama-3-8B-like layer: its 256 decode
+    rows; long context: 8192 of the rows after the first 8192).  Printed for
+    the record; refit mode exists to remove it."""
+    w = synth.WORKLOADS[wid]
+    n = 256 if wid == 2 else 8192
+    X = synth.generate(w, tensor, 0, w.s_prefill + n)
+    st = O.fit(_cfg(w), X[:, :, : w.s_prefill])
+    rate = O.clamp_fraction(st, X[:, :, w.s_prefill:])
+    print(f"clamp rate {w.name} tensor {tensor}: {rate:.2e}")
+    assert O.clamp_fraction(st, X[:, :, : w.s_prefill]) == 0.0
+    assert rate < 0.01
