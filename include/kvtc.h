@@ -168,6 +168,35 @@ int32_t kvtc_fit_host(const kvtc_config *cfg, const void *rows_host, int32_t dty
                       int64_t B, int64_t H, int64_t S,
                       void *state_out, size_t *state_bytes);
 
+/* Bytes that suffice for the state blob of any fit of this configuration and
+ * shape (host, no fitting): a caller can allocate this much, fit once and keep
+ * the first *state_bytes bytes the fit reports. */
+int32_t kvtc_fit_bytes_bound(const kvtc_config *cfg, int64_t B, int64_t H, size_t *bytes);
+
+/* Device workspace kvtc_fit_device needs for S prefill rows (per unit: the
+ * mean, its partial sums and the covariance in float64; per unit and slot: the
+ * basis and the range keys of the range pass). */
+int32_t kvtc_fit_workspace(const kvtc_config *cfg, int64_t B, int64_t H, int64_t S, size_t *bytes);
+
+/* The fit of kvtc_fit_host from rows already on the device (device + host).
+ * KVTC page, update_and_fetch: the local PCA of every unit is fitted in one
+ * batched call on the prefill (the page's batched SVD fit), then the DP
+ * allocation and the per-component ranges.  The mean and the centred
+ * covariance of every unit (float64 MFMA) and the min/max of every kept
+ * component's latents over the prefill rows run on the device; the
+ * eigen-decomposition, rank and DP allocation run on the host.  The call waits
+ * for its stream and returns the host blob.
+ *   rows_dev    [B, H, S, D] device rows of dtype, element strides (strides[3] == 1)
+ *   work_dev    device workspace of kvtc_fit_workspace() bytes, 256-byte aligned
+ *   state_out, state_bytes   as for kvtc_fit_host
+ * The result equals kvtc_fit_host's up to the order of float64 summation (the
+ * mean exactly for fp16 rows; eigenvalues, fp32 basis and ranges to their last
+ * rounding).  D % 64 == 0, at most 65535 units, and in DP mode the configured
+ * rank (or D) at most 256; KVTC_E_BUFSIZE for a missing or short workspace. */
+int32_t kvtc_fit_device(const kvtc_config *cfg, const void *rows_dev, int32_t dtype, const int64_t strides[4],
+                        int64_t B, int64_t H, int64_t S, void *work_dev, size_t work_bytes,
+                        void *state_out, size_t *state_bytes, void *hip_stream);
+
 /* Build a state blob from an already fitted frozen state (host), for example a
  * basis calibrated elsewhere.  Arrays are host memory, unit-major:
  *   ranks   int32 [U]           kept components per unit (1..rmax)

@@ -14,7 +14,9 @@ namespace kvtc {
 namespace {
 
 // Wave w owns tokens 16w..16w+15; N-block nb covers slots 16nb..16nb+15.
-template <bool MIXED, typename XT, int NB, bool XVEC>
+// With RANGES set (device fit) nothing is stored: the block's per-slot min and
+// max over its valid tokens go to a.keys with atomic min / max.
+template <bool MIXED, typename XT, int NB, bool XVEC, bool RANGES = false>
 __global__ __launch_bounds__(kThreads) void append_kernel(AppendArgs a) {
     extern __shared__ __align__(16) unsigned char smem[];
     double *xs = reinterpret_cast<double *>(smem);                         // [2][64][kAppPad]
@@ -123,6 +125,41 @@ __global__ __launch_bounds__(kThreads) void append_kernel(AppendArgs a) {
     // fp64 16x16x4 result layout: acc[nb][i] is row (lane>>4) + 4i, column lane&15, i.e.
     // the latent of token 16*wave + (lane>>4) + 4i and slot 16*nb + (lane&15)
     const int tbase = wave * 16 + (lane >> 4);
+    if constexpr (RANGES) {
+        // min / max over this lane's tokens, its wave's four token groups (lanes
+        // 16 apart) and the block's four waves (staged in the now idle row chunks)
+        double *red = xs;                                  // [4][NB*16][2]
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb) {
+            double mn = __builtin_huge_val(), mx = -__builtin_huge_val();
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+                if (tbase + 4 * i < nvalid) {
+                    mn = fmin(mn, acc[nb][i]);
+                    mx = fmax(mx, acc[nb][i]);
+                }
+            mn = fmin(mn, __shfl_xor(mn, 16, 64));
+            mx = fmax(mx, __shfl_xor(mx, 16, 64));
+            mn = fmin(mn, __shfl_xor(mn, 32, 64));
+            mx = fmax(mx, __shfl_xor(mx, 32, 64));
+            if (lane < 16) {
+                red[(wave * NB * 16 + nb * 16 + lane) * 2] = mn;
+                red[(wave * NB * 16 + nb * 16 + lane) * 2 + 1] = mx;
+            }
+        }
+        __syncthreads();
+        for (int j = tid; j < min(NB * 16, n_slots); j += kThreads) {
+            double mn = red[j * 2], mx = red[j * 2 + 1];
+            for (int w = 1; w < 4; ++w) {
+                mn = fmin(mn, red[(w * NB * 16 + j) * 2]);
+                mx = fmax(mx, red[(w * NB * 16 + j) * 2 + 1]);
+            }
+            unsigned long long *k = a.keys + (static_cast<int64_t>(u) * a.kslots + j) * 2;
+            atomicMin(k, order_key(mn));
+            atomicMax(k + 1, order_key(mx));
+        }
+        return;
+    }
     const int64_t ub = static_cast<int64_t>(u) * a.kslots;
     if constexpr (!MIXED) {
 #pragma unroll
@@ -587,6 +624,41 @@ int32_t launch_decode(const AppendPlan &p0, const AppendPlan *p1, hipStream_t st
                    : launch_decode_dg<float, 128>(m, p0.a.n, units, nblk, stream);
     return f16 ? launch_decode_dg<_Float16, 64>(m, p0.a.n, units, nblk, stream)
                : launch_decode_dg<float, 64>(m, p0.a.n, units, nblk, stream);
+}
+
+template <typename XT, int NB>
+int32_t launch_ranges_nb(const AppendArgs &a, int64_t U, hipStream_t stream) {
+    // the block's row chunks double as the [4][NB*16][2] reduction area
+    static_assert(2 * kAppTok * kAppPad >= 4 * NB * 16 * 2, "reduction area");
+    const size_t lds = 2 * kAppTok * kAppPad * sizeof(double) + 2 * NB * 16 * kAppPad * sizeof(float);
+    auto kern = a.x_vec ? append_kernel<false, XT, NB, true, true> : append_kernel<false, XT, NB, false, true>;
+    if (!allow_lds(reinterpret_cast<const void *>(kern))) return KVTC_E_DEVICE;
+    const int64_t tiles = (a.n + kAppTok - 1) / kAppTok;
+    if (tiles > 0x7FFFFFFF || U > 65535) return KVTC_E_SHAPE;
+    hipLaunchKernelGGL(kern, dim3(static_cast<unsigned>(tiles), static_cast<unsigned>(U)), dim3(kThreads), lds, stream,
+                       a);
+    return hipGetLastError() == hipSuccess ? KVTC_OK : KVTC_E_DEVICE;
+}
+
+template <typename XT>
+int32_t launch_ranges(const AppendArgs &a, int64_t U, int nb, hipStream_t st) {
+    switch (nb) {
+        case 1: return launch_ranges_nb<XT, 1>(a, U, st);
+        case 2: return launch_ranges_nb<XT, 2>(a, U, st);
+        case 4: return launch_ranges_nb<XT, 4>(a, U, st);
+        case 6: return launch_ranges_nb<XT, 6>(a, U, st);
+        case 8: return launch_ranges_nb<XT, 8>(a, U, st);
+        case 12: return launch_ranges_nb<XT, 12>(a, U, st);
+        case 16: return launch_ranges_nb<XT, 16>(a, U, st);
+        default: return KVTC_E_SHAPE;
+    }
+}
+
+// Device fit: the prefill rows go through the bulk append kernel's fp64 MFMA
+// projection; its per-slot min and max replace the quantise-and-pack step.
+int32_t launch_fit_ranges(const AppendArgs &a, int64_t units, int nb, int32_t dtype, hipStream_t stream) {
+    if (a.n == 0) return KVTC_OK;
+    return dtype == KVTC_F16 ? launch_ranges<_Float16>(a, units, nb, stream) : launch_ranges<float>(a, units, nb, stream);
 }
 
 // Refit mode: every row's latents come from append_small_kernel's fp64 MFMA

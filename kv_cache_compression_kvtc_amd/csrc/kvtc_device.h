@@ -55,6 +55,13 @@ __device__ inline double half_bits_to_double(uint16_t h) {
     return static_cast<double>(__builtin_bit_cast(_Float16, h));
 }
 
+// An unsigned integer whose order is the order of the double x (for atomic
+// min/max of doubles): negative values bit-inverted, others with the sign bit set.
+__device__ inline unsigned long long order_key(double x) {
+    const unsigned long long b = static_cast<unsigned long long>(__double_as_longlong(x));
+    return (b >> 63) ? ~b : (b | 0x8000000000000000ull);
+}
+
 // ORs a width-w code into an LSB-first bit row held as 32-bit words in LDS.
 __device__ inline void or_field(uint32_t *row, uint32_t off, uint32_t w, uint32_t c) {
     const uint32_t wi = off >> 5, sh = off & 31u;
@@ -87,6 +94,7 @@ struct AppendArgs {
     uint8_t *codes;                    // [U][capacity][row_stride]
     uint32_t *params;                  // [U][capacity][n_qg] packed (min16 | scale16 << 16)
     double *lat;                       // refit mode: latents [U][capacity][kslots] (else unused)
+    unsigned long long *keys;          // device fit: per-slot (min, max) order keys [U][kslots][2]
     int dg, D, hpu, groups, kslots, row_stride, n_qg, gs;
     float inv_dg, inv_q4;              // 1/dg and 4/dg: exact quotients of small indices
     int x_vec;                         // rows and strides aligned to 4 elements (raw vector loads)
@@ -319,6 +327,9 @@ int32_t launch_append_plan(const AppendPlan &p, hipStream_t stream);
 bool decode_path(const AppendPlan &p);
 int32_t launch_decode(const AppendPlan &p0, const AppendPlan *p1, hipStream_t stream);
 int append_nb(int kslots);
+// device fit: per-slot min and max of the latents of rows [0, n) into a.keys,
+// as order-preserving integer keys (kvtc_append.hip)
+int32_t launch_fit_ranges(const AppendArgs &a, int64_t units, int nb, int32_t dtype, hipStream_t stream);
 // refit mode: fp64 latents of rows [s0, s0 + n) into a.lat (kvtc_append.hip)
 int32_t launch_refit_project(const AppendPlan &p, hipStream_t stream);
 

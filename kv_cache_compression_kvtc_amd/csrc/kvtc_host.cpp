@@ -315,6 +315,16 @@ struct UnitFit {
     int rank = 0;
 };
 
+// Mean [dg] and 1/S covariance [dg][dg] of every unit's prefill rows.
+struct Moments {
+    explicit Moments(int64_t U) : mean(U), cov(U) {}
+    std::vector<std::vector<double>> mean, cov;
+};
+
+struct FrozenParts;
+// Fills qmin / qscale [U][rmax] (DP mode) from the frozen parts.
+typedef std::function<int32_t(const FrozenParts &, std::vector<float> &, std::vector<float> &)> RangeFn;
+
 // Reads unit u's prefill rows as float64, [S][dg], heads of the unit concatenated.
 void load_unit_rows(const void *rows, int32_t dtype, int64_t B, int64_t H, int64_t S, int D, int hpu,
                     int64_t u, std::vector<double> &Y) {
@@ -418,6 +428,8 @@ void eig_sorted(std::vector<double> &C, int dg, UnitFit &f) {
     }
 }
 
+void range_from_minmax(double mn, double mx, int b, float *qmin, float *qscale);
+
 // Frozen (min, scale) of every component with non-zero width, over the
 // prefill latents (Y - mu32) . basis32 evaluated in float64.
 void frozen_ranges(const std::vector<double> &Xraw, int64_t S, int dg, const float *mu32,
@@ -473,9 +485,7 @@ void frozen_ranges(const std::vector<double> &Xraw, int64_t S, int dg, const flo
             mx = std::max(mx, hi[static_cast<size_t>(t) * nc + c]);
         }
         const int i = comps[c];
-        qmin[i] = static_cast<float>(mn);
-        qscale[i] = mx > mn ? static_cast<float>((mx - mn) / static_cast<double>((1 << bits[i]) - 1))
-                            : 0.0f;
+        range_from_minmax(mn, mx, bits[i], &qmin[i], &qscale[i]);
     }
 }
 
@@ -737,6 +747,79 @@ uint64_t huffman_bits(const uint64_t *counts, int n) {
     return total;
 }
 
+// ------------------------------------------------------------ fit core
+// The fit after the per-unit moments, shared by the host and the device fits:
+// eigenpairs, rank, fp32 mean and basis, DP allocation, ranges, blob.
+struct FrozenParts {
+    int rmax = 0;
+    std::vector<int32_t> ranks;        // [U]
+    std::vector<float> mu;             // [U][dg]
+    std::vector<float> basis;          // [U][rmax][dg] row i = component i
+    std::vector<double> lam;           // [U][dg]
+    std::vector<uint8_t> bits;         // [U][rmax]
+};
+
+int32_t fit_from_moments(const kvtc_config *cfg, int64_t B, int64_t H, int64_t S, Moments &m, const RangeFn &ranges,
+                         void *state_out, size_t *state_bytes) {
+    const int hpu = cfg->heads_per_unit, dg = cfg->head_dim * hpu;
+    const int64_t U = B * (H / hpu);
+    std::vector<UnitFit> fits(U);
+    if (!parallel_for(U, [&](int64_t u) {
+            fits[u].mean = std::move(m.mean[u]);
+            eig_sorted(m.cov[u], dg, fits[u]);
+            std::vector<double>().swap(m.cov[u]);
+        }))
+        return KVTC_E_ARG;
+    // rank per unit (mixed mode stores one rank for every group)
+    FrozenParts fp;
+    for (int64_t u = 0; u < U; ++u) {
+        fits[u].rank = cfg->rank > 0 ? cfg->rank : energy_rank(fits[u].lam.data(), dg, cfg->energy_threshold);
+        fp.rmax = std::max(fp.rmax, fits[u].rank);
+    }
+    if (cfg->mode == KVTC_MODE_MIXED)
+        for (auto &f : fits) f.rank = fp.rmax;
+    const int rmax = fp.rmax;
+    fp.ranks.resize(U);
+    fp.mu.resize(static_cast<size_t>(U) * dg);
+    fp.basis.assign(static_cast<size_t>(U) * rmax * dg, 0.f);
+    fp.lam.resize(static_cast<size_t>(U) * dg);
+    fp.bits.assign(static_cast<size_t>(U) * rmax, 0);
+    std::vector<int> choices(cfg->choices, cfg->choices + cfg->n_choices);
+    std::atomic<bool> feasible{true};
+    if (!parallel_for(U, [&](int64_t u) {
+            const UnitFit &f = fits[u];
+            const int r = f.rank;
+            fp.ranks[u] = r;
+            for (int d = 0; d < dg; ++d) {
+                fp.mu[u * dg + d] = static_cast<float>(f.mean[d]);
+                fp.lam[u * dg + d] = f.lam[d];
+            }
+            for (int i = 0; i < r; ++i)
+                for (int d = 0; d < dg; ++d)
+                    fp.basis[(static_cast<size_t>(u) * rmax + i) * dg + d] =
+                        static_cast<float>(f.vecs[static_cast<size_t>(i) * dg + d]);
+            if (cfg->mode == KVTC_MODE_DP &&
+                !dp_allocate(f.lam.data(), r, cfg->bit_budget, choices, cfg->beta, &fp.bits[static_cast<size_t>(u) * rmax]))
+                feasible = false;
+        }))
+        return KVTC_E_ARG;
+    if (!feasible) return KVTC_E_CONFIG;
+    std::vector<float> qmin(static_cast<size_t>(U) * rmax, 0.f), qscale(static_cast<size_t>(U) * rmax, 0.f);
+    if (cfg->mode == KVTC_MODE_DP) {
+        const int32_t st = ranges(fp, qmin, qscale);
+        if (st != KVTC_OK) return st;
+    }
+    return build_blob(cfg, B, H, rmax, fp.ranks.data(), fp.mu.data(), fp.basis.data(), fp.lam.data(), fp.bits.data(),
+                      qmin.data(), qscale.data(), S, state_out, state_bytes);
+}
+
+// (min, scale) of a component of width b from the float64 min and max of its
+// latents, stored as fp32 (a constant component gets scale 0).
+void range_from_minmax(double mn, double mx, int b, float *qmin, float *qscale) {
+    *qmin = static_cast<float>(mn);
+    *qscale = mx > mn ? static_cast<float>((mx - mn) / static_cast<double>((1 << b) - 1)) : 0.0f;
+}
+
 }  // namespace
 }  // namespace kvtc
 
@@ -817,76 +900,155 @@ int32_t kvtc_fit_host(const kvtc_config *cfg, const void *rows_host, int32_t dty
     const int hpu = cfg->heads_per_unit, D = cfg->head_dim, dg = D * hpu;
     const int64_t U = B * (H / hpu);
     try {
-        std::vector<UnitFit> fits(U);
-        const bool by_unit = U >= num_threads();
-        // 1. mean, covariance, eigenpairs per unit
-        auto fit_unit = [&](int64_t u, bool inner) {
-            std::vector<double> Y, C;
-            load_unit_rows(rows_host, dtype, B, H, S, D, hpu, u, Y);
-            mean_cov(Y, S, dg, fits[u].mean, C, inner);
-            eig_sorted(C, dg, fits[u]);
-        };
-        if (by_unit) {
-            if (!parallel_for(U, [&](int64_t u) { fit_unit(u, false); })) return KVTC_E_ARG;
+        // 1. mean and covariance per unit
+        Moments m(U);
+        if (U >= num_threads()) {
+            if (!parallel_for(U, [&](int64_t u) {
+                    std::vector<double> Y;
+                    load_unit_rows(rows_host, dtype, B, H, S, D, hpu, u, Y);
+                    mean_cov(Y, S, dg, m.mean[u], m.cov[u], false);
+                }))
+                return KVTC_E_ARG;
         } else {
-            // few units: parallelise the covariance inside a unit, the eigensolvers across units
-            std::vector<std::vector<double>> Cs(U);
+            // few units: parallelise the covariance inside a unit
             for (int64_t u = 0; u < U; ++u) {
                 std::vector<double> Y;
                 load_unit_rows(rows_host, dtype, B, H, S, D, hpu, u, Y);
-                mean_cov(Y, S, dg, fits[u].mean, Cs[u], true);
+                mean_cov(Y, S, dg, m.mean[u], m.cov[u], true);
             }
-            if (!parallel_for(U, [&](int64_t u) { eig_sorted(Cs[u], dg, fits[u]); })) return KVTC_E_ARG;
         }
-        // 2. rank per unit (mixed mode stores one rank for every group)
-        int rmax = 0;
-        for (int64_t u = 0; u < U; ++u) {
-            fits[u].rank = cfg->rank > 0 ? cfg->rank
-                                         : energy_rank(fits[u].lam.data(), dg, cfg->energy_threshold);
-            rmax = std::max(rmax, fits[u].rank);
-        }
-        if (cfg->mode == KVTC_MODE_MIXED)
-            for (auto &f : fits) f.rank = rmax;
-        // 3. frozen parts: fp32 mean and basis, DP allocation, ranges
-        std::vector<int32_t> ranks(U);
-        std::vector<float> mu(static_cast<size_t>(U) * dg), basis(static_cast<size_t>(U) * rmax * dg, 0.f);
-        std::vector<double> lam(static_cast<size_t>(U) * dg);
-        std::vector<uint8_t> bits(static_cast<size_t>(U) * rmax, 0);
-        std::vector<float> qmin(static_cast<size_t>(U) * rmax, 0.f), qscale(static_cast<size_t>(U) * rmax, 0.f);
-        std::vector<int> choices(cfg->choices, cfg->choices + cfg->n_choices);
-        std::atomic<bool> feasible{true};
-        auto freeze = [&](int64_t u, bool inner) {
-            const UnitFit &f = fits[u];
-            const int r = f.rank;
-            ranks[u] = r;
-            for (int d = 0; d < dg; ++d) {
-                mu[u * dg + d] = static_cast<float>(f.mean[d]);
-                lam[u * dg + d] = f.lam[d];
+        // 2.-4. eigenpairs, rank, allocation; ranges over the prefill latents on the host
+        const RangeFn ranges = [&](const FrozenParts &fp, std::vector<float> &qmin, std::vector<float> &qscale) {
+            const bool inner = U < num_threads();
+            auto one = [&](int64_t u) {
+                std::vector<double> X;
+                load_unit_rows(rows_host, dtype, B, H, S, D, hpu, u, X);
+                frozen_ranges(X, S, dg, &fp.mu[u * dg], &fp.basis[static_cast<size_t>(u) * fp.rmax * dg], fp.ranks[u],
+                              &fp.bits[static_cast<size_t>(u) * fp.rmax], &qmin[static_cast<size_t>(u) * fp.rmax],
+                              &qscale[static_cast<size_t>(u) * fp.rmax], inner);
+            };
+            if (inner) {
+                for (int64_t u = 0; u < U; ++u) one(u);
+                return KVTC_OK;
             }
-            for (int i = 0; i < r; ++i)
-                for (int d = 0; d < dg; ++d)
-                    basis[(static_cast<size_t>(u) * rmax + i) * dg + d] =
-                        static_cast<float>(f.vecs[static_cast<size_t>(i) * dg + d]);
-            if (cfg->mode != KVTC_MODE_DP) return;
-            uint8_t *bu = &bits[static_cast<size_t>(u) * rmax];
-            if (!dp_allocate(f.lam.data(), r, cfg->bit_budget, choices, cfg->beta, bu)) {
-                feasible = false;
-                return;
-            }
-            std::vector<double> X;
-            load_unit_rows(rows_host, dtype, B, H, S, D, hpu, u, X);
-            frozen_ranges(X, S, dg, &mu[u * dg], &basis[static_cast<size_t>(u) * rmax * dg], r, bu,
-                          &qmin[static_cast<size_t>(u) * rmax], &qscale[static_cast<size_t>(u) * rmax],
-                          inner);
+            return parallel_for(U, one) ? KVTC_OK : KVTC_E_ARG;
         };
-        if (by_unit) {
-            if (!parallel_for(U, [&](int64_t u) { freeze(u, false); })) return KVTC_E_ARG;
-        } else {
-            for (int64_t u = 0; u < U; ++u) freeze(u, true);
-        }
-        if (!feasible) return KVTC_E_CONFIG;
-        return build_blob(cfg, B, H, rmax, ranks.data(), mu.data(), basis.data(), lam.data(),
-                          bits.data(), qmin.data(), qscale.data(), S, state_out, state_bytes);
+        return fit_from_moments(cfg, B, H, S, m, ranges, state_out, state_bytes);
+    } catch (const std::bad_alloc &) {
+        return KVTC_E_ARG;
+    }
+}
+
+int32_t kvtc_fit_bytes_bound(const kvtc_config *cfg, int64_t B, int64_t H, size_t *bytes) {
+    int32_t st = validate_config(cfg);
+    if (st != KVTC_OK) return st;
+    if (!bytes) return KVTC_E_ARG;
+    if (B < 1 || H < 1 || H % cfg->heads_per_unit != 0) return KVTC_E_SHAPE;
+    const int dg = cfg->head_dim * cfg->heads_per_unit;
+    const int64_t U = B * (H / cfg->heads_per_unit);
+    const int rmax = cfg->rank > 0 ? cfg->rank : dg;
+    const int kslots = std::max<int>(kSlotAlign, static_cast<int>(align_up(rmax, kSlotAlign)));
+    // every run of equal widths is padded to whole k-steps: at most one run per
+    // stored slot in DP mode, two runs (hi, lo) in mixed mode
+    const int kfetch = cfg->mode == KVTC_MODE_MIXED ? kslots + 2 * kKStep : kKStep * kslots;
+    *bytes = plan_layout(U, dg, rmax, kslots, kfetch).total;
+    return KVTC_OK;
+}
+
+namespace {
+// Slot capacity of the device fit's range pass: the configured rank (or the
+// unit width) rounded up to 16; group-head tensors need no ranges.
+int fit_device_kslots(const kvtc_config *cfg) {
+    if (cfg->mode != KVTC_MODE_DP) return 0;
+    const int dg = cfg->head_dim * cfg->heads_per_unit;
+    return static_cast<int>(align_up(cfg->rank > 0 ? cfg->rank : dg, kSlotAlign));
+}
+}  // namespace
+
+int32_t kvtc_fit_workspace(const kvtc_config *cfg, int64_t B, int64_t H, int64_t S, size_t *bytes) {
+    int32_t st = validate_config(cfg);
+    if (st != KVTC_OK) return st;
+    if (!bytes) return KVTC_E_ARG;
+    if (B < 1 || H < 1 || H % cfg->heads_per_unit != 0) return KVTC_E_SHAPE;
+    if (S < 2) return KVTC_E_CONFIG;
+    const int dg = cfg->head_dim * cfg->heads_per_unit;
+    const int64_t U = B * (H / cfg->heads_per_unit);
+    *bytes = fit_device_layout(U, dg, S, fit_device_kslots(cfg)).total;
+    return KVTC_OK;
+}
+
+int32_t kvtc_fit_device(const kvtc_config *cfg, const void *rows_dev, int32_t dtype, const int64_t strides[4],
+                        int64_t B, int64_t H, int64_t S, void *work_dev, size_t work_bytes, void *state_out,
+                        size_t *state_bytes, void *hip_stream) {
+    int32_t st = validate_config(cfg);
+    if (st != KVTC_OK) return st;
+    if (!rows_dev || !strides || !state_bytes) return KVTC_E_ARG;
+    if (dtype != KVTC_F32 && dtype != KVTC_F16) return KVTC_E_DTYPE;
+    if (B < 1 || H < 1 || H % cfg->heads_per_unit != 0) return KVTC_E_SHAPE;
+    if (strides[3] != 1 || strides[0] < 0 || strides[1] < 0 || strides[2] < 0) return KVTC_E_SHAPE;
+    if (S < 2) return KVTC_E_CONFIG;                      // fit needs a prefill with S > 1
+    const int hpu = cfg->heads_per_unit, D = cfg->head_dim, dg = D * hpu;
+    const int64_t U = B * (H / hpu);
+    const int ks = fit_device_kslots(cfg);
+    if (U > 65535 || ks > 256) return KVTC_E_SHAPE;
+    const FitDeviceLayout L = fit_device_layout(U, dg, S, ks);
+    if (!work_dev || work_bytes < L.total || reinterpret_cast<uintptr_t>(work_dev) % kSectionAlign)
+        return KVTC_E_BUFSIZE;
+    FitDeviceRows r{};
+    r.rows = rows_dev;
+    r.dtype = dtype;
+    r.sb = strides[0];
+    r.sh = strides[1];
+    r.ss = strides[2];
+    r.B = B;
+    r.H = H;
+    r.S = S;
+    r.D = D;
+    r.hpu = hpu;
+    r.dg = dg;
+    r.units = U;
+    r.kslots = ks;
+    r.work = work_dev;
+    r.stream = hip_stream;
+    try {
+        // 1. mean and covariance per unit, on the device
+        std::vector<double> mean(static_cast<size_t>(U) * dg), cov(static_cast<size_t>(U) * dg * dg);
+        st = fit_device_moments(r, mean.data(), cov.data());
+        if (st != KVTC_OK) return st;
+        Moments m(U);
+        if (!parallel_for(U, [&](int64_t u) {
+                m.mean[u].assign(mean.begin() + u * dg, mean.begin() + (u + 1) * dg);
+                m.cov[u].assign(cov.begin() + u * dg * dg, cov.begin() + (u + 1) * dg * dg);
+            }))
+            return KVTC_E_ARG;
+        std::vector<double>().swap(cov);
+        // 2.-4. eigenpairs, rank, allocation on the host; ranges over the prefill latents on the device
+        const RangeFn ranges = [&](const FrozenParts &fp, std::vector<float> &qmin, std::vector<float> &qscale) {
+            if (fp.rmax > ks) return KVTC_E_SHAPE;
+            std::vector<float> bs(static_cast<size_t>(U) * ks * dg, 0.f);
+            std::vector<int32_t> ns(U, 0);
+            for (int64_t u = 0; u < U; ++u)
+                for (int i = 0; i < fp.ranks[u]; ++i)
+                    if (fp.bits[static_cast<size_t>(u) * fp.rmax + i]) {
+                        std::memcpy(&bs[(static_cast<size_t>(u) * ks + ns[u]) * dg],
+                                    &fp.basis[(static_cast<size_t>(u) * fp.rmax + i) * dg], dg * sizeof(float));
+                        ++ns[u];
+                    }
+            std::vector<double> mn(static_cast<size_t>(U) * ks), mx(static_cast<size_t>(U) * ks);
+            const int32_t s2 = fit_device_ranges(r, fp.mu.data(), bs.data(), ns.data(), mn.data(), mx.data());
+            if (s2 != KVTC_OK) return s2;
+            for (int64_t u = 0; u < U; ++u) {
+                int j = 0;
+                for (int i = 0; i < fp.ranks[u]; ++i) {
+                    const size_t ci = static_cast<size_t>(u) * fp.rmax + i;
+                    if (!fp.bits[ci]) continue;
+                    const size_t sj = static_cast<size_t>(u) * ks + j++;
+                    range_from_minmax(mn[sj], mx[sj], fp.bits[ci], &qmin[ci], &qscale[ci]);
+                }
+            }
+            return KVTC_OK;
+        };
+        return fit_from_moments(cfg, B, H, S, m, ranges, state_out, state_bytes);
     } catch (const std::bad_alloc &) {
         return KVTC_E_ARG;
     }

@@ -95,4 +95,56 @@ inline int32_t check_state(const void *blob, const kvtc_state_header **out) {
     return KVTC_OK;
 }
 
+// ------------------------------------------------------------ device fit
+// The device half of kvtc_fit_device (kvtc_fit.hip); the host half (eigen-
+// decomposition, rank, allocation, blob) is kvtc_host.cpp's.  Plain types only:
+// the host half is compiled without the HIP headers.
+struct FitDeviceRows {
+    const void *rows;          // device [B, H, S, D] of dtype, element strides sb, sh, ss (d stride 1)
+    int32_t dtype;
+    int64_t sb, sh, ss;
+    int64_t B, H, S;
+    int D, hpu, dg;
+    int64_t units;
+    int kslots;                // slot capacity of the range pass (multiple of 16, <= 256; 0: no ranges)
+    void *work;                // device workspace, fit_device_layout(...).total bytes, 256-byte aligned
+    void *stream;              // hipStream_t
+};
+
+struct FitDeviceLayout {
+    uint64_t mpart, mean, cov, basis, mu32, ui, keys, total;
+    int mchunks;               // row chunks of the mean's partial sums
+};
+
+inline FitDeviceLayout fit_device_layout(int64_t U, int dg, int64_t S, int kslots) {
+    FitDeviceLayout L{};
+    int64_t mc = (S + 1023) / 1024;
+    L.mchunks = static_cast<int>(mc < 1 ? 1 : (mc > 64 ? 64 : mc));
+    const uint64_t u = static_cast<uint64_t>(U), d = static_cast<uint64_t>(dg), k = static_cast<uint64_t>(kslots);
+    uint64_t o = 0;
+    auto take = [&](uint64_t bytes) {
+        const uint64_t at = o;
+        o = align_up(o + (bytes ? bytes : 1), kSectionAlign);
+        return at;
+    };
+    L.mpart = take(u * L.mchunks * d * 8);
+    L.mean = take(u * d * 8);
+    L.cov = take(u * d * d * 8);
+    L.basis = take(u * k * d * 4);
+    L.mu32 = take(u * d * 4);
+    L.ui = take(u * sizeof(kvtc_unit_info));
+    L.keys = take(u * k * 16);
+    L.total = o;
+    return L;
+}
+
+// Mean [U][dg] and 1/S covariance [U][dg][dg] (float64, host memory) of every
+// unit's rows; waits for the stream.  Returns a status.
+int32_t fit_device_moments(const FitDeviceRows &r, double *mean_host, double *cov_host);
+// Per-slot min and max [U][kslots] (host) of the latents (x - mu32) . basis_j of
+// every row, in float64 (fp64 MFMA); basis_slots [U][kslots][dg] and mu32
+// [U][dg] fp32 host arrays, n_slots [U]; waits for the stream.
+int32_t fit_device_ranges(const FitDeviceRows &r, const float *mu32_host, const float *basis_slots_host,
+                          const int32_t *n_slots_host, double *mn_host, double *mx_host);
+
 }  // namespace kvtc

@@ -85,6 +85,10 @@ _sig = {
     "kvtc_status_string": (C.c_char_p, [_i32]),
     "kvtc_build_id": (C.c_char_p, []),
     "kvtc_fit_host": (_i32, [C.POINTER(Config), _vp, _i32, _i64, _i64, _i64, _vp, C.POINTER(_sz)]),
+    "kvtc_fit_bytes_bound": (_i32, [C.POINTER(Config), _i64, _i64, C.POINTER(_sz)]),
+    "kvtc_fit_workspace": (_i32, [C.POINTER(Config), _i64, _i64, _i64, C.POINTER(_sz)]),
+    "kvtc_fit_device": (_i32, [C.POINTER(Config), _vp, _i32, _P64, _i64, _i64, _i64, _vp, _sz, _vp, C.POINTER(_sz),
+                               _vp]),
     "kvtc_state_build": (_i32, [C.POINTER(Config), _i64, _i64, _i32, _vp, _vp, _vp, _vp, _vp, _vp,
                                 _vp, _i64, _vp, C.POINTER(_sz)]),
     "kvtc_allocate_bits": (_i32, [_vp, _i32, _i32, _vp, _i32, C.c_double, _vp]),
@@ -174,13 +178,39 @@ def kvtc_fit_host(cfg: Config, rows: np.ndarray) -> np.ndarray:
     if dtype is None:
         raise KVTCError(E_DTYPE, "kvtc_fit_host")
     B, H, S, D = rows.shape
-    size = C.c_size_t(0)
-    _check(_lib.kvtc_fit_host(C.byref(cfg), _host_ptr(rows), dtype, B, H, S, None, C.byref(size)),
-           "kvtc_fit_host(size)")
-    blob = np.zeros(size.value, dtype=np.uint8)
-    _check(_lib.kvtc_fit_host(C.byref(cfg), _host_ptr(rows), dtype, B, H, S, _host_ptr(blob),
-                              C.byref(size)), "kvtc_fit_host")
-    return blob
+    buf, size = _fit_buffer(cfg, B, H)
+    _check(_lib.kvtc_fit_host(C.byref(cfg), _host_ptr(rows), dtype, B, H, S, _host_ptr(buf), C.byref(size)),
+           "kvtc_fit_host")
+    return buf[: size.value].copy()
+
+
+def _fit_buffer(cfg: Config, B: int, H: int):
+    """A host buffer large enough for any fit of this configuration and shape,
+    so that one fit call suffices (np.empty: pages are only touched as written)."""
+    bound = C.c_size_t(0)
+    _check(_lib.kvtc_fit_bytes_bound(C.byref(cfg), B, H, C.byref(bound)), "kvtc_fit_bytes_bound")
+    return np.empty(bound.value, dtype=np.uint8), C.c_size_t(bound.value)
+
+
+def kvtc_fit_device(cfg: Config, rows, stream=None) -> np.ndarray:
+    """Fit one tensor's frozen state on device rows [B, H, S, D] (fp16/fp32 tensor,
+    any strides with a unit innermost one); returns the host blob.  The device
+    workspace is allocated here (torch) for the duration of the call."""
+    import torch
+    dtype = {torch.float16: F16, torch.float32: F32}.get(rows.dtype)
+    if dtype is None:
+        raise KVTCError(E_DTYPE, "kvtc_fit_device")
+    if rows.dim() != 4 or not rows.is_cuda:
+        raise KVTCError(E_SHAPE, "kvtc_fit_device: rows must be a device tensor [B, H, S, D]")
+    B, H, S, D = rows.shape
+    need = C.c_size_t(0)
+    _check(_lib.kvtc_fit_workspace(C.byref(cfg), B, H, S, C.byref(need)), "kvtc_fit_workspace")
+    work = torch.empty(need.value + 256, dtype=torch.uint8, device=rows.device)
+    off = (-work.data_ptr()) % 256
+    buf, size = _fit_buffer(cfg, B, H)
+    _check(_lib.kvtc_fit_device(C.byref(cfg), _dev_ptr(rows), dtype, _strides4(rows), B, H, S, work.data_ptr() + off,
+                                need.value, _host_ptr(buf), C.byref(size), _stream_ptr(stream)), "kvtc_fit_device")
+    return buf[: size.value].copy()
 
 
 def kvtc_state_build(cfg: Config, B: int, H: int, ranks, mu, basis, lam=None, bits=None, qmin=None,
