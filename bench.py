@@ -45,7 +45,8 @@ def parse():
     p.add_argument("--warmup", type=int, default=3)
     p.add_argument("--cpu-seconds", type=float, default=10.0, help="oracle sample budget")
     p.add_argument("--no-cpu-baseline", action="store_true")
-    p.add_argument("--extra", action="store_true", help="also time the other workloads")
+    p.add_argument("--no-extra", action="store_true", help="skip the other workloads (long context, "
+                   "group-head, Llama layer), which the default run also times")
     p.add_argument("--copy-calibration", action="store_true",
                    help="only run a device copy of known size (for HBM counter scaling)")
     p.add_argument("--pmc-summary", nargs=4, metavar=("FETCH_DIR", "WRITE_DIR", "CAL_FETCH_DIR", "CAL_WRITE_DIR"),
@@ -171,9 +172,14 @@ class TensorPath:
         X = x_host if x_host is not None else synth.generate(w, tensor, 0, s_total)
         cfg = K.make_config(w.mode, w.D, w.heads_per_unit, w.rank, w.energy, w.budget, w.choices,
                             w.beta, w.hi_bits, w.lo_bits, w.group_size, w.hi_fraction)
-        t = time.time()
-        self.blob = K.kvtc_fit_host(cfg, np.ascontiguousarray(X[:, :, :s_fit]))
-        self.fit_s = time.time() - t
+        self.x = torch.from_numpy(X).to(dev)
+        # the prefill fit runs on the device rows (kvtc_fit_device), timed from
+        # the call to the returned host blob
+        K.kvtc_fit_device(cfg, self.x[:1, :, :s_fit])       # first call: kernel set-up
+        torch.cuda.synchronize()
+        t = time.perf_counter()
+        self.blob = K.kvtc_fit_device(cfg, self.x[:, :, :s_fit])
+        self.fit_s = time.perf_counter() - t
         self.h = K.header(self.blob)
         self.K = K
         self.cap = capacity
@@ -181,7 +187,6 @@ class TensorPath:
         cb, pb = K.kvtc_store_bytes(self.blob, capacity)
         self.codes = torch.zeros(max(cb, 4), dtype=torch.uint8, device=dev)
         self.params = torch.zeros(max(pb // 4, 1), dtype=torch.int32, device=dev) if pb else None
-        self.x = torch.from_numpy(X).to(dev)
         self.out = torch.empty((w.B, w.H, capacity, w.D), dtype=torch.float16, device=dev)
         del X
 
@@ -216,7 +221,7 @@ class KVLayer:
         for tensor in (synth.KEY, synth.VALUE):
             t = time.time()
             self.paths.append(TensorPath(K, w, tensor, s_fit, s_total, capacity, dev))
-            log(f"setup tensor {tensor}: {time.time() - t:.1f}s (fit {self.paths[-1].fit_s:.1f}s)")
+            log(f"setup tensor {tensor}: {time.time() - t:.1f}s (device fit {self.paths[-1].fit_s * 1e3:.1f} ms)")
         k, v = self.paths
         self.append = K.PreparedAppendKV(k.append_ref(), v.append_ref(), capacity)
         self.fetch = K.PreparedFetchKV(k.fetch_ref(), v.fetch_ref(), capacity)
@@ -268,9 +273,25 @@ def time_batched_decode(K, args, dev):
     fetch_bytes = [layer.fetch_bytes(s) for s in sizes]
     append_bytes = layer.append_bytes(1) * args.steps
     h = layer.paths[0].h
+    # the traffic-only probe on the last step's rows: same launch plan and bytes
+    # as the fetch, no arithmetic (its output is placeholder values)
+    S_last = sizes[-1]
+    layer.fetch.probe(0, S_last)
+    torch.cuda.synchronize()
+    probe_ms = []
+    for _ in range(10):
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        layer.fetch.probe(0, S_last)
+        b.record()
+        probe_ms.append((a, b))
+    torch.cuda.synchronize()
+    probe_ms = [a.elapsed_time(b) for a, b in probe_ms]
+    probe = {"ms": float(np.mean(probe_ms)), "bytes": layer.fetch_bytes(S_last)}
     att = time_attend(K, layer, sizes[-1], dev)
     return dict(w=w, total_ms=total_ms, fetch_ms=fetch_ms, positions=positions,
-                fetch_bytes=fetch_bytes, append_bytes=append_bytes, sizes=sizes, header=h, attend=att)
+                fetch_bytes=fetch_bytes, append_bytes=append_bytes, sizes=sizes, header=h, attend=att,
+                probe=probe, fit_ms=[p.fit_s * 1e3 for p in layer.paths])
 
 
 def time_attend(K, layer, S, dev, reps=20):
@@ -322,13 +343,26 @@ def time_one_shot(K, wid, dev, reps=5):
             res["append_ms"].append(e[0].elapsed_time(e[1]))
             res["fetch_ms"].append(e[1].elapsed_time(e[2]))
     ap, fe = float(np.median(res["append_ms"])), float(np.median(res["fetch_ms"]))
+    # the fetch's traffic alone (probe), timed after the fetch timings
+    pr = []
+    for r in range(reps + 1):
+        e = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+        e[0].record()
+        layer.fetch.probe(0, S)
+        e[1].record()
+        torch.cuda.synchronize()
+        if r:
+            pr.append(e[0].elapsed_time(e[1]))
+    pm = float(np.median(pr))
     fb = layer.fetch_bytes(S)
     ab = layer.append_bytes(S - a0)
     return {"workload": w.name, "B": w.B, "H": w.H, "D": w.D, "S": S, "append_rows": S - a0,
             "append_ms": round(ap, 4), "fetch_ms": round(fe, 4),
             "tokens_per_s": round(w.B * w.H * S / ((ap + fe) / 1e3), 1),
             "fetch_GBps": round(fb / fe / 1e6, 1), "append_GBps": round(ab / ap / 1e6, 1),
-            "fetch_frac_hbm": round(fb / fe / 1e6 / PEAK_HBM_GBPS, 4)}
+            "fetch_frac_hbm": round(fb / fe / 1e6 / PEAK_HBM_GBPS, 4),
+            "probe_ms": round(pm, 4), "fetch_frac_of_probe": round(pm / fe, 4),
+            "prefill_fit_ms": [round(p.fit_s * 1e3, 1) for p in layer.paths]}
 
 
 def time_decode_steps(K, dev, steps=64):
@@ -375,6 +409,15 @@ def cpu_baseline(seconds):
         threads = max((i.get("num_threads", 1) for i in threadpool_info()), default=1)
     except Exception:
         threads = 1
+    cpu_model = "unknown"
+    try:
+        with open("/proc/cpuinfo") as fh:
+            for line in fh:
+                if line.startswith("model name"):
+                    cpu_model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
     rng = np.random.default_rng(7)
     order = rng.permutation(w.B * w.H)
     elapsed = 0.0
@@ -398,6 +441,8 @@ def cpu_baseline(seconds):
         if elapsed >= seconds and units >= 4:
             break
     return {"value": round(positions / elapsed, 1), "unit": "tokens/s", "cores": int(threads),
+            "os_cpu_count": os.cpu_count(), "cpu_model": cpu_model,
+            "affinity_cpus": len(os.sched_getaffinity(0)) if hasattr(os, "sched_getaffinity") else None,
             "kind": "oracle",
             "sample": f"{units} of {w.B * w.H} (b,h) units of the batched-decode workload, K and V: "
                       f"append 1 row + fetch {S0 + 1} rows each, numpy float64; "
@@ -471,7 +516,16 @@ def main():
     out["attend_from_codes"] = dict(a, S=r["sizes"][-1], note="one query per (b, h); softmax attention over all "
                                     "stored K and V rows computed from the codes, no fp16 K/V written",
                                     fetch_ms_same_rows=round(float(np.mean(r["fetch_ms"][-2:])), 4))
-    if args.extra:
+    pr = r["probe"]
+    probe_gbps = pr["bytes"] / (pr["ms"] / 1e3) / 1e9
+    out["roofline"]["probe_ceiling_GBps"] = round(probe_gbps, 1)
+    out["roofline"]["frac_of_probe_ceiling"] = round(achieved / probe_gbps, 4)
+    out["roofline"]["probe"] = ("kvtc_fetch_kv_probe: the fetch's launch plan and bytes (W slices, code rows, "
+                                f"whole output rows, NT stores), no arithmetic; {pr['ms']:.4f} ms at S={r['sizes'][-1]}")
+    out["prefill_fit_ms"] = {"K": round(r["fit_ms"][0], 1), "V": round(r["fit_ms"][1], 1),
+                             "call": "kvtc_fit_device, 512 units x 8192 rows, device moments and ranges, "
+                                     "host eigensolve and DP"}
+    if not args.no_extra:
         extra = []
         for fn in (lambda: time_one_shot(K, 5, dev), lambda: time_one_shot(K, 3, dev),
                    lambda: time_decode_steps(K, dev)):

@@ -328,6 +328,18 @@ int32_t kvtc_attend(const kvtc_tensor_ref *k, const kvtc_tensor_ref *v,
                     void *out_dev, const int64_t out_strides[3],
                     void *work_dev, size_t work_bytes, void *hip_stream);
 
+/* ----------------------------------------------------------- measurement
+ * Traffic probe of kvtc_fetch_kv (device): not part of the method.  Same
+ * arguments, validation and launch plan (blocks, waves, pairing) as
+ * kvtc_fetch_kv, and the same memory traffic -- every block reads its W slice
+ * and bias, every tile's code rows (and params) are read and its output rows
+ * written with 16-byte non-temporal stores -- but nothing is decoded or
+ * contracted and no store waits for a load.  Its rate is the practical
+ * ceiling of the fetch's traffic, the reference the fetch kernel is measured
+ * against.  The output rows receive placeholder values, not a reconstruction. */
+int32_t kvtc_fetch_kv_probe(const kvtc_tensor_ref *k, const kvtc_tensor_ref *v, int64_t s_begin, int64_t s_end,
+                            void *hip_stream);
+
 /* ------------------------------------------------------------ refit mode
  * KVTC cache module page, _TensorKVTC.append and _requantize: every call joins
  * the new rows to all rows accumulated so far, re-projects them through the

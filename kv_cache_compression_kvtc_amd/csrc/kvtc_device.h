@@ -246,6 +246,40 @@ __device__ __forceinline__ half8 decode_kstep(uint32_t kd, const uint32_t *myrow
 
 constexpr int kLdsMax = 160 * 1024;
 
+// Whether a fetch block takes the branch-free tile path: rows of at most 16
+// words per lane (four-wave group-head blocks with k >= 128 would spill on it).
+constexpr bool fetch_flat_path(bool mixed, int ks, int rw, int nw) { return rw <= 16 && !(mixed && nw == 4 && ks >= 8); }
+
+// Register words per lane the fetch kernel is instantiated with for tiles of
+// rw words per lane (the narrowest of 8, 16 or 24 that holds them; 16 only for
+// whole-head blocks).
+constexpr int fetch_rw_inst(int ndb, int rw) { return rw <= 8 ? 8 : (ndb == 4 && rw <= 16 ? 16 : 24); }
+
+// Dynamic LDS carve-up of a fetch block for one tensor: sets the offsets and
+// pitches in a and returns the bytes the block needs.  The W slice
+// [ds][kfetch + 8] fp16, room for the k-step descriptors, the bias [ds] fp32,
+// then per wave: the tile's rows back to back (plus slack for the 3-word field
+// window of a padded k-step's upper operand half; on the branch-free path at
+// least rw words per lane, all of which are stashed), the group-head params
+// (plus one dummy word per lane for the branch-free stash) and the output
+// staging of nh 32-column blocks.
+inline size_t fetch_lds_plan(FetchArgs &a, bool mixed, int ds, int nw, int nh, int rw, bool flat) {
+    a.wpitch = a.kfetch + 8;
+    a.opitch = 32 * nh + 8;
+    a.lds_w = 0;
+    a.lds_desc = static_cast<int>(align_up(static_cast<uint64_t>(ds) * a.wpitch * 2, 16));
+    a.lds_bias = static_cast<int>(align_up(a.lds_desc + 16, 16));
+    a.lds_wave = static_cast<int>(align_up(a.lds_bias + ds * 4, 16));
+    int rows_b = static_cast<int>(align_up((kFetTok * (a.row_stride / 4) + 8) * 4, 16));
+    if (flat) rows_b = std::max(rows_b, rw * 64 * 4);
+    const int par_b = mixed ? static_cast<int>(align_up((kFetTok * a.n_qg + 64) * 4, 16)) : 0;
+    const int out_b = static_cast<int>(align_up(kFetTok * a.opitch * 2, 16));
+    a.lds_par = rows_b;
+    a.lds_out = rows_b + par_b;
+    a.lds_rows = rows_b + par_b + out_b;                 // per-wave bytes
+    return a.lds_wave + nw * static_cast<size_t>(a.lds_rows);
+}
+
 // Lets a kernel use up to the whole LDS of a CU as dynamic shared memory (set
 // once per kernel and device).
 bool allow_lds(const void *kern);
@@ -332,6 +366,10 @@ int append_nb(int kslots);
 int32_t launch_fit_ranges(const AppendArgs &a, int64_t units, int nb, int32_t dtype, hipStream_t stream);
 // refit mode: fp64 latents of rows [s0, s0 + n) into a.lat (kvtc_append.hip)
 int32_t launch_refit_project(const AppendPlan &p, hipStream_t stream);
+
+// traffic probe of the fetch with the fetch's launch plan (kvtc_probe.hip):
+// ds columns per block, nw waves per block, the fetch's dynamic LDS bytes
+int32_t launch_fetch_probe(const FetchPair &m, int ds, int nw, bool mixed, int rw, size_t lds, hipStream_t stream);
 
 // fetch: one launcher per contraction length in 16-slot k-steps, each compiled
 // in a translation unit of its own (kvtc_fetch_ks.hip)

@@ -175,6 +175,33 @@ int32_t plan_fetch(const void *state_host, const void *state_dev, const void *co
 
 // One fetch launch for one plan (p1 == NULL) or for two plans of the same
 // mode and block width; the kernel is instantiated for the wider contraction.
+// The probe of one launch of launch_fetch_plans: same pair, blocks and waves.
+int32_t launch_probe_plans(const FetchPlan &p0, const FetchPlan *p1, hipStream_t stream) {
+    FetchPair m{};
+    m.t[0] = p0.a;
+    m.split = p0.a.nblocks;
+    m.nblocks_real = p0.a.nblocks;
+    int ks = p0.a.nks;
+    if (p1) {
+        m.t[1] = p1->a;
+        m.nblocks_real += p1->a.nblocks;
+        ks = std::max(ks, p1->a.nks);
+    }
+    m.nblocks_per_xcd = (m.nblocks_real + 7) / 8;
+    if (m.nblocks_per_xcd * 8 > 0x7FFFFFFF) return KVTC_E_SHAPE;
+    // the fetch kernel's waves per block and its dynamic LDS, so that as many
+    // probe blocks share a CU as fetch blocks would
+    const int ndb = p0.ds / 32;
+    const int nw = (p0.ds == 128 && ks >= 10) ? 8 : 4;
+    const int nh = nw == 8 ? ndb / 2 : ndb;
+    const int rw = fetch_rw_inst(ndb, std::max(p0.rw, p1 ? p1->rw : 0));
+    const bool flat = fetch_flat_path(p0.mixed, ks, rw, nw);
+    size_t lds = fetch_lds_plan(m.t[0], p0.mixed, p0.ds, nw, nh, rw, flat);
+    if (p1) lds = std::max(lds, fetch_lds_plan(m.t[1], p0.mixed, p0.ds, nw, nh, rw, flat));
+    if (lds > kLdsMax) return KVTC_E_SHAPE;
+    return launch_fetch_probe(m, p0.ds, nw, p0.mixed, rw, lds, stream);
+}
+
 int32_t launch_fetch_plans(const FetchPlan &p0, const FetchPlan *p1, hipStream_t stream) {
     FetchPair m{};
     m.t[0] = p0.a;
@@ -264,6 +291,32 @@ int32_t kvtc_fetch_kv(const kvtc_tensor_ref *k, const kvtc_tensor_ref *v, int64_
     st = launch_fetch_plans(pk, nullptr, stream);
     if (st != KVTC_OK) return st;
     return launch_fetch_plans(pv, nullptr, stream);
+}
+
+// ------------------------------------------------------------ measurement
+int32_t kvtc_fetch_kv_probe(const kvtc_tensor_ref *k, const kvtc_tensor_ref *v, int64_t s_begin, int64_t s_end,
+                            void *hip_stream) {
+    if (!k || !v) return KVTC_E_ARG;
+    FetchPlan pk, pv;
+    int32_t st = plan_fetch(k->state_host, k->state_dev, k->codes_dev, k->params_dev, k->capacity, s_begin, s_end,
+                            k->rows_dev, k->strides, &pk);
+    if (st != KVTC_OK) return st;
+    st = plan_fetch(v->state_host, v->state_dev, v->codes_dev, v->params_dev, v->capacity, s_begin, s_end,
+                    v->rows_dev, v->strides, &pv);
+    if (st != KVTC_OK || s_end == s_begin) return st;
+    hipStream_t stream = static_cast<hipStream_t>(hip_stream);
+    if (pk.mixed == pv.mixed && pk.ds == pv.ds) {
+        st = plan_fetch(k->state_host, k->state_dev, k->codes_dev, k->params_dev, k->capacity, s_begin, s_end,
+                        k->rows_dev, k->strides, &pk, 2);
+        if (st != KVTC_OK) return st;
+        st = plan_fetch(v->state_host, v->state_dev, v->codes_dev, v->params_dev, v->capacity, s_begin, s_end,
+                        v->rows_dev, v->strides, &pv, 2);
+        if (st != KVTC_OK) return st;
+        return launch_probe_plans(pk, &pv, stream);
+    }
+    st = launch_probe_plans(pk, nullptr, stream);
+    if (st != KVTC_OK) return st;
+    return launch_probe_plans(pv, nullptr, stream);
 }
 
 // ------------------------------------------------------------ refit mode

@@ -342,28 +342,12 @@ template <bool MIXED, int NDB, int KS, int RW>
 int32_t launch_fetch_rw(FetchPair m, int nt, hipStream_t stream) {
     constexpr int DS = 32 * NDB, NW = fetch_waves<NDB, KS>();
     constexpr int NH = fetch_epilogue_blocks<NDB, NW>();
+    static_assert(fetch_flat<MIXED, KS, RW, NW>() == fetch_flat_path(MIXED, KS, RW, NW), "flat path rule");
     size_t lds = 0;
     for (int i = 0; i < nt; ++i) {
         FetchArgs &a = m.t[i];
         if (kFetTok * (a.row_stride / 4 + (MIXED ? a.n_qg : 0)) > 64 * RW) return KVTC_E_SHAPE;
-        a.wpitch = a.kfetch + 8;
-        a.opitch = 32 * NH + 8;
-        a.lds_w = 0;
-        a.lds_desc = static_cast<int>(align_up(static_cast<uint64_t>(DS) * a.wpitch * 2, 16));
-        a.lds_bias = static_cast<int>(align_up(a.lds_desc + 16, 16));
-        a.lds_wave = static_cast<int>(align_up(a.lds_bias + DS * 4, 16));
-        // rows of a tile back to back, plus slack for the 3-word field window of the
-        // upper operand half of a padded k-step (the branch-free path stashes all
-        // RW words per lane, so its rows area holds at least that many)
-        int rows_b = static_cast<int>(align_up((kFetTok * (a.row_stride / 4) + 8) * 4, 16));
-        if (fetch_flat<MIXED, KS, RW, NW>()) rows_b = std::max(rows_b, RW * 64 * 4);
-        // (plus one dummy word per lane for the branch-free stash)
-        const int par_b = MIXED ? static_cast<int>(align_up((kFetTok * a.n_qg + 64) * 4, 16)) : 0;
-        const int out_b = static_cast<int>(align_up(kFetTok * a.opitch * 2, 16));
-        a.lds_par = rows_b;
-        a.lds_out = rows_b + par_b;
-        a.lds_rows = rows_b + par_b + out_b;                 // per-wave bytes
-        lds = std::max(lds, a.lds_wave + NW * static_cast<size_t>(a.lds_rows));
+        lds = std::max(lds, fetch_lds_plan(a, MIXED, DS, NW, NH, RW, fetch_flat<MIXED, KS, RW, NW>()));
     }
     if (lds > kLdsMax) return KVTC_E_SHAPE;
     const int64_t grid = m.nblocks_per_xcd * 8;
@@ -377,6 +361,7 @@ int32_t launch_fetch_rw(FetchPair m, int nt, hipStream_t stream) {
 // holds them (whole-head tiles: 8, 16 or 24 words per lane; 64-column: 8 or 24).
 template <bool MIXED, int NDB, int KS>
 int32_t launch_fetch_ks(const FetchPair &m, int nt, int rw, hipStream_t stream) {
+    static_assert(fetch_rw_inst(NDB, 8) == 8 && fetch_rw_inst(NDB, 9) == (NDB == 4 ? 16 : 24), "rw rule");
     if (rw <= 8) return launch_fetch_rw<MIXED, NDB, KS, 8>(m, nt, stream);
     if (NDB == 4 && rw <= 16) return launch_fetch_rw<MIXED, NDB, KS, (NDB == 4 ? 16 : 24)>(m, nt, stream);
     if (rw <= kFetchRegWords) return launch_fetch_rw<MIXED, NDB, KS, kFetchRegWords>(m, nt, stream);

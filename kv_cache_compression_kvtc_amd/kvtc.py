@@ -98,6 +98,7 @@ _sig = {
     "kvtc_bytes": (_i32, [_vp, _vp, _vp, _i64, _i64, C.POINTER(BytesReport)]),
     "kvtc_append_kv": (_i32, [C.POINTER(TensorRef), C.POINTER(TensorRef), _i64, _i64, _i64, _i64, _vp]),
     "kvtc_fetch_kv": (_i32, [C.POINTER(TensorRef), C.POINTER(TensorRef), _i64, _i64, _vp]),
+    "kvtc_fetch_kv_probe": (_i32, [C.POINTER(TensorRef), C.POINTER(TensorRef), _i64, _i64, _vp]),
     "kvtc_refit_bytes": (_i32, [_vp, _i64, C.POINTER(_sz), C.POINTER(_sz)]),
     "kvtc_append_refit": (_i32, [_vp, _vp, _vp, _i32, _P64, _i64, _i64, _i64, _i64, _vp, _vp, _vp, _i64, _vp]),
     "kvtc_fetch_refit": (_i32, [_vp, _vp, _vp, _vp, _i64, _i64, _i64, _vp, _P64, _vp]),
@@ -660,3 +661,11 @@ class PreparedFetchKV:
         for i in range(2):
             self._refs[i].rows_dev = self._out[i] + s0 * self._os[i]
         _check(self._fn(C.byref(self._refs[0]), C.byref(self._refs[1]), s0, s1, self._stream), "kvtc_fetch_kv")
+
+    def probe(self, s0: int, s1: int):
+        """kvtc_fetch_kv_probe with the same buffers: the fetch's traffic alone
+        (overwrites the output rows with placeholder values)."""
+        for i in range(2):
+            self._refs[i].rows_dev = self._out[i] + s0 * self._os[i]
+        _check(_lib.kvtc_fetch_kv_probe(C.byref(self._refs[0]), C.byref(self._refs[1]), s0, s1, self._stream),
+               "kvtc_fetch_kv_probe")

@@ -470,6 +470,28 @@ def test_prepared_kv_calls_match_the_plain_binding():
         app(S - 1, S + 1)
 
 
+def test_fetch_probe_writes_exactly_the_fetched_rows():
+    """The traffic probe (a measurement kernel) covers exactly the rows the fetch
+    writes: every output row in [s_begin, s_end) is overwritten, nothing else."""
+    print_case("fetch probe coverage")
+    for w in (small(4, B=2, s_prefill=1024, s_total=1024 + 45), small(3, H=16, s_prefill=2048, s_total=2048 + 33)):
+        Xk, Xv = synth.generate(w, 0), synth.generate(w, 1)
+        S = Xk.shape[2]
+        blobs = [blob_from_oracle(O.fit(oracle_cfg(w), X[:, :, :w.s_prefill])) for X in (Xk, Xv)]
+        st = [DeviceStore(b, S) for b in blobs]
+        for i, x in enumerate((Xk, Xv)):
+            st[i].append(x, 0)
+        outs = [torch.full((w.B, w.H, S, w.D), float("nan"), dtype=torch.float16, device="cuda:0") for _ in range(2)]
+        fet = K.PreparedFetchKV(*[(st[i].blob, st[i].blob_dev, st[i].codes, st[i].params, outs[i]) for i in range(2)], S)
+        sb, se = 7, S - 5
+        fet.probe(sb, se)
+        torch.cuda.synchronize()
+        for o in outs:
+            nan = torch.isnan(o)
+            assert not nan[:, :, sb:se].any()
+            assert nan[:, :, :sb].all() and nan[:, :, se:].all()
+
+
 # ---------------------------------------------------------------- decode attention from the codes
 ATTEND_CASES = [
     ("tiny", small(1)),
