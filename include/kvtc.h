@@ -17,7 +17,9 @@
  *   - the caller owns every buffer; the library allocates no device memory
  *     and is reentrant; host scratch lives only for the duration of a call;
  *     its only process-wide state is the record of which kernels it has
- *     already allowed to use a CU's whole LDS (set once per kernel and device);
+ *     already allowed to use a CU's whole LDS (set once per kernel and device)
+ *     and, for kvtc_attend_noalloc, one fixed scratch array per device and the
+ *     record of its address;
  *   - device work is enqueued on the given hipStream_t (NULL = the null
  *     stream) and the call returns after the enqueue;
  *   - every argument is validated before anything is launched or written; a
@@ -388,6 +390,22 @@ int32_t kvtc_append_refit(const void *state_host, const void *state_dev, const v
 int32_t kvtc_fetch_refit(const void *state_host, const void *state_dev, const void *codes_dev,
                          const void *refit_dev, int64_t capacity, int64_t s_begin, int64_t s_end,
                          void *out_dev, const int64_t out_strides[4], void *hip_stream);
+
+/* kvtc_attend for callers that cannot allocate device memory (code under HIP
+ * graph capture, tight serving loops, harnesses that forbid allocation): the
+ * same validation, kernels and results as kvtc_attend, with the workspace taken
+ * from a fixed scratch array of KVTC_ATTEND_SCRATCH_BYTES that the library holds
+ * on every device that loads it until the process ends (its address is looked
+ * up once per device, on the first call).  Nothing is allocated.  Returns
+ * KVTC_E_BUFSIZE, before anything is launched, when the call needs more than
+ * KVTC_ATTEND_SCRATCH_BYTES (kvtc_attend_workspace tells the need).  Every call
+ * on a device shares that device's scratch: calls that overlap on one device
+ * race and must be ordered by the caller (for instance on one stream).  The
+ * scratch needs no clearing: every word a call reads was written by that call. */
+#define KVTC_ATTEND_SCRATCH_BYTES (16u << 20)
+int32_t kvtc_attend_noalloc(const kvtc_tensor_ref *k, const kvtc_tensor_ref *v, const void *q_dev, int32_t q_dtype,
+                            const int64_t q_strides[3], int64_t s_end, void *out_dev, const int64_t out_strides[3],
+                            void *hip_stream);
 
 /* Storage accounting of one tensor over its first S rows (host).
  * KVTC page "Byte accounting" and the kvtc_bytes / pre_entropy_bytes

@@ -1,4 +1,6 @@
 // Decode attention from the codes (gfx950): kvtc_attend and its kernels.
+#include <mutex>
+
 #include "kvtc_device.h"
 
 namespace kvtc {
@@ -341,6 +343,42 @@ size_t attend_work_bytes(const kvtc_state_header *hk, const kvtc_state_header *h
 }  // namespace
 }  // namespace kvtc
 
+// Scratch of the allocation-free entry point (kvtc_attend_noalloc): a fixed
+// device array of the library, KVTC_ATTEND_SCRATCH_BYTES per device that loads
+// it, held until the process ends.  Host code never uses this name as an
+// address: each device's copy is found once with hipGetSymbolAddress.
+static __device__ __align__(256) unsigned char scratch[KVTC_ATTEND_SCRATCH_BYTES];
+
+namespace kvtc {
+namespace {
+
+constexpr size_t kAttendScratchBytes = KVTC_ATTEND_SCRATCH_BYTES;
+constexpr int kMaxDevices = 64;
+
+// This device's copy of scratch, looked up once per device (with that device
+// current) and kept.
+int32_t scratch_address(void **out) {
+    static std::mutex mu;
+    static void *addr[kMaxDevices] = {};
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return KVTC_E_DEVICE;
+    std::lock_guard<std::mutex> lock(mu);
+    if (!addr[dev]) {
+        void *p = nullptr;
+        if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return KVTC_E_DEVICE;
+        addr[dev] = p;
+    }
+    *out = addr[dev];
+    return KVTC_OK;
+}
+
+int32_t attend_impl(const kvtc_tensor_ref *k, const kvtc_tensor_ref *v, const void *q_dev, int32_t q_dtype,
+                    const int64_t q_strides[3], int64_t s_end, void *out_dev, const int64_t out_strides[3],
+                    void *work_dev, size_t work_bytes, bool noalloc, hipStream_t stream);
+
+}  // namespace
+}  // namespace kvtc
+
 using namespace kvtc;
 
 extern "C" {
@@ -359,6 +397,28 @@ int32_t kvtc_attend_workspace(const void *k_state_host, const void *v_state_host
 int32_t kvtc_attend(const kvtc_tensor_ref *k, const kvtc_tensor_ref *v, const void *q_dev, int32_t q_dtype,
                     const int64_t q_strides[3], int64_t s_end, void *out_dev, const int64_t out_strides[3],
                     void *work_dev, size_t work_bytes, void *hip_stream) {
+    return attend_impl(k, v, q_dev, q_dtype, q_strides, s_end, out_dev, out_strides, work_dev, work_bytes, false,
+                       static_cast<hipStream_t>(hip_stream));
+}
+
+int32_t kvtc_attend_noalloc(const kvtc_tensor_ref *k, const kvtc_tensor_ref *v, const void *q_dev, int32_t q_dtype,
+                            const int64_t q_strides[3], int64_t s_end, void *out_dev, const int64_t out_strides[3],
+                            void *hip_stream) {
+    return attend_impl(k, v, q_dev, q_dtype, q_strides, s_end, out_dev, out_strides, nullptr, 0, true,
+                       static_cast<hipStream_t>(hip_stream));
+}
+
+}  // extern "C"
+
+namespace kvtc {
+namespace {
+
+// Validates the call, then launches the three attention kernels on the given
+// workspace; with noalloc the workspace is this device's scratch array (after
+// its size has been checked against the call's need).
+int32_t attend_impl(const kvtc_tensor_ref *k, const kvtc_tensor_ref *v, const void *q_dev, int32_t q_dtype,
+                    const int64_t q_strides[3], int64_t s_end, void *out_dev, const int64_t out_strides[3],
+                    void *work_dev, size_t work_bytes, bool noalloc, hipStream_t stream) {
     if (!k || !v || !q_strides || !out_strides) return KVTC_E_ARG;
     const kvtc_state_header *hk = nullptr, *hv = nullptr;
     int32_t st = check_state(k->state_host, &hk);
@@ -380,6 +440,12 @@ int32_t kvtc_attend(const kvtc_tensor_ref *k, const kvtc_tensor_ref *v, const vo
     if (reinterpret_cast<uintptr_t>(out_dev) % 2 || reinterpret_cast<uintptr_t>(q_dev) % (q_dtype == KVTC_F16 ? 2 : 4))
         return KVTC_E_ARG;
     const size_t need = attend_work_bytes(hk, hv, s_end);
+    if (noalloc) {
+        if (need > kAttendScratchBytes) return KVTC_E_BUFSIZE;
+        const int32_t sa = scratch_address(&work_dev);
+        if (sa != KVTC_OK) return sa;
+        work_bytes = kAttendScratchBytes;
+    }
     if (!work_dev || work_bytes < need || reinterpret_cast<uintptr_t>(work_dev) % 256) return KVTC_E_BUFSIZE;
     const int64_t nchunks = (s_end + kAttChunk - 1) / kAttChunk;
     if (hk->units > 0x7FFFFFFF || nchunks > 0x7FFFFFFF || hk->units > 65535) return KVTC_E_SHAPE;
@@ -405,7 +471,6 @@ int32_t kvtc_attend(const kvtc_tensor_ref *k, const kvtc_tensor_ref *v, const vo
     a.qf = reinterpret_cast<uint16_t *>(wb + wl.qf);
     a.qmul = reinterpret_cast<float *>(wb + wl.qmul);
     a.part = reinterpret_cast<float *>(wb + wl.part);
-    hipStream_t stream = static_cast<hipStream_t>(hip_stream);
     const unsigned U = static_cast<unsigned>(hk->units);
     hipLaunchKernelGGL(attend_prep_kernel, dim3(U), dim3(256), 0, stream, a);
     if (hipGetLastError() != hipSuccess) return KVTC_E_DEVICE;
@@ -422,4 +487,5 @@ int32_t kvtc_attend(const kvtc_tensor_ref *k, const kvtc_tensor_ref *v, const vo
     return hipGetLastError() == hipSuccess ? KVTC_OK : KVTC_E_DEVICE;
 }
 
-}  // extern "C"
+}  // namespace
+}  // namespace kvtc

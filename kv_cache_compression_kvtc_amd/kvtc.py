@@ -105,6 +105,8 @@ _sig = {
     "kvtc_attend_workspace": (_i32, [_vp, _vp, _i64, C.POINTER(_sz)]),
     "kvtc_attend": (_i32, [C.POINTER(TensorRef), C.POINTER(TensorRef), _vp, _i32, _P64, _i64, _vp, _P64, _vp,
                            _sz, _vp]),
+    "kvtc_attend_noalloc": (_i32, [C.POINTER(TensorRef), C.POINTER(TensorRef), _vp, _i32, _P64, _i64, _vp, _P64,
+                                   _vp]),
 }
 for _name, (_res, _args) in _sig.items():
     _f = getattr(_lib, _name)
@@ -498,6 +500,19 @@ class Attend:
         os_ = (C.c_int64 * 3)(*[int(x) for x in out.stride()])
         _check(_lib.kvtc_attend(C.byref(self._refs[0]), C.byref(self._refs[1]), q.data_ptr(), dtype, qs, s_end,
                                 out.data_ptr(), os_, self._work, self._work_bytes, self._stream), "kvtc_attend")
+        return out
+
+    def noalloc(self, q, s_end: int, out):
+        """The same attention through kvtc_attend_noalloc (the library's fixed
+        scratch instead of this object's workspace); out: fp16 [B, H, D]."""
+        import torch
+        dtype = {torch.float16: F16, torch.float32: F32}.get(q.dtype)
+        if dtype is None:
+            raise KVTCError(E_DTYPE, "kvtc_attend_noalloc")
+        qs = (C.c_int64 * 3)(*[int(x) for x in q.stride()])
+        os_ = (C.c_int64 * 3)(*[int(x) for x in out.stride()])
+        _check(_lib.kvtc_attend_noalloc(C.byref(self._refs[0]), C.byref(self._refs[1]), q.data_ptr(), dtype, qs,
+                                        s_end, out.data_ptr(), os_, self._stream), "kvtc_attend_noalloc")
         return out
 
 

@@ -542,3 +542,25 @@ def test_bytes_report_hand_worked_values():
                hi_fraction=0.5) == dict(
         fixed_payload=60, entropy_payload=0, entropy_table=0, stored_payload=60, basis=16896, quant_params=40,
         total=16996, pre_entropy=16996, fp16_equiv=1280, n_survived=32, units_entropy_coded=0)
+
+
+@no_device_only
+def test_attend_noalloc_rejects_a_call_beyond_its_scratch():
+    """kvtc_attend_noalloc refuses, before touching the device, a call whose
+    workspace would exceed KVTC_ATTEND_SCRATCH_BYTES (16 MiB)."""
+    w = synth.WORKLOADS[1]
+    st = O.fit(oracle_cfg(w), synth.generate(w, 0, 0, 256))
+    blob = blob_from_oracle(st)
+    fake = C.c_void_p(0x1000)        # never dereferenced: the size check fails first
+    big = 1 << 24                    # rows: partial sums of 2**15 chunks per unit
+    assert K.kvtc_attend_workspace(blob, blob, big) > 16 << 20
+    refs = []
+    for _ in range(2):
+        r = K.TensorRef()
+        r.state_host, r.state_dev, r.codes_dev, r.capacity = blob.ctypes.data, 0x1000, 0x1000, big
+        refs.append(r)
+    fn = _raw("kvtc_attend_noalloc")
+    fn.restype = C.c_int32
+    fn.argtypes = K._sig["kvtc_attend_noalloc"][1]
+    qs = (C.c_int64 * 3)(2 * 64, 64, 1)
+    assert fn(C.byref(refs[0]), C.byref(refs[1]), fake, K.F16, qs, big, fake, qs, None) == K.E_BUFSIZE
