@@ -376,6 +376,92 @@ def huffman_bits(counts) -> int:
     return total
 
 
+def huffman_lengths(counts) -> np.ndarray:
+    """Code length of every symbol in an optimal prefix code for these counts
+    (0 for absent symbols): the depths of the leaves of a Huffman tree.  A lone
+    symbol gets length 1.  Which of several optimal length sets comes out depends
+    on tie-breaking; the total ``sum(counts * lengths)`` does not and equals
+    ``huffman_bits(counts)``."""
+    counts = [int(c) for c in counts]
+    lengths = np.zeros(len(counts), dtype=np.int64)
+    live = [i for i, c in enumerate(counts) if c > 0]
+    if len(live) == 1:
+        lengths[live[0]] = 1
+    if len(live) <= 1:
+        return lengths
+    # heap of (weight, tiebreak, symbols under the node); every merge deepens its symbols by one
+    heap = [(counts[i], i, [i]) for i in live]
+    heapq.heapify(heap)
+    nxt = len(counts)
+    while len(heap) > 1:
+        wa, _, sa = heapq.heappop(heap)
+        wb, _, sb = heapq.heappop(heap)
+        for i in sa + sb:
+            lengths[i] += 1
+        heapq.heappush(heap, (wa + wb, nxt, sa + sb))
+        nxt += 1
+    return lengths
+
+
+def canonical_codes(lengths) -> np.ndarray:
+    """Canonical prefix code of the given lengths: symbols ordered by (length,
+    symbol value) take consecutive code values, the value doubling (shifted
+    left) whenever the length grows; codes are read most significant bit first."""
+    lengths = np.asarray(lengths, dtype=np.int64)
+    codes = np.zeros(len(lengths), dtype=np.int64)
+    order = sorted((int(l), i) for i, l in enumerate(lengths) if l > 0)
+    code, prev = 0, 0
+    for k, (l, i) in enumerate(order):
+        if k:
+            code += 1
+        code <<= (l - prev)
+        prev = l
+        codes[i] = code
+    return codes
+
+
+def entropy_encode_unit(codes: np.ndarray, bits, lengths) -> bytes:
+    """One unit's entropy-coded payload: for each stored component in order, its
+    codes of every row in row order, each written as its canonical prefix code,
+    most significant code bit first; the stream's bit p is bit p % 8 of byte
+    p // 8 (the little-endian bit order of the code rows); zero-padded to whole
+    bytes.  ``codes [S, r]`` per component, ``lengths[i]`` the symbol lengths of
+    component i (ignored for dropped components)."""
+    out = []
+    for i, b in enumerate(bits):
+        if not b:
+            continue
+        can = canonical_codes(lengths[i])
+        for c in codes[:, i]:
+            l, v = int(lengths[i][c]), int(can[c])
+            out.extend((v >> (l - 1 - k)) & 1 for k in range(l))
+    out.extend([0] * (-len(out) % 8))
+    return np.packbits(np.array(out, dtype=np.uint8), bitorder="little").tobytes()
+
+
+def entropy_decode_unit(payload: bytes, S: int, bits, lengths) -> np.ndarray:
+    """Inverse of entropy_encode_unit: codes ``[S, r]`` (zero for dropped
+    components), decoded bit by bit against the canonical code of each
+    component's lengths."""
+    stream = np.unpackbits(np.frombuffer(payload, dtype=np.uint8), bitorder="little")
+    codes = np.zeros((S, len(bits)), dtype=np.int64)
+    p = 0
+    for i, b in enumerate(bits):
+        if not b:
+            continue
+        can = canonical_codes(lengths[i])
+        table = {(int(lengths[i][c]), int(can[c])): c for c in range(len(can)) if lengths[i][c] > 0}
+        for s in range(S):
+            v, l = 0, 0
+            while (l, v) not in table:
+                v = (v << 1) | int(stream[p])
+                p += 1
+                l += 1
+                assert l <= 64, "not a prefix code of these lengths"
+            codes[s, i] = table[(l, v)]
+    return codes
+
+
 # --------------------------------------------------------------------------
 # whole-tensor state, append, fetch
 # --------------------------------------------------------------------------
@@ -674,6 +760,66 @@ def bytes_report(st: TensorState, rows: np.ndarray, params, S: int) -> BytesRepo
             rep.total += fixed + proj + qp
             rep.pre_entropy += fixed + proj + qp
     return rep
+
+
+def entropy_archive(st: TensorState, rows: np.ndarray, S: int, lengths=None):
+    """The entropy-coded storage of a DP tensor's first S rows (KVTC page, "Byte
+    accounting": order-0 Huffman per kept component with a fixed-width fallback).
+    Per unit, in unit order, byte aligned:
+      coded (when payload + table < fixed width): the table -- for each kept
+        component, 2**b bytes, byte k the code length of symbol k (0 if absent)
+        -- then entropy_encode_unit's payload;
+      fixed width: the rows' bits back to back (row s at bits [s*rb, (s+1)*rb) of
+        the unit's part), ceil(S * rb / 8) bytes.
+    ``lengths[u][i]`` gives the code lengths to use (any optimal set; default:
+    huffman_lengths).  Returns (archive bytes, [(coded, offset, size)] per unit)."""
+    assert st.cfg.mode == "dp"
+    parts, info, off = [], [], 0
+    for u in range(st.U):
+        r = int(st.r[u])
+        bits = [int(b) for b in st.bits[u, :r]]
+        rb = sum(bits)
+        codes = unpack_rows(rows[u, :S], bits)
+        lens = [None] * r
+        for i, b in enumerate(bits):
+            if b:
+                lens[i] = (np.asarray(lengths[u][i]) if lengths is not None else
+                           huffman_lengths(np.bincount(codes[:, i], minlength=2 ** b)))
+        table = b"".join(bytes(lens[i].astype(np.uint8)) for i, b in enumerate(bits) if b)
+        fixed = (S * rb + 7) // 8
+        payload = entropy_encode_unit(codes, bits, lens)
+        if len(payload) + len(table) < fixed:
+            part, coded = table + payload, True
+        else:
+            plane = np.unpackbits(np.asarray(rows[u, :S], np.uint8), axis=1, bitorder="little")[:, :rb]
+            part, coded = np.packbits(plane.reshape(-1), bitorder="little").tobytes(), False
+        parts.append(part)
+        info.append((coded, off, len(part)))
+        off += len(part)
+    return b"".join(parts), info
+
+
+def entropy_restore(st: TensorState, archive: bytes, info, S: int) -> np.ndarray:
+    """Inverse of entropy_archive: the packed rows ``[U, S, row_stride]``."""
+    rows = np.zeros((st.U, S, st.row_stride), np.uint8)
+    for u, (coded, off, size) in enumerate(info):
+        r = int(st.r[u])
+        bits = [int(b) for b in st.bits[u, :r]]
+        part = archive[off: off + size]
+        if coded:
+            lens, p = [None] * r, 0
+            for i, b in enumerate(bits):
+                if b:
+                    lens[i] = np.frombuffer(part[p: p + 2 ** b], np.uint8).astype(np.int64)
+                    p += 2 ** b
+            rows[u] = pack_rows(entropy_decode_unit(part[p:], S, bits, lens), bits, st.row_stride)
+        else:
+            rb = sum(bits)
+            plane = np.unpackbits(np.frombuffer(part, np.uint8), bitorder="little")[: S * rb].reshape(S, rb)
+            full = np.zeros((S, 8 * st.row_stride), np.uint8)
+            full[:, :rb] = plane
+            rows[u] = np.packbits(full, axis=1, bitorder="little")
+    return rows
 
 
 def full_seq_bytes(B: int, H: int, S: int, D: int) -> int:

@@ -370,6 +370,75 @@ def test_identity_basis_reduces_to_per_channel_affine_quantisation(rng):
         assert np.array_equal(out[:, d], lo32 + q * sc32)
 
 
+# ---------------------------------------------------------------- entropy-coded storage
+def test_huffman_lengths_textbook_and_optimal(rng):
+    """Textbook case: counts 45, 13, 12, 16, 9, 5 have the optimal lengths 1, 3, 3,
+    3, 4, 4 (224 bits); in general the lengths satisfy Kraft's equality and their
+    total is the Huffman cost."""
+    assert O.huffman_lengths([45, 13, 12, 16, 9, 5]).tolist() == [1, 3, 3, 3, 4, 4]
+    assert O.huffman_lengths([0, 7, 0]).tolist() == [0, 1, 0]
+    assert O.huffman_lengths([0, 0]).tolist() == [0, 0]
+    for _ in range(30):
+        c = rng.integers(0, 50, size=int(rng.integers(2, 40)))
+        c[rng.integers(0, len(c))] += 1
+        l = O.huffman_lengths(c)
+        assert int((c * l).sum()) == O.huffman_bits(c)
+        if (c > 0).sum() > 1:
+            assert sum(2.0 ** -int(x) for x in l if x) == 1.0
+
+
+def test_canonical_codes_hand_example():
+    """Lengths (2, 1, 3, 3) -> ordered by (length, symbol): 1:'0', 0:'10',
+    2:'110', 3:'111'."""
+    assert O.canonical_codes([2, 1, 3, 3]).tolist() == [0b10, 0b0, 0b110, 0b111]
+
+
+def test_entropy_stream_hand_example_and_round_trip(rng):
+    """One 2-bit component, codes 0 0 0 1 3 (counts 3, 1, 0, 1): lengths 1, 2, 0, 2,
+    canonical codes '0', '10', -, '11'; the stream 0 0 0 10 11 packs LSB first
+    into the byte 0b01101000 = 0x68.  Random units round-trip, and their payload
+    is ceil(sum of Huffman costs / 8) bytes."""
+    codes = np.array([[0], [0], [0], [1], [3]])
+    lengths = [O.huffman_lengths(np.bincount(codes[:, 0], minlength=4))]
+    assert lengths[0].tolist() == [1, 2, 0, 2]
+    pay = O.entropy_encode_unit(codes, [2], lengths)
+    assert pay == bytes([0x68])
+    assert np.array_equal(O.entropy_decode_unit(pay, 5, [2], lengths), codes)
+    for _ in range(5):
+        bits = [8, 0, 3, 1, 2, 4]
+        S = int(rng.integers(1, 300))
+        codes = np.stack([rng.geometric(0.3, size=S).clip(1, 2 ** b) - 1 if b else np.zeros(S, int)
+                          for b in bits], axis=1)
+        lengths = [O.huffman_lengths(np.bincount(codes[:, i], minlength=2 ** b)) if b else None
+                   for i, b in enumerate(bits)]
+        pay = O.entropy_encode_unit(codes, bits, lengths)
+        total = sum(O.huffman_bits(np.bincount(codes[:, i], minlength=2 ** b)) for i, b in enumerate(bits) if b)
+        assert len(pay) == (total + 7) // 8
+        assert np.array_equal(O.entropy_decode_unit(pay, S, bits, lengths), codes)
+
+
+def test_entropy_archive_size_is_the_byte_accounting_and_restores():
+    """The archive holds exactly the accounting's stored payload plus tables
+    (KVTC page, "Byte accounting"), takes the coded form exactly for the units
+    the accounting codes, and restores the packed rows bit for bit."""
+    kinds = set()
+    for wid, tensor, S in ((1, 0, 288), (1, 1, 288), (4, 0, 700), (1, 0, 40)):
+        w = synth.WORKLOADS[wid]
+        f = dict(w.__dict__)
+        f.update(B=2 if wid == 4 else w.B, s_prefill=256 if wid == 1 else 600)
+        w = synth.Workload(**f)
+        X = synth.generate(w, tensor, 0, max(S, w.s_prefill))
+        st = O.fit(_cfg(w), X[:, :, : w.s_prefill])
+        rows, _ = O.append(st, X[:, :, :S])
+        rep = O.bytes_report(st, rows, None, S)
+        arc, info = O.entropy_archive(st, rows, S)
+        assert len(arc) == rep.stored_payload + rep.entropy_table
+        assert sum(c for c, _, _ in info) == rep.units_entropy_coded
+        assert np.array_equal(O.entropy_restore(st, arc, info, S), rows)
+        kinds |= {c for c, _, _ in info}
+    assert kinds == {True, False}            # both the coded form and the fixed-width fallback
+
+
 # ---------------------------------------------------------------- refit mode
 def _identity_state(bits, D=4):
     """One unit whose basis is the identity and mean zero: latents are the rows."""
