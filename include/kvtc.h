@@ -407,6 +407,97 @@ int32_t kvtc_attend_noalloc(const kvtc_tensor_ref *k, const kvtc_tensor_ref *v, 
                             const int64_t q_strides[3], int64_t s_end, void *out_dev, const int64_t out_strides[3],
                             void *hip_stream);
 
+/* ------------------------------------------------------- entropy-coded storage
+ * KVTC page, "Byte accounting" (and _encode_survived_codes): the stored latents
+ * are order-0 Huffman coded per kept component, and a fixed-width packing is
+ * kept instead whenever coding does not pay.  kvtc_entropy_encode turns the
+ * first S rows of a DP tensor's code store into that storage, an archive in
+ * device memory; kvtc_entropy_decode restores the fixed-width rows from it,
+ * bit for bit, for kvtc_fetch.  Per unit, in unit order, byte aligned, the
+ * archive holds
+ *   coded (when stream + table < fixed width): the table -- for each stored
+ *     slot in order, 2^b bytes, byte k the code length of symbol k (0 if
+ *     absent) -- then the stream: for each slot in order, the canonical prefix
+ *     code of every row's code in row order, most significant code bit first,
+ *     stream bit p being bit p % 8 of byte p / 8;
+ *   fixed width: the rows' bits back to back (row s at bits [s*rb, (s+1)*rb)
+ *     of the unit's part), ceil(S * rb / 8) bytes.
+ * So the archive is exactly kvtc_bytes' stored_payload + entropy_table.  The
+ * canonical code of given lengths orders the symbols by (length, value) and
+ * gives them consecutive code values, doubling at every length step.  Code
+ * lengths come from a Huffman tree on the slot's code counts (ties broken
+ * towards lower weight, then lower node index), at most 32 bits.
+ *
+ * The index (host blob, and a device copy for decoding) records what a
+ * parallel decoder needs besides the archive: per unit the part's offset, size
+ * and form; per slot the canonical decode table; per slot and chunk of
+ * chunk_rows rows the bit position of the chunk's first code.  It is not part
+ * of the stored bytes the pages count (it is recomputable from the archive). */
+#define KVTC_ENTROPY_MAGIC   0x4554564Bu  /* "KVTE" little-endian */
+#define KVTC_ENTROPY_VERSION 1u
+#define KVTC_ENTROPY_MAX_LEN 32
+
+typedef struct kvtc_entropy_unit {
+    uint64_t offset;         /* byte offset of the unit's part in the archive */
+    uint64_t bytes;          /* size of the part */
+    uint32_t coded;          /* 1: table + stream, 0: fixed width */
+    uint32_t table_bytes;    /* sum of 2^b over the unit's slots (the table, when coded) */
+} kvtc_entropy_unit;
+
+typedef struct kvtc_entropy_dec {
+    uint32_t first[KVTC_ENTROPY_MAX_LEN + 1];   /* first canonical code of each length */
+    uint16_t count[KVTC_ENTROPY_MAX_LEN + 1];   /* symbols of each length */
+    uint16_t base[KVTC_ENTROPY_MAX_LEN + 1];    /* index of the first symbol of each length */
+    uint32_t sym_off;                           /* offset of the slot's sorted symbols in off_syms */
+    uint32_t max_len;
+} kvtc_entropy_dec;
+
+typedef struct kvtc_entropy_header {
+    uint32_t magic, version;
+    int64_t  S;              /* rows covered */
+    int64_t  units;
+    int32_t  kslots;         /* as the state's */
+    int32_t  chunk_rows;     /* rows per decode chunk */
+    int32_t  nchunks;        /* ceil(S / chunk_rows) */
+    int32_t  nsym;           /* symbol positions per unit: the largest sum of 2^b over a unit's slots */
+    uint64_t archive_bytes;  /* stored_payload + entropy_table of kvtc_bytes */
+    uint64_t payload_bytes;  /* coded streams and fixed-width parts */
+    uint64_t table_bytes;    /* tables of the coded units */
+    int64_t  units_coded;
+    uint64_t off_unit;       /* kvtc_entropy_unit [units] */
+    uint64_t off_dec;        /* kvtc_entropy_dec [units][kslots] */
+    uint64_t off_syms;       /* uint8 [units][nsym]: each slot's symbols sorted by (length, value) */
+    uint64_t off_chunk;      /* uint64 [units][kslots][nchunks]: archive bit position of each chunk's first code */
+    uint64_t total_bytes;
+} kvtc_entropy_header;
+
+/* Sizes (host): the device workspace kvtc_entropy_encode needs, a bound on the
+ * archive (the fixed-width total; an archive is never larger) and the index. */
+int32_t kvtc_entropy_bytes(const void *state_host, int64_t S, size_t *work_bytes, size_t *archive_bytes,
+                           size_t *index_bytes);
+
+/* Encode rows [0, S) of a DP tensor's device code store (device + host; waits
+ * for its stream): code counts per slot on the device, code lengths and
+ * canonical tables on the host, the archive written on the device.
+ *   codes_dev     the code store of `capacity` rows (layout of kvtc_append)
+ *   work_dev      workspace of kvtc_entropy_bytes() bytes, 256-byte aligned
+ *   archive_dev   archive_bytes >= the bound, 4-byte aligned; on return its
+ *                 first header.archive_bytes bytes are the archive
+ *   index_host    index_bytes >= kvtc_entropy_bytes()'s, receives the index
+ * KVTC_E_STATE for a group-head tensor; KVTC_E_SHAPE if a code would be longer
+ * than KVTC_ENTROPY_MAX_LEN bits (needs more than ~3.5 million rows). */
+int32_t kvtc_entropy_encode(const void *state_host, const void *state_dev, const void *codes_dev, int64_t capacity,
+                            int64_t S, void *work_dev, size_t work_bytes, void *archive_dev, size_t archive_bytes,
+                            void *index_host, size_t index_bytes, void *hip_stream);
+
+/* Decode an archive back into rows [0, S) of a code store (device, enqueued on
+ * the stream): the rows come back bit-identical to the encoded ones.
+ *   index_host/index_dev  the index kvtc_entropy_encode returned, on host and
+ *                         device (same bytes; the device copy 16-byte aligned) */
+int32_t kvtc_entropy_decode(const void *state_host, const void *state_dev, const void *index_host,
+                            const void *index_dev, const void *archive_dev, void *codes_dev, int64_t capacity,
+                            void *hip_stream);
+
 /* Storage accounting of one tensor over its first S rows (host).
  * KVTC page "Byte accounting" and the kvtc_bytes / pre_entropy_bytes
  * properties: order-0 Huffman per kept DP component, kept only when payload +

@@ -820,6 +820,79 @@ void range_from_minmax(double mn, double mx, int b, float *qmin, float *qscale) 
     *qscale = mx > mn ? static_cast<float>((mx - mn) / static_cast<double>((1 << b) - 1)) : 0.0f;
 }
 
+// ------------------------------------------------------------ entropy coding
+// Code lengths of an optimal prefix code for counts[0..n) (the depths of a
+// Huffman tree's leaves; 0 for absent symbols, 1 for a lone symbol).  Nodes
+// merge lowest weight first, ties towards the lower node index (symbols are
+// nodes 0..n-1, merged nodes n, n+1, ... in creation order).  Returns the
+// longest length.
+int huffman_code_lengths(const uint32_t *counts, int n, uint8_t *len) {
+    std::fill(len, len + n, 0);
+    typedef std::pair<uint64_t, int> Node;               // (weight, index)
+    std::priority_queue<Node, std::vector<Node>, std::greater<Node>> q;
+    for (int i = 0; i < n; ++i)
+        if (counts[i]) q.push({counts[i], i});
+    if (q.empty()) return 0;
+    if (q.size() == 1) {
+        len[q.top().second] = 1;
+        return 1;
+    }
+    std::vector<int> parent(2 * n, -1);
+    int next = n;
+    while (q.size() > 1) {
+        const Node a = q.top();
+        q.pop();
+        const Node b = q.top();
+        q.pop();
+        parent[a.second] = next;
+        parent[b.second] = next;
+        q.push({a.first + b.first, next++});
+    }
+    // depths: a merged node's parent was created after it, so walk from the root down
+    std::vector<int> depth(next, 0);
+    for (int v = next - 2; v >= n; --v) depth[v] = depth[parent[v]] + 1;
+    int longest = 0;
+    for (int i = 0; i < n; ++i)
+        if (counts[i]) {
+            const int d = depth[parent[i]] + 1;
+            len[i] = static_cast<uint8_t>(std::min(d, 255));
+            longest = std::max(longest, d);
+        }
+    return longest;
+}
+
+// The encoder's shape of a DP tensor over S rows: symbol position of each slot
+// (prefix of 2^b in slot order), symbol positions per unit, chunks.
+struct EntropyShape {
+    std::vector<uint32_t> sym_off;     // [U][kslots]
+    int nsym = 1, nchunks = 0;
+};
+
+EntropyShape entropy_shape(const kvtc_state_header *h, const void *blob, int64_t S) {
+    EntropyShape e;
+    const auto *ui = section<kvtc_unit_info>(blob, h->off_unit);
+    const auto *sb = section<uint32_t>(blob, h->off_slot_bits);
+    e.sym_off.assign(static_cast<size_t>(h->units) * h->kslots, 0);
+    for (int64_t u = 0; u < h->units; ++u) {
+        uint32_t o = 0;
+        for (int j = 0; j < ui[u].n_slots; ++j) {
+            e.sym_off[u * h->kslots + j] = o;
+            o += 1u << (sb[u * h->kslots + j] >> 24);
+        }
+        e.nsym = std::max<int>(e.nsym, static_cast<int>(o));
+    }
+    e.nchunks = static_cast<int>((S + kEntropyChunk - 1) / kEntropyChunk);
+    return e;
+}
+
+// Upper bound of the archive: the fixed-width parts of all units, whole words.
+uint64_t entropy_archive_bound(const kvtc_state_header *h, const void *blob, int64_t S) {
+    const auto *ui = section<kvtc_unit_info>(blob, h->off_unit);
+    uint64_t b = 0;
+    for (int64_t u = 0; u < h->units; ++u) b += (static_cast<uint64_t>(S) * ui[u].row_bits + 7) / 8;
+    return align_up(b + 4, 4);
+}
+
 }  // namespace
 }  // namespace kvtc
 
@@ -1052,6 +1125,234 @@ int32_t kvtc_fit_device(const kvtc_config *cfg, const void *rows_dev, int32_t dt
     } catch (const std::bad_alloc &) {
         return KVTC_E_ARG;
     }
+}
+
+// ------------------------------------------------------------ entropy-coded storage
+int32_t kvtc_entropy_bytes(const void *state_host, int64_t S, size_t *work_bytes, size_t *archive_bytes,
+                           size_t *index_bytes) {
+    const kvtc_state_header *h = nullptr;
+    int32_t st = check_state(state_host, &h);
+    if (st != KVTC_OK) return st;
+    if (h->mode != KVTC_MODE_DP) return KVTC_E_STATE;
+    if (S < 0) return KVTC_E_ARG;
+    try {
+        const EntropyShape e = entropy_shape(h, state_host, S);
+        if (work_bytes) *work_bytes = entropy_work_layout(h->units, h->kslots, e.nsym, e.nchunks).total;
+        if (archive_bytes) *archive_bytes = entropy_archive_bound(h, state_host, S);
+        if (index_bytes) *index_bytes = entropy_index_layout(h->units, h->kslots, e.nsym, e.nchunks).total;
+    } catch (const std::bad_alloc &) {
+        return KVTC_E_ARG;
+    }
+    return KVTC_OK;
+}
+
+int32_t kvtc_entropy_encode(const void *state_host, const void *state_dev, const void *codes_dev, int64_t capacity,
+                            int64_t S, void *work_dev, size_t work_bytes, void *archive_dev, size_t archive_bytes,
+                            void *index_host, size_t index_bytes, void *hip_stream) {
+    const kvtc_state_header *h = nullptr;
+    int32_t st = check_state(state_host, &h);
+    if (st != KVTC_OK) return st;
+    if (h->mode != KVTC_MODE_DP) return KVTC_E_STATE;
+    if (!state_dev || !index_host) return KVTC_E_ARG;
+    if (S < 0 || capacity < 0) return KVTC_E_ARG;
+    if (S > capacity) return KVTC_E_CAPACITY;
+    if (h->units > 65535) return KVTC_E_SHAPE;
+    if (S > 0 && h->row_stride > 0 && (!codes_dev || reinterpret_cast<uintptr_t>(codes_dev) % 4)) return KVTC_E_ARG;
+    try {
+        const EntropyShape e = entropy_shape(h, state_host, S);
+        const int64_t U = h->units;
+        const int ks = h->kslots, nsym = e.nsym, nch = e.nchunks;
+        const EntropyWorkLayout W = entropy_work_layout(U, ks, nsym, nch);
+        const EntropyIndexLayout I = entropy_index_layout(U, ks, nsym, nch);
+        const uint64_t bound = entropy_archive_bound(h, state_host, S);
+        if (!work_dev || work_bytes < W.total || reinterpret_cast<uintptr_t>(work_dev) % kSectionAlign) return KVTC_E_BUFSIZE;
+        if (!archive_dev || archive_bytes < bound || reinterpret_cast<uintptr_t>(archive_dev) % 4) return KVTC_E_BUFSIZE;
+        if (index_bytes < I.total) return KVTC_E_BUFSIZE;
+        const auto *ui = section<kvtc_unit_info>(state_host, h->off_unit);
+        const auto *sbh = section<uint32_t>(state_host, h->off_slot_bits);
+        const char *sd = static_cast<const char *>(state_dev);
+        char *w = static_cast<char *>(work_dev);
+        EntropyDevArgs a{};
+        a.ui = reinterpret_cast<const kvtc_unit_info *>(sd + h->off_unit);
+        a.sbits = reinterpret_cast<const uint32_t *>(sd + h->off_slot_bits);
+        a.codes = static_cast<uint8_t *>(const_cast<void *>(codes_dev));
+        a.capacity = capacity;
+        a.S = S;
+        a.units = U;
+        a.kslots = ks;
+        a.row_stride = h->row_stride;
+        a.nsym = nsym;
+        a.nchunks = nch;
+        a.sym_off = reinterpret_cast<const uint32_t *>(w + W.sym_off);
+        a.counts = reinterpret_cast<uint32_t *>(w + W.counts);
+        a.enc_code = reinterpret_cast<const uint32_t *>(w + W.enc_code);
+        a.enc_len = reinterpret_cast<const uint8_t *>(w + W.enc_len);
+        a.unit = reinterpret_cast<const kvtc_entropy_unit *>(w + W.units);
+        a.slot_pos = reinterpret_cast<const uint64_t *>(w + W.slot_pos);
+        a.chunk_bits = reinterpret_cast<uint32_t *>(w + W.chunk_bits);
+        a.chunk_pos = reinterpret_cast<uint64_t *>(w + W.chunk_pos);
+        a.archive = static_cast<uint32_t *>(archive_dev);
+        a.archive_words = archive_bytes / 4;
+        a.stream = hip_stream;
+        // 1. counts of every slot's codes over rows [0, S), on the device
+        std::vector<uint32_t> counts(static_cast<size_t>(U) * nsym);
+        if (fit_device_upload(w + W.sym_off, e.sym_off.data(), e.sym_off.size() * 4, hip_stream) != KVTC_OK)
+            return KVTC_E_DEVICE;
+        st = entropy_device_counts(a, counts.data());
+        if (st != KVTC_OK) return st;
+        // 2. code lengths, canonical codes and decode tables per slot; the unit forms
+        std::memset(index_host, 0, I.total);
+        auto *hdr = static_cast<kvtc_entropy_header *>(index_host);
+        auto *units = section_mut<kvtc_entropy_unit>(index_host, I.off_unit);
+        auto *dec = section_mut<kvtc_entropy_dec>(index_host, I.off_dec);
+        auto *syms = section_mut<uint8_t>(index_host, I.off_syms);
+        auto *chunk = section_mut<uint64_t>(index_host, I.off_chunk);
+        std::vector<uint32_t> enc_code(static_cast<size_t>(U) * nsym, 0);
+        std::vector<uint8_t> enc_len(static_cast<size_t>(U) * nsym, 0);
+        std::vector<uint64_t> slot_bits(static_cast<size_t>(U) * ks, 0), slot_pos(static_cast<size_t>(U) * ks, 0);
+        std::atomic<bool> too_long{false};
+        if (!parallel_for(U, [&](int64_t u) {
+                for (int j = 0; j < ui[u].n_slots; ++j) {
+                    const int b = static_cast<int>(sbh[u * ks + j] >> 24), n = 1 << b;
+                    const size_t so = static_cast<size_t>(u) * nsym + e.sym_off[u * ks + j];
+                    const int longest = huffman_code_lengths(&counts[so], n, &enc_len[so]);
+                    if (longest > KVTC_ENTROPY_MAX_LEN) {
+                        too_long = true;
+                        return;
+                    }
+                    kvtc_entropy_dec &d = dec[u * ks + j];
+                    d.sym_off = e.sym_off[u * ks + j];
+                    d.max_len = static_cast<uint32_t>(longest);
+                    for (int k = 0; k < n; ++k) d.count[enc_len[so + k]] += enc_len[so + k] ? 1 : 0;
+                    uint32_t code = 0, idx = 0;
+                    for (int L = 1; L <= KVTC_ENTROPY_MAX_LEN; ++L) {
+                        d.first[L] = code;
+                        d.base[L] = static_cast<uint16_t>(idx);
+                        code = (code + d.count[L]) << 1;
+                        idx += d.count[L];
+                    }
+                    // symbols in (length, value) order take consecutive codes
+                    std::vector<uint32_t> next(d.first, d.first + KVTC_ENTROPY_MAX_LEN + 1);
+                    std::vector<uint16_t> put(d.base, d.base + KVTC_ENTROPY_MAX_LEN + 1);
+                    uint64_t bits = 0;
+                    for (int L = 1; L <= KVTC_ENTROPY_MAX_LEN; ++L)
+                        for (int k = 0; k < n; ++k)
+                            if (enc_len[so + k] == L) {
+                                const uint32_t c = next[L]++;
+                                syms[static_cast<size_t>(u) * nsym + d.sym_off + put[L]++] = static_cast<uint8_t>(k);
+                                uint32_t rev = 0;                 // emitted most significant bit first
+                                for (int t = 0; t < L; ++t) rev |= ((c >> t) & 1u) << (L - 1 - t);
+                                enc_code[so + k] = rev;
+                                bits += static_cast<uint64_t>(counts[so + k]) * L;
+                            }
+                    slot_bits[u * ks + j] = bits;
+                }
+            }))
+            return KVTC_E_ARG;
+        if (too_long) return KVTC_E_SHAPE;
+        uint64_t off = 0, payload = 0, tables = 0;
+        int64_t coded_units = 0;
+        for (int64_t u = 0; u < U; ++u) {
+            uint64_t hbits = 0, table = 0;
+            for (int j = 0; j < ui[u].n_slots; ++j) {
+                hbits += slot_bits[u * ks + j];
+                table += 1ull << (sbh[u * ks + j] >> 24);
+            }
+            const uint64_t fixed = (static_cast<uint64_t>(S) * ui[u].row_bits + 7) / 8;
+            const uint64_t coded_payload = (hbits + 7) / 8;
+            kvtc_entropy_unit &un = units[u];
+            un.offset = off;
+            un.table_bytes = static_cast<uint32_t>(table);
+            un.coded = coded_payload + table < fixed ? 1u : 0u;
+            un.bytes = un.coded ? table + coded_payload : fixed;
+            if (un.coded) {
+                uint64_t p = 8 * (off + table);
+                for (int j = 0; j < ui[u].n_slots; ++j) {
+                    slot_pos[u * ks + j] = p;
+                    p += slot_bits[u * ks + j];
+                }
+                payload += coded_payload;
+                tables += table;
+                ++coded_units;
+            } else {
+                payload += fixed;
+            }
+            off += un.bytes;
+        }
+        hdr->magic = KVTC_ENTROPY_MAGIC;
+        hdr->version = KVTC_ENTROPY_VERSION;
+        hdr->S = S;
+        hdr->units = U;
+        hdr->kslots = ks;
+        hdr->chunk_rows = kEntropyChunk;
+        hdr->nchunks = nch;
+        hdr->nsym = nsym;
+        hdr->archive_bytes = off;
+        hdr->payload_bytes = payload;
+        hdr->table_bytes = tables;
+        hdr->units_coded = coded_units;
+        hdr->off_unit = I.off_unit;
+        hdr->off_dec = I.off_dec;
+        hdr->off_syms = I.off_syms;
+        hdr->off_chunk = I.off_chunk;
+        hdr->total_bytes = I.total;
+        // 3. the archive, on the device; the chunk positions come back into the index
+        return entropy_device_encode(a, enc_code.data(), enc_len.data(), units, slot_pos.data(), chunk);
+    } catch (const std::bad_alloc &) {
+        return KVTC_E_ARG;
+    }
+}
+
+int32_t kvtc_entropy_decode(const void *state_host, const void *state_dev, const void *index_host,
+                            const void *index_dev, const void *archive_dev, void *codes_dev, int64_t capacity,
+                            void *hip_stream) {
+    const kvtc_state_header *h = nullptr;
+    int32_t st = check_state(state_host, &h);
+    if (st != KVTC_OK) return st;
+    if (h->mode != KVTC_MODE_DP) return KVTC_E_STATE;
+    if (!state_dev || !index_host || !index_dev || reinterpret_cast<uintptr_t>(index_dev) % 16) return KVTC_E_ARG;
+    const auto *hdr = static_cast<const kvtc_entropy_header *>(index_host);
+    if (hdr->magic != KVTC_ENTROPY_MAGIC || hdr->version != KVTC_ENTROPY_VERSION || hdr->units != h->units ||
+        hdr->kslots != h->kslots || hdr->chunk_rows != kEntropyChunk || hdr->S < 0 ||
+        hdr->nchunks != (hdr->S + kEntropyChunk - 1) / kEntropyChunk)
+        return KVTC_E_STATE;
+    try {
+        const EntropyShape e = entropy_shape(h, state_host, hdr->S);
+        const EntropyIndexLayout I = entropy_index_layout(h->units, h->kslots, e.nsym, e.nchunks);
+        if (hdr->nsym != e.nsym || hdr->off_unit != I.off_unit || hdr->off_dec != I.off_dec ||
+            hdr->off_syms != I.off_syms || hdr->off_chunk != I.off_chunk || hdr->total_bytes != I.total ||
+            hdr->archive_bytes > entropy_archive_bound(h, state_host, hdr->S))
+            return KVTC_E_STATE;
+    } catch (const std::bad_alloc &) {
+        return KVTC_E_ARG;
+    }
+    if (capacity < 0) return KVTC_E_ARG;
+    if (hdr->S > capacity) return KVTC_E_CAPACITY;
+    if (hdr->S == 0) return KVTC_OK;
+    if (h->row_stride > 0 && (!codes_dev || reinterpret_cast<uintptr_t>(codes_dev) % 4)) return KVTC_E_ARG;
+    if (!archive_dev || reinterpret_cast<uintptr_t>(archive_dev) % 4) return KVTC_E_ARG;
+    if (h->units > 65535) return KVTC_E_SHAPE;
+    const char *sd = static_cast<const char *>(state_dev);
+    const char *ix = static_cast<const char *>(index_dev);
+    EntropyDevArgs a{};
+    a.ui = reinterpret_cast<const kvtc_unit_info *>(sd + h->off_unit);
+    a.sbits = reinterpret_cast<const uint32_t *>(sd + h->off_slot_bits);
+    a.codes = static_cast<uint8_t *>(codes_dev);
+    a.capacity = capacity;
+    a.S = hdr->S;
+    a.units = h->units;
+    a.kslots = h->kslots;
+    a.row_stride = h->row_stride;
+    a.nsym = hdr->nsym;
+    a.nchunks = hdr->nchunks;
+    a.unit = reinterpret_cast<const kvtc_entropy_unit *>(ix + hdr->off_unit);
+    a.dec = reinterpret_cast<const kvtc_entropy_dec *>(ix + hdr->off_dec);
+    a.syms = reinterpret_cast<const uint8_t *>(ix + hdr->off_syms);
+    a.chunk_pos = reinterpret_cast<uint64_t *>(const_cast<char *>(ix + hdr->off_chunk));
+    a.archive = static_cast<uint32_t *>(const_cast<void *>(archive_dev));
+    a.archive_words = (hdr->archive_bytes + 3) / 4;
+    a.stream = hip_stream;
+    return entropy_device_decode(a);
 }
 
 int32_t kvtc_state_build(const kvtc_config *cfg, int64_t B, int64_t H, int32_t rmax,

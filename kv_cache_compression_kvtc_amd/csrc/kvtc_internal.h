@@ -147,4 +147,89 @@ int32_t fit_device_moments(const FitDeviceRows &r, double *mean_host, double *co
 int32_t fit_device_ranges(const FitDeviceRows &r, const float *mu32_host, const float *basis_slots_host,
                           const int32_t *n_slots_host, double *mn_host, double *mx_host);
 
+// ------------------------------------------------------------ entropy-coded storage
+// Layouts shared by the host half (kvtc_host.cpp: code lengths, canonical
+// tables, index) and the device half (kvtc_entropy.hip: counts, archive).
+constexpr int kEntropyChunk = 256;      // rows per decode chunk
+
+struct EntropyIndexLayout {
+    uint64_t off_unit, off_dec, off_syms, off_chunk, total;
+};
+
+inline EntropyIndexLayout entropy_index_layout(int64_t U, int kslots, int nsym, int nchunks) {
+    EntropyIndexLayout L{};
+    uint64_t o = align_up(sizeof(kvtc_entropy_header), kSectionAlign);
+    auto take = [&](uint64_t bytes) {
+        const uint64_t at = o;
+        o = align_up(o + (bytes ? bytes : 1), kSectionAlign);
+        return at;
+    };
+    const uint64_t u = static_cast<uint64_t>(U);
+    L.off_unit = take(u * sizeof(kvtc_entropy_unit));
+    L.off_dec = take(u * kslots * sizeof(kvtc_entropy_dec));
+    L.off_syms = take(u * static_cast<uint64_t>(nsym));
+    L.off_chunk = take(u * kslots * static_cast<uint64_t>(nchunks) * 8);
+    L.total = o;
+    return L;
+}
+
+// Device workspace of the encoder, sections 256-byte aligned.
+struct EntropyWorkLayout {
+    uint64_t sym_off, counts, enc_code, enc_len, units, slot_pos, chunk_bits, chunk_pos, total;
+};
+
+inline EntropyWorkLayout entropy_work_layout(int64_t U, int kslots, int nsym, int nchunks) {
+    EntropyWorkLayout L{};
+    uint64_t o = 0;
+    auto take = [&](uint64_t bytes) {
+        const uint64_t at = o;
+        o = align_up(o + (bytes ? bytes : 1), kSectionAlign);
+        return at;
+    };
+    const uint64_t u = static_cast<uint64_t>(U), k = static_cast<uint64_t>(kslots), n = static_cast<uint64_t>(nsym);
+    L.sym_off = take(u * k * 4);
+    L.counts = take(u * n * 4);
+    L.enc_code = take(u * n * 4);
+    L.enc_len = take(u * n);
+    L.units = take(u * sizeof(kvtc_entropy_unit));
+    L.slot_pos = take(u * k * 8);
+    L.chunk_bits = take(u * k * static_cast<uint64_t>(nchunks) * 4);
+    L.chunk_pos = take(u * k * static_cast<uint64_t>(nchunks) * 8);
+    L.total = o;
+    return L;
+}
+
+// What the device half of the encoder and decoder works on (device pointers).
+struct EntropyDevArgs {
+    const kvtc_unit_info *ui;          // state: per unit
+    const uint32_t *sbits;             // state: [U][kslots] bit offset | width << 24
+    uint8_t *codes;                    // code store [U][capacity][row_stride]
+    int64_t capacity, S, units;
+    int kslots, row_stride, nsym, nchunks;
+    const uint32_t *sym_off;           // [U][kslots] first symbol position of each slot
+    uint32_t *counts;                  // [U][nsym]
+    const uint32_t *enc_code;          // [U][nsym] bit-reversed canonical codes
+    const uint8_t *enc_len;            // [U][nsym] code lengths
+    const kvtc_entropy_unit *unit;     // [U]
+    const uint64_t *slot_pos;          // [U][kslots] archive bit position of each slot's stream
+    uint32_t *chunk_bits;              // [U][kslots][nchunks]
+    uint64_t *chunk_pos;               // [U][kslots][nchunks]
+    const kvtc_entropy_dec *dec;       // [U][kslots]
+    const uint8_t *syms;               // [U][nsym]
+    uint32_t *archive;                 // 32-bit words
+    uint64_t archive_words;
+    void *stream;                      // hipStream_t
+};
+
+// Host -> device copy on the stream (enqueued).
+int32_t fit_device_upload(void *dst_dev, const void *src_host, size_t bytes, void *stream);
+// Code counts [U][nsym] of rows [0, S) into counts_host (waits for the stream).
+int32_t entropy_device_counts(const EntropyDevArgs &a, uint32_t *counts_host);
+// The archive from the uploaded tables; chunk positions into chunk_pos_host (waits).
+int32_t entropy_device_encode(const EntropyDevArgs &a, const uint32_t *enc_code_host, const uint8_t *enc_len_host,
+                              const kvtc_entropy_unit *units_host, const uint64_t *slot_pos_host,
+                              uint64_t *chunk_pos_host);
+// Rows [0, S) of the code store from the archive (enqueued only).
+int32_t entropy_device_decode(const EntropyDevArgs &a);
+
 }  // namespace kvtc

@@ -67,6 +67,18 @@ class BytesReport(C.Structure):
         return {f[0]: int(getattr(self, f[0])) for f in self._fields_}
 
 
+class EntropyHeader(C.Structure):
+    _fields_ = [("magic", C.c_uint32), ("version", C.c_uint32), ("S", C.c_int64), ("units", C.c_int64),
+                ("kslots", C.c_int32), ("chunk_rows", C.c_int32), ("nchunks", C.c_int32), ("nsym", C.c_int32),
+                ("archive_bytes", C.c_uint64), ("payload_bytes", C.c_uint64), ("table_bytes", C.c_uint64),
+                ("units_coded", C.c_int64), ("off_unit", C.c_uint64), ("off_dec", C.c_uint64),
+                ("off_syms", C.c_uint64), ("off_chunk", C.c_uint64), ("total_bytes", C.c_uint64)]
+
+
+class EntropyUnit(C.Structure):
+    _fields_ = [("offset", C.c_uint64), ("bytes", C.c_uint64), ("coded", C.c_uint32), ("table_bytes", C.c_uint32)]
+
+
 class TensorRef(C.Structure):
     """One tensor's operands of a paired call (kvtc_tensor_ref)."""
     _fields_ = [("state_host", C.c_void_p), ("state_dev", C.c_void_p), ("codes_dev", C.c_void_p),
@@ -100,6 +112,9 @@ _sig = {
     "kvtc_fetch_kv": (_i32, [C.POINTER(TensorRef), C.POINTER(TensorRef), _i64, _i64, _vp]),
     "kvtc_fetch_kv_probe": (_i32, [C.POINTER(TensorRef), C.POINTER(TensorRef), _i64, _i64, _vp]),
     "kvtc_refit_bytes": (_i32, [_vp, _i64, C.POINTER(_sz), C.POINTER(_sz)]),
+    "kvtc_entropy_bytes": (_i32, [_vp, _i64, C.POINTER(_sz), C.POINTER(_sz), C.POINTER(_sz)]),
+    "kvtc_entropy_encode": (_i32, [_vp, _vp, _vp, _i64, _i64, _vp, _sz, _vp, _sz, _vp, _sz, _vp]),
+    "kvtc_entropy_decode": (_i32, [_vp, _vp, _vp, _vp, _vp, _vp, _i64, _vp]),
     "kvtc_append_refit": (_i32, [_vp, _vp, _vp, _i32, _P64, _i64, _i64, _i64, _i64, _vp, _vp, _vp, _i64, _vp]),
     "kvtc_fetch_refit": (_i32, [_vp, _vp, _vp, _vp, _i64, _i64, _i64, _vp, _P64, _vp]),
     "kvtc_attend_workspace": (_i32, [_vp, _vp, _i64, C.POINTER(_sz)]),
@@ -447,6 +462,55 @@ class RefitStore:
         raw = self.refit.cpu().numpy()
         get = lambda name: raw[sec[name][0]: sec[name][0] + sec[name][1]].view(np.float32).reshape(h.units, h.kslots)
         return get("qmin32").copy(), get("qscale32").copy()
+
+
+# ---------------------------------------------------------------- entropy-coded storage
+def kvtc_entropy_bytes(blob: np.ndarray, S: int):
+    """(device workspace, archive bound, index) bytes of entropy coding S rows."""
+    _check_blob(blob, "kvtc_entropy_bytes")
+    w, a, i = C.c_size_t(0), C.c_size_t(0), C.c_size_t(0)
+    _check(_lib.kvtc_entropy_bytes(_host_ptr(blob), S, C.byref(w), C.byref(a), C.byref(i)), "kvtc_entropy_bytes")
+    return w.value, a.value, i.value
+
+
+class EntropyArchive:
+    """The entropy-coded storage of rows [0, S) of a DP tensor's device code
+    store (kvtc_entropy_encode): ``archive`` (a device uint8 tensor holding
+    ``header.archive_bytes`` bytes) and ``index`` (host uint8 array) with its
+    device copy.  ``decode(codes)`` restores the rows into a code store."""
+
+    def __init__(self, blob, blob_dev, codes, capacity: int, S: int, stream=None):
+        import torch
+        _check_buffers(blob, blob_dev, codes, None, capacity, "EntropyArchive")
+        wb, ab, ib = kvtc_entropy_bytes(blob, S)
+        dev = blob_dev.device
+        work = torch.empty(wb + 256, dtype=torch.uint8, device=dev)
+        woff = (-work.data_ptr()) % 256
+        self.archive = torch.empty(ab, dtype=torch.uint8, device=dev)
+        self.index = np.zeros(ib, dtype=np.uint8)
+        self.blob, self.blob_dev, self.S = blob, blob_dev, S
+        _check(_lib.kvtc_entropy_encode(_host_ptr(blob), _dev_ptr(blob_dev), _dev_ptr(codes), capacity, S,
+                                        work.data_ptr() + woff, wb, _dev_ptr(self.archive), ab, _host_ptr(self.index),
+                                        ib, _stream_ptr(stream)), "kvtc_entropy_encode")
+        self.header = EntropyHeader.from_buffer_copy(self.index[: C.sizeof(EntropyHeader)].tobytes())
+        self.index_dev = torch.from_numpy(self.index).to(dev)
+
+    def units(self):
+        h = self.header
+        return [EntropyUnit.from_buffer_copy(self.index[h.off_unit + C.sizeof(EntropyUnit) * u:
+                                                        h.off_unit + C.sizeof(EntropyUnit) * (u + 1)].tobytes())
+                for u in range(h.units)]
+
+    def bytes(self) -> np.ndarray:
+        """The archive's stored bytes, on the host."""
+        return self.archive[: self.header.archive_bytes].cpu().numpy()
+
+    def decode(self, codes, capacity: int, stream=None):
+        """kvtc_entropy_decode into the code store ``codes`` (rows [0, S))."""
+        _check_buffers(self.blob, self.blob_dev, codes, None, capacity, "kvtc_entropy_decode")
+        _check(_lib.kvtc_entropy_decode(_host_ptr(self.blob), _dev_ptr(self.blob_dev), _host_ptr(self.index),
+                                        _dev_ptr(self.index_dev), _dev_ptr(self.archive), _dev_ptr(codes), capacity,
+                                        _stream_ptr(stream)), "kvtc_entropy_decode")
 
 
 def kvtc_attend_workspace(blob_k: np.ndarray, blob_v: np.ndarray, s_end: int) -> int:
