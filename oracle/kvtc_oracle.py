@@ -680,14 +680,20 @@ def attend_rows(Kh: np.ndarray, Vh: np.ndarray, q: np.ndarray) -> np.ndarray:
 
 def attend(st_k: TensorState, rows_k: np.ndarray, st_v: TensorState, rows_v: np.ndarray,
            q: np.ndarray, params_k=None, params_v=None) -> np.ndarray:
-    """Decode attention of queries ``q [B, H, D]`` over the reconstructed keys
-    and values of the stored rows: float64 ``[B, H, D]``."""
+    """Decode attention of queries ``q [B, Hq, D]`` over the reconstructed keys
+    and values of the stored rows: float64 ``[B, Hq, D]``.  Hq is a multiple G
+    of the stored heads H; query head hq attends KV head hq // G (grouped-query
+    attention with consecutive query heads sharing a KV head; G = 1 is one
+    query per head).  Group-head tensors are reconstructed as fetch does."""
     Kh, Vh = fetch(st_k, rows_k, params_k), fetch(st_v, rows_v, params_v)
     B, H = Kh.shape[:2]
-    out = np.zeros((B, H, Kh.shape[3]), np.float64)
+    Hq = q.shape[1]
+    assert Hq % H == 0, "query heads must be a multiple of the stored heads"
+    G = Hq // H
+    out = np.zeros((B, Hq, Kh.shape[3]), np.float64)
     for b in range(B):
-        for h in range(H):
-            out[b, h] = attend_rows(Kh[b, h], Vh[b, h], q[b, h])
+        for hq in range(Hq):
+            out[b, hq] = attend_rows(Kh[b, hq // G], Vh[b, hq // G], q[b, hq])
     return out
 
 

@@ -727,3 +727,53 @@ def test_frozen_mode_clamp_rate(wid, tensor):
     print(f"clamp rate {w.name} tensor {tensor}: {rate:.2e}")
     assert O.clamp_fraction(st, X[:, :, : w.s_prefill]) == 0.0
     assert rate < 0.01
+
+
+
+def _two_head_caches(mode):
+    """Stored keys and values of 2 heads (one group-head unit in mixed mode)."""
+    w = synth.WORKLOADS[1]
+    f = dict(w.__dict__)
+    f.update(H=2, s_prefill=200, s_total=200)
+    if mode == "mixed":
+        f.update(mode="mixed", heads_per_unit=2, rank=48, group_size=16)
+    w = synth.Workload(**f)
+    out = []
+    for tensor in (0, 1):
+        X = synth.generate(w, tensor)
+        st = O.fit(_cfg(w), X)
+        rows, params = O.append(st, X)
+        out.append((st, rows, params))
+    return out
+
+
+@pytest.mark.parametrize("mode", ["dp", "mixed"])
+def test_attend_grouped_query_heads(mode, rng):
+    """Grouped-query attention: with Hq = G * H query heads, query head hq sees
+    KV head hq // G; G = 1 is the plain per-head attention, equal query heads of
+    one group give equal outputs, and two query heads of different groups see
+    different caches.  Holds for a group-head cache (its heads reconstructed
+    from the shared projection) as for a per-head one."""
+    (sk, rk, pk), (sv, rv, pv) = _two_head_caches(mode)
+    D = sk.D
+    Kh, Vh = O.fetch(sk, rk, pk), O.fetch(sv, rv, pv)
+    q1 = rng.normal(size=(1, 2, D))
+    o1 = O.attend(sk, rk, sv, rv, q1, pk, pv)
+    for h in range(2):
+        assert np.array_equal(o1[0, h], O.attend_rows(Kh[0, h], Vh[0, h], q1[0, h]))
+    G = 3
+    q3 = rng.normal(size=(1, 2 * G, D))
+    q3[0, 1] = q3[0, 0]
+    o3 = O.attend(sk, rk, sv, rv, q3, pk, pv)
+    assert np.array_equal(o3[0, 0], o3[0, 1])
+    for hq in range(2 * G):
+        assert np.array_equal(o3[0, hq], O.attend_rows(Kh[0, hq // G], Vh[0, hq // G], q3[0, hq]))
+    # the same query in head 0 and head 1 of the cache attends different rows
+    q3[0, G] = q3[0, 0]
+    o3 = O.attend(sk, rk, sv, rv, q3, pk, pv)
+    assert not np.allclose(o3[0, 0], o3[0, G])
+    # a zero query is the plain mean of its KV head's values
+    z = np.zeros((1, 2 * G, D))
+    oz = O.attend(sk, rk, sv, rv, z, pk, pv)
+    for hq in range(2 * G):
+        assert np.allclose(oz[0, hq], Vh[0, hq // G].mean(axis=0), rtol=0, atol=1e-12)
