@@ -304,6 +304,21 @@ int32_t kvtc_fetch_kv(const kvtc_tensor_ref *k, const kvtc_tensor_ref *v,
 int32_t kvtc_attend_workspace(const void *k_state_host, const void *v_state_host, int64_t s_end,
                               size_t *bytes);
 
+/* kvtc_attend with Hq = q_heads query heads, a multiple G of the stored heads H
+ * (grouped-query attention: query head hq attends KV head hq / G, consecutive
+ * query heads sharing one; the Llama-3-8B-like layer has 32 query heads over 8
+ * KV heads).  q_dev [B, Hq, D], out_dev fp16 [B, Hq, D]; the other arguments,
+ * the arithmetic and the errors as for kvtc_attend.  Both kvtc_attend and this
+ * call serve per-head (DP) and group-head caches: for a group-head cache the
+ * (min, scale) of each token and quantisation group enter the scores through
+ * per-group code sums and the value sums through the dequantised latents.
+ * The queries per unit (G times heads_per_unit) are at most 32. */
+int32_t kvtc_attend_gqa_workspace(const void *k_state_host, const void *v_state_host, int64_t q_heads, int64_t s_end,
+                                  size_t *bytes);
+int32_t kvtc_attend_gqa(const kvtc_tensor_ref *k, const kvtc_tensor_ref *v, int64_t q_heads, const void *q_dev,
+                        int32_t q_dtype, const int64_t q_strides[3], int64_t s_end, void *out_dev,
+                        const int64_t out_strides[3], void *work_dev, size_t work_bytes, void *hip_stream);
+
 /* Decode attention over the stored rows [0, s_end) of a key and a value tensor,
  * computed from their codes without reconstructing keys or values (device).
  * TurboQuant cache module page, attend: one query per head is scored against
@@ -316,15 +331,16 @@ int32_t kvtc_attend_workspace(const void *k_state_host, const void *v_state_host
  * latent space: q is projected onto the key basis once, every stored key code
  * is weighted by it, and the softmax-weighted value codes are reconstructed
  * once per (b, h).
- *   k, v        DP-mode tensors with one head per unit and the same B, H, D
- *               (D <= 256); their rows_dev, dtype and strides are not used
+ *   k, v        tensors with the same B, H, D (D <= 256) and heads per unit,
+ *               per-head (DP) or group-head; their rows_dev, dtype and strides
+ *               are not used (params_dev is, for a group-head tensor)
  *   q_dev       queries [B, H, D] of dtype q_dtype (KVTC_F16 or KVTC_F32), element
  *               strides q_strides for (b, h, d), q_strides[2] == 1
  *   out_dev     fp16 [B, H, D] with element strides out_strides, out_strides[2] == 1
  *   work_dev    device workspace of at least kvtc_attend_workspace() bytes,
  *               256-byte aligned, owned by the caller (contents are scratch)
- * Needs 0 <= s_end <= both capacities; KVTC_E_STATE for a group-head tensor,
- * KVTC_E_BUFSIZE for a missing or short workspace. */
+ * Needs 0 <= s_end <= both capacities; KVTC_E_SHAPE for tensors of different
+ * shapes, KVTC_E_BUFSIZE for a missing or short workspace. */
 int32_t kvtc_attend(const kvtc_tensor_ref *k, const kvtc_tensor_ref *v,
                     const void *q_dev, int32_t q_dtype, const int64_t q_strides[3], int64_t s_end,
                     void *out_dev, const int64_t out_strides[3],

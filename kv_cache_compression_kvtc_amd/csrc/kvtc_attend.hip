@@ -339,6 +339,332 @@ size_t attend_work_bytes(const kvtc_state_header *hk, const kvtc_state_header *h
     return attend_work(hk, hv, s_end).total;
 }
 
+// ============================================================ general path
+// Any number G of query heads per KV head (grouped-query attention: query head
+// hq attends KV head hq / G) and per-head or group-head caches on either side.
+// A unit of hpu heads is attended by Q = hpu * G queries; query i of unit u is
+// query head (group(u) * hpu + i / G) * G + i % G and sees the D features
+// [(i / G) * D, (i / G + 1) * D) of the unit's rows.  With x_s = sum_j l_sj V_j + mu
+// and q~_ij = (q_i . V_j[slice_i]) / sqrt(D):
+//   per-head (DP) rows, l = min_j + c * scale_j:  score = sum_j c q~_ij scale_j + beta_i,
+//     beta_i = (q_i . mu[slice] + sum_j min_j (q_i . V_j[slice])) / sqrt(D);
+//   group-head rows, l = min16_g + c * scale16_g per token and quantisation group g:
+//     score = sum_g (min16_g P_ig + scale16_g sum_{j in g} c q~_ij) + q_i . mu[slice] / sqrt(D),
+//     P_ig = sum_{j in g} q~_ij;
+// the output is sum_j abar_ij V_j[slice_i] + mu[slice_i] with abar_ij = sum_s p_is l_sj.
+constexpr int kGenRows = 256;        // rows per partial block (one thread per row)
+constexpr int kGenMaxQ = 32;         // queries per unit
+
+struct GenSide {
+    const uint8_t *codes;
+    const uint32_t *params;            // group-head rows: [U][capacity][n_qg] (min16 | scale16 << 16)
+    int64_t capacity;
+    const kvtc_unit_info *ui;
+    const float *basis, *mu, *qmin, *qscale, *bias;
+    const int32_t *comp;
+    const uint32_t *sbits;
+    int kslots, rmax, row_words, n_qg, gs, mixed, dg;
+};
+
+struct GenArgs {
+    GenSide k, v;
+    const void *q;
+    int64_t qsb, qsh;
+    int q_f16;
+    _Float16 *out;
+    int64_t osb, osh;
+    int64_t s_end;
+    int nchunks, G, hpu, groups, D, Q;
+    float inv_sqrt_d;
+    float *qt;       // [U][Q][k.kslots]   q~ (times scale_j for per-head keys)
+    float *qb;       // [U][Q]             beta
+    float *qp;       // [U][Q][k.n_qg]     group sums of q~ (group-head keys)
+    float *part;     // [U][nchunks][Q][v.kslots + 2]: abar partial sums, then max, sum
+};
+
+__device__ inline void gen_query(const GenArgs &a, int u, int i, int &b, int &hq, int &slice) {
+    b = u / a.groups;
+    const int jh = i / a.G;
+    hq = ((u % a.groups) * a.hpu + jh) * a.G + i % a.G;
+    slice = jh * a.D;
+}
+
+// Per (unit, query): the score coefficients, in fixed orders.
+__global__ __launch_bounds__(256) void attend_gen_prep_kernel(GenArgs a) {
+    __shared__ float ql[kMaxSlots];
+    __shared__ float qts[kMaxSlots];
+    __shared__ float mpart[kMaxSlots];
+    const int u = blockIdx.x, i = blockIdx.y, tid = threadIdx.x;
+    int b, hq, slice;
+    gen_query(a, u, i, b, hq, slice);
+    for (int d = tid; d < a.D; d += blockDim.x)
+        ql[d] = a.q_f16 ? static_cast<float>(static_cast<const _Float16 *>(a.q)[b * a.qsb + hq * a.qsh + d])
+                        : static_cast<const float *>(a.q)[b * a.qsb + hq * a.qsh + d];
+    __syncthreads();
+    const GenSide &K = a.k;
+    const int ns = K.ui[u].n_slots;
+    for (int j = tid; j < K.kslots; j += blockDim.x) {
+        float qt = 0.f, mp = 0.f;
+        if (j < ns) {
+            const float *vrow = K.basis + (static_cast<int64_t>(u) * K.kslots + j) * K.dg + slice;
+            float dot = 0.f;
+            for (int d = 0; d < a.D; ++d) dot = fmaf(ql[d], vrow[d], dot);
+            if (K.mixed) {
+                qt = dot * a.inv_sqrt_d;
+            } else {
+                const int c = K.comp[static_cast<int64_t>(u) * K.kslots + j];
+                qt = K.qscale[static_cast<int64_t>(u) * K.rmax + c] * dot * a.inv_sqrt_d;
+                mp = K.qmin[static_cast<int64_t>(u) * K.rmax + c] * dot;
+            }
+        }
+        a.qt[(static_cast<int64_t>(u) * a.Q + i) * K.kslots + j] = qt;
+        qts[j] = qt;
+        mpart[j] = mp;
+    }
+    __syncthreads();
+    if (tid == 0) {
+        float beta = 0.f;
+        for (int d = 0; d < a.D; ++d) beta = fmaf(ql[d], K.mu[static_cast<int64_t>(u) * K.dg + slice + d], beta);
+        for (int j = 0; j < K.kslots; ++j) beta += mpart[j];
+        a.qb[static_cast<int64_t>(u) * a.Q + i] = beta * a.inv_sqrt_d;
+    }
+    if (K.mixed)
+        for (int g = tid; g < K.n_qg; g += blockDim.x) {
+            float p = 0.f;
+            for (int j = g * K.gs; j < min(ns, (g + 1) * K.gs); ++j) p += qts[j];
+            a.qp[(static_cast<int64_t>(u) * a.Q + i) * K.n_qg + g] = p;
+        }
+}
+
+// Stages the code rows (odd pitch) and, for group-head rows, their (min, scale)
+// words group-major, of rows [s0, s0 + n) of unit u.
+__device__ inline void gen_stage(const GenSide &T, int u, int64_t s0, int n, uint32_t *rows, int pitch,
+                                 uint32_t *prm) {
+    const uint32_t *src = reinterpret_cast<const uint32_t *>(T.codes) + (static_cast<int64_t>(u) * T.capacity + s0) * T.row_words;
+    for (int i = threadIdx.x; i < n * T.row_words; i += blockDim.x) {
+        const int r = i / T.row_words;
+        rows[r * pitch + (i - r * T.row_words)] = src[i];
+    }
+    if (T.mixed) {
+        const uint32_t *ps = T.params + (static_cast<int64_t>(u) * T.capacity + s0) * T.n_qg;
+        for (int i = threadIdx.x; i < n * T.n_qg; i += blockDim.x) {
+            const int r = i / T.n_qg;
+            prm[(i - r * T.n_qg) * kGenRows + r] = ps[i];
+        }
+    }
+}
+
+__device__ inline float half_lo(uint32_t p) { return static_cast<float>(__builtin_bit_cast(_Float16, static_cast<uint16_t>(p & 0xFFFFu))); }
+__device__ inline float half_hi(uint32_t p) { return static_cast<float>(__builtin_bit_cast(_Float16, static_cast<uint16_t>(p >> 16))); }
+
+// Per (chunk of 256 rows, unit): every query's scores of the chunk's rows (one
+// thread per row), the chunk's softmax max and sum per query, and the
+// p-weighted sums of every value slot (one thread per slot).
+template <int QM>
+__global__ __launch_bounds__(256) void attend_gen_partial_kernel(GenArgs a) {
+    extern __shared__ __align__(16) unsigned char smem[];
+    const GenSide &K = a.k, &V = a.v;
+    const int c = blockIdx.x, u = blockIdx.y, t = threadIdx.x, lane = t & 63, wave = t >> 6;
+    const int Q = a.Q;
+    float *qt = reinterpret_cast<float *>(smem);                     // [QM][K.kslots]
+    float *qb = qt + QM * K.kslots;                                  // [QM]
+    float *qp = qb + QM;                                             // [QM][K.n_qg]
+    float *sc = qp + QM * max(K.n_qg, 1);                            // [QM][256] scores, then weights
+    float *stat = sc + QM * kGenRows;                                // [QM][2]
+    uint32_t *sb = reinterpret_cast<uint32_t *>(stat + 2 * QM);     // [kMaxSlots]
+    uint32_t *rows = sb + kMaxSlots;                                 // [256][pitch]
+    const int pitch = (max(K.row_words, V.row_words) + 1) | 1;
+    uint32_t *prm = rows + kGenRows * pitch;                         // [n_qg][256]
+    const int64_t s0 = static_cast<int64_t>(c) * kGenRows;
+    const int nrows = static_cast<int>(min<int64_t>(kGenRows, a.s_end - s0));
+
+    for (int i = t; i < Q * K.kslots; i += blockDim.x) qt[i] = a.qt[static_cast<int64_t>(u) * Q * K.kslots + i];
+    for (int i = t; i < Q; i += blockDim.x) qb[i] = a.qb[static_cast<int64_t>(u) * Q + i];
+    if (K.mixed)
+        for (int i = t; i < Q * K.n_qg; i += blockDim.x) qp[i] = a.qp[static_cast<int64_t>(u) * Q * K.n_qg + i];
+    for (int j = t; j < K.kslots; j += blockDim.x) sb[j] = K.sbits[static_cast<int64_t>(u) * K.kslots + j];
+    gen_stage(K, u, s0, nrows, rows, pitch, prm);
+    __syncthreads();
+
+    float acc[QM];
+#pragma unroll
+    for (int i = 0; i < QM; ++i) acc[i] = i < Q ? qb[i] : 0.f;
+    if (t < nrows) {
+        const uint32_t *row = rows + t * pitch;
+        const int ns = K.ui[u].n_slots;
+        if (!K.mixed) {
+            for (int j = 0; j < ns; ++j) {
+                const float cf = static_cast<float>(row_field(row, sb[j]));
+#pragma unroll
+                for (int i = 0; i < QM; ++i)
+                    if (i < Q) acc[i] = fmaf(cf, qt[i * K.kslots + j], acc[i]);
+            }
+        } else {
+            for (int g = 0; g < K.n_qg; ++g) {
+                float gacc[QM];
+#pragma unroll
+                for (int i = 0; i < QM; ++i) gacc[i] = 0.f;
+                for (int j = g * K.gs; j < min(ns, (g + 1) * K.gs); ++j) {
+                    const float cf = static_cast<float>(row_field(row, sb[j]));
+#pragma unroll
+                    for (int i = 0; i < QM; ++i)
+                        if (i < Q) gacc[i] = fmaf(cf, qt[i * K.kslots + j], gacc[i]);
+                }
+                const uint32_t p = prm[g * kGenRows + t];
+                const float mn = half_lo(p), scl = half_hi(p);
+#pragma unroll
+                for (int i = 0; i < QM; ++i)
+                    if (i < Q) acc[i] = fmaf(scl, gacc[i], fmaf(mn, qp[i * K.n_qg + g], acc[i]));
+            }
+        }
+    }
+#pragma unroll
+    for (int i = 0; i < QM; ++i)
+        if (i < Q) sc[i * kGenRows + t] = t < nrows ? acc[i] : -__builtin_huge_valf();
+    __syncthreads();
+    // softmax statistics: wave w takes queries w, w + 4, ...
+    for (int i = wave; i < Q; i += 4) {
+        float m = -__builtin_huge_valf();
+        for (int r = lane; r < kGenRows; r += 64) m = fmaxf(m, sc[i * kGenRows + r]);
+        for (int o = 32; o >= 1; o >>= 1) m = fmaxf(m, __shfl_xor(m, o, 64));
+        float l = 0.f;
+        for (int r = lane; r < kGenRows; r += 64) {
+            const float p = r < nrows ? expf(sc[i * kGenRows + r] - m) : 0.f;
+            sc[i * kGenRows + r] = p;
+            l += p;
+        }
+        for (int o = 32; o >= 1; o >>= 1) l += __shfl_xor(l, o, 64);
+        if (lane == 0) {
+            stat[2 * i] = m;
+            stat[2 * i + 1] = l;
+        }
+    }
+    __syncthreads();
+    // value rows
+    for (int j = t; j < V.kslots; j += blockDim.x) sb[j] = V.sbits[static_cast<int64_t>(u) * V.kslots + j];
+    gen_stage(V, u, s0, nrows, rows, pitch, prm);
+    __syncthreads();
+    float va[QM];
+#pragma unroll
+    for (int i = 0; i < QM; ++i) va[i] = 0.f;
+    const int nv = V.ui[u].n_slots;
+    if (t < nv) {
+        const uint32_t sbj = sb[t];
+        const int g = V.mixed ? t / V.gs : 0;
+        for (int r = 0; r < nrows; ++r) {
+            const float cf = static_cast<float>(row_field(rows + r * pitch, sbj));
+            float l = cf;
+            if (V.mixed) {
+                const uint32_t p = prm[g * kGenRows + r];
+                l = fmaf(cf, half_hi(p), half_lo(p));
+            }
+#pragma unroll
+            for (int i = 0; i < QM; ++i)
+                if (i < Q) va[i] = fmaf(sc[i * kGenRows + r], l, va[i]);
+        }
+    }
+    float *dst = a.part + (static_cast<int64_t>(u) * a.nchunks + c) * Q * (V.kslots + 2);
+    if (t < V.kslots) {
+#pragma unroll
+        for (int i = 0; i < QM; ++i)
+            if (i < Q) dst[i * (V.kslots + 2) + t] = va[i];
+    }
+    for (int i = t; i < Q; i += blockDim.x) {
+        dst[i * (V.kslots + 2) + V.kslots] = stat[2 * i];
+        dst[i * (V.kslots + 2) + V.kslots + 1] = stat[2 * i + 1];
+    }
+}
+
+// Per (unit, query): merge the chunks and reconstruct the output once.
+__global__ __launch_bounds__(256) void attend_gen_merge_kernel(GenArgs a) {
+    __shared__ float coef[kMaxSlots];
+    __shared__ float red[4];
+    const int u = blockIdx.x, i = blockIdx.y, tid = threadIdx.x;
+    int b, hq, slice;
+    gen_query(a, u, i, b, hq, slice);
+    const GenSide &V = a.v;
+    const int nv = V.ui[u].n_slots, stride = V.kslots + 2;
+    const float *part = a.part + static_cast<int64_t>(u) * a.nchunks * a.Q * stride + static_cast<int64_t>(i) * stride;
+    const int64_t cstride = static_cast<int64_t>(a.Q) * stride;
+    float m = -__builtin_huge_valf();
+    for (int c = tid; c < a.nchunks; c += blockDim.x) m = fmaxf(m, part[c * cstride + V.kslots]);
+    const float M = block_reduce(m, red, true);
+    float l = 0.f;
+    for (int c = tid; c < a.nchunks; c += blockDim.x) l += expf(part[c * cstride + V.kslots] - M) * part[c * cstride + V.kslots + 1];
+    const float L = block_reduce(l, red, false);
+    for (int j = tid; j < V.kslots; j += blockDim.x) {
+        float s = 0.f;
+        if (j < nv) {
+            for (int c = 0; c < a.nchunks; ++c) s = fmaf(expf(part[c * cstride + V.kslots] - M), part[c * cstride + j], s);
+            s = s / L;
+            if (!V.mixed) s *= V.qscale[static_cast<int64_t>(u) * V.rmax + V.comp[static_cast<int64_t>(u) * V.kslots + j]];
+        }
+        coef[j] = s;
+    }
+    __syncthreads();
+    for (int d = tid; d < a.D; d += blockDim.x) {
+        float o = 0.f;
+        if (a.nchunks > 0) {
+            o = (V.mixed ? V.mu : V.bias)[static_cast<int64_t>(u) * V.dg + slice + d];
+            const float *vb = V.basis + static_cast<int64_t>(u) * V.kslots * V.dg + slice + d;
+            for (int j = 0; j < nv; ++j) o = fmaf(coef[j], vb[static_cast<int64_t>(j) * V.dg], o);
+        }
+        a.out[b * a.osb + hq * a.osh + d] = static_cast<_Float16>(o);
+    }
+}
+
+GenSide gen_side(const kvtc_state_header *h, const void *state_dev, const void *codes, const void *params,
+                 int64_t capacity) {
+    const char *sd = static_cast<const char *>(state_dev);
+    GenSide g{};
+    g.codes = static_cast<const uint8_t *>(codes);
+    g.params = static_cast<const uint32_t *>(params);
+    g.capacity = capacity;
+    g.ui = reinterpret_cast<const kvtc_unit_info *>(sd + h->off_unit);
+    g.basis = reinterpret_cast<const float *>(sd + h->off_basis);
+    g.mu = reinterpret_cast<const float *>(sd + h->off_mu);
+    g.qmin = reinterpret_cast<const float *>(sd + h->off_qmin);
+    g.qscale = reinterpret_cast<const float *>(sd + h->off_qscale);
+    g.bias = reinterpret_cast<const float *>(sd + h->off_bias);
+    g.comp = reinterpret_cast<const int32_t *>(sd + h->off_slot_comp);
+    g.sbits = reinterpret_cast<const uint32_t *>(sd + h->off_slot_bits);
+    g.kslots = h->kslots;
+    g.rmax = h->rmax;
+    g.row_words = h->row_stride / 4;
+    g.n_qg = h->mode == KVTC_MODE_MIXED ? h->n_qgroups : 0;
+    g.gs = h->group_size;
+    g.mixed = h->mode == KVTC_MODE_MIXED;
+    g.dg = h->dg;
+    return g;
+}
+
+// Workspace of the general path, regions 256-byte aligned: qt, qb, qp, part.
+struct GenWork {
+    uint64_t qt, qb, qp, part, total;
+};
+
+GenWork gen_work(const kvtc_state_header *hk, const kvtc_state_header *hv, int Q, int64_t s_end) {
+    GenWork w{};
+    const uint64_t U = static_cast<uint64_t>(hk->units);
+    const int64_t nch = (s_end + kGenRows - 1) / kGenRows;
+    const int ng = hk->mode == KVTC_MODE_MIXED ? hk->n_qgroups : 0;
+    w.qt = 0;
+    w.qb = align_up(U * Q * hk->kslots * 4, 256);
+    w.qp = w.qb + align_up(U * Q * 4, 256);
+    w.part = w.qp + align_up(U * Q * std::max(ng, 1) * 4, 256);
+    w.total = w.part + U * static_cast<uint64_t>(nch) * Q * (hv->kslots + 2) * 4;
+    return w;
+}
+
+size_t gen_lds_bytes(const kvtc_state_header *hk, const kvtc_state_header *hv, int QM) {
+    const int ng = hk->mode == KVTC_MODE_MIXED ? hk->n_qgroups : 0;
+    const int ngv = hv->mode == KVTC_MODE_MIXED ? hv->n_qgroups : 0;
+    const int pitch = (std::max(hk->row_stride, hv->row_stride) / 4 + 1) | 1;
+    return (static_cast<size_t>(QM) * hk->kslots + QM + static_cast<size_t>(QM) * std::max(ng, 1) +
+            static_cast<size_t>(QM) * kGenRows + 2 * QM) * 4 +
+           (kMaxSlots + static_cast<size_t>(kGenRows) * pitch + static_cast<size_t>(std::max(ng, ngv)) * kGenRows) * 4;
+}
+
 
 }  // namespace
 }  // namespace kvtc
@@ -372,9 +698,11 @@ int32_t scratch_address(void **out) {
     return KVTC_OK;
 }
 
-int32_t attend_impl(const kvtc_tensor_ref *k, const kvtc_tensor_ref *v, const void *q_dev, int32_t q_dtype,
-                    const int64_t q_strides[3], int64_t s_end, void *out_dev, const int64_t out_strides[3],
-                    void *work_dev, size_t work_bytes, bool noalloc, hipStream_t stream);
+int32_t attend_impl(const kvtc_tensor_ref *k, const kvtc_tensor_ref *v, int64_t q_heads, const void *q_dev,
+                    int32_t q_dtype, const int64_t q_strides[3], int64_t s_end, void *out_dev,
+                    const int64_t out_strides[3], void *work_dev, size_t work_bytes, bool noalloc, hipStream_t stream);
+int32_t attend_workspace_impl(const void *k_state_host, const void *v_state_host, int64_t q_heads, int64_t s_end,
+                              size_t *bytes);
 
 }  // namespace
 }  // namespace kvtc
@@ -384,27 +712,36 @@ using namespace kvtc;
 extern "C" {
 
 int32_t kvtc_attend_workspace(const void *k_state_host, const void *v_state_host, int64_t s_end, size_t *bytes) {
-    const kvtc_state_header *hk = nullptr, *hv = nullptr;
-    int32_t st = check_state(k_state_host, &hk);
+    const kvtc_state_header *hk = nullptr;
+    const int32_t st = check_state(k_state_host, &hk);
     if (st != KVTC_OK) return st;
-    st = check_state(v_state_host, &hv);
-    if (st != KVTC_OK) return st;
-    if (!bytes || s_end < 0) return KVTC_E_ARG;
-    *bytes = attend_work_bytes(hk, hv, s_end);
-    return KVTC_OK;
+    return attend_workspace_impl(k_state_host, v_state_host, hk->heads, s_end, bytes);
+}
+
+int32_t kvtc_attend_gqa_workspace(const void *k_state_host, const void *v_state_host, int64_t q_heads, int64_t s_end,
+                                  size_t *bytes) {
+    return attend_workspace_impl(k_state_host, v_state_host, q_heads, s_end, bytes);
 }
 
 int32_t kvtc_attend(const kvtc_tensor_ref *k, const kvtc_tensor_ref *v, const void *q_dev, int32_t q_dtype,
                     const int64_t q_strides[3], int64_t s_end, void *out_dev, const int64_t out_strides[3],
                     void *work_dev, size_t work_bytes, void *hip_stream) {
-    return attend_impl(k, v, q_dev, q_dtype, q_strides, s_end, out_dev, out_strides, work_dev, work_bytes, false,
+    return attend_impl(k, v, 0, q_dev, q_dtype, q_strides, s_end, out_dev, out_strides, work_dev, work_bytes, false,
                        static_cast<hipStream_t>(hip_stream));
+}
+
+int32_t kvtc_attend_gqa(const kvtc_tensor_ref *k, const kvtc_tensor_ref *v, int64_t q_heads, const void *q_dev,
+                        int32_t q_dtype, const int64_t q_strides[3], int64_t s_end, void *out_dev,
+                        const int64_t out_strides[3], void *work_dev, size_t work_bytes, void *hip_stream) {
+    if (q_heads < 1) return KVTC_E_ARG;
+    return attend_impl(k, v, q_heads, q_dev, q_dtype, q_strides, s_end, out_dev, out_strides, work_dev, work_bytes,
+                       false, static_cast<hipStream_t>(hip_stream));
 }
 
 int32_t kvtc_attend_noalloc(const kvtc_tensor_ref *k, const kvtc_tensor_ref *v, const void *q_dev, int32_t q_dtype,
                             const int64_t q_strides[3], int64_t s_end, void *out_dev, const int64_t out_strides[3],
                             void *hip_stream) {
-    return attend_impl(k, v, q_dev, q_dtype, q_strides, s_end, out_dev, out_strides, nullptr, 0, true,
+    return attend_impl(k, v, 0, q_dev, q_dtype, q_strides, s_end, out_dev, out_strides, nullptr, 0, true,
                        static_cast<hipStream_t>(hip_stream));
 }
 
@@ -413,33 +750,129 @@ int32_t kvtc_attend_noalloc(const kvtc_tensor_ref *k, const kvtc_tensor_ref *v, 
 namespace kvtc {
 namespace {
 
-// Validates the call, then launches the three attention kernels on the given
+// The path a call takes: the per-head kernels (DP caches, one query per head)
+// or the general ones; the workspace it needs; KVTC_OK or why it is refused.
+struct AttendRoute {
+    bool fast;
+    int Q, G, QM;
+    size_t work;
+};
+
+int32_t attend_route(const kvtc_state_header *hk, const kvtc_state_header *hv, int64_t q_heads, int64_t s_end,
+                     AttendRoute *r) {
+    if (hk->batch != hv->batch || hk->heads != hv->heads || hk->head_dim != hv->head_dim ||
+        hk->heads_per_unit != hv->heads_per_unit)
+        return KVTC_E_SHAPE;
+    if (q_heads < 1 || q_heads % hk->heads != 0) return KVTC_E_SHAPE;
+    const int64_t G = q_heads / hk->heads;
+    r->G = static_cast<int>(std::min<int64_t>(G, 1 << 20));
+    r->fast = G == 1 && attend_side_ok(hk) == KVTC_OK && attend_side_ok(hv) == KVTC_OK;
+    if (r->fast) {
+        r->Q = 1;
+        r->QM = 1;
+        r->work = attend_work_bytes(hk, hv, s_end);
+        return KVTC_OK;
+    }
+    const int64_t Q = G * hk->heads_per_unit;
+    if (Q > kGenMaxQ || hk->head_dim > kMaxSlots || hk->kslots > kMaxSlots || hv->kslots > kMaxSlots ||
+        hk->row_stride > kMaxRowStride || hv->row_stride > kMaxRowStride)
+        return KVTC_E_SHAPE;
+    r->Q = static_cast<int>(Q);
+    r->QM = Q <= 8 ? 8 : kGenMaxQ;
+    if (gen_lds_bytes(hk, hv, r->QM) > kLdsMax) return KVTC_E_SHAPE;
+    r->work = gen_work(hk, hv, r->Q, s_end).total;
+    return KVTC_OK;
+}
+
+int32_t attend_workspace_impl(const void *k_state_host, const void *v_state_host, int64_t q_heads, int64_t s_end,
+                              size_t *bytes) {
+    const kvtc_state_header *hk = nullptr, *hv = nullptr;
+    int32_t st = check_state(k_state_host, &hk);
+    if (st != KVTC_OK) return st;
+    st = check_state(v_state_host, &hv);
+    if (st != KVTC_OK) return st;
+    if (!bytes || s_end < 0) return KVTC_E_ARG;
+    AttendRoute r{};
+    st = attend_route(hk, hv, q_heads, s_end, &r);
+    if (st != KVTC_OK) return st;
+    *bytes = r.work;
+    return KVTC_OK;
+}
+
+int32_t launch_gen(const kvtc_tensor_ref *k, const kvtc_tensor_ref *v, const kvtc_state_header *hk,
+                   const kvtc_state_header *hv, const AttendRoute &r, const void *q_dev, int32_t q_dtype,
+                   const int64_t q_strides[3], int64_t s_end, void *out_dev, const int64_t out_strides[3],
+                   void *work_dev, hipStream_t stream) {
+    GenArgs a{};
+    a.k = gen_side(hk, k->state_dev, k->codes_dev, k->params_dev, k->capacity);
+    a.v = gen_side(hv, v->state_dev, v->codes_dev, v->params_dev, v->capacity);
+    a.q = q_dev;
+    a.qsb = q_strides[0];
+    a.qsh = q_strides[1];
+    a.q_f16 = q_dtype == KVTC_F16;
+    a.out = static_cast<_Float16 *>(out_dev);
+    a.osb = out_strides[0];
+    a.osh = out_strides[1];
+    a.s_end = s_end;
+    a.nchunks = static_cast<int>((s_end + kGenRows - 1) / kGenRows);
+    a.G = r.G;
+    a.hpu = hk->heads_per_unit;
+    a.groups = static_cast<int>(hk->heads / hk->heads_per_unit);
+    a.D = hk->head_dim;
+    a.Q = r.Q;
+    a.inv_sqrt_d = 1.0f / sqrtf(static_cast<float>(hk->head_dim));
+    const GenWork wl = gen_work(hk, hv, r.Q, s_end);
+    char *wb = static_cast<char *>(work_dev);
+    a.qt = reinterpret_cast<float *>(wb + wl.qt);
+    a.qb = reinterpret_cast<float *>(wb + wl.qb);
+    a.qp = reinterpret_cast<float *>(wb + wl.qp);
+    a.part = reinterpret_cast<float *>(wb + wl.part);
+    const unsigned U = static_cast<unsigned>(hk->units), Q = static_cast<unsigned>(r.Q);
+    hipLaunchKernelGGL(attend_gen_prep_kernel, dim3(U, Q), dim3(256), 0, stream, a);
+    if (hipGetLastError() != hipSuccess) return KVTC_E_DEVICE;
+    if (a.nchunks > 0) {
+        const size_t lds = gen_lds_bytes(hk, hv, r.QM);
+        auto kern = r.QM == 8 ? attend_gen_partial_kernel<8> : attend_gen_partial_kernel<kGenMaxQ>;
+        if (!allow_lds(reinterpret_cast<const void *>(kern))) return KVTC_E_DEVICE;
+        hipLaunchKernelGGL(kern, dim3(static_cast<unsigned>(a.nchunks), U), dim3(256), lds, stream, a);
+        if (hipGetLastError() != hipSuccess) return KVTC_E_DEVICE;
+    }
+    hipLaunchKernelGGL(attend_gen_merge_kernel, dim3(U, Q), dim3(256), 0, stream, a);
+    return hipGetLastError() == hipSuccess ? KVTC_OK : KVTC_E_DEVICE;
+}
+
+// Validates the call, then launches the attention kernels on the given
 // workspace; with noalloc the workspace is this device's scratch array (after
-// its size has been checked against the call's need).
-int32_t attend_impl(const kvtc_tensor_ref *k, const kvtc_tensor_ref *v, const void *q_dev, int32_t q_dtype,
-                    const int64_t q_strides[3], int64_t s_end, void *out_dev, const int64_t out_strides[3],
-                    void *work_dev, size_t work_bytes, bool noalloc, hipStream_t stream) {
+// its size has been checked against the call's need).  q_heads == 0: one query
+// per stored head.
+int32_t attend_impl(const kvtc_tensor_ref *k, const kvtc_tensor_ref *v, int64_t q_heads, const void *q_dev,
+                    int32_t q_dtype, const int64_t q_strides[3], int64_t s_end, void *out_dev,
+                    const int64_t out_strides[3], void *work_dev, size_t work_bytes, bool noalloc, hipStream_t stream) {
     if (!k || !v || !q_strides || !out_strides) return KVTC_E_ARG;
     const kvtc_state_header *hk = nullptr, *hv = nullptr;
     int32_t st = check_state(k->state_host, &hk);
     if (st != KVTC_OK) return st;
     st = check_state(v->state_host, &hv);
     if (st != KVTC_OK) return st;
-    if ((st = attend_side_ok(hk)) != KVTC_OK || (st = attend_side_ok(hv)) != KVTC_OK) return st;
-    if (hk->batch != hv->batch || hk->heads != hv->heads || hk->head_dim != hv->head_dim) return KVTC_E_SHAPE;
+    if (q_heads == 0) q_heads = hk->heads;
     if (q_dtype != KVTC_F16 && q_dtype != KVTC_F32) return KVTC_E_DTYPE;
     if (q_strides[2] != 1 || out_strides[2] != 1 || q_strides[0] < 0 || q_strides[1] < 0 || out_strides[0] < 0 ||
         out_strides[1] < 0)
         return KVTC_E_SHAPE;
     if (s_end < 0 || k->capacity < 0 || v->capacity < 0) return KVTC_E_ARG;
+    AttendRoute route{};
+    if ((st = attend_route(hk, hv, q_heads, s_end, &route)) != KVTC_OK) return st;
     if (s_end > k->capacity || s_end > v->capacity) return KVTC_E_CAPACITY;
     if (!k->state_dev || !v->state_dev || !q_dev || !out_dev) return KVTC_E_ARG;
     if (s_end > 0 && ((hk->row_stride > 0 && (!k->codes_dev || reinterpret_cast<uintptr_t>(k->codes_dev) % 4)) ||
                       (hv->row_stride > 0 && (!v->codes_dev || reinterpret_cast<uintptr_t>(v->codes_dev) % 4))))
         return KVTC_E_ARG;
+    if (s_end > 0 && ((hk->mode == KVTC_MODE_MIXED && (!k->params_dev || reinterpret_cast<uintptr_t>(k->params_dev) % 4)) ||
+                      (hv->mode == KVTC_MODE_MIXED && (!v->params_dev || reinterpret_cast<uintptr_t>(v->params_dev) % 4))))
+        return KVTC_E_ARG;
     if (reinterpret_cast<uintptr_t>(out_dev) % 2 || reinterpret_cast<uintptr_t>(q_dev) % (q_dtype == KVTC_F16 ? 2 : 4))
         return KVTC_E_ARG;
-    const size_t need = attend_work_bytes(hk, hv, s_end);
+    const size_t need = route.work;
     if (noalloc) {
         if (need > kAttendScratchBytes) return KVTC_E_BUFSIZE;
         const int32_t sa = scratch_address(&work_dev);
@@ -449,6 +882,8 @@ int32_t attend_impl(const kvtc_tensor_ref *k, const kvtc_tensor_ref *v, const vo
     if (!work_dev || work_bytes < need || reinterpret_cast<uintptr_t>(work_dev) % 256) return KVTC_E_BUFSIZE;
     const int64_t nchunks = (s_end + kAttChunk - 1) / kAttChunk;
     if (hk->units > 0x7FFFFFFF || nchunks > 0x7FFFFFFF || hk->units > 65535) return KVTC_E_SHAPE;
+    if (!route.fast)
+        return launch_gen(k, v, hk, hv, route, q_dev, q_dtype, q_strides, s_end, out_dev, out_strides, work_dev, stream);
 
     AttendArgs a{};
     a.k = attend_side(hk, k->state_dev, k->codes_dev, k->capacity);

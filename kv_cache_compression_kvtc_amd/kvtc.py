@@ -122,6 +122,9 @@ _sig = {
                            _sz, _vp]),
     "kvtc_attend_noalloc": (_i32, [C.POINTER(TensorRef), C.POINTER(TensorRef), _vp, _i32, _P64, _i64, _vp, _P64,
                                    _vp]),
+    "kvtc_attend_gqa_workspace": (_i32, [_vp, _vp, _i64, _i64, C.POINTER(_sz)]),
+    "kvtc_attend_gqa": (_i32, [C.POINTER(TensorRef), C.POINTER(TensorRef), _i64, _vp, _i32, _P64, _i64, _vp, _P64,
+                               _vp, _sz, _vp]),
 }
 for _name, (_res, _args) in _sig.items():
     _f = getattr(_lib, _name)
@@ -522,13 +525,24 @@ def kvtc_attend_workspace(blob_k: np.ndarray, blob_v: np.ndarray, s_end: int) ->
     return n.value
 
 
+def kvtc_attend_gqa_workspace(blob_k: np.ndarray, blob_v: np.ndarray, q_heads: int, s_end: int) -> int:
+    _check_blob(blob_k, "kvtc_attend_gqa_workspace")
+    _check_blob(blob_v, "kvtc_attend_gqa_workspace")
+    n = C.c_size_t(0)
+    _check(_lib.kvtc_attend_gqa_workspace(_host_ptr(blob_k), _host_ptr(blob_v), q_heads, s_end, C.byref(n)),
+           "kvtc_attend_gqa_workspace")
+    return n.value
+
+
 class Attend:
     """kvtc_attend with its buffers checked once: decode attention of queries
     [B, H, D] over store rows [0, s_end) of a key and a value tensor.  ``k`` and
     ``v`` are (blob, blob_dev, codes, params); the device workspace is allocated
-    here (torch) for ``capacity`` rows and reused by every call."""
+    here (torch) for ``capacity`` rows and reused by every call.  With
+    ``q_heads`` set, queries are [B, q_heads, D] and the call is kvtc_attend_gqa
+    (q_heads a multiple of H; query head hq attends KV head hq // (q_heads / H))."""
 
-    def __init__(self, k, v, capacity: int, stream=None):
+    def __init__(self, k, v, capacity: int, stream=None, q_heads=None):
         import torch
         self._keep = (k, v)
         self._refs = []
@@ -541,7 +555,9 @@ class Attend:
             self._refs.append(ref)
         self.h = header(k[0])
         self.capacity = capacity
-        nbytes = kvtc_attend_workspace(k[0], v[0], capacity)
+        self.q_heads = q_heads
+        nbytes = (kvtc_attend_workspace(k[0], v[0], capacity) if q_heads is None else
+                  kvtc_attend_gqa_workspace(k[0], v[0], q_heads, capacity))
         self.work = torch.empty(max(nbytes, 256) + 256, dtype=torch.uint8, device=k[1].device)
         off = (-self.work.data_ptr()) % 256
         self._work, self._work_bytes = self.work.data_ptr() + off, self.work.numel() - off
@@ -554,16 +570,22 @@ class Attend:
         dtype = {torch.float16: F16, torch.float32: F32}.get(q.dtype)
         if dtype is None:
             raise KVTCError(E_DTYPE, "kvtc_attend")
-        if not q.is_cuda or tuple(q.shape) != (h.batch, h.heads, h.head_dim):
-            raise KVTCError(E_SHAPE, "kvtc_attend: q must be a device tensor [B, H, D]")
+        hq = h.heads if self.q_heads is None else self.q_heads
+        if not q.is_cuda or tuple(q.shape) != (h.batch, hq, h.head_dim):
+            raise KVTCError(E_SHAPE, "kvtc_attend: q must be a device tensor [B, Hq, D]")
         if out is None:
-            out = torch.empty((h.batch, h.heads, h.head_dim), dtype=torch.float16, device=q.device)
+            out = torch.empty((h.batch, hq, h.head_dim), dtype=torch.float16, device=q.device)
         if out.dtype != torch.float16 or tuple(out.shape) != tuple(q.shape):
-            raise KVTCError(E_SHAPE, "kvtc_attend: out must be fp16 [B, H, D]")
+            raise KVTCError(E_SHAPE, "kvtc_attend: out must be fp16 [B, Hq, D]")
         qs = (C.c_int64 * 3)(*[int(x) for x in q.stride()])
         os_ = (C.c_int64 * 3)(*[int(x) for x in out.stride()])
-        _check(_lib.kvtc_attend(C.byref(self._refs[0]), C.byref(self._refs[1]), q.data_ptr(), dtype, qs, s_end,
-                                out.data_ptr(), os_, self._work, self._work_bytes, self._stream), "kvtc_attend")
+        if self.q_heads is None:
+            _check(_lib.kvtc_attend(C.byref(self._refs[0]), C.byref(self._refs[1]), q.data_ptr(), dtype, qs, s_end,
+                                    out.data_ptr(), os_, self._work, self._work_bytes, self._stream), "kvtc_attend")
+        else:
+            _check(_lib.kvtc_attend_gqa(C.byref(self._refs[0]), C.byref(self._refs[1]), self.q_heads, q.data_ptr(),
+                                        dtype, qs, s_end, out.data_ptr(), os_, self._work, self._work_bytes,
+                                        self._stream), "kvtc_attend_gqa")
         return out
 
     def noalloc(self, q, s_end: int, out):

@@ -388,8 +388,10 @@ def test_paired_entry_points_validate_both_tensors_before_launch():
 
 @no_device_only
 def test_attend_validates_before_launch():
-    """kvtc_attend rejects group-head tensors, short workspaces, rows past the
-    capacity and bad query types before anything is launched."""
+    """kvtc_attend rejects key and value tensors of different shapes, short
+    workspaces, rows past the capacity and bad query types before anything is
+    launched; kvtc_attend_gqa also query-head counts that are not a multiple of
+    the stored heads, or more than 32 queries per unit."""
     w = synth.WORKLOADS[1]
     st = O.fit(oracle_cfg(w), synth.generate(w, 0, 0, 256))
     blob = blob_from_oracle(st)
@@ -420,12 +422,27 @@ def test_attend_validates_before_launch():
     def call(kr, vr, qdt=K.F32, s_end=100, wbytes=need, work_ptr=work, qs=s3):
         return att(C.byref(kr), C.byref(vr), fake, qdt, qs, s_end, fake, s3, work_ptr, wbytes, None)
 
-    assert call(good, ref(mixed)) == K.E_STATE
+    assert call(good, ref(mixed)) == K.E_SHAPE              # 2 heads of 64 vs 8 heads of 128
     assert call(good, good, wbytes=need - 4) == K.E_BUFSIZE
     assert call(good, good, work_ptr=0) == K.E_BUFSIZE
     assert call(good, good, s_end=101) == K.E_CAPACITY
     assert call(good, good, qdt=5) == K.E_DTYPE
     assert call(good, good, qs=(C.c_int64 * 3)(128, 64, 2)) == K.E_SHAPE
+    gqa = _raw("kvtc_attend_gqa")
+    gqa.restype = C.c_int32
+    gqa.argtypes = K._sig["kvtc_attend_gqa"][1]
+    need4 = K.kvtc_attend_gqa_workspace(blob, blob, 8, 100)
+    assert need4 > need
+
+    def call_g(hq, wbytes=need4):
+        return gqa(C.byref(good), C.byref(good), hq, fake, K.F32, s3, 100, fake, s3, work, wbytes, None)
+
+    assert call_g(3) == K.E_SHAPE                   # not a multiple of the 2 stored heads
+    assert call_g(2 * 33) == K.E_SHAPE              # 33 queries per head
+    assert call_g(0) == K.E_ARG
+    assert call_g(8, wbytes=need4 - 4) == K.E_BUFSIZE
+    with pytest.raises(K.KVTCError):
+        K.kvtc_attend_gqa_workspace(blob, blob, 3, 100)
 
 
 def _state_status(blob):
