@@ -52,6 +52,11 @@ def parse():
     p.add_argument("--pmc-summary", nargs=4, metavar=("FETCH_DIR", "WRITE_DIR", "CAL_FETCH_DIR", "CAL_WRITE_DIR"),
                    help="write the HBM counter summary of the fetch kernel from four rocprofv3 --pmc "
                         "csv directories (FETCH_SIZE and WRITE_SIZE of this bench, then of --copy-calibration)")
+    p.add_argument("--trace-summary", nargs=3, metavar=("STATS_CSV", "TITLE", "COMMAND"),
+                   help="print a per-kernel table from a rocprofv3 --kernel-trace --stats kernel_stats.csv")
+    p.add_argument("--counter-summary", nargs="+", metavar="ARG",
+                   help="TITLE COMMAND DIR [DIR ...]: print a per-kernel table of the counters in the "
+                        "counter_collection.csv of each rocprofv3 --pmc output directory")
     return p.parse_args()
 
 
@@ -160,6 +165,51 @@ def pmc_summary(fetch_dir, write_dir, cal_fetch_dir, cal_write_dir):
         f"kernel_source_sha256_16: {source_hash()}",
     ]
     return "\n".join(lines) + "\n"
+
+
+def short_kernel(name):
+    """A kernel's name without namespaces, argument lists or return type, template arguments kept."""
+    n = re.sub(r"\(.*$", "", name)
+    n = n.replace("void ", "").replace("kvtc::", "").replace("(anonymous namespace)::", "")
+    n = n.replace("_Float16", "f16")
+    if "copyBuffer" in n or "copy" in n.lower():
+        return "device copy (ceiling)"
+    return n[:70]
+
+
+def trace_summary(csv_path, title, command):
+    """Per-kernel call count and durations from rocprofv3's kernel_stats.csv."""
+    import csv
+    rows = list(csv.DictReader(open(csv_path)))
+    out = [title, "command (from /tmp with TMPDIR=/tmp; R is the repository root):", "  " + command,
+           f"{'kernel':70s} {'calls':>6s} {'avg_us':>10s} {'min_us':>10s} {'max_us':>10s} {'share_%':>8s}"]
+    for r in rows:
+        out.append(f"{short_kernel(r['Name']):70s} {int(r['Calls']):6d} {float(r['AverageNs']) / 1e3:10.1f} "
+                   f"{float(r['MinNs']) / 1e3:10.1f} {float(r['MaxNs']) / 1e3:10.1f} {float(r['Percentage']):8.2f}")
+    return "\n".join(out) + "\n"
+
+
+def counter_summary(title, command, dirs):
+    """Mean per dispatch of every counter, per kernel, over rocprofv3 --pmc output directories."""
+    import collections
+    agg = collections.defaultdict(list)
+    counters = []
+    for d in dirs:
+        for r in _counter_rows(d):
+            k = short_kernel(r["Kernel_Name"])
+            agg[(k, r["Counter_Name"])].append(float(r["Counter_Value"]))
+            if r["Counter_Name"] not in counters:
+                counters.append(r["Counter_Name"])
+    kernels = sorted({k for k, _ in agg})
+    out = [title, "commands (from /tmp with TMPDIR=/tmp; R is the repository root; one pass per directory):",
+           "  " + command, "mean per dispatch over the run's dispatches of each kernel", ""]
+    for k in kernels:
+        vals = [(c, agg.get((k, c))) for c in counters]
+        out.append(k)
+        for c, v in vals:
+            if v:
+                out.append(f"    {c:28s} {sum(v) / len(v):14.6g}   ({len(v)} dispatches)")
+    return "\n".join(out) + "\n"
 
 
 # ------------------------------------------------------------------ workloads
@@ -463,6 +513,14 @@ def main():
         with open(PMC_SUMMARY, "w") as fh:
             fh.write(text)
         print(text, end="")
+        return
+    if args.trace_summary:
+        print(trace_summary(*args.trace_summary), end="")
+        return
+    if args.counter_summary:
+        if len(args.counter_summary) < 3:
+            raise SystemExit("--counter-summary TITLE COMMAND DIR [DIR ...]")
+        print(counter_summary(args.counter_summary[0], args.counter_summary[1], args.counter_summary[2:]), end="")
         return
     from kv_cache_compression_kvtc_amd.build import ensure_current
     ensure_current(log=log)                                # never time a library built from other sources
