@@ -150,6 +150,7 @@ struct FetchArgs {
     int64_t nblocks;                   // blocks of this tensor
     // dynamic LDS carve-up (bytes)
     int lds_w, lds_desc, lds_bias, lds_wave, lds_rows, lds_par, lds_out, wpitch, opitch;
+    int lds_b, lds_dummy;              // weight-stationary blocks: operand buffers, scratch words
 };
 
 // One fetch launch covers one tensor or two (the K and V of a layer): the
@@ -280,6 +281,41 @@ inline size_t fetch_lds_plan(FetchArgs &a, bool mixed, int ds, int nw, int nh, i
     return a.lds_wave + nw * static_cast<size_t>(a.lds_rows);
 }
 
+constexpr int kWsWaves = 8;                   // waves per weight-stationary block
+
+// Output columns of a weight-stationary block whose waves each hold ndbw
+// 32-column blocks of W.
+constexpr int fetch_ws_cols(int ndbw) { return 32 * ndbw * kWsWaves; }
+
+// fp16 pitch of a wave's output staging rows (ndbw 32-column blocks).
+constexpr int fetch_ws_pitch(int ndbw) { return 32 * ndbw + 8; }
+
+// Dynamic LDS carve-up of a weight-stationary block for one tensor (ks = the
+// launch's k-steps): the bias of the block's columns, two operand buffers of ks
+// k-steps [ks][64 lanes] x 8 fp16, two staging buffers of a tile's rows (plus
+// the 3-word slack of a field window) and group-head parameters (group-major),
+// one scratch word per thread for the stash of words past the tile, then each
+// wave's output staging [32][pitch] fp16.
+inline size_t fetch_ws_lds_plan(FetchArgs &a, bool mixed, int ks, int ndbw) {
+    a.wpitch = 0;
+    a.opitch = fetch_ws_pitch(ndbw);
+    a.lds_w = 0;
+    a.lds_desc = 0;
+    a.lds_bias = 0;
+    a.lds_b = fetch_ws_cols(ndbw) * 4;
+    a.lds_wave = a.lds_b + 2 * ks * 64 * 16;
+    const int rows_b = static_cast<int>(align_up((kFetTok * (a.row_stride / 4) + 8) * 4, 16));
+    const int par_b = mixed ? static_cast<int>(align_up(kFetTok * a.n_qg * 4, 16)) : 0;
+    a.lds_par = rows_b;
+    a.lds_rows = rows_b + par_b;                         // bytes per staging buffer
+    a.lds_dummy = a.lds_wave + 2 * a.lds_rows;
+    a.lds_out = a.lds_dummy + 64 * kWsWaves * 4;
+    return static_cast<size_t>(a.lds_out) + kWsWaves * kFetTok * a.opitch * 2;
+}
+
+// Row words each thread of a weight-stationary block loads per tile.
+constexpr int fetch_ws_rwb(int tile_words) { return (tile_words + 64 * kWsWaves - 1) / (64 * kWsWaves); }
+
 // Lets a kernel use up to the whole LDS of a CU as dynamic shared memory (set
 // once per kernel and device).
 bool allow_lds(const void *kern);
@@ -370,6 +406,9 @@ int32_t launch_refit_project(const AppendPlan &p, hipStream_t stream);
 // traffic probe of the fetch with the fetch's launch plan (kvtc_probe.hip):
 // ds columns per block, nw waves per block, the fetch's dynamic LDS bytes
 int32_t launch_fetch_probe(const FetchPair &m, int ds, int nw, bool mixed, int rw, size_t lds, hipStream_t stream);
+// the weight-stationary kernel's probe (group-head, ks k-steps, ndbw 32-column
+// blocks per wave, tile_words row and parameter words per tile)
+int32_t launch_fetch_ws_probe(FetchPair m, int nt, int ks, int ndbw, int tile_words, hipStream_t stream);
 
 // fetch: one launcher per contraction length in 16-slot k-steps, each compiled
 // in a translation unit of its own (kvtc_fetch_ks.hip)

@@ -151,18 +151,24 @@ int32_t plan_fetch(const void *state_host, const void *state_dev, const void *co
     a.n_qg = h->n_qgroups;
     a.nqg_inv = mixed ? 1.0f / static_cast<float>(h->n_qgroups) : 0.0f;
     // a block covers whole output rows of a head (128 columns) where the head
-    // size allows, so every token's fields are decoded once per head
-    const int DS = (h->head_dim % 128 == 0) ? 128 : 64;
+    // size allows, so every token's fields are decoded once per head; wide
+    // group-head units with long contractions take weight-stationary blocks of
+    // 512 columns
+    const bool ws = mixed && h->dg % fetch_ws_cols(2) == 0 && h->kfetch >= 128 &&
+                    fetch_ws_rwb(kFetTok * tw) <= 3;
+    const int DS = ws ? fetch_ws_cols(2) : (h->head_dim % 128 == 0) ? 128 : 64;
     a.nslices = h->dg / DS;
     const int64_t ntiles = (s_end - s_begin + kFetTok - 1) / kFetTok;
     if (ntiles > 0x7FFFFFFF) return KVTC_E_SHAPE;
     a.ntiles = static_cast<int>(ntiles);
     const int64_t work = h->units * a.nslices * ntiles;
-    const int nw = (DS == 128 && h->kfetch >= 160) ? 8 : 4;
-    // about two four-wave blocks, or one eight-wave block, per CU in one round
-    // (shared between the tensors of a paired launch)
-    const int64_t target = kFetchBlocks * 4 / nw / share;
-    const int64_t tpb = std::min<int64_t>(std::max<int64_t>(nw, (work + target - 1) / target), ntiles);
+    const int nw = ws ? kWsWaves : (DS == 128 && h->kfetch >= 160) ? 8 : 4;
+    // about two four-wave blocks, or one eight-wave block (weight-stationary
+    // included), per CU in one round (shared between the tensors of a paired
+    // launch); a weight-stationary block runs at least two tiles
+    const int64_t target = (ws ? kFetchBlocks / 2 : kFetchBlocks * 4 / nw) / share;
+    const int64_t tmin = ws ? 2 : nw;
+    const int64_t tpb = std::min<int64_t>(std::max<int64_t>(tmin, (work + target - 1) / target), ntiles);
     a.tiles_per_block = static_cast<int>(tpb);
     a.nchunks = static_cast<int>((ntiles + tpb - 1) / tpb);
     a.nblocks = h->units * a.nslices * a.nchunks;
@@ -189,6 +195,10 @@ int32_t launch_probe_plans(const FetchPlan &p0, const FetchPlan *p1, hipStream_t
     }
     m.nblocks_per_xcd = (m.nblocks_real + 7) / 8;
     if (m.nblocks_per_xcd * 8 > 0x7FFFFFFF) return KVTC_E_SHAPE;
+    if (p0.ds == fetch_ws_cols(2)) {
+        if (!p0.mixed) return KVTC_E_SHAPE;
+        return launch_fetch_ws_probe(m, p1 ? 2 : 1, ks, 2, 64 * std::max(p0.rw, p1 ? p1->rw : 0), stream);
+    }
     // the fetch kernel's waves per block and its dynamic LDS, so that as many
     // probe blocks share a CU as fetch blocks would
     const int ndb = p0.ds / 32;
@@ -217,9 +227,7 @@ int32_t launch_fetch_plans(const FetchPlan &p0, const FetchPlan *p1, hipStream_t
     }
     m.nblocks_per_xcd = (m.nblocks_real + 7) / 8;
     if (m.nblocks_per_xcd * 8 > 0x7FFFFFFF) return KVTC_E_SHAPE;
-    if (p0.ds == 128)
-        return launch_fetch(p0.mixed, 4, m, nt, ks, rw, stream);
-    return launch_fetch(p0.mixed, 2, m, nt, ks, rw, stream);
+    return launch_fetch(p0.mixed, p0.ds / 32, m, nt, ks, rw, stream);
 }
 
 }  // namespace

@@ -8,7 +8,7 @@
 // share CUs as the fetch does).  Its rate is the
 // practical ceiling of the fetch's traffic on this memory system, against
 // which the fetch kernel is measured.  What it writes is not a reconstruction.
-#include "kvtc_device.h"
+#include "kvtc_fetch_ws.h"
 
 namespace kvtc {
 namespace {
@@ -124,6 +124,21 @@ int32_t launch_probe_rw(const FetchPair &m, int ds, int nw, bool mixed, size_t l
 }
 
 }  // namespace
+
+// The weight-stationary kernel's probe is that kernel with its arithmetic
+// compiled out: the same blocks, staging, barriers and stores (of the bias).
+int32_t launch_fetch_ws_probe(FetchPair m, int nt, int ks, int ndbw, int tile_words, hipStream_t stream) {
+    if (ndbw != 2) return KVTC_E_SHAPE;
+    size_t lds = 0;
+    for (int i = 0; i < nt; ++i) lds = std::max(lds, fetch_ws_lds_plan(m.t[i], true, ks, ndbw));
+    if (lds > kLdsMax) return KVTC_E_SHAPE;
+    const int rwb = fetch_ws_rwb(tile_words);
+    if (rwb > 3) return KVTC_E_SHAPE;
+    auto kern = rwb <= 2 ? fetch_ws_kernel<true, 16, 2, 2, 2, true> : fetch_ws_kernel<true, 16, 2, 3, 2, true>;
+    if (!allow_lds(reinterpret_cast<const void *>(kern))) return KVTC_E_DEVICE;
+    hipLaunchKernelGGL(kern, dim3(static_cast<unsigned>(m.nblocks_per_xcd * 8)), dim3(64 * kWsWaves), lds, stream, m);
+    return hipGetLastError() == hipSuccess ? KVTC_OK : KVTC_E_DEVICE;
+}
 
 int32_t launch_fetch_probe(const FetchPair &m, int ds, int nw, bool mixed, int rw, size_t lds, hipStream_t stream) {
     switch (rw) {

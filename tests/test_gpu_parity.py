@@ -387,6 +387,10 @@ KV_CASES = [
     # instantiated for the value tensor's longer contraction (176 slots: eight waves)
     ("straddle-4-8-waves", small(4, B=3, s_prefill=2048, s_total=2048 + 45),
      small(2, B=3, s_prefill=2048, s_total=2048 + 45)),
+    # weight-stationary group-head blocks of two contractions in one launch: the
+    # value tensor's 160-slot k-steps end inside the key tensor's 256
+    ("palu-ranks-256-160", small(3, H=16, s_prefill=2048, s_total=2048 + 45),
+     small(3, H=16, s_prefill=2048, s_total=2048 + 45, rank=160)),
     # different modes: the call falls back to one launch per tensor
     ("dp-key-mixed-value", small(2, s_prefill=2048, s_total=2048 + 45),
      small(3, H=8, s_prefill=2048, s_total=2048 + 45)),
