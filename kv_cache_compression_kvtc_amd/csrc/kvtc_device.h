@@ -292,10 +292,11 @@ constexpr int fetch_ws_pitch(int ndbw) { return 32 * ndbw + 8; }
 
 // Dynamic LDS carve-up of a weight-stationary block for one tensor (ks = the
 // launch's k-steps): the bias of the block's columns, two operand buffers of ks
-// k-steps [ks][64 lanes] x 8 fp16, two staging buffers of a tile's rows (plus
-// the 3-word slack of a field window) and group-head parameters (group-major),
-// one scratch word per thread for the stash of words past the tile, then each
-// wave's output staging [32][pitch] fp16.
+// k-steps [ks][64 lanes] x 8 fp16, two staging buffers, each a tile's rows (plus
+// the slack of a field window), its group-head parameters (group-major) and one
+// scratch word per thread for the stash of words past the tile, then each
+// wave's output staging [32][pitch] fp16.  lds_par and lds_dummy are offsets
+// inside a staging buffer, lds_rows the buffer's size.
 inline size_t fetch_ws_lds_plan(FetchArgs &a, bool mixed, int ks, int ndbw) {
     a.wpitch = 0;
     a.opitch = fetch_ws_pitch(ndbw);
@@ -307,11 +308,15 @@ inline size_t fetch_ws_lds_plan(FetchArgs &a, bool mixed, int ks, int ndbw) {
     const int rows_b = static_cast<int>(align_up((kFetTok * (a.row_stride / 4) + 8) * 4, 16));
     const int par_b = mixed ? static_cast<int>(align_up(kFetTok * a.n_qg * 4, 16)) : 0;
     a.lds_par = rows_b;
-    a.lds_rows = rows_b + par_b;                         // bytes per staging buffer
-    a.lds_dummy = a.lds_wave + 2 * a.lds_rows;
-    a.lds_out = a.lds_dummy + 64 * kWsWaves * 4;
+    a.lds_dummy = rows_b + par_b;
+    a.lds_rows = rows_b + par_b + 64 * kWsWaves * 4;     // bytes per staging buffer
+    a.lds_out = a.lds_wave + 2 * a.lds_rows;
     return static_cast<size_t>(a.lds_out) + kWsWaves * kFetTok * a.opitch * 2;
 }
+
+// LDS a weight-stationary block's prologue stages its W rows through: per
+// wave 32 rows of 16 ks slots (pitch padded by 16 bytes).
+constexpr size_t fetch_ws_w_staging(int ks) { return static_cast<size_t>(kWsWaves) * 32 * (ks * 32 + 16); }
 
 // Row words each thread of a weight-stationary block loads per tile.
 constexpr int fetch_ws_rwb(int tile_words) { return (tile_words + 64 * kWsWaves - 1) / (64 * kWsWaves); }

@@ -131,10 +131,11 @@ int32_t launch_fetch_ws_probe(FetchPair m, int nt, int ks, int ndbw, int tile_wo
     if (ndbw != 2) return KVTC_E_SHAPE;
     size_t lds = 0;
     for (int i = 0; i < nt; ++i) lds = std::max(lds, fetch_ws_lds_plan(m.t[i], true, ks, ndbw));
+    lds = std::max(lds, fetch_ws_w_staging(ks));        // as the kernel requests, for the same occupancy
     if (lds > kLdsMax) return KVTC_E_SHAPE;
     const int rwb = fetch_ws_rwb(tile_words);
     if (rwb > 3) return KVTC_E_SHAPE;
-    auto kern = rwb <= 2 ? fetch_ws_kernel<true, 16, 2, 2, 2, true> : fetch_ws_kernel<true, 16, 2, 3, 2, true>;
+    auto kern = rwb <= 2 ? fetch_ws_kernel<true, 16, 2, 2, true> : fetch_ws_kernel<true, 16, 2, 3, true>;
     if (!allow_lds(reinterpret_cast<const void *>(kern))) return KVTC_E_DEVICE;
     hipLaunchKernelGGL(kern, dim3(static_cast<unsigned>(m.nblocks_per_xcd * 8)), dim3(64 * kWsWaves), lds, stream, m);
     return hipGetLastError() == hipSuccess ? KVTC_OK : KVTC_E_DEVICE;
