@@ -318,8 +318,9 @@ __global__ __launch_bounds__(64 * NW, 2) void fetch_kernel(FetchPair m) {
 #pragma unroll
     for (int p = 0; p < PF; ++p)
         if (t0 <= last) fetch_tile(min(t0 + p * NW, last), ring[p]);
-    int tile = t0;
-    for (; tile + (PF - 1) * NW < full_end; tile += PF * NW) {
+    // one round: the PF tiles from tile on, each stashed, its ring slot refilled
+    // PF tiles ahead, then processed
+    auto round = [&](int tile) __attribute__((always_inline)) {
 #pragma unroll
         for (int p = 0; p < PF; ++p) {
             const int tt = tile + p * NW;
@@ -327,6 +328,17 @@ __global__ __launch_bounds__(64 * NW, 2) void fetch_kernel(FetchPair m) {
             fetch_tile(min(tt + PF * NW, last), ring[p]);
             process(tt, std::true_type{});
         }
+    };
+    // The first round is peeled: the loop is then entered only after a round
+    // like its own body, so its waits are those of the steady state (each slot
+    // waits for its own rows, requested PF tiles back).  Entered straight from
+    // the prologue, the loads would be the youngest memory operations and the
+    // waits would drain everything, the previous tiles' stores included.
+    int tile = t0;
+    if (tile + (PF - 1) * NW < full_end) {
+        round(tile);
+        tile += PF * NW;
+        for (; tile + (PF - 1) * NW < full_end; tile += PF * NW) round(tile);
     }
 #pragma unroll
     for (int p = 0; p < PF; ++p) {
