@@ -56,6 +56,46 @@ __device__ inline uint32_t row_field(const uint32_t *row, uint32_t sb) {
     return __builtin_amdgcn_alignbit(row[wi + 1], row[wi], sh) & ((1u << w) - 1u);
 }
 
+// Staging of a chunk's code rows (256-thread blocks): word i of the chunk goes
+// to row i / row_words, word i % row_words, of an LDS array of odd pitch.  A
+// thread holds SB words per batch (words base + k*256 + tid), all loaded before
+// any is stored, so a chunk of up to 256*SB words costs one memory round trip
+// (issued early, the loads overlap other work).  The quotient from a float
+// reciprocal is exact for word indices below 2^16.
+constexpr int kStageB = 24;
+
+__device__ inline void stage_load(const uint32_t *src, int total, int base, uint32_t (&r)[kStageB]) {
+#pragma unroll
+    for (int k = 0; k < kStageB; ++k) {
+        const int i = base + k * 256 + static_cast<int>(threadIdx.x);
+        r[k] = i < total ? src[i] : 0u;
+    }
+}
+
+__device__ inline void stage_store(int total, int base, int row_words, int pitch, uint32_t *rows,
+                                   const uint32_t (&r)[kStageB]) {
+    const float inv = 1.0f / static_cast<float>(max(row_words, 1));
+#pragma unroll
+    for (int k = 0; k < kStageB; ++k) {
+        const int i = base + k * 256 + static_cast<int>(threadIdx.x);
+        if (i < total) {
+            const int q = static_cast<int>((static_cast<float>(i) + 0.5f) * inv);
+            rows[q * pitch + (i - q * row_words)] = r[k];
+        }
+    }
+}
+
+// The whole chunk: batch 0 from registers already loaded, the rest (chunks of
+// more than 256*kStageB words) loaded and stored batch by batch.
+__device__ inline void stage_rows(const uint32_t *src, int total, int row_words, int pitch, uint32_t *rows,
+                                  uint32_t (&r)[kStageB]) {
+    stage_store(total, 0, row_words, pitch, rows, r);
+    for (int base = 256 * kStageB; base < total; base += 256 * kStageB) {
+        stage_load(src, total, base, r);
+        stage_store(total, base, row_words, pitch, rows, r);
+    }
+}
+
 __device__ inline float block_reduce(float v, float *red, bool is_max) {
     for (int m = 32; m >= 1; m >>= 1) {
         const float o = __shfl_xor(v, m, 64);
@@ -140,25 +180,31 @@ __global__ __launch_bounds__(256) void attend_partial_kernel(AttendArgs a) {
     const int64_t s0 = static_cast<int64_t>(c) * kAttChunk;
     const int nrows = static_cast<int>(min<int64_t>(kAttChunk, a.s_end - s0));
     const int nv = V.ui[u].n_slots;
-    // word i of a chunk's rows goes to (i / row_words, i % row_words); the
-    // quotient from a float reciprocal is exact for i < 2^16
-    auto stage = [&](const AttendSide &T, int pitch) {
-        const uint32_t *src = reinterpret_cast<const uint32_t *>(T.codes) + (static_cast<int64_t>(u) * T.capacity + s0) * T.row_words;
-        const float inv = 1.0f / static_cast<float>(max(T.row_words, 1));
-        for (int i = tid; i < nrows * T.row_words; i += blockDim.x) {
-            const int r = static_cast<int>((static_cast<float>(i) + 0.5f) * inv);
-            rows[r * pitch + (i - r * T.row_words)] = src[i];
-        }
-    };
     const int kp = (K.row_words + 1) | 1, vp = (V.row_words + 1) | 1;   // odd, > row_words
 
-    for (int i = tid; i <= K.kslots; i += blockDim.x) qt_l[i] = a.qt[static_cast<int64_t>(u) * (K.kslots + 1) + i];
+    // the unit's coefficients and slot descriptors (at most 257, 256 and 256
+    // words: two, one and one per thread), then the chunk's key and value rows,
+    // all requested before any is used
+    uint32_t cq[2], cf, cs;
     {
-        const uint32_t *src = reinterpret_cast<const uint32_t *>(a.qf + static_cast<int64_t>(u) * 2 * K.kfetch);
-        for (int i = tid; i < K.kfetch; i += blockDim.x) ksb[i] = src[i];   // 2*kfetch halves
+        const float *qsrc = a.qt + static_cast<int64_t>(u) * (K.kslots + 1);
+        const uint32_t *fsrc = reinterpret_cast<const uint32_t *>(a.qf + static_cast<int64_t>(u) * 2 * K.kfetch);
+        cq[0] = tid <= K.kslots ? __float_as_uint(qsrc[tid]) : 0u;
+        cq[1] = tid + 256 <= K.kslots ? __float_as_uint(qsrc[tid + 256]) : 0u;
+        cf = tid < K.kfetch ? fsrc[tid] : 0u;                           // 2*kfetch halves
+        cs = tid < V.kslots ? V.sbits[static_cast<int64_t>(u) * V.kslots + tid] : 0u;
     }
-    for (int i = tid; i < V.kslots; i += blockDim.x) vsb[i] = V.sbits[static_cast<int64_t>(u) * V.kslots + i];
-    stage(K, kp);
+    const uint32_t *ksrc = reinterpret_cast<const uint32_t *>(K.codes) + (static_cast<int64_t>(u) * K.capacity + s0) * K.row_words;
+    const uint32_t *vsrc = reinterpret_cast<const uint32_t *>(V.codes) + (static_cast<int64_t>(u) * V.capacity + s0) * V.row_words;
+    const int ktot = nrows * K.row_words, vtot = nrows * V.row_words;
+    uint32_t kr[kStageB], vr[kStageB];
+    stage_load(ksrc, ktot, 0, kr);
+    stage_load(vsrc, vtot, 0, vr);
+    if (tid <= K.kslots) qt_l[tid] = __uint_as_float(cq[0]);
+    if (tid + 256 <= K.kslots) qt_l[tid + 256] = __uint_as_float(cq[1]);
+    if (tid < K.kfetch) ksb[tid] = cf;
+    if (tid < V.kslots) vsb[tid] = cs;
+    stage_rows(ksrc, ktot, K.row_words, kp, rows, kr);
     __syncthreads();
 
     // scores of this thread's two rows, k-step by k-step in the fetch order: the
@@ -216,7 +262,7 @@ __global__ __launch_bounds__(256) void attend_partial_kernel(AttendArgs a) {
         pl[r] = p;
         lsum += p;
     }
-    stage(V, vp);
+    stage_rows(vsrc, vtot, V.row_words, vp, rows, vr);   // the key rows are no longer read
     const float L = block_reduce(lsum, red, false);
     __syncthreads();
 
@@ -436,20 +482,45 @@ __global__ __launch_bounds__(256) void attend_gen_prep_kernel(GenArgs a) {
         }
 }
 
-// Stages the code rows (odd pitch) and, for group-head rows, their (min, scale)
-// words group-major, of rows [s0, s0 + n) of unit u.
-__device__ inline void gen_stage(const GenSide &T, int u, int64_t s0, int n, uint32_t *rows, int pitch,
-                                 uint32_t *prm) {
-    const uint32_t *src = reinterpret_cast<const uint32_t *>(T.codes) + (static_cast<int64_t>(u) * T.capacity + s0) * T.row_words;
-    for (int i = threadIdx.x; i < n * T.row_words; i += blockDim.x) {
-        const int r = i / T.row_words;
-        rows[r * pitch + (i - r * T.row_words)] = src[i];
+// n words from global memory into LDS, eight per thread in flight per batch.
+__device__ inline void lds_copy(uint32_t *dst, const uint32_t *src, int n) {
+    for (int base = 0; base < n; base += 256 * 8) {
+        uint32_t r[8];
+#pragma unroll
+        for (int k = 0; k < 8; ++k) {
+            const int i = base + k * 256 + static_cast<int>(threadIdx.x);
+            r[k] = i < n ? src[i] : 0u;
+        }
+#pragma unroll
+        for (int k = 0; k < 8; ++k) {
+            const int i = base + k * 256 + static_cast<int>(threadIdx.x);
+            if (i < n) dst[i] = r[k];
+        }
     }
+}
+
+// The code rows of rows [s0, s0 + n) of unit u (batch 0 already in r) at an
+// odd pitch and, for group-head rows, their (min, scale) words group-major.
+__device__ inline void gen_stage(const GenSide &T, const uint32_t *src, int n, uint32_t *rows, int pitch,
+                                 uint32_t *prm, const uint32_t *ps, uint32_t (&r)[kStageB]) {
+    stage_rows(src, n * T.row_words, T.row_words, pitch, rows, r);
     if (T.mixed) {
-        const uint32_t *ps = T.params + (static_cast<int64_t>(u) * T.capacity + s0) * T.n_qg;
-        for (int i = threadIdx.x; i < n * T.n_qg; i += blockDim.x) {
-            const int r = i / T.n_qg;
-            prm[(i - r * T.n_qg) * kGenRows + r] = ps[i];
+        const int total = n * T.n_qg;
+        for (int base = 0; base < total; base += 256 * 8) {
+            uint32_t pv[8];
+#pragma unroll
+            for (int k = 0; k < 8; ++k) {
+                const int i = base + k * 256 + static_cast<int>(threadIdx.x);
+                pv[k] = i < total ? ps[i] : 0u;
+            }
+#pragma unroll
+            for (int k = 0; k < 8; ++k) {
+                const int i = base + k * 256 + static_cast<int>(threadIdx.x);
+                if (i < total) {
+                    const int q = i / T.n_qg;
+                    prm[(i - q * T.n_qg) * kGenRows + q] = pv[k];
+                }
+            }
         }
     }
 }
@@ -478,12 +549,22 @@ __global__ __launch_bounds__(256) void attend_gen_partial_kernel(GenArgs a) {
     const int64_t s0 = static_cast<int64_t>(c) * kGenRows;
     const int nrows = static_cast<int>(min<int64_t>(kGenRows, a.s_end - s0));
 
-    for (int i = t; i < Q * K.kslots; i += blockDim.x) qt[i] = a.qt[static_cast<int64_t>(u) * Q * K.kslots + i];
-    for (int i = t; i < Q; i += blockDim.x) qb[i] = a.qb[static_cast<int64_t>(u) * Q + i];
+    // the chunk's key and value rows are requested first; the unit's
+    // coefficients and slot descriptors are copied while they are in flight
+    const uint32_t *ksrc = reinterpret_cast<const uint32_t *>(K.codes) + (static_cast<int64_t>(u) * K.capacity + s0) * K.row_words;
+    const uint32_t *vsrc = reinterpret_cast<const uint32_t *>(V.codes) + (static_cast<int64_t>(u) * V.capacity + s0) * V.row_words;
+    uint32_t kr[kStageB], vr[kStageB];
+    stage_load(ksrc, nrows * K.row_words, 0, kr);
+    stage_load(vsrc, nrows * V.row_words, 0, vr);
+    lds_copy(reinterpret_cast<uint32_t *>(qt), reinterpret_cast<const uint32_t *>(a.qt + static_cast<int64_t>(u) * Q * K.kslots),
+             Q * K.kslots);
+    lds_copy(reinterpret_cast<uint32_t *>(qb), reinterpret_cast<const uint32_t *>(a.qb + static_cast<int64_t>(u) * Q), Q);
     if (K.mixed)
-        for (int i = t; i < Q * K.n_qg; i += blockDim.x) qp[i] = a.qp[static_cast<int64_t>(u) * Q * K.n_qg + i];
-    for (int j = t; j < K.kslots; j += blockDim.x) sb[j] = K.sbits[static_cast<int64_t>(u) * K.kslots + j];
-    gen_stage(K, u, s0, nrows, rows, pitch, prm);
+        lds_copy(reinterpret_cast<uint32_t *>(qp), reinterpret_cast<const uint32_t *>(a.qp + static_cast<int64_t>(u) * Q * K.n_qg),
+                 Q * K.n_qg);
+    lds_copy(sb, K.sbits + static_cast<int64_t>(u) * K.kslots, K.kslots);
+    gen_stage(K, ksrc, nrows, rows, pitch, prm,
+              K.mixed ? K.params + (static_cast<int64_t>(u) * K.capacity + s0) * K.n_qg : nullptr, kr);
     __syncthreads();
 
     float acc[QM];
@@ -541,8 +622,9 @@ __global__ __launch_bounds__(256) void attend_gen_partial_kernel(GenArgs a) {
     }
     __syncthreads();
     // value rows
-    for (int j = t; j < V.kslots; j += blockDim.x) sb[j] = V.sbits[static_cast<int64_t>(u) * V.kslots + j];
-    gen_stage(V, u, s0, nrows, rows, pitch, prm);
+    lds_copy(sb, V.sbits + static_cast<int64_t>(u) * V.kslots, V.kslots);
+    gen_stage(V, vsrc, nrows, rows, pitch, prm,
+              V.mixed ? V.params + (static_cast<int64_t>(u) * V.capacity + s0) * V.n_qg : nullptr, vr);
     __syncthreads();
     float va[QM];
 #pragma unroll
