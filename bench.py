@@ -369,8 +369,10 @@ def time_attend(K, layer, S, dev, reps=20):
             "launches": "prep + partial + merge"}
 
 
-def time_one_shot(K, wid, dev, reps=5):
-    """Other workloads: one-shot append of the rows after the fit prefix + full fetch."""
+def time_one_shot(K, wid, dev, reps=10):
+    """Other workloads: one-shot append of the rows after the fit prefix + full
+    fetch, each kernel timed in a loop of its own (appending the same rows again
+    stores the same codes), then the fetch's traffic-only probe."""
     import torch
     from kv_cache_compression_kvtc_amd import synth
     w = synth.WORKLOADS[wid]
@@ -379,31 +381,25 @@ def time_one_shot(K, wid, dev, reps=5):
     a0 = 0 if w.s_prefill == S else w.s_prefill
     if a0:
         layer.append(0, a0)
+    layer.append(a0, S)
     torch.cuda.synchronize()
-    res = {"append_ms": [], "fetch_ms": []}
-    for r in range(reps + 1):
-        e = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
-        e[0].record()
-        layer.append(a0, S)
-        e[1].record()
-        layer.fetch(0, S)
-        e[2].record()
+
+    def med_ms(fn):
+        fn()
         torch.cuda.synchronize()
-        if r:
-            res["append_ms"].append(e[0].elapsed_time(e[1]))
-            res["fetch_ms"].append(e[1].elapsed_time(e[2]))
-    ap, fe = float(np.median(res["append_ms"])), float(np.median(res["fetch_ms"]))
-    # the fetch's traffic alone (probe), timed after the fetch timings
-    pr = []
-    for r in range(reps + 1):
-        e = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
-        e[0].record()
-        layer.fetch.probe(0, S)
-        e[1].record()
+        evs = []
+        for _ in range(reps):
+            e = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+            e[0].record()
+            fn()
+            e[1].record()
+            evs.append(e)
         torch.cuda.synchronize()
-        if r:
-            pr.append(e[0].elapsed_time(e[1]))
-    pm = float(np.median(pr))
+        return float(np.median([e[0].elapsed_time(e[1]) for e in evs]))
+
+    ap = med_ms(lambda: layer.append(a0, S))
+    fe = med_ms(lambda: layer.fetch(0, S))
+    pm = med_ms(lambda: layer.fetch.probe(0, S))
     fb = layer.fetch_bytes(S)
     ab = layer.append_bytes(S - a0)
     return {"workload": w.name, "B": w.B, "H": w.H, "D": w.D, "S": S, "append_rows": S - a0,
@@ -413,6 +409,64 @@ def time_one_shot(K, wid, dev, reps=5):
             "fetch_frac_hbm": round(fb / fe / 1e6 / PEAK_HBM_GBPS, 4),
             "probe_ms": round(pm, 4), "fetch_frac_of_probe": round(pm / fe, 4),
             "prefill_fit_ms": [round(p.fit_s * 1e3, 1) for p in layer.paths]}
+
+
+def time_modes(K, dev, reps=5):
+    """The other storage modes at the batched-decode shape (key tensor, 512 units,
+    8192 stored rows): a refit-mode decode step (kvtc_append_refit of one row,
+    which refits every range and re-packs all 8193 rows, then kvtc_fetch_refit
+    of all rows) and the entropy-coded storage of the 8193 rows
+    (kvtc_entropy_encode: device counts, host code tables, device encode; then
+    kvtc_entropy_decode back into a code store).  Medians of reps calls."""
+    import torch
+    from kv_cache_compression_kvtc_amd import synth
+    w = synth.WORKLOADS[4]
+    S0, cap = w.s_prefill, w.s_prefill + 1
+    p = TensorPath(K, w, synth.KEY, S0, cap, cap, dev)
+    K.kvtc_append(p.blob, p.blob_dev, p.x, 0, p.codes, p.params, cap)
+    rs = K.RefitStore(p.blob, p.blob_dev, cap)
+    rs.append(p.x[:, :, :S0], 0)
+    torch.cuda.synchronize()
+
+    def med_ms(fn, sync=False):
+        fn()
+        torch.cuda.synchronize()
+        ts = []
+        for _ in range(reps):
+            if sync:
+                t = time.perf_counter()
+                fn()
+                torch.cuda.synchronize()
+                ts.append((time.perf_counter() - t) * 1e3)
+            else:
+                e = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+                e[0].record()
+                fn()
+                e[1].record()
+                torch.cuda.synchronize()
+                ts.append(e[0].elapsed_time(e[1]))
+        return float(np.median(ts))
+
+    out = p.out[:, :, :cap]
+    step = med_ms(lambda: rs.append(p.x[:, :, S0:cap], S0))
+    fetch = med_ms(lambda: rs.fetch(0, cap, out))
+    frozen_fetch = med_ms(lambda: K.kvtc_fetch(p.blob, p.blob_dev, p.codes, p.params, cap, 0, cap, out))
+    arch = K.EntropyArchive(p.blob, p.blob_dev, p.codes, cap, cap)
+    enc = med_ms(lambda: K.EntropyArchive(p.blob, p.blob_dev, p.codes, cap, cap), sync=True)
+    codes2 = torch.zeros_like(p.codes)
+    dec = med_ms(lambda: arch.decode(codes2, cap))
+    same = bool(torch.equal(codes2, p.codes))
+    h = p.h
+    return {"workload": "batched-decode, key tensor: refit mode and entropy-coded storage",
+            "units": h.units, "rows": cap,
+            "refit_append_1_row_ms": round(step, 4),
+            "refit_fetch_ms": round(fetch, 4), "frozen_fetch_ms": round(frozen_fetch, 4),
+            "refit_latent_store_bytes": h.units * cap * h.kslots * 8,
+            "entropy_encode_ms": round(enc, 3), "entropy_decode_ms": round(dec, 4),
+            "entropy_archive_bytes": int(arch.header.archive_bytes),
+            "fixed_width_bytes": int(h.units * cap * h.row_stride),
+            "units_entropy_coded": int(arch.header.units_coded),
+            "decode_round_trip_exact": same}
 
 
 def time_decode_steps(K, dev, steps=64):
@@ -586,7 +640,7 @@ def main():
     if not args.no_extra:
         extra = []
         for fn in (lambda: time_one_shot(K, 5, dev), lambda: time_one_shot(K, 3, dev),
-                   lambda: time_decode_steps(K, dev)):
+                   lambda: time_decode_steps(K, dev), lambda: time_modes(K, dev)):
             torch.cuda.empty_cache()
             extra.append(fn())
             log(json.dumps(extra[-1]))
