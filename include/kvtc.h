@@ -254,7 +254,10 @@ int32_t kvtc_append(const void *state_host, const void *state_dev,
  *   out_dev    fp16 [B, H, s_end - s_begin, D] with element strides out_strides
  *              (out_strides[3] must be 1, rows 16-byte aligned); row s of the
  *              store goes to out index s - s_begin.
- * Needs 0 <= s_begin <= s_end <= capacity. */
+ * Needs 0 <= s_begin <= s_end <= capacity.  KVTC_E_SHAPE for head_dim not a
+ * multiple of 64 or more than 256 fetch slots, and where a stored row and its
+ * group-head parameters exceed 192 bytes (the 32-row tile the kernels stage in
+ * registers; appending and entropy coding take rows up to 256 bytes). */
 int32_t kvtc_fetch(const void *state_host, const void *state_dev,
                    const void *codes_dev, const void *params_dev, int64_t capacity,
                    int64_t s_begin, int64_t s_end,

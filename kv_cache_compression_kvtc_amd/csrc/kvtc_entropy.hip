@@ -7,7 +7,8 @@
 // here; the archive layout is the one kvtc.h documents.  Codes are emitted
 // most significant bit first into an LSB-first bit stream, so a code of length
 // L is written as its bit reversal; every write is an atomic OR into a 32-bit
-// word of the zeroed archive, since neighbouring codes share words.
+// word of the zeroed archive, since neighbouring codes share words.  The
+// decoder works per (unit, chunk of rows) in LDS and writes whole row words.
 #include <vector>
 
 #include "kvtc_device.h"
@@ -158,41 +159,98 @@ __global__ __launch_bounds__(kEntThreads) void entropy_plain_kernel(EntropyDevAr
     }
 }
 
-// One thread per (unit, slot, chunk) of a coded unit: canonical decoding of the
-// chunk's codes into the zeroed rows.
-__global__ __launch_bounds__(kEntThreads) void entropy_decode_kernel(EntropyDevArgs a) {
-    const int64_t t = static_cast<int64_t>(blockIdx.x) * kEntThreads + threadIdx.x;
-    const int64_t per_unit = static_cast<int64_t>(a.kslots) * a.nchunks;
-    if (t >= a.units * per_unit) return;
-    const int u = static_cast<int>(t / per_unit);
-    const int j = static_cast<int>((t % per_unit) / a.nchunks), c = static_cast<int>(t % a.nchunks);
-    if (!a.unit[u].coded || j >= a.ui[u].n_slots) return;
-    const kvtc_entropy_dec &d = a.dec[static_cast<int64_t>(u) * a.kslots + j];
-    const uint8_t *syms = a.syms + static_cast<int64_t>(u) * a.nsym + d.sym_off;
-    const int rw = a.row_stride >> 2;
-    const uint32_t sb = a.sbits[static_cast<int64_t>(u) * a.kslots + j];
-    const uint32_t off = sb & kOffsetMask;
-    uint32_t *rows = reinterpret_cast<uint32_t *>(a.codes) + static_cast<int64_t>(u) * a.capacity * rw;
-    const int64_t s1 = min(a.S, static_cast<int64_t>(c + 1) * kEntropyChunk);
-    const uint32_t maxl = d.max_len;
-    uint64_t pos = a.chunk_pos[t];
-    for (int64_t s = static_cast<int64_t>(c) * kEntropyChunk; s < s1; ++s) {
-        uint32_t v = 0, sym = 0;
-        for (uint32_t L = 1; L <= maxl; ++L) {
-            v = (v << 1) | read_bits(a.archive, a.archive_words, pos++, 1);
-            const uint32_t k = v - d.first[L];
-            if (v >= d.first[L] && k < d.count[L]) {
-                sym = syms[d.base[L] + k];
-                break;
-            }
-        }
-        // into the row: the field at its bit offset (bits above the width are zero)
-        uint32_t *row = rows + s * rw;
-        const uint32_t wi = off >> 5, sh = off & 31u;
-        const uint64_t x = static_cast<uint64_t>(sym) << sh;
-        atomicOr(row + wi, static_cast<uint32_t>(x));
-        if ((x >> 32) != 0u) atomicOr(row + wi + 1, static_cast<uint32_t>(x >> 32));
+// word w of the archive, zero past its end (a corrupt index)
+__device__ inline uint32_t arc_word(const uint32_t *arc, uint64_t nwords, uint64_t w) { return w < nwords ? arc[w] : 0u; }
+
+// Decoding state of one slot's stream in one chunk: a 64-bit window of the
+// archive refilled one aligned word at a time.
+struct BitWindow {
+    uint64_t win, next;
+    uint32_t nb;                                                        // valid bits in win
+};
+
+__device__ inline BitWindow window_at(const EntropyDevArgs &a, uint64_t pos) {
+    BitWindow w;
+    w.next = (pos >> 5) + 2;
+    w.win = ((static_cast<uint64_t>(arc_word(a.archive, a.archive_words, w.next - 1)) << 32) |
+             arc_word(a.archive, a.archive_words, w.next - 2)) >> (pos & 31u);
+    w.nb = 64u - static_cast<uint32_t>(pos & 31u);
+    return w;
+}
+
+// The next code of the stream, matched length by length against the slot's
+// canonical table (a code that matches no length decodes to 0)
+__device__ inline uint32_t next_symbol(const EntropyDevArgs &a, BitWindow &w, const kvtc_entropy_dec &d,
+                                       const uint8_t *syms) {
+    if (w.nb <= 32u) {                                                 // at least 33 bits before a code
+        w.win |= static_cast<uint64_t>(arc_word(a.archive, a.archive_words, w.next++)) << w.nb;
+        w.nb += 32u;
     }
+    uint32_t v = 0;
+    for (uint32_t L = 1; L <= d.max_len; ++L) {
+        v = (v << 1) | static_cast<uint32_t>(w.win & 1u);
+        w.win >>= 1;
+        --w.nb;
+        const uint32_t k = v - d.first[L];
+        if (v >= d.first[L] && k < d.count[L]) return syms[d.base[L] + k];
+    }
+    return 0u;
+}
+
+// One block per (chunk of kEntropyChunk rows, unit) of a coded unit.  Thread j
+// decodes slot j's codes of the chunk against the slot's canonical table,
+// staged in LDS, and its symbol list, in LDS (SLDS) or global memory.  Fields
+// are OR-ed into the chunk's rows in LDS (slots share row words); the block then
+// writes every word of those rows once.  The decode is a serial chain per
+// slot and chunk (each code's position follows from the previous code's
+// length); two chunks per block with the chains interleaved measured slower
+// (larger blocks, fewer resident).
+template <bool SLDS>
+__global__ __launch_bounds__(kEntThreads) void entropy_decode_kernel(EntropyDevArgs a) {
+    extern __shared__ __align__(16) uint32_t sm[];
+    const int c = blockIdx.x, u = blockIdx.y, tid = threadIdx.x;
+    if (!a.unit[u].coded) return;                                      // block-uniform
+    const int64_t s0 = static_cast<int64_t>(c) * kEntropyChunk;
+    const int n = static_cast<int>(min<int64_t>(kEntropyChunk, a.S - s0));
+    const int ns = a.ui[u].n_slots, rw = a.row_stride >> 2;
+    uint32_t *rows = sm;                                                // [kEntropyChunk][rw]
+    kvtc_entropy_dec *dec = reinterpret_cast<kvtc_entropy_dec *>(sm + kEntropyChunk * rw);   // [ns]
+    uint8_t *lsyms = reinterpret_cast<uint8_t *>(dec + a.kslots);                            // [nsym]
+    constexpr int kDecWords = sizeof(kvtc_entropy_dec) / 4;
+    const uint8_t *gsyms = a.syms + static_cast<int64_t>(u) * a.nsym;
+    for (int i = tid; i < n * rw; i += kEntThreads) rows[i] = 0u;
+    {
+        const uint32_t *src = reinterpret_cast<const uint32_t *>(a.dec + static_cast<int64_t>(u) * a.kslots);
+        uint32_t *dst = reinterpret_cast<uint32_t *>(dec);
+        for (int i = tid; i < ns * kDecWords; i += kEntThreads) dst[i] = src[i];
+        if constexpr (SLDS)
+            for (int i = tid; i < a.nsym; i += kEntThreads) lsyms[i] = gsyms[i];
+    }
+    __syncthreads();
+    if (tid < ns) {
+        const kvtc_entropy_dec &d = dec[tid];
+        const uint8_t *sy = (SLDS ? lsyms : gsyms) + d.sym_off;
+        const uint32_t sb = a.sbits[static_cast<int64_t>(u) * a.kslots + tid];
+        const uint32_t off = sb & kOffsetMask, wi = off >> 5, sh = off & 31u;
+        BitWindow w = window_at(a, a.chunk_pos[(static_cast<int64_t>(u) * a.kslots + tid) * a.nchunks + c]);
+        for (int s = 0; s < n; ++s) {
+            const uint64_t x = static_cast<uint64_t>(next_symbol(a, w, d, sy)) << sh;   // the field in row s
+            atomicOr(rows + s * rw + wi, static_cast<uint32_t>(x));
+            if ((x >> 32) != 0u) atomicOr(rows + s * rw + wi + 1, static_cast<uint32_t>(x >> 32));
+        }
+    }
+    __syncthreads();
+    uint32_t *out = reinterpret_cast<uint32_t *>(a.codes) + (static_cast<int64_t>(u) * a.capacity + s0) * rw;
+    for (int i = tid; i < n * rw; i += kEntThreads) out[i] = rows[i];
+}
+
+template <bool SLDS>
+int32_t launch_entropy_decode(const EntropyDevArgs &a, size_t lds, hipStream_t st) {
+    auto kern = entropy_decode_kernel<SLDS>;
+    if (!allow_lds(reinterpret_cast<const void *>(kern))) return KVTC_E_DEVICE;
+    hipLaunchKernelGGL(kern, dim3(static_cast<unsigned>(a.nchunks), static_cast<unsigned>(a.units)), dim3(kEntThreads),
+                       lds, st, a);
+    return hipGetLastError() == hipSuccess ? KVTC_OK : KVTC_E_DEVICE;
 }
 
 // Fixed-width units: one thread per (unit, row) copies the row's bits back.
@@ -210,16 +268,6 @@ __global__ __launch_bounds__(kEntThreads) void entropy_unplain_kernel(EntropyDev
             rows[s * rw + k] = n > 0 ? read_bits(a.archive, a.archive_words, pos + 32 * k, n) : 0u;
         }
     }
-}
-
-// Rows [0, S) of every unit zeroed (the decoder ORs fields into them).
-__global__ __launch_bounds__(kEntThreads) void entropy_clear_rows_kernel(EntropyDevArgs a) {
-    const int u = blockIdx.y;
-    const int rw = a.row_stride >> 2;
-    uint32_t *rows = reinterpret_cast<uint32_t *>(a.codes) + static_cast<int64_t>(u) * a.capacity * rw;
-    for (int64_t i = static_cast<int64_t>(blockIdx.x) * kEntThreads + threadIdx.x; i < a.S * rw;
-         i += static_cast<int64_t>(gridDim.x) * kEntThreads)
-        rows[i] = 0u;
 }
 
 unsigned grid_for(int64_t n) { return static_cast<unsigned>(std::max<int64_t>(1, std::min<int64_t>((n + kEntThreads - 1) / kEntThreads, 1 << 20))); }
@@ -284,12 +332,16 @@ int32_t entropy_device_decode(const EntropyDevArgs &a) {
     hipStream_t st = static_cast<hipStream_t>(a.stream);
     if (a.S == 0) return KVTC_OK;
     const uint64_t U = static_cast<uint64_t>(a.units);
-    const uint64_t nc = U * a.kslots * static_cast<uint64_t>(a.nchunks);
-    const unsigned gx = static_cast<unsigned>(std::min<int64_t>((a.S * (a.row_stride / 4) + kEntThreads - 1) / kEntThreads, 4096));
-    hipLaunchKernelGGL(entropy_clear_rows_kernel, dim3(std::max(gx, 1u), static_cast<unsigned>(U)), dim3(kEntThreads), 0, st, a);
-    if (hipGetLastError() != hipSuccess) return KVTC_E_DEVICE;
-    hipLaunchKernelGGL(entropy_decode_kernel, dim3(grid_for(static_cast<int64_t>(nc))), dim3(kEntThreads), 0, st, a);
-    if (hipGetLastError() != hipSuccess) return KVTC_E_DEVICE;
+    if (a.kslots > kEntThreads) return KVTC_E_SHAPE;
+    // coded units: every word of rows [0, S) written by the decoder; fixed-width
+    // units: by the copy below
+    // the symbol lists in LDS where they fit next to the rows and tables, else
+    // read from global memory (at most 64 KB of rows and 68 KB of tables: fits)
+    const size_t rows1 = static_cast<size_t>(kEntropyChunk) * (a.row_stride / 4) * 4;
+    const size_t tabs = static_cast<size_t>(a.kslots) * sizeof(kvtc_entropy_dec), syml = static_cast<size_t>(a.nsym);
+    const int32_t rc = rows1 + tabs + syml <= kLdsMax ? launch_entropy_decode<true>(a, rows1 + tabs + syml, st)
+                                                      : launch_entropy_decode<false>(a, rows1 + tabs, st);
+    if (rc != KVTC_OK) return rc;
     const unsigned gr = static_cast<unsigned>(std::min<int64_t>((a.S + kEntThreads - 1) / kEntThreads, 4096));
     hipLaunchKernelGGL(entropy_unplain_kernel, dim3(gr, static_cast<unsigned>(U)), dim3(kEntThreads), 0, st, a);
     return hipGetLastError() == hipSuccess ? KVTC_OK : KVTC_E_DEVICE;

@@ -42,6 +42,11 @@ ENTROPY_CASES = [
     ("llama-k", small(2, s_total=4096 + 40), 0, 4096 + 40),
     ("batched-b3-v", small(4, B=3, s_prefill=700, s_total=700), 1, 700),
     ("long-k-r4", small(5, s_prefill=4096, s_total=4096 + 300), 0, 4096 + 300),
+    # 256 slots of 8 bits: 256-byte rows and 64 K symbol positions per unit, the
+    # decoder's variant with the symbol lists in global memory (too large for
+    # LDS next to the rows and tables)
+    ("wide-rows-8bit", small(2, D=256, H=1, rank=256, budget=2048, choices=(0, 8), n_outliers_k=0,
+                             s_prefill=600, s_total=600), 0, 600),
 ]
 
 
@@ -72,7 +77,8 @@ def test_entropy_archive_matches_oracle_and_round_trips(name, w, tensor, S):
     back.codes.fill_(0xA5)
     arc.decode(back.codes, cap)
     assert np.array_equal(back.rows(S), rows)
-    assert torch.equal(back.fetch(0, S), ds.fetch(0, S))
+    if st.row_stride <= 192:                           # rows the fetch kernels take
+        assert torch.equal(back.fetch(0, S), ds.fetch(0, S))
 
 
 def test_entropy_full_size_batched_decode():
