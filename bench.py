@@ -150,12 +150,12 @@ def pmc_summary(fetch_dir, write_dir, cal_fetch_dir, cal_write_dir):
     write_b = float(np.mean(w)) * sw * 1024
     lines = [
         "# HBM traffic of the fetch kernel, batched-decode workload (B=64, H=8, D=128, S~8195, r=96, 320 bits/token)",
-        "commands (from the repository root, each in a run of its own, csv output):",
-        "  rocprofv3 --pmc FETCH_SIZE -d <fetch_dir> -o bd --output-format csv -- python3 bench.py --steps 3 --warmup 1 --no-cpu-baseline",
-        "  rocprofv3 --pmc WRITE_SIZE -d <write_dir> -o bd --output-format csv -- python3 bench.py --steps 3 --warmup 1 --no-cpu-baseline",
-        "  rocprofv3 --pmc FETCH_SIZE -d <cal_fetch_dir> -o cal --output-format csv -- python3 bench.py --copy-calibration",
-        "  rocprofv3 --pmc WRITE_SIZE -d <cal_write_dir> -o cal --output-format csv -- python3 bench.py --copy-calibration",
-        "  python3 bench.py --pmc-summary <fetch_dir> <write_dir> <cal_fetch_dir> <cal_write_dir>",
+        "commands (from /tmp with TMPDIR=/tmp; R is the repository root; each in a run of its own, csv output):",
+        "  rocprofv3 --pmc FETCH_SIZE -d <fetch_dir> -o bd --output-format csv -- python3 $R/bench.py --steps 3 --warmup 1 --no-cpu-baseline --no-extra",
+        "  rocprofv3 --pmc WRITE_SIZE -d <write_dir> -o bd --output-format csv -- python3 $R/bench.py --steps 3 --warmup 1 --no-cpu-baseline --no-extra",
+        "  rocprofv3 --pmc FETCH_SIZE -d <cal_fetch_dir> -o cal --output-format csv -- python3 $R/bench.py --copy-calibration",
+        "  rocprofv3 --pmc WRITE_SIZE -d <cal_write_dir> -o cal --output-format csv -- python3 $R/bench.py --copy-calibration",
+        "  python3 $R/bench.py --pmc-summary <fetch_dir> <write_dir> <cal_fetch_dir> <cal_write_dir>",
         f"copy calibration (1 GiB device copy): FETCH_SIZE {np.mean(cal_f):.0f} KiB -> scale {sf:.4f}; "
         f"WRITE_SIZE {np.mean(cal_w):.0f} KiB -> scale {sw:.4f}",
         f"fetch dispatches: {len(f)} (FETCH_SIZE), {len(w)} (WRITE_SIZE); each covers the K and the V tensor",
@@ -169,8 +169,21 @@ def pmc_summary(fetch_dir, write_dir, cal_fetch_dir, cal_write_dir):
 
 def short_kernel(name):
     """A kernel's name without namespaces, argument lists or return type, template arguments kept."""
-    n = re.sub(r"\(.*$", "", name)
-    n = n.replace("void ", "").replace("kvtc::", "").replace("(anonymous namespace)::", "")
+    m = re.match(r"_ZN4kvtc(?:12_GLOBAL__N_1)?(\d+)", name)
+    if m:
+        # rocprofv3 leaves some names mangled (binutils does not know the _Float16 code DF16_):
+        # render kvtc::name<template arguments> from the mangled form
+        n0 = int(m.group(1))
+        base = name[m.end():m.end() + n0]
+        rest = name[m.end() + n0:]
+        args = []
+        if rest.startswith("I"):
+            for t in re.findall(r"Lb[01]|DF16_|Li-?\d+E|L[a-z]\d+E", rest[1:rest.find("EE") + 1]):
+                args.append({"Lb0": "false", "Lb1": "true", "DF16_": "f16"}.get(t, re.sub(r"^L[a-z]|E$", "", t)))
+        name = base + (f"<{', '.join(args)}>" if args else "")
+    n = name.replace("(anonymous namespace)::", "")
+    n = re.sub(r"\(.*$", "", n)
+    n = n.replace("void ", "").replace("kvtc::", "")
     n = n.replace("_Float16", "f16")
     if "copyBuffer" in n or "copy" in n.lower():
         return "device copy (ceiling)"
