@@ -140,7 +140,12 @@ typedef struct kvtc_state_header {
                                (16-19, 0 = empty) | quantisation group (20-31, mixed mode) */
     uint64_t off_fslot;     /* int32  [units][kfetch] stored slot whose fetch operand is column k
                                of off_w16 (-1 = padding column) */
-    uint64_t reserved[2];
+    uint64_t off_vdig;      /* int8   [units][5][kslots][dg] the basis in exact integer digits for
+                               the int8 append: vq = rint(basis * 2^38) = sum_i d_i 256^i with
+                               balanced digits d_i in [-128, 127]; 0 (absent) when some basis
+                               entry exceeds 1 in magnitude */
+    uint64_t off_mv;        /* double [units][kslots] the int8 append's slot offset: mean . basis_j
+                               - 2^-62 * 0x808080 * sum_d vq_jd, in float64 (0 when off_vdig is) */
 } kvtc_state_header;
 
 /* ---------------------------------------------------------- entry points */
@@ -155,6 +160,11 @@ const char *kvtc_build_id(void);
 
 /* Human-readable name of a status code (static string). */
 const char *kvtc_status_string(int32_t status);
+
+/* HIP's message for the error behind the calling thread's last KVTC_E_DEVICE
+ * (a launch HIP refused, or a failed device call); "no error" if there was none.
+ * Static string. */
+const char *kvtc_device_error_string(void);
 
 /* Fit the frozen state of one tensor on its prefill rows (host).
  * KVTC page, update_and_fetch and _TensorKVTC.fit_prefill_from_pca: local PCA

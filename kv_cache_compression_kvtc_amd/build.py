@@ -67,7 +67,7 @@ def build(verbose: bool = False, jobs: int | None = None) -> str:
     steps = [["g++", *HOST_FLAGS, f'-DKVTC_BUILD_ID="{bid}"', "-c", os.path.join(CSRC, "kvtc_host.cpp"),
               "-o", os.path.join(BUILD, "kvtc_host.o")]]
     objs = [steps[0][-1]]
-    for name in ("kvtc_device", "kvtc_append", "kvtc_attend", "kvtc_refit", "kvtc_fit", "kvtc_probe", "kvtc_entropy"):
+    for name in ("kvtc_device", "kvtc_append", "kvtc_append_i8", "kvtc_attend", "kvtc_refit", "kvtc_fit", "kvtc_probe", "kvtc_entropy"):
         o = os.path.join(BUILD, name + ".o")
         steps.append(["hipcc", *HIP_FLAGS, "-c", os.path.join(CSRC, name + ".hip"), "-o", o])
         objs.append(o)

@@ -8,7 +8,7 @@
 // The projection runs on fp64 MFMA so that codes are decided from latents
 // accurate to ~1e-16, i.e. identical to a float64 evaluation except when a
 // value lies within rounding distance of a quantisation boundary.
-#include "kvtc_device.h"
+#include "kvtc_append_tile.h"
 
 namespace kvtc {
 namespace {
@@ -19,108 +19,20 @@ namespace {
 template <bool MIXED, typename XT, int NB, bool XVEC, bool RANGES = false>
 __global__ __launch_bounds__(kThreads) void append_kernel(AppendArgs a) {
     extern __shared__ __align__(16) unsigned char smem[];
-    double *xs = reinterpret_cast<double *>(smem);                         // [2][64][kAppPad]
-    float *vs = reinterpret_cast<float *>(xs + 2 * kAppTok * kAppPad);     // [2][NB*16][kAppPad]
-    uint32_t *rows = reinterpret_cast<uint32_t *>(vs + 2 * NB * 16 * kAppPad);  // [64][row_words]
+    uint32_t *rows = reinterpret_cast<uint32_t *>(smem + f64_stage_bytes(NB));  // [64][row_words]
 
     const int u = blockIdx.y;
     const int64_t t0 = static_cast<int64_t>(blockIdx.x) * kAppTok;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int b = u / a.groups, g = u % a.groups;
     const int nvalid = static_cast<int>(min<int64_t>(kAppTok, a.n - t0));
     const int n_slots = a.ui[u].n_slots;
     const int row_words = a.row_stride >> 2;
-    const XT *x = static_cast<const XT *>(a.x);
 
-    for (int w = tid; w < kAppTok * row_words; w += kThreads) rows[w] = 0u;
-
-    // staging map: thread -> (token, 4 consecutive columns) of a 64 x 16 chunk,
-    // and (slot, 4 columns) of the NB*16 x 16 basis chunk
-    const int st_tok = tid >> 2, st_col = (tid & 3) * 4;
-    constexpr int kVReps = (NB * 16 + 63) / 64;
-    // a chunk's loads only fill these registers (indices clamped, so no load
-    // sits behind a branch); centring and the fp64 conversion happen when the
-    // chunk is written to LDS, after the MFMAs of the previous chunk, so the
-    // loads are in flight during those MFMAs
-    typename RawX4<XT>::v xv;
-    XT xraw[4];
-    float muv[4];
-    float vr[kVReps][4];
-    const int tok_c = min(st_tok, nvalid - 1);
-
-    auto load_chunk = [&](int kc) {
-        const int gd = kc * kAppKC + st_col;          // column within the unit's row
-        const int j = gd / a.D, dd = gd - j * a.D;
-        const int h = g * a.hpu + j;
-        const float *mu = a.mu + static_cast<int64_t>(u) * a.dg + gd;
-        const XT *p = x + b * a.xsb + h * a.xsh + (t0 + tok_c) * a.xss + dd;
-        if constexpr (XVEC) {
-            xv = *reinterpret_cast<const typename RawX4<XT>::v *>(p);
-        } else {
-#pragma unroll
-            for (int i = 0; i < 4; ++i) xraw[i] = p[i];
-        }
-#pragma unroll
-        for (int i = 0; i < 4; ++i) muv[i] = mu[i];
-#pragma unroll
-        for (int rep = 0; rep < kVReps; ++rep) {
-            const int slot = min(rep * 64 + st_tok, a.kslots - 1);
-            const float *q = a.basis + (static_cast<int64_t>(u) * a.kslots + slot) * a.dg + gd;
-#pragma unroll
-            for (int i = 0; i < 4; ++i) vr[rep][i] = q[i];
-        }
-    };
-    auto store_chunk = [&](int buf) {
-        double *xb = xs + buf * kAppTok * kAppPad + st_tok * kAppPad + st_col;
-        const bool tok_ok = st_tok < nvalid;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const double xi = XVEC ? RawX4<XT>::get(xv, i) : load_x(&xraw[i]);
-            xb[i] = tok_ok ? xi - static_cast<double>(muv[i]) : 0.0;
-        }
-#pragma unroll
-        for (int rep = 0; rep < kVReps; ++rep) {
-            const int slot = rep * 64 + st_tok;
-            if (slot < NB * 16) {
-                const bool keep = slot < a.kslots;      // slots past kslots are zero
-                float *vb = vs + (buf * NB * 16 + slot) * kAppPad + st_col;
-#pragma unroll
-                for (int i = 0; i < 4; ++i) vb[i] = keep ? vr[rep][i] : 0.0f;
-            }
-        }
-    };
+    if constexpr (!RANGES)
+        for (int w = tid; w < kAppTok * row_words; w += kThreads) rows[w] = 0u;
 
     doublex4 acc[NB];
-#pragma unroll
-    for (int nb = 0; nb < NB; ++nb) acc[nb] = doublex4{0.0, 0.0, 0.0, 0.0};
-
-    const int nchunks = a.dg / kAppKC;
-    load_chunk(0);
-    store_chunk(0);
-    __syncthreads();
-    const int mrow = wave * 16 + (lane & 15);   // A operand row (token) of this lane
-    const int kcol = lane >> 4;                 // A/B operand k of this lane
-    // k-step order: k-step 4c + e of the contraction takes, at operand k = q, the
-    // feature 16c + 4q + e (c = 16-column chunk); every append kernel uses this
-    // order, so that a lane of the decode kernel holds its operands as whole
-    // 16-byte vectors of the basis
-    for (int kc = 0; kc < nchunks; ++kc) {
-        const int buf = kc & 1;
-        if (kc + 1 < nchunks) load_chunk(kc + 1);
-        const double *xb = xs + buf * kAppTok * kAppPad;
-        const float *vb = vs + buf * NB * 16 * kAppPad;
-#pragma unroll
-        for (int ks = 0; ks < kAppKC / 4; ++ks) {
-            const double av = xb[mrow * kAppPad + kcol * 4 + ks];
-#pragma unroll
-            for (int nb = 0; nb < NB; ++nb) {
-                const double bv = static_cast<double>(vb[(nb * 16 + (lane & 15)) * kAppPad + kcol * 4 + ks]);
-                acc[nb] = __builtin_amdgcn_mfma_f64_16x16x4f64(av, bv, acc[nb], 0, 0, 0);
-            }
-        }
-        if (kc + 1 < nchunks) store_chunk(buf ^ 1);
-        __syncthreads();
-    }
+    f64_project<XT, NB, XVEC>(a, u, t0, nvalid, 0, smem, acc);
 
     // fp64 16x16x4 result layout: acc[nb][i] is row (lane>>4) + 4i, column lane&15, i.e.
     // the latent of token 16*wave + (lane>>4) + 4i and slot 16*nb + (lane&15)
@@ -128,7 +40,7 @@ __global__ __launch_bounds__(kThreads) void append_kernel(AppendArgs a) {
     if constexpr (RANGES) {
         // min / max over this lane's tokens, its wave's four token groups (lanes
         // 16 apart) and the block's four waves (staged in the now idle row chunks)
-        double *red = xs;                                  // [4][NB*16][2]
+        double *red = reinterpret_cast<double *>(smem);   // [4][NB*16][2]
 #pragma unroll
         for (int nb = 0; nb < NB; ++nb) {
             double mn = __builtin_huge_val(), mx = -__builtin_huge_val();
@@ -160,87 +72,7 @@ __global__ __launch_bounds__(kThreads) void append_kernel(AppendArgs a) {
         }
         return;
     }
-    const int64_t ub = static_cast<int64_t>(u) * a.kslots;
-    if constexpr (!MIXED) {
-#pragma unroll
-        for (int nb = 0; nb < NB; ++nb) {
-            const int j = nb * 16 + (lane & 15);
-            if (j < n_slots) {
-                const double lo = a.qlo[ub + j], inv = a.qinv[ub + j];
-                const uint32_t sb = a.sbits[ub + j];
-                const uint32_t off = sb & kOffsetMask, w = sb >> 24;
-                const double cmax = static_cast<double>((1u << w) - 1u);
-#pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    const int t = tbase + 4 * i;
-                    if (t < nvalid) {
-                        const uint32_t c = static_cast<uint32_t>(quantise(acc[nb][i], lo, inv, cmax));
-                        or_field(rows + t * row_words, off, w, c);
-                    }
-                }
-            }
-        }
-    } else {
-        const int ngroups = (n_slots + a.gs - 1) / a.gs;
-        for (int gi = 0; gi < ngroups; ++gi) {
-            const int j0 = gi * a.gs, j1 = min(n_slots, j0 + a.gs);
-            const uint32_t w = a.sbits[ub + j0] >> 24;
-            const double cmax = static_cast<double>((1u << w) - 1u);
-            double mn[4], mx[4];
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                mn[i] = __builtin_huge_val();
-                mx[i] = -__builtin_huge_val();
-            }
-#pragma unroll
-            for (int nb = 0; nb < NB; ++nb) {
-                const int j = nb * 16 + (lane & 15);
-                if (j >= j0 && j < j1) {
-#pragma unroll
-                    for (int i = 0; i < 4; ++i) {
-                        mn[i] = fmin(mn[i], acc[nb][i]);
-                        mx[i] = fmax(mx[i], acc[nb][i]);
-                    }
-                }
-            }
-#pragma unroll
-            for (int m = 1; m < 16; m <<= 1) {
-#pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    mn[i] = fmin(mn[i], __shfl_xor(mn[i], m, 16));
-                    mx[i] = fmax(mx[i], __shfl_xor(mx[i], m, 16));
-                }
-            }
-            double lo16[4], inv16[4];
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const uint16_t hmin = half_bits_rne(mn[i]);
-                const uint16_t hscale = half_bits_rne((mx[i] - mn[i]) / cmax);
-                lo16[i] = half_bits_to_double(hmin);
-                const double sc = half_bits_to_double(hscale);
-                inv16[i] = sc > 0.0 ? 1.0 / sc : 0.0;
-                const int t = tbase + 4 * i;
-                if ((lane & 15) == 0 && t < nvalid)
-                    a.params[(static_cast<int64_t>(u) * a.capacity + a.s0 + t0 + t) * a.n_qg + gi] =
-                        static_cast<uint32_t>(hmin) | (static_cast<uint32_t>(hscale) << 16);
-            }
-#pragma unroll
-            for (int nb = 0; nb < NB; ++nb) {
-                const int j = nb * 16 + (lane & 15);
-                if (j >= j0 && j < j1) {
-                    const uint32_t off = a.sbits[ub + j] & kOffsetMask;
-#pragma unroll
-                    for (int i = 0; i < 4; ++i) {
-                        const int t = tbase + 4 * i;
-                        if (t < nvalid) {
-                            const uint32_t c = static_cast<uint32_t>(quantise(acc[nb][i], lo16[i], inv16[i], cmax));
-                            or_field(rows + t * row_words, off, w, c);
-                        }
-                    }
-                }
-            }
-        }
-    }
+    f64_quantise<MIXED, NB>(a, u, t0, nvalid, 0, acc, rows);
     __syncthreads();
     if (row_words > 0) {
         uint32_t *dst = reinterpret_cast<uint32_t *>(
@@ -488,13 +320,12 @@ __global__ __launch_bounds__(512) void append_decode_kernel(AppendPair m) {
 
 template <bool MIXED, typename XT, int NB>
 int32_t launch_append_nb(const AppendArgs &a, int64_t ntiles, int64_t U, hipStream_t stream) {
-    const size_t lds = 2 * kAppTok * kAppPad * sizeof(double) + 2 * NB * 16 * kAppPad * sizeof(float) +
-                       static_cast<size_t>(kAppTok) * (a.row_stride / 4) * sizeof(uint32_t);
+    const size_t lds = f64_stage_bytes(NB) + static_cast<size_t>(kAppTok) * (a.row_stride / 4) * sizeof(uint32_t);
     auto kern = a.x_vec ? append_kernel<MIXED, XT, NB, true> : append_kernel<MIXED, XT, NB, false>;
     if (!allow_lds(reinterpret_cast<const void *>(kern))) return KVTC_E_DEVICE;
     hipLaunchKernelGGL(kern, dim3(static_cast<unsigned>(ntiles), static_cast<unsigned>(U)), dim3(kThreads), lds,
                        stream, a);
-    return hipGetLastError() == hipSuccess ? KVTC_OK : KVTC_E_DEVICE;
+    return launch_status();
 }
 
 
@@ -514,7 +345,7 @@ int32_t launch_small_nb(const AppendArgs &a, int64_t U, hipStream_t stream) {
     const int64_t blocks = (a.n + kSmallRows - 1) / kSmallRows;
     hipLaunchKernelGGL(kern, dim3(static_cast<unsigned>(blocks), static_cast<unsigned>(U)), dim3(kThreads), lds,
                        stream, a);
-    return hipGetLastError() == hipSuccess ? KVTC_OK : KVTC_E_DEVICE;
+    return launch_status();
 }
 
 template <typename XT, int NB>
@@ -527,7 +358,7 @@ int32_t launch_refit_nb(const AppendArgs &a, int64_t U, hipStream_t stream) {
     if (blocks > 0x7FFFFFFF) return KVTC_E_SHAPE;
     hipLaunchKernelGGL(kern, dim3(static_cast<unsigned>(blocks), static_cast<unsigned>(U)), dim3(kThreads), lds,
                        stream, a);
-    return hipGetLastError() == hipSuccess ? KVTC_OK : KVTC_E_DEVICE;
+    return launch_status();
 }
 
 template <typename XT>
@@ -583,7 +414,7 @@ int32_t launch_decode_dg(const AppendPair &m, int64_t nrows, int64_t units, int 
     const int64_t blocks = (nrows + kSmallRows - 1) / kSmallRows;
     hipLaunchKernelGGL(kern, dim3(static_cast<unsigned>(blocks), static_cast<unsigned>(units)), dim3(64 * nblk), lds,
                        stream, m);
-    return hipGetLastError() == hipSuccess ? KVTC_OK : KVTC_E_DEVICE;
+    return launch_status();
 }
 
 // One decode launch for one plan (p1 == NULL) or for two plans of the same
@@ -630,14 +461,14 @@ template <typename XT, int NB>
 int32_t launch_ranges_nb(const AppendArgs &a, int64_t U, hipStream_t stream) {
     // the block's row chunks double as the [4][NB*16][2] reduction area
     static_assert(2 * kAppTok * kAppPad >= 4 * NB * 16 * 2, "reduction area");
-    const size_t lds = 2 * kAppTok * kAppPad * sizeof(double) + 2 * NB * 16 * kAppPad * sizeof(float);
+    const size_t lds = f64_stage_bytes(NB);
     auto kern = a.x_vec ? append_kernel<false, XT, NB, true, true> : append_kernel<false, XT, NB, false, true>;
     if (!allow_lds(reinterpret_cast<const void *>(kern))) return KVTC_E_DEVICE;
     const int64_t tiles = (a.n + kAppTok - 1) / kAppTok;
     if (tiles > 0x7FFFFFFF || U > 65535) return KVTC_E_SHAPE;
     hipLaunchKernelGGL(kern, dim3(static_cast<unsigned>(tiles), static_cast<unsigned>(U)), dim3(kThreads), lds, stream,
                        a);
-    return hipGetLastError() == hipSuccess ? KVTC_OK : KVTC_E_DEVICE;
+    return launch_status();
 }
 
 template <typename XT>
@@ -673,6 +504,7 @@ int32_t launch_refit_project(const AppendPlan &p, hipStream_t stream) {
 int32_t launch_append_plan(const AppendPlan &p, hipStream_t stream) {
     if (p.a.n == 0) return KVTC_OK;
     if (decode_path(p)) return launch_decode(p, nullptr, stream);
+    if (p.i8_ns) return launch_append_i8(p, stream);
     if (p.dtype == KVTC_F16)
         return p.mixed ? launch_append<true, _Float16>(p.a, p.ntiles, p.units, p.nb, stream)
                        : launch_append<false, _Float16>(p.a, p.ntiles, p.units, p.nb, stream);

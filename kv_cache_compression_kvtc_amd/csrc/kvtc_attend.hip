@@ -911,16 +911,16 @@ int32_t launch_gen(const kvtc_tensor_ref *k, const kvtc_tensor_ref *v, const kvt
     a.part = reinterpret_cast<float *>(wb + wl.part);
     const unsigned U = static_cast<unsigned>(hk->units), Q = static_cast<unsigned>(r.Q);
     hipLaunchKernelGGL(attend_gen_prep_kernel, dim3(U, Q), dim3(256), 0, stream, a);
-    if (hipGetLastError() != hipSuccess) return KVTC_E_DEVICE;
+    if (launch_status() != KVTC_OK) return KVTC_E_DEVICE;
     if (a.nchunks > 0) {
         const size_t lds = gen_lds_bytes(hk, hv, r.QM);
         auto kern = r.QM == 8 ? attend_gen_partial_kernel<8> : attend_gen_partial_kernel<kGenMaxQ>;
         if (!allow_lds(reinterpret_cast<const void *>(kern))) return KVTC_E_DEVICE;
         hipLaunchKernelGGL(kern, dim3(static_cast<unsigned>(a.nchunks), U), dim3(256), lds, stream, a);
-        if (hipGetLastError() != hipSuccess) return KVTC_E_DEVICE;
+        if (launch_status() != KVTC_OK) return KVTC_E_DEVICE;
     }
     hipLaunchKernelGGL(attend_gen_merge_kernel, dim3(U, Q), dim3(256), 0, stream, a);
-    return hipGetLastError() == hipSuccess ? KVTC_OK : KVTC_E_DEVICE;
+    return launch_status();
 }
 
 // Validates the call, then launches the attention kernels on the given
@@ -990,7 +990,7 @@ int32_t attend_impl(const kvtc_tensor_ref *k, const kvtc_tensor_ref *v, int64_t 
     a.part = reinterpret_cast<float *>(wb + wl.part);
     const unsigned U = static_cast<unsigned>(hk->units);
     hipLaunchKernelGGL(attend_prep_kernel, dim3(U), dim3(256), 0, stream, a);
-    if (hipGetLastError() != hipSuccess) return KVTC_E_DEVICE;
+    if (launch_status() != KVTC_OK) return KVTC_E_DEVICE;
     if (nchunks > 0) {
         const int rw = std::max(a.k.row_words, a.v.row_words);
         const size_t lds = (kMaxSlots + 4 + 2 * kMaxSlots + kAttChunk + 4 * kMaxSlots) * sizeof(float) +
@@ -998,10 +998,10 @@ int32_t attend_impl(const kvtc_tensor_ref *k, const kvtc_tensor_ref *v, int64_t 
         if (lds > kLdsMax) return KVTC_E_SHAPE;
         if (!allow_lds(reinterpret_cast<const void *>(attend_partial_kernel))) return KVTC_E_DEVICE;
         hipLaunchKernelGGL(attend_partial_kernel, dim3(static_cast<unsigned>(nchunks), U), dim3(256), lds, stream, a);
-        if (hipGetLastError() != hipSuccess) return KVTC_E_DEVICE;
+        if (launch_status() != KVTC_OK) return KVTC_E_DEVICE;
     }
     hipLaunchKernelGGL(attend_merge_kernel, dim3(U), dim3(256), 0, stream, a);
-    return hipGetLastError() == hipSuccess ? KVTC_OK : KVTC_E_DEVICE;
+    return launch_status();
 }
 
 }  // namespace

@@ -98,6 +98,8 @@ struct AppendArgs {
     int dg, D, hpu, groups, kslots, row_stride, n_qg, gs;
     float inv_dg, inv_q4;              // 1/dg and 4/dg: exact quotients of small indices
     int x_vec;                         // rows and strides aligned to 4 elements (raw vector loads)
+    const int8_t *vdig;                // int8 append: basis digits [U][5][kslots][dg] (null if absent)
+    const double *mv;                  // int8 append: mean . basis_j [U][kslots]
 };
 
 // Four consecutive input elements as raw bits (one 8- or 16-byte load), and
@@ -333,6 +335,7 @@ struct AppendPlan {
     int nb;                            // 16-slot N-blocks of the bulk kernels
     int32_t dtype;
     bool mixed;
+    int i8_ns, i8_nsg;                 // int8 append: 32-slot tiles per block, slot groups (0: not used)
 };
 
 struct FetchPlan {
@@ -398,7 +401,15 @@ int32_t launch_refit_requantise(const RefitArgs &a, int64_t units, hipStream_t s
 
 // ------------------------------------------------------------ launchers
 // append (kvtc_append.hip)
+// KVTC_OK after a launch that HIP accepted, else KVTC_E_DEVICE with HIP's error
+// kept for kvtc_device_error_string (per calling thread).
+int32_t launch_status();
+void note_device_error(hipError_t e);
+hipError_t g_device_error_value();
 int32_t launch_append_plan(const AppendPlan &p, hipStream_t stream);
+// Bulk append of fp16 rows on int8 MFMA with certified decisions
+// (kvtc_append_i8.hip); plans with i8_ns set only.
+int32_t launch_append_i8(const AppendPlan &p, hipStream_t stream);
 bool decode_path(const AppendPlan &p);
 int32_t launch_decode(const AppendPlan &p0, const AppendPlan *p1, hipStream_t stream);
 int append_nb(int kslots);

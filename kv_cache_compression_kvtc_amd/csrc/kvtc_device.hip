@@ -17,12 +17,34 @@ bool allow_lds(const void *kern) {
     static std::mutex mu;
     static std::set<std::pair<const void *, int>> done;
     int dev = 0;
-    if (hipGetDevice(&dev) != hipSuccess) return false;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) {
+        note_device_error(e);
+        return false;
+    }
     std::lock_guard<std::mutex> lock(mu);
     if (done.count({kern, dev})) return true;
-    if (hipFuncSetAttribute(kern, hipFuncAttributeMaxDynamicSharedMemorySize, kLdsMax) != hipSuccess) return false;
+    e = hipFuncSetAttribute(kern, hipFuncAttributeMaxDynamicSharedMemorySize, kLdsMax);
+    if (e != hipSuccess) {
+        note_device_error(e);
+        return false;
+    }
     done.insert({kern, dev});
     return true;
+}
+
+namespace {
+thread_local hipError_t g_device_error = hipSuccess;
+}
+
+void note_device_error(hipError_t e) { g_device_error = e; }
+hipError_t g_device_error_value() { return g_device_error; }
+
+int32_t launch_status() {
+    const hipError_t e = hipGetLastError();
+    if (e == hipSuccess) return KVTC_OK;
+    g_device_error = e;
+    return KVTC_E_DEVICE;
 }
 
 namespace {
@@ -102,6 +124,34 @@ int32_t plan_append(const void *state_host, const void *state_dev, const void *x
     p->nb = nb;
     p->dtype = dtype;
     p->mixed = mixed;
+    // bulk appends of fp16 rows run on int8 MFMA (kvtc_append_i8.hip) when the
+    // blob carries the basis digits, the units are wide (512 features or more:
+    // for narrower ones the fp64 kernel, whose per-code work is lighter, is
+    // faster), the contraction is whole rounds of four 32-feature k-steps of
+    // single heads, and each block's slot group owns whole row
+    // words (a group boundary inside a unit's slots falls on a word boundary)
+    p->i8_ns = p->i8_nsg = 0;
+    if (h->off_vdig && h->off_mv && dtype == KVTC_F16 && a.x_vec && n > 16 && h->dg % 128 == 0 &&
+        h->dg >= 512 && h->head_dim % 32 == 0 && h->dg <= 2048 && h->kslots > 32 &&
+        (!mixed || h->group_size == 32)) {
+        const int ns = h->kslots <= 128 ? (h->kslots + 31) / 32 : 2;
+        const int nsg = (h->kslots + 32 * ns - 1) / (32 * ns);
+        const char *sh = static_cast<const char *>(state_host);
+        const auto *ui = reinterpret_cast<const kvtc_unit_info *>(sh + h->off_unit);
+        const auto *sb = reinterpret_cast<const uint32_t *>(sh + h->off_slot_bits);
+        bool aligned = true;
+        for (int64_t u = 0; u < h->units && aligned; ++u)
+            for (int gi = 1; gi < nsg; ++gi) {
+                const int j = gi * 32 * ns;
+                if (j < ui[u].n_slots && (sb[u * h->kslots + j] & kOffsetMask) % 32 != 0) aligned = false;
+            }
+        if (aligned) {
+            a.vdig = reinterpret_cast<const int8_t *>(sd + h->off_vdig);
+            a.mv = reinterpret_cast<const double *>(sd + h->off_mv);
+            p->i8_ns = ns;
+            p->i8_nsg = nsg;
+        }
+    }
     return KVTC_OK;
 }
 
@@ -405,5 +455,7 @@ int32_t kvtc_fetch_refit(const void *state_host, const void *state_dev, const vo
     p.a.bias = reinterpret_cast<const float *>(rb + L.bias);
     return launch_fetch_plans(p, nullptr, static_cast<hipStream_t>(hip_stream));
 }
+
+const char *kvtc_device_error_string(void) { return hipGetErrorString(kvtc::g_device_error_value()); }
 
 }  // extern "C"

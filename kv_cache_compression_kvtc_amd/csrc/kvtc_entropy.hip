@@ -250,7 +250,7 @@ int32_t launch_entropy_decode(const EntropyDevArgs &a, size_t lds, hipStream_t s
     if (!allow_lds(reinterpret_cast<const void *>(kern))) return KVTC_E_DEVICE;
     hipLaunchKernelGGL(kern, dim3(static_cast<unsigned>(a.nchunks), static_cast<unsigned>(a.units)), dim3(kEntThreads),
                        lds, st, a);
-    return hipGetLastError() == hipSuccess ? KVTC_OK : KVTC_E_DEVICE;
+    return launch_status();
 }
 
 // Fixed-width units: one thread per (unit, row) copies the row's bits back.
@@ -285,12 +285,12 @@ int32_t entropy_device_counts(const EntropyDevArgs &a, uint32_t *counts_host) {
     hipStream_t st = static_cast<hipStream_t>(a.stream);
     const uint64_t n = static_cast<uint64_t>(a.units) * a.nsym;
     hipLaunchKernelGGL(fill_u32_kernel, dim3(grid_for(static_cast<int64_t>(n))), dim3(kEntThreads), 0, st, a.counts, n);
-    if (hipGetLastError() != hipSuccess) return KVTC_E_DEVICE;
+    if (launch_status() != KVTC_OK) return KVTC_E_DEVICE;
     const int64_t blocks = (a.S + kHistRows - 1) / kHistRows;
     if (blocks > 0) {
         hipLaunchKernelGGL(entropy_hist_kernel, dim3(static_cast<unsigned>(blocks), static_cast<unsigned>(a.units)),
                            dim3(kEntThreads), 0, st, a);
-        if (hipGetLastError() != hipSuccess) return KVTC_E_DEVICE;
+        if (launch_status() != KVTC_OK) return KVTC_E_DEVICE;
     }
     if (hipMemcpyAsync(counts_host, a.counts, n * 4, hipMemcpyDeviceToHost, st) != hipSuccess ||
         hipStreamSynchronize(st) != hipSuccess)
@@ -312,16 +312,16 @@ int32_t entropy_device_encode(const EntropyDevArgs &a, const uint32_t *enc_code_
         return KVTC_E_DEVICE;
     hipLaunchKernelGGL(fill_u32_kernel, dim3(grid_for(static_cast<int64_t>(a.archive_words))), dim3(kEntThreads), 0, st,
                        a.archive, a.archive_words);
-    if (hipGetLastError() != hipSuccess) return KVTC_E_DEVICE;
+    if (launch_status() != KVTC_OK) return KVTC_E_DEVICE;
     hipLaunchKernelGGL(entropy_chunk_bits_kernel, dim3(grid_for(static_cast<int64_t>(nc))), dim3(kEntThreads), 0, st, a);
-    if (hipGetLastError() != hipSuccess) return KVTC_E_DEVICE;
+    if (launch_status() != KVTC_OK) return KVTC_E_DEVICE;
     hipLaunchKernelGGL(entropy_chunk_pos_kernel, dim3(grid_for(static_cast<int64_t>(nk))), dim3(kEntThreads), 0, st, a);
-    if (hipGetLastError() != hipSuccess) return KVTC_E_DEVICE;
+    if (launch_status() != KVTC_OK) return KVTC_E_DEVICE;
     hipLaunchKernelGGL(entropy_encode_kernel, dim3(grid_for(static_cast<int64_t>(nc))), dim3(kEntThreads), 0, st, a);
-    if (hipGetLastError() != hipSuccess) return KVTC_E_DEVICE;
+    if (launch_status() != KVTC_OK) return KVTC_E_DEVICE;
     const unsigned gx = static_cast<unsigned>(std::min<int64_t>((a.S + kEntThreads - 1) / kEntThreads + 1, 4096));
     hipLaunchKernelGGL(entropy_plain_kernel, dim3(gx, static_cast<unsigned>(U)), dim3(kEntThreads), 0, st, a);
-    if (hipGetLastError() != hipSuccess) return KVTC_E_DEVICE;
+    if (launch_status() != KVTC_OK) return KVTC_E_DEVICE;
     if (hipMemcpyAsync(chunk_pos_host, a.chunk_pos, nc * 8, hipMemcpyDeviceToHost, st) != hipSuccess ||
         hipStreamSynchronize(st) != hipSuccess)
         return KVTC_E_DEVICE;
@@ -344,7 +344,7 @@ int32_t entropy_device_decode(const EntropyDevArgs &a) {
     if (rc != KVTC_OK) return rc;
     const unsigned gr = static_cast<unsigned>(std::min<int64_t>((a.S + kEntThreads - 1) / kEntThreads, 4096));
     hipLaunchKernelGGL(entropy_unplain_kernel, dim3(gr, static_cast<unsigned>(U)), dim3(kEntThreads), 0, st, a);
-    return hipGetLastError() == hipSuccess ? KVTC_OK : KVTC_E_DEVICE;
+    return launch_status();
 }
 
 }  // namespace kvtc

@@ -366,7 +366,7 @@ int32_t launch_fetch_rw(FetchPair m, int nt, hipStream_t stream) {
     auto kern = fetch_kernel<MIXED, NDB, KS, RW, NW, fetch_prefetch<MIXED, RW>()>;
     if (!allow_lds(reinterpret_cast<const void *>(kern))) return KVTC_E_DEVICE;
     hipLaunchKernelGGL(kern, dim3(static_cast<unsigned>(grid)), dim3(64 * NW), lds, stream, m);
-    return hipGetLastError() == hipSuccess ? KVTC_OK : KVTC_E_DEVICE;
+    return launch_status();
 }
 
 // Register staging of a tile's rows: the narrowest instantiated width that

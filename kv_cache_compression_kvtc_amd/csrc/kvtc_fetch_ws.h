@@ -405,7 +405,7 @@ int32_t launch_fetch_ws_rwb(FetchPair m, int nt, hipStream_t stream) {
     auto kern = fetch_ws_kernel<MIXED, KS, NDBW, RWB>;
     if (!allow_lds(reinterpret_cast<const void *>(kern))) return KVTC_E_DEVICE;
     hipLaunchKernelGGL(kern, dim3(static_cast<unsigned>(grid)), dim3(64 * kWsWaves), lds, stream, m);
-    return hipGetLastError() == hipSuccess ? KVTC_OK : KVTC_E_DEVICE;
+    return launch_status();
 }
 
 // Group-head contractions of 8 to 16 k-steps over 512-column blocks, tiles of

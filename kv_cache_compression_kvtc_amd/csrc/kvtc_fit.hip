@@ -195,12 +195,12 @@ template <typename XT>
 int32_t launch_moments(const FitKArgs &a, int64_t U, hipStream_t st) {
     const unsigned u = static_cast<unsigned>(U);
     hipLaunchKernelGGL(fit_mean_kernel<XT>, dim3((a.dg + 63) / 64, u, a.mchunks), dim3(kFitThreads), 0, st, a);
-    if (hipGetLastError() != hipSuccess) return KVTC_E_DEVICE;
+    if (launch_status() != KVTC_OK) return KVTC_E_DEVICE;
     hipLaunchKernelGGL(fit_mean_final_kernel, dim3(u), dim3(kFitThreads), 0, st, a);
-    if (hipGetLastError() != hipSuccess) return KVTC_E_DEVICE;
+    if (launch_status() != KVTC_OK) return KVTC_E_DEVICE;
     const int nt = a.dg / kCovTile;
     hipLaunchKernelGGL(fit_cov_kernel<XT>, dim3(nt * (nt + 1) / 2, u), dim3(kFitThreads), 0, st, a);
-    return hipGetLastError() == hipSuccess ? KVTC_OK : KVTC_E_DEVICE;
+    return launch_status();
 }
 
 }  // namespace
@@ -236,7 +236,7 @@ int32_t fit_device_ranges(const FitDeviceRows &r, const float *mu32_host, const 
         return KVTC_E_DEVICE;
     auto *kd = reinterpret_cast<unsigned long long *>(w + L.keys);
     hipLaunchKernelGGL(fill_keys_kernel, dim3(256), dim3(kFitThreads), 0, st, kd, static_cast<int64_t>(U * r.kslots));
-    if (hipGetLastError() != hipSuccess) return KVTC_E_DEVICE;
+    if (launch_status() != KVTC_OK) return KVTC_E_DEVICE;
     AppendArgs a{};
     a.x = r.rows;
     a.xsb = r.sb;

@@ -492,10 +492,11 @@ void frozen_ranges(const std::vector<double> &Xraw, int64_t S, int dg, const flo
 // -------------------------------------------------------------- blob build
 struct Layout {
     uint64_t off_unit, off_lambda, off_bits, off_qmin, off_qscale, off_mu, off_slot_comp,
-        off_slot_bits, off_basis, off_qlo, off_qinv, off_w16, off_bias, off_kdesc, off_fslot, total;
+        off_slot_bits, off_basis, off_qlo, off_qinv, off_w16, off_bias, off_kdesc, off_fslot, off_vdig, off_mv,
+        total;
 };
 
-Layout plan_layout(int64_t U, int dg, int rmax, int kslots, int kfetch) {
+Layout plan_layout(int64_t U, int dg, int rmax, int kslots, int kfetch, bool digits) {
     Layout L{};
     uint64_t o = align_up(sizeof(kvtc_state_header), kSectionAlign);
     auto take = [&](uint64_t bytes) {
@@ -518,6 +519,10 @@ Layout plan_layout(int64_t U, int dg, int rmax, int kslots, int kfetch) {
     L.off_bias = take(U * dg * sizeof(float));
     L.off_kdesc = take(U * static_cast<uint64_t>(kfetch / kKStep) * sizeof(uint32_t));
     L.off_fslot = take(U * static_cast<uint64_t>(kfetch) * sizeof(int32_t));
+    if (digits) {
+        L.off_vdig = take(U * 5 * static_cast<uint64_t>(kslots) * dg);
+        L.off_mv = take(U * static_cast<uint64_t>(kslots) * sizeof(double));
+    }
     L.total = o;
     return L;
 }
@@ -586,7 +591,19 @@ int32_t build_blob(const kvtc_config *cfg, int64_t B, int64_t H, int32_t rmax, c
     for (int64_t u = 0; u < U; ++u) max_steps = std::max(max_steps, n_ksteps[u]);
     const int kslots = std::max<int>(kSlotAlign, static_cast<int>(align_up(max_slots, kSlotAlign)));
     const int kfetch = kKStep * max_steps;
-    const Layout L = plan_layout(U, dg, rmax, kslots, kfetch);
+    // the int8 append's digit planes exist when every kept basis entry is at
+    // most 1 in magnitude (always so for an orthonormal basis)
+    bool digits = true;
+    for (int64_t u = 0; u < U && digits; ++u)
+        for (int i = 0; i < ranks[u] && digits; ++i) {
+            const float *src = &basis[(static_cast<size_t>(u) * rmax + i) * dg];
+            for (int d = 0; d < dg; ++d)
+                if (!(std::fabs(src[d]) <= 1.0f)) {
+                    digits = false;
+                    break;
+                }
+        }
+    const Layout L = plan_layout(U, dg, rmax, kslots, kfetch, digits);
     if (state_out == nullptr || *state_bytes < L.total) {
         *state_bytes = L.total;
         return state_out == nullptr ? KVTC_OK : KVTC_E_BUFSIZE;
@@ -634,7 +651,8 @@ int32_t build_blob(const kvtc_config *cfg, int64_t B, int64_t H, int32_t rmax, c
     h->off_bias = L.off_bias;
     h->off_kdesc = L.off_kdesc;
     h->off_fslot = L.off_fslot;
-    h->reserved[0] = h->reserved[1] = 0;
+    h->off_vdig = L.off_vdig;
+    h->off_mv = L.off_mv;
     h->total_bytes = L.total;
 
     auto *ui = section_mut<kvtc_unit_info>(state_out, L.off_unit);
@@ -652,6 +670,8 @@ int32_t build_blob(const kvtc_config *cfg, int64_t B, int64_t H, int32_t rmax, c
     auto *bias = section_mut<float>(state_out, L.off_bias);
     auto *kdesc = section_mut<uint32_t>(state_out, L.off_kdesc);
     auto *fslot = section_mut<int32_t>(state_out, L.off_fslot);
+    auto *vdig = digits ? section_mut<int8_t>(state_out, L.off_vdig) : nullptr;
+    auto *mv = digits ? section_mut<double>(state_out, L.off_mv) : nullptr;
 
     parallel_for(U, [&](int64_t u) {
         const int r = ranks[u];
@@ -685,6 +705,27 @@ int32_t build_blob(const kvtc_config *cfg, int64_t B, int64_t H, int32_t rmax, c
             const float *src = &basis[(static_cast<size_t>(u) * rmax + i) * dg];
             float *dst = &sbasis[sj * dg];
             for (int d = 0; d < dg; ++d) dst[d] = src[d];
+            if (digits) {
+                // rint(basis * 2^38) in five balanced base-256 digits, low digit first;
+                // |basis| <= 1 keeps the top digit within [-64, 64].  The slot's offset
+                // is mean . basis minus the constant the row digits leave out:
+                // the int8 append forms a row's digits from X ^ 0x808080, whose bytes
+                // as int8 sum to X - 0x808080 (X = x * 2^24).
+                double m = 0.0;
+                int64_t vsum = 0;
+                for (int d = 0; d < dg; ++d) {
+                    const int64_t vq = std::llrint(std::ldexp(static_cast<double>(src[d]), 38));
+                    vsum += vq;
+                    int64_t q = vq;
+                    for (int k = 0; k < 5; ++k) {
+                        const int64_t dk = static_cast<int8_t>(static_cast<uint8_t>(q & 0xFF));
+                        vdig[((static_cast<size_t>(u) * 5 + k) * kslots + j) * dg + d] = static_cast<int8_t>(dk);
+                        q = (q - dk) / 256;
+                    }
+                    m += static_cast<double>(mu[u * dg + d]) * static_cast<double>(src[d]);
+                }
+                mv[sj] = m - std::ldexp(static_cast<double>(vsum) * 8421504.0, -62);   // 8421504 = 0x808080
+            }
             double wscale = 1.0;
             if (cfg->mode == KVTC_MODE_DP) {
                 sqlo[sj] = static_cast<double>(qmin[ci]);
@@ -1024,7 +1065,7 @@ int32_t kvtc_fit_bytes_bound(const kvtc_config *cfg, int64_t B, int64_t H, size_
     // every run of equal widths is padded to whole k-steps: at most one run per
     // stored slot in DP mode, two runs (hi, lo) in mixed mode
     const int kfetch = cfg->mode == KVTC_MODE_MIXED ? kslots + 2 * kKStep : kKStep * kslots;
-    *bytes = plan_layout(U, dg, rmax, kslots, kfetch).total;
+    *bytes = plan_layout(U, dg, rmax, kslots, kfetch, true).total;   // the bound includes the digit planes
     return KVTC_OK;
 }
 

@@ -84,6 +84,17 @@ inline int32_t check_state(const void *blob, const kvtc_state_header **out) {
         if (s.off < sizeof(kvtc_state_header) || s.off % kSectionAlign != 0 || s.off >= h->total_bytes ||
             s.bytes > h->total_bytes - s.off)
             return KVTC_E_STATE;
+    // the int8 append's sections: both present or both absent
+    if ((h->off_vdig == 0) != (h->off_mv == 0)) return KVTC_E_STATE;
+    if (h->off_vdig) {
+        const struct {
+            uint64_t off, bytes;
+        } opt[] = {{h->off_vdig, U * 5 * ks * dg}, {h->off_mv, U * ks * 8}};
+        for (const auto &s : opt)
+            if (s.off < sizeof(kvtc_state_header) || s.off % kSectionAlign != 0 || s.off >= h->total_bytes ||
+                s.bytes > h->total_bytes - s.off)
+                return KVTC_E_STATE;
+    }
     // per-unit counts within the header's capacities (the kernels index the
     // slot arrays with them)
     const auto *ui = reinterpret_cast<const kvtc_unit_info *>(static_cast<const char *>(blob) + h->off_unit);

@@ -111,7 +111,7 @@ int32_t launch_probe_dn(const FetchPair &m, bool mixed, size_t lds, hipStream_t 
                       : fetch_probe_kernel<DS, NW, false, RW, (RW <= 8 ? 3 : (RW <= 16 ? 2 : 1))>;
     if (!allow_lds(reinterpret_cast<const void *>(kern))) return KVTC_E_DEVICE;
     hipLaunchKernelGGL(kern, dim3(static_cast<unsigned>(grid)), dim3(64 * NW), lds, stream, m);
-    return hipGetLastError() == hipSuccess ? KVTC_OK : KVTC_E_DEVICE;
+    return launch_status();
 }
 
 template <int RW>
@@ -138,7 +138,7 @@ int32_t launch_fetch_ws_probe(FetchPair m, int nt, int ks, int ndbw, int tile_wo
     auto kern = rwb <= 2 ? fetch_ws_kernel<true, 16, 2, 2, true> : fetch_ws_kernel<true, 16, 2, 3, true>;
     if (!allow_lds(reinterpret_cast<const void *>(kern))) return KVTC_E_DEVICE;
     hipLaunchKernelGGL(kern, dim3(static_cast<unsigned>(m.nblocks_per_xcd * 8)), dim3(64 * kWsWaves), lds, stream, m);
-    return hipGetLastError() == hipSuccess ? KVTC_OK : KVTC_E_DEVICE;
+    return launch_status();
 }
 
 int32_t launch_fetch_probe(const FetchPair &m, int ds, int nw, bool mixed, int rw, size_t lds, hipStream_t stream) {

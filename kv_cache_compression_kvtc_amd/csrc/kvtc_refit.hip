@@ -148,14 +148,14 @@ int32_t launch_refit_requantise(const RefitArgs &a0, int64_t units, hipStream_t 
     a.chunks = static_cast<int>((a.S + a.rows_per_chunk - 1) / a.rows_per_chunk);
     const unsigned U = static_cast<unsigned>(units);
     hipLaunchKernelGGL(refit_range_kernel, dim3(static_cast<unsigned>(a.chunks), U), dim3(kRefitThreads), 0, stream, a);
-    if (hipGetLastError() != hipSuccess) return KVTC_E_DEVICE;
+    if (launch_status() != KVTC_OK) return KVTC_E_DEVICE;
     hipLaunchKernelGGL(refit_finalize_kernel, dim3(U), dim3(kRefitThreads), 0, stream, a);
-    if (hipGetLastError() != hipSuccess) return KVTC_E_DEVICE;
+    if (launch_status() != KVTC_OK) return KVTC_E_DEVICE;
     const int64_t tiles = (a.S + kRefitRows - 1) / kRefitRows;
     if (tiles > 0x7FFFFFFF) return KVTC_E_SHAPE;
     const size_t lds = static_cast<size_t>(kRefitRows) * (a.row_stride / 4) * sizeof(uint32_t);
     hipLaunchKernelGGL(refit_requant_kernel, dim3(static_cast<unsigned>(tiles), U), dim3(kRefitThreads), lds, stream, a);
-    return hipGetLastError() == hipSuccess ? KVTC_OK : KVTC_E_DEVICE;
+    return launch_status();
 }
 
 }  // namespace kvtc

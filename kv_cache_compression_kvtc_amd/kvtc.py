@@ -23,7 +23,10 @@ MAGIC = 0x4354564B
 
 class KVTCError(RuntimeError):
     def __init__(self, status: int, what: str):
-        super().__init__(f"{what}: {status_string(status)} ({status})")
+        msg = f"{what}: {status_string(status)} ({status})"
+        if status == E_DEVICE and _lib is not None:
+            msg += ": " + _lib.kvtc_device_error_string().decode()
+        super().__init__(msg)
         self.status = status
 
 
@@ -54,7 +57,8 @@ class StateHeader(C.Structure):
                 ("off_mu", C.c_uint64), ("off_slot_comp", C.c_uint64), ("off_slot_bits", C.c_uint64),
                 ("off_basis", C.c_uint64), ("off_qlo", C.c_uint64), ("off_qinv", C.c_uint64),
                 ("off_w16", C.c_uint64), ("off_bias", C.c_uint64), ("total_bytes", C.c_uint64),
-                ("off_kdesc", C.c_uint64), ("off_fslot", C.c_uint64), ("reserved", C.c_uint64 * 2)]
+                ("off_kdesc", C.c_uint64), ("off_fslot", C.c_uint64), ("off_vdig", C.c_uint64),
+                ("off_mv", C.c_uint64)]
 
 
 class BytesReport(C.Structure):
@@ -96,6 +100,7 @@ _sig = {
     "kvtc_config_default": (None, [C.POINTER(Config), _i32, _i32]),
     "kvtc_status_string": (C.c_char_p, [_i32]),
     "kvtc_build_id": (C.c_char_p, []),
+    "kvtc_device_error_string": (C.c_char_p, []),
     "kvtc_fit_host": (_i32, [C.POINTER(Config), _vp, _i32, _i64, _i64, _i64, _vp, C.POINTER(_sz)]),
     "kvtc_fit_bytes_bound": (_i32, [C.POINTER(Config), _i64, _i64, C.POINTER(_sz)]),
     "kvtc_fit_workspace": (_i32, [C.POINTER(Config), _i64, _i64, _i64, C.POINTER(_sz)]),
@@ -636,6 +641,8 @@ def state_view(blob: np.ndarray) -> dict:
         "kdesc": sec(h.off_kdesc, np.uint32, (U, kf // 16)),
         "fslot": sec(h.off_fslot, np.int32, (U, kf)),
         "bias": sec(h.off_bias, np.float32, (U, dg)),
+        "vdig": sec(h.off_vdig, np.int8, (U, 5, ks, dg)) if h.off_vdig else None,
+        "mv": sec(h.off_mv, np.float64, (U, ks)) if h.off_mv else None,
     }
 
 

@@ -215,6 +215,30 @@ def test_state_build_derived_sections_follow_their_definitions():
         assert np.array_equal(v["qlo"][u, :ns], st.qmin32[u][comps].astype(np.float64))
         inv = np.where(sc > 0, 1.0 / np.where(sc > 0, sc, 1), 0.0)
         assert np.array_equal(v["qinv"][u, :ns], inv)
+        # int8 append operands: the five balanced base-256 digits of each slot's
+        # rint(basis * 2^38) (exact integers: int64 arithmetic), and mean . basis
+        dig = v["vdig"][u].astype(np.int64)                                 # [5, kslots, dg]
+        assert dig.min() >= -128 and dig.max() <= 127 and np.abs(dig[4]).max() <= 64
+        vq = np.rint(np.ldexp(st.V32[u][:, comps].astype(np.float64).T, 38)).astype(np.int64)   # [ns, dg]
+        got = sum(dig[k, :ns] * (256 ** k) for k in range(5))
+        assert np.array_equal(got, vq)
+        assert (dig[:, ns:] == 0).all()
+        # offset: mean . basis minus 2^-62 * 0x808080 * sum_d vq (the constant of the
+        # row digits, which are the bytes of x * 2^24 ^ 0x808080)
+        mv = Vc.T @ st.mu32[u].astype(np.float64) - np.ldexp(vq.sum(axis=1).astype(np.float64) * 0x808080, -62)
+        assert np.abs(v["mv"][u, :ns] - mv).max() <= 1e-12 * (np.abs(st.mu32[u]).sum() + st.Dg)
+
+
+def test_state_without_unit_basis_has_no_int8_operands():
+    """A basis entry above 1 in magnitude (not an orthonormal basis) leaves the
+    digit sections out: the blob says so with zero offsets."""
+    w = synth.WORKLOADS[1]
+    X = synth.generate(w, 1, 0, 256)
+    st = O.fit(oracle_cfg(w, budget=80), X)
+    st.V32 = st.V32.copy()
+    st.V32[0, 0, 0] = 1.5
+    v = K.state_view(blob_from_oracle(st))
+    assert v["header"].off_vdig == 0 and v["header"].off_mv == 0 and v["vdig"] is None
 
 
 # ---------------------------------------------------------------- bytes
