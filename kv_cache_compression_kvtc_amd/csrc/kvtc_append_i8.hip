@@ -94,7 +94,8 @@ __global__ __launch_bounds__(128 * NS, 2) void append_i8_kernel(AppendArgs a, in
 
     for (int w = tid; w < kI8Tok * row_words; w += NT) rows[w] = 0u;
     if (tid < kI8Tok) tabs[tid] = 0.f;
-    if (tid < 2) misc[tid] = 0.f;
+    if (tid < 4) misc[tid] = 0.f;
+    int *gmask = reinterpret_cast<int *>(misc + 2);   // 16-token groups with a decision left to the fp64 tile
     __syncthreads();
     {   // sum |mu| over the unit's row (a term of the error bound only)
         float s = 0.f;
@@ -262,7 +263,7 @@ __global__ __launch_bounds__(128 * NS, 2) void append_i8_kernel(AppendArgs a, in
     const bool tok_ok = tok < nvalid;
     const double E = 0x1p-39 * (1.5 * static_cast<double>(tabs[tok]) + 1.1 * static_cast<double>(a.dg) +
                                 0.5 * static_cast<double>(misc[0]));
-    bool bad = misc[1] != 0.f;
+    bool bad = false;        // a decision of this lane's token left to the fp64 tile
     double lt[16];
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
@@ -340,14 +341,21 @@ __global__ __launch_bounds__(128 * NS, 2) void append_i8_kernel(AppendArgs a, in
     // flag (any writer stores 1; a thread that read it early saw 0 or 1, both
     // consistent with the outcome); no static LDS, so the kernel may use the
     // whole LDS dynamically
-    if (bad) misc[1] = 1.f;
+    // the 16-token groups (the fp64 tile's waves) with a decision left to it;
+    // a row value outside the int8 range sends every group
+    if (bad) atomicOr(gmask, 1 << (tok >> 4));
     __syncthreads();
-    if (misc[1] != 0.f) {
-        // the fp64 tile of append_kernel on this block's tokens and slots
-        for (int w = tid; w < kI8Tok * row_words; w += NT) rows[w] = 0u;
+    const int need = misc[1] != 0.f ? 0xF : *gmask;
+    if (need) {
+        // the fp64 tile of append_kernel on this block's slots, for the groups
+        // that need it: their rows are cleared and rewritten, the others keep
+        // their certified codes (every row's result is its own: the same bytes)
+        for (int w = tid; w < kI8Tok * row_words; w += NT)
+            if ((need >> ((w / row_words) >> 4)) & 1) rows[w] = 0u;
         doublex4 acc64[2 * NS];
-        f64_project<_Float16, 2 * NS, true>(a, u, t0, nvalid, slot0, smem, acc64);
-        f64_quantise<MIXED, 2 * NS>(a, u, t0, nvalid, slot0, acc64, rows);
+        const bool active = wave < 4 && ((need >> wave) & 1);
+        f64_project<_Float16, 2 * NS, true>(a, u, t0, nvalid, slot0, smem, acc64, active);
+        if (active) f64_quantise<MIXED, 2 * NS>(a, u, t0, nvalid, slot0, acc64, rows);
         __syncthreads();
     }
 

@@ -19,7 +19,8 @@ __host__ __device__ constexpr size_t f64_stage_bytes(int nb) {
 
 // Latents of tokens [t0, t0 + nvalid) of unit u on slots [slot0, slot0 + 16 NB):
 // the block's first four waves hold the result, acc[nb][i] being the latent of
-// token 16*wave + (lane >> 4) + 4i and slot slot0 + 16nb + (lane & 15).  The
+// token 16*wave + (lane >> 4) + 4i and slot slot0 + 16nb + (lane & 15); a wave
+// called with active false skips its products (its tokens are not needed).  The
 // first 256 threads stage; every thread of the block must call this (barriers).
 // K-step order: k-step 4c + e of the contraction takes, at operand k = q, the
 // feature 16c + 4q + e (c = 16-column chunk); every append kernel uses this
@@ -27,7 +28,7 @@ __host__ __device__ constexpr size_t f64_stage_bytes(int nb) {
 // 16-byte vectors of the basis.
 template <typename XT, int NB, bool XVEC>
 __device__ __forceinline__ void f64_project(const AppendArgs &a, int u, int64_t t0, int nvalid, int slot0,
-                                            unsigned char *smem, doublex4 (&acc)[NB]) {
+                                            unsigned char *smem, doublex4 (&acc)[NB], bool active = true) {
     double *xs = reinterpret_cast<double *>(smem);                         // [2][64][kAppPad]
     float *vs = reinterpret_cast<float *>(xs + 2 * kAppTok * kAppPad);     // [2][NB*16][kAppPad]
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -105,7 +106,7 @@ __device__ __forceinline__ void f64_project(const AppendArgs &a, int u, int64_t 
     for (int kc = 0; kc < nchunks; ++kc) {
         const int buf = kc & 1;
         if (stager && kc + 1 < nchunks) load_chunk(kc + 1);
-        if (wave < 4) {
+        if (wave < 4 && active) {
             const double *xb = xs + buf * kAppTok * kAppPad;
             const float *vb = vs + buf * NB * 16 * kAppPad;
 #pragma unroll
