@@ -21,6 +21,7 @@ namespace {
 // partial softmax statistics (max, sum, weighted code sums) are merged per unit.
 constexpr int kAttChunk = 512;       // rows per partial block
 constexpr int kAttKsK = 16;          // k-steps of the key contraction (kfetch <= 256)
+constexpr int kAttPass = 4;          // value k-steps accumulated per pass over a chunk's rows
 
 struct AttendSide {
     const uint8_t *codes;
@@ -54,6 +55,22 @@ __device__ inline uint32_t row_field(const uint32_t *row, uint32_t sb) {
     const uint32_t off = sb & kOffsetMask, w = sb >> 24;
     const uint32_t wi = off >> 5, sh = off & 31u;
     return __builtin_amdgcn_alignbit(row[wi + 1], row[wi], sh) & ((1u << w) - 1u);
+}
+
+// Sum of v over each half of the wave (lanes 0-31 and 32-63), left in lanes
+// 16-31 and 48-63, with DPP moves only: neighbours in quads, then octets (half
+// row mirror), rows (row mirror), and row 0 (2) into row 1 (3).
+template <int CTRL, int ROWS>
+__device__ __forceinline__ float dpp_f32(float x) {
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, ROWS, 0xF, false));
+}
+__device__ __forceinline__ float half_wave_sum(float v) {
+    v += dpp_f32<0xB1, 0xF>(v);      // quad_perm [1,0,3,2]
+    v += dpp_f32<0x4E, 0xF>(v);      // quad_perm [2,3,0,1]
+    v += dpp_f32<0x141, 0xF>(v);     // row_half_mirror
+    v += dpp_f32<0x140, 0xF>(v);     // row_mirror
+    v += dpp_f32<0x142, 0xA>(v);     // row_bcast:15 into rows 1 and 3
+    return v;
 }
 
 // Staging of a chunk's code rows (256-thread blocks): word i of the chunk goes
@@ -179,20 +196,18 @@ __global__ __launch_bounds__(256) void attend_partial_kernel(AttendArgs a) {
     uint32_t *rows = reinterpret_cast<uint32_t *>(red + 4 * kMaxSlots);  // [kAttChunk][pitch]
     const int64_t s0 = static_cast<int64_t>(c) * kAttChunk;
     const int nrows = static_cast<int>(min<int64_t>(kAttChunk, a.s_end - s0));
-    const int nv = V.ui[u].n_slots;
     const int kp = (K.row_words + 1) | 1, vp = (V.row_words + 1) | 1;   // odd, > row_words
 
-    // the unit's coefficients and slot descriptors (at most 257, 256 and 256
-    // words: two, one and one per thread), then the chunk's key and value rows,
-    // all requested before any is used
-    uint32_t cq[2], cf, cs;
+    // the unit's coefficients (at most 257 and 256 words: two and one per
+    // thread), then the chunk's key and value rows, all requested before any is
+    // used
+    uint32_t cq[2], cf;
     {
         const float *qsrc = a.qt + static_cast<int64_t>(u) * (K.kslots + 1);
         const uint32_t *fsrc = reinterpret_cast<const uint32_t *>(a.qf + static_cast<int64_t>(u) * 2 * K.kfetch);
         cq[0] = tid <= K.kslots ? __float_as_uint(qsrc[tid]) : 0u;
         cq[1] = tid + 256 <= K.kslots ? __float_as_uint(qsrc[tid + 256]) : 0u;
         cf = tid < K.kfetch ? fsrc[tid] : 0u;                           // 2*kfetch halves
-        cs = tid < V.kslots ? V.sbits[static_cast<int64_t>(u) * V.kslots + tid] : 0u;
     }
     const uint32_t *ksrc = reinterpret_cast<const uint32_t *>(K.codes) + (static_cast<int64_t>(u) * K.capacity + s0) * K.row_words;
     const uint32_t *vsrc = reinterpret_cast<const uint32_t *>(V.codes) + (static_cast<int64_t>(u) * V.capacity + s0) * V.row_words;
@@ -203,7 +218,6 @@ __global__ __launch_bounds__(256) void attend_partial_kernel(AttendArgs a) {
     if (tid <= K.kslots) qt_l[tid] = __uint_as_float(cq[0]);
     if (tid + 256 <= K.kslots) qt_l[tid + 256] = __uint_as_float(cq[1]);
     if (tid < K.kfetch) ksb[tid] = cf;
-    if (tid < V.kslots) vsb[tid] = cs;
     stage_rows(ksrc, ktot, K.row_words, kp, rows, kr);
     __syncthreads();
 
@@ -266,26 +280,70 @@ __global__ __launch_bounds__(256) void attend_partial_kernel(AttendArgs a) {
     const float L = block_reduce(lsum, red, false);
     __syncthreads();
 
-    // p-weighted sums of the value codes: wave w takes rows w, w+4, ...; lane
-    // takes slots lane + 64t
-    float acc[kMaxSlots / 64];
-    uint32_t mysb[kMaxSlots / 64];
-#pragma unroll
-    for (int t = 0; t < kMaxSlots / 64; ++t) {
-        acc[t] = 0.f;
-        mysb[t] = lane + 64 * t < nv ? vsb[lane + 64 * t] : 0u;
-    }
-    const int ngroups = (nv + 63) >> 6;                // wave-uniform
-    for (int r = wave; r < nrows; r += 4) {
-        const float p = pl[r];
-        const uint32_t *row = rows + r * vp;
-#pragma unroll
-        for (int t = 0; t < kMaxSlots / 64; ++t)
-            if (t < ngroups) acc[t] = fmaf(p, static_cast<float>(row_field(row, mysb[t])), acc[t]);
-    }
+    // p-weighted sums of the value codes in the fetch order: wave w takes the
+    // 32-row tiles w, w + 4, ... of the chunk (lane: row lane & 31, half k-step
+    // lane >> 5) and decodes each of its k-steps' 8 codes as exact fp16 values
+    // (the fetch kernel's field decode); each code is accumulated as
+    // c * (p_hi + p_lo) in fp32 with one v_dot2, p * 2^12 split into two fp16
+    // parts (together within 2^-22 of p; the 2^12 keeps them normal).  The
+    // rows' sums are then added across the 32 row lanes, and the fetch columns
+    // mapped back to slots.  Up to kAttPass k-steps per pass over the rows.
     __syncthreads();                                   // the reductions' scratch is reused below
+    {
+        for (int j = lane; j < kMaxSlots; j += 64) red[wave * kMaxSlots + j] = 0.f;   // this wave's sums only
+        const int nksV = V.kfetch / 16;
+        const uint32_t half_k = lane >> 5;
+        const int tok = lane & 31;
+        const int ntiles = (nrows + 31) >> 5;
+        const int32_t *fs = V.fslot + static_cast<int64_t>(u) * V.kfetch;
+        for (int k0 = 0; k0 < nksV; k0 += kAttPass) {
+            uint32_t kd[kAttPass];
 #pragma unroll
-    for (int t = 0; t < kMaxSlots / 64; ++t) red[wave * kMaxSlots + lane + 64 * t] = acc[t];
+            for (int q = 0; q < kAttPass; ++q)
+                kd[q] = k0 + q < nksV ? __builtin_amdgcn_readfirstlane(V.kdesc[static_cast<int64_t>(u) * nksV + k0 + q])
+                                      : 0u;
+            float acc[kAttPass][8];
+#pragma unroll
+            for (int q = 0; q < kAttPass; ++q)
+#pragma unroll
+                for (int i = 0; i < 8; ++i) acc[q][i] = 0.f;
+            for (int t = wave; t < ntiles; t += 4) {
+                const int r = t * 32 + tok;
+                const float ps = r < nrows ? pl[r] * 4096.0f : 0.0f;
+                const _Float16 ph = static_cast<_Float16>(ps);
+                const half2 pw = {ph, static_cast<_Float16>(ps - static_cast<float>(ph))};
+                const uint32_t *row = rows + r * vp;
+#pragma unroll
+                for (int q = 0; q < kAttPass; ++q) {
+                    if (((kd[q] >> 16) & 0xFu) == 0u) continue;            // empty or past the end (uniform)
+                    const half8 cv = decode_kstep<false>(kd[q], row, nullptr, half_k);
+#pragma unroll
+                    for (int i = 0; i < 8; ++i) {
+                        const half2 cc = {cv[i], cv[i]};
+                        acc[q][i] = __builtin_amdgcn_fdot2(cc, pw, acc[q][i], false);
+                    }
+                }
+            }
+            // sums over the 32 row lanes of each half (in its lanes 16-31), then
+            // into this wave's slot sums (each slot has one fetch column;
+            // padding columns none)
+#pragma unroll
+            for (int q = 0; q < kAttPass; ++q)
+#pragma unroll
+                for (int i = 0; i < 8; ++i) acc[q][i] = half_wave_sum(acc[q][i]);
+            if (tok == 16) {
+#pragma unroll
+                for (int q = 0; q < kAttPass; ++q) {
+                    if (k0 + q >= nksV) break;
+#pragma unroll
+                    for (int i = 0; i < 8; ++i) {
+                        const int j = fs[(k0 + q) * 16 + half_k * 8 + i];
+                        if (j >= 0) red[wave * kMaxSlots + j] = acc[q][i] * 0x1p-12f;
+                    }
+                }
+            }
+        }
+    }
     __syncthreads();
     float *dst = a.part + (static_cast<int64_t>(u) * a.nchunks + c) * (V.kslots + 2);
     for (int j = tid; j < V.kslots; j += blockDim.x)
