@@ -43,7 +43,7 @@ struct AttendArgs {
     _Float16 *out;
     int64_t osb, osh;
     int64_t s_end;
-    int nchunks, H, D;
+    int nchunks, chunk_rows, H, D;     // chunks of chunk_rows rows (the last one shorter), <= kAttChunk
     float inv_sqrt_d;
     float *qt;          // [U][k.kslots + 1]: qt_j, then beta
     uint16_t *qf;       // [U][2][k.kfetch]: fp16 high and low parts of qt * 2^-e, fetch order
@@ -168,16 +168,18 @@ __global__ __launch_bounds__(256) void attend_prep_kernel(AttendArgs a) {
         a.qf[(static_cast<int64_t>(u) * 2 + 0) * k.kfetch + kk] = __builtin_bit_cast(uint16_t, hi);
         a.qf[(static_cast<int64_t>(u) * 2 + 1) * k.kfetch + kk] = __builtin_bit_cast(uint16_t, lo);
     }
+    // beta = (q . mu + sum_j min_j q . V_j) / sqrt(D), summed over the block
+    float bpart = 0.f;
+    for (int d = tid; d < a.D; d += blockDim.x) bpart = fmaf(ql[d], k.mu[static_cast<int64_t>(u) * a.D + d], bpart);
+    if (tid < k.kslots) bpart += mpart[tid];
+    const float beta = block_reduce(bpart, red, false);
     if (tid == 0) {
         a.qmul[u] = ldexpf(1.0f, e);
-        float beta = 0.f;
-        for (int d = 0; d < a.D; ++d) beta = fmaf(ql[d], k.mu[static_cast<int64_t>(u) * a.D + d], beta);
-        for (int j = 0; j < k.kslots; ++j) beta += mpart[j];
         a.qt[static_cast<int64_t>(u) * (k.kslots + 1) + k.kslots] = beta * a.inv_sqrt_d;
     }
 }
 
-// Per (chunk of kAttChunk rows, unit): scores from the key codes, the chunk's
+// Per (chunk of chunk_rows <= kAttChunk rows, unit): scores from the key codes, the chunk's
 // softmax max and sum, and the p-weighted sums of the value codes.  Rows are
 // staged in LDS at an odd pitch of at least row_words + 1 words: a thread per
 // row then reads without bank conflicts, and every row ends in a slack word for
@@ -194,8 +196,8 @@ __global__ __launch_bounds__(256) void attend_partial_kernel(AttendArgs a) {
     float *pl = reinterpret_cast<float *>(vsb + kMaxSlots);              // [kAttChunk]
     float *red = pl + kAttChunk;                                         // [4][kMaxSlots]
     uint32_t *rows = reinterpret_cast<uint32_t *>(red + 4 * kMaxSlots);  // [kAttChunk][pitch]
-    const int64_t s0 = static_cast<int64_t>(c) * kAttChunk;
-    const int nrows = static_cast<int>(min<int64_t>(kAttChunk, a.s_end - s0));
+    const int64_t s0 = static_cast<int64_t>(c) * a.chunk_rows;
+    const int nrows = static_cast<int>(min<int64_t>(a.chunk_rows, a.s_end - s0));
     const int kp = (K.row_words + 1) | 1, vp = (V.row_words + 1) | 1;   // odd, > row_words
 
     // the unit's coefficients (at most 257 and 256 words: two and one per
@@ -370,10 +372,20 @@ __global__ __launch_bounds__(256) void attend_merge_kernel(AttendArgs a) {
     for (int c = tid; c < a.nchunks; c += blockDim.x)
         l += expf(part[c * stride + V.kslots] - M) * part[c * stride + V.kslots + 1];
     const float L = block_reduce(l, red, false);
-    if (tid < V.kslots) {
-        float s = 0.f;
+    // the chunks' weights exp(m_c - M), 256 chunks at a time, shared by the slots
+    __shared__ float wch[256];
+    float s = 0.f;
+    for (int c0 = 0; c0 < a.nchunks; c0 += 256) {
+        __syncthreads();
+        if (c0 + tid < a.nchunks) wch[tid] = expf(part[(c0 + tid) * stride + V.kslots] - M);
+        __syncthreads();
         if (tid < nv) {
-            for (int c = 0; c < a.nchunks; ++c) s = fmaf(expf(part[c * stride + V.kslots] - M), part[c * stride + tid], s);
+            const int cn = min(256, a.nchunks - c0);
+            for (int c = 0; c < cn; ++c) s = fmaf(wch[c], part[(c0 + c) * stride + tid], s);
+        }
+    }
+    if (tid < V.kslots) {
+        if (tid < nv) {
             const int ci = V.comp[static_cast<int64_t>(u) * V.kslots + tid];
             s = s / L * V.qscale[static_cast<int64_t>(u) * V.rmax + ci];
         }
@@ -1037,6 +1049,8 @@ int32_t attend_impl(const kvtc_tensor_ref *k, const kvtc_tensor_ref *v, int64_t 
     a.osh = out_strides[1];
     a.s_end = s_end;
     a.nchunks = static_cast<int>(nchunks);
+    // rows shared evenly between the chunks (no nearly empty last chunk)
+    a.chunk_rows = nchunks > 0 ? static_cast<int>((s_end + nchunks - 1) / nchunks) : 0;
     a.H = static_cast<int>(hk->heads);
     a.D = hk->head_dim;
     a.inv_sqrt_d = 1.0f / sqrtf(static_cast<float>(hk->head_dim));
