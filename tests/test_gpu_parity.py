@@ -90,6 +90,38 @@ def test_append_matches_oracle(name, w, tensor):
     check_recon(O.fetch(st, dev_rows, prm), out, name)
 
 
+# ---------------------------------------------------------------- save / restore
+SAVE_CASES = [
+    ("batched", small(4, B=3, s_prefill=1000, s_total=1000 + 77), 0),
+    ("palu", small(3, H=16, s_prefill=2048, s_total=2048 + 45), 1),
+]
+
+
+@pytest.mark.parametrize("name,w,tensor", SAVE_CASES, ids=[c[0] for c in SAVE_CASES])
+def test_save_and_restore_mid_stream(name, w, tensor):
+    # KVTC page, the cache's state and offset setters: the state blob and the
+    # stored rows copied out in the middle of a stream and into fresh device
+    # buffers continue exactly as the original buffers do
+    print_case("save/restore", name)
+    X = synth.generate(w, tensor)
+    st = O.fit(oracle_cfg(w), X[:, :, : w.s_prefill])
+    blob = blob_from_oracle(st)
+    S, cut = X.shape[2], w.s_prefill + 21
+    a = DeviceStore(blob, capacity=S)
+    a.append(X[:, :, :w.s_prefill], 0)
+    a.append(X[:, :, w.s_prefill:cut], w.s_prefill)
+    # save: host copies of the blob, the rows so far and their params
+    saved = (blob.copy(), a.rows(cut).copy(), a.params_np(cut).copy() if a.params is not None else None)
+    b = DeviceStore(saved[0], capacity=S)
+    b.load_rows(saved[1], saved[2])
+    for ds in (a, b):
+        ds.append(X[:, :, cut:], cut)
+    assert np.array_equal(a.rows(S), b.rows(S))
+    if a.params is not None:
+        assert np.array_equal(a.params_np(S).view(np.uint16), b.params_np(S).view(np.uint16))
+    assert torch.equal(a.fetch(0, S), b.fetch(0, S))
+
+
 # ---------------------------------------------------------------- determinism
 def test_token_at_a_time_equals_all_at_once():
     # KVTC page, "NOT PATH-DEPENDENT": appending after prefill one token at a

@@ -5,6 +5,7 @@ bytes from the little-endian packing convention, closed forms, invariants of
 PCA, brute force on tiny DP instances, textbook Huffman facts and the byte
 formulas the pages define.
 """
+import io
 import itertools
 import json
 import math
@@ -308,6 +309,53 @@ def test_same_codes_whether_tokens_arrive_one_at_a_time_or_together():
         whole = O.append(st, X)[0]
         assert (one_by_one == together).all() and (together == whole).all()
         assert (O.to_f16(O.fetch(st, one_by_one)) == O.to_f16(O.fetch(st, whole))).all()
+
+
+def _save(st, rows, params, offset):
+    """Everything a stored tensor holds, as bytes (no pickles)."""
+    buf = io.BytesIO()
+    arrays = {f: np.asarray(getattr(st, f)) for f in ("r", "mu32", "lam", "V32", "bits", "qmin32", "qscale32")}
+    np.savez(buf, rows=rows, params=params if params is not None else np.zeros(0), offset=offset,
+             shape=np.array([st.B, st.H, st.D, st.hpu, st.row_stride]), **arrays)
+    return buf.getvalue()
+
+
+def _restore(cfg, blob):
+    z = np.load(io.BytesIO(blob))
+    B, H, D, hpu, stride = (int(v) for v in z["shape"])
+    st = O.TensorState(cfg, B, H, D, hpu, z["r"], z["mu32"], z["lam"], z["V32"], z["bits"], z["qmin32"],
+                       z["qscale32"], stride)
+    params = z["params"] if z["params"].size else None
+    return st, z["rows"], params, int(z["offset"])
+
+
+@pytest.mark.parametrize("wid", [1, 3])
+def test_save_and_restore_mid_stream_continues_identically(wid):
+    # KVTC page, the cache's state and offset setters: a cache saved in the middle
+    # of a stream and restored into new objects continues exactly as the original
+    # (the state and the stored rows are everything it holds)
+    w = synth.WORKLOADS[wid]
+    if wid == 3:
+        f = dict(w.__dict__)
+        f.update(H=8, s_prefill=300, s_total=340)
+        w = synth.Workload(**f)
+    S0, S = w.s_prefill, w.s_total
+    cut = S0 + 13
+    for tensor in (0, 1):
+        X = synth.generate(w, tensor, 0, S)
+        st = O.fit(_cfg(w), X[:, :, :S0])
+        rows_a, par_a = O.append(st, X[:, :, :cut])
+        st2, rows_s, par_s, off = _restore(st.cfg, _save(st, rows_a, par_a, cut))
+        assert off == cut
+        rows_b, par_b = O.append(st2, X[:, :, cut:])
+        rows = np.concatenate([rows_s, rows_b], axis=1)
+        whole, par_w = O.append(st, X)
+        assert np.array_equal(rows, whole)
+        params = None
+        if par_w is not None:
+            params = np.concatenate([par_s, par_b], axis=1)
+            assert np.array_equal(params.view(np.uint16), par_w.view(np.uint16))
+        assert (O.to_f16(O.fetch(st2, rows, params)) == O.to_f16(O.fetch(st, whole, par_w))).all()
 
 
 def test_near_lossless_at_full_rank_8_bits():
