@@ -19,9 +19,14 @@ namespace {
 // abar_j = sum_s p_s c_sj (softmax weights p summing to one), so neither keys nor
 // values are ever reconstructed per row.  The rows are split into chunks whose
 // partial softmax statistics (max, sum, weighted code sums) are merged per unit.
-constexpr int kAttChunk = 512;       // rows per partial block
+constexpr int kAttSegMax = 9216;     // rows per partial block at most (their scores stay in LDS)
+constexpr int kAttSeg = 256;         // rows per segment at least (unless the cache is shorter)
+constexpr int kAttBlocks = 512;      // partial blocks worth filling the GPU with (two per CU)
+constexpr int kAttWaves = 8;         // waves per partial block
+constexpr int kAttPairs = 8;         // scorer products whose operands a lane keeps in registers
+constexpr int kAttThreads = 64 * kAttWaves;
+constexpr int kAttStage = 3;         // staged 16-byte chunks per thread and sub-chunk (24 KiB per block)
 constexpr int kAttKsK = 16;          // k-steps of the key contraction (kfetch <= 256)
-constexpr int kAttPass = 4;          // value k-steps accumulated per pass over a chunk's rows
 
 struct AttendSide {
     const uint8_t *codes;
@@ -43,34 +48,143 @@ struct AttendArgs {
     _Float16 *out;
     int64_t osb, osh;
     int64_t s_end;
-    int nchunks, chunk_rows, H, D;     // chunks of chunk_rows rows (the last one shorter), <= kAttChunk
+    int nchunks, chunk_rows, H, D;     // segments of chunk_rows rows (the last one shorter), <= kAttSegMax
+    int sub;                           // rows per staged sub-chunk: 64, 128 or 256 (the window fits the staging)
     float inv_sqrt_d;
-    float *qt;          // [U][k.kslots + 1]: qt_j, then beta
-    uint16_t *qf;       // [U][2][k.kfetch]: fp16 high and low parts of qt * 2^-e, fetch order
-    float *qmul;        // [U]: 2^e
+    float *qt;          // [U][k.kslots + 1]: qt_j, then the scorer's offset
+    uint8_t *qa;        // [U][k.kfetch / 16][4][16]: int8 digits of Q (scorer operands, fetch order)
+    float *qmul;        // [U]: 2^(e - 30), the weight of one unit of Q
+    uint32_t *pairs;    // [U][1 + 2 kAttKsK]: count, then per scorer product ksA | ksB << 8 | w << 16, offA | offB << 16
     float *part;        // [U][nchunks][v.kslots + 2]: abar partial sums, then max, sum
 };
+
+typedef int i32x4 __attribute__((ext_vector_type(4)));
+typedef int i32x16 __attribute__((ext_vector_type(16)));
+
+// The sixteen codes of one k-step (16 fetch columns of width W; off: the
+// k-step's first bit in the lane's row) of a row as int8 bytes in four
+// registers: byte b of R[r] is the code of fetch column t = 4r + b of the
+// k-step, whose field starts at bit pos(W, t) of the k-step's window, with
+//   W = 8: 8t,  W = 4: 32(r >> 1) + 4(r & 1) + 8b,  W = 2: 8b + 2r,  W = 3: 3t,
+//   W = 1: 4r + b,
+// the bit positions the fetch kernel's decode gives its columns (so byte order
+// and fetch order agree).  8-bit codes become c - 128 (c ^ 0x80 read as int8),
+// which the callers correct for; narrower codes are their own values.  The
+// window reads up to five words from the k-step's first word; words past the
+// row's fields only reach padding columns.
+template <int W>
+__device__ __forceinline__ void kstep_bytes_w(uint32_t off, const uint32_t *row, uint32_t (&R)[4]) {
+    const uint32_t wi = off >> 5, sh = off & 31u;
+    if constexpr (W == 2) {
+        const uint32_t x = __builtin_amdgcn_alignbit(row[wi + 1], row[wi], sh);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) R[r] = (x >> (2 * r)) & 0x03030303u;
+    } else if constexpr (W == 4) {
+        const uint32_t x0 = __builtin_amdgcn_alignbit(row[wi + 1], row[wi], sh);
+        const uint32_t x1 = __builtin_amdgcn_alignbit(row[wi + 2], row[wi + 1], sh);
+        R[0] = x0 & 0x0F0F0F0Fu;
+        R[1] = (x0 >> 4) & 0x0F0F0F0Fu;
+        R[2] = x1 & 0x0F0F0F0Fu;
+        R[3] = (x1 >> 4) & 0x0F0F0F0Fu;
+    } else if constexpr (W == 8) {
+#pragma unroll
+        for (int r = 0; r < 4; ++r) R[r] = __builtin_amdgcn_alignbit(row[wi + r + 1], row[wi + r], sh) ^ 0x80808080u;
+    } else if constexpr (W == 1) {
+        // nibble r spread over the four bytes: the shifted copies 0, 7, 14, 21 of a
+        // 4-bit value never overlap, so the product has no carries
+        const uint32_t x = __builtin_amdgcn_alignbit(row[wi + 1], row[wi], sh);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) R[r] = (((x >> (4 * r)) & 0xFu) * 0x00204081u) & 0x01010101u;
+    } else if constexpr (W == 3) {
+        const uint32_t x0 = __builtin_amdgcn_alignbit(row[wi + 1], row[wi], sh);
+        const uint32_t x1 = __builtin_amdgcn_alignbit(row[wi + 2], row[wi + 1], sh);
+        const uint32_t y = __builtin_amdgcn_alignbit(x1, x0, 16);      // window bits 16..47
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            uint32_t v = 0;
+#pragma unroll
+            for (int b = 0; b < 4; ++b) {
+                const int t = 4 * r + b;
+                const uint32_t f = t < 6 ? (x0 >> (3 * t)) & 7u : (y >> (3 * t - 16)) & 7u;
+                v |= f << (8 * b);
+            }
+            R[r] = v;
+        }
+    } else {
+#pragma unroll
+        for (int r = 0; r < 4; ++r) R[r] = 0u;
+    }
+}
+
+// 4x4 byte transpose inside each quad of lanes (lanes 4q..4q+3): lane 4q+n
+// returns, as byte s, byte n of lane 4q+s's v.  Two butterfly stages, each a
+// DPP exchange with the partner lane and a byte select (s1, s2: the lane's
+// selectors from quad_selectors).
+__device__ __forceinline__ void quad_selectors(uint32_t lane, uint32_t &s1, uint32_t &s2) {
+    s1 = (lane & 1u) ? 0x03070105u : 0x06020400u;   // swaps lane bit 0 with byte bit 0
+    s2 = (lane & 2u) ? 0x03020706u : 0x05040100u;   // swaps lane bit 1 with byte bit 1
+}
+__device__ __forceinline__ uint32_t quad_transpose(uint32_t v, uint32_t s1, uint32_t s2) {
+    uint32_t p = static_cast<uint32_t>(__builtin_amdgcn_mov_dpp(static_cast<int>(v), 0xB1, 0xF, 0xF, false));
+    v = __builtin_amdgcn_perm(p, v, s1);
+    p = static_cast<uint32_t>(__builtin_amdgcn_mov_dpp(static_cast<int>(v), 0x4E, 0xF, 0xF, false));
+    return __builtin_amdgcn_perm(p, v, s2);
+}
+
+// The value side's operands of one k-step for the 4x4x4 products: lane n of a
+// quad ends with B[r] holding, as byte s, the code of fetch column 4r + n in
+// the quad's row s (kstep_bytes_w's bytes, transposed across the quad).  For
+// widths 2, 4 and 8 the raw window words are transposed first, which yields
+// the same bytes with fewer transposes.
+template <int W>
+__device__ __forceinline__ void kstep_bytes_quad_w(uint32_t off, const uint32_t *row, uint32_t s1, uint32_t s2,
+                                                   uint32_t (&B)[4]) {
+    const uint32_t wi = off >> 5, sh = off & 31u;
+    if constexpr (W == 2) {
+        const uint32_t u0 = quad_transpose(__builtin_amdgcn_alignbit(row[wi + 1], row[wi], sh), s1, s2);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) B[r] = (u0 >> (2 * r)) & 0x03030303u;
+    } else if constexpr (W == 4) {
+        const uint32_t u0 = quad_transpose(__builtin_amdgcn_alignbit(row[wi + 1], row[wi], sh), s1, s2);
+        const uint32_t u1 = quad_transpose(__builtin_amdgcn_alignbit(row[wi + 2], row[wi + 1], sh), s1, s2);
+        B[0] = u0 & 0x0F0F0F0Fu;
+        B[1] = (u0 >> 4) & 0x0F0F0F0Fu;
+        B[2] = u1 & 0x0F0F0F0Fu;
+        B[3] = (u1 >> 4) & 0x0F0F0F0Fu;
+    } else if constexpr (W == 8) {
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+            B[r] = quad_transpose(__builtin_amdgcn_alignbit(row[wi + r + 1], row[wi + r], sh), s1, s2) ^ 0x80808080u;
+    } else {
+        uint32_t R[4];
+        kstep_bytes_w<W>(off, row, R);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) B[r] = quad_transpose(R[r], s1, s2);
+    }
+}
+
+// One k-step's p-weighted sums over the sub-chunk's groups of 64 rows (at most
+// four; group g's digits of P in Ag[g], its rows at row0 + g * 64 * row_words).
+template <int W>
+__device__ __forceinline__ void value_kstep(i32x4 (&acc)[4], uint32_t off, const uint32_t *row0, int row_words,
+                                            int ng, const uint32_t (&Ag)[4], uint32_t s1, uint32_t s2) {
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+        if (g < ng) {
+            uint32_t B[4];
+            kstep_bytes_quad_w<W>(off, row0 + g * 64 * row_words, s1, s2, B);
+#pragma unroll
+            for (int rr = 0; rr < 4; ++rr)
+                acc[rr] = __builtin_amdgcn_mfma_i32_4x4x4i8(static_cast<int>(Ag[g]), static_cast<int>(B[rr]), acc[rr], 0,
+                                                            0, 0);
+        }
+    }
+}
 
 __device__ inline uint32_t row_field(const uint32_t *row, uint32_t sb) {
     const uint32_t off = sb & kOffsetMask, w = sb >> 24;
     const uint32_t wi = off >> 5, sh = off & 31u;
     return __builtin_amdgcn_alignbit(row[wi + 1], row[wi], sh) & ((1u << w) - 1u);
-}
-
-// Sum of v over each half of the wave (lanes 0-31 and 32-63), left in lanes
-// 16-31 and 48-63, with DPP moves only: neighbours in quads, then octets (half
-// row mirror), rows (row mirror), and row 0 (2) into row 1 (3).
-template <int CTRL, int ROWS>
-__device__ __forceinline__ float dpp_f32(float x) {
-    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, ROWS, 0xF, false));
-}
-__device__ __forceinline__ float half_wave_sum(float v) {
-    v += dpp_f32<0xB1, 0xF>(v);      // quad_perm [1,0,3,2]
-    v += dpp_f32<0x4E, 0xF>(v);      // quad_perm [2,3,0,1]
-    v += dpp_f32<0x141, 0xF>(v);     // row_half_mirror
-    v += dpp_f32<0x140, 0xF>(v);     // row_mirror
-    v += dpp_f32<0x142, 0xA>(v);     // row_bcast:15 into rows 1 and 3
-    return v;
 }
 
 // Staging of a chunk's code rows (256-thread blocks): word i of the chunk goes
@@ -110,6 +224,43 @@ __device__ inline void stage_rows(const uint32_t *src, int total, int row_words,
     for (int base = 256 * kStageB; base < total; base += 256 * kStageB) {
         stage_load(src, total, base, r);
         stage_store(total, base, row_words, pitch, rows, r);
+    }
+}
+
+// Staging of a sub-chunk's code rows: its bytes are copied as the 16-byte
+// chunks of the aligned window [a0, a0 + 16 nch) that covers them, chunk
+// k * kAttThreads + tid per thread (every load issued, past the end clamped to the last
+// chunk, so all are in flight before any is stored), into a linear LDS buffer:
+// the sub-chunk's row r then starts at word delta + r * row_words.  The window
+// lies in the pages of the rows it covers.
+typedef const u32x4 __attribute__((address_space(1))) *GlobalChunks;   // global memory (not flat)
+
+struct SubSrc {
+    GlobalChunks src;
+    int nch, delta;
+};
+
+__device__ inline SubSrc sub_src(const uint8_t *codes, int64_t row0, int nrows, int row_stride) {
+    const uintptr_t b0 = reinterpret_cast<uintptr_t>(codes) + static_cast<uintptr_t>(row0) * row_stride;
+    const uintptr_t a0 = b0 & ~static_cast<uintptr_t>(15);
+    SubSrc g;
+    g.src = reinterpret_cast<GlobalChunks>(a0);
+    g.delta = static_cast<int>((b0 - a0) >> 2);
+    g.nch = static_cast<int>((b0 - a0 + static_cast<uintptr_t>(nrows) * row_stride + 15) >> 4);
+    return g;
+}
+
+__device__ inline void sub_load(const SubSrc &g, u32x4 (&r)[kAttStage]) {
+#pragma unroll
+    for (int k = 0; k < kAttStage; ++k)
+        r[k] = g.src[min(k * kAttThreads + static_cast<int>(threadIdx.x), max(g.nch, 1) - 1)];
+}
+
+__device__ inline void sub_store(const SubSrc &g, uint32_t *buf, const u32x4 (&r)[kAttStage]) {
+#pragma unroll
+    for (int k = 0; k < kAttStage; ++k) {
+        const int i = k * kAttThreads + static_cast<int>(threadIdx.x);
+        if (i < g.nch) reinterpret_cast<u32x4 *>(buf)[i] = r[k];
     }
 }
 
@@ -154,19 +305,48 @@ __global__ __launch_bounds__(256) void attend_prep_kernel(AttendArgs a) {
         mpart[tid] = mp;
         qts[tid] = qt;
     }
-    // the scorer's operands in fetch order: qt * 2^-e as an fp16 high part and an
-    // fp16 remainder, with 2^e > max |qt| so that neither overflows (padding
-    // columns are zero)
+    // the scorer's operands in fetch order: Q = rint(qt * 2^(30 - e)), with
+    // 2^e > max |qt| so that |Q| < 2^30, as four balanced int8 digits
+    // (Q = sum_d d_d 256^d; the bytes of (Q + 0x808080) ^ 0x808080), digit d of
+    // fetch column 16 ks + t at byte (4 ks + d) * 16 + t; padding columns are zero.
+    // The scorer reads 8-bit codes as c - 128; the missing 128 * sum Q over the
+    // 8-bit columns is added to the offset.
     const float amax = block_reduce(fabsf(qt), red, true);
     int e = 0;
     if (amax > 0.f) frexpf(amax, &e);
+    const int nks = k.kfetch >> 4;
+    uint8_t *qa = a.qa + static_cast<int64_t>(u) * 4 * k.kfetch;
+    float q8 = 0.f;
     for (int kk = tid; kk < k.kfetch; kk += blockDim.x) {
         const int j = k.fslot[static_cast<int64_t>(u) * k.kfetch + kk];
-        const float v = j >= 0 ? ldexpf(qts[j], -e) : 0.f;
-        const _Float16 hi = static_cast<_Float16>(v);
-        const _Float16 lo = static_cast<_Float16>(v - static_cast<float>(hi));
-        a.qf[(static_cast<int64_t>(u) * 2 + 0) * k.kfetch + kk] = __builtin_bit_cast(uint16_t, hi);
-        a.qf[(static_cast<int64_t>(u) * 2 + 1) * k.kfetch + kk] = __builtin_bit_cast(uint16_t, lo);
+        const int ks = kk >> 4, t = kk & 15;
+        const int32_t Q = j >= 0 ? static_cast<int32_t>(rintf(ldexpf(qts[j], 30 - e))) : 0;
+        const uint32_t W = (static_cast<uint32_t>(Q) + 0x808080u) ^ 0x808080u;
+#pragma unroll
+        for (int d = 0; d < 4; ++d) qa[(ks * 4 + d) * 16 + t] = static_cast<uint8_t>(W >> (8 * d));
+        if (j >= 0 && ((k.kdesc[static_cast<int64_t>(u) * nks + ks] >> 16) & 0xFu) == 8u) q8 += static_cast<float>(Q);
+    }
+    const float c8 = block_reduce(q8, red, false);
+    // the scorer's products: consecutive k-steps of one width in pairs (lanes
+    // 0-31 take the first, lanes 32-63 the second, so a product decodes one width)
+    if (tid == 0) {
+        const uint32_t *kd = k.kdesc + static_cast<int64_t>(u) * nks;
+        uint32_t *pr = a.pairs + static_cast<int64_t>(u) * (1 + 2 * kAttKsK);
+        int np = 0;
+        for (int ks = 0; ks < nks;) {
+            const uint32_t w = (kd[ks] >> 16) & 0xFu;
+            if (w == 0u) {
+                ++ks;
+                continue;
+            }
+            const bool two = ks + 1 < nks && ((kd[ks + 1] >> 16) & 0xFu) == w;
+            const uint32_t kb = two ? static_cast<uint32_t>(ks + 1) : 0xFFu;
+            pr[1 + 2 * np] = static_cast<uint32_t>(ks) | (kb << 8) | (w << 16);
+            pr[2 + 2 * np] = (kd[ks] & 0xFFFFu) | (two ? (kd[ks + 1] & 0xFFFFu) << 16 : 0u);
+            ++np;
+            ks += two ? 2 : 1;
+        }
+        pr[0] = static_cast<uint32_t>(np);
     }
     // beta = (q . mu + sum_j min_j q . V_j) / sqrt(D), summed over the block
     float bpart = 0.f;
@@ -174,182 +354,262 @@ __global__ __launch_bounds__(256) void attend_prep_kernel(AttendArgs a) {
     if (tid < k.kslots) bpart += mpart[tid];
     const float beta = block_reduce(bpart, red, false);
     if (tid == 0) {
-        a.qmul[u] = ldexpf(1.0f, e);
-        a.qt[static_cast<int64_t>(u) * (k.kslots + 1) + k.kslots] = beta * a.inv_sqrt_d;
+        a.qmul[u] = ldexpf(1.0f, e - 30);
+        a.qt[static_cast<int64_t>(u) * (k.kslots + 1) + k.kslots] = beta * a.inv_sqrt_d + ldexpf(128.0f * c8, e - 30);
     }
 }
 
-// Per (chunk of chunk_rows <= kAttChunk rows, unit): scores from the key codes, the chunk's
-// softmax max and sum, and the p-weighted sums of the value codes.  Rows are
-// staged in LDS at an odd pitch of at least row_words + 1 words: a thread per
-// row then reads without bank conflicts, and every row ends in a slack word for
-// its last field window (fields end inside the row, so the slack word's bits
-// are always masked off).
-__global__ __launch_bounds__(256) void attend_partial_kernel(AttendArgs a) {
+// Per (segment of chunk_rows <= kAttSegMax rows, unit): scores from the key codes,
+// the segment's softmax max and sum, and the p-weighted sums of the value
+// codes, both contractions on int8 MFMA with exact int32 accumulation.  The
+// key rows, then the value rows, stream through two LDS buffers of `sub` rows
+// (linear copies of the rows' 16-byte-aligned windows, with slack words after
+// the last row for its k-step windows): while one buffer is decoded, the next
+// sub-chunk's chunks are in flight in registers.  The
+// segment's scores stay in LDS, turned into weights once the keys are done.
+template <int KW>
+__global__ __launch_bounds__(kAttThreads) void attend_partial_kernel(AttendArgs a) {
     extern __shared__ __align__(16) unsigned char smem[];
-    const int c = blockIdx.x, u = blockIdx.y, tid = threadIdx.x, lane = tid & 63;
+    const int c = blockIdx.x, u = blockIdx.y, tid = threadIdx.x;
+    const uint32_t lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const AttendSide &K = a.k, &V = a.v;
-    float *qt_l = reinterpret_cast<float *>(smem);                       // [K.kslots + 1]
-    uint32_t *ksb = reinterpret_cast<uint32_t *>(qt_l + kMaxSlots + 4);  // [2][K.kfetch] fp16 (16-byte aligned)
-    uint32_t *vsb = ksb + kMaxSlots;                                     // [V.kslots]
-    float *pl = reinterpret_cast<float *>(vsb + kMaxSlots);              // [kAttChunk]
-    float *red = pl + kAttChunk;                                         // [4][kMaxSlots]
-    uint32_t *rows = reinterpret_cast<uint32_t *>(red + 4 * kMaxSlots);  // [kAttChunk][pitch]
+    u32x4 *qal = reinterpret_cast<u32x4 *>(smem);                        // [kAttKsK][4] + 1 scorer operands
+    float *red = reinterpret_cast<float *>(qal + kAttKsK * 4 + 1);      // [kAttWaves] block reductions
+    float *pl = red + kAttWaves;                                         // [chunk_rows] scores, then weights
+    uint32_t *pw = reinterpret_cast<uint32_t *>(pl);                     //   as int8 digit words
+    const int sub = a.sub, bw = (sub * max(K.row_words, V.row_words) + 16 + 3) & ~3;   // buffer words
+    uint32_t *buf0 = reinterpret_cast<uint32_t *>(pl + ((a.chunk_rows + 3) & ~3));
+    uint32_t *buf1 = buf0 + bw;
     const int64_t s0 = static_cast<int64_t>(c) * a.chunk_rows;
     const int nrows = static_cast<int>(min<int64_t>(a.chunk_rows, a.s_end - s0));
-    const int kp = (K.row_words + 1) | 1, vp = (V.row_words + 1) | 1;   // odd, > row_words
+    const int nsub = (nrows + sub - 1) / sub;
+    // step j < nsub stages key sub-chunk j, step nsub + j value sub-chunk j
+    auto step_src = [&](int st) __attribute__((always_inline)) {
+        const bool key = st < nsub;
+        const int j = key ? st : st - nsub;
+        const AttendSide &T = key ? K : V;
+        return sub_src(T.codes, static_cast<int64_t>(u) * T.capacity + s0 + static_cast<int64_t>(j) * sub,
+                       min(sub, nrows - j * sub), T.row_words * 4);
+    };
 
-    // the unit's coefficients (at most 257 and 256 words: two and one per
-    // thread), then the chunk's key and value rows, all requested before any is
-    // used
-    uint32_t cq[2], cf;
-    {
-        const float *qsrc = a.qt + static_cast<int64_t>(u) * (K.kslots + 1);
-        const uint32_t *fsrc = reinterpret_cast<const uint32_t *>(a.qf + static_cast<int64_t>(u) * 2 * K.kfetch);
-        cq[0] = tid <= K.kslots ? __float_as_uint(qsrc[tid]) : 0u;
-        cq[1] = tid + 256 <= K.kslots ? __float_as_uint(qsrc[tid + 256]) : 0u;
-        cf = tid < K.kfetch ? fsrc[tid] : 0u;                           // 2*kfetch halves
+    u32x4 stg[kAttStage];
+    SubSrc g0 = step_src(0);
+    sub_load(g0, stg);
+    const int nksK = K.kfetch >> 4;
+    if (tid < 4 * nksK) qal[tid] = reinterpret_cast<const u32x4 *>(a.qa + static_cast<int64_t>(u) * 4 * K.kfetch)[tid];
+    if (tid == 0) qal[kAttKsK * 4] = u32x4{0u, 0u, 0u, 0u};
+    // the scorer's products (uniform widths), and per lane its k-step's offset
+    // and the LDS address of its A operand (digit row d < 4 of the lane's
+    // k-step; a zero vector for lanes 4-31 of a half and for a product's
+    // missing second k-step)
+    const uint32_t *pr = a.pairs + static_cast<int64_t>(u) * (1 + 2 * kAttKsK);
+    const int npairs = static_cast<int>(pr[0]);
+    // (the first kAttPairs products from registers, any others decoded per use)
+    auto pair_lane = [&](int m, uint32_t &wid, uint32_t &off, uint32_t &addr) __attribute__((always_inline)) {
+        const uint32_t meta = pr[1 + 2 * m], offs = pr[2 + 2 * m];
+        const bool hi = lane >= 32;
+        const uint32_t ks = hi ? (meta >> 8) & 0xFFu : meta & 0xFFu;
+        const bool ok = ks != 0xFFu;
+        wid = (meta >> 16) & 0xFu;
+        off = ok && hi ? offs >> 16 : offs & 0xFFFFu;
+        addr = ok && (lane & 31u) < 4u ? ks * 4u + (lane & 31u) : static_cast<uint32_t>(kAttKsK * 4);
+    };
+    uint32_t pwid[kAttPairs], poff[kAttPairs], paddr[kAttPairs];
+#pragma unroll
+    for (int m = 0; m < kAttPairs; ++m) {
+        pwid[m] = 0u;
+        poff[m] = 0u;
+        paddr[m] = kAttKsK * 4;
+        if (m < npairs) pair_lane(m, pwid[m], poff[m], paddr[m]);
     }
-    const uint32_t *ksrc = reinterpret_cast<const uint32_t *>(K.codes) + (static_cast<int64_t>(u) * K.capacity + s0) * K.row_words;
-    const uint32_t *vsrc = reinterpret_cast<const uint32_t *>(V.codes) + (static_cast<int64_t>(u) * V.capacity + s0) * V.row_words;
-    const int ktot = nrows * K.row_words, vtot = nrows * V.row_words;
-    uint32_t kr[kStageB], vr[kStageB];
-    stage_load(ksrc, ktot, 0, kr);
-    stage_load(vsrc, vtot, 0, vr);
-    if (tid <= K.kslots) qt_l[tid] = __uint_as_float(cq[0]);
-    if (tid + 256 <= K.kslots) qt_l[tid + 256] = __uint_as_float(cq[1]);
-    if (tid < K.kfetch) ksb[tid] = cf;
-    stage_rows(ksrc, ktot, K.row_words, kp, rows, kr);
+    const float beta = a.qt[static_cast<int64_t>(u) * (K.kslots + 1) + K.kslots], mul = a.qmul[u];
+    // this wave's value k-steps w + kAttWaves i: widths and offsets (uniform), and the
+    // stored slots of the columns lane n of a quad sums (fetch columns 4r + n)
+    const int nksV = V.kfetch >> 4;
+    const uint32_t n = lane & 3u;
+    uint32_t vw[KW], voff[KW];
+    int fsv[KW][4];
+#pragma unroll
+    for (int i = 0; i < KW; ++i) {
+        const int ks = wave + kAttWaves * i;
+        const uint32_t kd = ks < nksV ? V.kdesc[static_cast<int64_t>(u) * nksV + ks] : 0u;
+        vw[i] = (kd >> 16) & 0xFu;
+        voff[i] = kd & 0xFFFFu;
+#pragma unroll
+        for (int rr = 0; rr < 4; ++rr)
+            fsv[i][rr] = ks < nksV ? V.fslot[static_cast<int64_t>(u) * V.kfetch + ks * 16 + 4 * rr + static_cast<int>(n)] : -1;
+    }
+    uint32_t s1, s2;
+    quad_selectors(lane, s1, s2);
+    sub_store(g0, buf0, stg);
+    int dcur = g0.delta;                              // the current buffer's first-row word
     __syncthreads();
 
-    // scores of this thread's two rows, k-step by k-step in the fetch order: the
-    // fetch kernel's field decode gives a k-step's 16 codes as exact fp16 values,
-    // which are dotted (fp32 accumulation) with the high and low fp16 parts of the
-    // prescaled coefficients; rows past the chunk are decoded from stale words and
-    // never stored, and padding columns have zero coefficients
-    float mloc = -__builtin_huge_valf();
-    {
-        uint32_t kd[kAttKsK];
-        const int nksK = K.kfetch / 16;
+    float mloc = -__builtin_huge_valf(), M = 0.f, L = 0.f;
+    i32x4 acc[KW][4];
 #pragma unroll
-        for (int ks = 0; ks < kAttKsK; ++ks)
-            kd[ks] = ks < nksK ? __builtin_amdgcn_readfirstlane(K.kdesc[static_cast<int64_t>(u) * nksK + ks]) : 0u;
-        const _Float16 *qh = reinterpret_cast<const _Float16 *>(ksb), *ql = qh + K.kfetch;
-        const int r0 = tid, r1 = tid + 256;
-        const uint32_t *row0 = rows + r0 * kp, *row1 = rows + r1 * kp;
-        float acc0 = 0.f, acc1 = 0.f;
+    for (int i = 0; i < KW; ++i)
 #pragma unroll
-        for (int ks = 0; ks < kAttKsK; ++ks) {
-            if (((kd[ks] >> 16) & 0xFu) == 0u) continue;               // empty k-step (uniform)
-#pragma unroll
-            for (uint32_t hk = 0; hk < 2; ++hk) {
-                const half8 h8 = *reinterpret_cast<const half8 *>(qh + ks * 16 + hk * 8);
-                const half8 l8 = *reinterpret_cast<const half8 *>(ql + ks * 16 + hk * 8);
-                const half8 c0 = decode_kstep<false>(kd[ks], row0, nullptr, hk);
-                const half8 c1 = decode_kstep<false>(kd[ks], row1, nullptr, hk);
-#pragma unroll
-                for (int e = 0; e < 8; e += 2) {
-                    const half2 hv = {h8[e], h8[e + 1]}, lv = {l8[e], l8[e + 1]};
-                    const half2 v0 = {c0[e], c0[e + 1]}, v1 = {c1[e], c1[e + 1]};
-                    acc0 = __builtin_amdgcn_fdot2(v0, hv, acc0, false);
-                    acc0 = __builtin_amdgcn_fdot2(v0, lv, acc0, false);
-                    acc1 = __builtin_amdgcn_fdot2(v1, hv, acc1, false);
-                    acc1 = __builtin_amdgcn_fdot2(v1, lv, acc1, false);
-                }
-            }
+        for (int rr = 0; rr < 4; ++rr) acc[i][rr] = i32x4{0, 0, 0, 0};
+    int dsum = 0;                                     // sum over this lane's quads of digit n of P
+    for (int st = 0; st < 2 * nsub; ++st) {
+        const uint32_t *cur = ((st & 1) ? buf1 : buf0) + dcur;
+        uint32_t *nxt = (st & 1) ? buf0 : buf1;
+        const bool more = st + 1 < 2 * nsub;
+        SubSrc gn{};
+        if (more) {
+            gn = step_src(st + 1);
+            sub_load(gn, stg);
         }
-        const float beta = qt_l[K.kslots], mul = a.qmul[u];
-        acc0 = fmaf(acc0, mul, beta);
-        acc1 = fmaf(acc1, mul, beta);
-        if (r0 < nrows) {
-            pl[r0] = acc0;
-            mloc = acc0;
-        }
-        if (r1 < nrows) {
-            pl[r1] = acc1;
-            mloc = fmaxf(mloc, acc1);
-        }
-    }
-    const float M = block_reduce(mloc, red, true);     // (its barriers also end the score phase)
-    float lsum = 0.f;
-    for (int r = tid; r < nrows; r += blockDim.x) {
-        const float p = expf(pl[r] - M);
-        pl[r] = p;
-        lsum += p;
-    }
-    stage_rows(vsrc, vtot, V.row_words, vp, rows, vr);   // the key rows are no longer read
-    const float L = block_reduce(lsum, red, false);
-    __syncthreads();
-
-    // p-weighted sums of the value codes in the fetch order: wave w takes the
-    // 32-row tiles w, w + 4, ... of the chunk (lane: row lane & 31, half k-step
-    // lane >> 5) and decodes each of its k-steps' 8 codes as exact fp16 values
-    // (the fetch kernel's field decode); each code is accumulated as
-    // c * (p_hi + p_lo) in fp32 with one v_dot2, p * 2^12 split into two fp16
-    // parts (together within 2^-22 of p; the 2^12 keeps them normal).  The
-    // rows' sums are then added across the 32 row lanes, and the fetch columns
-    // mapped back to slots.  Up to kAttPass k-steps per pass over the rows.
-    __syncthreads();                                   // the reductions' scratch is reused below
-    {
-        for (int j = lane; j < kMaxSlots; j += 64) red[wave * kMaxSlots + j] = 0.f;   // this wave's sums only
-        const int nksV = V.kfetch / 16;
-        const uint32_t half_k = lane >> 5;
-        const int tok = lane & 31;
-        const int ntiles = (nrows + 31) >> 5;
-        const int32_t *fs = V.fslot + static_cast<int64_t>(u) * V.kfetch;
-        for (int k0 = 0; k0 < nksV; k0 += kAttPass) {
-            uint32_t kd[kAttPass];
+        if (st < nsub) {
+            // scores (32x32x32 products, D[d][row] = sum_k A[d][k] B[k][row]): A
+            // holds the query's digits (row d = digit d, rows 4-31 zero), B a
+            // tile's codes; lane l supplies row or column l & 31 over k-range
+            // 16(l >> 5), lanes 0-31 the pair's first k-step, lanes 32-63 its
+            // second.  Wave w takes tile w of the sub-chunk; lane l (< 32) ends
+            // with the four digit sums of the tile's row l.
+            const int j0 = st * sub, rows_j = min(sub, nrows - j0);
+            if (wave * 32 < sub) {
+                const uint32_t *row0 = cur + (wave * 32 + static_cast<int>(lane & 31)) * K.row_words;
+                i32x16 a0;
 #pragma unroll
-            for (int q = 0; q < kAttPass; ++q)
-                kd[q] = k0 + q < nksV ? __builtin_amdgcn_readfirstlane(V.kdesc[static_cast<int64_t>(u) * nksV + k0 + q])
-                                      : 0u;
-            float acc[kAttPass][8];
-#pragma unroll
-            for (int q = 0; q < kAttPass; ++q)
-#pragma unroll
-                for (int i = 0; i < 8; ++i) acc[q][i] = 0.f;
-            for (int t = wave; t < ntiles; t += 4) {
-                const int r = t * 32 + tok;
-                const float ps = r < nrows ? pl[r] * 4096.0f : 0.0f;
-                const _Float16 ph = static_cast<_Float16>(ps);
-                const half2 pw = {ph, static_cast<_Float16>(ps - static_cast<float>(ph))};
-                const uint32_t *row = rows + r * vp;
-#pragma unroll
-                for (int q = 0; q < kAttPass; ++q) {
-                    if (((kd[q] >> 16) & 0xFu) == 0u) continue;            // empty or past the end (uniform)
-                    const half8 cv = decode_kstep<false>(kd[q], row, nullptr, half_k);
-#pragma unroll
-                    for (int i = 0; i < 8; ++i) {
-                        const half2 cc = {cv[i], cv[i]};
-                        acc[q][i] = __builtin_amdgcn_fdot2(cc, pw, acc[q][i], false);
+                for (int i = 0; i < 16; ++i) a0[i] = 0;
+                // a lane without a k-step decodes its product's other one: its
+                // operand A is zero, so those products vanish
+                auto product = [&](uint32_t wid, uint32_t off, uint32_t addr) __attribute__((always_inline)) {
+                    const u32x4 qv = qal[addr];
+                    uint32_t R[4];
+                    switch (wid) {
+                        case 2: kstep_bytes_w<2>(off, row0, R); break;
+                        case 4: kstep_bytes_w<4>(off, row0, R); break;
+                        case 8: kstep_bytes_w<8>(off, row0, R); break;
+                        case 1: kstep_bytes_w<1>(off, row0, R); break;
+                        default: kstep_bytes_w<3>(off, row0, R); break;
                     }
+                    a0 = __builtin_amdgcn_mfma_i32_32x32x32_i8(__builtin_bit_cast(i32x4, qv),
+                                                               __builtin_bit_cast(i32x4, u32x4{R[0], R[1], R[2], R[3]}),
+                                                               a0, 0, 0, 0);
+                };
+#pragma unroll
+                for (int m = 0; m < kAttPairs; ++m)
+                    if (m < npairs) product(pwid[m], poff[m], paddr[m]);
+                for (int m = kAttPairs; m < npairs; ++m) {
+                    uint32_t wid, off, addr;
+                    pair_lane(m, wid, off, addr);
+                    product(wid, off, addr);
+                }
+                const int r0 = wave * 32 + static_cast<int>(lane);
+                if (lane < 32 && r0 < rows_j) {
+                    const float T = fmaf(static_cast<float>(a0[3]), 16777216.0f,
+                                         fmaf(static_cast<float>(a0[2]), 65536.0f,
+                                              fmaf(static_cast<float>(a0[1]), 256.0f, static_cast<float>(a0[0]))));
+                    const float sc = fmaf(T, mul, beta);
+                    pl[j0 + r0] = sc;
+                    mloc = fmaxf(mloc, sc);
                 }
             }
-            // sums over the 32 row lanes of each half (in its lanes 16-31), then
-            // into this wave's slot sums (each slot has one fetch column;
-            // padding columns none)
+        } else {
+            if (st == nsub) {
+                // every score is in: the weights p = exp(s - M), their sum, and
+                // their digit words (P = rint(p * 2^30) <= 2^30 as four balanced
+                // int8 digits) in place of the scores
+                M = block_reduce(mloc, red, true);
+                float lsum = 0.f;
+                for (int r = tid; r < nrows; r += blockDim.x) {
+                    const float p = expf(pl[r] - M);
+                    lsum += p;
+                    const uint32_t P = static_cast<uint32_t>(rintf(p * 1073741824.0f));
+                    pw[r] = (P + 0x808080u) ^ 0x808080u;
+                }
+                L = block_reduce(lsum, red, false);   // (its barriers publish the digit words)
+            }
+            // p-weighted sums of the value codes on 4x4x4 products (16 blocks of
+            // 4 lanes, D[d][col] = sum_k A[d][k] B[k][col]): lane l holds row l of
+            // each 64-row group (quad q: rows 4q..4q+3); A is the quad's digits of
+            // P, B its codes of fetch columns 4r + n (lane n, register r), both
+            // from the lanes' own rows by a byte transpose across the quad.  Wave
+            // w takes the k-steps w + kAttWaves i over every row.  Sums are exact in int32
+            // (|digit|, |code| <= 128, at most 9216 rows).
+            const int j0 = (st - nsub) * sub, rows_j = min(sub, nrows - j0);
+            const int ng = (rows_j + 63) >> 6;
+            uint32_t Ag[4];
 #pragma unroll
-            for (int q = 0; q < kAttPass; ++q)
+            for (int g = 0; g < 4; ++g) {
+                Ag[g] = 0u;
+                if (g < ng) {
+                    const int rl = g * 64 + static_cast<int>(lane);
+                    Ag[g] = quad_transpose(rl < rows_j ? pw[j0 + rl] : 0u, s1, s2);
+                    dsum = __builtin_amdgcn_sdot4(static_cast<int>(Ag[g]), 0x01010101, dsum, false);
+                }
+            }
+            // rows past the chunk have zero A; a group's rows stay inside the buffer
+            const uint32_t *vrow0 = cur + static_cast<int>(lane) * V.row_words;
 #pragma unroll
-                for (int i = 0; i < 8; ++i) acc[q][i] = half_wave_sum(acc[q][i]);
-            if (tok == 16) {
-#pragma unroll
-                for (int q = 0; q < kAttPass; ++q) {
-                    if (k0 + q >= nksV) break;
-#pragma unroll
-                    for (int i = 0; i < 8; ++i) {
-                        const int j = fs[(k0 + q) * 16 + half_k * 8 + i];
-                        if (j >= 0) red[wave * kMaxSlots + j] = acc[q][i] * 0x1p-12f;
-                    }
+            for (int i = 0; i < KW; ++i) {
+                switch (vw[i]) {
+                    case 2: value_kstep<2>(acc[i], voff[i], vrow0, V.row_words, ng, Ag, s1, s2); break;
+                    case 4: value_kstep<4>(acc[i], voff[i], vrow0, V.row_words, ng, Ag, s1, s2); break;
+                    case 8: value_kstep<8>(acc[i], voff[i], vrow0, V.row_words, ng, Ag, s1, s2); break;
+                    case 1: value_kstep<1>(acc[i], voff[i], vrow0, V.row_words, ng, Ag, s1, s2); break;
+                    case 3: value_kstep<3>(acc[i], voff[i], vrow0, V.row_words, ng, Ag, s1, s2); break;
+                    default: break;                            // no such k-step
                 }
             }
         }
+        if (more) {
+            sub_store(gn, nxt, stg);
+            dcur = gn.delta;
+        }
+        __syncthreads();
     }
-    __syncthreads();
+    if (nsub == 0) {                                   // (an empty segment: never launched)
+        M = -__builtin_huge_valf();
+    }
+
+    // totals over the 16 quads: rotations by 4 and 8 lanes inside each row of 16,
+    // then the row pairs and halves swapped in (lane n of every quad ends with
+    // its column's sums)
+    auto quad_total = [](int v) __attribute__((always_inline)) {
+        v += __builtin_amdgcn_update_dpp(0, v, 0x124, 0xF, 0xF, false);   // row_ror:4
+        v += __builtin_amdgcn_update_dpp(0, v, 0x128, 0xF, 0xF, false);   // row_ror:8
+        const auto p16 = __builtin_amdgcn_permlane16_swap(v, v, false, false);
+        v = static_cast<int>(p16[0]) + static_cast<int>(p16[1]);
+        const auto p32 = __builtin_amdgcn_permlane32_swap(v, v, false, false);
+        return static_cast<int>(p32[0]) + static_cast<int>(p32[1]);
+    };
+#pragma unroll
+    for (int i = 0; i < KW; ++i) {
+        if (vw[i] == 0u) continue;
+#pragma unroll
+        for (int rr = 0; rr < 4; ++rr)
+#pragma unroll
+            for (int dd = 0; dd < 4; ++dd) acc[i][rr][dd] = quad_total(acc[i][rr][dd]);
+    }
+    // sum P = sum_n 256^n (sum of digit n), digit n's sum held by lane n of each quad
+    const int dt = quad_total(dsum);
+    const double sp = static_cast<double>(__builtin_amdgcn_update_dpp(0, dt, 0x00, 0xF, 0xF, false)) +
+                      256.0 * static_cast<double>(__builtin_amdgcn_update_dpp(0, dt, 0x55, 0xF, 0xF, false)) +
+                      65536.0 * static_cast<double>(__builtin_amdgcn_update_dpp(0, dt, 0xAA, 0xF, 0xF, false)) +
+                      16777216.0 * static_cast<double>(__builtin_amdgcn_update_dpp(0, dt, 0xFF, 0xF, 0xF, false));
+    // abar of fetch column 16 ks + 4r + n = 2^-30 (sum_d 256^d acc_d), plus
+    // 128 * sum P for 8-bit columns (read as c - 128); lanes 0-3 write
     float *dst = a.part + (static_cast<int64_t>(u) * a.nchunks + c) * (V.kslots + 2);
-    for (int j = tid; j < V.kslots; j += blockDim.x)
-        dst[j] = (red[j] + red[kMaxSlots + j]) + (red[2 * kMaxSlots + j] + red[3 * kMaxSlots + j]);
+    if (lane < 4) {
+#pragma unroll
+        for (int i = 0; i < KW; ++i) {
+            if (vw[i] == 0u) continue;
+            const double corr = vw[i] == 8u ? 128.0 * sp : 0.0;
+#pragma unroll
+            for (int rr = 0; rr < 4; ++rr) {
+                const int j = fsv[i][rr];
+                if (j < 0) continue;
+                const i32x4 v = acc[i][rr];
+                const double T = ((static_cast<double>(v[3]) * 256.0 + v[2]) * 256.0 + v[1]) * 256.0 + v[0];
+                dst[j] = static_cast<float>((T + corr) * 0x1p-30);
+            }
+        }
+    }
     if (tid == 0) {
         dst[V.kslots] = M;
         dst[V.kslots + 1] = L;
@@ -435,18 +695,53 @@ AttendSide attend_side(const kvtc_state_header *h, const void *state_dev, const 
 }
 
 // Workspace regions, each 256-byte aligned: qt [U][kslots_k + 1] f32,
-// qf [U][2][kfetch_k] f16, qmul [U] f32, partial sums [U][nchunks][kslots_v + 2] f32.
+// qa [U][kfetch_k / 16][4][16] int8, qmul [U] f32, pairs [U][1 + 2 kAttKsK] u32,
+// partial sums [U][segments][kslots_v + 2] f32.
 struct AttendWork {
-    uint64_t qt, qf, qmul, part, total;
+    uint64_t qt, qa, qmul, pairs, part, total;
 };
+
+// Segments of the rows [0, s_end) for the partial blocks: at most kAttSegMax
+// rows each, and as many as fill kAttBlocks blocks over the units without
+// going below kAttSeg rows (a short cache gets fewer).  Every segment holds at
+// least one row.
+struct AttendSegs {
+    int64_t count;
+    int rows, sub;
+};
+
+AttendSegs attend_segs(const kvtc_state_header *hk, const kvtc_state_header *hv, int64_t s_end) {
+    AttendSegs g{};
+    // sub-chunks of 256, 128 or 64 rows whose 16-byte window fits the staged
+    // chunks (rows of up to 256 bytes fit at 64)
+    const int rs = std::max(hk->row_stride, hv->row_stride);
+    g.sub = 256;
+    while (g.sub > 64 && g.sub * rs + 16 > 16 * kAttThreads * kAttStage) g.sub >>= 1;
+    if (s_end <= 0) return g;
+    const int64_t units = std::max<int64_t>(1, hk->units);
+    const int64_t fill = std::min<int64_t>((kAttBlocks + units - 1) / units, (s_end + kAttSeg - 1) / kAttSeg);
+    const int64_t n0 = std::max<int64_t>({1, (s_end + kAttSegMax - 1) / kAttSegMax, fill});
+    g.rows = static_cast<int>((s_end + n0 - 1) / n0);
+    g.count = (s_end + g.rows - 1) / g.rows;
+    return g;
+}
+
+// LDS of a partial block: scorer operands, reductions, the segment's scores,
+// two sub-chunk buffers at the wider of the two odd pitches, eight slack words each.
+size_t attend_partial_lds(const AttendSegs &g, int k_row_words, int v_row_words) {
+    const size_t bw = (static_cast<size_t>(g.sub) * std::max(k_row_words, v_row_words) + 16 + 3) & ~static_cast<size_t>(3);
+    return (kAttKsK * 4 + 1) * sizeof(u32x4) + kAttWaves * sizeof(float) + static_cast<size_t>((g.rows + 3) & ~3) * sizeof(float) +
+           2 * bw * sizeof(uint32_t);
+}
 
 AttendWork attend_work(const kvtc_state_header *hk, const kvtc_state_header *hv, int64_t s_end) {
     AttendWork w{};
-    const int64_t nchunks = (s_end + kAttChunk - 1) / kAttChunk;
+    const int64_t nchunks = attend_segs(hk, hv, s_end).count;
     w.qt = 0;
-    w.qf = align_up(static_cast<uint64_t>(hk->units) * (hk->kslots + 1) * sizeof(float), 256);
-    w.qmul = w.qf + align_up(static_cast<uint64_t>(hk->units) * 2 * hk->kfetch * sizeof(uint16_t), 256);
-    w.part = w.qmul + align_up(static_cast<uint64_t>(hk->units) * sizeof(float), 256);
+    w.qa = align_up(static_cast<uint64_t>(hk->units) * (hk->kslots + 1) * sizeof(float), 256);
+    w.qmul = w.qa + align_up(static_cast<uint64_t>(hk->units) * 4 * hk->kfetch, 256);
+    w.pairs = w.qmul + align_up(static_cast<uint64_t>(hk->units) * sizeof(float), 256);
+    w.part = w.pairs + align_up(static_cast<uint64_t>(hk->units) * (1 + 2 * kAttKsK) * sizeof(uint32_t), 256);
     w.total = w.part + static_cast<uint64_t>(hv->units) * nchunks * (hv->kslots + 2) * sizeof(float);
     return w;
 }
@@ -1032,7 +1327,8 @@ int32_t attend_impl(const kvtc_tensor_ref *k, const kvtc_tensor_ref *v, int64_t 
         work_bytes = kAttendScratchBytes;
     }
     if (!work_dev || work_bytes < need || reinterpret_cast<uintptr_t>(work_dev) % 256) return KVTC_E_BUFSIZE;
-    const int64_t nchunks = (s_end + kAttChunk - 1) / kAttChunk;
+    const AttendSegs segs = attend_segs(hk, hv, s_end);
+    const int64_t nchunks = segs.count;
     if (hk->units > 0x7FFFFFFF || nchunks > 0x7FFFFFFF || hk->units > 65535) return KVTC_E_SHAPE;
     if (!route.fast)
         return launch_gen(k, v, hk, hv, route, q_dev, q_dtype, q_strides, s_end, out_dev, out_strides, work_dev, stream);
@@ -1049,27 +1345,30 @@ int32_t attend_impl(const kvtc_tensor_ref *k, const kvtc_tensor_ref *v, int64_t 
     a.osh = out_strides[1];
     a.s_end = s_end;
     a.nchunks = static_cast<int>(nchunks);
-    // rows shared evenly between the chunks (no nearly empty last chunk)
-    a.chunk_rows = nchunks > 0 ? static_cast<int>((s_end + nchunks - 1) / nchunks) : 0;
+    a.chunk_rows = segs.rows;
+    a.sub = segs.sub;
     a.H = static_cast<int>(hk->heads);
     a.D = hk->head_dim;
     a.inv_sqrt_d = 1.0f / sqrtf(static_cast<float>(hk->head_dim));
     const AttendWork wl = attend_work(hk, hv, s_end);
     char *wb = static_cast<char *>(work_dev);
     a.qt = reinterpret_cast<float *>(wb + wl.qt);
-    a.qf = reinterpret_cast<uint16_t *>(wb + wl.qf);
+    a.qa = reinterpret_cast<uint8_t *>(wb + wl.qa);
     a.qmul = reinterpret_cast<float *>(wb + wl.qmul);
+    a.pairs = reinterpret_cast<uint32_t *>(wb + wl.pairs);
     a.part = reinterpret_cast<float *>(wb + wl.part);
     const unsigned U = static_cast<unsigned>(hk->units);
     hipLaunchKernelGGL(attend_prep_kernel, dim3(U), dim3(256), 0, stream, a);
     if (launch_status() != KVTC_OK) return KVTC_E_DEVICE;
     if (nchunks > 0) {
-        const int rw = std::max(a.k.row_words, a.v.row_words);
-        const size_t lds = (kMaxSlots + 4 + 2 * kMaxSlots + kAttChunk + 4 * kMaxSlots) * sizeof(float) +
-                           (static_cast<size_t>(kAttChunk) * ((rw + 1) | 1) + 8) * sizeof(uint32_t);
+        const size_t lds = attend_partial_lds(segs, a.k.row_words, a.v.row_words);
         if (lds > kLdsMax) return KVTC_E_SHAPE;
-        if (!allow_lds(reinterpret_cast<const void *>(attend_partial_kernel))) return KVTC_E_DEVICE;
-        hipLaunchKernelGGL(attend_partial_kernel, dim3(static_cast<unsigned>(nchunks), U), dim3(256), lds, stream, a);
+        // value k-steps per wave (at most 16 k-steps over kAttWaves waves): 16
+        // accumulator registers each
+        const int kw = (a.v.kfetch / 16 + kAttWaves - 1) / kAttWaves;
+        auto kern = kw <= 1 ? attend_partial_kernel<1> : attend_partial_kernel<2>;
+        if (!allow_lds(reinterpret_cast<const void *>(kern))) return KVTC_E_DEVICE;
+        hipLaunchKernelGGL(kern, dim3(static_cast<unsigned>(nchunks), U), dim3(kAttThreads), lds, stream, a);
         if (launch_status() != KVTC_OK) return KVTC_E_DEVICE;
     }
     hipLaunchKernelGGL(attend_merge_kernel, dim3(U), dim3(256), 0, stream, a);

@@ -425,10 +425,11 @@ def test_attend_validates_before_launch():
     need = K.kvtc_attend_workspace(blob, blob, 100)
     U, ks, kf = st.U, K.header(blob).kslots, K.header(blob).kfetch
     up = lambda n: -(-n // 256) * 256
-    # regions: qt [U][ks+1] f32, fetch-order fp16 high/low coefficients [U][2][kf],
-    # the 2^e prescale [U] f32 (each 256-byte aligned), then one 512-row chunk of
-    # partial sums [U][1][ks + 2] f32 for 100 rows
-    assert need == up(U * (ks + 1) * 4) + up(U * 2 * kf * 2) + up(U * 4) + U * 1 * (ks + 2) * 4
+    # regions: qt [U][ks+1] f32, fetch-order int8 digit operands [U][kf/16][4][16],
+    # the 2^(e-30) prescale [U] f32, the scorer's k-step pairs [U][1 + 2*16] u32
+    # (each 256-byte aligned), then one segment of partial sums [U][1][ks + 2] f32
+    # for 100 rows (segments are at least 256 rows unless the cache is shorter)
+    assert need == up(U * (ks + 1) * 4) + up(U * 4 * kf) + up(U * 4) + up(U * 33 * 4) + U * 1 * (ks + 2) * 4
     fake = 0x1000
 
     def ref(b, capacity=100):
@@ -593,7 +594,7 @@ def test_attend_noalloc_rejects_a_call_beyond_its_scratch():
     st = O.fit(oracle_cfg(w), synth.generate(w, 0, 0, 256))
     blob = blob_from_oracle(st)
     fake = C.c_void_p(0x1000)        # never dereferenced: the size check fails first
-    big = 1 << 24                    # rows: partial sums of 2**15 chunks per unit
+    big = 1 << 29                    # rows: partial sums of 58255 segments (9216 rows) per unit
     assert K.kvtc_attend_workspace(blob, blob, big) > 16 << 20
     refs = []
     for _ in range(2):
