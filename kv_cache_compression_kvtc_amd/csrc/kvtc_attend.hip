@@ -163,21 +163,19 @@ __device__ __forceinline__ void kstep_bytes_quad_w(uint32_t off, const uint32_t 
     }
 }
 
-// One k-step's p-weighted sums over the sub-chunk's groups of 64 rows (at most
-// four; group g's digits of P in Ag[g], its rows at row0 + g * 64 * row_words).
-template <int W>
+// One k-step's p-weighted sums over the sub-chunk's G groups of 64 rows (group
+// g's digits of P in Ag[g], zero for rows past the chunk; its rows at
+// row0 + g * 64 * row_words).
+template <int W, int G>
 __device__ __forceinline__ void value_kstep(i32x4 (&acc)[4], uint32_t off, const uint32_t *row0, int row_words,
-                                            int ng, const uint32_t (&Ag)[4], uint32_t s1, uint32_t s2) {
+                                            const uint32_t (&Ag)[G], uint32_t s1, uint32_t s2) {
 #pragma unroll
-    for (int g = 0; g < 4; ++g) {
-        if (g < ng) {
-            uint32_t B[4];
-            kstep_bytes_quad_w<W>(off, row0 + g * 64 * row_words, s1, s2, B);
+    for (int g = 0; g < G; ++g) {
+        uint32_t B[4];
+        kstep_bytes_quad_w<W>(off, row0 + g * 64 * row_words, s1, s2, B);
 #pragma unroll
-            for (int rr = 0; rr < 4; ++rr)
-                acc[rr] = __builtin_amdgcn_mfma_i32_4x4x4i8(static_cast<int>(Ag[g]), static_cast<int>(B[rr]), acc[rr], 0,
-                                                            0, 0);
-        }
+        for (int rr = 0; rr < 4; ++rr)
+            acc[rr] = __builtin_amdgcn_mfma_i32_4x4x4i8(static_cast<int>(Ag[g]), static_cast<int>(B[rr]), acc[rr], 0, 0, 0);
     }
 }
 
@@ -367,7 +365,7 @@ __global__ __launch_bounds__(256) void attend_prep_kernel(AttendArgs a) {
 // the last row for its k-step windows): while one buffer is decoded, the next
 // sub-chunk's chunks are in flight in registers.  The
 // segment's scores stay in LDS, turned into weights once the keys are done.
-template <int KW>
+template <int KW, int G>
 __global__ __launch_bounds__(kAttThreads) void attend_partial_kernel(AttendArgs a) {
     extern __shared__ __align__(16) unsigned char smem[];
     const int c = blockIdx.x, u = blockIdx.y, tid = threadIdx.x;
@@ -385,12 +383,13 @@ __global__ __launch_bounds__(kAttThreads) void attend_partial_kernel(AttendArgs 
     const int nrows = static_cast<int>(min<int64_t>(a.chunk_rows, a.s_end - s0));
     const int nsub = (nrows + sub - 1) / sub;
     // step j < nsub stages key sub-chunk j, step nsub + j value sub-chunk j
+    const uint8_t *kfirst = K.codes + (static_cast<int64_t>(u) * K.capacity + s0) * K.row_words * 4;
+    const uint8_t *vfirst = V.codes + (static_cast<int64_t>(u) * V.capacity + s0) * V.row_words * 4;
     auto step_src = [&](int st) __attribute__((always_inline)) {
         const bool key = st < nsub;
         const int j = key ? st : st - nsub;
-        const AttendSide &T = key ? K : V;
-        return sub_src(T.codes, static_cast<int64_t>(u) * T.capacity + s0 + static_cast<int64_t>(j) * sub,
-                       min(sub, nrows - j * sub), T.row_words * 4);
+        const int rs = (key ? K.row_words : V.row_words) * 4;
+        return sub_src(key ? kfirst : vfirst, static_cast<int64_t>(j) * sub, min(sub, nrows - j * sub), rs);
     };
 
     u32x4 stg[kAttStage];
@@ -531,28 +530,25 @@ __global__ __launch_bounds__(kAttThreads) void attend_partial_kernel(AttendArgs 
             // from the lanes' own rows by a byte transpose across the quad.  Wave
             // w takes the k-steps w + kAttWaves i over every row.  Sums are exact in int32
             // (|digit|, |code| <= 128, at most 9216 rows).
+            // the sub-chunk's G = sub / 64 groups, rows past the chunk with zero
+            // A (their codes are stale words inside the buffer)
             const int j0 = (st - nsub) * sub, rows_j = min(sub, nrows - j0);
-            const int ng = (rows_j + 63) >> 6;
-            uint32_t Ag[4];
+            uint32_t Ag[G];
 #pragma unroll
-            for (int g = 0; g < 4; ++g) {
-                Ag[g] = 0u;
-                if (g < ng) {
-                    const int rl = g * 64 + static_cast<int>(lane);
-                    Ag[g] = quad_transpose(rl < rows_j ? pw[j0 + rl] : 0u, s1, s2);
-                    dsum = __builtin_amdgcn_sdot4(static_cast<int>(Ag[g]), 0x01010101, dsum, false);
-                }
+            for (int g = 0; g < G; ++g) {
+                const int rl = g * 64 + static_cast<int>(lane);
+                Ag[g] = quad_transpose(rl < rows_j ? pw[j0 + rl] : 0u, s1, s2);
+                dsum = __builtin_amdgcn_sdot4(static_cast<int>(Ag[g]), 0x01010101, dsum, false);
             }
-            // rows past the chunk have zero A; a group's rows stay inside the buffer
             const uint32_t *vrow0 = cur + static_cast<int>(lane) * V.row_words;
 #pragma unroll
             for (int i = 0; i < KW; ++i) {
                 switch (vw[i]) {
-                    case 2: value_kstep<2>(acc[i], voff[i], vrow0, V.row_words, ng, Ag, s1, s2); break;
-                    case 4: value_kstep<4>(acc[i], voff[i], vrow0, V.row_words, ng, Ag, s1, s2); break;
-                    case 8: value_kstep<8>(acc[i], voff[i], vrow0, V.row_words, ng, Ag, s1, s2); break;
-                    case 1: value_kstep<1>(acc[i], voff[i], vrow0, V.row_words, ng, Ag, s1, s2); break;
-                    case 3: value_kstep<3>(acc[i], voff[i], vrow0, V.row_words, ng, Ag, s1, s2); break;
+                    case 2: value_kstep<2, G>(acc[i], voff[i], vrow0, V.row_words, Ag, s1, s2); break;
+                    case 4: value_kstep<4, G>(acc[i], voff[i], vrow0, V.row_words, Ag, s1, s2); break;
+                    case 8: value_kstep<8, G>(acc[i], voff[i], vrow0, V.row_words, Ag, s1, s2); break;
+                    case 1: value_kstep<1, G>(acc[i], voff[i], vrow0, V.row_words, Ag, s1, s2); break;
+                    case 3: value_kstep<3, G>(acc[i], voff[i], vrow0, V.row_words, Ag, s1, s2); break;
                     default: break;                            // no such k-step
                 }
             }
@@ -1366,7 +1362,10 @@ int32_t attend_impl(const kvtc_tensor_ref *k, const kvtc_tensor_ref *v, int64_t 
         // value k-steps per wave (at most 16 k-steps over kAttWaves waves): 16
         // accumulator registers each
         const int kw = (a.v.kfetch / 16 + kAttWaves - 1) / kAttWaves;
-        auto kern = kw <= 1 ? attend_partial_kernel<1> : attend_partial_kernel<2>;
+        auto pick = [&](auto k1, auto k2) { return kw <= 1 ? k1 : k2; };
+        auto kern = a.sub == 256   ? pick(attend_partial_kernel<1, 4>, attend_partial_kernel<2, 4>)
+                    : a.sub == 128 ? pick(attend_partial_kernel<1, 2>, attend_partial_kernel<2, 2>)
+                                   : pick(attend_partial_kernel<1, 1>, attend_partial_kernel<2, 1>);
         if (!allow_lds(reinterpret_cast<const void *>(kern))) return KVTC_E_DEVICE;
         hipLaunchKernelGGL(kern, dim3(static_cast<unsigned>(nchunks), U), dim3(kAttThreads), lds, stream, a);
         if (launch_status() != KVTC_OK) return KVTC_E_DEVICE;
