@@ -51,11 +51,7 @@ struct AttendArgs {
     int nchunks, chunk_rows, H, D;     // segments of chunk_rows rows (the last one shorter), <= kAttSegMax
     int sub;                           // rows per staged sub-chunk: 64, 128 or 256 (the window fits the staging)
     float inv_sqrt_d;
-    float *qt;          // [U][k.kslots + 1]: qt_j, then the scorer's offset
-    uint8_t *qa;        // [U][k.kfetch / 16][4][16]: int8 digits of Q (scorer operands, fetch order)
-    float *qmul;        // [U]: 2^(e - 30), the weight of one unit of Q
-    uint32_t *pairs;    // [U][1 + 2 kAttKsK]: count, then per scorer product ksA | ksB << 8 | w << 16, offA | offB << 16
-    float *part;        // [U][nchunks][v.kslots + 2]: abar partial sums, then max, sum
+    float *part;        // [U][nchunks][v.kslots + 2]: abar partial sums, then max, sum (two or more segments)
 };
 
 typedef int i32x4 __attribute__((ext_vector_type(4)));
@@ -276,87 +272,6 @@ __device__ inline float block_reduce(float v, float *red, bool is_max) {
     return r;
 }
 
-// Per unit: the query's score coefficients qt_j and offset beta (fp32).
-__global__ __launch_bounds__(256) void attend_prep_kernel(AttendArgs a) {
-    __shared__ float ql[kMaxSlots];
-    __shared__ float mpart[kMaxSlots];
-    const int u = blockIdx.x, b = u / a.H, h = u % a.H, tid = threadIdx.x;
-    for (int d = tid; d < a.D; d += blockDim.x)
-        ql[d] = a.q_f16 ? static_cast<float>(static_cast<const _Float16 *>(a.q)[b * a.qsb + h * a.qsh + d])
-                        : static_cast<const float *>(a.q)[b * a.qsb + h * a.qsh + d];
-    __syncthreads();
-    const AttendSide &k = a.k;
-    const int ns = k.ui[u].n_slots;
-    float qt = 0.f, mp = 0.f;
-    if (tid < ns) {
-        const float *vrow = k.basis + (static_cast<int64_t>(u) * k.kslots + tid) * a.D;
-        float acc = 0.f;
-        for (int d = 0; d < a.D; ++d) acc = fmaf(ql[d], vrow[d], acc);
-        const int c = k.comp[static_cast<int64_t>(u) * k.kslots + tid];
-        qt = k.qscale[static_cast<int64_t>(u) * k.rmax + c] * acc * a.inv_sqrt_d;
-        mp = k.qmin[static_cast<int64_t>(u) * k.rmax + c] * acc;
-    }
-    __shared__ float qts[kMaxSlots];
-    __shared__ float red[4];
-    if (tid < k.kslots) {
-        a.qt[static_cast<int64_t>(u) * (k.kslots + 1) + tid] = qt;
-        mpart[tid] = mp;
-        qts[tid] = qt;
-    }
-    // the scorer's operands in fetch order: Q = rint(qt * 2^(30 - e)), with
-    // 2^e > max |qt| so that |Q| < 2^30, as four balanced int8 digits
-    // (Q = sum_d d_d 256^d; the bytes of (Q + 0x808080) ^ 0x808080), digit d of
-    // fetch column 16 ks + t at byte (4 ks + d) * 16 + t; padding columns are zero.
-    // The scorer reads 8-bit codes as c - 128; the missing 128 * sum Q over the
-    // 8-bit columns is added to the offset.
-    const float amax = block_reduce(fabsf(qt), red, true);
-    int e = 0;
-    if (amax > 0.f) frexpf(amax, &e);
-    const int nks = k.kfetch >> 4;
-    uint8_t *qa = a.qa + static_cast<int64_t>(u) * 4 * k.kfetch;
-    float q8 = 0.f;
-    for (int kk = tid; kk < k.kfetch; kk += blockDim.x) {
-        const int j = k.fslot[static_cast<int64_t>(u) * k.kfetch + kk];
-        const int ks = kk >> 4, t = kk & 15;
-        const int32_t Q = j >= 0 ? static_cast<int32_t>(rintf(ldexpf(qts[j], 30 - e))) : 0;
-        const uint32_t W = (static_cast<uint32_t>(Q) + 0x808080u) ^ 0x808080u;
-#pragma unroll
-        for (int d = 0; d < 4; ++d) qa[(ks * 4 + d) * 16 + t] = static_cast<uint8_t>(W >> (8 * d));
-        if (j >= 0 && ((k.kdesc[static_cast<int64_t>(u) * nks + ks] >> 16) & 0xFu) == 8u) q8 += static_cast<float>(Q);
-    }
-    const float c8 = block_reduce(q8, red, false);
-    // the scorer's products: consecutive k-steps of one width in pairs (lanes
-    // 0-31 take the first, lanes 32-63 the second, so a product decodes one width)
-    if (tid == 0) {
-        const uint32_t *kd = k.kdesc + static_cast<int64_t>(u) * nks;
-        uint32_t *pr = a.pairs + static_cast<int64_t>(u) * (1 + 2 * kAttKsK);
-        int np = 0;
-        for (int ks = 0; ks < nks;) {
-            const uint32_t w = (kd[ks] >> 16) & 0xFu;
-            if (w == 0u) {
-                ++ks;
-                continue;
-            }
-            const bool two = ks + 1 < nks && ((kd[ks + 1] >> 16) & 0xFu) == w;
-            const uint32_t kb = two ? static_cast<uint32_t>(ks + 1) : 0xFFu;
-            pr[1 + 2 * np] = static_cast<uint32_t>(ks) | (kb << 8) | (w << 16);
-            pr[2 + 2 * np] = (kd[ks] & 0xFFFFu) | (two ? (kd[ks + 1] & 0xFFFFu) << 16 : 0u);
-            ++np;
-            ks += two ? 2 : 1;
-        }
-        pr[0] = static_cast<uint32_t>(np);
-    }
-    // beta = (q . mu + sum_j min_j q . V_j) / sqrt(D), summed over the block
-    float bpart = 0.f;
-    for (int d = tid; d < a.D; d += blockDim.x) bpart = fmaf(ql[d], k.mu[static_cast<int64_t>(u) * a.D + d], bpart);
-    if (tid < k.kslots) bpart += mpart[tid];
-    const float beta = block_reduce(bpart, red, false);
-    if (tid == 0) {
-        a.qmul[u] = ldexpf(1.0f, e - 30);
-        a.qt[static_cast<int64_t>(u) * (k.kslots + 1) + k.kslots] = beta * a.inv_sqrt_d + ldexpf(128.0f * c8, e - 30);
-    }
-}
-
 // Per (segment of chunk_rows <= kAttSegMax rows, unit): scores from the key codes,
 // the segment's softmax max and sum, and the p-weighted sums of the value
 // codes, both contractions on int8 MFMA with exact int32 accumulation.  The
@@ -374,7 +289,12 @@ __global__ __launch_bounds__(kAttThreads) void attend_partial_kernel(AttendArgs 
     const AttendSide &K = a.k, &V = a.v;
     u32x4 *qal = reinterpret_cast<u32x4 *>(smem);                        // [kAttKsK][4] + 1 scorer operands
     float *red = reinterpret_cast<float *>(qal + kAttKsK * 4 + 1);      // [kAttWaves] block reductions
-    float *pl = red + kAttWaves;                                         // [chunk_rows] scores, then weights
+    float *ql = red + kAttWaves;                                         // [kMaxSlots] the query
+    float *qts = ql + kMaxSlots;                                         // [kMaxSlots] qt_j, then abar_j
+    float *mpt = qts + kMaxSlots;                                        // [kMaxSlots] min_j q.V_j
+    uint32_t *kds = reinterpret_cast<uint32_t *>(mpt + kMaxSlots);      // [kAttKsK] key k-step descriptors
+    uint32_t *ptab = kds + kAttKsK;                                      // [1 + 2 kAttKsK] scorer products
+    float *pl = reinterpret_cast<float *>(ptab + 1 + 2 * kAttKsK + 3);   // [chunk_rows] scores, then weights
     uint32_t *pw = reinterpret_cast<uint32_t *>(pl);                     //   as int8 digit words
     const int sub = a.sub, bw = (sub * max(K.row_words, V.row_words) + 16 + 3) & ~3;   // buffer words
     uint32_t *buf0 = reinterpret_cast<uint32_t *>(pl + ((a.chunk_rows + 3) & ~3));
@@ -395,18 +315,100 @@ __global__ __launch_bounds__(kAttThreads) void attend_partial_kernel(AttendArgs 
     u32x4 stg[kAttStage];
     SubSrc g0 = step_src(0);
     sub_load(g0, stg);
+    // ---- the query's scorer operands (while the first sub-chunk is in flight)
     const int nksK = K.kfetch >> 4;
-    if (tid < 4 * nksK) qal[tid] = reinterpret_cast<const u32x4 *>(a.qa + static_cast<int64_t>(u) * 4 * K.kfetch)[tid];
-    if (tid == 0) qal[kAttKsK * 4] = u32x4{0u, 0u, 0u, 0u};
+    float beta, mul;
+    {
+        const int b = u / a.H, h = u % a.H;
+        for (int d = tid; d < a.D; d += kAttThreads)
+            ql[d] = a.q_f16 ? static_cast<float>(static_cast<const _Float16 *>(a.q)[b * a.qsb + h * a.qsh + d])
+                            : static_cast<const float *>(a.q)[b * a.qsb + h * a.qsh + d];
+        if (tid < nksK) kds[tid] = K.kdesc[static_cast<int64_t>(u) * nksK + tid];
+        if (tid == 0) qal[kAttKsK * 4] = u32x4{0u, 0u, 0u, 0u};
+        __syncthreads();
+        // qt_j = scale_j (q . V_j) / sqrt(D), and min_j (q . V_j) for the offset
+        const int ns = K.ui[u].n_slots;
+        float qt = 0.f, mp = 0.f;
+        if (tid < ns) {
+            const float *vrow = K.basis + (static_cast<int64_t>(u) * K.kslots + tid) * a.D;
+            float acc0 = 0.f, acc1 = 0.f;
+            if ((a.D & 3) == 0 && (reinterpret_cast<uintptr_t>(K.basis) & 15u) == 0) {   // 16-byte rows
+                for (int d4 = 0; d4 < (a.D >> 2); ++d4) {
+                    const float4 v = reinterpret_cast<const float4 *>(vrow)[d4];
+                    acc0 = fmaf(ql[4 * d4], v.x, acc0);
+                    acc1 = fmaf(ql[4 * d4 + 1], v.y, acc1);
+                    acc0 = fmaf(ql[4 * d4 + 2], v.z, acc0);
+                    acc1 = fmaf(ql[4 * d4 + 3], v.w, acc1);
+                }
+            } else {
+                for (int d = 0; d < a.D; ++d) acc0 = fmaf(ql[d], vrow[d], acc0);
+            }
+            const float acc = acc0 + acc1;
+            const int cj = K.comp[static_cast<int64_t>(u) * K.kslots + tid];
+            qt = K.qscale[static_cast<int64_t>(u) * K.rmax + cj] * acc * a.inv_sqrt_d;
+            mp = K.qmin[static_cast<int64_t>(u) * K.rmax + cj] * acc;
+        }
+        if (tid < K.kslots) {
+            qts[tid] = qt;
+            mpt[tid] = mp;
+        }
+        // fetch column 16 ks + t: Q = rint(qt * 2^(30 - e)), 2^e > max |qt| so that
+        // |Q| < 2^30, as four balanced int8 digits (Q = sum_d d_d 256^d; the bytes
+        // of (Q + 0x808080) ^ 0x808080), digit d at byte (4 ks + d) * 16 + t;
+        // padding columns are zero.  The scorer reads 8-bit codes as c - 128; the
+        // missing 128 * sum Q over the 8-bit columns is added to the offset.
+        const float amax = block_reduce(fabsf(qt), red, true);
+        int e = 0;
+        if (amax > 0.f) frexpf(amax, &e);
+        float q8 = 0.f;
+        if (tid < K.kfetch) {
+            const int j = K.fslot[static_cast<int64_t>(u) * K.kfetch + tid];
+            const int ks = tid >> 4, t = tid & 15;
+            const int32_t Q = j >= 0 ? static_cast<int32_t>(rintf(ldexpf(qts[j], 30 - e))) : 0;
+            const uint32_t W = (static_cast<uint32_t>(Q) + 0x808080u) ^ 0x808080u;
+            uint8_t *qab = reinterpret_cast<uint8_t *>(qal);
+#pragma unroll
+            for (int d = 0; d < 4; ++d) qab[(ks * 4 + d) * 16 + t] = static_cast<uint8_t>(W >> (8 * d));
+            if (j >= 0 && ((kds[ks] >> 16) & 0xFu) == 8u) q8 = static_cast<float>(Q);
+        }
+        const float c8 = block_reduce(q8, red, false);
+        // (q . mu + sum_j min_j q . V_j) / sqrt(D)
+        float bpart = 0.f;
+        for (int d = tid; d < a.D; d += kAttThreads) bpart = fmaf(ql[d], K.mu[static_cast<int64_t>(u) * a.D + d], bpart);
+        if (tid < K.kslots) bpart += mpt[tid];
+        const float bsum = block_reduce(bpart, red, false);
+        beta = bsum * a.inv_sqrt_d + ldexpf(128.0f * c8, e - 30);
+        mul = ldexpf(1.0f, e - 30);
+        // the products: consecutive k-steps of one width in pairs (lanes 0-31 take
+        // the first, lanes 32-63 the second, so a product decodes one width)
+        if (tid == 0) {
+            int np = 0;
+            for (int ks = 0; ks < nksK;) {
+                const uint32_t w = (kds[ks] >> 16) & 0xFu;
+                if (w == 0u) {
+                    ++ks;
+                    continue;
+                }
+                const bool two = ks + 1 < nksK && ((kds[ks + 1] >> 16) & 0xFu) == w;
+                const uint32_t kb = two ? static_cast<uint32_t>(ks + 1) : 0xFFu;
+                ptab[1 + 2 * np] = static_cast<uint32_t>(ks) | (kb << 8) | (w << 16);
+                ptab[2 + 2 * np] = (kds[ks] & 0xFFFFu) | (two ? (kds[ks + 1] & 0xFFFFu) << 16 : 0u);
+                ++np;
+                ks += two ? 2 : 1;
+            }
+            ptab[0] = static_cast<uint32_t>(np);
+        }
+        __syncthreads();
+    }
     // the scorer's products (uniform widths), and per lane its k-step's offset
     // and the LDS address of its A operand (digit row d < 4 of the lane's
     // k-step; a zero vector for lanes 4-31 of a half and for a product's
     // missing second k-step)
-    const uint32_t *pr = a.pairs + static_cast<int64_t>(u) * (1 + 2 * kAttKsK);
-    const int npairs = static_cast<int>(pr[0]);
+    const int npairs = __builtin_amdgcn_readfirstlane(static_cast<int>(ptab[0]));
     // (the first kAttPairs products from registers, any others decoded per use)
     auto pair_lane = [&](int m, uint32_t &wid, uint32_t &off, uint32_t &addr) __attribute__((always_inline)) {
-        const uint32_t meta = pr[1 + 2 * m], offs = pr[2 + 2 * m];
+        const uint32_t meta = __builtin_amdgcn_readfirstlane(ptab[1 + 2 * m]);
+        const uint32_t offs = __builtin_amdgcn_readfirstlane(ptab[2 + 2 * m]);
         const bool hi = lane >= 32;
         const uint32_t ks = hi ? (meta >> 8) & 0xFFu : meta & 0xFFu;
         const bool ok = ks != 0xFFu;
@@ -422,7 +424,6 @@ __global__ __launch_bounds__(kAttThreads) void attend_partial_kernel(AttendArgs 
         paddr[m] = kAttKsK * 4;
         if (m < npairs) pair_lane(m, pwid[m], poff[m], paddr[m]);
     }
-    const float beta = a.qt[static_cast<int64_t>(u) * (K.kslots + 1) + K.kslots], mul = a.qmul[u];
     // this wave's value k-steps w + kAttWaves i: widths and offsets (uniform), and the
     // stored slots of the columns lane n of a quad sums (fetch columns 4r + n)
     const int nksV = V.kfetch >> 4;
@@ -589,8 +590,10 @@ __global__ __launch_bounds__(kAttThreads) void attend_partial_kernel(AttendArgs 
                       65536.0 * static_cast<double>(__builtin_amdgcn_update_dpp(0, dt, 0xAA, 0xF, 0xF, false)) +
                       16777216.0 * static_cast<double>(__builtin_amdgcn_update_dpp(0, dt, 0xFF, 0xF, 0xF, false));
     // abar of fetch column 16 ks + 4r + n = 2^-30 (sum_d 256^d acc_d), plus
-    // 128 * sum P for 8-bit columns (read as c - 128); lanes 0-3 write
-    float *dst = a.part + (static_cast<int64_t>(u) * a.nchunks + c) * (V.kslots + 2);
+    // 128 * sum P for 8-bit columns (read as c - 128); lanes 0-3 write, to the
+    // partial sums of a segment or (a single segment) to LDS for the output
+    const bool single = a.nchunks == 1;
+    float *dst = single ? qts : a.part + (static_cast<int64_t>(u) * a.nchunks + c) * (V.kslots + 2);
     if (lane < 4) {
 #pragma unroll
         for (int i = 0; i < KW; ++i) {
@@ -606,9 +609,28 @@ __global__ __launch_bounds__(kAttThreads) void attend_partial_kernel(AttendArgs 
             }
         }
     }
-    if (tid == 0) {
-        dst[V.kslots] = M;
-        dst[V.kslots + 1] = L;
+    if (!single) {
+        if (tid == 0) {
+            dst[V.kslots] = M;
+            dst[V.kslots + 1] = L;
+        }
+        return;
+    }
+    // a single segment: out = bias + sum_j (abar_j / L) scale_j V_j, rounded to fp16
+    // (the merge of one chunk, whose weight is 1)
+    __syncthreads();
+    const int nv = V.ui[u].n_slots;
+    if (tid < nv) {
+        const int cj = V.comp[static_cast<int64_t>(u) * V.kslots + tid];
+        mpt[tid] = qts[tid] / L * V.qscale[static_cast<int64_t>(u) * V.rmax + cj];
+    }
+    __syncthreads();
+    const int b = u / a.H, h = u % a.H;
+    for (int d = tid; d < a.D; d += kAttThreads) {
+        float o = V.bias[static_cast<int64_t>(u) * a.D + d];
+        const float *vb = V.basis + static_cast<int64_t>(u) * V.kslots * a.D + d;
+        for (int j = 0; j < nv; ++j) o = fmaf(mpt[j], vb[static_cast<int64_t>(j) * a.D], o);
+        a.out[b * a.osb + h * a.osh + d] = static_cast<_Float16>(o);
     }
 }
 
@@ -690,11 +712,10 @@ AttendSide attend_side(const kvtc_state_header *h, const void *state_dev, const 
     return sd_;
 }
 
-// Workspace regions, each 256-byte aligned: qt [U][kslots_k + 1] f32,
-// qa [U][kfetch_k / 16][4][16] int8, qmul [U] f32, pairs [U][1 + 2 kAttKsK] u32,
-// partial sums [U][segments][kslots_v + 2] f32.
+// Workspace: the partial sums [U][segments][kslots_v + 2] f32 when the rows
+// take two or more segments (one segment is finished in its block: none).
 struct AttendWork {
-    uint64_t qt, qa, qmul, pairs, part, total;
+    uint64_t part, total;
 };
 
 // Segments of the rows [0, s_end) for the partial blocks: at most kAttSegMax
@@ -722,23 +743,21 @@ AttendSegs attend_segs(const kvtc_state_header *hk, const kvtc_state_header *hv,
     return g;
 }
 
-// LDS of a partial block: scorer operands, reductions, the segment's scores,
-// two sub-chunk buffers at the wider of the two odd pitches, eight slack words each.
+// LDS of a partial block: scorer operands, reductions, the query's working
+// arrays and product table, the segment's scores, and two sub-chunk buffers
+// (the longer row times the sub-chunk plus sixteen slack words each).
 size_t attend_partial_lds(const AttendSegs &g, int k_row_words, int v_row_words) {
     const size_t bw = (static_cast<size_t>(g.sub) * std::max(k_row_words, v_row_words) + 16 + 3) & ~static_cast<size_t>(3);
-    return (kAttKsK * 4 + 1) * sizeof(u32x4) + kAttWaves * sizeof(float) + static_cast<size_t>((g.rows + 3) & ~3) * sizeof(float) +
+    return (kAttKsK * 4 + 1) * sizeof(u32x4) + (kAttWaves + 3 * kMaxSlots) * sizeof(float) +
+           (kAttKsK + 1 + 2 * kAttKsK + 3) * sizeof(uint32_t) + static_cast<size_t>((g.rows + 3) & ~3) * sizeof(float) +
            2 * bw * sizeof(uint32_t);
 }
 
 AttendWork attend_work(const kvtc_state_header *hk, const kvtc_state_header *hv, int64_t s_end) {
     AttendWork w{};
     const int64_t nchunks = attend_segs(hk, hv, s_end).count;
-    w.qt = 0;
-    w.qa = align_up(static_cast<uint64_t>(hk->units) * (hk->kslots + 1) * sizeof(float), 256);
-    w.qmul = w.qa + align_up(static_cast<uint64_t>(hk->units) * 4 * hk->kfetch, 256);
-    w.pairs = w.qmul + align_up(static_cast<uint64_t>(hk->units) * sizeof(float), 256);
-    w.part = w.pairs + align_up(static_cast<uint64_t>(hk->units) * (1 + 2 * kAttKsK) * sizeof(uint32_t), 256);
-    w.total = w.part + static_cast<uint64_t>(hv->units) * nchunks * (hv->kslots + 2) * sizeof(float);
+    w.part = 0;
+    w.total = nchunks >= 2 ? static_cast<uint64_t>(hv->units) * nchunks * (hv->kslots + 2) * sizeof(float) : 0;
     return w;
 }
 
@@ -1322,7 +1341,8 @@ int32_t attend_impl(const kvtc_tensor_ref *k, const kvtc_tensor_ref *v, int64_t 
         if (sa != KVTC_OK) return sa;
         work_bytes = kAttendScratchBytes;
     }
-    if (!work_dev || work_bytes < need || reinterpret_cast<uintptr_t>(work_dev) % 256) return KVTC_E_BUFSIZE;
+    if (need > 0 && (!work_dev || work_bytes < need || reinterpret_cast<uintptr_t>(work_dev) % 256))
+        return KVTC_E_BUFSIZE;
     const AttendSegs segs = attend_segs(hk, hv, s_end);
     const int64_t nchunks = segs.count;
     if (hk->units > 0x7FFFFFFF || nchunks > 0x7FFFFFFF || hk->units > 65535) return KVTC_E_SHAPE;
@@ -1347,15 +1367,8 @@ int32_t attend_impl(const kvtc_tensor_ref *k, const kvtc_tensor_ref *v, int64_t 
     a.D = hk->head_dim;
     a.inv_sqrt_d = 1.0f / sqrtf(static_cast<float>(hk->head_dim));
     const AttendWork wl = attend_work(hk, hv, s_end);
-    char *wb = static_cast<char *>(work_dev);
-    a.qt = reinterpret_cast<float *>(wb + wl.qt);
-    a.qa = reinterpret_cast<uint8_t *>(wb + wl.qa);
-    a.qmul = reinterpret_cast<float *>(wb + wl.qmul);
-    a.pairs = reinterpret_cast<uint32_t *>(wb + wl.pairs);
-    a.part = reinterpret_cast<float *>(wb + wl.part);
+    a.part = wl.total > 0 ? reinterpret_cast<float *>(static_cast<char *>(work_dev) + wl.part) : nullptr;
     const unsigned U = static_cast<unsigned>(hk->units);
-    hipLaunchKernelGGL(attend_prep_kernel, dim3(U), dim3(256), 0, stream, a);
-    if (launch_status() != KVTC_OK) return KVTC_E_DEVICE;
     if (nchunks > 0) {
         const size_t lds = attend_partial_lds(segs, a.k.row_words, a.v.row_words);
         if (lds > kLdsMax) return KVTC_E_SHAPE;
@@ -1369,7 +1382,9 @@ int32_t attend_impl(const kvtc_tensor_ref *k, const kvtc_tensor_ref *v, int64_t 
         if (!allow_lds(reinterpret_cast<const void *>(kern))) return KVTC_E_DEVICE;
         hipLaunchKernelGGL(kern, dim3(static_cast<unsigned>(nchunks), U), dim3(kAttThreads), lds, stream, a);
         if (launch_status() != KVTC_OK) return KVTC_E_DEVICE;
+        if (nchunks == 1) return KVTC_OK;            // the partial blocks wrote the output
     }
+    // two or more segments: merged per unit; no rows: zeros
     hipLaunchKernelGGL(attend_merge_kernel, dim3(U), dim3(256), 0, stream, a);
     return launch_status();
 }
