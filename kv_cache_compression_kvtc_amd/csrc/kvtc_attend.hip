@@ -1,5 +1,6 @@
 // Decode attention from the codes (gfx950): kvtc_attend and its kernels.
 #include <mutex>
+#include <type_traits>
 
 #include "kvtc_device.h"
 
@@ -68,6 +69,46 @@ typedef int i32x16 __attribute__((ext_vector_type(16)));
 // which the callers correct for; narrower codes are their own values.  The
 // window reads up to five words from the k-step's first word; words past the
 // row's fields only reach padding columns.
+// kstep_bytes_w from the window's five words x[0..4] (row words wi .. wi + 4,
+// read beforehand) and the bit shift sh = off & 31.
+template <int W>
+__device__ __forceinline__ void kstep_bytes_x(uint32_t sh, const uint32_t (&x)[5], uint32_t (&R)[4]) {
+    if constexpr (W == 2) {
+        const uint32_t v = __builtin_amdgcn_alignbit(x[1], x[0], sh);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) R[r] = (v >> (2 * r)) & 0x03030303u;
+    } else if constexpr (W == 4) {
+        const uint32_t x0 = __builtin_amdgcn_alignbit(x[1], x[0], sh);
+        const uint32_t x1 = __builtin_amdgcn_alignbit(x[2], x[1], sh);
+        R[0] = x0 & 0x0F0F0F0Fu;
+        R[1] = (x0 >> 4) & 0x0F0F0F0Fu;
+        R[2] = x1 & 0x0F0F0F0Fu;
+        R[3] = (x1 >> 4) & 0x0F0F0F0Fu;
+    } else if constexpr (W == 8) {
+#pragma unroll
+        for (int r = 0; r < 4; ++r) R[r] = __builtin_amdgcn_alignbit(x[r + 1], x[r], sh) ^ 0x80808080u;
+    } else if constexpr (W == 1) {
+        const uint32_t v = __builtin_amdgcn_alignbit(x[1], x[0], sh);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) R[r] = (((v >> (4 * r)) & 0xFu) * 0x00204081u) & 0x01010101u;
+    } else {
+        const uint32_t x0 = __builtin_amdgcn_alignbit(x[1], x[0], sh);
+        const uint32_t x1 = __builtin_amdgcn_alignbit(x[2], x[1], sh);
+        const uint32_t y = __builtin_amdgcn_alignbit(x1, x0, 16);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            uint32_t v = 0;
+#pragma unroll
+            for (int b = 0; b < 4; ++b) {
+                const int t = 4 * r + b;
+                const uint32_t f = t < 6 ? (x0 >> (3 * t)) & 7u : (y >> (3 * t - 16)) & 7u;
+                v |= f << (8 * b);
+            }
+            R[r] = v;
+        }
+    }
+}
+
 template <int W>
 __device__ __forceinline__ void kstep_bytes_w(uint32_t off, const uint32_t *row, uint32_t (&R)[4]) {
     const uint32_t wi = off >> 5, sh = off & 31u;
@@ -258,11 +299,26 @@ __device__ inline void sub_store(const SubSrc &g, uint32_t *buf, const u32x4 (&r
     }
 }
 
+// The wave's max or sum of v in every lane: quads and rows of 16 with DPP
+// moves (neighbours, pairs, half-row and row mirrors), then the row pairs and
+// halves of the wave swapped in.
+__device__ inline float wave_reduce(float v, bool is_max) {
+    auto op = [is_max](float x, float y) { return is_max ? fmaxf(x, y) : x + y; };
+    auto dpp = [](float x, auto ctrl) {
+        return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), decltype(ctrl)::value, 0xF, 0xF, false));
+    };
+    v = op(v, dpp(v, std::integral_constant<int, 0xB1>{}));    // quad_perm [1,0,3,2]
+    v = op(v, dpp(v, std::integral_constant<int, 0x4E>{}));    // quad_perm [2,3,0,1]
+    v = op(v, dpp(v, std::integral_constant<int, 0x141>{}));   // row_half_mirror
+    v = op(v, dpp(v, std::integral_constant<int, 0x140>{}));   // row_mirror
+    const auto p16 = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    v = op(__uint_as_float(p16[0]), __uint_as_float(p16[1]));
+    const auto p32 = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    return op(__uint_as_float(p32[0]), __uint_as_float(p32[1]));
+}
+
 __device__ inline float block_reduce(float v, float *red, bool is_max) {
-    for (int m = 32; m >= 1; m >>= 1) {
-        const float o = __shfl_xor(v, m, 64);
-        v = is_max ? fmaxf(v, o) : v + o;
-    }
+    v = wave_reduce(v, is_max);
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, nw = blockDim.x >> 6;
     __syncthreads();
     if (lane == 0) red[wave] = v;
@@ -294,7 +350,8 @@ __global__ __launch_bounds__(kAttThreads) void attend_partial_kernel(AttendArgs 
     float *mpt = qts + kMaxSlots;                                        // [kMaxSlots] min_j q.V_j
     uint32_t *kds = reinterpret_cast<uint32_t *>(mpt + kMaxSlots);      // [kAttKsK] key k-step descriptors
     uint32_t *ptab = kds + kAttKsK;                                      // [1 + 2 kAttKsK] scorer products
-    float *pl = reinterpret_cast<float *>(ptab + 1 + 2 * kAttKsK + 3);   // [chunk_rows] scores, then weights
+    uint32_t *plt = ptab + 1 + 2 * kAttKsK + 3;                          // [kAttPairs][64] lanes' product operands
+    float *pl = reinterpret_cast<float *>(plt + kAttPairs * 64);         // [chunk_rows] scores, then weights
     uint32_t *pw = reinterpret_cast<uint32_t *>(pl);                     //   as int8 digit words
     const int sub = a.sub, bw = (sub * max(K.row_words, V.row_words) + 16 + 3) & ~3;   // buffer words
     uint32_t *buf0 = reinterpret_cast<uint32_t *>(pl + ((a.chunk_rows + 3) & ~3));
@@ -311,6 +368,23 @@ __global__ __launch_bounds__(kAttThreads) void attend_partial_kernel(AttendArgs 
         const int rs = (key ? K.row_words : V.row_words) * 4;
         return sub_src(key ? kfirst : vfirst, static_cast<int64_t>(j) * sub, min(sub, nrows - j * sub), rs);
     };
+    // the next step's source, advanced by a running pointer (the key rows, then
+    // the value rows from their own first row)
+    const uint8_t *nxt_first = kfirst + static_cast<int64_t>(sub) * K.row_words * 4;
+    int nxt_rs = K.row_words * 4, nxt_left = nrows - sub;
+    SubSrc last_src{};
+    auto next_src = [&](int st1) __attribute__((always_inline)) {
+        if (st1 >= 2 * nsub) return last_src;         // past the last step: its chunks again
+        if (st1 == nsub) {
+            nxt_first = vfirst;
+            nxt_rs = V.row_words * 4;
+            nxt_left = nrows;
+        }
+        last_src = sub_src(nxt_first, 0, min(sub, nxt_left), nxt_rs);
+        nxt_first += static_cast<int64_t>(sub) * nxt_rs;
+        nxt_left -= sub;
+        return last_src;
+    };
 
     u32x4 stg[kAttStage];
     SubSrc g0 = step_src(0);
@@ -326,32 +400,31 @@ __global__ __launch_bounds__(kAttThreads) void attend_partial_kernel(AttendArgs 
         if (tid < nksK) kds[tid] = K.kdesc[static_cast<int64_t>(u) * nksK + tid];
         if (tid == 0) qal[kAttKsK * 4] = u32x4{0u, 0u, 0u, 0u};
         __syncthreads();
-        // qt_j = scale_j (q . V_j) / sqrt(D), and min_j (q . V_j) for the offset
+        // qt_j = scale_j (q . V_j) / sqrt(D), and min_j (q . V_j) for the offset:
+        // four lanes per slot, lane p of a quad taking the features d = p (mod 4)
         const int ns = K.ui[u].n_slots;
-        float qt = 0.f, mp = 0.f;
-        if (tid < ns) {
-            const float *vrow = K.basis + (static_cast<int64_t>(u) * K.kslots + tid) * a.D;
-            float acc0 = 0.f, acc1 = 0.f;
-            if ((a.D & 3) == 0 && (reinterpret_cast<uintptr_t>(K.basis) & 15u) == 0) {   // 16-byte rows
-                for (int d4 = 0; d4 < (a.D >> 2); ++d4) {
-                    const float4 v = reinterpret_cast<const float4 *>(vrow)[d4];
-                    acc0 = fmaf(ql[4 * d4], v.x, acc0);
-                    acc1 = fmaf(ql[4 * d4 + 1], v.y, acc1);
-                    acc0 = fmaf(ql[4 * d4 + 2], v.z, acc0);
-                    acc1 = fmaf(ql[4 * d4 + 3], v.w, acc1);
-                }
-            } else {
-                for (int d = 0; d < a.D; ++d) acc0 = fmaf(ql[d], vrow[d], acc0);
+        for (int jb = 0; jb < K.kslots; jb += kAttThreads / 4) {
+            const int j = jb + (tid >> 2), part = tid & 3;
+            float acc = 0.f;
+            if (j < ns) {
+                const float *vrow = K.basis + (static_cast<int64_t>(u) * K.kslots + j) * a.D;
+                for (int d = part; d < a.D; d += 4) acc = fmaf(ql[d], vrow[d], acc);
             }
-            const float acc = acc0 + acc1;
-            const int cj = K.comp[static_cast<int64_t>(u) * K.kslots + tid];
-            qt = K.qscale[static_cast<int64_t>(u) * K.rmax + cj] * acc * a.inv_sqrt_d;
-            mp = K.qmin[static_cast<int64_t>(u) * K.rmax + cj] * acc;
+            acc += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(acc), 0xB1, 0xF, 0xF, false));
+            acc += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(acc), 0x4E, 0xF, 0xF, false));
+            if (part == 0 && j < K.kslots) {
+                float qj = 0.f, mj = 0.f;
+                if (j < ns) {
+                    const int cj = K.comp[static_cast<int64_t>(u) * K.kslots + j];
+                    qj = K.qscale[static_cast<int64_t>(u) * K.rmax + cj] * acc * a.inv_sqrt_d;
+                    mj = K.qmin[static_cast<int64_t>(u) * K.rmax + cj] * acc;
+                }
+                qts[j] = qj;
+                mpt[j] = mj;
+            }
         }
-        if (tid < K.kslots) {
-            qts[tid] = qt;
-            mpt[tid] = mp;
-        }
+        __syncthreads();
+        const float qt = tid < K.kslots ? qts[tid] : 0.f;
         // fetch column 16 ks + t: Q = rint(qt * 2^(30 - e)), 2^e > max |qt| so that
         // |Q| < 2^30, as four balanced int8 digits (Q = sum_d d_d 256^d; the bytes
         // of (Q + 0x808080) ^ 0x808080), digit d at byte (4 ks + d) * 16 + t;
@@ -416,34 +489,33 @@ __global__ __launch_bounds__(kAttThreads) void attend_partial_kernel(AttendArgs 
         off = ok && hi ? offs >> 16 : offs & 0xFFFFu;
         addr = ok && (lane & 31u) < 4u ? ks * 4u + (lane & 31u) : static_cast<uint32_t>(kAttKsK * 4);
     };
-    uint32_t pwid[kAttPairs], poff[kAttPairs], paddr[kAttPairs];
+    // widths uniform; each lane's offset and operand address in an LDS table
+    // (offset | address << 16, one word per product and lane)
+    uint32_t pwid[kAttPairs];
 #pragma unroll
     for (int m = 0; m < kAttPairs; ++m) {
         pwid[m] = 0u;
-        poff[m] = 0u;
-        paddr[m] = kAttKsK * 4;
-        if (m < npairs) pair_lane(m, pwid[m], poff[m], paddr[m]);
+        if (m < npairs) {
+            uint32_t off, addr;
+            pair_lane(m, pwid[m], off, addr);
+            if (wave == 0) plt[m * 64 + lane] = off | (addr << 16);
+        }
     }
     // this wave's value k-steps w + kAttWaves i: widths and offsets (uniform), and the
     // stored slots of the columns lane n of a quad sums (fetch columns 4r + n)
     const int nksV = V.kfetch >> 4;
     const uint32_t n = lane & 3u;
     uint32_t vw[KW], voff[KW];
-    int fsv[KW][4];
 #pragma unroll
     for (int i = 0; i < KW; ++i) {
         const int ks = wave + kAttWaves * i;
         const uint32_t kd = ks < nksV ? V.kdesc[static_cast<int64_t>(u) * nksV + ks] : 0u;
         vw[i] = (kd >> 16) & 0xFu;
         voff[i] = kd & 0xFFFFu;
-#pragma unroll
-        for (int rr = 0; rr < 4; ++rr)
-            fsv[i][rr] = ks < nksV ? V.fslot[static_cast<int64_t>(u) * V.kfetch + ks * 16 + 4 * rr + static_cast<int>(n)] : -1;
     }
     uint32_t s1, s2;
     quad_selectors(lane, s1, s2);
     sub_store(g0, buf0, stg);
-    int dcur = g0.delta;                              // the current buffer's first-row word
     __syncthreads();
 
     float mloc = -__builtin_huge_valf(), M = 0.f, L = 0.f;
@@ -453,15 +525,16 @@ __global__ __launch_bounds__(kAttThreads) void attend_partial_kernel(AttendArgs 
 #pragma unroll
         for (int rr = 0; rr < 4; ++rr) acc[i][rr] = i32x4{0, 0, 0, 0};
     int dsum = 0;                                     // sum over this lane's quads of digit n of P
-    for (int st = 0; st < 2 * nsub; ++st) {
+    // Step st decodes buffer st & 1 and, at its start, loads the chunks of step
+    // st + 2 into the free staging set (every load issued: past the last step
+    // the last step's chunks again), so two sub-chunks are in flight while one
+    // is decoded; at its end it stores step st + 1's set into the other buffer.
+    auto step = [&](int st, u32x4 (&s_free)[kAttStage], u32x4 (&s_next)[kAttStage], const SubSrc &g_next,
+                    SubSrc &g_load, int dcur) __attribute__((always_inline)) {
         const uint32_t *cur = ((st & 1) ? buf1 : buf0) + dcur;
         uint32_t *nxt = (st & 1) ? buf0 : buf1;
-        const bool more = st + 1 < 2 * nsub;
-        SubSrc gn{};
-        if (more) {
-            gn = step_src(st + 1);
-            sub_load(gn, stg);
-        }
+        g_load = next_src(st + 2);
+        sub_load(g_load, s_free);
         if (st < nsub) {
             // scores (32x32x32 products, D[d][row] = sum_k A[d][k] B[k][row]): A
             // holds the query's digits (row d = digit d, rows 4-31 zero), B a
@@ -480,20 +553,27 @@ __global__ __launch_bounds__(kAttThreads) void attend_partial_kernel(AttendArgs 
                 auto product = [&](uint32_t wid, uint32_t off, uint32_t addr) __attribute__((always_inline)) {
                     const u32x4 qv = qal[addr];
                     uint32_t R[4];
-                    switch (wid) {
-                        case 2: kstep_bytes_w<2>(off, row0, R); break;
-                        case 4: kstep_bytes_w<4>(off, row0, R); break;
-                        case 8: kstep_bytes_w<8>(off, row0, R); break;
-                        case 1: kstep_bytes_w<1>(off, row0, R); break;
-                        default: kstep_bytes_w<3>(off, row0, R); break;
-                    }
+                    if (wid == 2u)
+                        kstep_bytes_w<2>(off, row0, R);
+                    else if (wid == 4u)
+                        kstep_bytes_w<4>(off, row0, R);
+                    else if (wid == 8u)
+                        kstep_bytes_w<8>(off, row0, R);
+                    else if (wid == 1u)
+                        kstep_bytes_w<1>(off, row0, R);
+                    else
+                        kstep_bytes_w<3>(off, row0, R);
                     a0 = __builtin_amdgcn_mfma_i32_32x32x32_i8(__builtin_bit_cast(i32x4, qv),
                                                                __builtin_bit_cast(i32x4, u32x4{R[0], R[1], R[2], R[3]}),
                                                                a0, 0, 0, 0);
                 };
 #pragma unroll
-                for (int m = 0; m < kAttPairs; ++m)
-                    if (m < npairs) product(pwid[m], poff[m], paddr[m]);
+                for (int m = 0; m < kAttPairs; ++m) {
+                    if (m < npairs) {
+                        const uint32_t pe = plt[m * 64 + lane];
+                        product(pwid[m], pe & 0xFFFFu, pe >> 16);
+                    }
+                }
                 for (int m = kAttPairs; m < npairs; ++m) {
                     uint32_t wid, off, addr;
                     pair_lane(m, wid, off, addr);
@@ -554,11 +634,19 @@ __global__ __launch_bounds__(kAttThreads) void attend_partial_kernel(AttendArgs 
                 }
             }
         }
-        if (more) {
-            sub_store(gn, nxt, stg);
-            dcur = gn.delta;
-        }
+        if (st + 1 < 2 * nsub) sub_store(g_next, nxt, s_next);
         __syncthreads();
+    };
+    u32x4 stg2[kAttStage];
+    SubSrc g1 = next_src(1);
+    sub_load(g1, stg2);
+    SubSrc gA = g0, gB = g1;
+    for (int st = 0; st < 2 * nsub; st += 2) {
+        SubSrc ga, gb;
+        step(st, stg, stg2, gB, ga, gA.delta);
+        step(st + 1, stg2, stg, ga, gb, gB.delta);
+        gA = ga;
+        gB = gb;
     }
     if (nsub == 0) {                                   // (an empty segment: never launched)
         M = -__builtin_huge_valf();
@@ -601,7 +689,7 @@ __global__ __launch_bounds__(kAttThreads) void attend_partial_kernel(AttendArgs 
             const double corr = vw[i] == 8u ? 128.0 * sp : 0.0;
 #pragma unroll
             for (int rr = 0; rr < 4; ++rr) {
-                const int j = fsv[i][rr];
+                const int j = V.fslot[static_cast<int64_t>(u) * V.kfetch + (wave + kAttWaves * i) * 16 + 4 * rr + static_cast<int>(n)];
                 if (j < 0) continue;
                 const i32x4 v = acc[i][rr];
                 const double T = ((static_cast<double>(v[3]) * 256.0 + v[2]) * 256.0 + v[1]) * 256.0 + v[0];
@@ -625,12 +713,23 @@ __global__ __launch_bounds__(kAttThreads) void attend_partial_kernel(AttendArgs 
         mpt[tid] = qts[tid] / L * V.qscale[static_cast<int64_t>(u) * V.rmax + cj];
     }
     __syncthreads();
+    // np parts per feature (np * D <= 512 partial sums in ql and qts), part p
+    // summing the slots j = p (mod np)
     const int b = u / a.H, h = u % a.H;
-    for (int d = tid; d < a.D; d += kAttThreads) {
-        float o = V.bias[static_cast<int64_t>(u) * a.D + d];
+    const int np = a.D <= 128 ? 4 : 2;
+    float *ob = ql;
+    if (tid < np * a.D) {
+        const int d = tid % a.D, part = tid / a.D;
         const float *vb = V.basis + static_cast<int64_t>(u) * V.kslots * a.D + d;
-        for (int j = 0; j < nv; ++j) o = fmaf(mpt[j], vb[static_cast<int64_t>(j) * a.D], o);
-        a.out[b * a.osb + h * a.osh + d] = static_cast<_Float16>(o);
+        float o = 0.f;
+        for (int j = part; j < nv; j += np) o = fmaf(mpt[j], vb[static_cast<int64_t>(j) * a.D], o);
+        ob[part * a.D + d] = o;
+    }
+    __syncthreads();
+    if (tid < a.D) {
+        float o = V.bias[static_cast<int64_t>(u) * a.D + tid];
+        for (int p2 = 0; p2 < np; ++p2) o += ob[p2 * a.D + tid];
+        a.out[b * a.osb + h * a.osh + tid] = static_cast<_Float16>(o);
     }
 }
 
@@ -749,7 +848,8 @@ AttendSegs attend_segs(const kvtc_state_header *hk, const kvtc_state_header *hv,
 size_t attend_partial_lds(const AttendSegs &g, int k_row_words, int v_row_words) {
     const size_t bw = (static_cast<size_t>(g.sub) * std::max(k_row_words, v_row_words) + 16 + 3) & ~static_cast<size_t>(3);
     return (kAttKsK * 4 + 1) * sizeof(u32x4) + (kAttWaves + 3 * kMaxSlots) * sizeof(float) +
-           (kAttKsK + 1 + 2 * kAttKsK + 3) * sizeof(uint32_t) + static_cast<size_t>((g.rows + 3) & ~3) * sizeof(float) +
+           (kAttKsK + 1 + 2 * kAttKsK + 3 + kAttPairs * 64) * sizeof(uint32_t) +
+           static_cast<size_t>((g.rows + 3) & ~3) * sizeof(float) +
            2 * bw * sizeof(uint32_t);
 }
 
