@@ -379,7 +379,7 @@ def time_attend(K, layer, S, dev, reps=20):
     return {"ms_per_call": round(ms, 4), "positions_per_s": round(h.batch * h.heads * S / (ms / 1e3), 1),
             "algorithmic_bytes": nbytes, "GBps": round(nbytes / (ms / 1e3) / 1e9, 1),
             "frac_hbm": round(nbytes / (ms / 1e3) / 1e9 / PEAK_HBM_GBPS, 4),
-            "launches": "prep + partial + merge"}
+            "launches": "one partial launch (one segment per unit; longer caches add a merge launch)"}
 
 
 def time_one_shot(K, wid, dev, reps=10):

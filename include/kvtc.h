@@ -312,8 +312,11 @@ int32_t kvtc_fetch_kv(const kvtc_tensor_ref *k, const kvtc_tensor_ref *v,
                       int64_t s_begin, int64_t s_end, void *hip_stream);
 
 /* Bytes of device workspace kvtc_attend needs for rows [0, s_end) of the given
- * key and value states (per unit: the query's score coefficients; per unit and
- * chunk of 512 rows: partial softmax statistics). */
+ * key and value states: partial softmax statistics per unit and segment when
+ * the rows take two or more segments (segments of at most 9216 rows, at least
+ * 256 unless the cache is shorter, enough of them to give the device about 512
+ * blocks); 0 when every unit's rows fit one segment.  kvtc_attend_gqa's general
+ * path (grouped query heads, group-head caches) has its own figure. */
 int32_t kvtc_attend_workspace(const void *k_state_host, const void *v_state_host, int64_t s_end,
                               size_t *bytes);
 
@@ -351,7 +354,8 @@ int32_t kvtc_attend_gqa(const kvtc_tensor_ref *k, const kvtc_tensor_ref *v, int6
  *               strides q_strides for (b, h, d), q_strides[2] == 1
  *   out_dev     fp16 [B, H, D] with element strides out_strides, out_strides[2] == 1
  *   work_dev    device workspace of at least kvtc_attend_workspace() bytes,
- *               256-byte aligned, owned by the caller (contents are scratch)
+ *               256-byte aligned, owned by the caller (contents are scratch);
+ *               may be NULL when that size is 0
  * Needs 0 <= s_end <= both capacities; KVTC_E_SHAPE for tensors of different
  * shapes, KVTC_E_BUFSIZE for a missing or short workspace. */
 int32_t kvtc_attend(const kvtc_tensor_ref *k, const kvtc_tensor_ref *v,

@@ -534,6 +534,12 @@ ATTEND_CASES = [
     ("batched", small(4, B=3, s_prefill=2048, s_total=2048 + 45)),
     ("long", small(5, s_prefill=4096, s_total=4096 + 1000)),
     ("llama", small(2, s_total=4096 + 77)),
+    # wide rows: 256 slots of 8 bits (256-byte rows, 64-row staging, 16 value
+    # k-steps: two per wave) and 192 slots in mixed widths (96-byte rows,
+    # 128-row staging, more than eight value k-steps)
+    ("wide-8bit", small(4, B=1, H=2, D=256, s_prefill=1024, s_total=1024 + 45, rank=256, budget=2048,
+                        choices=(0, 8))),
+    ("wide-mixed", small(4, B=1, H=2, D=256, s_prefill=1024, s_total=1024 + 45, rank=192, budget=768)),
 ]
 
 
@@ -571,7 +577,8 @@ def test_attend_matches_oracle(name, w):
     rng = np.random.default_rng(5)
     q = rng.normal(size=(w.B, w.H, w.D)) * 1.5
     qd = torch.from_numpy(q.astype(np.float32)).cuda()
-    for s_end in (S, S - 517 if S > 600 else S - 1, 1):
+    # (200 rows and 1 row: one segment per unit, finished in its blocks)
+    for s_end in (S, S - 517 if S > 600 else S - 1, 200, 1):
         ref = O.attend(sts[0], rows[0][:, :s_end], sts[1], rows[1][:, :s_end], q)
         Vh = O.fetch(sts[1], rows[1][:, :s_end])
         check_attend(ref, att(qd, s_end), Vh, f"{name} s_end={s_end}")
