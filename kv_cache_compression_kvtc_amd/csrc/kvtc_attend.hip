@@ -351,7 +351,9 @@ __global__ __launch_bounds__(kAttThreads) void attend_partial_kernel(AttendArgs 
     uint32_t *kds = reinterpret_cast<uint32_t *>(mpt + kMaxSlots);      // [kAttKsK] key k-step descriptors
     uint32_t *ptab = kds + kAttKsK;                                      // [1 + 2 kAttKsK] scorer products
     uint32_t *plt = ptab + 1 + 2 * kAttKsK + 3;                          // [kAttPairs][64] lanes' product operands
-    float *pl = reinterpret_cast<float *>(plt + kAttPairs * 64);         // [chunk_rows] scores, then weights
+    int *vfs = reinterpret_cast<int *>(plt + kAttPairs * 64);            // [kMaxSlots] value slot of each fetch column
+    float *vsc = reinterpret_cast<float *>(vfs + kMaxSlots);            // [kMaxSlots] value scale of each slot
+    float *pl = vsc + kMaxSlots;                                         // [chunk_rows] scores, then weights
     uint32_t *pw = reinterpret_cast<uint32_t *>(pl);                     //   as int8 digit words
     const int sub = a.sub, bw = (sub * max(K.row_words, V.row_words) + 16 + 3) & ~3;   // buffer words
     uint32_t *buf0 = reinterpret_cast<uint32_t *>(pl + ((a.chunk_rows + 3) & ~3));
@@ -391,20 +393,45 @@ __global__ __launch_bounds__(kAttThreads) void attend_partial_kernel(AttendArgs 
     sub_load(g0, stg);
     // ---- the query's scorer operands (while the first sub-chunk is in flight)
     const int nksK = K.kfetch >> 4;
-    float beta, mul;
+    float beta, mul, bias_t;
     {
         const int b = u / a.H, h = u % a.H;
-        for (int d = tid; d < a.D; d += kAttThreads)
-            ql[d] = a.q_f16 ? static_cast<float>(static_cast<const _Float16 *>(a.q)[b * a.qsb + h * a.qsh + d])
-                            : static_cast<const float *>(a.q)[b * a.qsb + h * a.qsh + d];
-        if (tid < nksK) kds[tid] = K.kdesc[static_cast<int64_t>(u) * nksK + tid];
+        // every global operand of the prologue and of the output is requested
+        // before the first use (one memory round trip, not one per step)
+        const int ns = K.ui[u].n_slots, nv = V.ui[u].n_slots;
+        const float qd = tid < a.D ? (a.q_f16 ? static_cast<float>(static_cast<const _Float16 *>(a.q)[b * a.qsb + h * a.qsh + tid])
+                                              : static_cast<const float *>(a.q)[b * a.qsb + h * a.qsh + tid])
+                                   : 0.f;
+        const uint32_t kdt = tid < nksK ? K.kdesc[static_cast<int64_t>(u) * nksK + tid] : 0u;
+        const int fsl = tid < K.kfetch ? K.fslot[static_cast<int64_t>(u) * K.kfetch + tid] : -1;
+        const float mu_t = tid < a.D ? K.mu[static_cast<int64_t>(u) * a.D + tid] : 0.f;
+        bias_t = tid < a.D ? V.bias[static_cast<int64_t>(u) * a.D + tid] : 0.f;
+        const int vfs_t = tid < V.kfetch ? V.fslot[static_cast<int64_t>(u) * V.kfetch + tid] : -1;
+        const int vc_t = tid < nv ? V.comp[static_cast<int64_t>(u) * V.kslots + tid] : 0;
+        const float vsc_t = tid < nv ? V.qscale[static_cast<int64_t>(u) * V.rmax + vc_t] : 0.f;
+        // the key ranges of the slots this lane's quad forms (at most 2 x 128 slots)
+        float ksc[2], kmn[2];
+#pragma unroll
+        for (int pj = 0; pj < 2; ++pj) {
+            const int j = pj * (kAttThreads / 4) + (tid >> 2);
+            const int cj = j < ns ? K.comp[static_cast<int64_t>(u) * K.kslots + j] : 0;
+            ksc[pj] = j < ns ? K.qscale[static_cast<int64_t>(u) * K.rmax + cj] : 0.f;
+            kmn[pj] = j < ns ? K.qmin[static_cast<int64_t>(u) * K.rmax + cj] : 0.f;
+        }
+        if (tid < a.D) ql[tid] = qd;
+        if (tid < nksK) kds[tid] = kdt;
+        if (tid < kMaxSlots) {
+            vfs[tid] = vfs_t;
+            vsc[tid] = vsc_t;
+        }
         if (tid == 0) qal[kAttKsK * 4] = u32x4{0u, 0u, 0u, 0u};
         __syncthreads();
         // qt_j = scale_j (q . V_j) / sqrt(D), and min_j (q . V_j) for the offset:
         // four lanes per slot, lane p of a quad taking the features d = p (mod 4)
-        const int ns = K.ui[u].n_slots;
-        for (int jb = 0; jb < K.kslots; jb += kAttThreads / 4) {
-            const int j = jb + (tid >> 2), part = tid & 3;
+#pragma unroll
+        for (int pj = 0; pj < 2; ++pj) {
+            const int j = pj * (kAttThreads / 4) + (tid >> 2), part = tid & 3;
+            if (pj * (kAttThreads / 4) >= K.kslots) break;                   // (uniform)
             float acc = 0.f;
             if (j < ns) {
                 const float *vrow = K.basis + (static_cast<int64_t>(u) * K.kslots + j) * a.D;
@@ -413,14 +440,8 @@ __global__ __launch_bounds__(kAttThreads) void attend_partial_kernel(AttendArgs 
             acc += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(acc), 0xB1, 0xF, 0xF, false));
             acc += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(acc), 0x4E, 0xF, 0xF, false));
             if (part == 0 && j < K.kslots) {
-                float qj = 0.f, mj = 0.f;
-                if (j < ns) {
-                    const int cj = K.comp[static_cast<int64_t>(u) * K.kslots + j];
-                    qj = K.qscale[static_cast<int64_t>(u) * K.rmax + cj] * acc * a.inv_sqrt_d;
-                    mj = K.qmin[static_cast<int64_t>(u) * K.rmax + cj] * acc;
-                }
-                qts[j] = qj;
-                mpt[j] = mj;
+                qts[j] = ksc[pj] * acc * a.inv_sqrt_d;
+                mpt[j] = kmn[pj] * acc;
             }
         }
         __syncthreads();
@@ -435,7 +456,7 @@ __global__ __launch_bounds__(kAttThreads) void attend_partial_kernel(AttendArgs 
         if (amax > 0.f) frexpf(amax, &e);
         float q8 = 0.f;
         if (tid < K.kfetch) {
-            const int j = K.fslot[static_cast<int64_t>(u) * K.kfetch + tid];
+            const int j = fsl;
             const int ks = tid >> 4, t = tid & 15;
             const int32_t Q = j >= 0 ? static_cast<int32_t>(rintf(ldexpf(qts[j], 30 - e))) : 0;
             const uint32_t W = (static_cast<uint32_t>(Q) + 0x808080u) ^ 0x808080u;
@@ -446,8 +467,7 @@ __global__ __launch_bounds__(kAttThreads) void attend_partial_kernel(AttendArgs 
         }
         const float c8 = block_reduce(q8, red, false);
         // (q . mu + sum_j min_j q . V_j) / sqrt(D)
-        float bpart = 0.f;
-        for (int d = tid; d < a.D; d += kAttThreads) bpart = fmaf(ql[d], K.mu[static_cast<int64_t>(u) * a.D + d], bpart);
+        float bpart = tid < a.D ? qd * mu_t : 0.f;
         if (tid < K.kslots) bpart += mpt[tid];
         const float bsum = block_reduce(bpart, red, false);
         beta = bsum * a.inv_sqrt_d + ldexpf(128.0f * c8, e - 30);
@@ -689,7 +709,7 @@ __global__ __launch_bounds__(kAttThreads) void attend_partial_kernel(AttendArgs 
             const double corr = vw[i] == 8u ? 128.0 * sp : 0.0;
 #pragma unroll
             for (int rr = 0; rr < 4; ++rr) {
-                const int j = V.fslot[static_cast<int64_t>(u) * V.kfetch + (wave + kAttWaves * i) * 16 + 4 * rr + static_cast<int>(n)];
+                const int j = vfs[(wave + kAttWaves * i) * 16 + 4 * rr + static_cast<int>(n)];
                 if (j < 0) continue;
                 const i32x4 v = acc[i][rr];
                 const double T = ((static_cast<double>(v[3]) * 256.0 + v[2]) * 256.0 + v[1]) * 256.0 + v[0];
@@ -708,10 +728,7 @@ __global__ __launch_bounds__(kAttThreads) void attend_partial_kernel(AttendArgs 
     // (the merge of one chunk, whose weight is 1)
     __syncthreads();
     const int nv = V.ui[u].n_slots;
-    if (tid < nv) {
-        const int cj = V.comp[static_cast<int64_t>(u) * V.kslots + tid];
-        mpt[tid] = qts[tid] / L * V.qscale[static_cast<int64_t>(u) * V.rmax + cj];
-    }
+    if (tid < nv) mpt[tid] = qts[tid] / L * vsc[tid];
     __syncthreads();
     // np parts per feature (np * D <= 512 partial sums in ql and qts), part p
     // summing the slots j = p (mod np)
@@ -727,7 +744,7 @@ __global__ __launch_bounds__(kAttThreads) void attend_partial_kernel(AttendArgs 
     }
     __syncthreads();
     if (tid < a.D) {
-        float o = V.bias[static_cast<int64_t>(u) * a.D + tid];
+        float o = bias_t;
         for (int p2 = 0; p2 < np; ++p2) o += ob[p2 * a.D + tid];
         a.out[b * a.osb + h * a.osh + tid] = static_cast<_Float16>(o);
     }
@@ -848,7 +865,7 @@ AttendSegs attend_segs(const kvtc_state_header *hk, const kvtc_state_header *hv,
 size_t attend_partial_lds(const AttendSegs &g, int k_row_words, int v_row_words) {
     const size_t bw = (static_cast<size_t>(g.sub) * std::max(k_row_words, v_row_words) + 16 + 3) & ~static_cast<size_t>(3);
     return (kAttKsK * 4 + 1) * sizeof(u32x4) + (kAttWaves + 3 * kMaxSlots) * sizeof(float) +
-           (kAttKsK + 1 + 2 * kAttKsK + 3 + kAttPairs * 64) * sizeof(uint32_t) +
+           (kAttKsK + 1 + 2 * kAttKsK + 3 + kAttPairs * 64 + 2 * kMaxSlots) * sizeof(uint32_t) +
            static_cast<size_t>((g.rows + 3) & ~3) * sizeof(float) +
            2 * bw * sizeof(uint32_t);
 }
