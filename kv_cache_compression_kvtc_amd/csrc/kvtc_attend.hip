@@ -613,22 +613,39 @@ __global__ __launch_bounds__(kAttThreads) void attend_partial_kernel(AttendArgs 
             if (st == nsub) {
                 // every score is in: the weights p = exp(s - M), their sum, and
                 // their digit words (P = rint(p * 2^30) <= 2^30 as four balanced
-                // int8 digits) in place of the scores
+                // int8 digits) in place of the scores.  A thread takes a quad of
+                // rows and stores its words transposed: word 4q + n holds digit n
+                // of rows 4q..4q+3 (byte s: row 4q + s), operand A as the value
+                // products read it.
                 M = block_reduce(mloc, red, true);
                 float lsum = 0.f;
-                for (int r = tid; r < nrows; r += blockDim.x) {
-                    const float p = expf(pl[r] - M);
-                    lsum += p;
-                    const uint32_t P = static_cast<uint32_t>(rintf(p * 1073741824.0f));
-                    pw[r] = (P + 0x808080u) ^ 0x808080u;
+                for (int q4 = tid; 4 * q4 < nrows; q4 += blockDim.x) {
+                    const u32x4 sc4 = reinterpret_cast<const u32x4 *>(pl)[q4];
+                    uint32_t W[4];
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        const float p = 4 * q4 + i < nrows ? expf(__uint_as_float(sc4[i]) - M) : 0.f;
+                        lsum += p;
+                        const uint32_t P = static_cast<uint32_t>(rintf(p * 1073741824.0f));
+                        W[i] = (P + 0x808080u) ^ 0x808080u;
+                    }
+                    // 4x4 byte transpose: T[n] byte s = W[s] byte n
+                    const uint32_t x01l = __builtin_amdgcn_perm(W[1], W[0], 0x05010400u);   // W0.0 W1.0 W0.1 W1.1
+                    const uint32_t x01h = __builtin_amdgcn_perm(W[1], W[0], 0x07030602u);   // W0.2 W1.2 W0.3 W1.3
+                    const uint32_t x23l = __builtin_amdgcn_perm(W[3], W[2], 0x05010400u);
+                    const uint32_t x23h = __builtin_amdgcn_perm(W[3], W[2], 0x07030602u);
+                    const u32x4 T = {__builtin_amdgcn_perm(x23l, x01l, 0x05040100u), __builtin_amdgcn_perm(x23l, x01l, 0x07060302u),
+                                     __builtin_amdgcn_perm(x23h, x01h, 0x05040100u), __builtin_amdgcn_perm(x23h, x01h, 0x07060302u)};
+                    reinterpret_cast<u32x4 *>(pw)[q4] = T;
                 }
                 L = block_reduce(lsum, red, false);   // (its barriers publish the digit words)
             }
             // p-weighted sums of the value codes on 4x4x4 products (16 blocks of
             // 4 lanes, D[d][col] = sum_k A[d][k] B[k][col]): lane l holds row l of
             // each 64-row group (quad q: rows 4q..4q+3); A is the quad's digits of
-            // P, B its codes of fetch columns 4r + n (lane n, register r), both
-            // from the lanes' own rows by a byte transpose across the quad.  Wave
+            // P (stored transposed), B its codes of fetch columns 4r + n (lane n,
+            // register r), from the lanes' own rows by a byte transpose across
+            // the quad.  Wave
             // w takes the k-steps w + kAttWaves i over every row.  Sums are exact in int32
             // (|digit|, |code| <= 128, at most 9216 rows).
             // the sub-chunk's G = sub / 64 groups, rows past the chunk with zero
@@ -638,7 +655,7 @@ __global__ __launch_bounds__(kAttThreads) void attend_partial_kernel(AttendArgs 
 #pragma unroll
             for (int g = 0; g < G; ++g) {
                 const int rl = g * 64 + static_cast<int>(lane);
-                Ag[g] = quad_transpose(rl < rows_j ? pw[j0 + rl] : 0u, s1, s2);
+                Ag[g] = (rl & ~3) < rows_j ? pw[j0 + rl] : 0u;          // (quads past the chunk: zero)
                 dsum = __builtin_amdgcn_sdot4(static_cast<int>(Ag[g]), 0x01010101, dsum, false);
             }
             const uint32_t *vrow0 = cur + static_cast<int>(lane) * V.row_words;
