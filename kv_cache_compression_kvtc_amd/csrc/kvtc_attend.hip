@@ -28,6 +28,7 @@ constexpr int kAttPairs = 8;         // scorer products whose operands a lane ke
 constexpr int kAttThreads = 64 * kAttWaves;
 constexpr int kAttStage = 3;         // staged 16-byte chunks per thread and sub-chunk (24 KiB per block)
 constexpr int kAttKsK = 16;          // k-steps of the key contraction (kfetch <= 256)
+constexpr int kAttBatch = 16;        // basis loads in flight per lane (prologue and output)
 
 struct AttendSide {
     const uint8_t *codes;
@@ -388,9 +389,11 @@ __global__ __launch_bounds__(kAttThreads) void attend_partial_kernel(AttendArgs 
         return last_src;
     };
 
-    u32x4 stg[kAttStage];
+    u32x4 stg[kAttStage], stg2[kAttStage];
     SubSrc g0 = step_src(0);
     sub_load(g0, stg);
+    SubSrc g1 = next_src(1);
+    sub_load(g1, stg2);
     // ---- the query's scorer operands (while the first sub-chunk is in flight)
     const int nksK = K.kfetch >> 4;
     float beta, mul, bias_t;
@@ -428,14 +431,42 @@ __global__ __launch_bounds__(kAttThreads) void attend_partial_kernel(AttendArgs 
         __syncthreads();
         // qt_j = scale_j (q . V_j) / sqrt(D), and min_j (q . V_j) for the offset:
         // four lanes per slot, lane p of a quad taking the features d = p (mod 4)
+        // (or, rows of 16-byte multiples, the features 4f..4f+3 for f = p (mod 4))
+        const bool vec4 = (a.D & 3) == 0 && (reinterpret_cast<uintptr_t>(K.basis) & 15u) == 0;
 #pragma unroll
         for (int pj = 0; pj < 2; ++pj) {
             const int j = pj * (kAttThreads / 4) + (tid >> 2), part = tid & 3;
             if (pj * (kAttThreads / 4) >= K.kslots) break;                   // (uniform)
             float acc = 0.f;
             if (j < ns) {
+                // the row's loads issued kAttBatch at a time (one memory round
+                // trip per batch, not per feature)
                 const float *vrow = K.basis + (static_cast<int64_t>(u) * K.kslots + j) * a.D;
-                for (int d = part; d < a.D; d += 4) acc = fmaf(ql[d], vrow[d], acc);
+                if (vec4) {                                                  // 16-byte rows: lane p takes quads p (mod 4)
+                    const float4 *vr4 = reinterpret_cast<const float4 *>(vrow);
+                    const float4 *q4 = reinterpret_cast<const float4 *>(ql);
+                    for (int f0 = part; f0 < (a.D >> 2); f0 += 4 * (kAttBatch / 2)) {
+                        float4 v[kAttBatch / 2];
+#pragma unroll
+                        for (int k = 0; k < kAttBatch / 2; ++k)
+                            v[k] = f0 + 4 * k < (a.D >> 2) ? vr4[f0 + 4 * k] : float4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                        for (int k = 0; k < kAttBatch / 2; ++k)
+                            if (f0 + 4 * k < (a.D >> 2)) {
+                                const float4 qv = q4[f0 + 4 * k];
+                                acc = fmaf(qv.x, v[k].x, fmaf(qv.y, v[k].y, fmaf(qv.z, v[k].z, fmaf(qv.w, v[k].w, acc))));
+                            }
+                    }
+                } else {                                                     // (a device blob off 16 bytes)
+                    for (int d0 = part; d0 < a.D; d0 += 4 * kAttBatch) {
+                        float v[kAttBatch];
+#pragma unroll
+                        for (int k = 0; k < kAttBatch; ++k) v[k] = d0 + 4 * k < a.D ? vrow[d0 + 4 * k] : 0.f;
+#pragma unroll
+                        for (int k = 0; k < kAttBatch; ++k)
+                            if (d0 + 4 * k < a.D) acc = fmaf(ql[d0 + 4 * k], v[k], acc);
+                    }
+                }
             }
             acc += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(acc), 0xB1, 0xF, 0xF, false));
             acc += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(acc), 0x4E, 0xF, 0xF, false));
@@ -674,9 +705,6 @@ __global__ __launch_bounds__(kAttThreads) void attend_partial_kernel(AttendArgs 
         if (st + 1 < 2 * nsub) sub_store(g_next, nxt, s_next);
         __syncthreads();
     };
-    u32x4 stg2[kAttStage];
-    SubSrc g1 = next_src(1);
-    sub_load(g1, stg2);
     SubSrc gA = g0, gB = g1;
     for (int st = 0; st < 2 * nsub; st += 2) {
         SubSrc ga, gb;
@@ -756,7 +784,17 @@ __global__ __launch_bounds__(kAttThreads) void attend_partial_kernel(AttendArgs 
         const int d = tid % a.D, part = tid / a.D;
         const float *vb = V.basis + static_cast<int64_t>(u) * V.kslots * a.D + d;
         float o = 0.f;
-        for (int j = part; j < nv; j += np) o = fmaf(mpt[j], vb[static_cast<int64_t>(j) * a.D], o);
+        for (int j0 = part; j0 < nv; j0 += np * 2 * kAttBatch) {
+            float v[2 * kAttBatch];
+#pragma unroll
+            for (int k = 0; k < 2 * kAttBatch; ++k) {
+                const int j = j0 + np * k;
+                v[k] = j < nv ? vb[static_cast<int64_t>(j) * a.D] : 0.f;
+            }
+#pragma unroll
+            for (int k = 0; k < 2 * kAttBatch; ++k)
+                if (j0 + np * k < nv) o = fmaf(mpt[j0 + np * k], v[k], o);
+        }
         ob[part * a.D + d] = o;
     }
     __syncthreads();
@@ -808,7 +846,14 @@ __global__ __launch_bounds__(256) void attend_merge_kernel(AttendArgs a) {
         if (a.nchunks > 0) {
             o = V.bias[static_cast<int64_t>(u) * a.D + d];
             const float *vb = V.basis + static_cast<int64_t>(u) * V.kslots * a.D + d;
-            for (int j = 0; j < nv; ++j) o = fmaf(coef[j], vb[static_cast<int64_t>(j) * a.D], o);
+            for (int j0 = 0; j0 < nv; j0 += kAttBatch) {
+                float v[kAttBatch];
+#pragma unroll
+                for (int k = 0; k < kAttBatch; ++k) v[k] = j0 + k < nv ? vb[static_cast<int64_t>(j0 + k) * a.D] : 0.f;
+#pragma unroll
+                for (int k = 0; k < kAttBatch; ++k)
+                    if (j0 + k < nv) o = fmaf(coef[j0 + k], v[k], o);
+            }
         }
         a.out[b * a.osb + h * a.osh + d] = static_cast<_Float16>(o);
     }
