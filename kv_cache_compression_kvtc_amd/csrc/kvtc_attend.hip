@@ -29,6 +29,10 @@ constexpr int kAttThreads = 64 * kAttWaves;
 constexpr int kAttStage = 3;         // staged 16-byte chunks per thread and sub-chunk (24 KiB per block)
 constexpr int kAttKsK = 16;          // k-steps of the key contraction (kfetch <= 256)
 constexpr int kAttBatch = 16;        // basis loads in flight per lane (prologue and output)
+// Code widths a partial kernel decodes (bit W set for width W): every width, or
+// only 2, 4 and 8 bits (the common choice sets; a shorter dispatch per k-step)
+constexpr int kWidthsAll = (1 << 1) | (1 << 2) | (1 << 3) | (1 << 4) | (1 << 8);
+constexpr int kWidths248 = (1 << 2) | (1 << 4) | (1 << 8);
 
 struct AttendSide {
     const uint8_t *codes;
@@ -217,6 +221,54 @@ __device__ __forceinline__ void value_kstep(i32x4 (&acc)[4], uint32_t off, const
     }
 }
 
+// A k-step's score operand bytes for a width known only at run time (uniform),
+// among the widths WS allows.
+template <int WS>
+__device__ __forceinline__ void kstep_bytes_any(uint32_t wid, uint32_t off, const uint32_t *row0, uint32_t (&R)[4]) {
+    if constexpr (WS == kWidths248) {
+        if (wid == 4u)
+            kstep_bytes_w<4>(off, row0, R);
+        else if (wid == 2u)
+            kstep_bytes_w<2>(off, row0, R);
+        else
+            kstep_bytes_w<8>(off, row0, R);
+    } else {
+        if (wid == 2u)
+            kstep_bytes_w<2>(off, row0, R);
+        else if (wid == 4u)
+            kstep_bytes_w<4>(off, row0, R);
+        else if (wid == 8u)
+            kstep_bytes_w<8>(off, row0, R);
+        else if (wid == 1u)
+            kstep_bytes_w<1>(off, row0, R);
+        else
+            kstep_bytes_w<3>(off, row0, R);
+    }
+}
+
+// value_kstep for a run-time width among those WS allows (0: no k-step).
+template <int WS, int G>
+__device__ __forceinline__ void value_kstep_any(uint32_t wid, i32x4 (&acc)[4], uint32_t off, const uint32_t *row0,
+                                                int row_words, const uint32_t (&Ag)[G], uint32_t s1, uint32_t s2) {
+    if constexpr (WS == kWidths248) {
+        if (wid == 4u)
+            value_kstep<4, G>(acc, off, row0, row_words, Ag, s1, s2);
+        else if (wid == 2u)
+            value_kstep<2, G>(acc, off, row0, row_words, Ag, s1, s2);
+        else if (wid == 8u)
+            value_kstep<8, G>(acc, off, row0, row_words, Ag, s1, s2);
+    } else {
+        switch (wid) {
+            case 2: value_kstep<2, G>(acc, off, row0, row_words, Ag, s1, s2); break;
+            case 4: value_kstep<4, G>(acc, off, row0, row_words, Ag, s1, s2); break;
+            case 8: value_kstep<8, G>(acc, off, row0, row_words, Ag, s1, s2); break;
+            case 1: value_kstep<1, G>(acc, off, row0, row_words, Ag, s1, s2); break;
+            case 3: value_kstep<3, G>(acc, off, row0, row_words, Ag, s1, s2); break;
+            default: break;                                    // no such k-step
+        }
+    }
+}
+
 __device__ inline uint32_t row_field(const uint32_t *row, uint32_t sb) {
     const uint32_t off = sb & kOffsetMask, w = sb >> 24;
     const uint32_t wi = off >> 5, sh = off & 31u;
@@ -337,7 +389,7 @@ __device__ inline float block_reduce(float v, float *red, bool is_max) {
 // the last row for its k-step windows): while one buffer is decoded, the next
 // sub-chunk's chunks are in flight in registers.  The
 // segment's scores stay in LDS, turned into weights once the keys are done.
-template <int KW, int G>
+template <int KW, int G, int WS>
 __global__ __launch_bounds__(kAttThreads) void attend_partial_kernel(AttendArgs a) {
     extern __shared__ __align__(16) unsigned char smem[];
     const int c = blockIdx.x, u = blockIdx.y, tid = threadIdx.x;
@@ -604,16 +656,7 @@ __global__ __launch_bounds__(kAttThreads) void attend_partial_kernel(AttendArgs 
                 auto product = [&](uint32_t wid, uint32_t off, uint32_t addr) __attribute__((always_inline)) {
                     const u32x4 qv = qal[addr];
                     uint32_t R[4];
-                    if (wid == 2u)
-                        kstep_bytes_w<2>(off, row0, R);
-                    else if (wid == 4u)
-                        kstep_bytes_w<4>(off, row0, R);
-                    else if (wid == 8u)
-                        kstep_bytes_w<8>(off, row0, R);
-                    else if (wid == 1u)
-                        kstep_bytes_w<1>(off, row0, R);
-                    else
-                        kstep_bytes_w<3>(off, row0, R);
+                    kstep_bytes_any<WS>(wid, off, row0, R);
                     a0 = __builtin_amdgcn_mfma_i32_32x32x32_i8(__builtin_bit_cast(i32x4, qv),
                                                                __builtin_bit_cast(i32x4, u32x4{R[0], R[1], R[2], R[3]}),
                                                                a0, 0, 0, 0);
@@ -691,16 +734,7 @@ __global__ __launch_bounds__(kAttThreads) void attend_partial_kernel(AttendArgs 
             }
             const uint32_t *vrow0 = cur + static_cast<int>(lane) * V.row_words;
 #pragma unroll
-            for (int i = 0; i < KW; ++i) {
-                switch (vw[i]) {
-                    case 2: value_kstep<2, G>(acc[i], voff[i], vrow0, V.row_words, Ag, s1, s2); break;
-                    case 4: value_kstep<4, G>(acc[i], voff[i], vrow0, V.row_words, Ag, s1, s2); break;
-                    case 8: value_kstep<8, G>(acc[i], voff[i], vrow0, V.row_words, Ag, s1, s2); break;
-                    case 1: value_kstep<1, G>(acc[i], voff[i], vrow0, V.row_words, Ag, s1, s2); break;
-                    case 3: value_kstep<3, G>(acc[i], voff[i], vrow0, V.row_words, Ag, s1, s2); break;
-                    default: break;                            // no such k-step
-                }
-            }
+            for (int i = 0; i < KW; ++i) value_kstep_any<WS, G>(vw[i], acc[i], voff[i], vrow0, V.row_words, Ag, s1, s2);
         }
         if (st + 1 < 2 * nsub) sub_store(g_next, nxt, s_next);
         __syncthreads();
@@ -1554,10 +1588,22 @@ int32_t attend_impl(const kvtc_tensor_ref *k, const kvtc_tensor_ref *v, int64_t 
         // value k-steps per wave (at most 16 k-steps over kAttWaves waves): 16
         // accumulator registers each
         const int kw = (a.v.kfetch / 16 + kAttWaves - 1) / kAttWaves;
-        auto pick = [&](auto k1, auto k2) { return kw <= 1 ? k1 : k2; };
-        auto kern = a.sub == 256   ? pick(attend_partial_kernel<1, 4>, attend_partial_kernel<2, 4>)
-                    : a.sub == 128 ? pick(attend_partial_kernel<1, 2>, attend_partial_kernel<2, 2>)
-                                   : pick(attend_partial_kernel<1, 1>, attend_partial_kernel<2, 1>);
+        // the short width dispatch when both tensors' width choices (which every
+        // stored width is one of) are within {0, 2, 4, 8}
+        auto narrow = [](const kvtc_state_header *h) {
+            for (int i = 0; i < std::min<int>(h->n_choices, KVTC_MAX_CHOICES); ++i)
+                if (h->choices[i] != 0 && h->choices[i] != 2 && h->choices[i] != 4 && h->choices[i] != 8) return false;
+            return true;
+        };
+        const bool w248 = narrow(hk) && narrow(hv);
+        auto pick = [&](auto k1, auto k2, auto k1n, auto k2n) { return w248 ? (kw <= 1 ? k1n : k2n) : (kw <= 1 ? k1 : k2); };
+        auto kern = a.sub == 256 ? pick(attend_partial_kernel<1, 4, kWidthsAll>, attend_partial_kernel<2, 4, kWidthsAll>,
+                                        attend_partial_kernel<1, 4, kWidths248>, attend_partial_kernel<2, 4, kWidths248>)
+                    : a.sub == 128
+                        ? pick(attend_partial_kernel<1, 2, kWidthsAll>, attend_partial_kernel<2, 2, kWidthsAll>,
+                               attend_partial_kernel<1, 2, kWidths248>, attend_partial_kernel<2, 2, kWidths248>)
+                        : pick(attend_partial_kernel<1, 1, kWidthsAll>, attend_partial_kernel<2, 1, kWidthsAll>,
+                               attend_partial_kernel<1, 1, kWidths248>, attend_partial_kernel<2, 1, kWidths248>);
         if (!allow_lds(reinterpret_cast<const void *>(kern))) return KVTC_E_DEVICE;
         hipLaunchKernelGGL(kern, dim3(static_cast<unsigned>(nchunks), U), dim3(kAttThreads), lds, stream, a);
         if (launch_status() != KVTC_OK) return KVTC_E_DEVICE;

@@ -540,6 +540,12 @@ ATTEND_CASES = [
     ("wide-8bit", small(4, B=1, H=2, D=256, s_prefill=1024, s_total=1024 + 45, rank=256, budget=2048,
                         choices=(0, 8))),
     ("wide-mixed", small(4, B=1, H=2, D=256, s_prefill=1024, s_total=1024 + 45, rank=192, budget=768)),
+    # 96 slots of 8 bits: 96-byte rows (128-row staging), six value k-steps
+    ("mid-8bit", small(4, B=1, H=2, s_prefill=1024, s_total=1024 + 45, rank=96, budget=768, choices=(0, 8))),
+    # one, three and four value k-steps (most waves without one)
+    ("few-ksteps", small(4, B=1, H=2, s_prefill=1024, s_total=1024 + 45, rank=40, budget=80)),
+    ("three-ksteps", small(1, rank=16, budget=32)),
+    ("one-kstep", small(1, rank=16, budget=64, choices=(0, 4))),
 ]
 
 
