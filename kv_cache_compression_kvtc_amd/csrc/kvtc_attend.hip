@@ -406,10 +406,10 @@ __global__ __launch_bounds__(kAttThreads) void attend_partial_kernel(AttendArgs 
     uint32_t *plt = ptab + 1 + 2 * kAttKsK + 3;                          // [kAttPairs][64] lanes' product operands
     int *vfs = reinterpret_cast<int *>(plt + kAttPairs * 64);            // [kMaxSlots] value slot of each fetch column
     float *vsc = reinterpret_cast<float *>(vfs + kMaxSlots);            // [kMaxSlots] value scale of each slot
-    float *pl = vsc + kMaxSlots;                                         // [chunk_rows] scores, then weights
+    float *pl = vsc + kMaxSlots;                                         // [chunk_rows, rounded up to sub] scores, then weights
     uint32_t *pw = reinterpret_cast<uint32_t *>(pl);                     //   as int8 digit words
     const int sub = a.sub, bw = (sub * max(K.row_words, V.row_words) + 16 + 3) & ~3;   // buffer words
-    uint32_t *buf0 = reinterpret_cast<uint32_t *>(pl + ((a.chunk_rows + 3) & ~3));
+    uint32_t *buf0 = reinterpret_cast<uint32_t *>(pl + (a.chunk_rows + sub - 1) / sub * sub);
     uint32_t *buf1 = buf0 + bw;
     const int64_t s0 = static_cast<int64_t>(c) * a.chunk_rows;
     const int nrows = static_cast<int>(min<int64_t>(a.chunk_rows, a.s_end - s0));
@@ -632,13 +632,13 @@ __global__ __launch_bounds__(kAttThreads) void attend_partial_kernel(AttendArgs 
     // st + 2 into the free staging set (every load issued: past the last step
     // the last step's chunks again), so two sub-chunks are in flight while one
     // is decoded; at its end it stores step st + 1's set into the other buffer.
-    auto step = [&](int st, u32x4 (&s_free)[kAttStage], u32x4 (&s_next)[kAttStage], const SubSrc &g_next,
-                    SubSrc &g_load, int dcur) __attribute__((always_inline)) {
+    auto step = [&](auto key_c, int st, u32x4 (&s_free)[kAttStage], u32x4 (&s_next)[kAttStage],
+                    const SubSrc &g_next, SubSrc &g_load, int dcur) __attribute__((always_inline)) {
         const uint32_t *cur = ((st & 1) ? buf1 : buf0) + dcur;
         uint32_t *nxt = (st & 1) ? buf0 : buf1;
         g_load = next_src(st + 2);
         sub_load(g_load, s_free);
-        if (st < nsub) {
+        if constexpr (decltype(key_c)::value) {
             // scores (32x32x32 products, D[d][row] = sum_k A[d][k] B[k][row]): A
             // holds the query's digits (row d = digit d, rows 4-31 zero), B a
             // tile's codes; lane l supplies row or column l & 31 over k-range
@@ -693,7 +693,7 @@ __global__ __launch_bounds__(kAttThreads) void attend_partial_kernel(AttendArgs 
                 // products read it.
                 M = block_reduce(mloc, red, true);
                 float lsum = 0.f;
-                for (int q4 = tid; 4 * q4 < nrows; q4 += blockDim.x) {
+                for (int q4 = tid; 4 * q4 < nsub * sub; q4 += blockDim.x) {     // (zero words up to the last sub-chunk's end)
                     const u32x4 sc4 = reinterpret_cast<const u32x4 *>(pl)[q4];
                     uint32_t W[4];
 #pragma unroll
@@ -722,14 +722,13 @@ __global__ __launch_bounds__(kAttThreads) void attend_partial_kernel(AttendArgs 
             // the quad.  Wave
             // w takes the k-steps w + kAttWaves i over every row.  Sums are exact in int32
             // (|digit|, |code| <= 128, at most 9216 rows).
-            // the sub-chunk's G = sub / 64 groups, rows past the chunk with zero
+            // the sub-chunk's G = sub / 64 groups, rows past the segment with zero
             // A (their codes are stale words inside the buffer)
-            const int j0 = (st - nsub) * sub, rows_j = min(sub, nrows - j0);
+            const int j0 = (st - nsub) * sub;
             uint32_t Ag[G];
 #pragma unroll
             for (int g = 0; g < G; ++g) {
-                const int rl = g * 64 + static_cast<int>(lane);
-                Ag[g] = (rl & ~3) < rows_j ? pw[j0 + rl] : 0u;          // (quads past the chunk: zero)
+                Ag[g] = pw[j0 + g * 64 + static_cast<int>(lane)];
                 dsum = __builtin_amdgcn_sdot4(static_cast<int>(Ag[g]), 0x01010101, dsum, false);
             }
             const uint32_t *vrow0 = cur + static_cast<int>(lane) * V.row_words;
@@ -739,11 +738,32 @@ __global__ __launch_bounds__(kAttThreads) void attend_partial_kernel(AttendArgs 
         if (st + 1 < 2 * nsub) sub_store(g_next, nxt, s_next);
         __syncthreads();
     };
+    // the key steps, then the value steps, each loop taking two steps at a time
+    // (the staging sets alternate); an odd number of sub-chunks puts the last
+    // key step and the first value step in one pair
+    const std::integral_constant<bool, true> key_step;
+    const std::integral_constant<bool, false> value_step;
     SubSrc gA = g0, gB = g1;
-    for (int st = 0; st < 2 * nsub; st += 2) {
+    int st = 0;
+    for (; st + 1 < nsub; st += 2) {
         SubSrc ga, gb;
-        step(st, stg, stg2, gB, ga, gA.delta);
-        step(st + 1, stg2, stg, ga, gb, gB.delta);
+        step(key_step, st, stg, stg2, gB, ga, gA.delta);
+        step(key_step, st + 1, stg2, stg, ga, gb, gB.delta);
+        gA = ga;
+        gB = gb;
+    }
+    if (st < nsub) {
+        SubSrc ga, gb;
+        step(key_step, st, stg, stg2, gB, ga, gA.delta);
+        step(value_step, st + 1, stg2, stg, ga, gb, gB.delta);
+        gA = ga;
+        gB = gb;
+        st += 2;
+    }
+    for (; st < 2 * nsub; st += 2) {
+        SubSrc ga, gb;
+        step(value_step, st, stg, stg2, gB, ga, gA.delta);
+        step(value_step, st + 1, stg2, stg, ga, gb, gB.delta);
         gA = ga;
         gB = gb;
     }
@@ -962,7 +982,7 @@ size_t attend_partial_lds(const AttendSegs &g, int k_row_words, int v_row_words)
     const size_t bw = (static_cast<size_t>(g.sub) * std::max(k_row_words, v_row_words) + 16 + 3) & ~static_cast<size_t>(3);
     return (kAttKsK * 4 + 1) * sizeof(u32x4) + (kAttWaves + 3 * kMaxSlots) * sizeof(float) +
            (kAttKsK + 1 + 2 * kAttKsK + 3 + kAttPairs * 64 + 2 * kMaxSlots) * sizeof(uint32_t) +
-           static_cast<size_t>((g.rows + 3) & ~3) * sizeof(float) +
+           static_cast<size_t>((g.rows + g.sub - 1) / g.sub * g.sub) * sizeof(float) +
            2 * bw * sizeof(uint32_t);
 }
 
