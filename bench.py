@@ -42,7 +42,9 @@ def parse():
     p = argparse.ArgumentParser()
     p.add_argument("--gpus", type=int, default=1)
     p.add_argument("--steps", type=int, default=20)
-    p.add_argument("--warmup", type=int, default=3)
+    # (about 25 ms of untimed steps: after the host-side set-up the first ~20 ms of
+    # launches run up to 7% slower than the steady state)
+    p.add_argument("--warmup", type=int, default=40)
     p.add_argument("--cpu-seconds", type=float, default=10.0, help="oracle sample budget")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--no-extra", action="store_true", help="skip the other workloads (long context, "

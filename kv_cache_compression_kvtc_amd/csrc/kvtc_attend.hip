@@ -29,10 +29,6 @@ constexpr int kAttThreads = 64 * kAttWaves;
 constexpr int kAttStage = 3;         // staged 16-byte chunks per thread and sub-chunk (24 KiB per block)
 constexpr int kAttKsK = 16;          // k-steps of the key contraction (kfetch <= 256)
 constexpr int kAttBatch = 16;        // basis loads in flight per lane (prologue and output)
-// Code widths a partial kernel decodes (bit W set for width W): every width, or
-// only 2, 4 and 8 bits (the common choice sets; a shorter dispatch per k-step)
-constexpr int kWidthsAll = (1 << 1) | (1 << 2) | (1 << 3) | (1 << 4) | (1 << 8);
-constexpr int kWidths248 = (1 << 2) | (1 << 4) | (1 << 8);
 
 struct AttendSide {
     const uint8_t *codes;
@@ -1608,14 +1604,8 @@ int32_t attend_impl(const kvtc_tensor_ref *k, const kvtc_tensor_ref *v, int64_t 
         // value k-steps per wave (at most 16 k-steps over kAttWaves waves): 16
         // accumulator registers each
         const int kw = (a.v.kfetch / 16 + kAttWaves - 1) / kAttWaves;
-        // the short width dispatch when both tensors' width choices (which every
-        // stored width is one of) are within {0, 2, 4, 8}
-        auto narrow = [](const kvtc_state_header *h) {
-            for (int i = 0; i < std::min<int>(h->n_choices, KVTC_MAX_CHOICES); ++i)
-                if (h->choices[i] != 0 && h->choices[i] != 2 && h->choices[i] != 4 && h->choices[i] != 8) return false;
-            return true;
-        };
-        const bool w248 = narrow(hk) && narrow(hv);
+        // the short width dispatch when both tensors' widths are within {0, 2, 4, 8}
+        const bool w248 = widths_248(hk) && widths_248(hv);
         auto pick = [&](auto k1, auto k2, auto k1n, auto k2n) { return w248 ? (kw <= 1 ? k1n : k2n) : (kw <= 1 ? k1 : k2); };
         auto kern = a.sub == 256 ? pick(attend_partial_kernel<1, 4, kWidthsAll>, attend_partial_kernel<2, 4, kWidthsAll>,
                                         attend_partial_kernel<1, 4, kWidths248>, attend_partial_kernel<2, 4, kWidths248>)

@@ -160,7 +160,21 @@ struct FetchArgs {
 struct FetchPair {
     FetchArgs t[2];
     int64_t split, nblocks_real, nblocks_per_xcd;
+    bool narrow;                       // (host) every width of both tensors is 0, 2, 4 or 8
 };
+
+// Code widths a kernel decodes (bit W set for width W): every width, or only 2,
+// 4 and 8 bits (the common choice sets; a shorter dispatch per k-step).
+constexpr int kWidthsAll = (1 << 1) | (1 << 2) | (1 << 3) | (1 << 4) | (1 << 8);
+constexpr int kWidths248 = (1 << 2) | (1 << 4) | (1 << 8);
+
+// Whether a tensor's width choices (which every stored width is one of) are
+// all among 0, 2, 4 and 8.
+inline bool widths_248(const kvtc_state_header *h) {
+    for (int i = 0; i < std::min<int>(h->n_choices, KVTC_MAX_CHOICES); ++i)
+        if (h->choices[i] != 0 && h->choices[i] != 2 && h->choices[i] != 4 && h->choices[i] != 8) return false;
+    return true;
+}
 
 typedef _Float16 half2 __attribute__((ext_vector_type(2)));
 typedef float float2v __attribute__((ext_vector_type(2)));
@@ -189,7 +203,7 @@ __device__ inline void small_fields(uint32_t lo, uint32_t (&pr)[4]) {
 // dequantised with the row's fp16 (min, scale) of the k-step's quantisation
 // group in one fp16 fma; mypar points at the lane's token in the group-major
 // parameter staging.
-template <bool MIXED>
+template <bool MIXED, int WS = kWidthsAll>
 __device__ __forceinline__ half8 decode_kstep(uint32_t kd, const uint32_t *myrow, const uint32_t *mypar,
                                               uint32_t half_k) {
     const uint32_t w = (kd >> 16) & 0xFu;
@@ -211,7 +225,7 @@ __device__ __forceinline__ half8 decode_kstep(uint32_t kd, const uint32_t *myrow
         pr[1] = __builtin_amdgcn_perm(kMagic, ev, 0x04030402u);
         pr[2] = __builtin_amdgcn_perm(kMagic, od, 0x04010400u);
         pr[3] = __builtin_amdgcn_perm(kMagic, od, 0x04030402u);
-    } else if (w == 2u) {
+    } else if (WS == kWidths248 || w == 2u) {
         // slots 0,4,8,12 then 1,5,9,13 (2,6,10,14 then 3,7,11,15 in the upper half)
         const uint32_t t = lo >> (half_k << 2);
         const uint32_t ev = t & 0x03030303u, od = (t >> 2) & 0x03030303u;
@@ -342,6 +356,7 @@ struct FetchPlan {
     FetchArgs a;
     int ds, rw;                        // columns per block (128 or 64), row words per lane
     bool mixed;
+    bool narrow;                       // DP with every width choice among 0, 2, 4, 8
 };
 
 // ------------------------------------------------------------ refit mode

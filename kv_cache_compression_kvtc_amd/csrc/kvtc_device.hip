@@ -226,6 +226,7 @@ int32_t plan_fetch(const void *state_host, const void *state_dev, const void *co
     p->ds = DS;
     p->rw = (kFetTok * tw + 63) / 64;
     p->mixed = mixed;
+    p->narrow = !mixed && widths_248(h);
     return KVTC_OK;
 }
 
@@ -275,6 +276,7 @@ int32_t launch_fetch_plans(const FetchPlan &p0, const FetchPlan *p1, hipStream_t
         rw = std::max(rw, p1->rw);
         nt = 2;
     }
+    m.narrow = p0.narrow && (!p1 || p1->narrow);
     m.nblocks_per_xcd = (m.nblocks_real + 7) / 8;
     if (m.nblocks_per_xcd * 8 > 0x7FFFFFFF) return KVTC_E_SHAPE;
     return launch_fetch(p0.mixed, p0.ds / 32, m, nt, ks, rw, stream);

@@ -111,7 +111,7 @@ constexpr int fetch_prefetch() { return RW <= 8 ? (MIXED ? 2 : 3) : (RW <= 16 &&
 // epilogue writes whole rows of the slice, 16-byte chunks of up to four rows
 // per store; with eight waves (long contractions) one block does, and the
 // epilogue writes the slice in two halves.
-template <bool MIXED, int NDB, int KS, int RW, int NW, int PF>
+template <bool MIXED, int NDB, int KS, int RW, int NW, int PF, int WS>
 __global__ __launch_bounds__(64 * NW, 2) void fetch_kernel(FetchPair m) {
     extern __shared__ __align__(16) unsigned char smem[];
     constexpr int DS = 32 * NDB;
@@ -269,7 +269,7 @@ __global__ __launch_bounds__(64 * NW, 2) void fetch_kernel(FetchPair m) {
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks) {
             if (((kd[ks] >> 16) & 0xFu) == 0u) continue;          // empty k-step (wave-uniform)
-            const half8 bv = decode_kstep<MIXED>(kd[ks], myrow, mypar, half_k);
+            const half8 bv = decode_kstep<MIXED, WS>(kd[ks], myrow, mypar, half_k);
 #pragma unroll
             for (int db = 0; db < NDB; ++db) {
                 const half8 av = *reinterpret_cast<const half8 *>(wl + (db * 32 + tok) * a.wpitch + ks * 16 + half_k * 8);
@@ -363,7 +363,10 @@ int32_t launch_fetch_rw(FetchPair m, int nt, hipStream_t stream) {
     }
     if (lds > kLdsMax) return KVTC_E_SHAPE;
     const int64_t grid = m.nblocks_per_xcd * 8;
-    auto kern = fetch_kernel<MIXED, NDB, KS, RW, NW, fetch_prefetch<MIXED, RW>()>;
+    constexpr int PF = fetch_prefetch<MIXED, RW>();
+    auto kern = fetch_kernel<MIXED, NDB, KS, RW, NW, PF, kWidthsAll>;
+    if constexpr (!MIXED)
+        if (m.narrow) kern = fetch_kernel<MIXED, NDB, KS, RW, NW, PF, kWidths248>;
     if (!allow_lds(reinterpret_cast<const void *>(kern))) return KVTC_E_DEVICE;
     hipLaunchKernelGGL(kern, dim3(static_cast<unsigned>(grid)), dim3(64 * NW), lds, stream, m);
     return launch_status();
