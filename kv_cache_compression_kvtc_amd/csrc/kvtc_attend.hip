@@ -628,6 +628,7 @@ __global__ __launch_bounds__(kAttThreads) void attend_partial_kernel(AttendArgs 
     // st + 2 into the free staging set (every load issued: past the last step
     // the last step's chunks again), so two sub-chunks are in flight while one
     // is decoded; at its end it stores step st + 1's set into the other buffer.
+    uint32_t pe_r[kAttPairs];                         // the lane's product operands, held through the key steps
     auto step = [&](auto key_c, int st, u32x4 (&s_free)[kAttStage], u32x4 (&s_next)[kAttStage],
                     const SubSrc &g_next, SubSrc &g_load, int dcur) __attribute__((always_inline)) {
         const uint32_t *cur = ((st & 1) ? buf1 : buf0) + dcur;
@@ -660,8 +661,7 @@ __global__ __launch_bounds__(kAttThreads) void attend_partial_kernel(AttendArgs 
 #pragma unroll
                 for (int m = 0; m < kAttPairs; ++m) {
                     if (m < npairs) {
-                        const uint32_t pe = plt[m * 64 + lane];
-                        product(pwid[m], pe & 0xFFFFu, pe >> 16);
+                        product(pwid[m], pe_r[m] & 0xFFFFu, pe_r[m] >> 16);
                     }
                 }
                 for (int m = kAttPairs; m < npairs; ++m) {
@@ -740,6 +740,8 @@ __global__ __launch_bounds__(kAttThreads) void attend_partial_kernel(AttendArgs 
     const std::integral_constant<bool, true> key_step;
     const std::integral_constant<bool, false> value_step;
     SubSrc gA = g0, gB = g1;
+#pragma unroll
+    for (int m = 0; m < kAttPairs; ++m) pe_r[m] = plt[m * 64 + lane];   // (entries past npairs unused)
     int st = 0;
     for (; st + 1 < nsub; st += 2) {
         SubSrc ga, gb;
