@@ -70,46 +70,6 @@ typedef int i32x16 __attribute__((ext_vector_type(16)));
 // which the callers correct for; narrower codes are their own values.  The
 // window reads up to five words from the k-step's first word; words past the
 // row's fields only reach padding columns.
-// kstep_bytes_w from the window's five words x[0..4] (row words wi .. wi + 4,
-// read beforehand) and the bit shift sh = off & 31.
-template <int W>
-__device__ __forceinline__ void kstep_bytes_x(uint32_t sh, const uint32_t (&x)[5], uint32_t (&R)[4]) {
-    if constexpr (W == 2) {
-        const uint32_t v = __builtin_amdgcn_alignbit(x[1], x[0], sh);
-#pragma unroll
-        for (int r = 0; r < 4; ++r) R[r] = (v >> (2 * r)) & 0x03030303u;
-    } else if constexpr (W == 4) {
-        const uint32_t x0 = __builtin_amdgcn_alignbit(x[1], x[0], sh);
-        const uint32_t x1 = __builtin_amdgcn_alignbit(x[2], x[1], sh);
-        R[0] = x0 & 0x0F0F0F0Fu;
-        R[1] = (x0 >> 4) & 0x0F0F0F0Fu;
-        R[2] = x1 & 0x0F0F0F0Fu;
-        R[3] = (x1 >> 4) & 0x0F0F0F0Fu;
-    } else if constexpr (W == 8) {
-#pragma unroll
-        for (int r = 0; r < 4; ++r) R[r] = __builtin_amdgcn_alignbit(x[r + 1], x[r], sh) ^ 0x80808080u;
-    } else if constexpr (W == 1) {
-        const uint32_t v = __builtin_amdgcn_alignbit(x[1], x[0], sh);
-#pragma unroll
-        for (int r = 0; r < 4; ++r) R[r] = (((v >> (4 * r)) & 0xFu) * 0x00204081u) & 0x01010101u;
-    } else {
-        const uint32_t x0 = __builtin_amdgcn_alignbit(x[1], x[0], sh);
-        const uint32_t x1 = __builtin_amdgcn_alignbit(x[2], x[1], sh);
-        const uint32_t y = __builtin_amdgcn_alignbit(x1, x0, 16);
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-            uint32_t v = 0;
-#pragma unroll
-            for (int b = 0; b < 4; ++b) {
-                const int t = 4 * r + b;
-                const uint32_t f = t < 6 ? (x0 >> (3 * t)) & 7u : (y >> (3 * t - 16)) & 7u;
-                v |= f << (8 * b);
-            }
-            R[r] = v;
-        }
-    }
-}
-
 template <int W>
 __device__ __forceinline__ void kstep_bytes_w(uint32_t off, const uint32_t *row, uint32_t (&R)[4]) {
     const uint32_t wi = off >> 5, sh = off & 31u;
@@ -552,23 +512,29 @@ __global__ __launch_bounds__(kAttThreads) void attend_partial_kernel(AttendArgs 
         beta = bsum * a.inv_sqrt_d + ldexpf(128.0f * c8, e - 30);
         mul = ldexpf(1.0f, e - 30);
         // the products: consecutive k-steps of one width in pairs (lanes 0-31 take
-        // the first, lanes 32-63 the second, so a product decodes one width)
-        if (tid == 0) {
-            int np = 0;
-            for (int ks = 0; ks < nksK;) {
-                const uint32_t w = (kds[ks] >> 16) & 0xFu;
-                if (w == 0u) {
-                    ++ks;
-                    continue;
-                }
-                const bool two = ks + 1 < nksK && ((kds[ks + 1] >> 16) & 0xFu) == w;
-                const uint32_t kb = two ? static_cast<uint32_t>(ks + 1) : 0xFFu;
-                ptab[1 + 2 * np] = static_cast<uint32_t>(ks) | (kb << 8) | (w << 16);
-                ptab[2 + 2 * np] = (kds[ks] & 0xFFFFu) | (two ? (kds[ks + 1] & 0xFFFFu) << 16 : 0u);
-                ++np;
-                ks += two ? 2 : 1;
+        // the first, lanes 32-63 the second, so a product decodes one width).
+        // Wave 0, lane l for k-step l: a run of equal widths starts where the
+        // width changes; k-steps at even positions of a run of nonzero width head
+        // a product, with the next one if it is in the run; products in k-step
+        // order (heads counted below each lane).
+        if (wave == 0) {
+            const int l = static_cast<int>(lane);
+            const uint32_t kdl = l < nksK ? kds[l] : 0u;
+            const uint32_t w = (kdl >> 16) & 0xFu;
+            const uint32_t wprev = __shfl_up(w, 1), wnext = __shfl_down(w, 1), kdn = __shfl_down(kdl, 1);
+            const uint64_t starts = __ballot(l == 0 || w != wprev);
+            const uint64_t upto = l == 63 ? ~0ull : (2ull << l) - 1ull;
+            const int run0 = 63 - __clzll(starts & upto);
+            const bool head = w != 0u && ((l - run0) & 1) == 0;
+            const uint64_t heads = __ballot(head);
+            if (head) {
+                const int np = __popcll(heads & ((1ull << l) - 1ull));
+                const bool two = l + 1 < nksK && wnext == w;
+                const uint32_t kb = two ? static_cast<uint32_t>(l + 1) : 0xFFu;
+                ptab[1 + 2 * np] = static_cast<uint32_t>(l) | (kb << 8) | (w << 16);
+                ptab[2 + 2 * np] = (kdl & 0xFFFFu) | (two ? (kdn & 0xFFFFu) << 16 : 0u);
             }
-            ptab[0] = static_cast<uint32_t>(np);
+            if (l == 0) ptab[0] = static_cast<uint32_t>(__popcll(heads));
         }
         __syncthreads();
     }
