@@ -257,6 +257,13 @@ __global__ __launch_bounds__(64 * NW, 2) void fetch_kernel(FetchPair m) {
     for (int ks = 0; ks < KS; ++ks)
         kd[ks] = ks < a.nks ? __builtin_amdgcn_readfirstlane(a.kdesc[static_cast<int64_t>(u) * a.nks + ks]) : 0u;
 
+    // this lane's W rows (A operand: row db * 32 + tok, its k-half), one address
+    // per 32-column block for the whole block: the per-k-step offsets are
+    // constants (no pitch multiply or argument reload in the tile loop)
+    const _Float16 *wrow[NDB];
+#pragma unroll
+    for (int db = 0; db < NDB; ++db) wrow[db] = wl + (db * 32 + tok) * a.wpitch + half_k * 8;
+
     auto process = [&](int tile, auto full) {
         constexpr bool kFull = decltype(full)::value;
         const int64_t s = a.s_begin + static_cast<int64_t>(tile) * kFetTok;
@@ -272,7 +279,7 @@ __global__ __launch_bounds__(64 * NW, 2) void fetch_kernel(FetchPair m) {
             const half8 bv = decode_kstep<MIXED, WS>(kd[ks], myrow, mypar, half_k);
 #pragma unroll
             for (int db = 0; db < NDB; ++db) {
-                const half8 av = *reinterpret_cast<const half8 *>(wl + (db * 32 + tok) * a.wpitch + ks * 16 + half_k * 8);
+                const half8 av = *reinterpret_cast<const half8 *>(wrow[db] + ks * 16);
                 acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_f16(av, bv, acc[db], 0, 0, 0);
             }
         }
