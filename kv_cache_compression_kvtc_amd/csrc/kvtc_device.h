@@ -212,7 +212,19 @@ __device__ __forceinline__ half8 decode_kstep(uint32_t kd, const uint32_t *myrow
     const uint32_t r0 = myrow[wi], r1 = myrow[wi + 1];
     const uint32_t lo = __builtin_amdgcn_alignbit(r1, r0, sh);
     uint32_t pr[4];                                        // 4 packed half2 of 1024 + code
-    if (w == 8u) {
+    if constexpr (WS == kWidths248) {
+        // widths 2, 4 and 8 in one branch-free form (uniform selects): the
+        // eight codes land in the bytes of x0:x1 in the orders below
+        const uint32_t hi = __builtin_amdgcn_alignbit(myrow[wi + 2], r1, sh);
+        const uint32_t t = w == 2u ? lo >> (half_k << 2) : lo;
+        const uint32_t msk = w == 8u ? 0xFFFFFFFFu : (w == 4u ? 0x0F0F0F0Fu : 0x03030303u);
+        const uint32_t x0 = t & msk;
+        const uint32_t x1 = (w == 8u ? hi : t >> (w == 4u ? 4u : 2u)) & msk;
+        pr[0] = __builtin_amdgcn_perm(kMagic, x0, 0x04010400u);
+        pr[1] = __builtin_amdgcn_perm(kMagic, x0, 0x04030402u);
+        pr[2] = __builtin_amdgcn_perm(kMagic, x1, 0x04010400u);
+        pr[3] = __builtin_amdgcn_perm(kMagic, x1, 0x04030402u);
+    } else if (w == 8u) {
         const uint32_t hi = __builtin_amdgcn_alignbit(myrow[wi + 2], r1, sh);
         pr[0] = __builtin_amdgcn_perm(kMagic, lo, 0x04010400u);
         pr[1] = __builtin_amdgcn_perm(kMagic, lo, 0x04030402u);
@@ -225,7 +237,7 @@ __device__ __forceinline__ half8 decode_kstep(uint32_t kd, const uint32_t *myrow
         pr[1] = __builtin_amdgcn_perm(kMagic, ev, 0x04030402u);
         pr[2] = __builtin_amdgcn_perm(kMagic, od, 0x04010400u);
         pr[3] = __builtin_amdgcn_perm(kMagic, od, 0x04030402u);
-    } else if (WS == kWidths248 || w == 2u) {
+    } else if (w == 2u) {
         // slots 0,4,8,12 then 1,5,9,13 (2,6,10,14 then 3,7,11,15 in the upper half)
         const uint32_t t = lo >> (half_k << 2);
         const uint32_t ev = t & 0x03030303u, od = (t >> 2) & 0x03030303u;
