@@ -202,7 +202,8 @@ __device__ inline void small_fields(uint32_t lo, uint32_t (&pr)[4]) {
 // window and turned into exact fp16 integers.  In group-head mode each code is
 // dequantised with the row's fp16 (min, scale) of the k-step's quantisation
 // group in one fp16 fma; mypar points at the lane's token in the group-major
-// parameter staging.
+// parameter staging.  Widths 2, 4 and 8 share one branch-free form; with WS =
+// kWidthsAll two uniform tests route 1 and 3 bits to their own extraction.
 template <bool MIXED, int WS = kWidthsAll>
 __device__ __forceinline__ half8 decode_kstep(uint32_t kd, const uint32_t *myrow, const uint32_t *mypar,
                                               uint32_t half_k) {
@@ -212,9 +213,15 @@ __device__ __forceinline__ half8 decode_kstep(uint32_t kd, const uint32_t *myrow
     const uint32_t r0 = myrow[wi], r1 = myrow[wi + 1];
     const uint32_t lo = __builtin_amdgcn_alignbit(r1, r0, sh);
     uint32_t pr[4];                                        // 4 packed half2 of 1024 + code
-    if constexpr (WS == kWidths248) {
-        // widths 2, 4 and 8 in one branch-free form (uniform selects): the
-        // eight codes land in the bytes of x0:x1 in the orders below
+    if (WS != kWidths248 && w == 1u) {
+        small_fields<1>(lo, pr);
+    } else if (WS != kWidths248 && w == 3u) {
+        small_fields<3>(lo, pr);
+    } else {
+        // widths 2, 4 and 8 in one branch-free form (uniform selects): 8 bits:
+        // the window's eight bytes; 4 bits: nibbles stored 0,2,4,6,1,3,5,7 (even
+        // then odd nibbles); 2 bits: slots 0,4,8,12 then 1,5,9,13 (2,6,10,14 then
+        // 3,7,11,15 in the upper half)
         const uint32_t hi = __builtin_amdgcn_alignbit(myrow[wi + 2], r1, sh);
         const uint32_t t = w == 2u ? lo >> (half_k << 2) : lo;
         const uint32_t msk = w == 8u ? 0xFFFFFFFFu : (w == 4u ? 0x0F0F0F0Fu : 0x03030303u);
@@ -224,31 +231,6 @@ __device__ __forceinline__ half8 decode_kstep(uint32_t kd, const uint32_t *myrow
         pr[1] = __builtin_amdgcn_perm(kMagic, x0, 0x04030402u);
         pr[2] = __builtin_amdgcn_perm(kMagic, x1, 0x04010400u);
         pr[3] = __builtin_amdgcn_perm(kMagic, x1, 0x04030402u);
-    } else if (w == 8u) {
-        const uint32_t hi = __builtin_amdgcn_alignbit(myrow[wi + 2], r1, sh);
-        pr[0] = __builtin_amdgcn_perm(kMagic, lo, 0x04010400u);
-        pr[1] = __builtin_amdgcn_perm(kMagic, lo, 0x04030402u);
-        pr[2] = __builtin_amdgcn_perm(kMagic, hi, 0x04010400u);
-        pr[3] = __builtin_amdgcn_perm(kMagic, hi, 0x04030402u);
-    } else if (w == 4u) {
-        // nibbles of a 4-bit k-step are stored in the order 0,2,4,6,1,3,5,7
-        const uint32_t ev = lo & 0x0F0F0F0Fu, od = (lo >> 4) & 0x0F0F0F0Fu;
-        pr[0] = __builtin_amdgcn_perm(kMagic, ev, 0x04010400u);
-        pr[1] = __builtin_amdgcn_perm(kMagic, ev, 0x04030402u);
-        pr[2] = __builtin_amdgcn_perm(kMagic, od, 0x04010400u);
-        pr[3] = __builtin_amdgcn_perm(kMagic, od, 0x04030402u);
-    } else if (w == 2u) {
-        // slots 0,4,8,12 then 1,5,9,13 (2,6,10,14 then 3,7,11,15 in the upper half)
-        const uint32_t t = lo >> (half_k << 2);
-        const uint32_t ev = t & 0x03030303u, od = (t >> 2) & 0x03030303u;
-        pr[0] = __builtin_amdgcn_perm(kMagic, ev, 0x04010400u);
-        pr[1] = __builtin_amdgcn_perm(kMagic, ev, 0x04030402u);
-        pr[2] = __builtin_amdgcn_perm(kMagic, od, 0x04010400u);
-        pr[3] = __builtin_amdgcn_perm(kMagic, od, 0x04030402u);
-    } else if (w == 1u) {
-        small_fields<1>(lo, pr);
-    } else {
-        small_fields<3>(lo, pr);
     }
     half8 bv;
 #pragma unroll
