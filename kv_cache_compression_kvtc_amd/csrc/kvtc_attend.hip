@@ -940,8 +940,9 @@ AttendSegs attend_segs(const kvtc_state_header *hk, const kvtc_state_header *hv,
 }
 
 // LDS of a partial block: scorer operands, reductions, the query's working
-// arrays and product table, the segment's scores, and two sub-chunk buffers
-// (the longer row times the sub-chunk plus sixteen slack words each).
+// arrays and product table, the segment's scores (rounded up to whole
+// sub-chunks, whose weight digits past the last row are zero), and two sub-chunk
+// buffers (the longer row times the sub-chunk plus sixteen slack words each).
 size_t attend_partial_lds(const AttendSegs &g, int k_row_words, int v_row_words) {
     const size_t bw = (static_cast<size_t>(g.sub) * std::max(k_row_words, v_row_words) + 16 + 3) & ~static_cast<size_t>(3);
     return (kAttKsK * 4 + 1) * sizeof(u32x4) + (kAttWaves + 3 * kMaxSlots) * sizeof(float) +
