@@ -589,7 +589,6 @@ __global__ __launch_bounds__(kAttThreads) void attend_partial_kernel(AttendArgs 
     for (int i = 0; i < KW; ++i)
 #pragma unroll
         for (int rr = 0; rr < 4; ++rr) acc[i][rr] = i32x4{0, 0, 0, 0};
-    int dsum = 0;                                     // sum over this lane's quads of digit n of P
     // Step st decodes buffer st & 1 and, at its start, loads the chunks of step
     // st + 2 into the free staging set (every load issued: past the last step
     // the last step's chunks again), so two sub-chunks are in flight while one
@@ -655,6 +654,7 @@ __global__ __launch_bounds__(kAttThreads) void attend_partial_kernel(AttendArgs 
                 // products read it.
                 M = block_reduce(mloc, red, true);
                 float lsum = 0.f;
+                uint64_t psum = 0;
                 for (int q4 = tid; 4 * q4 < nsub * sub; q4 += blockDim.x) {     // (zero words up to the last sub-chunk's end)
                     const u32x4 sc4 = reinterpret_cast<const u32x4 *>(pl)[q4];
                     uint32_t W[4];
@@ -663,6 +663,7 @@ __global__ __launch_bounds__(kAttThreads) void attend_partial_kernel(AttendArgs 
                         const float p = 4 * q4 + i < nrows ? expf(__uint_as_float(sc4[i]) - M) : 0.f;
                         lsum += p;
                         const uint32_t P = static_cast<uint32_t>(rintf(p * 1073741824.0f));
+                        psum += P;
                         W[i] = (P + 0x808080u) ^ 0x808080u;
                     }
                     // 4x4 byte transpose: T[n] byte s = W[s] byte n
@@ -674,7 +675,12 @@ __global__ __launch_bounds__(kAttThreads) void attend_partial_kernel(AttendArgs 
                                      __builtin_amdgcn_perm(x23h, x01h, 0x05040100u), __builtin_amdgcn_perm(x23h, x01h, 0x07060302u)};
                     reinterpret_cast<u32x4 *>(pw)[q4] = T;
                 }
-                L = block_reduce(lsum, red, false);   // (its barriers publish the digit words)
+                // sum P exactly (below 2^44) for the 8-bit columns' correction: per
+                // wave, into the scorer operands' space (free once the keys are done)
+#pragma unroll
+                for (int o = 32; o >= 1; o >>= 1) psum += __shfl_xor(psum, o);
+                if (lane == 0) reinterpret_cast<uint64_t *>(qal)[wave] = psum;
+                L = block_reduce(lsum, red, false);   // (its barriers publish the digit words and sums)
             }
             // p-weighted sums of the value codes on 4x4x4 products (16 blocks of
             // 4 lanes, D[d][col] = sum_k A[d][k] B[k][col]): lane l holds row l of
@@ -691,7 +697,6 @@ __global__ __launch_bounds__(kAttThreads) void attend_partial_kernel(AttendArgs 
 #pragma unroll
             for (int g = 0; g < G; ++g) {
                 Ag[g] = pw[j0 + g * 64 + static_cast<int>(lane)];
-                dsum = __builtin_amdgcn_sdot4(static_cast<int>(Ag[g]), 0x01010101, dsum, false);
             }
             const uint32_t *vrow0 = cur + static_cast<int>(lane) * V.row_words;
 #pragma unroll
@@ -754,12 +759,10 @@ __global__ __launch_bounds__(kAttThreads) void attend_partial_kernel(AttendArgs 
 #pragma unroll
             for (int dd = 0; dd < 4; ++dd) acc[i][rr][dd] = quad_total(acc[i][rr][dd]);
     }
-    // sum P = sum_n 256^n (sum of digit n), digit n's sum held by lane n of each quad
-    const int dt = quad_total(dsum);
-    const double sp = static_cast<double>(__builtin_amdgcn_update_dpp(0, dt, 0x00, 0xF, 0xF, false)) +
-                      256.0 * static_cast<double>(__builtin_amdgcn_update_dpp(0, dt, 0x55, 0xF, 0xF, false)) +
-                      65536.0 * static_cast<double>(__builtin_amdgcn_update_dpp(0, dt, 0xAA, 0xF, 0xF, false)) +
-                      16777216.0 * static_cast<double>(__builtin_amdgcn_update_dpp(0, dt, 0xFF, 0xF, 0xF, false));
+    // sum P over the segment (the waves' exact sums from the softmax pass)
+    double sp = 0.0;
+#pragma unroll
+    for (int w = 0; w < kAttWaves; ++w) sp += static_cast<double>(reinterpret_cast<const uint64_t *>(qal)[w]);
     // abar of fetch column 16 ks + 4r + n = 2^-30 (sum_d 256^d acc_d), plus
     // 128 * sum P for 8-bit columns (read as c - 128); lanes 0-3 write, to the
     // partial sums of a segment or (a single segment) to LDS for the output
