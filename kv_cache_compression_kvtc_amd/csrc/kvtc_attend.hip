@@ -26,7 +26,7 @@ constexpr int kAttBlocks = 512;      // partial blocks worth filling the GPU wit
 constexpr int kAttWaves = 8;         // waves per partial block
 constexpr int kAttPairs = 8;         // scorer products whose operands a lane keeps in registers
 constexpr int kAttThreads = 64 * kAttWaves;
-constexpr int kAttStage = 3;         // staged 16-byte chunks per thread and sub-chunk (24 KiB per block)
+constexpr int kAttStage = 3;         // staged 16-byte chunks per thread and sub-chunk at most (24 KiB per block)
 constexpr int kAttKsK = 16;          // k-steps of the key contraction (kfetch <= 256)
 constexpr int kAttBatch = 16;        // basis loads in flight per lane (prologue and output)
 
@@ -294,15 +294,17 @@ __device__ inline SubSrc sub_src(const uint8_t *codes, int64_t row0, int nrows, 
     return g;
 }
 
-__device__ inline void sub_load(const SubSrc &g, u32x4 (&r)[kAttStage]) {
+template <int ST>
+__device__ inline void sub_load(const SubSrc &g, u32x4 (&r)[ST]) {
 #pragma unroll
-    for (int k = 0; k < kAttStage; ++k)
+    for (int k = 0; k < ST; ++k)
         r[k] = g.src[min(k * kAttThreads + static_cast<int>(threadIdx.x), max(g.nch, 1) - 1)];
 }
 
-__device__ inline void sub_store(const SubSrc &g, uint32_t *buf, const u32x4 (&r)[kAttStage]) {
+template <int ST>
+__device__ inline void sub_store(const SubSrc &g, uint32_t *buf, const u32x4 (&r)[ST]) {
 #pragma unroll
-    for (int k = 0; k < kAttStage; ++k) {
+    for (int k = 0; k < ST; ++k) {
         const int i = k * kAttThreads + static_cast<int>(threadIdx.x);
         if (i < g.nch) reinterpret_cast<u32x4 *>(buf)[i] = r[k];
     }
@@ -345,7 +347,7 @@ __device__ inline float block_reduce(float v, float *red, bool is_max) {
 // the last row for its k-step windows): while one buffer is decoded, the next
 // sub-chunk's chunks are in flight in registers.  The
 // segment's scores stay in LDS, turned into weights once the keys are done.
-template <int KW, int G, int WS>
+template <int KW, int G, int WS, int ST>
 __global__ __launch_bounds__(kAttThreads) void attend_partial_kernel(AttendArgs a) {
     extern __shared__ __align__(16) unsigned char smem[];
     const int c = blockIdx.x, u = blockIdx.y, tid = threadIdx.x;
@@ -397,7 +399,7 @@ __global__ __launch_bounds__(kAttThreads) void attend_partial_kernel(AttendArgs 
         return last_src;
     };
 
-    u32x4 stg[kAttStage], stg2[kAttStage];
+    u32x4 stg[ST], stg2[ST];
     SubSrc g0 = step_src(0);
     sub_load(g0, stg);
     SubSrc g1 = next_src(1);
@@ -594,7 +596,7 @@ __global__ __launch_bounds__(kAttThreads) void attend_partial_kernel(AttendArgs 
     // the last step's chunks again), so two sub-chunks are in flight while one
     // is decoded; at its end it stores step st + 1's set into the other buffer.
     uint32_t pe_r[kAttPairs];                         // the lane's product operands, held through the key steps
-    auto step = [&](auto key_c, int st, u32x4 (&s_free)[kAttStage], u32x4 (&s_next)[kAttStage],
+    auto step = [&](auto key_c, int st, u32x4 (&s_free)[ST], u32x4 (&s_next)[ST],
                     const SubSrc &g_next, SubSrc &g_load, int dcur) __attribute__((always_inline)) {
         const uint32_t *cur = ((st & 1) ? buf1 : buf0) + dcur;
         uint32_t *nxt = (st & 1) ? buf0 : buf1;
@@ -1578,14 +1580,21 @@ int32_t attend_impl(const kvtc_tensor_ref *k, const kvtc_tensor_ref *v, int64_t 
         const int kw = (a.v.kfetch / 16 + kAttWaves - 1) / kAttWaves;
         // the short width dispatch when both tensors' widths are within {0, 2, 4, 8}
         const bool w248 = widths_248(hk) && widths_248(hv);
+        // two staged chunks per thread where a 256-row sub-chunk fits them (fewer
+        // loads per step), else three
+        const int rs = std::max(hk->row_stride, hv->row_stride);
+        const bool st2 = a.sub == 256 && a.sub * rs + 16 <= 16 * kAttThreads * 2;
         auto pick = [&](auto k1, auto k2, auto k1n, auto k2n) { return w248 ? (kw <= 1 ? k1n : k2n) : (kw <= 1 ? k1 : k2); };
-        auto kern = a.sub == 256 ? pick(attend_partial_kernel<1, 4, kWidthsAll>, attend_partial_kernel<2, 4, kWidthsAll>,
-                                        attend_partial_kernel<1, 4, kWidths248>, attend_partial_kernel<2, 4, kWidths248>)
+        auto kern = a.sub == 256
+                        ? (st2 ? pick(attend_partial_kernel<1, 4, kWidthsAll, 2>, attend_partial_kernel<2, 4, kWidthsAll, 2>,
+                                      attend_partial_kernel<1, 4, kWidths248, 2>, attend_partial_kernel<2, 4, kWidths248, 2>)
+                               : pick(attend_partial_kernel<1, 4, kWidthsAll, 3>, attend_partial_kernel<2, 4, kWidthsAll, 3>,
+                                      attend_partial_kernel<1, 4, kWidths248, 3>, attend_partial_kernel<2, 4, kWidths248, 3>))
                     : a.sub == 128
-                        ? pick(attend_partial_kernel<1, 2, kWidthsAll>, attend_partial_kernel<2, 2, kWidthsAll>,
-                               attend_partial_kernel<1, 2, kWidths248>, attend_partial_kernel<2, 2, kWidths248>)
-                        : pick(attend_partial_kernel<1, 1, kWidthsAll>, attend_partial_kernel<2, 1, kWidthsAll>,
-                               attend_partial_kernel<1, 1, kWidths248>, attend_partial_kernel<2, 1, kWidths248>);
+                        ? pick(attend_partial_kernel<1, 2, kWidthsAll, 3>, attend_partial_kernel<2, 2, kWidthsAll, 3>,
+                               attend_partial_kernel<1, 2, kWidths248, 3>, attend_partial_kernel<2, 2, kWidths248, 3>)
+                        : pick(attend_partial_kernel<1, 1, kWidthsAll, 3>, attend_partial_kernel<2, 1, kWidthsAll, 3>,
+                               attend_partial_kernel<1, 1, kWidths248, 3>, attend_partial_kernel<2, 1, kWidths248, 3>);
         if (!allow_lds(reinterpret_cast<const void *>(kern))) return KVTC_E_DEVICE;
         hipLaunchKernelGGL(kern, dim3(static_cast<unsigned>(nchunks), U), dim3(kAttThreads), lds, stream, a);
         if (launch_status() != KVTC_OK) return KVTC_E_DEVICE;

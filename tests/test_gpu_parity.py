@@ -546,6 +546,9 @@ ATTEND_CASES = [
     ("few-ksteps", small(4, B=1, H=2, s_prefill=1024, s_total=1024 + 45, rank=40, budget=80)),
     ("three-ksteps", small(1, rank=16, budget=32)),
     ("one-kstep", small(1, rank=16, budget=64, choices=(0, 4))),
+    # 72-byte rows: 256-row sub-chunks staged three chunks per thread (rows up to
+    # 63 bytes take two)
+    ("rows-72", small(4, B=1, H=2, s_prefill=1024, s_total=1024 + 45, rank=96, budget=576)),
 ]
 
 
